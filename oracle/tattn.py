@@ -1,0 +1,364 @@
+"""Three-tier tile-sparse attention, computed plainly on the CPU -- TEST
+INFRASTRUCTURE ONLY (tests, smoke check and the bench's cpu_baseline leg).
+
+Per (batch, head) the method runs four steps; each function below names the
+passage it follows.  Notation: N tokens, head dim d, query blocks I of Bq rows
+(m_I real rows), key blocks J of Bk keys (n_J real keys); the last blocks are
+ragged and keep their real sizes.
+
+  O1/O2 pool        q_I, k_J, v_J block means            (Triage: block means;
+                                                          HierPAS: lightweight
+                                                          eager estimate)
+  O3    router      p_IJ = softmax_J(q_I.k_J/sqrt(d) + ln n_J)
+                                                         (APT: attention
+                                                          probability as the
+                                                          importance metric)
+  O4    tiers       dual thresholds tau_hi / tau_lo, optional top-k, or the
+                    entropy-derived head-adaptive top-k; diagonal tiles FULL
+                                                         (APT: dual
+                                                          thresholds; HierPAS:
+                                                          top-k and head-wise
+                                                          retention ratios)
+  O5    fp8         E4M3 codes with one scale per block   (HierPAS: reduced
+                                                          precision)
+  O6/O7 attention   per-tile partials (m, l, o) for FULL / LOW / SKIP tiles,
+                    merged exactly                        (Triage: skip =
+                                                          block means, one
+                                                          fused pass)
+
+Precision: float64 throughout, except that every fp8 code is decided on a
+float32 value (the precision in which the kernel decides it).  Means are
+accumulated in float64 and stored as float32.
+"""
+import math
+
+import numpy as np
+
+from . import e4m3
+
+SKIP, LOW, FULL = 0, 1, 2
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+# ----------------------------------------------------------------------------- O1
+def block_sizes(n: int, b: int) -> np.ndarray:
+    """Real sizes of the ceil(n/b) contiguous blocks of b tokens (last one ragged).
+    Blocks are contiguous runs of the row-major (t, h, w) token order."""
+    nb = -(-n // b)
+    sizes = np.full(nb, b, dtype=np.int64)
+    sizes[-1] = n - (nb - 1) * b
+    return sizes
+
+
+# ----------------------------------------------------------------------------- O2
+def pool_means(x: np.ndarray, b: int) -> np.ndarray:
+    """Block means of x [n, d]: float64 sum divided by the real block size,
+    rounded to float32 (Triage: a skipped tile is replaced by its block means;
+    HierPAS: a lightweight estimate of the attention pattern)."""
+    n, d = x.shape
+    sizes = block_sizes(n, b)
+    out = np.empty((sizes.size, d), dtype=np.float32)
+    x64 = x.astype(np.float64)
+    for j, s in enumerate(sizes):
+        blk = x64[j * b: j * b + s]
+        out[j] = (blk.sum(axis=0) / float(s)).astype(np.float32)
+    return out
+
+
+# ----------------------------------------------------------------------------- O3
+def router(qbar: np.ndarray, kbar: np.ndarray, n: int, bk: int):
+    """Block router: S_IJ = <q_I, k_J>/sqrt(d) + ln n_J and p_IJ = softmax over J
+    (APT: attention probabilities rank the tiles; the ln n_J term makes p_IJ the
+    block's share of attention mass when every key of J equals k_J).
+    Returns (S, p) in float64, shape [Nq, Nk]."""
+    d = qbar.shape[1]
+    nk = block_sizes(n, bk).astype(np.float64)
+    S = (qbar.astype(np.float64) @ kbar.astype(np.float64).T) / math.sqrt(d) + np.log(nk)[None, :]
+    mx = S.max(axis=1, keepdims=True)
+    e = np.exp(S - mx)
+    p = e / e.sum(axis=1, keepdims=True)
+    return S, p
+
+
+# ----------------------------------------------------------------------------- O4
+def diagonal_mask(n: int, bq: int, bk: int) -> np.ndarray:
+    """Tiles whose key-token range intersects the query block's token range
+    ("the diagonal block is always full"); with bq != bk a row has several."""
+    nq, nk = -(-n // bq), -(-n // bk)
+    m = np.zeros((nq, nk), dtype=bool)
+    for i in range(nq):
+        r0, r1 = i * bq, min(n, (i + 1) * bq)
+        j0, j1 = r0 // bk, (r1 - 1) // bk
+        m[i, j0:j1 + 1] = True
+    return m
+
+
+def row_ranks(p: np.ndarray) -> np.ndarray:
+    """Rank of every tile within its row by (p descending, J ascending)."""
+    nq, nk = p.shape
+    ranks = np.empty((nq, nk), dtype=np.int64)
+    cols = np.arange(nk)
+    for i in range(nq):
+        order = np.lexsort((cols, -p[i]))
+        ranks[i, order] = cols
+    return ranks
+
+
+def tiers_threshold(p: np.ndarray, tau_hi: float, tau_lo: float, top_k: int = 0) -> np.ndarray:
+    """Dual thresholds on the router probability (APT's dual thresholding at
+    tile granularity): FULL if p >= tau_hi, LOW if tau_lo <= p < tau_hi, SKIP
+    below tau_lo.  With top_k > 0 only a row's top_k tiles (HierPAS: top-k) may
+    be kept; thresholds then act inside them.  Diagonal forcing is separate."""
+    t = np.full(p.shape, SKIP, dtype=np.uint8)
+    t[p >= tau_lo] = LOW
+    t[p >= tau_hi] = FULL
+    if top_k > 0:
+        t[row_ranks(p) >= top_k] = SKIP
+    return t
+
+
+def head_retention(p: np.ndarray, samples: int, keep_min: float, keep_max: float):
+    """Sampling-based entropy -> head-wise retention ratio (HierPAS).  Rows
+    I_s = floor(s*Nq/S), s < S = min(samples, Nq); H_I = -sum_J p ln p;
+    r_h = clip(exp(mean_s H)/Nk, keep_min, keep_max) (the perplexity share of
+    key blocks); k_h = ceil(r_h * Nk).  The exp(mean entropy)/Nk mapping is a
+    reading of the pages, which give no formula: parity unpinned."""
+    nq, nk = p.shape
+    S = min(samples, nq)
+    rows = (np.arange(S) * nq) // S
+    P = p[rows]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(P > 0, P * np.log(P), 0.0)
+    H = -plogp.sum(axis=1)
+    r = float(np.clip(math.exp(float(H.mean())) / nk, keep_min, keep_max))
+    k = int(math.ceil(r * nk))
+    return r, k, H
+
+
+def tiers_adaptive(p: np.ndarray, k_h: int, full_frac: float) -> np.ndarray:
+    """Head-adaptive tiers: per row, the k_h highest-p tiles are kept; the top
+    ceil(full_frac * k_h) of them run in bf16 (FULL), the rest of the kept ones
+    in fp8 (LOW), the remainder is skipped."""
+    ranks = row_ranks(p)
+    nfull = int(math.ceil(full_frac * k_h))
+    t = np.full(p.shape, SKIP, dtype=np.uint8)
+    t[ranks < k_h] = LOW
+    t[ranks < nfull] = FULL
+    return t
+
+
+def build_lists(t: np.ndarray):
+    """Per query block: kept/skipped key-block indices, [FULL asc | LOW asc |
+    SKIP asc], and the three counts (APT's mask management, as compacted lists)."""
+    nq, nk = t.shape
+    lists = np.empty((nq, nk), dtype=np.int16)
+    counts = np.empty((nq, 3), dtype=np.int32)
+    for i in range(nq):
+        f = np.nonzero(t[i] == FULL)[0]
+        lo = np.nonzero(t[i] == LOW)[0]
+        s = np.nonzero(t[i] == SKIP)[0]
+        lists[i] = np.concatenate([f, lo, s]).astype(np.int16)
+        counts[i] = (f.size, lo.size, s.size)
+    return lists, counts
+
+
+# ----------------------------------------------------------------------------- O5
+def quantise_blocks(x: np.ndarray, b: int):
+    """fp8 E4M3 codes with one scale per block of b rows (HierPAS: reduced
+    precision for less critical regions).  a = max|X_block| (float32);
+    a == 0 -> inv = scale = 1; else inv = fl32(448/a), scale = fl32(a/448);
+    code = E(fl32(x * inv)).  Returns (codes uint8 [n, d], scale f32, inv f32)."""
+    n, d = x.shape
+    x32 = x.astype(np.float32)
+    sizes = block_sizes(n, b)
+    scale = np.empty(sizes.size, dtype=np.float32)
+    inv = np.empty(sizes.size, dtype=np.float32)
+    codes = np.empty((n, d), dtype=np.uint8)
+    for j, s in enumerate(sizes):
+        blk = x32[j * b: j * b + s]
+        a = np.float32(np.abs(blk).max())
+        if a == 0:
+            iv, sc = np.float32(1.0), np.float32(1.0)
+        else:
+            iv, sc = np.float32(448.0) / a, a / np.float32(448.0)
+        inv[j], scale[j] = iv, sc
+        codes[j * b: j * b + s] = e4m3.encode((blk * iv).astype(np.float32))
+    return codes, scale, inv
+
+
+# ----------------------------------------------------------------------------- O6/O7
+def _padded(x, nb, b):
+    n, d = x.shape
+    out = np.zeros((nb * b, d), dtype=np.float64)
+    out[:n] = x
+    return out.reshape(nb, b, d)
+
+
+def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
+                      rows=None, return_partials=False):
+    """One pass over all tiles of every query row, merging per-tile partials
+    exactly (Triage: skip, low precision and full tiles in a single pass).
+
+    FULL: s_j = <q_i,k_j>/sqrt(d); partial (max s, sum e^{s-m}, sum e^{s-m} v_j).
+    LOW:  s^_j = <q^_i,k^_j>/sqrt(d) with X^ = decode(X8) * scale;
+          m_t = max_j s^_j; pi_j = decode(E(fl32(448 e^{s^_j - m_t}))) / 448;
+          partial (m_t, sum pi_j, sum pi_j v^_j).
+    SKIP: sigma = <q_i, k_J>/sqrt(d) + ln n_J; partial (sigma, 1, v_J): one
+          score weighted by n_J, valued by the block mean (Triage).
+    Merge: M = max m; O_i = sum o e^{m-M} / sum l e^{m-M}.
+
+    q, k, v: [n, d] (values as float64); t: tier map [Nq, Nk].
+    ``rows`` restricts the computation to those query blocks (others left 0).
+    Returns O float64 [n, d] (and the per-row partial lists if requested)."""
+    n, d = q.shape
+    nq, nk = t.shape
+    isd = 1.0 / math.sqrt(d)
+    ksz = block_sizes(n, bk)
+    valid = np.arange(bk)[None, :] < ksz[:, None]                      # [Nk, Bk]
+    Kp = _padded(k.astype(np.float64), nk, bk)
+    Vp = _padded(v.astype(np.float64), nk, bk)
+    kblk = np.repeat(np.arange(nk), bk)[:n]
+    qblk = np.repeat(np.arange(nq), bq)[:n]
+    Kh = _padded(e4m3.decode(k8), nk, bk)                              # code values
+    Vh = _padded(e4m3.decode(v8) * sv.astype(np.float64)[kblk][:, None], nk, bk)
+    Qc = e4m3.decode(q8)
+    kb64, vb64 = kbar.astype(np.float64), vbar.astype(np.float64)
+    lnk = np.log(ksz.astype(np.float64))
+    out = np.zeros((n, d), dtype=np.float64)
+    partials = {}
+    for i in (range(nq) if rows is None else rows):
+        r0, r1 = i * bq, min(n, (i + 1) * bq)
+        Q = q[r0:r1].astype(np.float64)
+        ms, ls, os_ = [], [], []
+        F = np.nonzero(t[i] == FULL)[0]
+        if F.size:
+            s = (Q @ Kp[F].reshape(-1, d).T).reshape(r1 - r0, F.size, bk) * isd
+            s = np.where(valid[F][None], s, -np.inf)
+            m = s.max(axis=2)
+            e = np.exp(s - m[..., None])
+            ms.append(m)
+            ls.append(e.sum(axis=2))
+            os_.append(np.matmul(e.transpose(1, 0, 2), Vp[F]).transpose(1, 0, 2))
+        L = np.nonzero(t[i] == LOW)[0]
+        if L.size:
+            raw = (Qc[r0:r1] @ Kh[L].reshape(-1, d).T).reshape(r1 - r0, L.size, bk)
+            sc = float(sq[i]) * sk.astype(np.float64)[L] * isd            # [nL]
+            sh = raw * sc[None, :, None]
+            sh = np.where(valid[L][None], sh, -np.inf)
+            mt = sh.max(axis=2)
+            tq = (448.0 * np.exp(sh - mt[..., None])).astype(np.float32)
+            pi = e4m3.decode(e4m3.encode(tq)) / 448.0
+            pi = np.where(valid[L][None], pi, 0.0)
+            ms.append(mt)
+            ls.append(pi.sum(axis=2))
+            os_.append(np.matmul(pi.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
+        Sk = np.nonzero(t[i] == SKIP)[0]
+        skip_sigma = None
+        if Sk.size:
+            skip_sigma = Q @ kb64[Sk].T * isd + lnk[Sk][None, :]          # [m, nS]
+        # merge (O7)
+        allm = [x for x in ms] + ([skip_sigma] if skip_sigma is not None else [])
+        M = np.max(np.concatenate(allm, axis=1), axis=1)                   # [m]
+        num = np.zeros((r1 - r0, d))
+        den = np.zeros(r1 - r0)
+        for m, l, o in zip(ms, ls, os_):
+            w = np.exp(m - M[:, None])
+            den += (w * l).sum(axis=1)
+            num += np.einsum("it,itd->id", w, o)
+        if skip_sigma is not None:
+            w = np.exp(skip_sigma - M[:, None])
+            den += w.sum(axis=1)
+            num += w @ vb64[Sk]
+        out[r0:r1] = num / den[:, None]
+        if return_partials:
+            partials[i] = (ms, ls, os_, skip_sigma, M, den)
+    if return_partials:
+        return out, partials
+    return out
+
+
+def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
+    """Dense [n, n] weight matrix W of the method on tiny inputs, together with
+    the value matrix each weight multiplies: FULL W_ij = e^{s_ij-M}/L against
+    v_j; LOW W_ij = pi_j e^{m_t-M}/L against v^_j; SKIP W_ij = e^{sigma-M}/(n_J L)
+    against v_j.  Then O = rowsum(W * Vsel)."""
+    n, d = q.shape
+    nq, nk = t.shape
+    isd = 1.0 / math.sqrt(d)
+    ksz = block_sizes(n, bk)
+    kblk = np.repeat(np.arange(nk), bk)[:n]
+    qblk = np.repeat(np.arange(nq), bq)[:n]
+    khat = e4m3.decode(k8)
+    vhat = e4m3.decode(v8) * sv.astype(np.float64)[kblk][:, None]
+    qc = e4m3.decode(q8)
+    W = np.zeros((n, n))
+    sel_low = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        I = qblk[i]
+        logits = np.full(n, -np.inf)
+        for J in range(nk):
+            j0, j1 = J * bk, J * bk + ksz[J]
+            if t[I, J] == FULL:
+                logits[j0:j1] = (k[j0:j1] @ q[i]) * isd
+            elif t[I, J] == SKIP:
+                sig = float(q[i] @ kbar[J].astype(np.float64)) * isd + math.log(ksz[J])
+                logits[j0:j1] = sig - math.log(ksz[J])
+            else:
+                sh = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
+                mt = sh.max()
+                pi = e4m3.decode(e4m3.encode((448.0 * np.exp(sh - mt)).astype(np.float32))) / 448.0
+                logits[j0:j1] = mt + np.log(np.where(pi > 0, pi, 1e-300))
+                logits[j0:j1][pi == 0] = -np.inf
+                sel_low[i, j0:j1] = True
+        M = logits.max()
+        w = np.exp(logits - M)
+        W[i] = w / w.sum()
+    vsel = np.where(sel_low[:, :, None], vhat[None, :, :], v[None, :, :].astype(np.float64))
+    return W, vsel
+
+
+def naive_attention(q, k, v):
+    """Textbook softmax(Q K^T / sqrt(d)) V in float64."""
+    d = q.shape[1]
+    s = q.astype(np.float64) @ k.astype(np.float64).T / math.sqrt(d)
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e / e.sum(axis=1, keepdims=True)) @ v.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- whole plan / forward
+def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
+    """Steps O1-O5 for one (batch, head): q, k, v [n, d].  ``cfg_like`` needs
+    block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
+    full_frac, entropy_samples.  Returns a dict of every intermediate."""
+    mode = cfg_like.mode if mode is None else mode
+    n, d = q.shape
+    bq, bk = cfg_like.block_q, cfg_like.block_k
+    qbar = pool_means(q, bq)
+    kbar = pool_means(k, bk)
+    vbar = pool_means(v, bk)
+    S, p = router(qbar, kbar, n, bk)
+    r_h, k_h = None, None
+    if mode == 0:      # threshold
+        t = tiers_threshold(p, cfg_like.tau_hi, cfg_like.tau_lo, cfg_like.top_k)
+    elif mode == 1:    # adaptive
+        r_h, k_h, _ = head_retention(p, cfg_like.entropy_samples, cfg_like.keep_min, cfg_like.keep_max)
+        t = tiers_adaptive(p, k_h, cfg_like.full_frac)
+    elif mode == 2:    # all full
+        t = np.full(p.shape, FULL, dtype=np.uint8)
+    else:              # external
+        t = np.array(external_tiers, dtype=np.uint8, copy=True)
+    t[diagonal_mask(n, bq, bk)] = FULL
+    lists, counts = build_lists(t)
+    q8, sq, iq = quantise_blocks(q, bq)
+    k8, sk, ik = quantise_blocks(k, bk)
+    v8, sv, iv = quantise_blocks(v, bk)
+    return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
+                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h)
+
+
+def oracle_forward(q, k, v, plan, bq, bk, rows=None):
+    return attention_forward(q, k, v, plan["tiers"], bq, bk, plan["kbar"], plan["vbar"],
+                             plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],
+                             rows=rows)

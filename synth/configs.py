@@ -1,0 +1,76 @@
+"""The five workloads on which the three-tier tile-sparse attention is run.
+
+Shapes, tile sizes, thresholds and generator parameters restate the five
+workload descriptions that accompany the method: a tiny 4x8x8 latent grid, a
+small 8x16x16 grid, a Wan-like 21x30x52 grid with 40 heads, a
+HunyuanVideo-like 33x45x80 grid with 24 heads, and the Wan-like grid again with
+fine 64x16 tiles and head-adaptive retention.  Token counts come from the
+latent grids (frames x height x width).
+"""
+from dataclasses import dataclass, field, replace
+from typing import Tuple
+
+# Mode names follow the C ABI's tattn_mode enumeration.
+MODE_THRESHOLD = 0
+MODE_ADAPTIVE = 1
+MODE_ALL_FULL = 2
+MODE_EXTERNAL = 3
+
+
+@dataclass(frozen=True)
+class WorkloadConfig:
+    cfg_id: int                 # 1..5; seeds the generator stream
+    name: str
+    batch: int
+    heads: int
+    grid: Tuple[int, int, int]  # latent (T, Hg, Wg); tokens are the row-major flattening
+    head_dim: int
+    block_q: int
+    block_k: int
+    tau_hi: float
+    tau_lo: float
+    mode: int = MODE_THRESHOLD
+    top_k: int = 0
+    keep_min: float = 0.05
+    keep_max: float = 0.50
+    full_frac: float = 0.10
+    entropy_samples: int = 256
+    noise_sigma: float = 0.5
+    temperature: bool = False   # per-head temperature T_h ~ U(0.5, 2) divides Q
+    input_fp32: bool = False    # the tiny workload is specified in fp32
+    seed_cfg_id: int = 0        # generator stream to draw from (0: own cfg_id)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def seq_len(self) -> int:
+        t, h, w = self.grid
+        return t * h * w
+
+    @property
+    def n_qblocks(self) -> int:
+        return -(-self.seq_len // self.block_q)
+
+    @property
+    def n_kblocks(self) -> int:
+        return -(-self.seq_len // self.block_k)
+
+    def with_(self, **kw) -> "WorkloadConfig":
+        return replace(self, **kw)
+
+
+CONFIGS = {
+    1: WorkloadConfig(1, "tiny", 1, 2, (4, 8, 8), 64, 64, 64, 0.05, 0.005,
+                      noise_sigma=0.3, input_fp32=True),
+    2: WorkloadConfig(2, "small", 1, 12, (8, 16, 16), 64, 128, 64, 0.02, 0.002,
+                      noise_sigma=0.5),
+    3: WorkloadConfig(3, "wan_like", 1, 40, (21, 30, 52), 128, 128, 64, 0.01, 0.001,
+                      noise_sigma=0.5, temperature=True),
+    4: WorkloadConfig(4, "hunyuan_like", 1, 24, (33, 45, 80), 128, 128, 64, 0.01, 0.001,
+                      noise_sigma=0.5, temperature=True),
+    5: WorkloadConfig(5, "fine_adaptive", 1, 40, (21, 30, 52), 128, 64, 16, 0.01, 0.001,
+                      mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_cfg_id=3),
+}
+
+
+def get_config(cfg_id: int) -> WorkloadConfig:
+    return CONFIGS[cfg_id]
