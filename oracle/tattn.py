@@ -20,14 +20,17 @@ ragged and keep their real sizes.
                                                           top-k and head-wise
                                                           retention ratios)
   O5    fp8         E4M3 codes with one scale per block   (HierPAS: reduced
-                                                          precision)
+                                                          precision); a low
+                                                          tile runs attention
+                                                          on these copies
   O6/O7 attention   per-tile partials (m, l, o) for FULL / LOW / SKIP tiles,
                     merged exactly                        (Triage: skip =
                                                           block means, one
                                                           fused pass)
 
 Precision: float64 throughout, except that every fp8 code is decided on a
-float32 value (the precision in which the kernel decides it).  Means are
+float32 value and the low tier's dequantised values are formed in float32 and
+rounded to float16 (the precisions in which the kernel forms them).  Means are
 accumulated in float64 and stored as float32.
 """
 import math
@@ -187,6 +190,16 @@ def quantise_blocks(x: np.ndarray, b: int):
     return codes, scale, inv
 
 
+def low_values(v8: np.ndarray, sv: np.ndarray, b: int) -> np.ndarray:
+    """Value operand of low-precision tiles: the dequantised E4M3 value
+    decode(code) * scale, formed in float32 and rounded to float16 (the
+    precision in which the kernel forms it).  Returns float64 [n, d]."""
+    n = v8.shape[0]
+    blk = np.repeat(np.arange(-(-n // b)), b)[:n]
+    prod = e4m3.decode(v8).astype(np.float32) * sv.astype(np.float32)[blk][:, None]
+    return prod.astype(np.float32).astype(np.float16).astype(np.float64)
+
+
 # ----------------------------------------------------------------------------- O6/O7
 def _padded(x, nb, b):
     n, d = x.shape
@@ -201,9 +214,10 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     exactly (Triage: skip, low precision and full tiles in a single pass).
 
     FULL: s_j = <q_i,k_j>/sqrt(d); partial (max s, sum e^{s-m}, sum e^{s-m} v_j).
-    LOW:  s^_j = <q^_i,k^_j>/sqrt(d) with X^ = decode(X8) * scale;
-          m_t = max_j s^_j; pi_j = decode(E(fl32(448 e^{s^_j - m_t}))) / 448;
-          partial (m_t, sum pi_j, sum pi_j v^_j).
+    LOW:  the same on the E4M3 copies: s^_j = <q^_i,k^_j>/sqrt(d) with
+          X^ = decode(X8) * scale (q^, k^ exact in float64), values
+          v^_j = fl16(fl32(decode(V8_j) * scale_J)) (the fp16 value operand
+          the low tier multiplies); partial (max s^, sum e^{s^-m}, sum e^{s^-m} v^_j).
     SKIP: sigma = <q_i, k_J>/sqrt(d) + ln n_J; partial (sigma, 1, v_J): one
           score weighted by n_J, valued by the block mean (Triage).
     Merge: M = max m; O_i = sum o e^{m-M} / sum l e^{m-M}.
@@ -221,7 +235,7 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     kblk = np.repeat(np.arange(nk), bk)[:n]
     qblk = np.repeat(np.arange(nq), bq)[:n]
     Kh = _padded(e4m3.decode(k8), nk, bk)                              # code values
-    Vh = _padded(e4m3.decode(v8) * sv.astype(np.float64)[kblk][:, None], nk, bk)
+    Vh = _padded(low_values(v8, sv, bk), nk, bk)
     Qc = e4m3.decode(q8)
     kb64, vb64 = kbar.astype(np.float64), vbar.astype(np.float64)
     lnk = np.log(ksz.astype(np.float64))
@@ -247,12 +261,10 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
             sh = raw * sc[None, :, None]
             sh = np.where(valid[L][None], sh, -np.inf)
             mt = sh.max(axis=2)
-            tq = (448.0 * np.exp(sh - mt[..., None])).astype(np.float32)
-            pi = e4m3.decode(e4m3.encode(tq)) / 448.0
-            pi = np.where(valid[L][None], pi, 0.0)
+            e = np.exp(sh - mt[..., None])
             ms.append(mt)
-            ls.append(pi.sum(axis=2))
-            os_.append(np.matmul(pi.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
+            ls.append(e.sum(axis=2))
+            os_.append(np.matmul(e.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
         Sk = np.nonzero(t[i] == SKIP)[0]
         skip_sigma = None
         if Sk.size:
@@ -281,7 +293,7 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
 def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
     """Dense [n, n] weight matrix W of the method on tiny inputs, together with
     the value matrix each weight multiplies: FULL W_ij = e^{s_ij-M}/L against
-    v_j; LOW W_ij = pi_j e^{m_t-M}/L against v^_j; SKIP W_ij = e^{sigma-M}/(n_J L)
+    v_j; LOW W_ij = e^{s^_ij-M}/L against v^_j; SKIP W_ij = e^{sigma-M}/(n_J L)
     against v_j.  Then O = rowsum(W * Vsel)."""
     n, d = q.shape
     nq, nk = t.shape
@@ -290,7 +302,7 @@ def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
     kblk = np.repeat(np.arange(nk), bk)[:n]
     qblk = np.repeat(np.arange(nq), bq)[:n]
     khat = e4m3.decode(k8)
-    vhat = e4m3.decode(v8) * sv.astype(np.float64)[kblk][:, None]
+    vhat = low_values(v8, sv, bk)
     qc = e4m3.decode(q8)
     W = np.zeros((n, n))
     sel_low = np.zeros((n, n), dtype=bool)
@@ -305,11 +317,7 @@ def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
                 sig = float(q[i] @ kbar[J].astype(np.float64)) * isd + math.log(ksz[J])
                 logits[j0:j1] = sig - math.log(ksz[J])
             else:
-                sh = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
-                mt = sh.max()
-                pi = e4m3.decode(e4m3.encode((448.0 * np.exp(sh - mt)).astype(np.float32))) / 448.0
-                logits[j0:j1] = mt + np.log(np.where(pi > 0, pi, 1e-300))
-                logits[j0:j1][pi == 0] = -np.inf
+                logits[j0:j1] = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
                 sel_low[i, j0:j1] = True
         M = logits.max()
         w = np.exp(logits - M)

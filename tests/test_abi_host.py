@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports every function declared
+in include/tattn.h, and host-only validation / workspace sizing behave."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_sparse_mixed_amd as tsm
+from tile_sparse_mixed_amd import Config, make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tattn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tsm.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def good(**kw):
+    base = dict(batch=1, heads=40, seq_len=32760, head_dim=128, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001)
+    base.update(kw)
+    return make_config(**base)
+
+
+def status(lib, cfg):
+    return lib.tattn_validate(ctypes.byref(cfg))
+
+
+def test_valid_configs(lib):
+    assert status(lib, good()) == 0
+    assert status(lib, good(head_dim=64, block_q=64, seq_len=256, heads=2)) == 0
+    assert status(lib, good(mode="all_full")) == 0
+    assert status(lib, good(mode="adaptive")) == 0
+    assert status(lib, good(seq_len=118800, heads=24)) == 0
+    assert status(lib, good(top_k=10)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -1), (dict(heads=-1), -1), (dict(seq_len=0), -1),
+    (dict(head_dim=96), -2), (dict(block_q=32), -2), (dict(block_k=16), -2),
+    (dict(tau_hi=0.001, tau_lo=0.01), -1), (dict(tau_lo=-0.1), -1), (dict(tau_hi=float("inf")), -1),
+    (dict(top_k=-1), -1), (dict(top_k=513), -1), (dict(mode=7), -1),
+    (dict(mode="adaptive", keep_min=0.6, keep_max=0.5), -1), (dict(mode="adaptive", full_frac=0.0), -1),
+    (dict(mode="adaptive", entropy_samples=0), -1),
+    (dict(seq_len=64 * 5000), -2),
+])
+def test_invalid_configs(lib, kw, code):
+    st = status(lib, good(**kw))
+    assert st == code, (kw, st, lib.tattn_last_error())
+    assert lib.tattn_last_error()
+
+
+def test_dtype_and_stride_rules(lib):
+    c = good()
+    c.in_dtype = 1
+    assert status(lib, c) == -2
+    c = good()
+    c.out_dtype = 5
+    assert status(lib, c) == -1
+    c = good()
+    c.stride_n = 100
+    assert status(lib, c) == -1
+    c = good()
+    c.stride_n = 64
+    assert status(lib, c) == -1
+    assert lib.tattn_validate(None) == -1
+
+
+def test_workspace_formula(lib):
+    c = good()
+    n = ctypes.c_size_t()
+    assert lib.tattn_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == 0
+    BH, Nq, Nk, D = 40, 256, 512, 128
+    # dominant regions: fp8 K and V^T, bf16 V^T, float64 logits, p, tiers, lists, means
+    floor = BH * Nk * 64 * D * 4 + BH * Nq * Nk * (8 + 4 + 1 + 2) + BH * (Nq + 2 * Nk) * D * 4
+    assert floor <= n.value <= floor * 1.05
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(head_dim=96)), ctypes.byref(n)) == -2
+
+
+def test_plan_rejects_bad_pointers_before_any_launch(lib):
+    c = good(seq_len=256, heads=2, head_dim=64, block_q=64)
+    out = ctypes.c_void_p()
+    assert lib.tattn_plan(ctypes.byref(c), None, None, None, None, 0, None, ctypes.byref(out)) == -1
+    # misaligned q (not 16-byte) is rejected on the host
+    assert lib.tattn_plan(ctypes.byref(c), 8, 16, 32, 256, 1 << 30, None, ctypes.byref(out)) == -1
+    # workspace too small / misaligned / missing
+    assert lib.tattn_plan(ctypes.byref(c), 16, 32, 48, 256, 16, None, ctypes.byref(out)) == -3
+    assert lib.tattn_plan(ctypes.byref(c), 16, 32, 48, 300, 1 << 30, None, ctypes.byref(out)) == -3
+    assert lib.tattn_plan(ctypes.byref(c), 16, 32, 48, None, 1 << 30, None, ctypes.byref(out)) == -3
+    assert out.value is None
+    assert lib.tattn_forward(None, 16, 32, 48, 64, None) == -1
+    assert lib.tattn_plan_stats(None, None) == -1
+    lib.tattn_plan_destroy(None)
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.tattn_status_str(s)
+    assert lib.tattn_status_str(-99) == b"unknown status"

@@ -1,0 +1,190 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Bars (see the method's tolerances): pooled means, scales and E4M3 codes
+bit-exact; the tier map bit-exact outside the 1e-5 relative band around each
+threshold; lists and counts exact; the output under the oracle's tier map
+within max-abs 1e-2 and mean-abs 1e-3 (unit-scale V), and within 5e-3 max-abs
+when every tile is FULL.
+"""
+import numpy as np
+import pytest
+
+from oracle import tattn as T
+from synth import CONFIGS
+
+from gpu_cases import OracleCfg, band_mask, device_inputs, gpu_plan, oracle_head
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": CONFIGS[1],
+    "small": CONFIGS[2],
+    "ragged128": CONFIGS[3].with_(grid=(2, 10, 50), heads=3),          # N=1000: Nq=8 (last 104), Nk=16 (last 40)
+    "ragged64x64": CONFIGS[2].with_(grid=(3, 7, 9), heads=2, block_q=64, head_dim=128),   # N=189
+    "d64_ragged": CONFIGS[2].with_(grid=(5, 9, 13), heads=2),         # N=585
+}
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def case(request):
+    name = request.param
+    cfg = SMALL[name]
+    _log(f"[case {name}] N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} tile={cfg.block_q}x{cfg.block_k}")
+    g, dev = device_inputs(cfg)
+    oc = OracleCfg(cfg)
+    oracle = [[oracle_head(g, b, h, oc) for h in range(cfg.heads)] for b in range(cfg.batch)]
+    return name, cfg, g, dev, oc, oracle
+
+
+def test_pool_bitexact(case):
+    name, cfg, g, dev, oc, orc = case
+    p = gpu_plan(dev, cfg)
+    pool = p.pool()
+    k8, v8 = p.codes()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            o = orc[b][h]
+            for key in ("qbar", "kbar", "vbar", "sq", "sk", "sv"):
+                assert np.array_equal(pool[key][b, h], o[key]), (name, key, h)
+            assert np.array_equal(k8[b, h], o["k8"]), (name, "k8", h)
+            assert np.array_equal(v8[b, h], o["v8"]), (name, "v8", h)
+
+
+def test_router_tiers_and_lists(case):
+    name, cfg, g, dev, oc, orc = case
+    p = gpu_plan(dev, cfg)
+    tiers, pgpu = p.tiers(with_p=True)
+    lists, counts = p.lists()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            o = orc[b][h]
+            band = band_mask(o["p"], oc.tau_hi, oc.tau_lo)
+            assert np.array_equal(tiers[b, h][~band], o["tiers"][~band]), (name, h)
+            assert np.max(np.abs(pgpu[b, h] - o["p"]) / o["p"]) < 1e-6
+            li, co = T.build_lists(tiers[b, h])
+            assert np.array_equal(lists[b, h], li) and np.array_equal(counts[b, h], co), (name, h)
+
+
+def test_router_top_k():
+    cfg = CONFIGS[2].with_(heads=3, top_k=7)
+    g, dev = device_inputs(cfg)
+    oc = OracleCfg(cfg)
+    p = gpu_plan(dev, cfg)
+    tiers = p.tiers()
+    for h in range(cfg.heads):
+        o = oracle_head(g, 0, h, oc)
+        band = band_mask(o["p"], oc.tau_hi, oc.tau_lo)
+        assert np.array_equal(tiers[0, h][~band], o["tiers"][~band])
+        kept_nondiag = (o["tiers"] != 0) & ~T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
+        assert kept_nondiag.sum(axis=1).max() <= 7
+
+
+def _compare(out, ref, max_abs, mean_abs, what):
+    err = np.abs(out.astype(np.float64) - ref)
+    _log(f"  {what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= max_abs, (what, err.max())
+    assert err.mean() <= mean_abs, (what, err.mean())
+
+
+def test_all_full_equals_dense(case):
+    name, cfg, g, dev, oc, orc = case
+    import tile_sparse_mixed_amd as tsm
+    p = gpu_plan(dev, cfg, mode="all_full")
+    assert np.all(p.tiers() == 2)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    for h in range(cfg.heads):
+        ref = T.naive_attention(g["q"][0, h], g["k"][0, h], g["v"][0, h])
+        _compare(out[0, h], ref, 5e-3, 1e-3, f"{name} all-full h{h}")
+
+
+def test_forward_under_oracle_tiers(case):
+    name, cfg, g, dev, oc, orc = case
+    import tile_sparse_mixed_amd as tsm
+    p = gpu_plan(dev, cfg, mode="external")
+    t = np.stack([[orc[b][h]["tiers"] for h in range(cfg.heads)] for b in range(cfg.batch)])
+    p.set_tiers(t)
+    assert np.array_equal(p.tiers(), t)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    for h in range(cfg.heads):
+        o = orc[0][h]
+        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], o, cfg.block_q, cfg.block_k)
+        _compare(out[0, h], ref, 1e-2, 1e-3, f"{name} oracle-tiers h{h}")
+
+
+def test_forward_random_tiers(case):
+    """Random maps exercise every tier (and ragged tiles) far more than routing does."""
+    name, cfg, g, dev, oc, orc = case
+    import tile_sparse_mixed_amd as tsm
+    p = gpu_plan(dev, cfg, mode="external")
+    rng = np.random.default_rng(17)
+    t = rng.choice(np.array([0, 1, 2], np.uint8), p=[0.5, 0.35, 0.15],
+                   size=(cfg.batch, cfg.heads, cfg.n_qblocks, cfg.n_kblocks))
+    p.set_tiers(t)
+    tg = p.tiers()
+    for h in range(cfg.heads):
+        diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
+        assert np.all(tg[0, h][diag] == 2) and np.array_equal(tg[0, h][~diag], t[0, h][~diag])
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    for h in range(cfg.heads):
+        o = oracle_head(g, 0, h, oc, mode=3, external=tg[0, h])
+        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], o, cfg.block_q, cfg.block_k)
+        _compare(out[0, h], ref, 1e-2, 1e-3, f"{name} random-tiers h{h}")
+
+
+def test_threshold_end_to_end_bf16_out(case):
+    name, cfg, g, dev, oc, orc = case
+    import tile_sparse_mixed_amd as tsm
+    p = gpu_plan(dev, cfg, out_fp32=False)
+    tg = p.tiers()
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).float().cpu().numpy()
+    for h in range(cfg.heads):
+        o = oracle_head(g, 0, h, oc, mode=3, external=tg[0, h])
+        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], o, cfg.block_q, cfg.block_k)
+        # bf16 output adds up to half a bf16 ulp (2^-9 relative) of rounding
+        err = np.abs(out[0, h] - ref) - np.abs(ref) * 2.0 ** -9
+        assert err.max() <= 1e-2 and np.abs(out[0, h] - ref).mean() <= 1.5e-3, (name, h)
+
+
+def test_constant_keys_skip_is_exact():
+    cfg = CONFIGS[3].with_(grid=(2, 10, 50), heads=2)
+    import torch
+    import tile_sparse_mixed_amd as tsm
+    g, dev = device_inputs(cfg)
+    n, bk = cfg.seq_len, cfg.block_k
+    nk = cfg.n_kblocks
+    kc = g["k"][0, :, ::bk, :]                                           # first key of every block
+    kconst = np.repeat(kc, bk, axis=1)[:, :n]
+    g["k"][0] = kconst
+    bits = (kconst.view(np.uint32) >> 16).astype(np.uint16)
+    dev["k"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda().unsqueeze(0).contiguous()
+    p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=bk, tau_hi=2.0, tau_lo=2.0,
+                 out_fp32=True)
+    tg = p.tiers()
+    diag = T.diagonal_mask(n, cfg.block_q, bk)
+    assert np.all(tg[0, :, ~diag] == 0)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    for h in range(cfg.heads):
+        ref = T.naive_attention(g["q"][0, h], g["k"][0, h], g["v"][0, h])
+        # exact identity; the kernel's bf16 block means add <= 2^-9 relative on skipped terms
+        _compare(out[0, h], ref, 1e-2, 1e-3, f"constant-keys h{h}")
+
+
+def test_unit_values_give_unit_output():
+    cfg = CONFIGS[3].with_(grid=(2, 10, 50), heads=2)
+    import torch
+    import tile_sparse_mixed_amd as tsm
+    g, dev = device_inputs(cfg)
+    dev["v"] = torch.ones_like(dev["v"])
+    rng = np.random.default_rng(3)
+    t = rng.integers(0, 3, size=(1, cfg.heads, cfg.n_qblocks, cfg.n_kblocks)).astype(np.uint8)
+    for mode in ("external", "all_full", "threshold"):
+        p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k,
+                     tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo, mode=mode, out_fp32=True)
+        if mode == "external":
+            p.set_tiers(t)
+        out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+        assert np.max(np.abs(out - 1.0)) < 1e-3, (mode, np.max(np.abs(out - 1.0)))

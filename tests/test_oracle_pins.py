@@ -244,3 +244,20 @@ def test_lists_partition_and_order():
         f, lo, s = lists[i][:nf], lists[i][nf:nf + nl], lists[i][nf + nl:]
         assert np.all(np.diff(f) > 0) and np.all(np.diff(lo) > 0) and np.all(np.diff(s) > 0)
         assert np.all(t[i, f] == FULL) and np.all(t[i, lo] == LOW) and np.all(t[i, s] == SKIP)
+
+
+def test_low_values_round_once_to_fp16():
+    """The low tier's value operand is decode(code) * scale rounded to fp16:
+    within half an fp16 ulp of the exact product, and exact when the scale is
+    a power of two (the code values have 4 significant bits)."""
+    r = np.random.default_rng(8)
+    codes = r.integers(0, 256, size=(64 * 3, 8)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    sv = (r.uniform(0.001, 0.05, size=3)).astype(np.float32)
+    got = T.low_values(codes, sv, 64)
+    exact = T.e4m3.decode(codes) * np.repeat(sv.astype(np.float64), 64)[:, None]
+    tol = np.maximum(np.abs(exact) * 2.0 ** -11, 2.0 ** -25)
+    assert np.all(np.abs(got - exact) <= tol * 1.0000001)
+    p2 = np.array([2.0 ** -7, 2.0 ** -3, 1.0], np.float32)
+    assert np.array_equal(T.low_values(codes, p2, 64), T.e4m3.decode(codes) * np.repeat(p2.astype(np.float64), 64)[:, None])
