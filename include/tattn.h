@@ -1,0 +1,184 @@
+/*
+ * tattn.h -- three-tier tile-sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, per (batch, head), an approximation of
+ * softmax(Q K^T / sqrt(d)) V in which every (query-block I, key-block J) tile
+ * runs in one of three tiers:
+ *   FULL  exact scores and values in bf16 (fp32 accumulation),
+ *   LOW   fp8 E4M3 operands with one scale per block,
+ *   SKIP  the tile is replaced by its block means: one score
+ *         q_i . kbar_J / sqrt(d) + ln n_J valued by vbar_J.
+ * Tiers come from a block router, p_IJ = softmax_J(qbar_I . kbar_J / sqrt(d)
+ * + ln n_J), with dual thresholds tau_hi / tau_lo and an optional per-row
+ * top-k, or from an entropy-derived per-head top-k; diagonal tiles are always
+ * FULL.  Sources of the method:
+ *   - "Triage" (abstract): three approximation tiers per tile, skipping by
+ *     block means, one fused kernel over all tiers in a single pass.
+ *   - "APT" (abstract): attention probability as the importance metric; dual
+ *     thresholds select elements and assign precision; mask management and
+ *     tile dataflow.
+ *   - "HierPAS" (abstract): a lightweight eager estimate of the attention
+ *     pattern, sampling-based entropy for head-wise retention ratios,
+ *     progressively reduced precision, a top-k engine.
+ *   - "FG-Attn" (abstract): M x N tile granularity.
+ *
+ * Conventions
+ *   - Every pointer is a DEVICE pointer unless its comment says "host".
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Calls are asynchronous on `stream` except those marked SYNC, which
+ *     synchronise `stream` before returning.
+ *   - Every call returns a tattn_status; nothing aborts and no C++ exception
+ *     crosses the ABI.  tattn_last_error() gives a thread-local message for
+ *     the last failing call on the calling thread.
+ *   - Arguments are validated before anything is launched: a call that
+ *     returns an error has launched nothing and written nothing.
+ *   - Tensors Q, K, V, O are [batch, heads, seq_len, head_dim] bf16 (O may
+ *     be fp32), head_dim contiguous, sharing the element strides of the
+ *     config; base pointers 16-byte aligned and stride_n a multiple of 8.
+ *   - The library never allocates device memory: the caller passes a
+ *     workspace of tattn_workspace_bytes() bytes and owns it.
+ */
+#ifndef TATTN_H
+#define TATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TATTN_OK = 0,
+  TATTN_E_INVALID = -1,      /* a null pointer, bad size, bad threshold, misalignment */
+  TATTN_E_UNSUPPORTED = -2,  /* a valid request outside what the kernels implement    */
+  TATTN_E_WORKSPACE = -3,    /* workspace missing, misaligned or too small             */
+  TATTN_E_HIP = -4,          /* a HIP runtime call or kernel launch failed             */
+  TATTN_E_STATE = -5         /* a plan used against other tensors, or in the wrong mode */
+} tattn_status;
+
+/* Tier-map byte values. */
+typedef enum { TATTN_SKIP = 0, TATTN_LOW = 1, TATTN_FULL = 2 } tattn_tier;
+
+typedef enum {
+  TATTN_MODE_THRESHOLD = 0,  /* FULL if p >= tau_hi, LOW if tau_lo <= p < tau_hi, else SKIP;
+                                top_k > 0 first keeps only the row's top_k tiles        */
+  TATTN_MODE_ADAPTIVE = 1,   /* per head k_h from the entropy of p on sampled rows; per row
+                                the top ceil(full_frac*k_h) tiles FULL, the rest of the top
+                                k_h LOW, the remainder SKIP                              */
+  TATTN_MODE_ALL_FULL = 2,   /* every tile FULL: dense attention through the same kernel */
+  TATTN_MODE_EXTERNAL = 3    /* tiers supplied with tattn_plan_set_tiers                 */
+} tattn_mode;
+
+typedef enum { TATTN_BF16 = 0, TATTN_FP32 = 1 } tattn_dtype;
+
+typedef struct {
+  int32_t batch, heads, seq_len, head_dim; /* head_dim in {64, 128}                          */
+  int32_t block_q, block_k;                /* (64, 64) or (128, 64)                          */
+  float tau_hi, tau_lo;                    /* 0 <= tau_lo <= tau_hi, finite                  */
+  int32_t top_k;                           /* 0 = off, else 1..ceil(seq_len/block_k)         */
+  int32_t mode;                            /* tattn_mode                                     */
+  float keep_min, keep_max, full_frac;     /* ADAPTIVE: retention clip and FULL share        */
+  int32_t entropy_samples;                 /* ADAPTIVE: number of sampled query blocks       */
+  int32_t in_dtype, out_dtype;             /* in: TATTN_BF16; out: TATTN_BF16 or TATTN_FP32  */
+  int64_t stride_b, stride_h, stride_n;    /* element strides shared by Q, K, V and O        */
+} tattn_config;
+
+typedef struct tattn_plan_s* tattn_plan_t;  /* opaque host object; device state is in the workspace */
+
+typedef struct {
+  int64_t n_full, n_low, n_skip;  /* tiles per tier, over all (b, h, I, J)           */
+  int64_t n_diag;                 /* diagonal tiles (always FULL)                    */
+  double flops_bf16;              /* executed 16-bit MFMA flops: FULL and SKIP tiles,
+                                     and the P.V half of LOW tiles                  */
+  double flops_fp8;               /* executed fp8 MFMA flops: the score half of LOW  */
+  double flops_dense;             /* 4 * N^2 * d * B * H: dense-equivalent work      */
+} tattn_stats;
+
+/* Check a config without touching any device.  Host only; no HIP calls. */
+tattn_status tattn_validate(const tattn_config* cfg);
+
+/* Bytes of workspace that tattn_plan needs for `cfg` (host only).  The
+ * workspace must be 256-byte aligned; its layout is private to the library. */
+tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes /* host out */);
+
+/*
+ * Build a plan: block pooling, fp8 quantisation and routing.
+ *  1. Block means qbar_I, kbar_J, vbar_J (float64 sums, stored as float32) and,
+ *     per block, amax, scale = amax/448 and E4M3 codes of K and V (V kept as the
+ *     fp16 dequantised values the low tier multiplies), plus the Q-block scales
+ *     ("Triage": block means; "HierPAS": reduced precision).
+ *  2. Router p_IJ = softmax_J(qbar_I . kbar_J / sqrt(d) + ln n_J) in float64
+ *     ("APT": attention probability as importance), and
+ *  3. the tier map by `cfg->mode` (dual thresholds, top-k, entropy-adaptive,
+ *     all-full) with diagonal tiles forced FULL, compacted per query block into
+ *     [FULL asc | LOW asc | SKIP asc] key-block lists.
+ * q, k, v: the caller's tensors.  The plan keeps derived copies of K and V
+ * (E4M3 codes, a transposed fp16 V, means) in `workspace`, so a later
+ * tattn_forward must be given the same k and v pointers with unchanged
+ * contents.  *out receives a new host handle (free with tattn_plan_destroy);
+ * it stays valid while the workspace lives.  In TATTN_MODE_EXTERNAL the
+ * router is not run and the plan has no tiers until tattn_plan_set_tiers.
+ */
+tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, const void* v,
+                        void* workspace, size_t workspace_bytes, void* stream, tattn_plan_t* out);
+
+/*
+ * The fused three-tier pass ("Triage": one kernel, all tiers, single pass):
+ * for every query block, an online softmax over its FULL tiles (bf16 MFMA),
+ * its LOW tiles (scores from E4M3 Q and K on fp8 MFMA, values from E4M3 V) and
+ * its SKIP tiles (block means with a ln n_J bias), then O = acc / l.
+ * o: output tensor with the config's strides, dtype cfg->out_dtype.
+ * k and v must be the pointers the plan was built with (TATTN_E_STATE if not).
+ */
+tattn_status tattn_forward(tattn_plan_t plan, const void* q, const void* k, const void* v, void* o,
+                           void* stream);
+
+/* SYNC.  Replace the plan's tier map with a host map [B, H, Nq, Nk] of bytes in
+ * {0, 1, 2}; diagonal tiles are forced FULL and the lists rebuilt.  Only for a
+ * plan built in TATTN_MODE_EXTERNAL (TATTN_E_STATE otherwise); a byte outside
+ * {0,1,2} gives TATTN_E_INVALID and leaves the plan unchanged. */
+tattn_status tattn_plan_set_tiers(tattn_plan_t plan, const uint8_t* host_tiers, void* stream);
+
+/* SYNC.  Copy out the tier map [B, H, Nq, Nk] (bytes) and/or the router
+ * probabilities p [B, H, Nq, Nk] (float32, rounded from the float64 values;
+ * zero in ALL_FULL and EXTERNAL modes).  Either host pointer may be NULL. */
+tattn_status tattn_plan_get_tiers(tattn_plan_t plan, uint8_t* host_tiers, float* host_p, void* stream);
+
+/* SYNC.  Copy out the compacted lists [B, H, Nq, Nk] (int16 key-block indices,
+ * per row FULL ascending, then LOW ascending, then SKIP ascending) and/or the
+ * counts [B, H, Nq, 3] (int32: n_full, n_low, n_skip).  Either may be NULL. */
+tattn_status tattn_plan_get_lists(tattn_plan_t plan, int16_t* host_lists, int32_t* host_counts,
+                                  void* stream);
+
+/* SYNC.  Copy out the pooled statistics: qbar [B,H,Nq,d], kbar and vbar
+ * [B,H,Nk,d] (float32), and the E4M3 scales sq [B,H,Nq], sk and sv [B,H,Nk]
+ * (float32, amax/448, 1 for an all-zero block).  Any pointer may be NULL. */
+tattn_status tattn_plan_get_pool(tattn_plan_t plan, float* qbar, float* kbar, float* vbar, float* sq,
+                                 float* sk, float* sv, void* stream);
+
+/* SYNC.  Copy out, in the canonical layout [B, H, seq_len, head_dim], the
+ * E4M3 codes of K (bytes) and the low tier's value operand (fp16 bit
+ * patterns of fl16(fl32(decode(E4M3(v * inv)) * scale)) per element of V).
+ * Either may be NULL. */
+tattn_status tattn_plan_get_codes(tattn_plan_t plan, uint8_t* host_k8, uint16_t* host_vlow, void* stream);
+
+/* SYNC.  Tier counts and executed / dense-equivalent flops of the plan. */
+tattn_status tattn_plan_stats(tattn_plan_t plan, tattn_stats* host_out);
+
+/* SYNC.  ADAPTIVE mode: per (b, h) k_h (int32 [B*H]) and r_h (float64 [B*H]);
+ * either may be NULL.  TATTN_E_STATE for other modes. */
+tattn_status tattn_plan_get_kh(tattn_plan_t plan, int32_t* host_kh, double* host_rh);
+
+/* Free the host handle (the workspace stays the caller's).  NULL is ignored. */
+void tattn_plan_destroy(tattn_plan_t plan);
+
+/* Static strings; never NULL. */
+const char* tattn_status_str(tattn_status status);
+const char* tattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TATTN_H */

@@ -1,0 +1,260 @@
+// K1: block pooling and per-block E4M3 quantisation, one streaming pass over
+// Q, K and V (HBM-bound).
+//
+// Per (b, h, key block J) one workgroup reads K_J and V_J once and writes
+//   kbar_J, vbar_J   float32 block means (float64 sums / n_J; "Triage": a skipped
+//                    tile is replaced by its block means),
+//   kbar16, kbarlo   the K means as a bf16 pair hi + lo (hi = bf16(kbar), lo =
+//                    bf16(kbar - hi)), the score operand of skipped tiles,
+//   vbar16           the V means rounded to fp16 (value operand of skipped tiles),
+//   sk_J, sv_J       amax/448 (1 for an all-zero block),
+//   k8               E4M3 codes of K_J, row-major with k8_pos d order,
+//   vt               V_J as fp16, transposed ([d][key]) in the vt_pos key order
+//                    the fused kernel's P.V uses,
+//   vlow             the low tier's V operand, fl16(fl32(decode(E4M3(v * inv)) * sv)),
+//                    in the same transposed layout.
+// Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
+#include "tattn_device.hpp"
+#include "tattn_internal.hpp"
+
+namespace tattn {
+namespace {
+
+constexpr int kThreads = 256;
+
+// fl32(448 / a) and fl32(a / 448), correctly rounded: a float64 quotient of
+// two floats rounded once to float equals the correctly rounded float quotient.
+// An all-zero block gets 1 for both.
+__device__ inline float inv448(float a) { return a == 0.0f ? 1.0f : static_cast<float>(448.0 / static_cast<double>(a)); }
+__device__ inline float scale448(float a) { return a == 0.0f ? 1.0f : static_cast<float>(static_cast<double>(a) / 448.0); }
+
+// Block-wide float max; `red` holds kThreads/64 floats.
+__device__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; i++) r = __builtin_fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// Column sums of a block of `rows` real rows (<= BLK) of a [N, D] bf16 tensor
+// slice starting at `base` (row stride sn elements).  Each thread keeps its
+// ROWS_PER_THREAD row chunks of 8 values in `vals` (float) for later use.
+// Returns, for threads t < D, the float64 column sum of column t.
+template <int D, int BLK>
+struct BlockLoad {
+  static constexpr int CH = D / 8;              // 16-byte chunks per row
+  static constexpr int RT = kThreads / CH;      // threads per column chunk
+  static constexpr int RPT = (BLK + RT - 1) / RT;
+  float vals[RPT][8];
+};
+
+template <int D, int BLK>
+__device__ void load_block(const uint16_t* __restrict__ base, int64_t sn, int rows, BlockLoad<D, BLK>& bl,
+                           double* __restrict__ red /* [RT][D] */, double& colsum, float& amax) {
+  using BL = BlockLoad<D, BLK>;
+  const int t = threadIdx.x;
+  const int c = t % BL::CH, r0 = t / BL::CH;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) acc[e] = 0.0;
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < BL::RPT; i++) {
+    const int r = r0 + i * BL::RT;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (r < rows && r < BLK) raw = *reinterpret_cast<const uint4*>(base + (int64_t)r * sn + c * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float f = __uint_as_float(e & 1 ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+      bl.vals[i][e] = f;
+      acc[e] += static_cast<double>(f);
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(f));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) red[r0 * D + c * 8 + e] = acc[e];
+  amax = mx;
+  __syncthreads();
+  colsum = 0.0;
+  if (t < D) {
+    double s = 0.0;
+    for (int i = 0; i < BL::RT; i++) s += red[i * D + t];
+    colsum = s;
+  }
+  __syncthreads();
+}
+
+template <int D, int BK>
+__global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
+  static_assert(BK == kTile, "key blocks are 64 keys");
+  using BL = BlockLoad<D, BK>;
+  __shared__ double red[BL::RT * D];
+  __shared__ float fred[kThreads / 64];
+  __shared__ uint16_t tileT[BK * D];   // V block as bf16, [key][d], for the transposed stores
+
+  const Dims& dm = a.d;
+  const int bh = blockIdx.x / dm.Nk, J = blockIdx.x % dm.Nk;
+  const int b = bh / dm.H, h = bh % dm.H;
+  const int rows = min(BK, dm.N - J * BK);
+  const int64_t off = (int64_t)b * dm.sb + (int64_t)h * dm.sh + (int64_t)J * BK * dm.sn;
+  unsigned char* ws = a.ws;
+  float* kbar = reinterpret_cast<float*>(ws + a.L.kbar) + ((int64_t)bh * dm.Nk + J) * D;
+  float* vbar = reinterpret_cast<float*>(ws + a.L.vbar) + ((int64_t)bh * dm.Nk + J) * D;
+  uint16_t* kbar16 = reinterpret_cast<uint16_t*>(ws + a.L.kbar16) + ((int64_t)bh * dm.Nk + J) * D;
+  uint16_t* kbarlo = reinterpret_cast<uint16_t*>(ws + a.L.kbarlo) + ((int64_t)bh * dm.Nk + J) * D;
+  uint16_t* vbar16 = reinterpret_cast<uint16_t*>(ws + a.L.vbar16) + ((int64_t)bh * dm.Nk + J) * D;
+  float* sk = reinterpret_cast<float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk + J;
+  float* sv = reinterpret_cast<float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk + J;
+  unsigned char* k8 = ws + a.L.k8 + ((int64_t)bh * dm.Nk + J) * BK * D;
+  uint16_t* vlow = reinterpret_cast<uint16_t*>(ws + a.L.vlow) + ((int64_t)bh * dm.Nk + J) * BK * D;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + a.L.vt) + ((int64_t)bh * dm.Nk + J) * BK * D;
+
+  const int t = threadIdx.x;
+  const int c = t % BL::CH, r0 = t / BL::CH;
+  BL bl;
+  double colsum;
+  float amax;
+
+  // ---- K: means, scale, codes (row-major, k8_pos order inside each row)
+  load_block<D, BK>(a.k + off, dm.sn, rows, bl, red, colsum, amax);
+  if (t < D) {
+    const float m = static_cast<float>(colsum / static_cast<double>(rows));
+    kbar[t] = m;
+    const uint16_t hi = f32_to_bf16(m);
+    kbar16[t] = hi;
+    kbarlo[t] = f32_to_bf16(m - bf16_to_f32(hi));   // the difference is exact in fp32
+  }
+  amax = block_max(amax, fred);
+  {
+    const float inv = inv448(amax);
+    if (t == 0) *sk = scale448(amax);
+#pragma unroll
+    for (int i = 0; i < BL::RPT; i++) {
+      const int r = r0 + i * BL::RT;
+      if (r >= BK) break;
+      int w0 = 0, w1 = 0;
+      w0 = cvt_fp8x2<false>(bl.vals[i][0] * inv, bl.vals[i][1] * inv, w0);
+      w0 = cvt_fp8x2<true>(bl.vals[i][2] * inv, bl.vals[i][3] * inv, w0);
+      w1 = cvt_fp8x2<false>(bl.vals[i][4] * inv, bl.vals[i][5] * inv, w1);
+      w1 = cvt_fp8x2<true>(bl.vals[i][6] * inv, bl.vals[i][7] * inv, w1);
+      // 8 consecutive d of one chunk land contiguously at k8_pos(8c)
+      *reinterpret_cast<uint2*>(k8 + r * D + k8_pos(c * 8)) = make_uint2(w0, w1);
+    }
+  }
+
+  // ---- V: means, scale, transposed codes and transposed bf16 values
+  load_block<D, BK>(a.v + off, dm.sn, rows, bl, red, colsum, amax);
+  if (t < D) {
+    const float m = static_cast<float>(colsum / static_cast<double>(rows));
+    vbar[t] = m;
+    vbar16[t] = f32_to_f16(m);
+  }
+#pragma unroll
+  for (int i = 0; i < BL::RPT; i++) {
+    const int r = r0 + i * BL::RT;
+    if (r >= BK) break;
+#pragma unroll
+    for (int e = 0; e < 8; e++) tileT[r * D + c * 8 + e] = f32_to_bf16(bl.vals[i][e]);  // exact: inputs are bf16
+  }
+  amax = block_max(amax, fred);   // contains the barrier that publishes tileT
+  const float inv = inv448(amax);
+  if (t == 0) *sv = scale448(amax);
+  // vt (fp16): D rows of 64 keys (128 bytes) = 8 chunks of 8 elements; element e of
+  // row d holds key with vt_pos(key) == e.
+  for (int u = t; u < D * 8; u += kThreads) {
+    const int d = u >> 3, q = u & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; e2++) {
+      uint32_t lohi[2];
+#pragma unroll
+      for (int z = 0; z < 2; z++) {
+        const int e = q * 8 + e2 * 2 + z;           // element index in the row
+        // invert vt_pos: e = (2(p/8) + hh)*8 + p%8
+        const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
+        const int key = 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
+        // bf16 -> fp16 is exact for |v| in [2^-14, 65504]; smaller values round
+        lohi[z] = f32_to_f16(bf16_to_f32(tileT[key * D + d]));
+      }
+      w[e2] = lohi[0] | (lohi[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(vt + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  // vlow: same layout as vt; element = fl16(fl32(decode(code)) * sv) of the E4M3 code
+  // of v * inv (the hardware converter decodes exactly).
+  const float svf = scale448(amax);
+  for (int u = t; u < D * 8; u += kThreads) {
+    const int d = u >> 3, q = u & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; e2++) {
+      float f[2];
+#pragma unroll
+      for (int z = 0; z < 2; z++) {
+        const int e = q * 8 + e2 * 2 + z;
+        const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
+        const int key = 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
+        f[z] = bf16_to_f32(tileT[key * D + d]) * inv;
+      }
+      const int code2 = cvt_fp8x2<false>(f[0], f[1], 0);
+      const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8(code2, false);
+      // Round the product to fp32 first, then to fp16: the empty asm keeps the
+      // compiler from fusing both roundings into one mixed-precision FMA.
+      float p0 = dec.x * svf, p1 = dec.y * svf;
+      __asm__("" : "+v"(p0), "+v"(p1));
+      w[e2] = uint32_t(f32_to_f16(p0)) | (uint32_t(f32_to_f16(p1)) << 16);
+    }
+    *reinterpret_cast<uint4*>(vlow + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int D, int BQ>
+__global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
+  using BL = BlockLoad<D, BQ>;
+  __shared__ double red[BL::RT * D];
+  __shared__ float fred[kThreads / 64];
+  const Dims& dm = a.d;
+  const int bh = blockIdx.x / dm.Nq, I = blockIdx.x % dm.Nq;
+  const int b = bh / dm.H, h = bh % dm.H;
+  const int rows = min(BQ, dm.N - I * BQ);
+  const int64_t off = (int64_t)b * dm.sb + (int64_t)h * dm.sh + (int64_t)I * BQ * dm.sn;
+  unsigned char* ws = a.ws;
+  float* qbar = reinterpret_cast<float*>(ws + a.L.qbar) + ((int64_t)bh * dm.Nq + I) * D;
+  BL bl;
+  double colsum;
+  float amax;
+  load_block<D, BQ>(a.q + off, dm.sn, rows, bl, red, colsum, amax);
+  if (threadIdx.x < D) qbar[threadIdx.x] = static_cast<float>(colsum / static_cast<double>(rows));
+  amax = block_max(amax, fred);
+  if (threadIdx.x == 0) {
+    reinterpret_cast<float*>(ws + a.L.sq)[(int64_t)bh * dm.Nq + I] = scale448(amax);
+    reinterpret_cast<float*>(ws + a.L.iq)[(int64_t)bh * dm.Nq + I] = inv448(amax);
+  }
+}
+
+template <int D>
+hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
+  const Dims& d = a.d;
+  hipLaunchKernelGGL((k1_kv<D, 64>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d.Bq == 128)
+    hipLaunchKernelGGL((k1_q<D, 128>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_q<D, 64>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
+  return a.d.D == 128 ? launch_pool_d<128>(a, s) : launch_pool_d<64>(a, s);
+}
+
+}  // namespace tattn

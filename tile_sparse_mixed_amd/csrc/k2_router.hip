@@ -1,0 +1,365 @@
+// K2: block router, tier assignment and tile-list compaction.
+//
+// K2a  S_IJ = <qbar_I, kbar_J> / sqrt(d) + ln n_J in float64, tiled 32 query
+//      blocks x 64 key blocks per workgroup through LDS ("APT": attention
+//      probability of the block as the importance metric; the ln n_J term
+//      weights a key block by its real size).
+// K2b  per query block I: p_IJ = softmax_J(S_IJ) (float64), then the tier map:
+//        THRESHOLD  FULL if p >= tau_hi, LOW if p >= tau_lo, else SKIP, after an
+//                   optional top-k by (p desc, J asc) ("APT": dual thresholds;
+//                   "HierPAS": top-k),
+//        ADAPTIVE   k_h from the entropy of p on sampled rows (K2e), then the top
+//                   ceil(full_frac*k_h) tiles FULL, the rest of the top k_h LOW
+//                   ("HierPAS": sampling-based entropy, head-wise retention),
+//        ALL_FULL   every tile FULL;
+//      diagonal tiles forced FULL; then a stable compaction into
+//      [FULL asc | LOW asc | SKIP asc] with wavefront ballots.
+// K2c  compaction only, for a tier map supplied by the caller.
+// Ranks and cuts use exact comparisons of the float64 p values.
+#include "tattn_device.hpp"
+#include "tattn_internal.hpp"
+
+namespace tattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRouterMaxNk = 4096;
+
+// ------------------------------------------------------------------ K2a
+template <int D>
+__global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
+  __shared__ float qT[D][32];   // qbar transposed [d][row]
+  __shared__ float kT[D][64];   // kbar transposed [d][J]
+  const Dims& dm = a.d;
+  const int bh = blockIdx.z;
+  const int I0 = blockIdx.y * 32, J0 = blockIdx.x * 64;
+  const float* qbar = reinterpret_cast<const float*>(a.ws + a.L.qbar) + (int64_t)bh * dm.Nq * D;
+  const float* kbar = reinterpret_cast<const float*>(a.ws + a.L.kbar) + (int64_t)bh * dm.Nk * D;
+  const int t = threadIdx.x;
+  for (int u = t; u < 32 * D; u += kThreads) {
+    const int r = u / D, c = u % D;
+    qT[c][r] = (I0 + r < dm.Nq) ? qbar[(int64_t)(I0 + r) * D + c] : 0.0f;
+  }
+  for (int u = t; u < 64 * D; u += kThreads) {
+    const int r = u / D, c = u % D;
+    kT[c][r] = (J0 + r < dm.Nk) ? kbar[(int64_t)(J0 + r) * D + c] : 0.0f;
+  }
+  __syncthreads();
+  const int rg = t / 16, jg = t % 16;   // rows 2rg, 2rg+1; key blocks 4jg..4jg+3
+  double acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < D; c++) {
+    const float2 qv = *reinterpret_cast<const float2*>(&qT[c][2 * rg]);
+    const float4 kv = *reinterpret_cast<const float4*>(&kT[c][4 * jg]);
+    const double q0 = qv.x, q1 = qv.y;
+    const double k[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      acc[0][j] = fma(q0, k[j], acc[0][j]);
+      acc[1][j] = fma(q1, k[j], acc[1][j]);
+    }
+  }
+  double* S = reinterpret_cast<double*>(a.ws + a.L.S) + (int64_t)bh * dm.Nq * dm.Nk;
+  const double sd = sqrt(static_cast<double>(D));
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int I = I0 + 2 * rg + i;
+    if (I >= dm.Nq) continue;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int J = J0 + 4 * jg + j;
+      if (J >= dm.Nk) continue;
+      const int nJ = min(dm.Bk, dm.N - J * dm.Bk);
+      S[(int64_t)I * dm.Nk + J] = acc[i][j] / sd + log(static_cast<double>(nJ));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ block reductions
+struct Red {
+  double d[kWaves];
+  int i[kWaves * 4];
+};
+
+__device__ double block_max_d(double v, Red& r) {
+  v = wave_max_d(v);
+  if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double m = r.d[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; w++) m = fmax(m, r.d[w]);
+  __syncthreads();
+  return m;
+}
+__device__ double block_sum_d(double v, Red& r) {
+  v = wave_sum_d(v);
+  if ((threadIdx.x & 63) == 0) r.d[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = r.d[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; w++) s += r.d[w];
+  __syncthreads();
+  return s;
+}
+__device__ int block_sum_i(int v, Red& r) {
+  v = wave_sum_i(v);
+  if ((threadIdx.x & 63) == 0) r.i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; w++) s += r.i[w];
+  __syncthreads();
+  return s;
+}
+
+// Bits of the k-th largest value (k >= 1) among the non-negative doubles
+// pv[0..n): the largest x with #{p >= x} >= k, built from the top bit down.
+__device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
+  uint64_t prefix = 0;
+  for (int bit = 62; bit >= 0; bit--) {
+    const uint64_t cand = prefix | (1ull << bit);
+    int c = 0;
+    for (int J = threadIdx.x; J < n; J += kThreads) c += (__double_as_longlong(pv[J]) >= (long long)cand);
+    if (block_sum_i(c, r) >= k) prefix = cand;
+  }
+  return prefix;
+}
+
+// rank(J) < k  <=>  p_J > x_k  or  (p_J == x_k and J is among the first `need`
+// tiles equal to x_k in ascending J), need = k - #{p > x_k}.  Marks such
+// tiles in `keep` (1) and the rest 0.
+__device__ void mark_top_k(const double* pv, int n, int k, unsigned char* keep, Red& r) {
+  if (k >= n) {
+    for (int J = threadIdx.x; J < n; J += kThreads) keep[J] = 1;
+    __syncthreads();
+    return;
+  }
+  if (k <= 0) {
+    for (int J = threadIdx.x; J < n; J += kThreads) keep[J] = 0;
+    __syncthreads();
+    return;
+  }
+  const uint64_t xb = kth_largest_bits(pv, n, k, r);
+  int gt = 0;
+  for (int J = threadIdx.x; J < n; J += kThreads) gt += ((uint64_t)__double_as_longlong(pv[J]) > xb);
+  const int need = k - block_sum_i(gt, r);
+  int base = 0;   // equal-to-x tiles already seen in earlier chunks
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int J0 = 0; J0 < n; J0 += kThreads) {
+    const int J = J0 + threadIdx.x;
+    const uint64_t b = J < n ? (uint64_t)__double_as_longlong(pv[J]) : 0;
+    const bool eq = J < n && b == xb;
+    const uint64_t bal = __ballot(eq);
+    const int pre = __popcll(bal & ((1ull << lane) - 1));
+    if (lane == 0) r.i[w] = __popcll(bal);
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ww++) {
+      if (ww < w) woff += r.i[ww];
+      tot += r.i[ww];
+    }
+    if (J < n) keep[J] = (b > xb) || (eq && base + woff + pre < need);
+    base += tot;
+    __syncthreads();
+  }
+}
+
+// Diagonal tiles of query block I: key blocks whose token range meets I's.
+__device__ inline void diag_range(const Dims& dm, int I, int& j0, int& j1) {
+  const int r0 = I * dm.Bq, r1 = min(dm.N, (I + 1) * dm.Bq);
+  j0 = r0 / dm.Bk;
+  j1 = (r1 - 1) / dm.Bk;
+}
+
+// Stable compaction of the tier row `tr` (in LDS) into lists/counts.
+__device__ void compact_row(const unsigned char* tr, int n, int16_t* list, int* counts, Red& r) {
+  int c[3] = {0, 0, 0};
+  for (int J = threadIdx.x; J < n; J += kThreads) c[tr[J]]++;
+  const int nF = block_sum_i(c[2], r), nL = block_sum_i(c[1], r), nS = block_sum_i(c[0], r);
+  if (threadIdx.x == 0) {
+    counts[0] = nF;
+    counts[1] = nL;
+    counts[2] = nS;
+    counts[3] = 0;
+  }
+  int base[3] = {nF + nL, nF, 0};   // indexed by tier value: SKIP, LOW, FULL
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int J0 = 0; J0 < n; J0 += kThreads) {
+    const int J = J0 + threadIdx.x;
+    const int tv = J < n ? tr[J] : -1;
+    int pre = 0;
+#pragma unroll
+    for (int T = 0; T < 3; T++) {
+      const uint64_t bal = __ballot(tv == T);
+      if (tv == T) pre = __popcll(bal & ((1ull << lane) - 1));
+      if (lane == 0) r.i[w * 4 + T] = __popcll(bal);
+    }
+    __syncthreads();
+    int woff[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ww++)
+#pragma unroll
+      for (int T = 0; T < 3; T++) {
+        if (ww < w) woff[T] += r.i[ww * 4 + T];
+        tot[T] += r.i[ww * 4 + T];
+      }
+    if (tv >= 0) list[base[tv] + woff[tv] + pre] = static_cast<int16_t>(J);
+#pragma unroll
+    for (int T = 0; T < 3; T++) base[T] += tot[T];
+    __syncthreads();
+  }
+}
+
+enum { K2B_TIERS = 0, K2B_ENTROPY = 1 };
+
+// One workgroup per (b, h, I) (tiers) or per (b, h, sampled row s) (entropy).
+template <int WHAT>
+__global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
+  __shared__ double pv[kRouterMaxNk];
+  __shared__ unsigned char tr[kRouterMaxNk];
+  __shared__ unsigned char keep[kRouterMaxNk];
+  __shared__ Red r;
+  const Dims& dm = a.d;
+  const int n = dm.Nk;
+  int bh, I, s = 0;
+  if (WHAT == K2B_ENTROPY) {
+    const int S = min(a.samples, dm.Nq);
+    bh = blockIdx.x / S;
+    s = blockIdx.x % S;
+    I = (int)(((int64_t)s * dm.Nq) / S);
+  } else {
+    bh = blockIdx.x / dm.Nq;
+    I = blockIdx.x % dm.Nq;
+  }
+  const int64_t row = (int64_t)bh * dm.Nq + I;
+  const double* S = reinterpret_cast<const double*>(a.ws + a.L.S) + row * n;
+  if (a.mode != TATTN_MODE_ALL_FULL) {
+    double mx = -INFINITY;
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      pv[J] = S[J];
+      mx = fmax(mx, pv[J]);
+    }
+    mx = block_max_d(mx, r);
+    double sum = 0.0;
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      const double e = exp(pv[J] - mx);
+      pv[J] = e;
+      sum += e;
+    }
+    sum = block_sum_d(sum, r);
+    for (int J = threadIdx.x; J < n; J += kThreads) pv[J] = pv[J] / sum;
+    __syncthreads();
+  }
+  if (WHAT == K2B_ENTROPY) {
+    double hsum = 0.0;
+    for (int J = threadIdx.x; J < n; J += kThreads) hsum += pv[J] > 0.0 ? pv[J] * log(pv[J]) : 0.0;
+    hsum = block_sum_d(hsum, r);
+    if (threadIdx.x == 0) reinterpret_cast<double*>(a.ws + a.L.ent)[(int64_t)bh * min(a.samples, dm.Nq) + s] = -hsum;
+    return;
+  }
+  float* pout = reinterpret_cast<float*>(a.ws + a.L.p) + row * n;
+  unsigned char* tout = a.ws + a.L.tiers + row * n;
+  if (a.mode == TATTN_MODE_ALL_FULL) {
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      tr[J] = TATTN_FULL;
+      pout[J] = 0.0f;
+    }
+  } else if (a.mode == TATTN_MODE_THRESHOLD) {
+    const double th = a.tau_hi, tl = a.tau_lo;
+    if (a.top_k > 0) mark_top_k(pv, n, a.top_k, keep, r);
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      const double p = pv[J];
+      unsigned char t = p >= th ? TATTN_FULL : (p >= tl ? TATTN_LOW : TATTN_SKIP);
+      if (a.top_k > 0 && !keep[J]) t = TATTN_SKIP;
+      tr[J] = t;
+      pout[J] = static_cast<float>(p);
+    }
+  } else {  // ADAPTIVE
+    const int S2 = min(a.samples, dm.Nq);
+    const double* ent = reinterpret_cast<const double*>(a.ws + a.L.ent) + (int64_t)bh * S2;
+    double hs = 0.0;
+    for (int i = 0; i < S2; i++) hs += ent[i];   // same order in every workgroup of this head
+    double rr = exp(hs / S2) / n;
+    rr = fmin(fmax(rr, (double)a.keep_min), (double)a.keep_max);
+    const int kh = (int)ceil(rr * n);
+    const int nfull = (int)ceil((double)a.full_frac * kh);
+    if (I == 0 && threadIdx.x == 0) {
+      reinterpret_cast<int*>(a.ws + a.L.kh)[bh] = kh;
+      reinterpret_cast<double*>(a.ws + a.L.rh)[bh] = rr;
+    }
+    mark_top_k(pv, n, kh, keep, r);
+    for (int J = threadIdx.x; J < n; J += kThreads) tr[J] = keep[J] ? TATTN_LOW : TATTN_SKIP;
+    __syncthreads();
+    mark_top_k(pv, n, nfull, keep, r);
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      if (keep[J]) tr[J] = TATTN_FULL;
+      pout[J] = static_cast<float>(pv[J]);
+    }
+  }
+  __syncthreads();
+  int j0, j1;
+  diag_range(dm, I, j0, j1);
+  for (int J = j0 + threadIdx.x; J <= j1; J += kThreads) tr[J] = TATTN_FULL;
+  __syncthreads();
+  for (int J = threadIdx.x; J < n; J += kThreads) tout[J] = tr[J];
+  compact_row(tr, n, reinterpret_cast<int16_t*>(a.ws + a.L.lists) + row * n,
+              reinterpret_cast<int*>(a.ws + a.L.counts) + row * 4, r);
+}
+
+__global__ __launch_bounds__(kThreads) void k2c_compact(RouterArgs a) {
+  __shared__ unsigned char tr[kRouterMaxNk];
+  __shared__ Red r;
+  const Dims& dm = a.d;
+  const int n = dm.Nk;
+  const int bh = blockIdx.x / dm.Nq, I = blockIdx.x % dm.Nq;
+  const int64_t row = (int64_t)bh * dm.Nq + I;
+  unsigned char* tg = a.ws + a.L.tiers + row * n;
+  for (int J = threadIdx.x; J < n; J += kThreads) tr[J] = tg[J];
+  __syncthreads();
+  int j0, j1;
+  diag_range(dm, I, j0, j1);
+  for (int J = j0 + threadIdx.x; J <= j1; J += kThreads) tr[J] = TATTN_FULL;
+  __syncthreads();
+  for (int J = threadIdx.x; J < n; J += kThreads) tg[J] = tr[J];
+  compact_row(tr, n, reinterpret_cast<int16_t*>(a.ws + a.L.lists) + row * n,
+              reinterpret_cast<int*>(a.ws + a.L.counts) + row * 4, r);
+}
+
+}  // namespace
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
+  const Dims& d = a.d;
+  if (d.Nk > kRouterMaxNk) return hipErrorInvalidValue;
+  if (a.mode != TATTN_MODE_ALL_FULL) {
+    dim3 grid((d.Nk + 63) / 64, (d.Nq + 31) / 32, d.BH);
+    if (d.D == 128)
+      hipLaunchKernelGGL((k2a_scores<128>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k2a_scores<64>), grid, dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.mode == TATTN_MODE_ADAPTIVE) {
+    const int S = min(a.samples, d.Nq);
+    hipLaunchKernelGGL((k2b_rows<K2B_ENTROPY>), dim3(d.BH * S), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k2b_rows<K2B_TIERS>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const RouterArgs& a, hipStream_t s) {
+  const Dims& d = a.d;
+  if (d.Nk > kRouterMaxNk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k2c_compact, dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tattn

@@ -1,0 +1,104 @@
+// Device-side helpers shared by the tattn kernels (gfx950 / CDNA4).
+//
+// Operand layouts of the matrix instructions used here (wave64):
+//   v_mfma_f32_32x32x16_bf16: lane l holds A[m = l%32][k = (l/32)*8 + t] and
+//     B[k = (l/32)*8 + t][n = l%32], t = 0..7; result register r of lane l is
+//     D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32], r = 0..15.
+//   v_mfma_f32_32x32x16_f16 has the same layout with fp16 operands.
+//   v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3): lane l holds 32 bytes of row
+//     m = l%32 of A and of column n = l%32 of B in the same k positions
+//     (group l/32, byte p); the result layout is the one above.
+// The kernels compute S^T = K Q^T so that each lane owns one query column and
+// softmax statistics stay inside a lane pair (l, l^32).  The contraction over
+// keys in P.V pairs the P values a lane already holds with V stored
+// transposed and key-permuted to match (see kperm_* below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2_448 = 8.807354922057604f;
+
+// ---------------------------------------------------------------------------
+// Key permutation inside a 64-key tile.  In the S^T result of two 32x32
+// blocks (keys 32b..32b+31), lane half h holds register r of block b for key
+//   key(b, r, h) = 32b + 8(r/4) + 4h + r%4,
+// i.e. P value number p = 16b + r of that lane.  The P.V contraction uses the
+// lane's own P values as the B operand, so V must be stored with the same key
+// order:
+//   fp8  (K = 64 per instruction): byte 32h + p of a transposed V row.
+//   bf16 (K = 16 per instruction, chunk c = p/8): element (2c + h)*8 + p%8.
+__host__ __device__ inline int key_p(int key) {  // P index inside its lane half
+  return 16 * (key >> 5) + 4 * ((key >> 3) & 3) + (key & 3);
+}
+__host__ __device__ inline int key_h(int key) { return (key >> 2) & 1; }
+__host__ __device__ inline int v8_pos(int key) { return 32 * key_h(key) + key_p(key); }
+__host__ __device__ inline int vt_pos(int key) {
+  const int p = key_p(key);
+  return (2 * (p >> 3) + key_h(key)) * 8 + (p & 7);
+}
+
+// d permutation of a stored fp8 K row: byte position 64i + 32g + p holds
+// d = 64i + 16(p/8) + 8g + p%8, so that a lane (group g) reads its 32 bytes
+// for instruction i contiguously, in the order its bf16 Q registers give.
+__host__ __device__ inline int k8_pos(int d) {
+  const int i = d >> 6, dd = d & 63;
+  const int g = (dd >> 3) & 1;
+  const int p = 8 * (dd >> 4) + (dd & 7);
+  return 64 * i + 32 * g + p;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 (OCP) conversion: round to nearest even on the hardware converter.
+// The converter does not saturate above 464, so values are clamped first.
+template <bool HI>
+__device__ inline int cvt_fp8x2(float a, float b, int old) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+// Same, for values already known to lie in [0, 448 * (1 + 2^-20)].
+template <bool HI>
+__device__ inline int cvt_fp8x2_nosat(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+__device__ inline uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+__device__ inline uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (wave64).
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline double wave_max_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace tattn

@@ -1,0 +1,411 @@
+// Host runtime of the tattn C ABI: validation (pure host), workspace layout,
+// launch sequencing on the caller's stream and HIP-error -> status mapping.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tattn.h"
+#include "tattn_device.hpp"
+#include "tattn_internal.hpp"
+
+namespace tattn {
+
+static thread_local std::string g_err;
+
+static tattn_status fail(tattn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static tattn_status fail(tattn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+static tattn_status ok() {
+  g_err.clear();
+  return TATTN_OK;
+}
+static tattn_status hip_fail(hipError_t e, const char* what) {
+  return fail(TATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+Dims make_dims(const tattn_config& c) {
+  Dims d;
+  d.B = c.batch;
+  d.H = c.heads;
+  d.BH = c.batch * c.heads;
+  d.N = c.seq_len;
+  d.D = c.head_dim;
+  d.Bq = c.block_q;
+  d.Bk = c.block_k;
+  d.Nq = (c.seq_len + c.block_q - 1) / c.block_q;
+  d.Nk = (c.seq_len + c.block_k - 1) / c.block_k;
+  d.sb = c.stride_b;
+  d.sh = c.stride_h;
+  d.sn = c.stride_n;
+  return d;
+}
+
+Layout make_layout(const Dims& d, int entropy_samples) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + kAlign - 1) / kAlign * kAlign;
+    return at;
+  };
+  const size_t BH = d.BH, Nq = d.Nq, Nk = d.Nk, D = d.D, Bk = d.Bk;
+  const size_t S = std::max(1, std::min(entropy_samples, d.Nq));
+  L.qbar = take(BH * Nq * D * 4);
+  L.kbar = take(BH * Nk * D * 4);
+  L.vbar = take(BH * Nk * D * 4);
+  L.kbar16 = take(BH * Nk * D * 2);
+  L.kbarlo = take(BH * Nk * D * 2);
+  L.vbar16 = take(BH * Nk * D * 2);
+  L.sq = take(BH * Nq * 4);
+  L.iq = take(BH * Nq * 4);
+  L.sk = take(BH * Nk * 4);
+  L.sv = take(BH * Nk * 4);
+  L.k8 = take(BH * Nk * Bk * D);
+  L.vlow = take(BH * Nk * Bk * D * 2);
+  L.vt = take(BH * Nk * Bk * D * 2);
+  L.S = take(BH * Nq * Nk * 8);
+  L.p = take(BH * Nq * Nk * 4);
+  L.tiers = take(BH * Nq * Nk);
+  L.lists = take(BH * Nq * Nk * 2);
+  L.counts = take(BH * Nq * 4 * 4);
+  L.ent = take(BH * S * 8);
+  L.kh = take(BH * 4);
+  L.rh = take(BH * 8);
+  L.flag = take(16);
+  L.total = off;
+  return L;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static tattn_status validate(const tattn_config* c) {
+  if (!c) return fail(TATTN_E_INVALID, "config is NULL");
+  if (c->batch < 1 || c->heads < 1 || c->seq_len < 1)
+    return fail(TATTN_E_INVALID, "batch, heads and seq_len must be >= 1 (got %d, %d, %d)", c->batch, c->heads,
+                c->seq_len);
+  if (c->head_dim < 1 || c->block_q < 1 || c->block_k < 1)
+    return fail(TATTN_E_INVALID, "head_dim, block_q and block_k must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(TATTN_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (c->block_k != kTile || (c->block_q != 64 && c->block_q != 128))
+    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported ((64,64) or (128,64))", c->block_q, c->block_k);
+  if (c->mode < 0 || c->mode > 3) return fail(TATTN_E_INVALID, "mode %d out of range", c->mode);
+  if (!std::isfinite(c->tau_hi) || !std::isfinite(c->tau_lo) || c->tau_lo < 0.0f || c->tau_lo > c->tau_hi)
+    return fail(TATTN_E_INVALID, "thresholds need 0 <= tau_lo <= tau_hi (got %g, %g)", c->tau_lo, c->tau_hi);
+  const int64_t nq = (c->seq_len + (int64_t)c->block_q - 1) / c->block_q;
+  const int64_t nk = (c->seq_len + (int64_t)c->block_k - 1) / c->block_k;
+  if (c->top_k < 0 || c->top_k > nk) return fail(TATTN_E_INVALID, "top_k %d outside [0, %lld]", c->top_k, (long long)nk);
+  if (c->mode == TATTN_MODE_ADAPTIVE) {
+    if (!(c->keep_min > 0.0f) || !(c->keep_max >= c->keep_min) || !(c->keep_max <= 1.0f))
+      return fail(TATTN_E_INVALID, "adaptive mode needs 0 < keep_min <= keep_max <= 1");
+    if (!(c->full_frac > 0.0f) || !(c->full_frac <= 1.0f))
+      return fail(TATTN_E_INVALID, "adaptive mode needs 0 < full_frac <= 1");
+    if (c->entropy_samples < 1) return fail(TATTN_E_INVALID, "entropy_samples must be >= 1");
+  }
+  if (c->in_dtype != TATTN_BF16) {
+    if (c->in_dtype == TATTN_FP32) return fail(TATTN_E_UNSUPPORTED, "fp32 inputs are not supported (bf16 only)");
+    return fail(TATTN_E_INVALID, "in_dtype %d unknown", c->in_dtype);
+  }
+  if (c->out_dtype != TATTN_BF16 && c->out_dtype != TATTN_FP32)
+    return fail(TATTN_E_INVALID, "out_dtype %d unknown", c->out_dtype);
+  if (c->stride_n < c->head_dim || c->stride_h < 1 || c->stride_b < 1)
+    return fail(TATTN_E_INVALID, "strides must be positive with stride_n >= head_dim");
+  if ((c->stride_n % 8) || (c->stride_h % 8) || (c->stride_b % 8))
+    return fail(TATTN_E_INVALID, "strides must be multiples of 8 elements (16-byte rows)");
+  if (nk > kMaxNk / 2) return fail(TATTN_E_UNSUPPORTED, "%lld key blocks exceed the router limit of 4096", (long long)nk);
+  if ((int64_t)c->batch * c->heads * nq > 0x7fffffffLL || (int64_t)c->batch * c->heads * nk > 0x7fffffffLL)
+    return fail(TATTN_E_UNSUPPORTED, "problem too large for one launch");
+  return ok();
+}
+
+}  // namespace tattn
+
+using namespace tattn;
+
+struct tattn_plan_s {
+  tattn_config cfg;
+  Dims d;
+  Layout L;
+  unsigned char* ws;
+  const void* k;
+  const void* v;
+  bool has_tiers;
+};
+
+extern "C" {
+
+tattn_status tattn_validate(const tattn_config* cfg) { return validate(cfg); }
+
+tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes) {
+  tattn_status st = validate(cfg);
+  if (st != TATTN_OK) return st;
+  if (!bytes) return fail(TATTN_E_INVALID, "bytes is NULL");
+  *bytes = make_layout(make_dims(*cfg), cfg->entropy_samples).total;
+  return ok();
+}
+
+static RouterArgs router_args(const tattn_plan_s* p) {
+  RouterArgs r;
+  r.ws = p->ws;
+  r.L = p->L;
+  r.d = p->d;
+  r.mode = p->cfg.mode;
+  r.tau_hi = p->cfg.tau_hi;
+  r.tau_lo = p->cfg.tau_lo;
+  r.top_k = p->cfg.top_k;
+  r.keep_min = p->cfg.keep_min;
+  r.keep_max = p->cfg.keep_max;
+  r.full_frac = p->cfg.full_frac;
+  r.samples = std::max(1, p->cfg.entropy_samples);
+  return r;
+}
+
+tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, const void* v, void* workspace,
+                        size_t workspace_bytes, void* stream, tattn_plan_t* out) {
+  tattn_status st = validate(cfg);
+  if (st != TATTN_OK) return st;
+  if (!out) return fail(TATTN_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!q || !k || !v) return fail(TATTN_E_INVALID, "q, k and v must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
+  const Dims d = make_dims(*cfg);
+  const Layout L = make_layout(d, cfg->entropy_samples);
+  if (!workspace) return fail(TATTN_E_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(TATTN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  tattn_plan_s* p = new (std::nothrow) tattn_plan_s;
+  if (!p) return fail(TATTN_E_INVALID, "out of host memory");
+  p->cfg = *cfg;
+  p->d = d;
+  p->L = L;
+  p->ws = static_cast<unsigned char*>(workspace);
+  p->k = k;
+  p->v = v;
+  p->has_tiers = cfg->mode != TATTN_MODE_EXTERNAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+              p->ws, L, d};
+  hipError_t e = launch_pool(pa, s);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "pool kernel launch");
+  }
+  if (cfg->mode != TATTN_MODE_EXTERNAL) {
+    e = launch_router(router_args(p), s);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "router kernel launch");
+    }
+  }
+  *out = p;
+  return ok();
+}
+
+tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const void* v, void* o, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!q || !o) return fail(TATTN_E_INVALID, "q and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(TATTN_E_INVALID, "q and o must be 16-byte aligned");
+  if (k != p->k || v != p->v) return fail(TATTN_E_STATE, "k and v differ from the tensors the plan was built with");
+  if (!p->has_tiers) return fail(TATTN_E_STATE, "external-mode plan has no tiers yet (call tattn_plan_set_tiers)");
+  AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), o,
+             p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d};
+  hipError_t e = launch_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return ok();
+}
+
+static tattn_status copy_out(void* dst, const unsigned char* src, size_t bytes, hipStream_t s) {
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "device-to-host copy");
+  return TATTN_OK;
+}
+static tattn_status sync(hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  return ok();
+}
+
+tattn_status tattn_plan_set_tiers(tattn_plan_t p, const uint8_t* host_tiers, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (p->cfg.mode != TATTN_MODE_EXTERNAL) return fail(TATTN_E_STATE, "set_tiers needs a plan built in EXTERNAL mode");
+  if (!host_tiers) return fail(TATTN_E_INVALID, "tiers is NULL");
+  const size_t n = (size_t)p->d.BH * p->d.Nq * p->d.Nk;
+  for (size_t i = 0; i < n; i++)
+    if (host_tiers[i] > 2) return fail(TATTN_E_INVALID, "tier byte %u at index %zu is not 0, 1 or 2", host_tiers[i], i);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(p->ws + p->L.tiers, host_tiers, n, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "host-to-device copy");
+  e = launch_compact(router_args(p), s);
+  if (e != hipSuccess) return hip_fail(e, "compaction kernel launch");
+  tattn_status st = sync(s);
+  if (st == TATTN_OK) p->has_tiers = true;
+  return st;
+}
+
+tattn_status tattn_plan_get_tiers(tattn_plan_t p, uint8_t* host_tiers, float* host_p, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!p->has_tiers) return fail(TATTN_E_STATE, "plan has no tiers yet");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)p->d.BH * p->d.Nq * p->d.Nk;
+  tattn_status st;
+  if (host_tiers && (st = copy_out(host_tiers, p->ws + p->L.tiers, n, s)) != TATTN_OK) return st;
+  if (host_p) {
+    if (p->cfg.mode == TATTN_MODE_EXTERNAL || p->cfg.mode == TATTN_MODE_ALL_FULL) {
+      std::memset(host_p, 0, n * 4);
+    } else if ((st = copy_out(host_p, p->ws + p->L.p, n * 4, s)) != TATTN_OK) {
+      return st;
+    }
+  }
+  return sync(s);
+}
+
+tattn_status tattn_plan_get_lists(tattn_plan_t p, int16_t* host_lists, int32_t* host_counts, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!p->has_tiers) return fail(TATTN_E_STATE, "plan has no tiers yet");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t rows = (size_t)p->d.BH * p->d.Nq;
+  tattn_status st;
+  if (host_lists && (st = copy_out(host_lists, p->ws + p->L.lists, rows * p->d.Nk * 2, s)) != TATTN_OK) return st;
+  if (host_counts) {
+    std::vector<int32_t> c4(rows * 4);
+    if ((st = copy_out(c4.data(), p->ws + p->L.counts, rows * 16, s)) != TATTN_OK) return st;
+    if ((st = sync(s)) != TATTN_OK) return st;
+    for (size_t r = 0; r < rows; r++)
+      for (int j = 0; j < 3; j++) host_counts[r * 3 + j] = c4[r * 4 + j];
+  }
+  return sync(s);
+}
+
+tattn_status tattn_plan_get_pool(tattn_plan_t p, float* qbar, float* kbar, float* vbar, float* sq, float* sk, float* sv,
+                                 void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Dims& d = p->d;
+  const size_t BH = d.BH;
+  tattn_status st;
+  if (qbar && (st = copy_out(qbar, p->ws + p->L.qbar, BH * d.Nq * d.D * 4, s)) != TATTN_OK) return st;
+  if (kbar && (st = copy_out(kbar, p->ws + p->L.kbar, BH * d.Nk * d.D * 4, s)) != TATTN_OK) return st;
+  if (vbar && (st = copy_out(vbar, p->ws + p->L.vbar, BH * d.Nk * d.D * 4, s)) != TATTN_OK) return st;
+  if (sq && (st = copy_out(sq, p->ws + p->L.sq, BH * d.Nq * 4, s)) != TATTN_OK) return st;
+  if (sk && (st = copy_out(sk, p->ws + p->L.sk, BH * d.Nk * 4, s)) != TATTN_OK) return st;
+  if (sv && (st = copy_out(sv, p->ws + p->L.sv, BH * d.Nk * 4, s)) != TATTN_OK) return st;
+  return sync(s);
+}
+
+tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* host_vlow, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Dims& d = p->d;
+  const size_t tile = (size_t)kTile * d.D, tiles = (size_t)d.BH * d.Nk;
+  tattn_status st;
+  if (host_k8) {
+    std::vector<uint8_t> buf(tile * tiles);
+    if ((st = copy_out(buf.data(), p->ws + p->L.k8, buf.size(), s)) != TATTN_OK) return st;
+    if ((st = sync(s)) != TATTN_OK) return st;
+    for (size_t bh = 0; bh < (size_t)d.BH; bh++)
+      for (int J = 0; J < d.Nk; J++) {
+        const uint8_t* t = buf.data() + (bh * d.Nk + J) * tile;
+        for (int r = 0; r < kTile && J * kTile + r < d.N; r++) {
+          uint8_t* o = host_k8 + (bh * d.N + J * kTile + r) * d.D;
+          for (int c = 0; c < d.D; c++) o[c] = t[r * d.D + k8_pos(c)];
+        }
+      }
+  }
+  if (host_vlow) {
+    std::vector<uint16_t> buf(tile * tiles);
+    if ((st = copy_out(buf.data(), p->ws + p->L.vlow, buf.size() * 2, s)) != TATTN_OK) return st;
+    if ((st = sync(s)) != TATTN_OK) return st;
+    for (size_t bh = 0; bh < (size_t)d.BH; bh++)
+      for (int J = 0; J < d.Nk; J++) {
+        const uint16_t* t = buf.data() + (bh * d.Nk + J) * tile;
+        for (int r = 0; r < kTile && J * kTile + r < d.N; r++) {
+          uint16_t* o = host_vlow + (bh * d.N + J * kTile + r) * d.D;
+          for (int c = 0; c < d.D; c++) o[c] = t[c * kTile + vt_pos(r)];
+        }
+      }
+  }
+  return ok();
+}
+
+tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!out) return fail(TATTN_E_INVALID, "stats is NULL");
+  if (!p->has_tiers) return fail(TATTN_E_STATE, "plan has no tiers yet");
+  const Dims& d = p->d;
+  std::vector<uint8_t> t((size_t)d.BH * d.Nq * d.Nk);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "device synchronize");
+  e = hipMemcpy(t.data(), p->ws + p->L.tiers, t.size(), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "device-to-host copy");
+  tattn_stats st{};
+  const double D = d.D;
+  for (int bh = 0; bh < d.BH; bh++)
+    for (int I = 0; I < d.Nq; I++) {
+      const double mI = std::min(d.Bq, d.N - I * d.Bq);
+      const int r0 = I * d.Bq, r1 = std::min(d.N, (I + 1) * d.Bq);
+      const int j0 = r0 / d.Bk, j1 = (r1 - 1) / d.Bk;
+      st.n_diag += j1 - j0 + 1;
+      const uint8_t* tr = t.data() + ((size_t)bh * d.Nq + I) * d.Nk;
+      for (int J = 0; J < d.Nk; J++) {
+        const double nJ = std::min(d.Bk, d.N - J * d.Bk);
+        if (tr[J] == TATTN_FULL) {
+          st.n_full++;
+          st.flops_bf16 += 4.0 * mI * nJ * D;
+        } else if (tr[J] == TATTN_LOW) {   // fp8 scores, 16-bit P.V
+          st.n_low++;
+          st.flops_fp8 += 2.0 * mI * nJ * D;
+          st.flops_bf16 += 2.0 * mI * nJ * D;
+        } else {
+          st.n_skip++;
+          st.flops_bf16 += 4.0 * mI * D;
+        }
+      }
+    }
+  st.flops_dense = 4.0 * (double)d.N * d.N * D * d.BH;
+  *out = st;
+  return ok();
+}
+
+tattn_status tattn_plan_get_kh(tattn_plan_t p, int32_t* host_kh, double* host_rh) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (p->cfg.mode != TATTN_MODE_ADAPTIVE) return fail(TATTN_E_STATE, "k_h exists only in ADAPTIVE mode");
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "device synchronize");
+  if (host_kh && (e = hipMemcpy(host_kh, p->ws + p->L.kh, (size_t)p->d.BH * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "device-to-host copy");
+  if (host_rh && (e = hipMemcpy(host_rh, p->ws + p->L.rh, (size_t)p->d.BH * 8, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "device-to-host copy");
+  return ok();
+}
+
+void tattn_plan_destroy(tattn_plan_t p) { delete p; }
+
+const char* tattn_status_str(tattn_status s) {
+  switch (s) {
+    case TATTN_OK: return "ok";
+    case TATTN_E_INVALID: return "invalid argument";
+    case TATTN_E_UNSUPPORTED: return "unsupported configuration";
+    case TATTN_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TATTN_E_HIP: return "HIP runtime error";
+    case TATTN_E_STATE: return "plan in the wrong state";
+  }
+  return "unknown status";
+}
+
+const char* tattn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

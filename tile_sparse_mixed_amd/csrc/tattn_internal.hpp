@@ -1,0 +1,87 @@
+// Internal interfaces of the tattn library: workspace layout and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/tattn.h"
+
+namespace tattn {
+
+constexpr int kTile = 64;          // key-tile width the fused kernel works in
+constexpr int kMaxNk = 8192;       // key blocks per row (int16 lists, router LDS)
+constexpr int kAlign = 256;
+
+// Sizes derived from a validated config.
+struct Dims {
+  int B, H, BH, N, D, Bq, Bk, Nq, Nk;
+  int64_t sb, sh, sn;
+};
+
+// Byte offsets of every region inside the caller's workspace.
+struct Layout {
+  size_t qbar, kbar, vbar;      // f32 [BH][Nq|Nk][D]
+  size_t kbar16, kbarlo;        // bf16 [BH][Nk][D]  K block means as hi + lo bf16 pair (scores of
+                                //                    skipped tiles: kbar = hi + lo to ~2^-17)
+  size_t vbar16;                // fp16 [BH][Nk][D]  block means of V (values of skipped tiles)
+  size_t sq, iq;                // f32 [BH][Nq]   scale and inverse scale of each Q block
+  size_t sk, sv;                // f32 [BH][Nk]
+  size_t k8;                    // u8  [BH][Nk][Bk][D]   d permuted within a row
+  size_t vlow;                  // fp16 [BH][Nk][D][Bk]  low-tier values fl16(decode(E4M3) * sv), transposed
+                                //                        and key-permuted like vt
+  size_t vt;                    // fp16 [BH][Nk][D][Bk]  V^T, keys permuted within a row
+  size_t S;                     // f64 [BH][Nq][Nk]   router logits (scratch)
+  size_t p;                     // f32 [BH][Nq][Nk]
+  size_t tiers;                 // u8  [BH][Nq][Nk]
+  size_t lists;                 // i16 [BH][Nq][Nk]
+  size_t counts;                // i32 [BH][Nq][4]
+  size_t ent;                   // f64 [BH][Ssamp]   entropy of the sampled rows
+  size_t kh;                    // i32 [BH]
+  size_t rh;                    // f64 [BH]
+  size_t flag;                  // i32 [4]   device-side error flags
+  size_t total;
+};
+
+Dims make_dims(const tattn_config& c);
+Layout make_layout(const Dims& d, int entropy_samples);
+
+// ---- launchers (all asynchronous on `s`; return the launch status)
+struct PoolArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  unsigned char* ws;
+  Layout L;
+  Dims d;
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+
+struct RouterArgs {
+  unsigned char* ws;
+  Layout L;
+  Dims d;
+  int mode;
+  float tau_hi, tau_lo;
+  int top_k;
+  float keep_min, keep_max, full_frac;
+  int samples;
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+// Rebuild lists and counts from the tier map already in the workspace
+// (diagonal tiles forced FULL first).
+hipError_t launch_compact(const RouterArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  void* o;
+  int out_fp32;
+  unsigned char* ws;
+  Layout L;
+  Dims d;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+}  // namespace tattn
