@@ -6,7 +6,9 @@
 //                    tile is replaced by its block means),
 //   kbar16, kbarlo   the K means as a bf16 pair hi + lo (hi = bf16(kbar), lo =
 //                    bf16(kbar - hi)), the score operand of skipped tiles,
-//   vbar16           the V means rounded to fp16 (value operand of skipped tiles),
+//   vbarT            the V means rounded to fp16, stored transposed per chunk of 64
+//                    key blocks in vt_pos order (value operand of skipped tiles);
+//                    the last block also zeroes the chunk's columns past Nk,
 //   sk_J, sv_J       amax/448 (1 for an all-zero block),
 //   k8               E4M3 codes of K_J, row-major with k8_pos d order,
 //   vt               V_J as fp16, transposed ([d][key]) in the vt_pos key order
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   float* vbar = reinterpret_cast<float*>(ws + a.L.vbar) + ((int64_t)bh * dm.Nk + J) * D;
   uint16_t* kbar16 = reinterpret_cast<uint16_t*>(ws + a.L.kbar16) + ((int64_t)bh * dm.Nk + J) * D;
   uint16_t* kbarlo = reinterpret_cast<uint16_t*>(ws + a.L.kbarlo) + ((int64_t)bh * dm.Nk + J) * D;
-  uint16_t* vbar16 = reinterpret_cast<uint16_t*>(ws + a.L.vbar16) + ((int64_t)bh * dm.Nk + J) * D;
+  uint16_t* vbarT = reinterpret_cast<uint16_t*>(ws + a.L.vbarT) + ((int64_t)bh * dm.NkC + J / 64) * 64 * D;
   float* sk = reinterpret_cast<float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk + J;
   float* sv = reinterpret_cast<float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk + J;
   unsigned char* k8 = ws + a.L.k8 + ((int64_t)bh * dm.Nk + J) * BK * D;
@@ -153,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   if (t < D) {
     const float m = static_cast<float>(colsum / static_cast<double>(rows));
     vbar[t] = m;
-    vbar16[t] = f32_to_f16(m);
+    vbarT[t * 64 + vt_pos(J & 63)] = f32_to_f16(m);
+    if (J == dm.Nk - 1)   // finite zeros in the chunk's unused columns (they meet P = 0)
+      for (int j = (J & 63) + 1; j < 64; j++) vbarT[t * 64 + vt_pos(j)] = 0;
   }
 #pragma unroll
   for (int i = 0; i < BL::RPT; i++) {

@@ -3,71 +3,80 @@
 // and a tile dataflow; "FG-Attn": dense work only on kept tiles).
 //
 // One workgroup per (b, h, query block I) of BQ = 32 * NW rows; wave w owns
-// rows 32w..32w+31.  The workgroup walks the block's compacted list:
-//   FULL tiles   K (bf16, the caller's tensor) and V^T (fp16 transposed copy,
-//                exact for bf16 values in fp16's normal range): S^T = K Q^T on
-//                v_mfma_f32_32x32x16_bf16, O^T += V^T P^T on the fp16 variant
-//                (P in [0, 2^8] keeps 3 more mantissa bits than bf16 would),
-//   LOW tiles    E4M3 K codes and the fp16 dequantised E4M3 V: S^T on
-//                v_mfma_f32_32x32x64_f8f6f4 from the E4M3 Q and K copies, scaled
-//                by sq*sk; P.V on the fp16 instruction as for FULL tiles,
-//   SKIP chunks  up to 64 skipped key blocks gathered as pseudo-keys kbar_J
-//                (a bf16 hi + lo pair, two MFMAs, so the skipped scores keep
-//                ~2^-17 precision) with a log2(n_J) bias and values vbar_J
-//                (fp16): one score per
-//                skipped block weighted by n_J ("Triage": block means),
-// keeping an online softmax per query row in base 2.  Tiles stream through
-// two LDS stages (register-staged global loads overlap the current tile's
-// math).  S^T puts one query per lane, so row statistics need only the lane
-// pair (l, l^32).
+// rows 32w..32w+31 and computes S^T = K Q^T, so each lane holds one query
+// column and its softmax statistics stay inside the lane pair (l, l^32).
+// The workgroup walks a sequence of 64-key steps:
+//   FULL      a kept tile: K (bf16, the caller's tensor) and V^T (fp16
+//             copy, exact for bf16 values in fp16's normal range); S^T on
+//             v_mfma_f32_32x32x16_bf16, O^T += V^T P^T on the fp16 variant
+//             (P in [0, 2^8] keeps 3 more mantissa bits than bf16 would),
+//   LOW       a low-precision tile: S^T on v_mfma_f32_32x32x64_f8f6f4 from the
+//             E4M3 copies of Q and K scaled by sq*sk; P.V against the fp16
+//             dequantised E4M3 V,
+//   SKIP_S    64 pooled keys kbar_J of one chunk of 64 key blocks, as a bf16
+//             hi + lo pair (two MFMAs: ~2^-17 precision), each scored with a
+//             log2(n_J) bias if J is skipped in this row and -inf otherwise
+//             ("Triage": a skipped tile is one score weighted by n_J),
+//   SKIP_PV   the same chunk's block means vbar_J (fp16, transposed) for P.V.
+// Skipped blocks are visited as whole chunks of 64 (contiguous operands),
+// masked to the row's SKIP set; chunks with no skipped block are not visited.
 //
-// Running state per lane (query row): m (base-2 reference), l (sum of the
-// rounded weights the MFMAs multiply, relative to 2^m) and the O^T
-// accumulator.  m is raised only when a tile's max exceeds it by more than 8
-// (weights stay <= 2^8), so most tiles skip the accumulator rescale.
+// Data movement: every step's operands go global -> LDS with direct
+// global_load_lds_dwordx4 (no staging registers) into one of two stage
+// buffers while the other stage is computed; the XOR swizzle that keeps the
+// MFMA operand reads bank-conflict free is applied by choosing each lane's
+// source address.  A step ends with vmcnt(0) + s_barrier, which publishes the
+// next stage; the plain barrier (no fence) keeps the next DMA in flight.
+//
+// Running state per lane: m (base-2 reference), l (sum of the weights
+// relative to 2^m) and the O^T accumulator.  m is raised only when a tile's
+// max exceeds it by more than 8, so most steps skip the rescale.
 #include "tattn_device.hpp"
 #include "tattn_internal.hpp"
 
 namespace tattn {
 namespace {
 
-constexpr float kLazy = 8.0f;     // raise m only when a tile max exceeds it by this much (log2)
+constexpr float kLazy = 8.0f;   // raise m only when a tile max exceeds it by this much (log2)
 
-template <int D, int NW>
-struct Cfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BQ = NW * 32;
-  static constexpr int KCH = D / 8;               // 16-byte chunks of a bf16 K row
-  static constexpr int STAGE = 384 * D;           // bytes of one LDS stage: K | V^T | K lo (skip chunks)
-  static constexpr int KPT = (64 * KCH) / NT;     // bf16 K chunks per thread
-  static constexpr int VPT = (D * 8) / NT;        // bf16 V^T chunks per thread
-  static constexpr int K8PT = (64 * D / 16) / NT; // fp8 K chunks per thread
-  static constexpr int SREG = 2 * KPT + VPT;      // a skip chunk stages K hi, V and K lo
-  static_assert((64 * KCH) % NT == 0 && (D * 8) % NT == 0, "tile split");
-  static_assert((64 * D / 16) % NT == 0, "fp8 tile split");
-};
+enum StepKind { kFull = 0, kLow = 1, kSkipS = 2, kSkipPV = 3 };
 
-// swizzled byte offsets inside a stage
+typedef __attribute__((address_space(3))) void lds_void;
+
+// vmcnt(0) with expcnt and lgkmcnt unconstrained (gfx9 s_waitcnt encoding).
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One wave: copy 64 lanes x 16 bytes to LDS[dst .. dst+1024), lane l's bytes
+// coming from src (a per-lane global address).
+__device__ inline void dma16(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// Swizzled byte offsets of 16-byte chunk `ch` of a row inside a stage region.
 template <int D>
-__device__ inline int offK(int row, int ch) { return row * (2 * D) + ((ch ^ (row & 7)) << 4); }
-__device__ inline int offV(int d, int ch) { return d * 128 + ((ch ^ (d & 7)) << 4); }
+__device__ inline int offK(int row, int ch) { return row * (2 * D) + ((ch ^ (row & 7)) << 4); }   // [64][D] bf16
+__device__ inline int offV(int d, int ch) { return d * 128 + ((ch ^ (d & 7)) << 4); }               // [D][64] 16-bit
 template <int D>
-__device__ inline int offK8(int row, int ch) {
+__device__ inline int offK8(int row, int ch) {                                                      // [64][D] bytes
   return D == 128 ? row * 128 + ((ch ^ (row & 7)) << 4) : row * 64 + ((ch ^ ((row >> 1) & 3)) << 4);
 }
 
-enum StepKind { kFull = 0, kLow = 1, kSkip = 2 };
-
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void k3_attn(AttnArgs a) {
-  using C = Cfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
-  __shared__ float sbias[2][64];
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
+void k3_attn(AttnArgs a) {
+  constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
+  constexpr int R1 = 128 * D;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+  __shared__ int16_t slist[kMaxNk];          // the row's FULL then LOW key blocks
+  __shared__ unsigned char stier[kMaxNk];    // the row's tier map
+  __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
+  __shared__ int snc;
 
   const Dims& dm = a.d;
-  // ---- XCD-aware work mapping: consecutive workgroups go round-robin over
-  // the 8 XCDs; give each XCD a contiguous range of (b, h, I) so that the
-  // query blocks of a head share that XCD's L2.
+  // ---- XCD-aware work mapping: workgroups are dispatched round-robin over the
+  // 8 XCDs; give each XCD a contiguous range of (b, h, I) so the query blocks
+  // of a head share that XCD's L2.
   const int G = dm.BH * dm.Nq;
   int w_item;
   {
@@ -81,27 +90,44 @@ __global__ __launch_bounds__(NW * 64) void k3_attn(AttnArgs a) {
   const int64_t row = (int64_t)bh * dm.Nq + I;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 31, lh = lane >> 5;   // query column inside the wave, lane half
+  const int ln = lane & 31, lh = lane >> 5;
 
-  unsigned char* ws = a.ws;
+  const unsigned char* ws = a.ws;
   const int* counts = reinterpret_cast<const int*>(ws + a.L.counts) + row * 4;
-  const int nF = counts[0], nL = counts[1], nS = counts[2];
-  const int16_t* list = reinterpret_cast<const int16_t*>(ws + a.L.lists) + row * dm.Nk;
-  const int nSc = (nS + 63) >> 6;
-  const int nSteps = nF + nL + nSc;
+  const int nF = counts[0], nL = counts[1];
+  const int nK = nF + nL;
+  {
+    const int16_t* list = reinterpret_cast<const int16_t*>(ws + a.L.lists) + row * dm.Nk;
+    const unsigned char* tiers = ws + a.L.tiers + row * dm.Nk;
+    for (int i = tid; i < nK; i += NW * 64) slist[i] = list[i];
+    for (int i = tid; i < dm.Nk; i += NW * 64) stier[i] = tiers[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    bool has = false;
+    if (lane < dm.NkC) {
+      const int j1 = min(64 * lane + 64, dm.Nk);
+      for (int j = 64 * lane; j < j1 && !has; j++) has = stier[j] == TATTN_SKIP;
+    }
+    const uint64_t bal = __ballot(has);
+    if (has) schunk[__popcll(bal & ((1ull << lane) - 1))] = static_cast<unsigned char>(lane);
+    if (lane == 0) snc = __popcll(bal);
+  }
+  __syncthreads();
+  const int nSteps = nK + 2 * snc;
 
   const uint16_t* kin = a.k + toff;
-  const uint16_t* vt = reinterpret_cast<const uint16_t*>(ws + a.L.vt) + (int64_t)bh * dm.Nk * 64 * D;  // fp16 bits
+  const uint16_t* vt = reinterpret_cast<const uint16_t*>(ws + a.L.vt) + (int64_t)bh * dm.Nk * 64 * D;
   const unsigned char* k8 = ws + a.L.k8 + (int64_t)bh * dm.Nk * 64 * D;
   const uint16_t* vlow = reinterpret_cast<const uint16_t*>(ws + a.L.vlow) + (int64_t)bh * dm.Nk * 64 * D;
-  const uint16_t* kb16 = reinterpret_cast<const uint16_t*>(ws + a.L.kbar16) + (int64_t)bh * dm.Nk * D;
+  const uint16_t* kbhi = reinterpret_cast<const uint16_t*>(ws + a.L.kbar16) + (int64_t)bh * dm.Nk * D;
   const uint16_t* kblo = reinterpret_cast<const uint16_t*>(ws + a.L.kbarlo) + (int64_t)bh * dm.Nk * D;
-  const uint16_t* vb16 = reinterpret_cast<const uint16_t*>(ws + a.L.vbar16) + (int64_t)bh * dm.Nk * D;
+  const uint16_t* vbT = reinterpret_cast<const uint16_t*>(ws + a.L.vbarT) + (int64_t)bh * dm.NkC * 64 * D;
   const float* skp = reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk;
 
   // ---- Q rows of this wave as bf16 B operands: lane (ln, lh) holds
   // q[row][16c + 8lh .. +8] for chunk c.
-  const int qrow = I * C::BQ + wave * 32 + ln;
+  const int qrow = I * (32 * NW) + wave * 32 + ln;
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; c++) {
@@ -109,7 +135,7 @@ __global__ __launch_bounds__(NW * 64) void k3_attn(AttnArgs a) {
     if (qrow < dm.N) v = *reinterpret_cast<const uint4*>(a.q + toff + (int64_t)qrow * dm.sn + 16 * c + 8 * lh);
     qreg[c] = __builtin_bit_cast(bf16x8, v);
   }
-  // fp8 copy for LOW tiles: 32 bytes per instruction i = chunks 4i..4i+3
+  // E4M3 copy for LOW tiles: 32 bytes per instruction i = bf16 chunks 4i..4i+3
   i32x8 q8reg[D / 64];
   const float sq = reinterpret_cast<const float*>(ws + a.L.sq)[row];
   if (nL > 0) {
@@ -131,111 +157,59 @@ __global__ __launch_bounds__(NW * 64) void k3_attn(AttnArgs a) {
     }
   }
 
-  // ---- staging: global -> registers -> LDS
-  uint4 stg[C::SREG];
-  float bias_stg = -INFINITY;
-
-  auto step_kind = [&](int t) { return t < nF ? kFull : (t < nF + nL ? kLow : kSkip); };
-
-  auto stage_load = [&](int t) {
-    const int kind = step_kind(t);
-    if (kind == kFull) {
-      const int J = list[t];
-      const uint16_t* vtile = vt + (int64_t)J * 64 * D;
-#pragma unroll
-      for (int i = 0; i < C::KPT; i++) {
-        const int u = tid + i * C::NT, r = u / C::KCH, ch = u % C::KCH;
-        const int g = J * 64 + r;
-        stg[i] = g < dm.N ? *reinterpret_cast<const uint4*>(kin + (int64_t)g * dm.sn + ch * 8) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < C::VPT; i++) {
-        const int u = tid + i * C::NT;
-        stg[C::KPT + i] = *reinterpret_cast<const uint4*>(vtile + u * 8);
-      }
-    } else if (kind == kLow) {
-      const int J = list[t];
-      const unsigned char* ktile = k8 + (int64_t)J * 64 * D;
-      const uint16_t* vtile = vlow + (int64_t)J * 64 * D;
-#pragma unroll
-      for (int i = 0; i < C::K8PT; i++) stg[i] = *reinterpret_cast<const uint4*>(ktile + (tid + i * C::NT) * 16);
-#pragma unroll
-      for (int i = 0; i < C::VPT; i++) stg[C::K8PT + i] = *reinterpret_cast<const uint4*>(vtile + (tid + i * C::NT) * 8);
-    } else {
-      const int base = nF + nL + ((t - nF - nL) << 6);
-      const int cnt = min(64, nF + nL + nS - base);
-#pragma unroll
-      for (int i = 0; i < C::KPT; i++) {
-        const int u = tid + i * C::NT, s = u / C::KCH, ch = u % C::KCH;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0), kl = make_uint4(0, 0, 0, 0);
-        if (s < cnt) {
-          const int J = list[base + s];
-          kv = *reinterpret_cast<const uint4*>(kb16 + (int64_t)J * D + ch * 8);
-          vv = *reinterpret_cast<const uint4*>(vb16 + (int64_t)J * D + ch * 8);
-          kl = *reinterpret_cast<const uint4*>(kblo + (int64_t)J * D + ch * 8);
-        }
-        stg[i] = kv;
-        stg[C::KPT + i] = vv;   // KPT == VPT here (both 8D/NT)
-        stg[C::KPT + C::VPT + i] = kl;
-      }
-      if (tid < 64) {
-        bias_stg = -INFINITY;
-        if (tid < cnt) {
-          const int J = list[base + tid];
-          bias_stg = __log2f(static_cast<float>(min(64, dm.N - J * 64)));
-        }
-      }
-    }
+  auto step_kind = [&](int t) {
+    if (t < nF) return (int)kFull;
+    if (t < nK) return (int)kLow;
+    return ((t - nK) & 1) ? (int)kSkipPV : (int)kSkipS;
   };
 
-  auto stage_store = [&](int t, int buf) {
-    unsigned char* st = smem + buf * C::STAGE;
+  // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
+  //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
+  //   LOW     R0 = K8 [64][D] E4M3,      R1 = V low^T [D][64] fp16
+  //   SKIP_S  R0 = kbar hi [64][D] bf16, R1 = kbar lo [64][D] bf16
+  //   SKIP_PV                            R1 = vbar^T [D][64] fp16
+  auto load_rows16 = [&](unsigned char* reg, auto row_ptr) {   // [64][D] 16-bit rows
+    constexpr int CH = D / 8, RPI = 1024 / (2 * D);          // chunks per row, rows per instruction
+#pragma unroll
+    for (int k = wave; k < D / 8; k += NW) {
+      const int r = k * RPI + lane / CH, pos = lane % CH;
+      dma16(row_ptr(r) + 8 * (pos ^ (r & 7)), reg + k * 1024);
+    }
+  };
+  auto load_vt16 = [&](unsigned char* reg, const uint16_t* tile) {   // [D][64] 16-bit rows of 128 B
+#pragma unroll
+    for (int k = wave; k < D / 8; k += NW) {
+      const int r = 8 * k + (lane >> 3), pos = lane & 7;
+      dma16(tile + r * 64 + 8 * (pos ^ (r & 7)), reg + k * 1024);
+    }
+  };
+  auto issue = [&](int t, unsigned char* st) {
     const int kind = step_kind(t);
-    if (kind == kFull || kind == kSkip) {
+    if (kind == kFull) {
+      const int J = slist[t];
+      load_rows16(st, [&](int r) { return kin + (int64_t)min(J * 64 + r, dm.N - 1) * dm.sn; });
+      load_vt16(st + R1, vt + (int64_t)J * 64 * D);
+    } else if (kind == kLow) {
+      const int J = slist[t];
+      const unsigned char* tile = k8 + (int64_t)J * 64 * D;
 #pragma unroll
-      for (int i = 0; i < C::KPT; i++) {
-        const int u = tid + i * C::NT, r = u / C::KCH, ch = u % C::KCH;
-        *reinterpret_cast<uint4*>(st + offK<D>(r, ch)) = stg[i];
+      for (int k = wave; k < D / 16; k += NW) {
+        if (D == 128) {
+          const int r = 8 * k + (lane >> 3), pos = lane & 7;
+          dma16(tile + r * 128 + 16 * (pos ^ (r & 7)), st + k * 1024);
+        } else {
+          const int r = 16 * k + (lane >> 2), pos = lane & 3;
+          dma16(tile + r * 64 + 16 * (pos ^ ((r >> 1) & 3)), st + k * 1024);
+        }
       }
-      unsigned char* sv = st + 128 * D;
-      if (kind == kFull) {
-#pragma unroll
-        for (int i = 0; i < C::VPT; i++) {
-          const int u = tid + i * C::NT, d = u >> 3, ch = u & 7;
-          *reinterpret_cast<uint4*>(sv + offV(d, ch)) = stg[C::KPT + i];
-        }
-      } else {
-        // gathered vbar rows (fp16), written transposed: element (key s, d) -> row d, vt_pos(s)
-#pragma unroll
-        for (int i = 0; i < C::KPT; i++) {
-          const int u = tid + i * C::NT, s = u / C::KCH, ch = u % C::KCH;
-          const int pos = vt_pos(s), q = pos >> 3, e = pos & 7;
-          const uint32_t w4[4] = {stg[C::KPT + i].x, stg[C::KPT + i].y, stg[C::KPT + i].z, stg[C::KPT + i].w};
-#pragma unroll
-          for (int z = 0; z < 8; z++) {
-            const int d = ch * 8 + z;
-            const uint16_t val = static_cast<uint16_t>(z & 1 ? (w4[z >> 1] >> 16) : (w4[z >> 1] & 0xffffu));
-            *reinterpret_cast<uint16_t*>(sv + offV(d, q) + 2 * e) = val;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < C::KPT; i++) {
-          const int u = tid + i * C::NT, r = u / C::KCH, ch = u % C::KCH;
-          *reinterpret_cast<uint4*>(st + 256 * D + offK<D>(r, ch)) = stg[C::KPT + C::VPT + i];
-        }
-        if (tid < 64) sbias[buf][tid] = bias_stg;
-      }
+      load_vt16(st + R1, vlow + (int64_t)J * 64 * D);
     } else {
-#pragma unroll
-      for (int i = 0; i < C::K8PT; i++) {
-        const int u = tid + i * C::NT;
-        const int r = u / (D / 16), ch = u % (D / 16);
-        *reinterpret_cast<uint4*>(st + offK8<D>(r, ch)) = stg[i];
-      }
-#pragma unroll
-      for (int i = 0; i < C::VPT; i++) {
-        const int u = tid + i * C::NT, d = u >> 3, ch = u & 7;
-        *reinterpret_cast<uint4*>(st + 128 * D + offV(d, ch)) = stg[C::K8PT + i];
+      const int c = schunk[(t - nK) >> 1];
+      if (kind == kSkipS) {
+        load_rows16(st, [&](int r) { return kbhi + (int64_t)min(64 * c + r, dm.Nk - 1) * D; });
+        load_rows16(st + R1, [&](int r) { return kblo + (int64_t)min(64 * c + r, dm.Nk - 1) * D; });
+      } else {
+        load_vt16(st + R1, vbT + (int64_t)c * 64 * D);
       }
     }
   };
@@ -245,136 +219,138 @@ __global__ __launch_bounds__(NW * 64) void k3_attn(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
+  f16x8 pb[4];
   const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
 
-  // Raise the reference max of the lanes whose tile max exceeds it by more
-  // than kLazy; rescale their l and accumulator.
-  auto raise_max = [&](float tm) {
-    const bool need = tm > m_run + kLazy;
-    if (__ballot(need)) {
-      const float mn = need ? tm : m_run;
-      const float al = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
-      l_run *= al;
-#pragma unroll
-      for (int db = 0; db < D / 32; db++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[db][r] *= al;
-      m_run = mn;
-    }
-  };
-
-  if (nSteps > 0) {
-    stage_load(0);
-    stage_store(0, 0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < nSteps; t++) {
-    const int buf = t & 1;
-    if (t + 1 < nSteps) stage_load(t + 1);
-    const unsigned char* st = smem + buf * C::STAGE;
+  auto compute = [&](int t, const unsigned char* st) {
     const int kind = step_kind(t);
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-
-    // ---- scores S^T = K Q^T for the 64 keys of the step
-    if (kind == kLow) {
+    if (kind != kSkipPV) {
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      if (kind == kLow) {
 #pragma unroll
-      for (int i = 0; i < D / 64; i++) {
+        for (int i = 0; i < D / 64; i++) {
 #pragma unroll
-        for (int b = 0; b < 2; b++) {
-          const int r = 32 * b + ln;
-          const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
-          const uint4 lo = *reinterpret_cast<const uint4*>(st + offK8<D>(r, ch0));
-          const uint4 hi = *reinterpret_cast<const uint4*>(st + offK8<D>(r, ch0 + 1));
-          const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8reg[i], s[b], 0, 0, 0, 0, 0, 0);
+          for (int b = 0; b < 2; b++) {
+            const int r = 32 * b + ln;
+            const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + offK8<D>(r, ch0));
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + offK8<D>(r, ch0 + 1));
+            const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8reg[i], s[b], 0, 0, 0, 0, 0, 0);
+          }
         }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < D / 16; c++) {
-#pragma unroll
-        for (int b = 0; b < 2; b++) {
-          const int r = 32 * b + ln;
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + offK<D>(r, 2 * c + lh));
-          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[b], 0, 0, 0);
-        }
-      }
-      if (kind == kSkip) {   // low half of the pooled keys
+      } else {
 #pragma unroll
         for (int c = 0; c < D / 16; c++) {
 #pragma unroll
           for (int b = 0; b < 2; b++) {
             const int r = 32 * b + ln;
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + 256 * D + offK<D>(r, 2 * c + lh));
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + offK<D>(r, 2 * c + lh));
             s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[b], 0, 0, 0);
           }
         }
-      }
-    }
-
-    // ---- online softmax: x in base-2 units
-    float x[32];
-    float tmax = -INFINITY;
-    if (kind == kSkip) {
-      const float* bs = sbias[buf];
+        if (kind == kSkipS) {
 #pragma unroll
-      for (int b = 0; b < 2; b++)
+          for (int c = 0; c < D / 16; c++) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float4 bb = *reinterpret_cast<const float4*>(bs + 32 * b + 8 * j + 4 * lh);
-          const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float v = __builtin_fmaf(s[b][4 * j + i], cF, bv[i]);
-            x[16 * b + 4 * j + i] = v;
-            tmax = __builtin_fmaxf(tmax, v);
+            for (int b = 0; b < 2; b++) {
+              const int r = 32 * b + ln;
+              const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + R1 + offK<D>(r, 2 * c + lh));
+              s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[b], 0, 0, 0);
+            }
           }
         }
-    } else {
-      const int J = list[t];
-      const int nvalid = min(64, dm.N - J * 64);
-      const float c = kind == kLow ? sq * skp[J] * cF : cF;
+      }
+      // ---- online softmax in base 2.  Key of register (b, r): 32b + 8(r/4) + 4lh + r%4.
+      float tmax = -INFINITY;
+      float c;
+      if (kind == kSkipS) {
+        // per-key bias: log2(n_J) for the row's skipped blocks, -inf otherwise
+        const int c0 = 64 * schunk[(t - nK) >> 1];
 #pragma unroll
-      for (int b = 0; b < 2; b++)
+        for (int b = 0; b < 2; b++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int key = 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const float v = key < nvalid ? s[b][r] * c : -INFINITY;
-          x[16 * b + r] = v;
-          tmax = __builtin_fmaxf(tmax, v);
+          for (int r = 0; r < 16; r++) {
+            const int J = c0 + 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const bool sk = J < dm.Nk && stier[J] == TATTN_SKIP;
+            const float lg = J == dm.Nk - 1 ? __log2f(static_cast<float>(dm.N - J * 64)) : 6.0f;
+            s[b][r] = sk ? __builtin_fmaf(s[b][r], cF, lg) : -INFINITY;
+            tmax = __builtin_fmaxf(tmax, s[b][r]);
+          }
+        c = 1.0f;
+      } else {
+        const int J = slist[t];
+        c = kind == kLow ? sq * skp[J] * cF : cF;
+        if (J == dm.Nk - 1) {   // ragged last tile: mask keys past N
+          const int nvalid = dm.N - J * 64;
+#pragma unroll
+          for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int key = 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
+              if (key >= nvalid) s[b][r] = -INFINITY;
+            }
         }
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) tmax = __builtin_fmaxf(tmax, s[b][r]);
+        tmax *= c;
+      }
+      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const bool need = tmax > m_run + kLazy;
+      if (__ballot(need)) {
+        const float mn = need ? tmax : m_run;
+        const float al = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= al;
+#pragma unroll
+        for (int db = 0; db < D / 32; db++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[db][r] *= al;
+        m_run = mn;
+      }
+      const float nm = -m_run;
+      float psum = 0.0f;
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+        for (int tt = 0; tt < 8; tt++) {
+          const int e = 8 * cc + tt;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c, nm));
+          psum += p;
+          pb[cc][tt] = static_cast<_Float16>(p);
+        }
+      l_run += psum;
     }
-    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    raise_max(tmax);
-    f16x8 pb[4];
+    if (kind != kSkipS) {
+      // ---- O^T += V^T P^T (fp16: V, the low tier's V, or the skipped blocks' means)
 #pragma unroll
-    for (int cc = 0; cc < 4; cc++)
+      for (int cc = 0; cc < 4; cc++) {
 #pragma unroll
-      for (int tt = 0; tt < 8; tt++)
-        pb[cc][tt] = static_cast<_Float16>(__builtin_amdgcn_exp2f(x[8 * cc + tt] - m_run));
-    // l sums exactly the rounded weights that enter P.V
-    float psum = 0.0f;
-#pragma unroll
-    for (int cc = 0; cc < 4; cc++)
-#pragma unroll
-      for (int tt = 0; tt < 8; tt++) psum += static_cast<float>(pb[cc][tt]);
-    l_run += psum;
-
-    // ---- O^T += V^T P^T (fp16 values: V, the low tier's V, or the skipped blocks' means)
-    const unsigned char* sv = st + 128 * D;
-#pragma unroll
-    for (int cc = 0; cc < 4; cc++) {
-#pragma unroll
-      for (int db = 0; db < D / 32; db++) {
-        const int d = 32 * db + ln;
-        const f16x8 av = *reinterpret_cast<const f16x8*>(sv + offV(d, 2 * cc + lh));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[cc], acc[db], 0, 0, 0);
+        for (int db = 0; db < D / 32; db++) {
+          const int d = 32 * db + ln;
+          const f16x8 av = *reinterpret_cast<const f16x8*>(st + R1 + offV(d, 2 * cc + lh));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[cc], acc[db], 0, 0, 0);
+        }
       }
     }
+  };
 
-    if (t + 1 < nSteps) stage_store(t + 1, buf ^ 1);
-    __syncthreads();
+  // ---- the step loop: two stages, unrolled by two so each stage is a
+  // distinct LDS object (the DMA into one never orders reads of the other).
+  if (nSteps > 0) issue(0, st0);
+  wait_vm0();
+  __syncthreads();
+  for (int t = 0; t < nSteps; t += 2) {
+    if (t + 1 < nSteps) issue(t + 1, st1);
+    compute(t, st0);
+    wait_vm0();
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 >= nSteps) break;
+    if (t + 2 < nSteps) issue(t + 2, st0);
+    compute(t + 1, st1);
+    wait_vm0();
+    __builtin_amdgcn_s_barrier();
   }
 
   // ---- epilogue: O = acc / l

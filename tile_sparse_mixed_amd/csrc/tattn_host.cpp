@@ -47,6 +47,7 @@ Dims make_dims(const tattn_config& c) {
   d.Bk = c.block_k;
   d.Nq = (c.seq_len + c.block_q - 1) / c.block_q;
   d.Nk = (c.seq_len + c.block_k - 1) / c.block_k;
+  d.NkC = (d.Nk + 63) / 64;
   d.sb = c.stride_b;
   d.sh = c.stride_h;
   d.sn = c.stride_n;
@@ -68,7 +69,7 @@ Layout make_layout(const Dims& d, int entropy_samples) {
   L.vbar = take(BH * Nk * D * 4);
   L.kbar16 = take(BH * Nk * D * 2);
   L.kbarlo = take(BH * Nk * D * 2);
-  L.vbar16 = take(BH * Nk * D * 2);
+  L.vbarT = take(BH * (size_t)d.NkC * 64 * D * 2);
   L.sq = take(BH * Nq * 4);
   L.iq = take(BH * Nq * 4);
   L.sk = take(BH * Nk * 4);
@@ -125,7 +126,7 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "strides must be positive with stride_n >= head_dim");
   if ((c->stride_n % 8) || (c->stride_h % 8) || (c->stride_b % 8))
     return fail(TATTN_E_INVALID, "strides must be multiples of 8 elements (16-byte rows)");
-  if (nk > kMaxNk / 2) return fail(TATTN_E_UNSUPPORTED, "%lld key blocks exceed the router limit of 4096", (long long)nk);
+  if (nk > kMaxNk) return fail(TATTN_E_UNSUPPORTED, "%lld key blocks exceed the limit of %d", (long long)nk, kMaxNk);
   if ((int64_t)c->batch * c->heads * nq > 0x7fffffffLL || (int64_t)c->batch * c->heads * nk > 0x7fffffffLL)
     return fail(TATTN_E_UNSUPPORTED, "problem too large for one launch");
   return ok();

@@ -11,12 +11,13 @@
 namespace tattn {
 
 constexpr int kTile = 64;          // key-tile width the fused kernel works in
-constexpr int kMaxNk = 8192;       // key blocks per row (int16 lists, router LDS)
+constexpr int kMaxNk = 4096;       // key blocks per row (router and fused-kernel LDS rows)
 constexpr int kAlign = 256;
 
 // Sizes derived from a validated config.
 struct Dims {
   int B, H, BH, N, D, Bq, Bk, Nq, Nk;
+  int NkC;   // chunks of 64 key blocks: ceil(Nk / 64)
   int64_t sb, sh, sn;
 };
 
@@ -25,7 +26,8 @@ struct Layout {
   size_t qbar, kbar, vbar;      // f32 [BH][Nq|Nk][D]
   size_t kbar16, kbarlo;        // bf16 [BH][Nk][D]  K block means as hi + lo bf16 pair (scores of
                                 //                    skipped tiles: kbar = hi + lo to ~2^-17)
-  size_t vbar16;                // fp16 [BH][Nk][D]  block means of V (values of skipped tiles)
+  size_t vbarT;                 // fp16 [BH][NkC][D][64]  V block means, transposed per chunk of 64
+                                //   blocks in vt_pos order, zero past Nk (values of skipped tiles)
   size_t sq, iq;                // f32 [BH][Nq]   scale and inverse scale of each Q block
   size_t sk, sv;                // f32 [BH][Nk]
   size_t k8;                    // u8  [BH][Nk][Bk][D]   d permuted within a row
