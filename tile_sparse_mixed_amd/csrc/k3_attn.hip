@@ -22,11 +22,14 @@
 // masked to the row's SKIP set; chunks with no skipped block are not visited.
 //
 // Data movement: every step's operands go global -> LDS with direct
-// global_load_lds_dwordx4 (no staging registers) into one of two stage
-// buffers while the other stage is computed; the XOR swizzle that keeps the
-// MFMA operand reads bank-conflict free is applied by choosing each lane's
-// source address.  A step ends with vmcnt(0) + s_barrier, which publishes the
-// next stage; the plain barrier (no fence) keeps the next DMA in flight.
+// buffer_load_dwordx4 ... lds (no staging registers) into one of two stage
+// buffers while the other stage is computed.  Scalar buffer resources carry
+// the bases, so a lane needs one 32-bit offset per load pattern, and a
+// per-tile resource over the caller's K returns zeros for rows past N.  The
+// XOR swizzle that keeps the MFMA operand reads bank-conflict free is applied
+// by choosing each lane's source offset.  A step ends with vmcnt(0) +
+// s_barrier, which publishes the next stage; the plain barrier (no fence)
+// keeps the next step's DMA in flight during the current step's math.
 //
 // Running state per lane: m (base-2 reference), l (sum of the weights
 // relative to 2^m) and the O^T accumulator.  m is raised only when a tile's
@@ -46,10 +49,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 // vmcnt(0) with expcnt and lgkmcnt unconstrained (gfx9 s_waitcnt encoding).
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// One wave: copy 64 lanes x 16 bytes to LDS[dst .. dst+1024), lane l's bytes
-// coming from src (a per-lane global address).
-__device__ inline void dma16(const void* src, unsigned char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+// One wave: copy 64 lanes x 16 bytes into LDS[dst .. dst+1024); lane l's bytes
+// come from byte offset voff (per lane) + soff (uniform) of buffer `r`.  A
+// read past the buffer's num_records returns zeros.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
 // Swizzled byte offsets of 16-byte chunk `ch` of a row inside a stage region.
@@ -89,7 +98,8 @@ void k3_attn(AttnArgs a) {
   const int64_t toff = (int64_t)bidx * dm.sb + (int64_t)hidx * dm.sh;
   const int64_t row = (int64_t)bh * dm.Nq + I;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, lh = lane >> 5;
 
   const unsigned char* ws = a.ws;
@@ -157,6 +167,8 @@ void k3_attn(AttnArgs a) {
     }
   }
 
+  const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
+
   auto step_kind = [&](int t) {
     if (t < nF) return (int)kFull;
     if (t < nK) return (int)kLow;
@@ -168,49 +180,67 @@ void k3_attn(AttnArgs a) {
   //   LOW     R0 = K8 [64][D] E4M3,      R1 = V low^T [D][64] fp16
   //   SKIP_S  R0 = kbar hi [64][D] bf16, R1 = kbar lo [64][D] bf16
   //   SKIP_PV                            R1 = vbar^T [D][64] fp16
-  auto load_rows16 = [&](unsigned char* reg, auto row_ptr) {   // [64][D] 16-bit rows
-    constexpr int CH = D / 8, RPI = 1024 / (2 * D);          // chunks per row, rows per instruction
+  // Wave w issues the 1 KB instructions k = w, w + NW, ...  A 16-bit row of D
+  // elements spans D/8 chunks, so one instruction covers RPI = 1024/(2D) rows
+  // and a lane's row parity pattern (r & 7) is the same for all its k.
+  constexpr int CH = D / 8, RPI = 1024 / (2 * D), NI16 = D / 8 / NW, NI8 = D / 16 / NW;
+  const int rr16 = lane / CH, pos16 = lane % CH;   // row within an instruction, chunk slot
+  const int sw16 = (pos16 ^ ((wave * RPI + rr16) & 7)) * 16;   // source chunk byte offset, all k
+  const int voffK = rr16 * (int)dm.sn * 2 + sw16;                // caller's K rows (stride sn)
+  const int voffKb = rr16 * 2 * D + sw16;                        // kbar rows (stride D)
+  const int voffV = (lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7)) * 16);   // [D][64] 16-bit tiles
+  const int voffK8 = D == 128 ? voffV : (lane >> 2) * 64 + (((lane & 3) ^ (((lane >> 2) >> 1) & 3)) * 16);
+  const __amdgpu_buffer_rsrc_t rVT = make_rsrc(vt, (uint32_t)dm.Nk * 128 * D);
+  const __amdgpu_buffer_rsrc_t rVL = make_rsrc(vlow, (uint32_t)dm.Nk * 128 * D);
+  const __amdgpu_buffer_rsrc_t rK8 = make_rsrc(k8, (uint32_t)dm.Nk * 64 * D);
+  const __amdgpu_buffer_rsrc_t rKH = make_rsrc(kbhi, (uint32_t)dm.Nk * 2 * D);
+  const __amdgpu_buffer_rsrc_t rKL = make_rsrc(kblo, (uint32_t)dm.Nk * 2 * D);
+  const __amdgpu_buffer_rsrc_t rVB = make_rsrc(vbT, (uint32_t)dm.NkC * 128 * D);
+  float cst0 = 0.0f, cst1 = 0.0f;   // score scale of the step staged in st0 / st1
+
+  auto load_vt16 = [&](unsigned char* reg, __amdgpu_buffer_rsrc_t r, int base) {   // [D][64] 16-bit
 #pragma unroll
-    for (int k = wave; k < D / 8; k += NW) {
-      const int r = k * RPI + lane / CH, pos = lane % CH;
-      dma16(row_ptr(r) + 8 * (pos ^ (r & 7)), reg + k * 1024);
+    for (int i = 0; i < NI16; i++) {
+      const int k = wave + NW * i;
+      dma16(r, reg + k * 1024, voffV, base + k * 1024);
     }
   };
-  auto load_vt16 = [&](unsigned char* reg, const uint16_t* tile) {   // [D][64] 16-bit rows of 128 B
-#pragma unroll
-    for (int k = wave; k < D / 8; k += NW) {
-      const int r = 8 * k + (lane >> 3), pos = lane & 7;
-      dma16(tile + r * 64 + 8 * (pos ^ (r & 7)), reg + k * 1024);
-    }
-  };
-  auto issue = [&](int t, unsigned char* st) {
+  auto issue = [&](int t, unsigned char* st, float& cst) {
     const int kind = step_kind(t);
     if (kind == kFull) {
       const int J = slist[t];
-      load_rows16(st, [&](int r) { return kin + (int64_t)min(J * 64 + r, dm.N - 1) * dm.sn; });
-      load_vt16(st + R1, vt + (int64_t)J * 64 * D);
+      // one resource per tile: rows past N read as zeros (and are masked)
+      const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
+      const __amdgpu_buffer_rsrc_t rK = make_rsrc(kin + (int64_t)J * 64 * dm.sn, rows * (uint32_t)dm.sn * 2);
+#pragma unroll
+      for (int i = 0; i < NI16; i++) {
+        const int k = wave + NW * i;
+        dma16(rK, st + k * 1024, voffK + k * RPI * (int)dm.sn * 2, 0);
+      }
+      load_vt16(st + R1, rVT, J * 128 * D);
+      cst = cF;
     } else if (kind == kLow) {
       const int J = slist[t];
-      const unsigned char* tile = k8 + (int64_t)J * 64 * D;
 #pragma unroll
-      for (int k = wave; k < D / 16; k += NW) {
-        if (D == 128) {
-          const int r = 8 * k + (lane >> 3), pos = lane & 7;
-          dma16(tile + r * 128 + 16 * (pos ^ (r & 7)), st + k * 1024);
-        } else {
-          const int r = 16 * k + (lane >> 2), pos = lane & 3;
-          dma16(tile + r * 64 + 16 * (pos ^ ((r >> 1) & 3)), st + k * 1024);
-        }
+      for (int i = 0; i < NI8; i++) {
+        const int k = wave + NW * i;
+        dma16(rK8, st + k * 1024, voffK8, J * 64 * D + k * 1024);
       }
-      load_vt16(st + R1, vlow + (int64_t)J * 64 * D);
+      load_vt16(st + R1, rVL, J * 128 * D);
+      cst = sq * skp[J] * cF;
     } else {
       const int c = schunk[(t - nK) >> 1];
       if (kind == kSkipS) {
-        load_rows16(st, [&](int r) { return kbhi + (int64_t)min(64 * c + r, dm.Nk - 1) * D; });
-        load_rows16(st + R1, [&](int r) { return kblo + (int64_t)min(64 * c + r, dm.Nk - 1) * D; });
+#pragma unroll
+        for (int i = 0; i < NI16; i++) {
+          const int k = wave + NW * i;
+          dma16(rKH, st + k * 1024, voffKb, c * 128 * D + k * 1024);
+          dma16(rKL, st + R1 + k * 1024, voffKb, c * 128 * D + k * 1024);
+        }
       } else {
-        load_vt16(st + R1, vbT + (int64_t)c * 64 * D);
+        load_vt16(st + R1, rVB, c * 128 * D);
       }
+      cst = 1.0f;
     }
   };
 
@@ -220,9 +250,8 @@ void k3_attn(AttnArgs a) {
   for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   f16x8 pb[4];
-  const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
 
-  auto compute = [&](int t, const unsigned char* st) {
+  auto compute = [&](int t, const unsigned char* st, float cst) {
     const int kind = step_kind(t);
     if (kind != kSkipPV) {
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -280,7 +309,7 @@ void k3_attn(AttnArgs a) {
         c = 1.0f;
       } else {
         const int J = slist[t];
-        c = kind == kLow ? sq * skp[J] * cF : cF;
+        c = cst;
         if (J == dm.Nk - 1) {   // ragged last tile: mask keys past N
           const int nvalid = dm.N - J * 64;
 #pragma unroll
@@ -338,17 +367,17 @@ void k3_attn(AttnArgs a) {
 
   // ---- the step loop: two stages, unrolled by two so each stage is a
   // distinct LDS object (the DMA into one never orders reads of the other).
-  if (nSteps > 0) issue(0, st0);
+  if (nSteps > 0) issue(0, st0, cst0);
   wait_vm0();
   __syncthreads();
   for (int t = 0; t < nSteps; t += 2) {
-    if (t + 1 < nSteps) issue(t + 1, st1);
-    compute(t, st0);
+    if (t + 1 < nSteps) issue(t + 1, st1, cst1);
+    compute(t, st0, cst0);
     wait_vm0();
     __builtin_amdgcn_s_barrier();
     if (t + 1 >= nSteps) break;
-    if (t + 2 < nSteps) issue(t + 2, st0);
-    compute(t + 1, st1);
+    if (t + 2 < nSteps) issue(t + 2, st0, cst0);
+    compute(t + 1, st1, cst1);
     wait_vm0();
     __builtin_amdgcn_s_barrier();
   }
