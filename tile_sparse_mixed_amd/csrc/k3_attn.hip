@@ -34,6 +34,8 @@
 // Running state per lane: m (base-2 reference), l (sum of the weights
 // relative to 2^m) and the O^T accumulator.  m is raised only when a tile's
 // max exceeds it by more than 8, so most steps skip the rescale.
+#include <type_traits>
+
 #include "tattn_device.hpp"
 #include "tattn_internal.hpp"
 
@@ -61,13 +63,39 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
+// Pins the schedule of a run of n (LDS read, MFMA) pairs: `ahead` reads are
+// issued first, then each MFMA is followed by the next read, so `ahead` reads
+// stay in flight instead of each MFMA waiting on a just-issued read.
+template <int N, int AHEAD>
+__device__ inline void pipeline_reads_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// LDS swizzles.  An MFMA operand read has the lanes of a half-wave read 16
+// bytes at the same logical chunk of 32 consecutive rows.  gfx950 serves a
+// ds_read_b128 16 lanes at a time across 64 four-byte banks (256 bytes), so
+// 16 consecutive rows must land on 16 distinct 16-byte slots modulo 256; the
+// chunk index is XORed with a function of the row chosen so that this holds
+// (and also 8 rows modulo 128 bytes).  Measured: XORing with (row & 7) alone
+// left ~1 bank-conflict cycle per LDS access.
+__device__ inline int swz256(int r) { return r & 15; }                          // 256-byte rows
+__device__ inline int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }        // 128-byte rows
+__device__ inline int swz64(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }  // 64-byte rows
 // Swizzled byte offsets of 16-byte chunk `ch` of a row inside a stage region.
 template <int D>
-__device__ inline int offK(int row, int ch) { return row * (2 * D) + ((ch ^ (row & 7)) << 4); }   // [64][D] bf16
-__device__ inline int offV(int d, int ch) { return d * 128 + ((ch ^ (d & 7)) << 4); }               // [D][64] 16-bit
+__device__ inline int offK(int row, int ch) {                                   // [64][D] bf16
+  return D == 128 ? row * 256 + ((ch ^ swz256(row)) << 4) : row * 128 + ((ch ^ swz128(row)) << 4);
+}
+__device__ inline int offV(int d, int ch) { return d * 128 + ((ch ^ swz128(d)) << 4); }   // [D][64] 16-bit
 template <int D>
-__device__ inline int offK8(int row, int ch) {                                                      // [64][D] bytes
-  return D == 128 ? row * 128 + ((ch ^ (row & 7)) << 4) : row * 64 + ((ch ^ ((row >> 1) & 3)) << 4);
+__device__ inline int offK8(int row, int ch) {                                  // [64][D] bytes
+  return D == 128 ? row * 128 + ((ch ^ swz128(row)) << 4) : row * 64 + ((ch ^ swz64(row)) << 4);
 }
 
 template <int D, int NW>
@@ -75,8 +103,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_
 void k3_attn(AttnArgs a) {
   constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
   constexpr int R1 = 128 * D;
-  __shared__ __attribute__((aligned(1024))) unsigned char st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[2 * STAGE];   // two stages
   __shared__ int16_t slist[kMaxNk];          // the row's FULL then LOW key blocks
   __shared__ unsigned char stier[kMaxNk];    // the row's tier map
   __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
@@ -142,10 +169,257 @@ void k3_attn(AttnArgs a) {
     if (qrow < dm.N) v = *reinterpret_cast<const uint4*>(a.q + toff + (int64_t)qrow * dm.sn + 16 * c + 8 * lh);
     qreg[c] = __builtin_bit_cast(bf16x8, v);
   }
-  // E4M3 copy for LOW tiles: 32 bytes per instruction i = bf16 chunks 4i..4i+3
-  i32x8 q8reg[D / 64];
   const float sq = reinterpret_cast<const float*>(ws + a.L.sq)[row];
-  if (nL > 0) {
+  const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
+
+  // step order: FULL tiles, then the skip chunks (score / P.V pairs), then LOW
+  // tiles, so the bf16 Q registers are dead before the E4M3 copy is made.
+  const int nS2 = 2 * snc, tLow = nF + nS2;
+  auto step_kind = [&](int t) {
+    if (t < nF) return (int)kFull;
+    if (t < tLow) return ((t - nF) & 1) ? (int)kSkipPV : (int)kSkipS;
+    return (int)kLow;
+  };
+  auto list_at = [&](int t) { return (int)slist[t < nF ? t : t - nS2]; };   // FULL or LOW step
+
+  // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
+  //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
+  //   LOW     R0 = K8 [64][D] E4M3,      R1 = V low^T [D][64] fp16
+  //   SKIP_S  R0 = kbar hi [64][D] bf16, R1 = kbar lo [64][D] bf16
+  //   SKIP_PV                            R1 = vbar^T [D][64] fp16
+  // Wave w issues the 1 KB instructions k = w, w + NW, ...  A 16-bit row of D
+  // elements spans D/8 chunks, so one instruction covers RPI = 1024/(2D) rows.
+  constexpr int CH = D / 8, RPI = 1024 / (2 * D), NI16 = D / 8 / NW, NI8 = D / 16 / NW;
+  const int rr16 = lane / CH, pos16 = lane % CH;   // row within an instruction, chunk slot
+  // source chunk byte offset of a 16-bit row tile for instruction k (the LDS
+  // slot pos16 of row r holds logical chunk pos16 ^ swz(r))
+  auto sw16 = [&](int k) {
+    const int r = k * RPI + rr16;
+    return (pos16 ^ (D == 128 ? swz256(r) : swz128(r))) * 16;
+  };
+  // [D][64] 16-bit tiles: instruction k covers rows 8k..8k+7, so swz128(r) =
+  // ((lane >> 3) & 7) ^ (k & 1), and k & 1 == wave & 1 because NW is even.
+  const int voffV = (lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) * 16);
+  // [64][D] E4M3 tiles: 128-byte rows for D = 128 (as above), 64-byte rows for D = 64
+  // (instruction k covers rows 16k..16k+15: swz64(r) = ((lane >> 3) & 3) ^ (lane >> 5)).
+  const int voffK8 = D == 128 ? voffV
+                              : (lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 16);
+  const __amdgpu_buffer_rsrc_t rVT = make_rsrc(vt, (uint32_t)dm.Nk * 128 * D);
+  const __amdgpu_buffer_rsrc_t rVL = make_rsrc(vlow, (uint32_t)dm.Nk * 128 * D);
+  const __amdgpu_buffer_rsrc_t rK8 = make_rsrc(k8, (uint32_t)dm.Nk * 64 * D);
+  const __amdgpu_buffer_rsrc_t rKH = make_rsrc(kbhi, (uint32_t)dm.Nk * 2 * D);
+  const __amdgpu_buffer_rsrc_t rKL = make_rsrc(kblo, (uint32_t)dm.Nk * 2 * D);
+  const __amdgpu_buffer_rsrc_t rVB = make_rsrc(vbT, (uint32_t)dm.NkC * 128 * D);
+
+  auto load_vt16 = [&](unsigned char* reg, __amdgpu_buffer_rsrc_t r, int base) {   // [D][64] 16-bit
+#pragma unroll
+    for (int i = 0; i < NI16; i++) {
+      const int k = wave + NW * i;
+      dma16(r, reg + k * 1024, voffV, base + k * 1024);
+    }
+  };
+  auto issue = [&](int t, unsigned char* st, float& cst) {
+    const int kind = step_kind(t);
+    if (kind == kFull) {
+      const int J = list_at(t);
+      // one resource per tile: rows past N read as zeros (and are masked)
+      const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
+      const __amdgpu_buffer_rsrc_t rK = make_rsrc(kin + (int64_t)J * 64 * dm.sn, rows * (uint32_t)dm.sn * 2);
+#pragma unroll
+      for (int i = 0; i < NI16; i++) {
+        const int k = wave + NW * i;
+        dma16(rK, st + k * 1024, (k * RPI + rr16) * (int)dm.sn * 2 + sw16(k), 0);
+      }
+      load_vt16(st + R1, rVT, J * 128 * D);
+      cst = cF;
+    } else if (kind == kLow) {
+      const int J = list_at(t);
+#pragma unroll
+      for (int i = 0; i < NI8; i++) {
+        const int k = wave + NW * i;
+        dma16(rK8, st + k * 1024, voffK8, J * 64 * D + k * 1024);
+      }
+      load_vt16(st + R1, rVL, J * 128 * D);
+      cst = sq * skp[J] * cF;
+    } else {
+      const int c = schunk[(t - nF) >> 1];
+      if (kind == kSkipS) {
+#pragma unroll
+        for (int i = 0; i < NI16; i++) {
+          const int k = wave + NW * i;
+          const int vo = rr16 * 2 * D + sw16(k);
+          dma16(rKH, st + k * 1024, vo, c * 128 * D + k * 1024);
+          dma16(rKL, st + R1 + k * 1024, vo, c * 128 * D + k * 1024);
+        }
+      } else {
+        load_vt16(st + R1, rVB, c * 128 * D);
+      }
+      cst = 1.0f;
+    }
+  };
+
+  // ---- online-softmax state
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  f16x8 pb[4];
+
+  // ---- score blocks S^T = K Q^T of the 64 keys of a step (two 32x32 blocks)
+  // All operands of a phase are read from LDS before its MFMAs are issued, so
+  // the reads overlap each other instead of each waiting on the previous MFMA.
+  auto scores_bf16 = [&](const unsigned char* kt, f32x16* s) {
+    bf16x8 ka[D / 8];
+#pragma unroll
+    for (int cq = 0; cq < D / 16; cq++)
+#pragma unroll
+      for (int b = 0; b < 2; b++) ka[2 * cq + b] = *reinterpret_cast<const bf16x8*>(kt + offK<D>(32 * b + ln, 2 * cq + lh));
+#pragma unroll
+    for (int cq = 0; cq < D / 16; cq++)
+#pragma unroll
+      for (int b = 0; b < 2; b++) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[2 * cq + b], qreg[cq], s[b], 0, 0, 0);
+    pipeline_reads_mfma<D / 8, D / 16>();
+  };
+  auto scores_fp8 = [&](const unsigned char* kt, f32x16* s, const i32x8* q8) {
+    i32x8 ka[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 64; i++) {
+#pragma unroll
+      for (int b = 0; b < 2; b++) {
+        const int r = 32 * b + ln;
+        const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
+        const uint4 lo = *reinterpret_cast<const uint4*>(kt + offK8<D>(r, ch0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(kt + offK8<D>(r, ch0 + 1));
+        ka[2 * i + b] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < D / 64; i++)
+#pragma unroll
+      for (int b = 0; b < 2; b++)
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[2 * i + b], q8[i], s[b], 0, 0, 0, 0, 0, 0);
+  };
+  // Key of register (b, r) of this lane: 32b + 8(r/4) + 4lh + r%4.  Masks keys
+  // >= nvalid (the ragged last tile).
+  auto mask_tail = [&](f32x16* s, int nvalid) {
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        if (32 * b + 8 * (r >> 2) + 4 * lh + (r & 3) >= nvalid) s[b][r] = -INFINITY;
+  };
+  // ---- online softmax of x = s * c (base-2 units; tmax already scaled) into
+  // the fp16 P operand, raising m when needed.
+  auto softmax = [&](f32x16* s, float c, float tmax) {
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const bool need = tmax > m_run + kLazy;
+    if (__ballot(need)) {
+      const float mn = need ? tmax : m_run;
+      const float al = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
+      l_run *= al;
+#pragma unroll
+      for (int db = 0; db < D / 32; db++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[db][r] *= al;
+      m_run = mn;
+    }
+    const float nm = -m_run;
+    float psum = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int tt = 0; tt < 8; tt++) {
+        const int e = 8 * cc + tt;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c, nm));
+        psum += p;
+        pb[cc][tt] = static_cast<_Float16>(p);
+      }
+    l_run += psum;
+  };
+  auto row_max = [&](const f32x16* s) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) m = __builtin_fmaxf(m, s[b][r]);
+    return m;
+  };
+  // ---- O^T += V^T P^T from region R1 (fp16 V, low-tier V, or block means)
+  auto pv = [&](const unsigned char* st) {
+    f16x8 va[D / 8];
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int db = 0; db < D / 32; db++)
+        va[cc * (D / 32) + db] = *reinterpret_cast<const f16x8*>(st + R1 + offV(32 * db + ln, 2 * cc + lh));
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int db = 0; db < D / 32; db++)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cc * (D / 32) + db], pb[cc], acc[db], 0, 0, 0);
+    pipeline_reads_mfma<D / 8, D / 16>();
+  };
+  // a kept tile (FULL: bf16 scores, LOW: E4M3 scores) staged in `st`
+  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, float c, const i32x8* q8) {
+    constexpr bool LOW = decltype(low_tag)::value;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    if constexpr (LOW) scores_fp8(st, s, q8);
+    else scores_bf16(st, s);
+    const int J = list_at(t);
+    if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
+    softmax(s, c, row_max(s) * c);
+    pv(st);
+  };
+  // pooled keys of a chunk of 64 skipped-candidate blocks: scores only
+  auto skip_scores = [&](int t, const unsigned char* st) {
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    scores_bf16(st, s);
+    scores_bf16(st + R1, s);   // low half of kbar
+    // bias log2(n_J) for the row's skipped blocks, -inf for the others
+    const int c0 = 64 * schunk[(t - nF) >> 1];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int J = c0 + 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const bool sk = J < dm.Nk && stier[J] == TATTN_SKIP;
+        const float lg = J == dm.Nk - 1 ? __log2f(static_cast<float>(dm.N - J * 64)) : 6.0f;
+        s[b][r] = sk ? __builtin_fmaf(s[b][r], cF, lg) : -INFINITY;
+        tmax = __builtin_fmaxf(tmax, s[b][r]);
+      }
+    softmax(s, 1.0f, tmax);
+  };
+
+  // ---- the step loop, in phases (FULL, LOW, then skip chunks as score / P.V
+  // pairs).  Step t computes from stage t & 1 while step t+1's DMA fills the
+  // other stage; the explicit vmcnt(0) + barrier publishes it.
+  auto stage = [&](int t) { return st0 + (t & 1) * STAGE; };
+  auto next = [&](int t) {
+    wait_vm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  float cst[2] = {0.0f, 0.0f};
+  if (nSteps > 0) issue(0, stage(0), cst[0]);
+  wait_vm0();
+  __syncthreads();
+  int t = 0;
+  for (; t < nF; t++) {
+    if (t + 1 < nSteps) issue(t + 1, stage(t + 1), cst[(t + 1) & 1]);
+    kept_step(std::false_type{}, t, stage(t), cst[t & 1], nullptr);
+    next(t);
+  }
+  for (; t < tLow; t += 2) {
+    issue(t + 1, stage(t + 1), cst[(t + 1) & 1]);
+    skip_scores(t, stage(t));
+    next(t);
+    if (t + 2 < nSteps) issue(t + 2, stage(t + 2), cst[t & 1]);
+    pv(stage(t + 1));
+    next(t + 1);
+  }
+  if (t < nSteps) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
+                      // fp8 instruction i = bf16 chunks 4i..4i+3)
+    i32x8 q8reg[D / 64];
     const float iq = reinterpret_cast<const float*>(ws + a.L.iq)[row];
 #pragma unroll
     for (int i = 0; i < D / 64; i++) {
@@ -162,221 +436,11 @@ void k3_attn(AttnArgs a) {
         q8reg[i][2 * cc + 1] = hi;
       }
     }
-  }
-
-  const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
-
-  auto step_kind = [&](int t) {
-    if (t < nF) return (int)kFull;
-    if (t < nK) return (int)kLow;
-    return ((t - nK) & 1) ? (int)kSkipPV : (int)kSkipS;
-  };
-
-  // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
-  //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
-  //   LOW     R0 = K8 [64][D] E4M3,      R1 = V low^T [D][64] fp16
-  //   SKIP_S  R0 = kbar hi [64][D] bf16, R1 = kbar lo [64][D] bf16
-  //   SKIP_PV                            R1 = vbar^T [D][64] fp16
-  // Wave w issues the 1 KB instructions k = w, w + NW, ...  A 16-bit row of D
-  // elements spans D/8 chunks, so one instruction covers RPI = 1024/(2D) rows
-  // and a lane's row parity pattern (r & 7) is the same for all its k.
-  constexpr int CH = D / 8, RPI = 1024 / (2 * D), NI16 = D / 8 / NW, NI8 = D / 16 / NW;
-  const int rr16 = lane / CH, pos16 = lane % CH;   // row within an instruction, chunk slot
-  const int sw16 = (pos16 ^ ((wave * RPI + rr16) & 7)) * 16;   // source chunk byte offset, all k
-  const int voffK = rr16 * (int)dm.sn * 2 + sw16;                // caller's K rows (stride sn)
-  const int voffKb = rr16 * 2 * D + sw16;                        // kbar rows (stride D)
-  const int voffV = (lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7)) * 16);   // [D][64] 16-bit tiles
-  const int voffK8 = D == 128 ? voffV : (lane >> 2) * 64 + (((lane & 3) ^ (((lane >> 2) >> 1) & 3)) * 16);
-  const __amdgpu_buffer_rsrc_t rVT = make_rsrc(vt, (uint32_t)dm.Nk * 128 * D);
-  const __amdgpu_buffer_rsrc_t rVL = make_rsrc(vlow, (uint32_t)dm.Nk * 128 * D);
-  const __amdgpu_buffer_rsrc_t rK8 = make_rsrc(k8, (uint32_t)dm.Nk * 64 * D);
-  const __amdgpu_buffer_rsrc_t rKH = make_rsrc(kbhi, (uint32_t)dm.Nk * 2 * D);
-  const __amdgpu_buffer_rsrc_t rKL = make_rsrc(kblo, (uint32_t)dm.Nk * 2 * D);
-  const __amdgpu_buffer_rsrc_t rVB = make_rsrc(vbT, (uint32_t)dm.NkC * 128 * D);
-  float cst0 = 0.0f, cst1 = 0.0f;   // score scale of the step staged in st0 / st1
-
-  auto load_vt16 = [&](unsigned char* reg, __amdgpu_buffer_rsrc_t r, int base) {   // [D][64] 16-bit
-#pragma unroll
-    for (int i = 0; i < NI16; i++) {
-      const int k = wave + NW * i;
-      dma16(r, reg + k * 1024, voffV, base + k * 1024);
+    for (; t < nSteps; t++) {
+      if (t + 1 < nSteps) issue(t + 1, stage(t + 1), cst[(t + 1) & 1]);
+      kept_step(std::true_type{}, t, stage(t), cst[t & 1], q8reg);
+      next(t);
     }
-  };
-  auto issue = [&](int t, unsigned char* st, float& cst) {
-    const int kind = step_kind(t);
-    if (kind == kFull) {
-      const int J = slist[t];
-      // one resource per tile: rows past N read as zeros (and are masked)
-      const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
-      const __amdgpu_buffer_rsrc_t rK = make_rsrc(kin + (int64_t)J * 64 * dm.sn, rows * (uint32_t)dm.sn * 2);
-#pragma unroll
-      for (int i = 0; i < NI16; i++) {
-        const int k = wave + NW * i;
-        dma16(rK, st + k * 1024, voffK + k * RPI * (int)dm.sn * 2, 0);
-      }
-      load_vt16(st + R1, rVT, J * 128 * D);
-      cst = cF;
-    } else if (kind == kLow) {
-      const int J = slist[t];
-#pragma unroll
-      for (int i = 0; i < NI8; i++) {
-        const int k = wave + NW * i;
-        dma16(rK8, st + k * 1024, voffK8, J * 64 * D + k * 1024);
-      }
-      load_vt16(st + R1, rVL, J * 128 * D);
-      cst = sq * skp[J] * cF;
-    } else {
-      const int c = schunk[(t - nK) >> 1];
-      if (kind == kSkipS) {
-#pragma unroll
-        for (int i = 0; i < NI16; i++) {
-          const int k = wave + NW * i;
-          dma16(rKH, st + k * 1024, voffKb, c * 128 * D + k * 1024);
-          dma16(rKL, st + R1 + k * 1024, voffKb, c * 128 * D + k * 1024);
-        }
-      } else {
-        load_vt16(st + R1, rVB, c * 128 * D);
-      }
-      cst = 1.0f;
-    }
-  };
-
-  // ---- online-softmax state
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
-  f16x8 pb[4];
-
-  auto compute = [&](int t, const unsigned char* st, float cst) {
-    const int kind = step_kind(t);
-    if (kind != kSkipPV) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      if (kind == kLow) {
-#pragma unroll
-        for (int i = 0; i < D / 64; i++) {
-#pragma unroll
-          for (int b = 0; b < 2; b++) {
-            const int r = 32 * b + ln;
-            const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
-            const uint4 lo = *reinterpret_cast<const uint4*>(st + offK8<D>(r, ch0));
-            const uint4 hi = *reinterpret_cast<const uint4*>(st + offK8<D>(r, ch0 + 1));
-            const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8reg[i], s[b], 0, 0, 0, 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < D / 16; c++) {
-#pragma unroll
-          for (int b = 0; b < 2; b++) {
-            const int r = 32 * b + ln;
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + offK<D>(r, 2 * c + lh));
-            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[b], 0, 0, 0);
-          }
-        }
-        if (kind == kSkipS) {
-#pragma unroll
-          for (int c = 0; c < D / 16; c++) {
-#pragma unroll
-            for (int b = 0; b < 2; b++) {
-              const int r = 32 * b + ln;
-              const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + R1 + offK<D>(r, 2 * c + lh));
-              s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[c], s[b], 0, 0, 0);
-            }
-          }
-        }
-      }
-      // ---- online softmax in base 2.  Key of register (b, r): 32b + 8(r/4) + 4lh + r%4.
-      float tmax = -INFINITY;
-      float c;
-      if (kind == kSkipS) {
-        // per-key bias: log2(n_J) for the row's skipped blocks, -inf otherwise
-        const int c0 = 64 * schunk[(t - nK) >> 1];
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int J = c0 + 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const bool sk = J < dm.Nk && stier[J] == TATTN_SKIP;
-            const float lg = J == dm.Nk - 1 ? __log2f(static_cast<float>(dm.N - J * 64)) : 6.0f;
-            s[b][r] = sk ? __builtin_fmaf(s[b][r], cF, lg) : -INFINITY;
-            tmax = __builtin_fmaxf(tmax, s[b][r]);
-          }
-        c = 1.0f;
-      } else {
-        const int J = slist[t];
-        c = cst;
-        if (J == dm.Nk - 1) {   // ragged last tile: mask keys past N
-          const int nvalid = dm.N - J * 64;
-#pragma unroll
-          for (int b = 0; b < 2; b++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-              const int key = 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
-              if (key >= nvalid) s[b][r] = -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) tmax = __builtin_fmaxf(tmax, s[b][r]);
-        tmax *= c;
-      }
-      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const bool need = tmax > m_run + kLazy;
-      if (__ballot(need)) {
-        const float mn = need ? tmax : m_run;
-        const float al = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
-        l_run *= al;
-#pragma unroll
-        for (int db = 0; db < D / 32; db++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) acc[db][r] *= al;
-        m_run = mn;
-      }
-      const float nm = -m_run;
-      float psum = 0.0f;
-#pragma unroll
-      for (int cc = 0; cc < 4; cc++)
-#pragma unroll
-        for (int tt = 0; tt < 8; tt++) {
-          const int e = 8 * cc + tt;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c, nm));
-          psum += p;
-          pb[cc][tt] = static_cast<_Float16>(p);
-        }
-      l_run += psum;
-    }
-    if (kind != kSkipS) {
-      // ---- O^T += V^T P^T (fp16: V, the low tier's V, or the skipped blocks' means)
-#pragma unroll
-      for (int cc = 0; cc < 4; cc++) {
-#pragma unroll
-        for (int db = 0; db < D / 32; db++) {
-          const int d = 32 * db + ln;
-          const f16x8 av = *reinterpret_cast<const f16x8*>(st + R1 + offV(d, 2 * cc + lh));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[cc], acc[db], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  // ---- the step loop: two stages, unrolled by two so each stage is a
-  // distinct LDS object (the DMA into one never orders reads of the other).
-  if (nSteps > 0) issue(0, st0, cst0);
-  wait_vm0();
-  __syncthreads();
-  for (int t = 0; t < nSteps; t += 2) {
-    if (t + 1 < nSteps) issue(t + 1, st1, cst1);
-    compute(t, st0, cst0);
-    wait_vm0();
-    __builtin_amdgcn_s_barrier();
-    if (t + 1 >= nSteps) break;
-    if (t + 2 < nSteps) issue(t + 2, st0, cst0);
-    compute(t + 1, st1, cst1);
-    wait_vm0();
-    __builtin_amdgcn_s_barrier();
   }
 
   // ---- epilogue: O = acc / l
