@@ -108,14 +108,15 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   unsigned char* ws = a.ws;
   float* kbar = reinterpret_cast<float*>(ws + a.L.kbar) + ((int64_t)bh * dm.Nk + J) * D;
   float* vbar = reinterpret_cast<float*>(ws + a.L.vbar) + ((int64_t)bh * dm.Nk + J) * D;
-  uint16_t* kbar16 = reinterpret_cast<uint16_t*>(ws + a.L.kbar16) + ((int64_t)bh * dm.Nk + J) * D;
-  uint16_t* kbarlo = reinterpret_cast<uint16_t*>(ws + a.L.kbarlo) + ((int64_t)bh * dm.Nk + J) * D;
-  uint16_t* vbarT = reinterpret_cast<uint16_t*>(ws + a.L.vbarT) + ((int64_t)bh * dm.NkC + J / 64) * 64 * D;
+  unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
+  uint16_t* kbar16 = reinterpret_cast<uint16_t*>(slab + a.L.sl.kbhi) + (int64_t)J * D;
+  uint16_t* kbarlo = reinterpret_cast<uint16_t*>(slab + a.L.sl.kblo) + (int64_t)J * D;
+  uint16_t* vbarT = reinterpret_cast<uint16_t*>(slab + a.L.sl.vbarT) + (int64_t)(J / 64) * 64 * D;
   float* sk = reinterpret_cast<float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk + J;
   float* sv = reinterpret_cast<float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk + J;
-  unsigned char* k8 = ws + a.L.k8 + ((int64_t)bh * dm.Nk + J) * BK * D;
-  uint16_t* vlow = reinterpret_cast<uint16_t*>(ws + a.L.vlow) + ((int64_t)bh * dm.Nk + J) * BK * D;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + a.L.vt) + ((int64_t)bh * dm.Nk + J) * BK * D;
+  unsigned char* k8 = slab + a.L.sl.k8 + (int64_t)J * BK * D;
+  uint16_t* vlow = reinterpret_cast<uint16_t*>(slab + a.L.sl.vlow) + (int64_t)J * BK * D;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(slab + a.L.sl.vt) + (int64_t)J * BK * D;
 
   const int t = threadIdx.x;
   const int c = t % BL::CH, r0 = t / BL::CH;

@@ -151,12 +151,8 @@ void k3_attn(AttnArgs a) {
   const int nSteps = nK + 2 * snc;
 
   const uint16_t* kin = a.k + toff;
-  const uint16_t* vt = reinterpret_cast<const uint16_t*>(ws + a.L.vt) + (int64_t)bh * dm.Nk * 64 * D;
-  const unsigned char* k8 = ws + a.L.k8 + (int64_t)bh * dm.Nk * 64 * D;
-  const uint16_t* vlow = reinterpret_cast<const uint16_t*>(ws + a.L.vlow) + (int64_t)bh * dm.Nk * 64 * D;
-  const uint16_t* kbhi = reinterpret_cast<const uint16_t*>(ws + a.L.kbar16) + (int64_t)bh * dm.Nk * D;
-  const uint16_t* kblo = reinterpret_cast<const uint16_t*>(ws + a.L.kbarlo) + (int64_t)bh * dm.Nk * D;
-  const uint16_t* vbT = reinterpret_cast<const uint16_t*>(ws + a.L.vbarT) + (int64_t)bh * dm.NkC * 64 * D;
+  const unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
+  const Slab SL = a.L.sl;
   const float* skp = reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk;
 
   // ---- Q rows of this wave as bf16 B operands: lane (ln, lh) holds
@@ -204,12 +200,9 @@ void k3_attn(AttnArgs a) {
   // (instruction k covers rows 16k..16k+15: swz64(r) = ((lane >> 3) & 3) ^ (lane >> 5)).
   const int voffK8 = D == 128 ? voffV
                               : (lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 16);
-  const __amdgpu_buffer_rsrc_t rVT = make_rsrc(vt, (uint32_t)dm.Nk * 128 * D);
-  const __amdgpu_buffer_rsrc_t rVL = make_rsrc(vlow, (uint32_t)dm.Nk * 128 * D);
-  const __amdgpu_buffer_rsrc_t rK8 = make_rsrc(k8, (uint32_t)dm.Nk * 64 * D);
-  const __amdgpu_buffer_rsrc_t rKH = make_rsrc(kbhi, (uint32_t)dm.Nk * 2 * D);
-  const __amdgpu_buffer_rsrc_t rKL = make_rsrc(kblo, (uint32_t)dm.Nk * 2 * D);
-  const __amdgpu_buffer_rsrc_t rVB = make_rsrc(vbT, (uint32_t)dm.NkC * 128 * D);
+  // one resource over this head's slab; every workspace operand is a scalar
+  // sub-offset of it
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(slab, (uint32_t)SL.bytes);
 
   auto load_vt16 = [&](unsigned char* reg, __amdgpu_buffer_rsrc_t r, int base) {   // [D][64] 16-bit
 #pragma unroll
@@ -230,16 +223,16 @@ void k3_attn(AttnArgs a) {
         const int k = wave + NW * i;
         dma16(rK, st + k * 1024, (k * RPI + rr16) * (int)dm.sn * 2 + sw16(k), 0);
       }
-      load_vt16(st + R1, rVT, J * 128 * D);
+      load_vt16(st + R1, rS, (int)SL.vt + J * 128 * D);
       cst = cF;
     } else if (kind == kLow) {
       const int J = list_at(t);
 #pragma unroll
       for (int i = 0; i < NI8; i++) {
         const int k = wave + NW * i;
-        dma16(rK8, st + k * 1024, voffK8, J * 64 * D + k * 1024);
+        dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
       }
-      load_vt16(st + R1, rVL, J * 128 * D);
+      load_vt16(st + R1, rS, (int)SL.vlow + J * 128 * D);
       cst = sq * skp[J] * cF;
     } else {
       const int c = schunk[(t - nF) >> 1];
@@ -248,11 +241,11 @@ void k3_attn(AttnArgs a) {
         for (int i = 0; i < NI16; i++) {
           const int k = wave + NW * i;
           const int vo = rr16 * 2 * D + sw16(k);
-          dma16(rKH, st + k * 1024, vo, c * 128 * D + k * 1024);
-          dma16(rKL, st + R1 + k * 1024, vo, c * 128 * D + k * 1024);
+          dma16(rS, st + k * 1024, vo, (int)SL.kbhi + c * 128 * D + k * 1024);
+          dma16(rS, st + R1 + k * 1024, vo, (int)SL.kblo + c * 128 * D + k * 1024);
         }
       } else {
-        load_vt16(st + R1, rVB, c * 128 * D);
+        load_vt16(st + R1, rS, (int)SL.vbarT + c * 128 * D);
       }
       cst = 1.0f;
     }

@@ -67,16 +67,27 @@ Layout make_layout(const Dims& d, int entropy_samples) {
   L.qbar = take(BH * Nq * D * 4);
   L.kbar = take(BH * Nk * D * 4);
   L.vbar = take(BH * Nk * D * 4);
-  L.kbar16 = take(BH * Nk * D * 2);
-  L.kbarlo = take(BH * Nk * D * 2);
-  L.vbarT = take(BH * (size_t)d.NkC * 64 * D * 2);
   L.sq = take(BH * Nq * 4);
   L.iq = take(BH * Nq * 4);
   L.sk = take(BH * Nk * 4);
   L.sv = take(BH * Nk * 4);
-  L.k8 = take(BH * Nk * Bk * D);
-  L.vlow = take(BH * Nk * Bk * D * 2);
-  L.vt = take(BH * Nk * Bk * D * 2);
+  {
+    Slab& sl = L.sl;
+    size_t o = 0;
+    auto sub = [&](size_t bytes) {
+      const size_t at = o;
+      o += (bytes + kAlign - 1) / kAlign * kAlign;
+      return at;
+    };
+    sl.vt = sub(Nk * Bk * D * 2);
+    sl.vlow = sub(Nk * Bk * D * 2);
+    sl.k8 = sub(Nk * Bk * D);
+    sl.kbhi = sub(Nk * D * 2);
+    sl.kblo = sub(Nk * D * 2);
+    sl.vbarT = sub((size_t)d.NkC * 64 * D * 2);
+    sl.bytes = o;
+  }
+  L.slab = take(BH * L.sl.bytes);
   L.S = take(BH * Nq * Nk * 8);
   L.p = take(BH * Nq * Nk * 4);
   L.tiers = take(BH * Nq * Nk);
@@ -311,32 +322,21 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
   if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Dims& d = p->d;
-  const size_t tile = (size_t)kTile * d.D, tiles = (size_t)d.BH * d.Nk;
+  const size_t tile = (size_t)kTile * d.D;
   tattn_status st;
-  if (host_k8) {
-    std::vector<uint8_t> buf(tile * tiles);
-    if ((st = copy_out(buf.data(), p->ws + p->L.k8, buf.size(), s)) != TATTN_OK) return st;
+  std::vector<uint8_t> slab(p->L.sl.bytes);
+  for (size_t bh = 0; bh < (size_t)d.BH; bh++) {
+    if ((st = copy_out(slab.data(), p->ws + p->L.slab + bh * p->L.sl.bytes, slab.size(), s)) != TATTN_OK) return st;
     if ((st = sync(s)) != TATTN_OK) return st;
-    for (size_t bh = 0; bh < (size_t)d.BH; bh++)
-      for (int J = 0; J < d.Nk; J++) {
-        const uint8_t* t = buf.data() + (bh * d.Nk + J) * tile;
-        for (int r = 0; r < kTile && J * kTile + r < d.N; r++) {
-          uint8_t* o = host_k8 + (bh * d.N + J * kTile + r) * d.D;
-          for (int c = 0; c < d.D; c++) o[c] = t[r * d.D + k8_pos(c)];
-        }
-      }
-  }
-  if (host_vlow) {
-    std::vector<uint16_t> buf(tile * tiles);
-    if ((st = copy_out(buf.data(), p->ws + p->L.vlow, buf.size() * 2, s)) != TATTN_OK) return st;
-    if ((st = sync(s)) != TATTN_OK) return st;
-    for (size_t bh = 0; bh < (size_t)d.BH; bh++)
-      for (int J = 0; J < d.Nk; J++) {
-        const uint16_t* t = buf.data() + (bh * d.Nk + J) * tile;
-        for (int r = 0; r < kTile && J * kTile + r < d.N; r++) {
-          uint16_t* o = host_vlow + (bh * d.N + J * kTile + r) * d.D;
-          for (int c = 0; c < d.D; c++) o[c] = t[c * kTile + vt_pos(r)];
-        }
+    const uint8_t* k8 = slab.data() + p->L.sl.k8;
+    const uint16_t* vl = reinterpret_cast<const uint16_t*>(slab.data() + p->L.sl.vlow);
+    for (int J = 0; J < d.Nk; J++)
+      for (int r = 0; r < kTile && J * kTile + r < d.N; r++) {
+        const size_t n = (size_t)J * kTile + r;
+        if (host_k8)
+          for (int c = 0; c < d.D; c++) host_k8[(bh * d.N + n) * d.D + c] = k8[J * tile + r * d.D + k8_pos(c)];
+        if (host_vlow)
+          for (int c = 0; c < d.D; c++) host_vlow[(bh * d.N + n) * d.D + c] = vl[J * tile + c * kTile + vt_pos(r)];
       }
   }
   return ok();

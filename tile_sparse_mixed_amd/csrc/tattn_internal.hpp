@@ -21,19 +21,27 @@ struct Dims {
   int64_t sb, sh, sn;
 };
 
+// Per-head slab of everything the fused kernel reads besides Q and the
+// caller's K: one contiguous block per (b, h), so a single buffer resource
+// with scalar sub-offsets covers it.  Offsets are bytes from the slab start.
+struct Slab {
+  size_t vt;      // fp16 [Nk][D][64]   V^T, keys permuted within a tile (vt_pos)
+  size_t vlow;    // fp16 [Nk][D][64]   low-tier values fl16(decode(E4M3) * sv), same layout
+  size_t k8;      // u8   [Nk][64][D]   E4M3 K, d permuted within a row (k8_pos)
+  size_t kbhi;    // bf16 [Nk][D]       K block means, hi part
+  size_t kblo;    // bf16 [Nk][D]       K block means, lo part (kbar = hi + lo to ~2^-17)
+  size_t vbarT;   // fp16 [NkC][D][64]  V block means transposed per chunk of 64 blocks,
+                  //                    vt_pos order, zero past Nk
+  size_t bytes;   // slab size (256-byte multiple)
+};
+
 // Byte offsets of every region inside the caller's workspace.
 struct Layout {
   size_t qbar, kbar, vbar;      // f32 [BH][Nq|Nk][D]
-  size_t kbar16, kbarlo;        // bf16 [BH][Nk][D]  K block means as hi + lo bf16 pair (scores of
-                                //                    skipped tiles: kbar = hi + lo to ~2^-17)
-  size_t vbarT;                 // fp16 [BH][NkC][D][64]  V block means, transposed per chunk of 64
-                                //   blocks in vt_pos order, zero past Nk (values of skipped tiles)
   size_t sq, iq;                // f32 [BH][Nq]   scale and inverse scale of each Q block
   size_t sk, sv;                // f32 [BH][Nk]
-  size_t k8;                    // u8  [BH][Nk][Bk][D]   d permuted within a row
-  size_t vlow;                  // fp16 [BH][Nk][D][Bk]  low-tier values fl16(decode(E4M3) * sv), transposed
-                                //                        and key-permuted like vt
-  size_t vt;                    // fp16 [BH][Nk][D][Bk]  V^T, keys permuted within a row
+  size_t slab;                  // [BH] slabs of Slab::bytes each
+  Slab sl;
   size_t S;                     // f64 [BH][Nq][Nk]   router logits (scratch)
   size_t p;                     // f32 [BH][Nq][Nk]
   size_t tiers;                 // u8  [BH][Nq][Nk]
