@@ -209,10 +209,10 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
       }
       const int code2 = cvt_fp8x2<false>(f[0], f[1], 0);
       const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8(code2, false);
-      // Round the product to fp32 first, then to fp16: the empty asm keeps the
-      // compiler from fusing both roundings into one mixed-precision FMA.
+      // Round the product to fp32 first, then to fp16: the opaque step keeps
+      // the compiler from fusing both roundings into one mixed-precision FMA.
       float p0 = dec.x * svf, p1 = dec.y * svf;
-      __asm__("" : "+v"(p0), "+v"(p1));
+      opaque(p0, p1);
       w[e2] = uint32_t(f32_to_f16(p0)) | (uint32_t(f32_to_f16(p1)) << 16);
     }
     *reinterpret_cast<uint4*>(vlow + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);

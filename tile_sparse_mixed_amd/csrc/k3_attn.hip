@@ -23,7 +23,11 @@
 //
 // Data movement: every step's operands go global -> LDS with direct
 // buffer_load_dwordx4 ... lds (no staging registers) into one of two stage
-// buffers while the other stage is computed.  Scalar buffer resources carry
+// buffers while the other stage is computed.  The two stages are distinct
+// __shared__ arrays and every step knows its stage at compile time (the step
+// loops are unrolled by two): the compiler's wait insertion then sees that the
+// DMA into one stage cannot alias the operand reads of the other and does not
+// put a vmcnt(0) in front of them, which would serialise the copy and the math.  Scalar buffer resources carry
 // the bases, so a lane needs one 32-bit offset per load pattern, and a
 // per-tile resource over the caller's K returns zeros for rows past N.  The
 // XOR swizzle that keeps the MFMA operand reads bank-conflict free is applied
@@ -50,6 +54,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // vmcnt(0) with expcnt and lgkmcnt unconstrained (gfx9 s_waitcnt encoding).
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// vmcnt(0) and lgkmcnt(0): this wave's DMA has landed and its LDS reads have
+// returned (the compiler may leave the last operand reads of a step in flight
+// and consume them after the barrier, while other waves already refill that
+// stage).
+__device__ inline void wait_vm0_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
 // One wave: copy 64 lanes x 16 bytes into LDS[dst .. dst+1024); lane l's bytes
 // come from byte offset voff (per lane) + soff (uniform) of buffer `r`.  A
@@ -103,9 +112,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_
 void k3_attn(AttnArgs a) {
   constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
   constexpr int R1 = 128 * D;
-  __shared__ __attribute__((aligned(1024))) unsigned char st0[2 * STAGE];   // two stages
+  __shared__ __attribute__((aligned(1024))) unsigned char stA[STAGE];   // stage of even steps
+  __shared__ __attribute__((aligned(1024))) unsigned char stB[STAGE];   // stage of odd steps
   __shared__ int16_t slist[kMaxNk];          // the row's FULL then LOW key blocks
-  __shared__ unsigned char stier[kMaxNk];    // the row's tier map
+  __shared__ uint64_t smask[64];             // per visited chunk: bit j = block 64c + j skipped
   __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
   __shared__ int snc;
 
@@ -132,19 +142,22 @@ void k3_attn(AttnArgs a) {
   const int nK = nF + nL;
   {
     const int16_t* list = reinterpret_cast<const int16_t*>(ws + a.L.lists) + row * dm.Nk;
-    const unsigned char* tiers = ws + a.L.tiers + row * dm.Nk;
     for (int i = tid; i < nK; i += NW * 64) slist[i] = list[i];
-    for (int i = tid; i < dm.Nk; i += NW * 64) stier[i] = tiers[i];
   }
-  __syncthreads();
-  if (wave == 0) {
-    bool has = false;
+  if (wave == 0) {   // lane c: the skip mask of key-block chunk c, from the tier row
+    const unsigned char* tiers = ws + a.L.tiers + row * dm.Nk;
+    uint64_t m = 0;
     if (lane < dm.NkC) {
-      const int j1 = min(64 * lane + 64, dm.Nk);
-      for (int j = 64 * lane; j < j1 && !has; j++) has = stier[j] == TATTN_SKIP;
+      const int j0 = 64 * lane, n = min(64, dm.Nk - j0);
+      for (int j = 0; j < n; j++) m |= static_cast<uint64_t>(tiers[j0 + j] == TATTN_SKIP) << j;
     }
+    const bool has = m != 0;
     const uint64_t bal = __ballot(has);
-    if (has) schunk[__popcll(bal & ((1ull << lane) - 1))] = static_cast<unsigned char>(lane);
+    if (has) {
+      const int ci = __popcll(bal & ((1ull << lane) - 1));
+      schunk[ci] = static_cast<unsigned char>(lane);
+      smask[ci] = m;
+    }
     if (lane == 0) snc = __popcll(bal);
   }
   __syncthreads();
@@ -153,7 +166,11 @@ void k3_attn(AttnArgs a) {
   const uint16_t* kin = a.k + toff;
   const unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
   const Slab SL = a.L.sl;
-  const float* skp = reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk;
+  // sk is read through the constant address space: a uniform load there is a
+  // scalar load, counted by lgkmcnt, so waiting for it does not also wait for
+  // the DMA already in flight (a vector load would share vmcnt with it).
+  typedef __attribute__((address_space(4))) const float cfloat;
+  cfloat* skp = (cfloat*)(reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk);
 
   // ---- Q rows of this wave as bf16 B operands: lane (ln, lh) holds
   // q[row][16c + 8lh .. +8] for chunk c.
@@ -171,7 +188,7 @@ void k3_attn(AttnArgs a) {
   // step order: FULL tiles, then the skip chunks (score / P.V pairs), then LOW
   // tiles, so the bf16 Q registers are dead before the E4M3 copy is made.
   const int nS2 = 2 * snc, tLow = nF + nS2;
-  auto step_kind = [&](int t) {
+  auto step_kind = [&](int t) __attribute__((always_inline)) {
     if (t < nF) return (int)kFull;
     if (t < tLow) return ((t - nF) & 1) ? (int)kSkipPV : (int)kSkipS;
     return (int)kLow;
@@ -187,18 +204,27 @@ void k3_attn(AttnArgs a) {
   // elements spans D/8 chunks, so one instruction covers RPI = 1024/(2D) rows.
   constexpr int CH = D / 8, RPI = 1024 / (2 * D), NI16 = D / 8 / NW, NI8 = D / 16 / NW;
   const int rr16 = lane / CH, pos16 = lane % CH;   // row within an instruction, chunk slot
-  // source chunk byte offset of a 16-bit row tile for instruction k (the LDS
-  // slot pos16 of row r holds logical chunk pos16 ^ swz(r))
-  auto sw16 = [&](int k) {
-    const int r = k * RPI + rr16;
-    return (pos16 ^ (D == 128 ? swz256(r) : swz128(r))) * 16;
-  };
+  // Per-lane source offsets of a 16-bit [64][D] row tile.  Instruction
+  // k = wave + NW i covers rows k RPI .. k RPI + RPI - 1; LDS slot pos16 of row
+  // r holds logical chunk pos16 ^ swz(r).  For D = 128, swz256(4k + rr16) =
+  // 4 (k & 3) + rr16 takes 4 / NW values over i (NW = 4: one, NW = 2: two, by
+  // i & 1); for D = 64, swz128(8k + rr16) = rr16 ^ (k & 1) with k & 1 = wave & 1.
+  // So a lane needs NSW offsets, instruction i using index i % NSW.
+  constexpr int NSW = D == 128 ? 4 / NW : 1;
+  int lk[NSW], lkb[NSW];   // caller's K (row stride sn), pooled K (row stride 2D)
+#pragma unroll
+  for (int j = 0; j < NSW; j++) {
+    const int r = (wave + NW * j) * RPI + rr16;
+    const int sw = (pos16 ^ (D == 128 ? swz256(r) : swz128(r))) * 16;
+    lk[j] = rr16 * (int)dm.sn * 2 + sw;
+    lkb[j] = rr16 * 2 * D + sw;
+  }
   // [D][64] 16-bit tiles: instruction k covers rows 8k..8k+7, so swz128(r) =
   // ((lane >> 3) & 7) ^ (k & 1), and k & 1 == wave & 1 because NW is even.
-  const int voffV = (lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) * 16);
+  int voffV = (lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) * 16);
   // [64][D] E4M3 tiles: 128-byte rows for D = 128 (as above), 64-byte rows for D = 64
   // (instruction k covers rows 16k..16k+15: swz64(r) = ((lane >> 3) & 3) ^ (lane >> 5)).
-  const int voffK8 = D == 128 ? voffV
+  int voffK8 = D == 128 ? voffV
                               : (lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 16);
   // one resource over this head's slab; every workspace operand is a scalar
   // sub-offset of it
@@ -211,9 +237,12 @@ void k3_attn(AttnArgs a) {
       dma16(r, reg + k * 1024, voffV, base + k * 1024);
     }
   };
-  auto issue = [&](int t, unsigned char* st, float& cst) {
+  // KINDS: bit mask of the step kinds that can occur where this is called; the
+  // other branches are not generated, so their address terms are not kept live.
+  auto issue = [&](auto kinds, int t, unsigned char* st, float& cst) __attribute__((always_inline)) {
+    constexpr int KINDS = decltype(kinds)::value;
     const int kind = step_kind(t);
-    if (kind == kFull) {
+    if ((KINDS & (1 << kFull)) && kind == kFull) {
       const int J = list_at(t);
       // one resource per tile: rows past N read as zeros (and are masked)
       const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
@@ -221,11 +250,13 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NI16; i++) {
         const int k = wave + NW * i;
-        dma16(rK, st + k * 1024, (k * RPI + rr16) * (int)dm.sn * 2 + sw16(k), 0);
+        // the row offset stays in the lane offset: the range check that zeroes
+        // rows past N covers the lane offset, not the scalar one
+        dma16(rK, st + k * 1024, lk[i % NSW] + k * RPI * (int)dm.sn * 2, 0);
       }
       load_vt16(st + R1, rS, (int)SL.vt + J * 128 * D);
       cst = cF;
-    } else if (kind == kLow) {
+    } else if ((KINDS & (1 << kLow)) && kind == kLow) {
       const int J = list_at(t);
 #pragma unroll
       for (int i = 0; i < NI8; i++) {
@@ -236,19 +267,45 @@ void k3_attn(AttnArgs a) {
       cst = sq * skp[J] * cF;
     } else {
       const int c = schunk[(t - nF) >> 1];
-      if (kind == kSkipS) {
+      if ((KINDS & (1 << kSkipS)) && kind == kSkipS) {
 #pragma unroll
         for (int i = 0; i < NI16; i++) {
           const int k = wave + NW * i;
-          const int vo = rr16 * 2 * D + sw16(k);
-          dma16(rS, st + k * 1024, vo, (int)SL.kbhi + c * 128 * D + k * 1024);
-          dma16(rS, st + R1 + k * 1024, vo, (int)SL.kblo + c * 128 * D + k * 1024);
+          dma16(rS, st + k * 1024, lkb[i % NSW], (int)SL.kbhi + c * 128 * D + k * 1024);
+          dma16(rS, st + R1 + k * 1024, lkb[i % NSW], (int)SL.kblo + c * 128 * D + k * 1024);
         }
-      } else {
+      } else if (KINDS & (1 << kSkipPV)) {
         load_vt16(st + R1, rS, (int)SL.vbarT + c * 128 * D);
       }
       cst = 1.0f;
     }
+  };
+
+  // ---- per-lane LDS operand offsets, relative to a stage.  Rows 32b + ln have
+  // the swizzle of row ln, so the b = 1 half is a constant offset away.  They
+  // are made opaque at every step: that keeps the compiler
+  // from hoisting one copy of each address per stage out of the loops and
+  // lets it fold the stage base into the ds_read immediate instead.
+  constexpr int KROW = D == 128 ? 256 : 128;   // bytes per bf16 K row
+  constexpr int K8ROW = D;                     // bytes per E4M3 K row
+  int offk[D / 16], offv[4], offk8[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 16; c++) offk[c] = offK<D>(ln, 2 * c + lh);
+#pragma unroll
+  for (int c = 0; c < 4; c++) offv[c] = R1 + offV(ln, 2 * c + lh);
+#pragma unroll
+  for (int i = 0; i < D / 64; i++) {
+    const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
+    offk8[2 * i] = offK8<D>(ln, ch0);
+    offk8[2 * i + 1] = offK8<D>(ln, ch0 + 1);
+  }
+  auto refresh = [&]() __attribute__((always_inline)) {
+    opaque_arr(offk);
+    opaque_arr(offv);
+    opaque_arr(offk8);
+    opaque_arr(lk);
+    opaque_arr(lkb);
+    opaque(voffV, voffK8);
   };
 
   // ---- online-softmax state
@@ -261,28 +318,26 @@ void k3_attn(AttnArgs a) {
   // ---- score blocks S^T = K Q^T of the 64 keys of a step (two 32x32 blocks)
   // All operands of a phase are read from LDS before its MFMAs are issued, so
   // the reads overlap each other instead of each waiting on the previous MFMA.
-  auto scores_bf16 = [&](const unsigned char* kt, f32x16* s) {
+  auto scores_bf16 = [&](const unsigned char* kt, f32x16* s) __attribute__((always_inline)) {
     bf16x8 ka[D / 8];
 #pragma unroll
     for (int cq = 0; cq < D / 16; cq++)
 #pragma unroll
-      for (int b = 0; b < 2; b++) ka[2 * cq + b] = *reinterpret_cast<const bf16x8*>(kt + offK<D>(32 * b + ln, 2 * cq + lh));
+      for (int b = 0; b < 2; b++) ka[2 * cq + b] = *reinterpret_cast<const bf16x8*>(kt + offk[cq] + b * 32 * KROW);
 #pragma unroll
     for (int cq = 0; cq < D / 16; cq++)
 #pragma unroll
       for (int b = 0; b < 2; b++) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[2 * cq + b], qreg[cq], s[b], 0, 0, 0);
     pipeline_reads_mfma<D / 8, D / 16>();
   };
-  auto scores_fp8 = [&](const unsigned char* kt, f32x16* s, const i32x8* q8) {
+  auto scores_fp8 = [&](const unsigned char* kt, f32x16* s, const i32x8* q8) __attribute__((always_inline)) {
     i32x8 ka[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 64; i++) {
 #pragma unroll
       for (int b = 0; b < 2; b++) {
-        const int r = 32 * b + ln;
-        const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
-        const uint4 lo = *reinterpret_cast<const uint4*>(kt + offK8<D>(r, ch0));
-        const uint4 hi = *reinterpret_cast<const uint4*>(kt + offK8<D>(r, ch0 + 1));
+        const uint4 lo = *reinterpret_cast<const uint4*>(kt + offk8[2 * i] + b * 32 * K8ROW);
+        const uint4 hi = *reinterpret_cast<const uint4*>(kt + offk8[2 * i + 1] + b * 32 * K8ROW);
         ka[2 * i + b] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
@@ -294,16 +349,20 @@ void k3_attn(AttnArgs a) {
   };
   // Key of register (b, r) of this lane: 32b + 8(r/4) + 4lh + r%4.  Masks keys
   // >= nvalid (the ragged last tile).
-  auto mask_tail = [&](f32x16* s, int nvalid) {
+  // Runs once per row; the opaque limit keeps its 32 lane masks from being
+  // hoisted out of the loop and held in registers for the whole pass.
+  auto mask_tail = [&](f32x16* s, int nvalid) __attribute__((always_inline)) {
+    int lim = nvalid - 4 * lh;
+    opaque(lim);
 #pragma unroll
     for (int b = 0; b < 2; b++)
 #pragma unroll
       for (int r = 0; r < 16; r++)
-        if (32 * b + 8 * (r >> 2) + 4 * lh + (r & 3) >= nvalid) s[b][r] = -INFINITY;
+        if (32 * b + 8 * (r >> 2) + (r & 3) >= lim) s[b][r] = -INFINITY;
   };
   // ---- online softmax of x = s * c (base-2 units; tmax already scaled) into
   // the fp16 P operand, raising m when needed.
-  auto softmax = [&](f32x16* s, float c, float tmax) {
+  auto softmax = [&](f32x16* s, float c, float tmax) __attribute__((always_inline)) {
     tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const bool need = tmax > m_run + kLazy;
     if (__ballot(need)) {
@@ -329,7 +388,7 @@ void k3_attn(AttnArgs a) {
       }
     l_run += psum;
   };
-  auto row_max = [&](const f32x16* s) {
+  auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
     float m = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; b++)
@@ -338,13 +397,13 @@ void k3_attn(AttnArgs a) {
     return m;
   };
   // ---- O^T += V^T P^T from region R1 (fp16 V, low-tier V, or block means)
-  auto pv = [&](const unsigned char* st) {
+  auto pv = [&](const unsigned char* st) __attribute__((always_inline)) {
     f16x8 va[D / 8];
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
 #pragma unroll
       for (int db = 0; db < D / 32; db++)
-        va[cc * (D / 32) + db] = *reinterpret_cast<const f16x8*>(st + R1 + offV(32 * db + ln, 2 * cc + lh));
+        va[cc * (D / 32) + db] = *reinterpret_cast<const f16x8*>(st + offv[cc] + db * 32 * 128);
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
 #pragma unroll
@@ -353,7 +412,7 @@ void k3_attn(AttnArgs a) {
     pipeline_reads_mfma<D / 8, D / 16>();
   };
   // a kept tile (FULL: bf16 scores, LOW: E4M3 scores) staged in `st`
-  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, float c, const i32x8* q8) {
+  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, float c, const i32x8* q8) __attribute__((always_inline)) {
     constexpr bool LOW = decltype(low_tag)::value;
     f32x16 s[2] = {f32x16{}, f32x16{}};
     if constexpr (LOW) scores_fp8(st, s, q8);
@@ -364,51 +423,97 @@ void k3_attn(AttnArgs a) {
     pv(st);
   };
   // pooled keys of a chunk of 64 skipped-candidate blocks: scores only
-  auto skip_scores = [&](int t, const unsigned char* st) {
+  auto skip_scores = [&](int t, const unsigned char* st) __attribute__((always_inline)) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
     scores_bf16(st, s);
     scores_bf16(st + R1, s);   // low half of kbar
-    // bias log2(n_J) for the row's skipped blocks, -inf for the others
-    const int c0 = 64 * schunk[(t - nF) >> 1];
+    // bias log2(n_J) for the row's skipped blocks, -inf for the others.  Key
+    // 32b + 8(r/4) + 4lh + r%4 of the chunk is bit 32b + 8(r/4) + r%4 of the
+    // chunk's mask shifted right by 4lh.
+    const int ci = (t - nF) >> 1;
+    const uint64_t msk = smask[ci] >> (4 * lh);
+    const uint32_t mw[2] = {static_cast<uint32_t>(msk), static_cast<uint32_t>(msk >> 32)};
+    // position of the ragged last block inside this lane's view of the chunk
+    // (only the chunk holding block Nk - 1 can match)
+    const int lastpos = dm.Nk - 1 - 64 * schunk[ci] - 4 * lh;
+    const float lglast = __log2f(static_cast<float>(dm.N - (dm.Nk - 1) * 64));
     float tmax = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; b++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int J = c0 + 32 * b + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const bool sk = J < dm.Nk && stier[J] == TATTN_SKIP;
-        const float lg = J == dm.Nk - 1 ? __log2f(static_cast<float>(dm.N - J * 64)) : 6.0f;
+        const int pos = 8 * (r >> 2) + (r & 3);
+        const bool sk = (mw[b] >> pos) & 1u;
+        const float lg = 32 * b + pos == lastpos ? lglast : 6.0f;
         s[b][r] = sk ? __builtin_fmaf(s[b][r], cF, lg) : -INFINITY;
         tmax = __builtin_fmaxf(tmax, s[b][r]);
       }
     softmax(s, 1.0f, tmax);
   };
 
-  // ---- the step loop, in phases (FULL, LOW, then skip chunks as score / P.V
-  // pairs).  Step t computes from stage t & 1 while step t+1's DMA fills the
-  // other stage; the explicit vmcnt(0) + barrier publishes it.
-  auto stage = [&](int t) { return st0 + (t & 1) * STAGE; };
-  auto next = [&](int t) {
-    wait_vm0();
-    __builtin_amdgcn_s_barrier();
+  // ---- the step loop, in phases (FULL, skip chunks as score / P.V pairs, then
+  // LOW).  Step t computes from stage t & 1 while step t+1's DMA fills the
+  // other stage; the explicit vmcnt(0) + barrier publishes it.  The parity is
+  // a compile-time tag, so each stage is a distinct array at every access.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  float cA = 0.0f, cB = 0.0f;   // per-stage score scale
+  auto stg = [&](auto p) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (decltype(p)::value) return stB;
+    else return stA;
   };
-  float cst[2] = {0.0f, 0.0f};
-  if (nSteps > 0) issue(0, stage(0), cst[0]);
+  auto scl = [&](auto p) __attribute__((always_inline)) -> float& {
+    if constexpr (decltype(p)::value) return cB;
+    else return cA;
+  };
+  auto flip = [](auto p) { return std::integral_constant<int, 1 - decltype(p)::value>{}; };
+  auto next = [&]() __attribute__((always_inline)) {
+    wait_vm0_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    refresh();
+  };
+  using KAll = std::integral_constant<int, 15>;
+  using KAfterFull = std::integral_constant<int, (1 << kFull) | (1 << kSkipS) | (1 << kLow)>;
+  using KSkipS = std::integral_constant<int, 1 << kSkipS>;
+  using KSkipPV = std::integral_constant<int, 1 << kSkipPV>;
+  using KAfterSkip = std::integral_constant<int, (1 << kSkipS) | (1 << kLow)>;
+  using KLow = std::integral_constant<int, 1 << kLow>;
+  if (nSteps > 0) issue(KAll{}, 0, stA, cA);
   wait_vm0();
   __syncthreads();
   int t = 0;
-  for (; t < nF; t++) {
-    if (t + 1 < nSteps) issue(t + 1, stage(t + 1), cst[(t + 1) & 1]);
-    kept_step(std::false_type{}, t, stage(t), cst[t & 1], nullptr);
-    next(t);
-  }
-  for (; t < tLow; t += 2) {
-    issue(t + 1, stage(t + 1), cst[(t + 1) & 1]);
-    skip_scores(t, stage(t));
-    next(t);
-    if (t + 2 < nSteps) issue(t + 2, stage(t + 2), cst[t & 1]);
-    pv(stage(t + 1));
-    next(t + 1);
+  // a phase of single steps [t, end): two copies of the body, one per parity
+  auto run_phase = [&](int end, auto body) __attribute__((always_inline)) {
+    while (t < end) {
+      if ((t & 1) == 0) {
+        body(P0{}, t);
+        if (++t == end) break;
+      }
+      body(P1{}, t);
+      ++t;
+    }
+  };
+  run_phase(nF, [&](auto p, int tt) __attribute__((always_inline)) {
+    if (tt + 1 < nSteps) issue(KAfterFull{}, tt + 1, stg(flip(p)), scl(flip(p)));
+    kept_step(std::false_type{}, tt, stg(p), scl(p), nullptr);
+    next();
+  });
+  // skip pairs keep the parity of their first step
+  auto skip_pairs = [&](auto p) __attribute__((always_inline)) {
+    for (; t < tLow; t += 2) {
+      issue(KSkipPV{}, t + 1, stg(flip(p)), scl(flip(p)));
+      skip_scores(t, stg(p));
+      next();
+      if (t + 2 < nSteps) issue(KAfterSkip{}, t + 2, stg(p), scl(p));
+      pv(stg(flip(p)));
+      next();
+    }
+  };
+  if (t < tLow) {
+    if (t & 1) skip_pairs(P1{});
+    else skip_pairs(P0{});
   }
   if (t < nSteps) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
                       // fp8 instruction i = bf16 chunks 4i..4i+3)
@@ -429,11 +534,11 @@ void k3_attn(AttnArgs a) {
         q8reg[i][2 * cc + 1] = hi;
       }
     }
-    for (; t < nSteps; t++) {
-      if (t + 1 < nSteps) issue(t + 1, stage(t + 1), cst[(t + 1) & 1]);
-      kept_step(std::true_type{}, t, stage(t), cst[t & 1], q8reg);
-      next(t);
-    }
+    run_phase(nSteps, [&](auto p, int tt) __attribute__((always_inline)) {
+      if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
+      kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
+      next();
+    });
   }
 
   // ---- epilogue: O = acc / l

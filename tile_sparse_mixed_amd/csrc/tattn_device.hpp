@@ -101,4 +101,28 @@ __device__ inline int wave_sum_i(int v) {
   return v;
 }
 
+// Register values made opaque to the optimiser: nothing is hoisted, folded or
+// fused across this point.  Each statement holds one real s_nop because the
+// compiler's hazard recognizer counts an inline asm statement as one wait
+// state: an empty statement placed between an MFMA and a read of its result
+// would make it skip nops that the hardware needs.
+template <class A>
+__device__ inline void opaque(A& a) { __asm__ volatile("s_nop 0" : "+v"(a)); }
+template <class A, class B>
+__device__ inline void opaque(A& a, B& b) { __asm__ volatile("s_nop 0" : "+v"(a), "+v"(b)); }
+template <class A, class B, class C, class E>
+__device__ inline void opaque(A& a, B& b, C& c, E& e) {
+  __asm__ volatile("s_nop 0" : "+v"(a), "+v"(b), "+v"(c), "+v"(e));
+}
+template <int N>
+__device__ inline void opaque_arr(int (&x)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "opaque_arr: 1, 2, 4 or 8 registers");
+  if constexpr (N == 1) opaque(x[0]);
+  else if constexpr (N == 2) opaque(x[0], x[1]);
+  else if constexpr (N == 4) opaque(x[0], x[1], x[2], x[3]);
+  else
+    __asm__ volatile("s_nop 0" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                     "+v"(x[6]), "+v"(x[7]));
+}
+
 }  // namespace tattn
