@@ -192,3 +192,42 @@ def test_unit_values_give_unit_output():
             p.set_tiers(t)
         out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
         assert np.max(np.abs(out - 1.0)) < 1e-3, (mode, np.max(np.abs(out - 1.0)))
+
+
+def _rank_ambiguous_rows(p, k):
+    """Rows whose k-th and (k+1)-th largest p are equal to rounding: which of
+    them is kept is then a tie either side may break."""
+    if k <= 0 or k >= p.shape[1]:
+        return np.zeros(p.shape[0], bool)
+    s = -np.sort(-p, axis=1)
+    return np.abs(s[:, k - 1] - s[:, k]) <= 1e-12 * s[:, k - 1]
+
+
+@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged"])
+def test_adaptive_mode(name):
+    """Entropy-adaptive mode: k_h and r_h per head, rank tiers (top ceil(full_frac
+    k_h) FULL, the rest of the top k_h LOW), lists, and the output under them."""
+    import tile_sparse_mixed_amd as tsm
+    cfg = SMALL[name].with_(mode=1)
+    g, dev = device_inputs(cfg)
+    oc = OracleCfg(cfg)
+    p = gpu_plan(dev, cfg)
+    kh, rh = p.kh()
+    tiers = p.tiers()
+    lists, counts = p.lists()
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    nk = cfg.n_kblocks
+    for h in range(cfg.heads):
+        o = oracle_head(g, 0, h, oc)
+        assert abs(rh[h] - o["r_h"]) <= 1e-12 * o["r_h"], (name, h, rh[h], o["r_h"])
+        near_int = abs(o["r_h"] * nk - round(o["r_h"] * nk)) <= 1e-9
+        assert kh[h] == o["k_h"] or near_int, (name, h, kh[h], o["k_h"])
+        if kh[h] == o["k_h"]:
+            nfull = int(np.ceil(oc.full_frac * o["k_h"]))
+            amb = _rank_ambiguous_rows(o["p"], o["k_h"]) | _rank_ambiguous_rows(o["p"], nfull)
+            assert np.array_equal(tiers[0, h][~amb], o["tiers"][~amb]), (name, h)
+        li, co = T.build_lists(tiers[0, h])
+        assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), (name, h)
+        oe = oracle_head(g, 0, h, oc, mode=3, external=tiers[0, h])
+        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], oe, cfg.block_q, cfg.block_k)
+        _compare(out[0, h], ref, 1e-2, 1e-3, f"{name} adaptive h{h} (k_h {kh[h]})")
