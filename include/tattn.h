@@ -74,7 +74,7 @@ typedef enum { TATTN_BF16 = 0, TATTN_FP32 = 1 } tattn_dtype;
 
 typedef struct {
   int32_t batch, heads, seq_len, head_dim; /* head_dim in {64, 128}                          */
-  int32_t block_q, block_k;                /* (64, 64) or (128, 64)                          */
+  int32_t block_q, block_k;                /* block_q 64 or 128; block_k 64 or 16            */
   float tau_hi, tau_lo;                    /* 0 <= tau_lo <= tau_hi, finite                  */
   int32_t top_k;                           /* 0 = off, else 1..ceil(seq_len/block_k)         */
   int32_t mode;                            /* tattn_mode                                     */

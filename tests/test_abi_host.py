@@ -52,7 +52,8 @@ def test_valid_configs(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -1), (dict(heads=-1), -1), (dict(seq_len=0), -1),
-    (dict(head_dim=96), -2), (dict(block_q=32), -2), (dict(block_k=16), -2),
+    (dict(head_dim=96), -2), (dict(block_q=32), -2), (dict(block_k=32), -2),
+    (dict(block_k=16, strides=(40 * 32760 * 128 * 4096, 32760 * 128 * 4096, 128 * 4096)), -2),
     (dict(tau_hi=0.001, tau_lo=0.01), -1), (dict(tau_lo=-0.1), -1), (dict(tau_hi=float("inf")), -1),
     (dict(top_k=-1), -1), (dict(top_k=513), -1), (dict(mode=7), -1),
     (dict(mode="adaptive", keep_min=0.6, keep_max=0.5), -1), (dict(mode="adaptive", full_frac=0.0), -1),

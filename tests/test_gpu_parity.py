@@ -22,6 +22,9 @@ SMALL = {
     "ragged128": CONFIGS[3].with_(grid=(2, 10, 50), heads=3),          # N=1000: Nq=8 (last 104), Nk=16 (last 40)
     "ragged64x64": CONFIGS[2].with_(grid=(3, 7, 9), heads=2, block_q=64, head_dim=128),   # N=189
     "d64_ragged": CONFIGS[2].with_(grid=(5, 9, 13), heads=2),         # N=585
+    # 64q x 16k tiles: FULL / LOW steps gather four key blocks
+    "fine64x16": CONFIGS[5].with_(grid=(2, 10, 50), heads=2, mode=0),  # N=1000: Nq=16 (last 40), Nk=63 (last 8)
+    "fine_d64": CONFIGS[2].with_(grid=(5, 9, 13), heads=2, block_q=64, block_k=16),   # N=585: Nk=37 (last 9)
 }
 
 
@@ -203,7 +206,7 @@ def _rank_ambiguous_rows(p, k):
     return np.abs(s[:, k - 1] - s[:, k]) <= 1e-12 * s[:, k - 1]
 
 
-@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged"])
+@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged", "fine64x16", "fine_d64"])
 def test_adaptive_mode(name):
     """Entropy-adaptive mode: k_h and r_h per head, rank tiers (top ceil(full_frac
     k_h) FULL, the rest of the top k_h LOW), lists, and the output under them."""

@@ -11,8 +11,9 @@
 //                    the last block also zeroes the chunk's columns past Nk,
 //   sk_J, sv_J       amax/448 (1 for an all-zero block),
 //   k8               E4M3 codes of K_J, row-major with k8_pos d order,
-//   vt               V_J as fp16, transposed ([d][key]) in the vt_pos key order
-//                    the fused kernel's P.V uses,
+//   vt               V_J as fp16, transposed ([d][key]) in the key order the
+//                    fused kernel's P.V uses (vt_pos for 64-key blocks, vt16_pos
+//                    for 16-key blocks, which the kernel gathers four at a time),
 //   vlow             the low tier's V operand, fl16(fl32(decode(E4M3(v * inv)) * sv)),
 //                    in the same transposed layout.
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
@@ -94,7 +95,8 @@ __device__ void load_block(const uint16_t* __restrict__ base, int64_t sn, int ro
 
 template <int D, int BK>
 __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
-  static_assert(BK == kTile, "key blocks are 64 keys");
+  static_assert(BK == 64 || BK == 16, "key blocks are 64 or 16 keys");
+  constexpr int QR = BK / 8;   // 16-byte chunks per stored row of BK keys
   using BL = BlockLoad<D, BK>;
   __shared__ double red[BL::RT * D];
   __shared__ float fred[kThreads / 64];
@@ -170,20 +172,17 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   amax = block_max(amax, fred);   // contains the barrier that publishes tileT
   const float inv = inv448(amax);
   if (t == 0) *sv = scale448(amax);
-  // vt (fp16): D rows of 64 keys (128 bytes) = 8 chunks of 8 elements; element e of
-  // row d holds key with vt_pos(key) == e.
-  for (int u = t; u < D * 8; u += kThreads) {
-    const int d = u >> 3, q = u & 7;
+  // vt (fp16): D rows of BK keys = QR chunks of 8 elements; element e of row d
+  // holds key vt_key<BK>(e).
+  for (int u = t; u < D * QR; u += kThreads) {
+    const int d = u / QR, q = u % QR;
     uint32_t w[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; e2++) {
       uint32_t lohi[2];
 #pragma unroll
       for (int z = 0; z < 2; z++) {
-        const int e = q * 8 + e2 * 2 + z;           // element index in the row
-        // invert vt_pos: e = (2(p/8) + hh)*8 + p%8
-        const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
-        const int key = 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
+        const int key = vt_key<BK>(q * 8 + e2 * 2 + z);
         // bf16 -> fp16 is exact for |v| in [2^-14, 65504]; smaller values round
         lohi[z] = f32_to_f16(bf16_to_f32(tileT[key * D + d]));
       }
@@ -194,17 +193,15 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   // vlow: same layout as vt; element = fl16(fl32(decode(code)) * sv) of the E4M3 code
   // of v * inv (the hardware converter decodes exactly).
   const float svf = scale448(amax);
-  for (int u = t; u < D * 8; u += kThreads) {
-    const int d = u >> 3, q = u & 7;
+  for (int u = t; u < D * QR; u += kThreads) {
+    const int d = u / QR, q = u % QR;
     uint32_t w[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; e2++) {
       float f[2];
 #pragma unroll
       for (int z = 0; z < 2; z++) {
-        const int e = q * 8 + e2 * 2 + z;
-        const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
-        const int key = 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
+        const int key = vt_key<BK>(q * 8 + e2 * 2 + z);
         f[z] = bf16_to_f32(tileT[key * D + d]) * inv;
       }
       const int code2 = cvt_fp8x2<false>(f[0], f[1], 0);
@@ -246,7 +243,10 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
 template <int D>
 hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
   const Dims& d = a.d;
-  hipLaunchKernelGGL((k1_kv<D, 64>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  if (d.Bk == 64)
+    hipLaunchKernelGGL((k1_kv<D, 64>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_kv<D, 16>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d.Bq == 128)

@@ -20,6 +20,10 @@
 //   SKIP_PV   the same chunk's block means vbar_J (fp16, transposed) for P.V.
 // Skipped blocks are visited as whole chunks of 64 (contiguous operands),
 // masked to the row's SKIP set; chunks with no skipped block are not visited.
+// With 16-key blocks ("FG-Attn": M x N tiles with a small N) a FULL or LOW
+// step gathers up to four consecutive entries of the row's list into one
+// 64-key step: K and E4M3 K rows per DMA instruction, V^T columns per lane (a
+// 16-key block keeps its within-group key order at any column group).
 //
 // Data movement: every step's operands go global -> LDS with direct
 // buffer_load_dwordx4 ... lds (no staging registers) into one of two stage
@@ -107,9 +111,17 @@ __device__ inline int offK8(int row, int ch) {                                  
   return D == 128 ? row * 128 + ((ch ^ swz128(row)) << 4) : row * 64 + ((ch ^ swz64(row)) << 4);
 }
 
-template <int D, int NW>
+// score scale of each 16-key group of a staged step (one value for 64-key blocks)
+template <int G>
+struct StepScale {
+  float c[G];
+};
+
+template <int D, int NW, int BK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
+  static_assert(BK == 64 || BK == 16, "key blocks are 64 or 16 keys");
+  constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
   constexpr int R1 = 128 * D;
   __shared__ __attribute__((aligned(1024))) unsigned char stA[STAGE];   // stage of even steps
@@ -161,7 +173,8 @@ void k3_attn(AttnArgs a) {
     if (lane == 0) snc = __popcll(bal);
   }
   __syncthreads();
-  const int nSteps = nK + 2 * snc;
+  const int sF = (nF + G - 1) / G, sL = (nL + G - 1) / G;   // FULL / LOW steps
+  const int nSteps = sF + 2 * snc + sL;
 
   const uint16_t* kin = a.k + toff;
   const unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
@@ -187,13 +200,23 @@ void k3_attn(AttnArgs a) {
 
   // step order: FULL tiles, then the skip chunks (score / P.V pairs), then LOW
   // tiles, so the bf16 Q registers are dead before the E4M3 copy is made.
-  const int nS2 = 2 * snc, tLow = nF + nS2;
+  const int nS2 = 2 * snc, tLow = sF + nS2;
   auto step_kind = [&](int t) __attribute__((always_inline)) {
-    if (t < nF) return (int)kFull;
-    if (t < tLow) return ((t - nF) & 1) ? (int)kSkipPV : (int)kSkipS;
+    if (t < sF) return (int)kFull;
+    if (t < tLow) return ((t - sF) & 1) ? (int)kSkipPV : (int)kSkipS;
     return (int)kLow;
   };
-  auto list_at = [&](int t) { return (int)slist[t < nF ? t : t - nS2]; };   // FULL or LOW step
+  // list entry of key block g of a FULL or LOW step, and the end of its list
+  auto list_idx = [&](int t, int g) { return t < sF ? G * t + g : nF + G * (t - tLow) + g; };
+  auto list_end = [&](int t) { return t < sF ? nF : nK; };
+  auto list_at = [&](int t) { return (int)slist[list_idx(t, 0)]; };
+  // the G key blocks of a step; a group past the list end repeats the first
+  // block (finite operands; its scores are masked)
+  auto step_blocks = [&](int t, int* J) __attribute__((always_inline)) {
+    const int i0 = list_idx(t, 0), e = list_end(t);
+#pragma unroll
+    for (int g = 0; g < G; g++) J[g] = __builtin_amdgcn_readfirstlane((int)slist[i0 + g < e ? i0 + g : i0]);
+  };
 
   // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
   //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
@@ -229,6 +252,29 @@ void k3_attn(AttnArgs a) {
   // one resource over this head's slab; every workspace operand is a scalar
   // sub-offset of it
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(slab, (uint32_t)SL.bytes);
+  // 16-key blocks: LDS slot (row d, chunk lane & 7) of a [D][64] 16-bit tile
+  // holds logical chunk lc = (lane & 7) ^ swz128(d), i.e. 8 keys of column
+  // group lc / 2; the lane fetches them from that group's block, stored
+  // [D][16] (32 bytes per row d), half lc & 1 of the row.
+  const int vlc = (lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1);
+  const int vgrp = vlc >> 1;
+  const int vlane = (lane >> 3) * 32 + (vlc & 1) * 16;
+  // caller's K as one resource per head for 16-key gathers: rows past N read as zero
+  const __amdgpu_buffer_rsrc_t rKh = make_rsrc(kin, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
+  // V^T rows of the step's G blocks (per-block [D][BK] layout) from `base`
+  auto load_vt16g = [&](unsigned char* reg, int base, const int* J) __attribute__((always_inline)) {
+    if constexpr (G == 1) {
+      (void)reg; (void)base; (void)J;
+    } else {
+      const int Jl = vgrp == 0 ? J[0] : vgrp == 1 ? J[1] : vgrp == 2 ? J[2] : J[3];
+      const int vo = vlane + Jl * (D * 32);
+#pragma unroll
+      for (int i = 0; i < NI16; i++) {
+        const int k = wave + NW * i;
+        dma16(rS, reg + k * 1024, vo, base + k * 256);
+      }
+    }
+  };
 
   auto load_vt16 = [&](unsigned char* reg, __amdgpu_buffer_rsrc_t r, int base) {   // [D][64] 16-bit
 #pragma unroll
@@ -239,10 +285,42 @@ void k3_attn(AttnArgs a) {
   };
   // KINDS: bit mask of the step kinds that can occur where this is called; the
   // other branches are not generated, so their address terms are not kept live.
-  auto issue = [&](auto kinds, int t, unsigned char* st, float& cst) __attribute__((always_inline)) {
+  auto issue = [&](auto kinds, int t, unsigned char* st, StepScale<G>& cst) __attribute__((always_inline)) {
     constexpr int KINDS = decltype(kinds)::value;
     const int kind = step_kind(t);
-    if ((KINDS & (1 << kFull)) && kind == kFull) {
+    if constexpr (G > 1) {
+      if (((KINDS & (1 << kFull)) && kind == kFull) || ((KINDS & (1 << kLow)) && kind == kLow)) {
+        int J[G];
+        step_blocks(t, J);
+        if (kind == kFull) {
+#pragma unroll
+          for (int i = 0; i < NI16; i++) {
+            const int k = wave + NW * i;
+            const int row0 = k * RPI;                // first stage row of the instruction
+            const int g = row0 >> 4;
+            const int Jg = g == 0 ? J[0] : g == 1 ? J[1] : g == 2 ? J[2] : J[3];
+            dma16(rKh, st + k * 1024, lk[i % NSW] + (Jg * 16 + (row0 & 15)) * (int)dm.sn * 2, 0);
+          }
+          load_vt16g(st + R1, (int)SL.vt, J);
+#pragma unroll
+          for (int g = 0; g < G; g++) cst.c[g] = cF;
+        } else {
+#pragma unroll
+          for (int i = 0; i < NI8; i++) {
+            const int k = wave + NW * i;
+            const int row0 = k * (1024 / D);         // E4M3 rows are D bytes
+            const int g = row0 >> 4;
+            const int Jg = g == 0 ? J[0] : g == 1 ? J[1] : g == 2 ? J[2] : J[3];
+            dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + (Jg * 16 + (row0 & 15)) * D);
+          }
+          load_vt16g(st + R1, (int)SL.vlow, J);
+#pragma unroll
+          for (int g = 0; g < G; g++) cst.c[g] = sq * skp[J[g]] * cF;
+        }
+        return;
+      }
+    }
+    if (G == 1 && (KINDS & (1 << kFull)) && kind == kFull) {
       const int J = list_at(t);
       // one resource per tile: rows past N read as zeros (and are masked)
       const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
@@ -255,8 +333,8 @@ void k3_attn(AttnArgs a) {
         dma16(rK, st + k * 1024, lk[i % NSW] + k * RPI * (int)dm.sn * 2, 0);
       }
       load_vt16(st + R1, rS, (int)SL.vt + J * 128 * D);
-      cst = cF;
-    } else if ((KINDS & (1 << kLow)) && kind == kLow) {
+      cst.c[0] = cF;
+    } else if (G == 1 && (KINDS & (1 << kLow)) && kind == kLow) {
       const int J = list_at(t);
 #pragma unroll
       for (int i = 0; i < NI8; i++) {
@@ -264,9 +342,9 @@ void k3_attn(AttnArgs a) {
         dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
       }
       load_vt16(st + R1, rS, (int)SL.vlow + J * 128 * D);
-      cst = sq * skp[J] * cF;
+      cst.c[0] = sq * skp[J] * cF;
     } else {
-      const int c = schunk[(t - nF) >> 1];
+      const int c = schunk[(t - sF) >> 1];
       if ((KINDS & (1 << kSkipS)) && kind == kSkipS) {
 #pragma unroll
         for (int i = 0; i < NI16; i++) {
@@ -277,7 +355,8 @@ void k3_attn(AttnArgs a) {
       } else if (KINDS & (1 << kSkipPV)) {
         load_vt16(st + R1, rS, (int)SL.vbarT + c * 128 * D);
       }
-      cst = 1.0f;
+#pragma unroll
+      for (int g = 0; g < G; g++) cst.c[g] = 1.0f;
     }
   };
 
@@ -362,7 +441,7 @@ void k3_attn(AttnArgs a) {
   };
   // ---- online softmax of x = s * c (base-2 units; tmax already scaled) into
   // the fp16 P operand, raising m when needed.
-  auto softmax = [&](f32x16* s, float c, float tmax) __attribute__((always_inline)) {
+  auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
     tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const bool need = tmax > m_run + kLazy;
     if (__ballot(need)) {
@@ -382,7 +461,7 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 8; tt++) {
         const int e = 8 * cc + tt;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c, nm));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cs.c[G == 1 ? 0 : cc], nm));
         psum += p;
         pb[cc][tt] = static_cast<_Float16>(p);
       }
@@ -412,14 +491,44 @@ void k3_attn(AttnArgs a) {
     pipeline_reads_mfma<D / 8, D / 16>();
   };
   // a kept tile (FULL: bf16 scores, LOW: E4M3 scores) staged in `st`
-  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, float c, const i32x8* q8) __attribute__((always_inline)) {
+  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q8) __attribute__((always_inline)) {
     constexpr bool LOW = decltype(low_tag)::value;
     f32x16 s[2] = {f32x16{}, f32x16{}};
     if constexpr (LOW) scores_fp8(st, s, q8);
     else scores_bf16(st, s);
-    const int J = list_at(t);
-    if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
-    softmax(s, c, row_max(s) * c);
+    if constexpr (G == 1) {
+      const int J = list_at(t);
+      if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
+      softmax(s, c, row_max(s) * c.c[0]);
+    } else {
+      // Lists are ascending, so a partial group or the ragged last block only
+      // occurs in the last step of the phase.  Register (b, r) is key
+      // 8((r >> 2) & 1) + 4lh + r % 4 of group 2b + r / 8.
+      if (t == (LOW ? nSteps - 1 : sF - 1)) {
+        const int i0 = list_idx(t, 0), e = list_end(t);
+        int lim[G];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          const int Jg = (int)slist[i0 + g < e ? i0 + g : i0];
+          lim[g] = (i0 + g >= e ? 0 : Jg == dm.Nk - 1 ? dm.N - 16 * Jg : 16) - 4 * lh;
+          opaque(lim[g]);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            if (8 * ((r >> 2) & 1) + (r & 3) >= lim[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
+        tmax = __builtin_fmaxf(tmax, m * c.c[cc]);
+      }
+      softmax(s, c, tmax);
+    }
     pv(st);
   };
   // pooled keys of a chunk of 64 skipped-candidate blocks: scores only
@@ -430,13 +539,14 @@ void k3_attn(AttnArgs a) {
     // bias log2(n_J) for the row's skipped blocks, -inf for the others.  Key
     // 32b + 8(r/4) + 4lh + r%4 of the chunk is bit 32b + 8(r/4) + r%4 of the
     // chunk's mask shifted right by 4lh.
-    const int ci = (t - nF) >> 1;
+    const int ci = (t - sF) >> 1;
     const uint64_t msk = smask[ci] >> (4 * lh);
     const uint32_t mw[2] = {static_cast<uint32_t>(msk), static_cast<uint32_t>(msk >> 32)};
     // position of the ragged last block inside this lane's view of the chunk
     // (only the chunk holding block Nk - 1 can match)
     const int lastpos = dm.Nk - 1 - 64 * schunk[ci] - 4 * lh;
-    const float lglast = __log2f(static_cast<float>(dm.N - (dm.Nk - 1) * 64));
+    const float lglast = __log2f(static_cast<float>(dm.N - (dm.Nk - 1) * BK));
+    constexpr float lgfull = BK == 64 ? 6.0f : 4.0f;   // log2(BK)
     float tmax = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; b++)
@@ -444,11 +554,14 @@ void k3_attn(AttnArgs a) {
       for (int r = 0; r < 16; r++) {
         const int pos = 8 * (r >> 2) + (r & 3);
         const bool sk = (mw[b] >> pos) & 1u;
-        const float lg = 32 * b + pos == lastpos ? lglast : 6.0f;
+        const float lg = 32 * b + pos == lastpos ? lglast : lgfull;
         s[b][r] = sk ? __builtin_fmaf(s[b][r], cF, lg) : -INFINITY;
         tmax = __builtin_fmaxf(tmax, s[b][r]);
       }
-    softmax(s, 1.0f, tmax);
+    StepScale<G> one;
+#pragma unroll
+    for (int g = 0; g < G; g++) one.c[g] = 1.0f;
+    softmax(s, one, tmax);
   };
 
   // ---- the step loop, in phases (FULL, skip chunks as score / P.V pairs, then
@@ -457,12 +570,12 @@ void k3_attn(AttnArgs a) {
   // a compile-time tag, so each stage is a distinct array at every access.
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  float cA = 0.0f, cB = 0.0f;   // per-stage score scale
+  StepScale<G> cA{}, cB{};   // per-stage score scale
   auto stg = [&](auto p) __attribute__((always_inline)) -> unsigned char* {
     if constexpr (decltype(p)::value) return stB;
     else return stA;
   };
-  auto scl = [&](auto p) __attribute__((always_inline)) -> float& {
+  auto scl = [&](auto p) __attribute__((always_inline)) -> StepScale<G>& {
     if constexpr (decltype(p)::value) return cB;
     else return cA;
   };
@@ -495,7 +608,7 @@ void k3_attn(AttnArgs a) {
       ++t;
     }
   };
-  run_phase(nF, [&](auto p, int tt) __attribute__((always_inline)) {
+  run_phase(sF, [&](auto p, int tt) __attribute__((always_inline)) {
     if (tt + 1 < nSteps) issue(KAfterFull{}, tt + 1, stg(flip(p)), scl(flip(p)));
     kept_step(std::false_type{}, tt, stg(p), scl(p), nullptr);
     next();
@@ -572,7 +685,10 @@ void k3_attn(AttnArgs a) {
 
 template <int D, int NW>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k3_attn<D, NW>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+  if (a.d.Bk == 64)
+    hipLaunchKernelGGL((k3_attn<D, NW, 64>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k3_attn<D, NW, 16>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

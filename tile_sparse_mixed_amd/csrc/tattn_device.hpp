@@ -49,6 +49,19 @@ __host__ __device__ inline int vt_pos(int key) {
   return (2 * (p >> 3) + key_h(key)) * 8 + (p & 7);
 }
 
+// Within one group of 16 keys (16g..16g+15, one P chunk of the P.V MFMA) the
+// permutation does not depend on g: vt_pos(16g + k) = 16g + vt16_pos(k), a
+// swap of key bits 2 and 3.  A 16-key block stored with this order can be
+// placed at any column group of a 64-key tile.
+__host__ __device__ inline int vt16_pos(int k) { return 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3); }
+// key whose value sits at element e of a stored row of BK keys (BK = 64 or 16)
+template <int BK>
+__host__ __device__ inline int vt_key(int e) {
+  if (BK == 16) return (e & 3) | ((e >> 1) & 4) | ((e << 1) & 8);
+  const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
+  return 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
+}
+
 // d permutation of a stored fp8 K row: byte position 64i + 32g + p holds
 // d = 64i + 16(p/8) + 8g + p%8, so that a lane (group g) reads its 32 bytes
 // for instruction i contiguously, in the order its bf16 Q registers give.

@@ -112,8 +112,9 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "head_dim, block_q and block_k must be >= 1");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(TATTN_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
-  if (c->block_k != kTile || (c->block_q != 64 && c->block_q != 128))
-    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported ((64,64) or (128,64))", c->block_q, c->block_k);
+  if ((c->block_k != 64 && c->block_k != 16) || (c->block_q != 64 && c->block_q != 128))
+    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported (block_q 64 or 128, block_k 64 or 16)", c->block_q,
+                c->block_k);
   if (c->mode < 0 || c->mode > 3) return fail(TATTN_E_INVALID, "mode %d out of range", c->mode);
   if (!std::isfinite(c->tau_hi) || !std::isfinite(c->tau_lo) || c->tau_lo < 0.0f || c->tau_lo > c->tau_hi)
     return fail(TATTN_E_INVALID, "thresholds need 0 <= tau_lo <= tau_hi (got %g, %g)", c->tau_lo, c->tau_hi);
@@ -140,6 +141,9 @@ static tattn_status validate(const tattn_config* c) {
   if (nk > kMaxNk) return fail(TATTN_E_UNSUPPORTED, "%lld key blocks exceed the limit of %d", (long long)nk, kMaxNk);
   if ((int64_t)c->batch * c->heads * nq > 0x7fffffffLL || (int64_t)c->batch * c->heads * nk > 0x7fffffffLL)
     return fail(TATTN_E_UNSUPPORTED, "problem too large for one launch");
+  // 16-key blocks address a head's K rows with 32-bit byte offsets
+  if (c->block_k == 16 && (int64_t)c->seq_len * c->stride_n * 2 > 0x7fffffffLL)
+    return fail(TATTN_E_UNSUPPORTED, "seq_len x stride_n too large for 16-key blocks");
   return ok();
 }
 
@@ -322,7 +326,7 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
   if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Dims& d = p->d;
-  const size_t tile = (size_t)kTile * d.D;
+  const size_t tile = (size_t)d.Bk * d.D;
   tattn_status st;
   std::vector<uint8_t> slab(p->L.sl.bytes);
   for (size_t bh = 0; bh < (size_t)d.BH; bh++) {
@@ -331,12 +335,12 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
     const uint8_t* k8 = slab.data() + p->L.sl.k8;
     const uint16_t* vl = reinterpret_cast<const uint16_t*>(slab.data() + p->L.sl.vlow);
     for (int J = 0; J < d.Nk; J++)
-      for (int r = 0; r < kTile && J * kTile + r < d.N; r++) {
-        const size_t n = (size_t)J * kTile + r;
+      for (int r = 0; r < d.Bk && J * d.Bk + r < d.N; r++) {
+        const size_t n = (size_t)J * d.Bk + r;
         if (host_k8)
           for (int c = 0; c < d.D; c++) host_k8[(bh * d.N + n) * d.D + c] = k8[J * tile + r * d.D + k8_pos(c)];
         if (host_vlow)
-          for (int c = 0; c < d.D; c++) host_vlow[(bh * d.N + n) * d.D + c] = vl[J * tile + c * kTile + vt_pos(r)];
+          for (int c = 0; c < d.D; c++) host_vlow[(bh * d.N + n) * d.D + c] = vl[J * tile + c * d.Bk + (d.Bk == 64 ? vt_pos(r) : vt16_pos(r))];
       }
   }
   return ok();
