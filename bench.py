@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-allfull", action="store_true", help="skip the all-full comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--gen-heads", type=int, default=0,
+                    help="generate only this many heads and tile them to the workload's head count (same shapes "
+                         "and launch; for the large workloads, whose full host-side generation takes minutes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for counter scaling)")
     return ap.parse_args()
@@ -50,15 +53,15 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic():
+def load_traffic(config_id):
     """HBM traffic of one K3 launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel source and this workload; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash() or t.get("config_id") != config_id:
         return None
     return t.get("bytes_per_launch")
 
@@ -116,23 +119,31 @@ def main():
     from synth import CONFIGS, generate
 
     cfg = CONFIGS[args.config]
-    if cfg.mode != 0:
-        print("bench.py: only threshold-mode workloads are benchmarked", file=sys.stderr)
+    if cfg.mode not in (0, 1):
+        print("bench.py: only threshold and entropy-adaptive workloads are benchmarked", file=sys.stderr)
         sys.exit(2)
+    run_mode = "adaptive" if cfg.mode == 1 else "threshold"
     print(f"[bench] generating {cfg.name}: N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim}", file=sys.stderr,
           flush=True)
-    g = generate(cfg)
-    dev = {n: torch.from_numpy(g["bits"][n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    tiled = 0 < args.gen_heads < cfg.heads
+    g = generate(cfg.with_(heads=args.gen_heads) if tiled else cfg)
+    dev = {}
+    for n in ("q", "k", "v"):
+        t = torch.from_numpy(g["bits"][n].view(np.int16)).view(torch.bfloat16).cuda()
+        if tiled:
+            t = t.index_select(1, torch.arange(cfg.heads, device="cuda") % args.gen_heads).contiguous()
+        dev[n] = t
     q, k, v = dev["q"], dev["k"], dev["v"]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def mk(mode, ws=None):
         return tsm.plan(q, k, v, block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
-                        top_k=cfg.top_k, mode=mode, workspace=ws)
+                        top_k=cfg.top_k, mode=mode, keep_min=cfg.keep_min, keep_max=cfg.keep_max,
+                        full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, workspace=ws)
 
     out = torch.empty_like(q)
-    plan = mk("threshold")
+    plan = mk(run_mode)
     tsm.forward(plan, q, k, v, out)
     torch.cuda.synchronize()
     st = plan.stats()
@@ -140,7 +151,7 @@ def main():
     ws = torch.empty_like(plan.workspace)   # the timed steps re-plan into one workspace
 
     def step():
-        p = mk("threshold", ws)
+        p = mk(run_mode, ws)
         tsm.forward(p, q, k, v, out)
         return p
 
@@ -171,7 +182,7 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    ms_plan = timed(lambda: mk("threshold", ws), args.steps)
+    ms_plan = timed(lambda: mk(run_mode, ws), args.steps)
     ms_k3 = timed(lambda: tsm.forward(plan, q, k, v, out), args.steps)
 
     ms_allfull = None
@@ -193,7 +204,7 @@ def main():
     bf16_equiv = st["flops_bf16"] + st["flops_fp8"] * PEAK_BF16 / PEAK_FP8
     achieved = bf16_equiv / (ms_k3 * 1e-3) / 1e12
     tiles = st["n_full"] + st["n_low"] + st["n_skip"]
-    traffic = load_traffic()
+    traffic = load_traffic(args.config)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -207,10 +218,13 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16+fp8 (fp32 accumulate)", "data": "synthetic",
+        "dtype": "bf16+fp8 (fp32 accumulate)",
+        "data": "synthetic" + (f" ({args.gen_heads} generated heads tiled to {cfg.heads})" if tiled else ""),
         "config": {"workload": f"{cfg.name}: {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]}={cfg.seq_len} tokens, "
                                f"{cfg.heads} heads, d={cfg.head_dim}, tiles {cfg.block_q}q x {cfg.block_k}k, "
-                               f"tau_hi={cfg.tau_hi}, tau_lo={cfg.tau_lo}",
+                               + (f"tau_hi={cfg.tau_hi}, tau_lo={cfg.tau_lo}" if run_mode == "threshold" else
+                                  f"entropy-adaptive k_h (keep {cfg.keep_min}-{cfg.keep_max}, FULL share "
+                                  f"{cfg.full_frac}, {cfg.entropy_samples} sampled query blocks)"),
                    "batch": cfg.batch, "seq_len": cfg.seq_len, "heads": cfg.heads, "head_dim": cfg.head_dim},
         "kernel_ms": {"plan_k1_k2": round(ms_plan, 4), "forward_k3": round(ms_k3, 4),
                       "forward_k3_all_full": None if ms_allfull is None else round(ms_allfull, 4)},

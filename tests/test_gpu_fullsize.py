@@ -74,3 +74,49 @@ def test_full_size_sampled(name):
             excess = d - np.abs(ref[r0:r1]) * 2.0 ** -9
             _log(f"  h{h} block {I}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
             assert excess.max() <= 1e-2 and d.mean() <= 1.5e-3, (name, h, I, d.max(), d.mean())
+
+
+def test_full_size_fine_adaptive():
+    """The fine-grained head-adaptive workload: 32760 tokens x 40 heads, 64q x 16k
+    tiles, k_h from the entropy of p on 256 sampled query blocks per head."""
+    import tile_sparse_mixed_amd as tsm
+    import torch
+    cfg = CONFIGS[5]
+    gen_heads, sample_heads = 3, [0, 20, 38]
+    _log(f"[full fine_adaptive] N={cfg.seq_len} H={cfg.heads} tile={cfg.block_q}x{cfg.block_k}")
+    g = generate(cfg.with_(heads=gen_heads))
+    dev = _device_tiled(g["bits"], cfg.heads)
+    p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, mode="adaptive",
+                 keep_min=cfg.keep_min, keep_max=cfg.keep_max, full_frac=cfg.full_frac,
+                 entropy_samples=cfg.entropy_samples)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    kh, rh = p.kh()
+    tiers = p.tiers()
+    oc = OracleCfg(cfg)
+    nq, nk = cfg.n_qblocks, cfg.n_kblocks
+    rows = [0, nq // 2 + 3, nq - 1]
+    for h in sample_heads:
+        src = h % gen_heads
+        q, k, v = g["q"][0, src], g["k"][0, src], g["v"][0, src]
+        o = T.oracle_plan(q, k, v, oc)
+        assert abs(rh[h] - o["r_h"]) <= 1e-12 * o["r_h"], (h, rh[h], o["r_h"])
+        if kh[h] != o["k_h"]:
+            assert abs(o["r_h"] * nk - round(o["r_h"] * nk)) <= 1e-9, (h, kh[h], o["k_h"])
+        else:
+            nfull = int(np.ceil(oc.full_frac * o["k_h"]))
+            srt = -np.sort(-o["p"], axis=1)
+            amb = np.zeros(nq, bool)
+            for kk in (o["k_h"], nfull):
+                if 0 < kk < nk:
+                    amb |= np.abs(srt[:, kk - 1] - srt[:, kk]) <= 1e-12 * srt[:, kk - 1]
+            assert np.array_equal(tiers[0, h][~amb], o["tiers"][~amb]), h
+        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
+        ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k, rows=rows)
+        got = out[0, h].float().cpu().numpy()
+        for I in rows:
+            r0, r1 = I * cfg.block_q, min(cfg.seq_len, (I + 1) * cfg.block_q)
+            d = np.abs(got[r0:r1] - ref[r0:r1])
+            excess = d - np.abs(ref[r0:r1]) * 2.0 ** -9
+            _log(f"  h{h} (k_h {kh[h]}) block {I}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}")
+            assert excess.max() <= 1e-2 and d.mean() <= 1.5e-3, (h, I, d.max(), d.mean())
