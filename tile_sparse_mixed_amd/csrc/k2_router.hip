@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
 struct Red {
   double d[kWaves];
   int i[kWaves * 4];
+  int hist[256];   // radix-select digit histogram
+  int sel[2];      // selected digit, count of candidates above it
 };
 
 __device__ double block_max_d(double v, Red& r) {
@@ -117,15 +119,58 @@ __device__ int block_sum_i(int v, Red& r) {
   return s;
 }
 
-// Bits of the k-th largest value (k >= 1) among the non-negative doubles
-// pv[0..n): the largest x with #{p >= x} >= k, built from the top bit down.
+// Bits of the k-th largest value (1 <= k <= n) among the non-negative doubles
+// pv[0..n).  Non-negative doubles order like their bit patterns, so this is a
+// radix select from the top byte down: per byte, a histogram of that byte over
+// the values that match the bytes chosen so far, then the byte at which the
+// count from the top reaches the remaining rank.  (Measured against 11-bit
+// digits: 8-bit digits are faster; fewer bins to clear and scan per pass
+// outweigh the contention of the top byte.)
 __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
-  uint64_t prefix = 0;
-  for (int bit = 62; bit >= 0; bit--) {
-    const uint64_t cand = prefix | (1ull << bit);
-    int c = 0;
-    for (int J = threadIdx.x; J < n; J += kThreads) c += (__double_as_longlong(pv[J]) >= (long long)cand);
-    if (block_sum_i(c, r) >= k) prefix = cand;
+  uint64_t prefix = 0, mask = 0;
+  int kk = k;   // rank of the wanted value among the values matching `prefix`
+  const int lane = threadIdx.x & 63;
+  for (int sh = 56; sh >= 0; sh -= 8) {
+    constexpr int bins = 256;
+    for (int i = threadIdx.x; i < bins; i += kThreads) r.hist[i] = 0;
+    __syncthreads();
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
+      if ((b & mask) == prefix) atomicAdd(&r.hist[(b >> sh) & (bins - 1)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l owns digits 255 - 4l .. 252 - 4l (descending);
+      // inclusive scan of the lane totals from the top digit down
+      const int w = bins >> 6;
+      int tot = 0;
+      for (int j = 0; j < w; j++) tot += r.hist[bins - 1 - lane * w - j];
+      int cum = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int up = __shfl_up(cum, o, 64);
+        if (lane >= o) cum += up;
+      }
+      const uint64_t hit = __ballot(cum >= kk);
+      const int L = __ffsll((long long)hit) - 1;   // first lane whose range reaches kk
+      if (lane == L) {
+        int above = cum - tot;
+        for (int j = 0; j < w; j++) {
+          const int c = r.hist[bins - 1 - lane * w - j];
+          if (above + c >= kk) {
+            r.sel[0] = bins - 1 - lane * w - j;
+            r.sel[1] = above;
+            break;
+          }
+          above += c;
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)r.sel[0] << sh;
+    mask |= (uint64_t)(bins - 1) << sh;
+    kk -= r.sel[1];
+    __syncthreads();
   }
   return prefix;
 }
@@ -218,15 +263,19 @@ __device__ void compact_row(const unsigned char* tr, int n, int16_t* list, int* 
 
 enum { K2B_TIERS = 0, K2B_ENTROPY = 1 };
 
+inline size_t k2b_lds_bytes(int nk) { return ((size_t)nk * 10 + 15) / 16 * 16; }
+
 // One workgroup per (b, h, I) (tiers) or per (b, h, sampled row s) (entropy).
 template <int WHAT>
 __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
-  __shared__ double pv[kRouterMaxNk];
-  __shared__ unsigned char tr[kRouterMaxNk];
-  __shared__ unsigned char keep[kRouterMaxNk];
+  // row buffers sized by the launch for this Nk: p (f64), tiers, keep marks
+  extern __shared__ __attribute__((aligned(16))) unsigned char k2b_dyn[];
   __shared__ Red r;
   const Dims& dm = a.d;
   const int n = dm.Nk;
+  double* pv = reinterpret_cast<double*>(k2b_dyn);
+  unsigned char* tr = k2b_dyn + (size_t)n * 8;
+  unsigned char* keep = tr + n;
   int bh, I, s = 0;
   if (WHAT == K2B_ENTROPY) {
     const int S = min(a.samples, dm.Nq);
@@ -283,8 +332,11 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
   } else {  // ADAPTIVE
     const int S2 = min(a.samples, dm.Nq);
     const double* ent = reinterpret_cast<const double*>(a.ws + a.L.ent) + (int64_t)bh * S2;
-    double hs = 0.0;
-    for (int i = 0; i < S2; i++) hs += ent[i];   // same order in every workgroup of this head
+    // block-parallel sum of the head's sampled entropies: a fixed reduction
+    // tree, so every workgroup of this head gets the same k_h
+    double hv = 0.0;
+    for (int i = threadIdx.x; i < S2; i += kThreads) hv += ent[i];
+    const double hs = block_sum_d(hv, r);
     double rr = exp(hs / S2) / n;
     rr = fmin(fmax(rr, (double)a.keep_min), (double)a.keep_max);
     const int kh = (int)ceil(rr * n);
@@ -347,11 +399,11 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   }
   if (a.mode == TATTN_MODE_ADAPTIVE) {
     const int S = min(a.samples, d.Nq);
-    hipLaunchKernelGGL((k2b_rows<K2B_ENTROPY>), dim3(d.BH * S), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k2b_rows<K2B_ENTROPY>), dim3(d.BH * S), dim3(kThreads), k2b_lds_bytes(d.Nk), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k2b_rows<K2B_TIERS>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k2b_rows<K2B_TIERS>), dim3(d.BH * d.Nq), dim3(kThreads), k2b_lds_bytes(d.Nk), s, a);
   return hipGetLastError();
 }
 
