@@ -1,6 +1,6 @@
 // K2: block router, tier assignment and tile-list compaction.
 //
-// K2a  S_IJ = <qbar_I, kbar_J> / sqrt(d) + ln n_J in float64, tiled 32 query
+// K2a  S_IJ = <qbar_I, kbar_J> / sqrt(d) + ln n_J in float64, tiled 64 query
 //      blocks x 64 key blocks per workgroup through LDS ("APT": attention
 //      probability of the block as the importance metric; the ln n_J term
 //      weights a key block by its real size).
@@ -29,53 +29,63 @@ constexpr int kRouterMaxNk = 4096;
 // ------------------------------------------------------------------ K2a
 template <int D>
 __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
-  __shared__ float qT[D][32];   // qbar transposed [d][row]
-  __shared__ float kT[D][64];   // kbar transposed [d][J]
+  // 64 query blocks x 64 key blocks per workgroup; each thread owns a 4 x 4
+  // block of S.  The operands pass through LDS as float64, 16 values of d at
+  // a time, so the inner loop is 4 LDS reads per 16 FMAs and no conversions.
+  constexpr int DC = 16;
+  __shared__ __attribute__((aligned(16))) double qs[DC][64];   // qbar chunk, [d][row]
+  __shared__ __attribute__((aligned(16))) double ks[DC][64];   // kbar chunk, [d][J]
   const Dims& dm = a.d;
   const int bh = blockIdx.z;
-  const int I0 = blockIdx.y * 32, J0 = blockIdx.x * 64;
+  const int I0 = blockIdx.y * 64, J0 = blockIdx.x * 64;
   const float* qbar = reinterpret_cast<const float*>(a.ws + a.L.qbar) + (int64_t)bh * dm.Nq * D;
   const float* kbar = reinterpret_cast<const float*>(a.ws + a.L.kbar) + (int64_t)bh * dm.Nk * D;
   const int t = threadIdx.x;
-  for (int u = t; u < 32 * D; u += kThreads) {
-    const int r = u / D, c = u % D;
-    qT[c][r] = (I0 + r < dm.Nq) ? qbar[(int64_t)(I0 + r) * D + c] : 0.0f;
-  }
-  for (int u = t; u < 64 * D; u += kThreads) {
-    const int r = u / D, c = u % D;
-    kT[c][r] = (J0 + r < dm.Nk) ? kbar[(int64_t)(J0 + r) * D + c] : 0.0f;
-  }
-  __syncthreads();
-  const int rg = t / 16, jg = t % 16;   // rows 2rg, 2rg+1; key blocks 4jg..4jg+3
-  double acc[2][4];
+  const int rg = t / 16, jg = t % 16;   // rows 4rg..4rg+3, key blocks 4jg..4jg+3
+  double acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = 0.0;
-#pragma unroll 8
-  for (int c = 0; c < D; c++) {
-    const float2 qv = *reinterpret_cast<const float2*>(&qT[c][2 * rg]);
-    const float4 kv = *reinterpret_cast<const float4*>(&kT[c][4 * jg]);
-    const double q0 = qv.x, q1 = qv.y;
-    const double k[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      acc[0][j] = fma(q0, k[j], acc[0][j]);
-      acc[1][j] = fma(q1, k[j], acc[1][j]);
+  for (int c0 = 0; c0 < D; c0 += DC) {
+    // 64 rows x 16 d of each operand: thread t loads row t / 4, d 4(t % 4) .. +3
+    {
+      const int r = t >> 2, c = 4 * (t & 3);
+      float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (I0 + r < dm.Nq) qv = *reinterpret_cast<const float4*>(qbar + (int64_t)(I0 + r) * D + c0 + c);
+      if (J0 + r < dm.Nk) kv = *reinterpret_cast<const float4*>(kbar + (int64_t)(J0 + r) * D + c0 + c);
+      qs[c][r] = qv.x; qs[c + 1][r] = qv.y; qs[c + 2][r] = qv.z; qs[c + 3][r] = qv.w;
+      ks[c][r] = kv.x; ks[c + 1][r] = kv.y; ks[c + 2][r] = kv.z; ks[c + 3][r] = kv.w;
     }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < DC; c++) {
+      const double2 q01 = *reinterpret_cast<const double2*>(&qs[c][4 * rg]);
+      const double2 q23 = *reinterpret_cast<const double2*>(&qs[c][4 * rg + 2]);
+      const double2 k01 = *reinterpret_cast<const double2*>(&ks[c][4 * jg]);
+      const double2 k23 = *reinterpret_cast<const double2*>(&ks[c][4 * jg + 2]);
+      const double q[4] = {q01.x, q01.y, q23.x, q23.y};
+      const double k[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = fma(q[i], k[j], acc[i][j]);
+    }
+    __syncthreads();
   }
   double* S = reinterpret_cast<double*>(a.ws + a.L.S) + (int64_t)bh * dm.Nq * dm.Nk;
-  const double sd = sqrt(static_cast<double>(D));
+  const double isd = 1.0 / sqrt(static_cast<double>(D));
+  const double lg_full = log(static_cast<double>(dm.Bk));
+  const double lg_last = log(static_cast<double>(dm.N - (dm.Nk - 1) * dm.Bk));
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int I = I0 + 2 * rg + i;
+  for (int i = 0; i < 4; i++) {
+    const int I = I0 + 4 * rg + i;
     if (I >= dm.Nq) continue;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int J = J0 + 4 * jg + j;
       if (J >= dm.Nk) continue;
-      const int nJ = min(dm.Bk, dm.N - J * dm.Bk);
-      S[(int64_t)I * dm.Nk + J] = acc[i][j] / sd + log(static_cast<double>(nJ));
+      S[(int64_t)I * dm.Nk + J] = fma(acc[i][j], isd, J == dm.Nk - 1 ? lg_last : lg_full);
     }
   }
 }
@@ -389,7 +399,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   const Dims& d = a.d;
   if (d.Nk > kRouterMaxNk) return hipErrorInvalidValue;
   if (a.mode != TATTN_MODE_ALL_FULL) {
-    dim3 grid((d.Nk + 63) / 64, (d.Nq + 31) / 32, d.BH);
+    dim3 grid((d.Nk + 63) / 64, (d.Nq + 63) / 64, d.BH);
     if (d.D == 128)
       hipLaunchKernelGGL((k2a_scores<128>), grid, dim3(kThreads), 0, s, a);
     else
