@@ -455,16 +455,22 @@ void k3_attn(AttnArgs a) {
       m_run = mn;
     }
     const float nm = -m_run;
-    float psum = 0.0f;
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
 #pragma unroll
       for (int tt = 0; tt < 8; tt++) {
         const int e = 8 * cc + tt;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cs.c[G == 1 ? 0 : cc], nm));
-        psum += p;
-        pb[cc][tt] = static_cast<_Float16>(p);
+        pb[cc][tt] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cs.c[G == 1 ? 0 : cc], nm)));
       }
+    // l accumulates the fp16 P values the P.V MFMA multiplies, two per
+    // v_dot2_f32_f16 (fp32 accumulation)
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    float psum = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) psum = __builtin_amdgcn_fdot2(h2{pb[cc][2 * j], pb[cc][2 * j + 1]}, one2, psum, false);
     l_run += psum;
   };
   auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
