@@ -147,6 +147,21 @@ def main():
     tsm.forward(plan, q, k, v, out)
     torch.cuda.synchronize()
     st = plan.stats()
+    # tiles whose router probability lies within 1e-5 (relative) of a threshold:
+    # the band where a tier may legitimately differ between implementations
+    n_band = None
+    if run_mode == "threshold":
+        pr = plan.tiers(with_p=True)[1]
+        n_band = int(sum(np.count_nonzero(np.abs(pr - np.float32(t)) <= 1e-5 * np.float32(t))
+                         for t in (cfg.tau_hi, cfg.tau_lo)))
+        del pr
+    kh_summary = None
+    if run_mode == "adaptive":   # k_h per head: min / median / max and a 10-bin histogram
+        kh = plan.kh()[0]
+        hist, edges = np.histogram(kh, bins=10)
+        kh_summary = {"k_h_min": int(kh.min()), "k_h_median": float(np.median(kh)), "k_h_max": int(kh.max()),
+                      "of_n_kblocks": cfg.n_kblocks, "histogram": hist.tolist(),
+                      "bin_edges": [round(float(e), 1) for e in edges]}
 
     ws = torch.empty_like(plan.workspace)   # the timed steps re-plan into one workspace
 
@@ -171,26 +186,40 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # per-stage times on the same stream: plan alone, forward alone
+    # per-stage times on the same stream: plan alone, forward alone.  One event
+    # per repetition, no synchronisation in between: mean, median and min.
     def timed(fn, reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
+        ev[0].record(stream)
+        for i in range(reps):
             fn()
-        b.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+        return ev[0].elapsed_time(ev[-1]) / reps, per[len(per) // 2], per[0]
 
-    ms_plan = timed(lambda: mk(run_mode, ws), args.steps)
-    ms_k3 = timed(lambda: tsm.forward(plan, q, k, v, out), args.steps)
+    ms_plan, med_plan, min_plan = timed(lambda: mk(run_mode, ws), args.steps)
+    ms_k3, med_k3, min_k3 = timed(lambda: tsm.forward(plan, q, k, v, out), args.steps)
 
     ms_allfull = None
+    quality = None
     if not args.no_allfull:
         pf = mk("all_full")
-        tsm.forward(pf, q, k, v, out)
-        ms_allfull = timed(lambda: tsm.forward(pf, q, k, v, out), max(3, args.steps // 4))
+        dense_out = torch.empty_like(out)
+        tsm.forward(pf, q, k, v, dense_out)
+        ms_allfull = timed(lambda: tsm.forward(pf, q, k, v, dense_out), max(3, args.steps // 4))[0]
         del pf
+        # approximation quality of the sparse output against the all-full one
+        # (reported, not gated: the pages give no bound)
+        a, b = out.float(), dense_out.float()
+        diff = (a - b).flatten(2)
+        num = diff.pow(2).sum(-1)
+        quality = {"vs": "all-full forward (bf16 output)",
+                   "max_abs": round(float(diff.abs().max()), 5),
+                   "rel_l2": round(float((num.sum() / b.flatten(2).pow(2).sum()).sqrt()), 6),
+                   "cosine_min_row": round(float(torch.nn.functional.cosine_similarity(a, b, dim=-1).min()), 6)}
+        del dense_out, a, b, diff, num
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -227,14 +256,19 @@ def main():
                                   f"{cfg.full_frac}, {cfg.entropy_samples} sampled query blocks)"),
                    "batch": cfg.batch, "seq_len": cfg.seq_len, "heads": cfg.heads, "head_dim": cfg.head_dim},
         "kernel_ms": {"plan_k1_k2": round(ms_plan, 4), "forward_k3": round(ms_k3, 4),
-                      "forward_k3_all_full": None if ms_allfull is None else round(ms_allfull, 4)},
+                      "forward_k3_all_full": None if ms_allfull is None else round(ms_allfull, 4),
+                      "plan_median": round(med_plan, 4), "plan_min": round(min_plan, 4),
+                      "forward_median": round(med_k3, 4), "forward_min": round(min_k3, 4)},
         "speedup_vs_all_full": None if ms_allfull is None else round(ms_allfull / ms_k3, 3),
         "forward_dense_equiv_tflops": round(dense / (ms_k3 * 1e-3) / 1e12, 2),
         "forward_executed_tflops": round(executed / (ms_k3 * 1e-3) / 1e12, 2),
         "mfma_utilisation_kept_tiles": round(achieved / PEAK_BF16, 4),
         "all_full_tflops": None if ms_allfull is None else round(dense / (ms_allfull * 1e-3) / 1e12, 2),
         "tiers": {"full": round(st["n_full"] / tiles, 4), "low": round(st["n_low"] / tiles, 4),
-                  "skip": round(st["n_skip"] / tiles, 4)},
+                  "skip": round(st["n_skip"] / tiles, 4), "diagonal": st["n_diag"],
+                  "near_threshold": n_band},
+        "head_retention": kh_summary,
+        "quality": quality,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16, 4), "traffic": traffic,
                      "kernel": "k3_attn (fused three-tier forward)",

@@ -14,11 +14,15 @@ ragged and keep their real sizes.
                                                           probability as the
                                                           importance metric)
   O4    tiers       dual thresholds tau_hi / tau_lo, optional top-k, or the
-                    entropy-derived head-adaptive top-k; diagonal tiles FULL
+                    entropy-derived head-adaptive top-k, or the price router
+                    (predicted per-tier error from block second moments
+                    against one price); diagonal tiles FULL
                                                          (APT: dual
                                                           thresholds; HierPAS:
                                                           top-k and head-wise
-                                                          retention ratios)
+                                                          retention ratios;
+                                                          Triage: error-
+                                                          predicting router)
   O5    fp8         E4M3 codes with one scale per block   (HierPAS: reduced
                                                           precision); a low
                                                           tile runs attention
@@ -149,6 +153,121 @@ def tiers_adaptive(p: np.ndarray, k_h: int, full_frac: float) -> np.ndarray:
     t[ranks < k_h] = LOW
     t[ranks < nfull] = FULL
     return t
+
+
+# ----------------------------------------------------------------------------- O4b price router
+# Triage's router predicts, from block statistics, the output error a tile
+# would incur under each tier and moves it to a more accurate tier only when
+# the predicted error reduction is worth the extra compute at one price.  The
+# pages give no formula; the model below is this implementation's reading
+# (parity unpinned as a predictor; its exact identities are pinned).
+
+E4M3_U = 2.0 ** -4          # largest relative rounding error of an E4M3 normal value
+COST_FULL, COST_LOW = 1.0, 0.75   # bf16-equivalent MFMA work per tile: LOW = fp8 scores (half) + fp16 P.V
+
+
+def cost_skip(bk: int) -> float:
+    """Work of a skipped block relative to a FULL tile of the same shape: one
+    pseudo-key scored twice (bf16 hi + lo parts of k_J) plus its P.V share."""
+    return 1.5 / bk
+
+
+def block_moments(x: np.ndarray, b: int):
+    """Second-moment statistics of each block of b rows (real size s), from
+    float64 sums S1_c = sum_i x_ic and S2_c = sum_i x_ic^2:
+      m2[j, c]  = S2_c / s                         (mean square per dimension)
+      var[j, c] = max(S2_c / s - (S1_c / s)^2, 0)  (variance per dimension)
+      tot_m2[j] = sum_c m2, tot_var[j] = sum_c var, mnorm[j] = sqrt(sum_c (S1_c / s)^2)
+    every output rounded once to float32."""
+    n, d = x.shape
+    sizes = block_sizes(n, b)
+    nb = sizes.size
+    m2 = np.empty((nb, d), np.float32)
+    var = np.empty((nb, d), np.float32)
+    tot_m2 = np.empty(nb, np.float32)
+    tot_var = np.empty(nb, np.float32)
+    mnorm = np.empty(nb, np.float32)
+    x64 = x.astype(np.float64)
+    for j, sz in enumerate(sizes):
+        blk = x64[j * b: j * b + sz]
+        mean = blk.sum(axis=0) / float(sz)
+        msq = (blk * blk).sum(axis=0) / float(sz)
+        vr = np.maximum(msq - mean * mean, 0.0)
+        m2[j], var[j] = msq.astype(np.float32), vr.astype(np.float32)
+        tot_m2[j], tot_var[j] = np.float32(msq.sum()), np.float32(vr.sum())
+        mnorm[j] = np.float32(math.sqrt(float((mean * mean).sum())))
+    return dict(m2=m2, var=var, tot_m2=tot_m2, tot_var=tot_var, mnorm=mnorm)
+
+
+def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d):
+    """Predicted relative output error of every tile (I, J) under SKIP and LOW
+    (FULL: 0), float64 [Nq, Nk] each.  Inputs are the float32 block statistics
+    of block_moments (q2 = query m2 per dimension, m2q its total; kvar = key
+    variance per dimension, m2k the key mean square total; vvar, m2v, vnorm =
+    value variance total, mean square total and mean norm) and the real key
+    block sizes n_k.
+
+    Within a tile a key's score deviates from the pooled score by
+    delta = q_i.(k_j - k_J)/sqrt(d); over the tile's (query, key) pairs its
+    mean square, taking the dimensions as uncorrelated, is
+        s2 = sum_c q2[I, c] kvar[J, c] / d.
+    The weights e^delta are taken as lognormal.  The block's mass then exceeds
+    the pooled estimate n_J e^S by the log-gain
+        g = s2/2                        (s2 <= 2 ln n_J: the lognormal mean)
+        g = sqrt(2 s2 ln n_J) - ln n_J  (beyond: the largest of n_J scores
+                                         dominates the sum)
+    and the weights keep n_eff = max(1, n_J e^-s2) keys' worth of values.
+      SKIP  (block means, one score weighted by n_J): the mass falls short by
+            the factor e^-g and the block-mean value misses the weighted mean:
+            eS = vnorm (1 - e^-g) + sqrt(vvar max(0, 1/n_eff - 1/n_J)).
+      LOW   (E4M3 copies of q, k, v): rounding errors of relative RMS u/sqrt(3)
+            add score noise of variance sl2 = (2u^2/3) m2q m2k / d^2 and value
+            noise of RMS u sqrt(m2v/3):
+            eL = vnorm expm1(sl2/2)
+                 + (sqrt(vvar expm1(sl2)) + u sqrt(m2v/3)) / sqrt(n_eff).
+    The norm of the block mean stands in for the distance between the tile's
+    output and the row's.  Returns (s2, g, eS, eL)."""
+    q2 = q2.astype(np.float64)
+    kvar = kvar.astype(np.float64)
+    s2 = (q2 @ kvar.T) / d                                              # [Nq, Nk]
+    sl2 = (2.0 * E4M3_U ** 2 / 3.0) * np.outer(m2q.astype(np.float64), m2k.astype(np.float64)) / float(d * d)
+    nj = n_k.astype(np.float64)[None, :]
+    lnn = np.log(nj)
+    g = np.where(s2 <= 2.0 * lnn, 0.5 * s2, np.sqrt(2.0 * s2 * lnn) - lnn)
+    neff = np.maximum(1.0, nj * np.exp(-s2))
+    vn = vnorm.astype(np.float64)[None, :]
+    vv = vvar.astype(np.float64)[None, :]
+    mv = m2v.astype(np.float64)[None, :]
+    eS = vn * (-np.expm1(-g)) + np.sqrt(vv * np.maximum(0.0, 1.0 / neff - 1.0 / nj))
+    eL = vn * np.expm1(0.5 * sl2) + (np.sqrt(vv * np.expm1(sl2)) + E4M3_U * np.sqrt(mv / 3.0)) / np.sqrt(neff)
+    return s2, g, eS, eL
+
+
+def corrected_shares(S: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """The router's row softmax with every tile's log-mass raised by its
+    spread gain g: p~_IJ = softmax_J(S_IJ + g_IJ), float64."""
+    x = S + g
+    e = np.exp(x - x.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def tiers_price(p: np.ndarray, eS: np.ndarray, eL: np.ndarray, price: float, bk: int):
+    """Each tile takes the tier t minimising p_IJ * e_t + price * cost_t, i.e.
+    it moves to a more accurate tier only when the predicted error reduction
+    (the relative error scaled by the tile's share p of the row) pays for the
+    extra work at the given price (Triage: one price sets the trade-off).
+    Ties go to the cheaper tier.  Returns the tier map and the three
+    objectives."""
+    lam = float(price)
+    oS = p * eS + lam * cost_skip(bk)
+    oL = p * eL + lam * COST_LOW
+    oF = np.full(p.shape, lam * COST_FULL)
+    t = np.full(p.shape, SKIP, dtype=np.uint8)
+    best = oS.copy()
+    t[oL < best] = LOW
+    best = np.minimum(best, oL)
+    t[oF < best] = FULL
+    return t, (oS, oL, oF)
 
 
 def build_lists(t: np.ndarray):
@@ -339,7 +458,8 @@ def naive_attention(q, k, v):
 def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     """Steps O1-O5 for one (batch, head): q, k, v [n, d].  ``cfg_like`` needs
     block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
-    full_frac, entropy_samples.  Returns a dict of every intermediate."""
+    full_frac, entropy_samples (and price for mode 4, the price router).
+    Returns a dict of every intermediate."""
     mode = cfg_like.mode if mode is None else mode
     n, d = q.shape
     bq, bk = cfg_like.block_q, cfg_like.block_k
@@ -348,6 +468,7 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     vbar = pool_means(v, bk)
     S, p = router(qbar, kbar, n, bk)
     r_h, k_h = None, None
+    price_info = None
     if mode == 0:      # threshold
         t = tiers_threshold(p, cfg_like.tau_hi, cfg_like.tau_lo, cfg_like.top_k)
     elif mode == 1:    # adaptive
@@ -355,6 +476,13 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
         t = tiers_adaptive(p, k_h, cfg_like.full_frac)
     elif mode == 2:    # all full
         t = np.full(p.shape, FULL, dtype=np.uint8)
+    elif mode == 4:    # price
+        qm, km, vm = block_moments(q, bq), block_moments(k, bk), block_moments(v, bk)
+        s2, g, eS, eL = tile_error_model(qm["m2"], qm["tot_m2"], km["var"], km["tot_m2"], vm["tot_var"],
+                                         vm["tot_m2"], vm["mnorm"], block_sizes(n, bk), d)
+        pt = corrected_shares(S, g)
+        t, objs = tiers_price(pt, eS, eL, cfg_like.price, bk)
+        price_info = dict(qm=qm, km=km, vm=vm, s2=s2, g=g, pt=pt, eS=eS, eL=eL, objs=objs)
     else:              # external
         t = np.array(external_tiers, dtype=np.uint8, copy=True)
     t[diagonal_mask(n, bq, bk)] = FULL
@@ -363,7 +491,7 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     k8, sk, ik = quantise_blocks(k, bk)
     v8, sv, iv = quantise_blocks(v, bk)
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
-                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h)
+                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info)
 
 
 def oracle_forward(q, k, v, plan, bq, bk, rows=None):
