@@ -10,10 +10,14 @@
  *         q_i . kbar_J / sqrt(d) + ln n_J valued by vbar_J.
  * Tiers come from a block router, p_IJ = softmax_J(qbar_I . kbar_J / sqrt(d)
  * + ln n_J), with dual thresholds tau_hi / tau_lo and an optional per-row
- * top-k, or from an entropy-derived per-head top-k; diagonal tiles are always
- * FULL.  Sources of the method:
+ * top-k, or from an entropy-derived per-head top-k, or from a per-tile error
+ * prediction weighed against one price; diagonal tiles are always FULL.
+ * Sources of the method:
  *   - "Triage" (abstract): three approximation tiers per tile, skipping by
- *     block means, one fused kernel over all tiers in a single pass.
+ *     block means, one fused kernel over all tiers in a single pass; a
+ *     router that predicts each tile's error under each tier from block
+ *     statistics and promotes a tile only when the error reduction pays for
+ *     the extra compute at a single price.
  *   - "APT" (abstract): attention probability as the importance metric; dual
  *     thresholds select elements and assign precision; mask management and
  *     tile dataflow.
@@ -67,7 +71,10 @@ typedef enum {
                                 the top ceil(full_frac*k_h) tiles FULL, the rest of the top
                                 k_h LOW, the remainder SKIP                              */
   TATTN_MODE_ALL_FULL = 2,   /* every tile FULL: dense attention through the same kernel */
-  TATTN_MODE_EXTERNAL = 3    /* tiers supplied with tattn_plan_set_tiers                 */
+  TATTN_MODE_EXTERNAL = 3,   /* tiers supplied with tattn_plan_set_tiers                 */
+  TATTN_MODE_PRICE = 4       /* each tile takes the tier minimising predicted error plus
+                                price * work, the error predicted from block second
+                                moments (see tattn_plan)                                 */
 } tattn_mode;
 
 typedef enum { TATTN_BF16 = 0, TATTN_FP32 = 1 } tattn_dtype;
@@ -82,6 +89,8 @@ typedef struct {
   int32_t entropy_samples;                 /* ADAPTIVE: number of sampled query blocks       */
   int32_t in_dtype, out_dtype;             /* in: TATTN_BF16; out: TATTN_BF16 or TATTN_FP32  */
   int64_t stride_b, stride_h, stride_n;    /* element strides shared by Q, K, V and O        */
+  float price;                             /* PRICE: error per FULL tile of work, >= 0,
+                                              finite; ignored by the other modes             */
 } tattn_config;
 
 typedef struct tattn_plan_s* tattn_plan_t;  /* opaque host object; device state is in the workspace */
@@ -111,8 +120,23 @@ tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes /* hos
  *  2. Router p_IJ = softmax_J(qbar_I . kbar_J / sqrt(d) + ln n_J) in float64
  *     ("APT": attention probability as importance), and
  *  3. the tier map by `cfg->mode` (dual thresholds, top-k, entropy-adaptive,
- *     all-full) with diagonal tiles forced FULL, compacted per query block into
- *     [FULL asc | LOW asc | SKIP asc] key-block lists.
+ *     all-full, price) with diagonal tiles forced FULL, compacted per query
+ *     block into [FULL asc | LOW asc | SKIP asc] key-block lists.
+ * TATTN_MODE_PRICE ("Triage": error predicted from block statistics, one
+ * price) also takes second moments in step 1 (per block and dimension the
+ * mean square of Q and the variance of K; per key block the variance total,
+ * mean-square total and mean norm of V and the mean-square total of K).  Per
+ * tile it predicts the within-tile score spread
+ * s2 = sum_c q2[I,c] kvar[J,c] / d, a lognormal log-mass gain g (s2/2, or
+ * sqrt(2 s2 ln n_J) - ln n_J beyond s2 = 2 ln n_J) and n_eff =
+ * max(1, n_J e^-s2); the relative errors
+ *   SKIP  vnorm (1 - e^-g) + sqrt(vvar max(0, 1/n_eff - 1/n_J)),
+ *   LOW   vnorm expm1(sl2/2) + (sqrt(vvar expm1(sl2)) + u sqrt(m2v/3)) / sqrt(n_eff),
+ *         sl2 = (2u^2/3) m2q m2k / d^2, u = 2^-4,
+ *   FULL  0;
+ * shares p~ = softmax_J(S + g); and gives the tile the tier with the least
+ * p~ * error + price * work (work FULL 1, LOW 0.75, SKIP 1.5 / block_k;
+ * ties to the cheaper tier).  All in float64.
  * q, k, v: the caller's tensors.  The plan keeps derived copies of K and V
  * (E4M3 codes, a transposed fp16 V, means) in `workspace`, so a later
  * tattn_forward must be given the same k and v pointers with unchanged
@@ -162,6 +186,15 @@ tattn_status tattn_plan_get_pool(tattn_plan_t plan, float* qbar, float* kbar, fl
  * patterns of fl16(fl32(decode(E4M3(v * inv)) * scale)) per element of V).
  * Either may be NULL. */
 tattn_status tattn_plan_get_codes(tattn_plan_t plan, uint8_t* host_k8, uint16_t* host_vlow, void* stream);
+
+/* SYNC.  PRICE mode: copy out the block second moments the router used
+ * (float32): q2 [B,H,Nq,d] and m2q [B,H,Nq] (query mean square per dimension
+ * and its total), kvar [B,H,Nk,d] and m2k [B,H,Nk] (key variance per
+ * dimension, key mean-square total), vvar, m2v, vnorm [B,H,Nk] (value variance
+ * total, mean-square total, norm of the mean).  Each from float64 sums,
+ * rounded once.  Any pointer may be NULL; TATTN_E_STATE for other modes. */
+tattn_status tattn_plan_get_moments(tattn_plan_t plan, float* q2, float* m2q, float* kvar, float* m2k,
+                                    float* vvar, float* m2v, float* vnorm, void* stream);
 
 /* SYNC.  Tier counts and executed / dense-equivalent flops of the plan. */
 tattn_status tattn_plan_stats(tattn_plan_t plan, tattn_stats* host_out);

@@ -48,6 +48,8 @@ def test_valid_configs(lib):
     assert status(lib, good(mode="adaptive")) == 0
     assert status(lib, good(seq_len=118800, heads=24)) == 0
     assert status(lib, good(top_k=10)) == 0
+    assert status(lib, good(mode="price", price=0.01)) == 0
+    assert status(lib, good(mode="price", price=0.0)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -59,6 +61,8 @@ def test_valid_configs(lib):
     (dict(mode="adaptive", keep_min=0.6, keep_max=0.5), -1), (dict(mode="adaptive", full_frac=0.0), -1),
     (dict(mode="adaptive", entropy_samples=0), -1),
     (dict(seq_len=64 * 5000), -2),
+    (dict(mode="price", price=-1.0), -1), (dict(mode="price", price=float("nan")), -1),
+    (dict(mode=5), -1),
 ])
 def test_invalid_configs(lib, kw, code):
     st = status(lib, good(**kw))
@@ -94,6 +98,11 @@ def test_workspace_formula(lib):
              + BH * Nk * D * 6)
     assert floor <= n.value <= floor * 1.05
     assert lib.tattn_workspace_bytes(ctypes.byref(good(head_dim=96)), ctypes.byref(n)) == -2
+    # the price router adds its second moments and a float64 spread per tile
+    m = ctypes.c_size_t()
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="price", price=0.01)), ctypes.byref(m)) == 0
+    extra = BH * Nq * Nk * 8 + BH * (Nq + Nk) * D * 4 + BH * (Nq + 4 * Nk) * 4
+    assert extra <= m.value - n.value <= extra * 1.05
 
 
 def test_plan_rejects_bad_pointers_before_any_launch(lib):

@@ -1,0 +1,124 @@
+"""GPU parity of the price router (TATTN_MODE_PRICE): the block second moments
+against the oracle's, the tier map against the oracle's outside near-ties of
+the objectives, the output under the GPU's tiers, and the monotone response to
+the price.  Inputs come from the position-correlated generator; a lower
+projection gain is used as well, because at the workloads' gain the fp8 score
+noise is too large for the low tier ever to be chosen."""
+import numpy as np
+import pytest
+
+from oracle import tattn as T
+from synth import CONFIGS, generate
+from synth.gen import to_bf16_bits, bf16_bits_to_f32
+
+from gpu_cases import OracleCfg
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (config, overrides, projection gain or None)
+    "small_gain1": (2, dict(heads=3), 1.0),
+    "small": (2, dict(heads=2), None),
+    "d128_ragged": (3, dict(heads=2, grid=(3, 10, 23)), None),           # N = 690
+    "d128_ragged_gain1": (3, dict(heads=2, grid=(3, 10, 23), temperature=False), 1.0),
+    "fine64x16": (5, dict(heads=2, grid=(2, 10, 50), mode=4), 1.0),        # N = 1000, Nk = 63
+}
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _inputs(name):
+    import torch
+    cid, over, gain = CASES[name]
+    cfg = CONFIGS[cid].with_(**over)
+    g = generate(cfg, **({} if gain is None else dict(a_gain=gain)))
+    bits = g["bits"]
+    if bits is None:
+        bits = {n: to_bf16_bits(g[n]) for n in ("q", "k", "v")}
+        for n in ("q", "k", "v"):
+            g[n] = bf16_bits_to_f32(bits[n])
+    dev = {n: torch.from_numpy(bits[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    return cfg, g, dev
+
+
+def _plan(dev, cfg, price, out_fp32=True):
+    import tile_sparse_mixed_amd as tsm
+    return tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, mode="price",
+                    price=price, out_fp32=out_fp32)
+
+
+def _oracle(g, h, cfg, price):
+    oc = OracleCfg(cfg, mode=4)
+    oc.price = float(np.float32(price))   # the ABI takes the price as float32
+    return T.oracle_plan(g["q"][0, h], g["k"][0, h], g["v"][0, h], oc)
+
+
+def _near_tie(objs, rel=1e-9):
+    """Tiles whose best two objectives agree to `rel`: float64 rounding of the
+    exp / log / sqrt chain may pick either tier."""
+    o = np.sort(np.stack(objs), axis=0)
+    return np.abs(o[1] - o[0]) <= rel * np.maximum(np.abs(o[1]), 1e-300)
+
+
+@pytest.mark.parametrize("name", ["small", "d128_ragged", "fine64x16"])
+def test_moments_match_oracle(name):
+    cfg, g, dev = _inputs(name)
+    p = _plan(dev, cfg, 0.01)
+    m = p.moments()
+    for h in range(cfg.heads):
+        qm = T.block_moments(g["q"][0, h], cfg.block_q)
+        km = T.block_moments(g["k"][0, h], cfg.block_k)
+        vm = T.block_moments(g["v"][0, h], cfg.block_k)
+        pairs = [("q2", qm["m2"]), ("m2q", qm["tot_m2"]), ("kvar", km["var"]), ("m2k", km["tot_m2"]),
+                 ("vvar", vm["tot_var"]), ("m2v", vm["tot_m2"]), ("vnorm", vm["mnorm"])]
+        for key, ref in pairs:
+            got = m[key][0, h]
+            # float64 sums rounded once to float32: equal up to the last bit of
+            # the totals, whose float64 summation order differs
+            np.testing.assert_allclose(got, ref, rtol=2.0 ** -23, atol=0, err_msg=f"{name} h{h} {key}")
+            if key in ("q2", "kvar"):
+                assert np.mean(got == ref) > 0.999, (name, h, key)
+
+
+@pytest.mark.parametrize("name,price", [("small_gain1", 0.01), ("small_gain1", 0.03), ("small_gain1", 0.1),
+                                        ("small", 0.01), ("d128_ragged", 0.003), ("d128_ragged_gain1", 0.3),
+                                        ("fine64x16", 0.03)])
+def test_price_tiers_and_output(name, price):
+    cfg, g, dev = _inputs(name)
+    p = _plan(dev, cfg, price)
+    out = __import__("tile_sparse_mixed_amd").forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    tiers = p.tiers()
+    lists, counts = p.lists()
+    frac = [round(float((tiers == x).mean()), 3) for x in (2, 1, 0)]
+    _log(f"[price {name} {price}] FULL/LOW/SKIP {frac}")
+    for h in range(cfg.heads):
+        o = _oracle(g, h, cfg, price)
+        tie = _near_tie(o["price"]["objs"])
+        diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
+        ok = ~tie | diag
+        assert tie.mean() < 1e-3, (name, h, tie.mean())
+        mism = (tiers[0, h] != o["tiers"]) & ok
+        assert not mism.any(), (name, h, np.argwhere(mism)[:5])
+        li, co = T.build_lists(tiers[0, h])
+        assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co)
+        oe = T.oracle_plan(g["q"][0, h], g["k"][0, h], g["v"][0, h], OracleCfg(cfg), mode=3,
+                           external_tiers=tiers[0, h])
+        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], oe, cfg.block_q, cfg.block_k)
+        err = np.abs(out[0, h].astype(np.float64) - ref)
+        _log(f"  h{h}: ties {int(tie.sum())}  max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+        assert err.max() <= 1e-2 and err.mean() <= 1e-3
+
+
+def test_price_monotone_on_gpu():
+    """A higher price never moves a tile to a more accurate tier."""
+    cfg, g, dev = _inputs("small_gain1")
+    prev = None
+    for price in [0.0, 1e-3, 1e-2, 3e-2, 1e-1, 1.0, 1e6]:
+        t = _plan(dev, cfg, price).tiers().astype(np.int64)
+        if prev is not None:
+            assert np.all(t <= prev), price
+        prev = t
+    diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
+    assert np.all(prev[..., ~diag] == 0) and np.all(prev[..., diag] == 2)

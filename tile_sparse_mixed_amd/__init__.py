@@ -15,12 +15,13 @@ import os
 import numpy as np
 
 __all__ = ["plan", "forward", "Plan", "TattnError", "load_library", "Config", "Stats",
-           "MODE_THRESHOLD", "MODE_ADAPTIVE", "MODE_ALL_FULL", "MODE_EXTERNAL", "SKIP", "LOW", "FULL"]
+           "MODE_THRESHOLD", "MODE_ADAPTIVE", "MODE_ALL_FULL", "MODE_EXTERNAL", "MODE_PRICE",
+           "SKIP", "LOW", "FULL"]
 
-MODE_THRESHOLD, MODE_ADAPTIVE, MODE_ALL_FULL, MODE_EXTERNAL = 0, 1, 2, 3
+MODE_THRESHOLD, MODE_ADAPTIVE, MODE_ALL_FULL, MODE_EXTERNAL, MODE_PRICE = 0, 1, 2, 3, 4
 SKIP, LOW, FULL = 0, 1, 2
 _MODES = {"threshold": MODE_THRESHOLD, "adaptive": MODE_ADAPTIVE, "all_full": MODE_ALL_FULL,
-          "external": MODE_EXTERNAL}
+          "external": MODE_EXTERNAL, "price": MODE_PRICE}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtattn.so")
 _lib = None
 
@@ -38,7 +39,8 @@ class Config(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("keep_min", ctypes.c_float), ("keep_max", ctypes.c_float),
                 ("full_frac", ctypes.c_float), ("entropy_samples", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+                ("price", ctypes.c_float)]
 
 
 class Stats(ctypes.Structure):
@@ -64,6 +66,7 @@ _SIGS = {
     "tattn_plan_get_codes": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_stats": (ctypes.c_int, [_VP, ctypes.POINTER(Stats)]),
     "tattn_plan_get_kh": (ctypes.c_int, [_VP, _VP, _VP]),
+    "tattn_plan_get_moments": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_destroy": (None, [_VP]),
     "tattn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "tattn_last_error": (ctypes.c_char_p, []),
@@ -96,13 +99,13 @@ def _check(status):
 
 def make_config(batch, heads, seq_len, head_dim, block_q, block_k, tau_hi=0.0, tau_lo=0.0, top_k=0,
                 mode="threshold", keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256,
-                out_fp32=False, strides=None):
+                out_fp32=False, strides=None, price=0.0):
     if strides is None:
         strides = (heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
     return Config(batch, heads, seq_len, head_dim, block_q, block_k, float(tau_hi), float(tau_lo), int(top_k), m,
                   float(keep_min), float(keep_max), float(full_frac), int(entropy_samples), 0,
-                  1 if out_fp32 else 0, *[int(s) for s in strides])
+                  1 if out_fp32 else 0, *[int(s) for s in strides], float(price))
 
 
 def _stream():
@@ -190,6 +193,18 @@ class Plan:
         _check(load_library().tattn_plan_stats(self._handle, ctypes.byref(st)))
         return st.as_dict()
 
+    def moments(self):
+        """Price mode: the block second moments the router used (float32)."""
+        d = self.cfg.head_dim
+        out = dict(q2=np.empty(self._shape(self.n_q, d), np.float32), m2q=np.empty(self._shape(self.n_q), np.float32),
+                   kvar=np.empty(self._shape(self.n_k, d), np.float32), m2k=np.empty(self._shape(self.n_k), np.float32),
+                   vvar=np.empty(self._shape(self.n_k), np.float32), m2v=np.empty(self._shape(self.n_k), np.float32),
+                   vnorm=np.empty(self._shape(self.n_k), np.float32))
+        _check(load_library().tattn_plan_get_moments(self._handle, *[out[k].ctypes.data for k in
+                                                                     ("q2", "m2q", "kvar", "m2k", "vvar", "m2v",
+                                                                      "vnorm")], _stream()))
+        return out
+
     def kh(self):
         bh = self.cfg.batch * self.cfg.heads
         kh = np.empty(bh, np.int32)
@@ -213,14 +228,14 @@ def _check_tensors(q, k, v):
 
 def plan(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, mode="threshold",
          keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256, out_fp32=False,
-         workspace=None) -> Plan:
+         workspace=None, price=0.0) -> Plan:
     """Pool, quantise and route (K1, K2).  q, k, v: bf16 [B, H, N, d] on the GPU.
     ``workspace`` (a uint8 GPU tensor, e.g. an earlier plan's) is reused when
     large enough; the earlier plan must not be used afterwards."""
     _check_tensors(q, k, v)
     B, H, N, d = q.shape
     cfg = make_config(B, H, N, d, block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
-                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3])
+                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price)
     return Plan(cfg, q, k, v, workspace=workspace)
 
 

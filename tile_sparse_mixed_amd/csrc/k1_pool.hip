@@ -17,6 +17,10 @@
 //   vlow             the low tier's V operand, fl16(fl32(decode(E4M3(v * inv)) * sv)),
 //                    in the same transposed layout.
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
+// For the price router both also write second moments from float64 sums of
+// squares ("Triage": the router works from block statistics): per dimension
+// the query mean square and the key variance, per block the key and value
+// mean-square totals, the value variance total and the norm of the value mean.
 #include "tattn_device.hpp"
 #include "tattn_internal.hpp"
 
@@ -56,15 +60,16 @@ struct BlockLoad {
   float vals[RPT][8];
 };
 
-template <int D, int BLK>
+template <int D, int BLK, bool MOM = false>
 __device__ void load_block(const uint16_t* __restrict__ base, int64_t sn, int rows, BlockLoad<D, BLK>& bl,
-                           double* __restrict__ red /* [RT][D] */, double& colsum, float& amax) {
+                           double* __restrict__ red /* [RT][D] */, double& colsum, float& amax,
+                           double* colsq = nullptr) {
   using BL = BlockLoad<D, BLK>;
   const int t = threadIdx.x;
   const int c = t % BL::CH, r0 = t / BL::CH;
-  double acc[8];
+  double acc[8], acc2[8];
 #pragma unroll
-  for (int e = 0; e < 8; e++) acc[e] = 0.0;
+  for (int e = 0; e < 8; e++) acc[e] = acc2[e] = 0.0;
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < BL::RPT; i++) {
@@ -77,6 +82,7 @@ __device__ void load_block(const uint16_t* __restrict__ base, int64_t sn, int ro
       const float f = __uint_as_float(e & 1 ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
       bl.vals[i][e] = f;
       acc[e] += static_cast<double>(f);
+      if (MOM) acc2[e] += static_cast<double>(f) * static_cast<double>(f);   // exact product of bf16 values
       mx = __builtin_fmaxf(mx, __builtin_fabsf(f));
     }
   }
@@ -91,15 +97,56 @@ __device__ void load_block(const uint16_t* __restrict__ base, int64_t sn, int ro
     colsum = s;
   }
   __syncthreads();
+  if (MOM) {   // the same reduction for the column sums of squares
+#pragma unroll
+    for (int e = 0; e < 8; e++) red[r0 * D + c * 8 + e] = acc2[e];
+    __syncthreads();
+    *colsq = 0.0;
+    if (t < D) {
+      double s = 0.0;
+      for (int i = 0; i < BL::RT; i++) s += red[i * D + t];
+      *colsq = s;
+    }
+    __syncthreads();
+  }
 }
 
-template <int D, int BK>
+// Block-wide float64 sum; `red` holds kThreads/64 doubles.
+__device__ double block_sum_d(double v, double* red) {
+  v = wave_sum_d(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; i++) r += red[i];
+  __syncthreads();
+  return r;
+}
+
+// Second moments of a block column from its float64 sums (threads t < D):
+// mean square S2/n and variance max(S2/n - (S1/n)^2, 0), each rounded once per
+// operation (no fused multiply-add), as the price router's statistics define.
+struct ColMoments {
+  double mean, msq, var;
+};
+__device__ inline ColMoments col_moments(double s1, double s2, int n) {
+  const double dn = static_cast<double>(n);
+  ColMoments m;
+  m.mean = s1 / dn;
+  m.msq = s2 / dn;
+  m.var = fmax(__dsub_rn(m.msq, __dmul_rn(m.mean, m.mean)), 0.0);
+  return m;
+}
+
+template <int D, int BK, bool MOM>
 __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   static_assert(BK == 64 || BK == 16, "key blocks are 64 or 16 keys");
   constexpr int QR = BK / 8;   // 16-byte chunks per stored row of BK keys
   using BL = BlockLoad<D, BK>;
   __shared__ double red[BL::RT * D];
   __shared__ float fred[kThreads / 64];
+  __shared__ double dred[kThreads / 64];
   __shared__ uint16_t tileT[BK * D];   // V block as bf16, [key][d], for the transposed stores
 
   const Dims& dm = a.d;
@@ -123,17 +170,24 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   const int t = threadIdx.x;
   const int c = t % BL::CH, r0 = t / BL::CH;
   BL bl;
-  double colsum;
+  double colsum, colsq = 0.0;
   float amax;
+  const int64_t kb = (int64_t)bh * dm.Nk + J;   // this block's index in the [BH][Nk] statistics
 
   // ---- K: means, scale, codes (row-major, k8_pos order inside each row)
-  load_block<D, BK>(a.k + off, dm.sn, rows, bl, red, colsum, amax);
+  load_block<D, BK, MOM>(a.k + off, dm.sn, rows, bl, red, colsum, amax, &colsq);
   if (t < D) {
     const float m = static_cast<float>(colsum / static_cast<double>(rows));
     kbar[t] = m;
     const uint16_t hi = f32_to_bf16(m);
     kbar16[t] = hi;
     kbarlo[t] = f32_to_bf16(m - bf16_to_f32(hi));   // the difference is exact in fp32
+  }
+  if (MOM) {   // key variance per dimension and the mean-square total
+    const ColMoments cm = col_moments(colsum, colsq, rows);
+    if (t < D) reinterpret_cast<float*>(a.ws + a.L.kvar)[kb * D + t] = static_cast<float>(cm.var);
+    const double tot = block_sum_d(t < D ? cm.msq : 0.0, dred);
+    if (t == 0) reinterpret_cast<float*>(a.ws + a.L.m2k)[kb] = static_cast<float>(tot);
   }
   amax = block_max(amax, fred);
   {
@@ -154,13 +208,24 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   }
 
   // ---- V: means, scale, transposed codes and transposed bf16 values
-  load_block<D, BK>(a.v + off, dm.sn, rows, bl, red, colsum, amax);
+  load_block<D, BK, MOM>(a.v + off, dm.sn, rows, bl, red, colsum, amax, &colsq);
   if (t < D) {
     const float m = static_cast<float>(colsum / static_cast<double>(rows));
     vbar[t] = m;
     vbarT[t * 64 + vt_pos(J & 63)] = f32_to_f16(m);
     if (J == dm.Nk - 1)   // finite zeros in the chunk's unused columns (they meet P = 0)
       for (int j = (J & 63) + 1; j < 64; j++) vbarT[t * 64 + vt_pos(j)] = 0;
+  }
+  if (MOM) {   // value variance total, mean-square total and the norm of the mean
+    const ColMoments cm = col_moments(colsum, colsq, rows);
+    const double tv = block_sum_d(t < D ? cm.var : 0.0, dred);
+    const double tm = block_sum_d(t < D ? cm.msq : 0.0, dred);
+    const double tn = block_sum_d(t < D ? __dmul_rn(cm.mean, cm.mean) : 0.0, dred);
+    if (t == 0) {
+      reinterpret_cast<float*>(a.ws + a.L.vvar)[kb] = static_cast<float>(tv);
+      reinterpret_cast<float*>(a.ws + a.L.m2v)[kb] = static_cast<float>(tm);
+      reinterpret_cast<float*>(a.ws + a.L.vnorm)[kb] = static_cast<float>(sqrt(tn));
+    }
   }
 #pragma unroll
   for (int i = 0; i < BL::RPT; i++) {
@@ -216,11 +281,12 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool MOM>
 __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   using BL = BlockLoad<D, BQ>;
   __shared__ double red[BL::RT * D];
   __shared__ float fred[kThreads / 64];
+  __shared__ double dred[kThreads / 64];
   const Dims& dm = a.d;
   const int bh = blockIdx.x / dm.Nq, I = blockIdx.x % dm.Nq;
   const int b = bh / dm.H, h = bh % dm.H;
@@ -229,10 +295,17 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   unsigned char* ws = a.ws;
   float* qbar = reinterpret_cast<float*>(ws + a.L.qbar) + ((int64_t)bh * dm.Nq + I) * D;
   BL bl;
-  double colsum;
+  double colsum, colsq = 0.0;
   float amax;
-  load_block<D, BQ>(a.q + off, dm.sn, rows, bl, red, colsum, amax);
+  load_block<D, BQ, MOM>(a.q + off, dm.sn, rows, bl, red, colsum, amax, &colsq);
   if (threadIdx.x < D) qbar[threadIdx.x] = static_cast<float>(colsum / static_cast<double>(rows));
+  if (MOM) {   // query mean square per dimension and its total
+    const int64_t qb = (int64_t)bh * dm.Nq + I;
+    const ColMoments cm = col_moments(colsum, colsq, rows);
+    if (threadIdx.x < D) reinterpret_cast<float*>(ws + a.L.q2)[qb * D + threadIdx.x] = static_cast<float>(cm.msq);
+    const double tot = block_sum_d(threadIdx.x < D ? cm.msq : 0.0, dred);
+    if (threadIdx.x == 0) reinterpret_cast<float*>(ws + a.L.m2q)[qb] = static_cast<float>(tot);
+  }
   amax = block_max(amax, fred);
   if (threadIdx.x == 0) {
     reinterpret_cast<float*>(ws + a.L.sq)[(int64_t)bh * dm.Nq + I] = scale448(amax);
@@ -240,26 +313,27 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool MOM>
 hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
   const Dims& d = a.d;
   if (d.Bk == 64)
-    hipLaunchKernelGGL((k1_kv<D, 64>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_kv<D, 64, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k1_kv<D, 16>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_kv<D, 16, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d.Bq == 128)
-    hipLaunchKernelGGL((k1_q<D, 128>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_q<D, 128, MOM>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k1_q<D, 64>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_q<D, 64, MOM>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
-  return a.d.D == 128 ? launch_pool_d<128>(a, s) : launch_pool_d<64>(a, s);
+  if (a.moments) return a.d.D == 128 ? launch_pool_d<128, true>(a, s) : launch_pool_d<64, true>(a, s);
+  return a.d.D == 128 ? launch_pool_d<128, false>(a, s) : launch_pool_d<64, false>(a, s);
 }
 
 }  // namespace tattn

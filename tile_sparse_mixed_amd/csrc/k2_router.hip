@@ -11,7 +11,10 @@
 //        ADAPTIVE   k_h from the entropy of p on sampled rows (K2e), then the top
 //                   ceil(full_frac*k_h) tiles FULL, the rest of the top k_h LOW
 //                   ("HierPAS": sampling-based entropy, head-wise retention),
-//        ALL_FULL   every tile FULL;
+//        ALL_FULL   every tile FULL,
+//        PRICE      per tile the tier with the least predicted error (from
+//                   block second moments, K2a's spread product) plus price x
+//                   work ("Triage": error-predicting router, one price);
 //      diagonal tiles forced FULL; then a stable compaction into
 //      [FULL asc | LOW asc | SKIP asc] with wavefront ballots.
 // K2c  compaction only, for a tier map supplied by the caller.
@@ -27,7 +30,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kRouterMaxNk = 4096;
 
 // ------------------------------------------------------------------ K2a
-template <int D>
+// SPREAD: the same product over the price router's second moments, the
+// within-tile score spread s2_IJ = sum_c q2_I,c kvar_J,c / d.
+template <int D, bool SPREAD>
 __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
   // 64 query blocks x 64 key blocks per workgroup; each thread owns a 4 x 4
   // block of S.  The operands pass through LDS as float64, 16 values of d at
@@ -38,8 +43,8 @@ __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
   const Dims& dm = a.d;
   const int bh = blockIdx.z;
   const int I0 = blockIdx.y * 64, J0 = blockIdx.x * 64;
-  const float* qbar = reinterpret_cast<const float*>(a.ws + a.L.qbar) + (int64_t)bh * dm.Nq * D;
-  const float* kbar = reinterpret_cast<const float*>(a.ws + a.L.kbar) + (int64_t)bh * dm.Nk * D;
+  const float* qbar = reinterpret_cast<const float*>(a.ws + (SPREAD ? a.L.q2 : a.L.qbar)) + (int64_t)bh * dm.Nq * D;
+  const float* kbar = reinterpret_cast<const float*>(a.ws + (SPREAD ? a.L.kvar : a.L.kbar)) + (int64_t)bh * dm.Nk * D;
   const int t = threadIdx.x;
   const int rg = t / 16, jg = t % 16;   // rows 4rg..4rg+3, key blocks 4jg..4jg+3
   double acc[4][4];
@@ -73,10 +78,11 @@ __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
     }
     __syncthreads();
   }
-  double* S = reinterpret_cast<double*>(a.ws + a.L.S) + (int64_t)bh * dm.Nq * dm.Nk;
-  const double isd = 1.0 / sqrt(static_cast<double>(D));
-  const double lg_full = log(static_cast<double>(dm.Bk));
-  const double lg_last = log(static_cast<double>(dm.N - (dm.Nk - 1) * dm.Bk));
+  double* S = reinterpret_cast<double*>(a.ws + (SPREAD ? a.L.s2 : a.L.S)) + (int64_t)bh * dm.Nq * dm.Nk;
+  // 1/d is exact for d a power of two, so the spread is acc / d exactly
+  const double isd = SPREAD ? 1.0 / static_cast<double>(D) : 1.0 / sqrt(static_cast<double>(D));
+  const double lg_full = SPREAD ? 0.0 : log(static_cast<double>(dm.Bk));
+  const double lg_last = SPREAD ? 0.0 : log(static_cast<double>(dm.N - (dm.Nk - 1) * dm.Bk));
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int I = I0 + 4 * rg + i;
@@ -271,6 +277,45 @@ __device__ void compact_row(const unsigned char* tr, int n, int16_t* list, int* 
   }
 }
 
+// ------------------------------------------------------------------ price router
+// Per-tile error model of the price router ("Triage": a tile's error under
+// each tier predicted from block statistics; one price trades error against
+// work).  Evaluated with every operation rounded on its own (no fused
+// multiply-add), in float64.
+constexpr double kE4m3U = 0.0625;   // 2^-4: largest relative rounding error of an E4M3 normal value
+
+// log-mass gain of a tile over its pooled estimate: lognormal mean s2/2 up to
+// s2 = 2 ln n, beyond it the largest of n scores dominates
+__device__ inline double spread_gain(double s2, double lnn) {
+#pragma clang fp contract(off)
+  return s2 <= 2.0 * lnn ? 0.5 * s2 : sqrt(2.0 * s2 * lnn) - lnn;
+}
+
+struct PriceTile {
+  double s2, n, vnorm, vvar, m2v, sl2;
+};
+// the tier with the least p~ * error + price * work; ties to the cheaper tier
+__device__ inline unsigned char price_tier(const PriceTile& x, double pt, double price, double cost_skip) {
+#pragma clang fp contract(off)
+  const double neff = fmax(1.0, x.n * exp(-x.s2));
+  const double lnn = log(x.n);
+  const double g = spread_gain(x.s2, lnn);
+  const double eS = x.vnorm * (-expm1(-g)) + sqrt(x.vvar * fmax(0.0, 1.0 / neff - 1.0 / x.n));
+  const double eL = x.vnorm * expm1(0.5 * x.sl2) +
+                    (sqrt(x.vvar * expm1(x.sl2)) + kE4m3U * sqrt(x.m2v / 3.0)) / sqrt(neff);
+  const double oS = pt * eS + price * cost_skip;
+  const double oL = pt * eL + price * 0.75;
+  const double oF = price * 1.0;
+  unsigned char t = TATTN_SKIP;
+  double best = oS;
+  if (oL < best) {
+    t = TATTN_LOW;
+    best = oL;
+  }
+  if (oF < best) t = TATTN_FULL;
+  return t;
+}
+
 enum { K2B_TIERS = 0, K2B_ENTROPY = 1 };
 
 inline size_t k2b_lds_bytes(int nk) { return ((size_t)nk * 10 + 15) / 16 * 16; }
@@ -339,6 +384,47 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
       tr[J] = t;
       pout[J] = static_cast<float>(p);
     }
+  } else if (a.mode == TATTN_MODE_PRICE) {
+    // p is exported; the decision uses the shares corrected by each tile's
+    // spread gain, p~ = softmax_J(S + g)
+    const double* s2r = reinterpret_cast<const double*>(a.ws + a.L.s2) + row * n;
+    const float* m2k = reinterpret_cast<const float*>(a.ws + a.L.m2k) + (int64_t)bh * n;
+    const float* vvar = reinterpret_cast<const float*>(a.ws + a.L.vvar) + (int64_t)bh * n;
+    const float* m2v = reinterpret_cast<const float*>(a.ws + a.L.m2v) + (int64_t)bh * n;
+    const float* vnorm = reinterpret_cast<const float*>(a.ws + a.L.vnorm) + (int64_t)bh * n;
+    const double m2q = reinterpret_cast<const float*>(a.ws + a.L.m2q)[row];
+    const double nfull = dm.Bk, nlast = dm.N - (dm.Nk - 1) * dm.Bk;
+    const double lnf = log(nfull), lnl = log(nlast);
+    double mx = -INFINITY;
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      pout[J] = static_cast<float>(pv[J]);
+      const double x = S[J] + spread_gain(s2r[J], J == n - 1 ? lnl : lnf);
+      pv[J] = x;
+      mx = fmax(mx, x);
+    }
+    mx = block_max_d(mx, r);
+    double sum = 0.0;
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      const double e = exp(pv[J] - mx);
+      pv[J] = e;
+      sum += e;
+    }
+    sum = block_sum_d(sum, r);
+    const double price = a.price, cost_skip = 1.5 / static_cast<double>(dm.Bk);
+    const double cu = 2.0 * kE4m3U * kE4m3U / 3.0, dd = static_cast<double>(dm.D) * static_cast<double>(dm.D);
+    for (int J = threadIdx.x; J < n; J += kThreads) {
+      PriceTile x;
+      x.s2 = s2r[J];
+      x.n = J == n - 1 ? nlast : nfull;
+      x.vnorm = vnorm[J];
+      x.vvar = vvar[J];
+      x.m2v = m2v[J];
+      {
+#pragma clang fp contract(off)
+        x.sl2 = cu * (m2q * static_cast<double>(m2k[J])) / dd;
+      }
+      tr[J] = price_tier(x, pv[J] / sum, price, cost_skip);
+    }
   } else {  // ADAPTIVE
     const int S2 = min(a.samples, dm.Nq);
     const double* ent = reinterpret_cast<const double*>(a.ws + a.L.ent) + (int64_t)bh * S2;
@@ -401,9 +487,18 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   if (a.mode != TATTN_MODE_ALL_FULL) {
     dim3 grid((d.Nk + 63) / 64, (d.Nq + 63) / 64, d.BH);
     if (d.D == 128)
-      hipLaunchKernelGGL((k2a_scores<128>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((k2a_scores<128, false>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((k2a_scores<64>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((k2a_scores<64, false>), grid, dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.mode == TATTN_MODE_PRICE) {
+    dim3 grid((d.Nk + 63) / 64, (d.Nq + 63) / 64, d.BH);
+    if (d.D == 128)
+      hipLaunchKernelGGL((k2a_scores<128, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k2a_scores<64, true>), grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

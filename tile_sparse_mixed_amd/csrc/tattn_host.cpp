@@ -54,7 +54,7 @@ Dims make_dims(const tattn_config& c) {
   return d;
 }
 
-Layout make_layout(const Dims& d, int entropy_samples) {
+Layout make_layout(const Dims& d, int entropy_samples, bool moments) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -96,6 +96,15 @@ Layout make_layout(const Dims& d, int entropy_samples) {
   L.ent = take(BH * S * 8);
   L.kh = take(BH * 4);
   L.rh = take(BH * 8);
+  const size_t mq = moments ? BH * Nq : 0, mk = moments ? BH * Nk : 0;
+  L.q2 = take(mq * D * 4);
+  L.m2q = take(mq * 4);
+  L.kvar = take(mk * D * 4);
+  L.m2k = take(mk * 4);
+  L.vvar = take(mk * 4);
+  L.m2v = take(mk * 4);
+  L.vnorm = take(mk * 4);
+  L.s2 = take(mq * Nk * 8);
   L.flag = take(16);
   L.total = off;
   return L;
@@ -115,7 +124,9 @@ static tattn_status validate(const tattn_config* c) {
   if ((c->block_k != 64 && c->block_k != 16) || (c->block_q != 64 && c->block_q != 128))
     return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported (block_q 64 or 128, block_k 64 or 16)", c->block_q,
                 c->block_k);
-  if (c->mode < 0 || c->mode > 3) return fail(TATTN_E_INVALID, "mode %d out of range", c->mode);
+  if (c->mode < 0 || c->mode > 4) return fail(TATTN_E_INVALID, "mode %d out of range", c->mode);
+  if (c->mode == TATTN_MODE_PRICE && (!std::isfinite(c->price) || c->price < 0.0f))
+    return fail(TATTN_E_INVALID, "price must be finite and >= 0 (got %g)", c->price);
   if (!std::isfinite(c->tau_hi) || !std::isfinite(c->tau_lo) || c->tau_lo < 0.0f || c->tau_lo > c->tau_hi)
     return fail(TATTN_E_INVALID, "thresholds need 0 <= tau_lo <= tau_hi (got %g, %g)", c->tau_lo, c->tau_hi);
   const int64_t nq = (c->seq_len + (int64_t)c->block_q - 1) / c->block_q;
@@ -169,7 +180,7 @@ tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes) {
   tattn_status st = validate(cfg);
   if (st != TATTN_OK) return st;
   if (!bytes) return fail(TATTN_E_INVALID, "bytes is NULL");
-  *bytes = make_layout(make_dims(*cfg), cfg->entropy_samples).total;
+  *bytes = make_layout(make_dims(*cfg), cfg->entropy_samples, cfg->mode == TATTN_MODE_PRICE).total;
   return ok();
 }
 
@@ -186,6 +197,7 @@ static RouterArgs router_args(const tattn_plan_s* p) {
   r.keep_max = p->cfg.keep_max;
   r.full_frac = p->cfg.full_frac;
   r.samples = std::max(1, p->cfg.entropy_samples);
+  r.price = p->cfg.price;
   return r;
 }
 
@@ -198,7 +210,7 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
   if (!q || !k || !v) return fail(TATTN_E_INVALID, "q, k and v must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
   const Dims d = make_dims(*cfg);
-  const Layout L = make_layout(d, cfg->entropy_samples);
+  const Layout L = make_layout(d, cfg->entropy_samples, cfg->mode == TATTN_MODE_PRICE);
   if (!workspace) return fail(TATTN_E_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -214,7 +226,7 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
   p->has_tiers = cfg->mode != TATTN_MODE_EXTERNAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-              p->ws, L, d};
+              p->ws, L, d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0};
   hipError_t e = launch_pool(pa, s);
   if (e != hipSuccess) {
     delete p;
@@ -344,6 +356,24 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
       }
   }
   return ok();
+}
+
+tattn_status tattn_plan_get_moments(tattn_plan_t p, float* q2, float* m2q, float* kvar, float* m2k, float* vvar,
+                                    float* m2v, float* vnorm, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (p->cfg.mode != TATTN_MODE_PRICE) return fail(TATTN_E_STATE, "second moments exist only in PRICE mode");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Dims& d = p->d;
+  const size_t nq = (size_t)d.BH * d.Nq, nk = (size_t)d.BH * d.Nk;
+  tattn_status st;
+  if (q2 && (st = copy_out(q2, p->ws + p->L.q2, nq * d.D * 4, s)) != TATTN_OK) return st;
+  if (m2q && (st = copy_out(m2q, p->ws + p->L.m2q, nq * 4, s)) != TATTN_OK) return st;
+  if (kvar && (st = copy_out(kvar, p->ws + p->L.kvar, nk * d.D * 4, s)) != TATTN_OK) return st;
+  if (m2k && (st = copy_out(m2k, p->ws + p->L.m2k, nk * 4, s)) != TATTN_OK) return st;
+  if (vvar && (st = copy_out(vvar, p->ws + p->L.vvar, nk * 4, s)) != TATTN_OK) return st;
+  if (m2v && (st = copy_out(m2v, p->ws + p->L.m2v, nk * 4, s)) != TATTN_OK) return st;
+  if (vnorm && (st = copy_out(vnorm, p->ws + p->L.vnorm, nk * 4, s)) != TATTN_OK) return st;
+  return sync(s);
 }
 
 tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {

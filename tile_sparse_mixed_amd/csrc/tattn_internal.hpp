@@ -50,12 +50,17 @@ struct Layout {
   size_t ent;                   // f64 [BH][Ssamp]   entropy of the sampled rows
   size_t kh;                    // i32 [BH]
   size_t rh;                    // f64 [BH]
+  // price router only (zero-sized otherwise): block second moments, f32
+  size_t q2, m2q;               // [BH][Nq][D], [BH][Nq]   query mean square per dim, total
+  size_t kvar, m2k;             // [BH][Nk][D], [BH][Nk]   key variance per dim, mean-square total
+  size_t vvar, m2v, vnorm;      // [BH][Nk] each           value variance total, mean-square total, mean norm
+  size_t s2;                    // f64 [BH][Nq][Nk]        within-tile score spread
   size_t flag;                  // i32 [4]   device-side error flags
   size_t total;
 };
 
 Dims make_dims(const tattn_config& c);
-Layout make_layout(const Dims& d, int entropy_samples);
+Layout make_layout(const Dims& d, int entropy_samples, bool moments);
 
 // ---- launchers (all asynchronous on `s`; return the launch status)
 struct PoolArgs {
@@ -65,6 +70,7 @@ struct PoolArgs {
   unsigned char* ws;
   Layout L;
   Dims d;
+  int moments;   // also write the second-moment statistics (price router)
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 
@@ -77,6 +83,7 @@ struct RouterArgs {
   int top_k;
   float keep_min, keep_max, full_frac;
   int samples;
+  float price;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 // Rebuild lists and counts from the tier map already in the workspace
