@@ -42,6 +42,8 @@ def parse():
                          "and launch; for the large workloads, whose full host-side generation takes minutes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for counter scaling)")
+    ap.add_argument("--price", type=float, default=None,
+                    help="route with the price router at this price instead of the workload's own tier rule")
     return ap.parse_args()
 
 
@@ -66,7 +68,7 @@ def load_traffic(config_id):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(g, cfg, budget_s):
+def cpu_baseline(g, cfg, budget_s, price=None):
     """Time the oracle (plan + forward) on one head: its full router, then as
     many query blocks as fit in the budget.  Returns dense-equivalent TFLOP/s
     of the sample, scaled like the GPU figure (4 * rows * N * d per row block)."""
@@ -76,9 +78,10 @@ def cpu_baseline(g, cfg, budget_s):
     class OC:
         block_q, block_k = cfg.block_q, cfg.block_k
         tau_hi, tau_lo = float(np.float32(cfg.tau_hi)), float(np.float32(cfg.tau_lo))
-        top_k, mode = cfg.top_k, cfg.mode
+        top_k, mode = cfg.top_k, (4 if price is not None else cfg.mode)
         keep_min, keep_max, full_frac = 0.05, 0.5, 0.1
         entropy_samples = 256
+    OC.price = float(np.float32(price)) if price is not None else 0.0
     q, k, v = g["q"][0, 0], g["k"][0, 0], g["v"][0, 0]
     t0 = time.perf_counter()
     plan = T.oracle_plan(q, k, v, OC)
@@ -122,7 +125,7 @@ def main():
     if cfg.mode not in (0, 1):
         print("bench.py: only threshold and entropy-adaptive workloads are benchmarked", file=sys.stderr)
         sys.exit(2)
-    run_mode = "adaptive" if cfg.mode == 1 else "threshold"
+    run_mode = "price" if args.price is not None else ("adaptive" if cfg.mode == 1 else "threshold")
     print(f"[bench] generating {cfg.name}: N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim}", file=sys.stderr,
           flush=True)
     tiled = 0 < args.gen_heads < cfg.heads
@@ -140,7 +143,8 @@ def main():
     def mk(mode, ws=None):
         return tsm.plan(q, k, v, block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
                         top_k=cfg.top_k, mode=mode, keep_min=cfg.keep_min, keep_max=cfg.keep_max,
-                        full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, workspace=ws)
+                        full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, workspace=ws,
+                        price=args.price or 0.0)
 
     out = torch.empty_like(q)
     plan = mk(run_mode)
@@ -238,7 +242,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(g, cfg, args.cpu_seconds)
+        cpu = cpu_baseline(g, cfg, args.cpu_seconds, args.price)
 
     res = {
         "metric": "attention kernel ms + dense-equiv TFLOPS, 32760 tok x 40 heads x d128, 1 MI355X",
@@ -252,6 +256,7 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]}={cfg.seq_len} tokens, "
                                f"{cfg.heads} heads, d={cfg.head_dim}, tiles {cfg.block_q}q x {cfg.block_k}k, "
                                + (f"tau_hi={cfg.tau_hi}, tau_lo={cfg.tau_lo}" if run_mode == "threshold" else
+                                  f"price router, price={args.price}" if run_mode == "price" else
                                   f"entropy-adaptive k_h (keep {cfg.keep_min}-{cfg.keep_max}, FULL share "
                                   f"{cfg.full_frac}, {cfg.entropy_samples} sampled query blocks)"),
                    "batch": cfg.batch, "seq_len": cfg.seq_len, "heads": cfg.heads, "head_dim": cfg.head_dim},
