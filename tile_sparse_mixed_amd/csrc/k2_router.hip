@@ -18,6 +18,7 @@
 //      diagonal tiles forced FULL; then a stable compaction into
 //      [FULL asc | LOW asc | SKIP asc] with wavefront ballots.
 // K2c  compaction only, for a tier map supplied by the caller.
+// K2d  the order in which the fused kernel takes its rows (longest last rows first).
 // Ranks and cuts use exact comparisons of the float64 p values.
 #include "tattn_device.hpp"
 #include "tattn_internal.hpp"
@@ -102,6 +103,7 @@ struct Red {
   int i[kWaves * 4];
   int hist[256];   // radix-select digit histogram
   int sel[2];      // selected digit, count of candidates above it
+  int chunk[kMaxNk / 64];   // per chunk of 64 key blocks: holds a skipped block
 };
 
 __device__ double block_max_d(double v, Red& r) {
@@ -238,16 +240,29 @@ __device__ inline void diag_range(const Dims& dm, int I, int& j0, int& j1) {
   j1 = (r1 - 1) / dm.Bk;
 }
 
-// Stable compaction of the tier row `tr` (in LDS) into lists/counts.
-__device__ void compact_row(const unsigned char* tr, int n, int16_t* list, int* counts, Red& r) {
+// Stable compaction of the tier row `tr` (in LDS) into lists/counts.  counts
+// = (n_full, n_low, n_skip, steps): steps is the number of steps the fused
+// kernel takes for the row, ceil(nF/G) + ceil(nL/G) + 2 x (chunks of 64 key
+// blocks holding a skipped block), G = 64 / Bk key blocks per step; it orders
+// the fused kernel's work.
+__device__ void compact_row(const unsigned char* tr, int n, int bk, int16_t* list, int* counts, Red& r) {
   int c[3] = {0, 0, 0};
-  for (int J = threadIdx.x; J < n; J += kThreads) c[tr[J]]++;
+  const int nch = (n + 63) / 64;
+  for (int i = threadIdx.x; i < nch; i += kThreads) r.chunk[i] = 0;
+  __syncthreads();
+  for (int J = threadIdx.x; J < n; J += kThreads) {
+    c[tr[J]]++;
+    if (tr[J] == TATTN_SKIP) r.chunk[J >> 6] = 1;
+  }
   const int nF = block_sum_i(c[2], r), nL = block_sum_i(c[1], r), nS = block_sum_i(c[0], r);
   if (threadIdx.x == 0) {
+    int snc = 0;
+    for (int i = 0; i < nch; i++) snc += r.chunk[i];
+    const int G = 64 / bk;
     counts[0] = nF;
     counts[1] = nL;
     counts[2] = nS;
-    counts[3] = 0;
+    counts[3] = (nF + G - 1) / G + (nL + G - 1) / G + 2 * snc;
   }
   int base[3] = {nF + nL, nF, 0};   // indexed by tier value: SKIP, LOW, FULL
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -316,7 +331,59 @@ __device__ inline unsigned char price_tier(const PriceTile& x, double pt, double
   return t;
 }
 
-enum { K2B_TIERS = 0, K2B_ENTROPY = 1 };
+// The price router's tier row: p is exported; the decision uses the shares
+// corrected by each tile's spread gain, p~ = softmax_J(S + g).  pv holds p on
+// entry and is reused for p~.
+__device__ void price_row(const RouterArgs& a, int bh, int64_t row, const double* S, double* pv,
+                                       unsigned char* tr, float* pout, Red& r) {
+  const Dims& dm = a.d;
+  const int n = dm.Nk;
+  // p is exported; the decision uses the shares corrected by each tile's
+  // spread gain, p~ = softmax_J(S + g)
+  const double* s2r = reinterpret_cast<const double*>(a.ws + a.L.s2) + row * n;
+  const float* m2k = reinterpret_cast<const float*>(a.ws + a.L.m2k) + (int64_t)bh * n;
+  const float* vvar = reinterpret_cast<const float*>(a.ws + a.L.vvar) + (int64_t)bh * n;
+  const float* m2v = reinterpret_cast<const float*>(a.ws + a.L.m2v) + (int64_t)bh * n;
+  const float* vnorm = reinterpret_cast<const float*>(a.ws + a.L.vnorm) + (int64_t)bh * n;
+  const double m2q = reinterpret_cast<const float*>(a.ws + a.L.m2q)[row];
+  const double nfull = dm.Bk, nlast = dm.N - (dm.Nk - 1) * dm.Bk;
+  const double lnf = log(nfull), lnl = log(nlast);
+  double mx = -INFINITY;
+  for (int J = threadIdx.x; J < n; J += kThreads) {
+    pout[J] = static_cast<float>(pv[J]);
+    const double x = S[J] + spread_gain(s2r[J], J == n - 1 ? lnl : lnf);
+    pv[J] = x;
+    mx = fmax(mx, x);
+  }
+  mx = block_max_d(mx, r);
+  double sum = 0.0;
+  for (int J = threadIdx.x; J < n; J += kThreads) {
+    const double e = exp(pv[J] - mx);
+    pv[J] = e;
+    sum += e;
+  }
+  sum = block_sum_d(sum, r);
+  const double price = a.price, cost_skip = 1.5 / static_cast<double>(dm.Bk);
+  const double cu = 2.0 * kE4m3U * kE4m3U / 3.0, dd = static_cast<double>(dm.D) * static_cast<double>(dm.D);
+  for (int J = threadIdx.x; J < n; J += kThreads) {
+    PriceTile x;
+    x.s2 = s2r[J];
+    x.n = J == n - 1 ? nlast : nfull;
+    x.vnorm = vnorm[J];
+    x.vvar = vvar[J];
+    x.m2v = m2v[J];
+    {
+#pragma clang fp contract(off)
+      x.sl2 = cu * (m2q * static_cast<double>(m2k[J])) / dd;
+    }
+    tr[J] = price_tier(x, pv[J] / sum, price, cost_skip);
+  }
+}
+
+// K2B_PRICE is the tier pass of the price router: its error model needs many
+// more registers, so it is an instance of its own and the other modes keep
+// their occupancy.
+enum { K2B_TIERS = 0, K2B_ENTROPY = 1, K2B_PRICE = 2 };
 
 inline size_t k2b_lds_bytes(int nk) { return ((size_t)nk * 10 + 15) / 16 * 16; }
 
@@ -369,7 +436,9 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
   }
   float* pout = reinterpret_cast<float*>(a.ws + a.L.p) + row * n;
   unsigned char* tout = a.ws + a.L.tiers + row * n;
-  if (a.mode == TATTN_MODE_ALL_FULL) {
+  if constexpr (WHAT == K2B_PRICE) {
+    price_row(a, bh, row, S, pv, tr, pout, r);
+  } else if (a.mode == TATTN_MODE_ALL_FULL) {
     for (int J = threadIdx.x; J < n; J += kThreads) {
       tr[J] = TATTN_FULL;
       pout[J] = 0.0f;
@@ -383,47 +452,6 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
       if (a.top_k > 0 && !keep[J]) t = TATTN_SKIP;
       tr[J] = t;
       pout[J] = static_cast<float>(p);
-    }
-  } else if (a.mode == TATTN_MODE_PRICE) {
-    // p is exported; the decision uses the shares corrected by each tile's
-    // spread gain, p~ = softmax_J(S + g)
-    const double* s2r = reinterpret_cast<const double*>(a.ws + a.L.s2) + row * n;
-    const float* m2k = reinterpret_cast<const float*>(a.ws + a.L.m2k) + (int64_t)bh * n;
-    const float* vvar = reinterpret_cast<const float*>(a.ws + a.L.vvar) + (int64_t)bh * n;
-    const float* m2v = reinterpret_cast<const float*>(a.ws + a.L.m2v) + (int64_t)bh * n;
-    const float* vnorm = reinterpret_cast<const float*>(a.ws + a.L.vnorm) + (int64_t)bh * n;
-    const double m2q = reinterpret_cast<const float*>(a.ws + a.L.m2q)[row];
-    const double nfull = dm.Bk, nlast = dm.N - (dm.Nk - 1) * dm.Bk;
-    const double lnf = log(nfull), lnl = log(nlast);
-    double mx = -INFINITY;
-    for (int J = threadIdx.x; J < n; J += kThreads) {
-      pout[J] = static_cast<float>(pv[J]);
-      const double x = S[J] + spread_gain(s2r[J], J == n - 1 ? lnl : lnf);
-      pv[J] = x;
-      mx = fmax(mx, x);
-    }
-    mx = block_max_d(mx, r);
-    double sum = 0.0;
-    for (int J = threadIdx.x; J < n; J += kThreads) {
-      const double e = exp(pv[J] - mx);
-      pv[J] = e;
-      sum += e;
-    }
-    sum = block_sum_d(sum, r);
-    const double price = a.price, cost_skip = 1.5 / static_cast<double>(dm.Bk);
-    const double cu = 2.0 * kE4m3U * kE4m3U / 3.0, dd = static_cast<double>(dm.D) * static_cast<double>(dm.D);
-    for (int J = threadIdx.x; J < n; J += kThreads) {
-      PriceTile x;
-      x.s2 = s2r[J];
-      x.n = J == n - 1 ? nlast : nfull;
-      x.vnorm = vnorm[J];
-      x.vvar = vvar[J];
-      x.m2v = m2v[J];
-      {
-#pragma clang fp contract(off)
-        x.sl2 = cu * (m2q * static_cast<double>(m2k[J])) / dd;
-      }
-      tr[J] = price_tier(x, pv[J] / sum, price, cost_skip);
     }
   } else {  // ADAPTIVE
     const int S2 = min(a.samples, dm.Nq);
@@ -456,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
   for (int J = j0 + threadIdx.x; J <= j1; J += kThreads) tr[J] = TATTN_FULL;
   __syncthreads();
   for (int J = threadIdx.x; J < n; J += kThreads) tout[J] = tr[J];
-  compact_row(tr, n, reinterpret_cast<int16_t*>(a.ws + a.L.lists) + row * n,
+  compact_row(tr, n, dm.Bk, reinterpret_cast<int16_t*>(a.ws + a.L.lists) + row * n,
               reinterpret_cast<int*>(a.ws + a.L.counts) + row * 4, r);
 }
 
@@ -475,8 +503,66 @@ __global__ __launch_bounds__(kThreads) void k2c_compact(RouterArgs a) {
   for (int J = j0 + threadIdx.x; J <= j1; J += kThreads) tr[J] = TATTN_FULL;
   __syncthreads();
   for (int J = threadIdx.x; J < n; J += kThreads) tg[J] = tr[J];
-  compact_row(tr, n, reinterpret_cast<int16_t*>(a.ws + a.L.lists) + row * n,
+  compact_row(tr, n, dm.Bk, reinterpret_cast<int16_t*>(a.ws + a.L.lists) + row * n,
               reinterpret_cast<int*>(a.ws + a.L.counts) + row * 4, r);
+}
+
+// ------------------------------------------------------------------ K2d work order
+// The fused kernel takes its (b, h, I) work items in the order written here.
+// Rows stay in their natural head-major order (a couple of heads in flight, so
+// their K/V stay in the shared last-level cache) except the last kTailRows,
+// which are sorted by descending step count: the longest rows start first and
+// the short ones fill the slots that free up at the end, so the grid does not
+// finish on a few long rows.  Rows with equal counts land in any order (the
+// result of every row is independent of when it runs).
+constexpr int kTailRows = 2048;
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBins = 8192;   // step counts: <= Nk + 2 * ceil(Nk / 64) < 8192
+constexpr int kBinsPerThread = kOrderBins / kOrderThreads;
+
+__global__ __launch_bounds__(kOrderThreads) void k2d_order(RouterArgs a) {
+  __shared__ int hist[kOrderBins];   // indexed by u = kOrderBins - 1 - count (descending counts)
+  __shared__ int wsum[kOrderThreads / 64];
+  const Dims& dm = a.d;
+  const int total = dm.BH * dm.Nq;
+  const int T = min(total, kTailRows), head = total - T;
+  const int* counts = reinterpret_cast<const int*>(a.ws + a.L.counts);
+  int* order = reinterpret_cast<int*>(a.ws + a.L.order);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < head; i += kOrderThreads) order[i] = i;
+  for (int i = t; i < kOrderBins; i += kOrderThreads) hist[i] = 0;
+  __syncthreads();
+  for (int i = t; i < T; i += kOrderThreads)
+    atomicAdd(&hist[kOrderBins - 1 - min(counts[(head + i) * 4 + 3], kOrderBins - 1)], 1);
+  __syncthreads();
+  // exclusive prefix over u: thread t owns u in [8t, 8t + 8)
+  int loc[kBinsPerThread], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; j++) {
+    loc[j] = hist[kBinsPerThread * t + j];
+    sum += loc[j];
+  }
+  int inc = sum;   // inclusive scan of the thread sums inside the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += up;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int ww = 0; ww < w; ww++) base += wsum[ww];
+  int run = base + inc - sum;
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; j++) {
+    hist[kBinsPerThread * t + j] = run;
+    run += loc[j];
+  }
+  __syncthreads();
+  for (int i = t; i < T; i += kOrderThreads) {
+    const int u = kOrderBins - 1 - min(counts[(head + i) * 4 + 3], kOrderBins - 1);
+    order[head + atomicAdd(&hist[u], 1)] = head + i;
+  }
 }
 
 }  // namespace
@@ -508,7 +594,13 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k2b_rows<K2B_TIERS>), dim3(d.BH * d.Nq), dim3(kThreads), k2b_lds_bytes(d.Nk), s, a);
+  if (a.mode == TATTN_MODE_PRICE)
+    hipLaunchKernelGGL((k2b_rows<K2B_PRICE>), dim3(d.BH * d.Nq), dim3(kThreads), k2b_lds_bytes(d.Nk), s, a);
+  else
+    hipLaunchKernelGGL((k2b_rows<K2B_TIERS>), dim3(d.BH * d.Nq), dim3(kThreads), k2b_lds_bytes(d.Nk), s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2d_order, dim3(1), dim3(kOrderThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -516,6 +608,9 @@ hipError_t launch_compact(const RouterArgs& a, hipStream_t s) {
   const Dims& d = a.d;
   if (d.Nk > kRouterMaxNk) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k2c_compact, dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2d_order, dim3(1), dim3(kOrderThreads), 0, s, a);
   return hipGetLastError();
 }
 

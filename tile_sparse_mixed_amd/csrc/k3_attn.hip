@@ -132,13 +132,15 @@ void k3_attn(AttnArgs a) {
   __shared__ int snc;
 
   const Dims& dm = a.d;
-  // ---- work mapping: workgroup x takes (b, h, I) = x in row-major order.  The
-  // dispatcher deals consecutive workgroups round-robin to the 8 XCDs, so the
-  // ~2 heads in flight at a time are shared by all XCDs and their K/V tiles
-  // (~34 MB per head at d = 128) stay resident in the shared 256 MB MALL.
-  // Giving each XCD its own contiguous range of heads instead put 8 heads in
-  // flight (~270 MB) and measured ~15x the compulsory HBM reads.
-  const int w_item = blockIdx.x;
+  // ---- work mapping: workgroup x takes row (b, h, I) = order[x], which is the
+  // row-major order except that the last rows are sorted longest first (the
+  // router's work order).  The dispatcher deals consecutive workgroups
+  // round-robin to the 8 XCDs, so the ~2 heads in flight at a time are shared
+  // by all XCDs and their K/V tiles (~34 MB per head at d = 128) stay resident
+  // in the shared 256 MB MALL.  Giving each XCD its own contiguous range of
+  // heads instead put 8 heads in flight (~270 MB) and measured ~15x the
+  // compulsory HBM reads.
+  const int w_item = reinterpret_cast<const int*>(a.ws + a.L.order)[blockIdx.x];
   const int bh = w_item / dm.Nq, I = w_item % dm.Nq;
   const int bidx = bh / dm.H, hidx = bh % dm.H;
   const int64_t toff = (int64_t)bidx * dm.sb + (int64_t)hidx * dm.sh;

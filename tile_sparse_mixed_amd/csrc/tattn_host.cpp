@@ -93,6 +93,7 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments) {
   L.tiers = take(BH * Nq * Nk);
   L.lists = take(BH * Nq * Nk * 2);
   L.counts = take(BH * Nq * 4 * 4);
+  L.order = take(BH * Nq * 4);
   L.ent = take(BH * S * 8);
   L.kh = take(BH * 4);
   L.rh = take(BH * 8);

@@ -46,7 +46,8 @@ struct Layout {
   size_t p;                     // f32 [BH][Nq][Nk]
   size_t tiers;                 // u8  [BH][Nq][Nk]
   size_t lists;                 // i16 [BH][Nq][Nk]
-  size_t counts;                // i32 [BH][Nq][4]
+  size_t counts;                // i32 [BH][Nq][4]   n_full, n_low, n_skip, fused-kernel steps
+  size_t order;                 // i32 [BH * Nq]     the fused kernel's row order
   size_t ent;                   // f64 [BH][Ssamp]   entropy of the sampled rows
   size_t kh;                    // i32 [BH]
   size_t rh;                    // f64 [BH]
