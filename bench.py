@@ -205,6 +205,9 @@ def main():
 
     ms_plan, med_plan, min_plan = timed(lambda: mk(run_mode, ws), args.steps)
     ms_k3, med_k3, min_k3 = timed(lambda: tsm.forward(plan, q, k, v, out), args.steps)
+    # plan reuse across diffusion steps: re-pool and re-quantise (K1) only
+    ms_replan = timed(lambda: tsm.replan(plan, q, k, v), args.steps)[0]
+    ms_reuse = timed(lambda: (tsm.replan(plan, q, k, v), tsm.forward(plan, q, k, v, out)), args.steps)[0]
 
     ms_allfull = None
     quality = None
@@ -262,6 +265,7 @@ def main():
                    "batch": cfg.batch, "seq_len": cfg.seq_len, "heads": cfg.heads, "head_dim": cfg.head_dim},
         "kernel_ms": {"plan_k1_k2": round(ms_plan, 4), "forward_k3": round(ms_k3, 4),
                       "forward_k3_all_full": None if ms_allfull is None else round(ms_allfull, 4),
+                      "replan_k1": round(ms_replan, 4), "step_with_plan_reuse": round(ms_reuse, 4),
                       "plan_median": round(med_plan, 4), "plan_min": round(min_plan, 4),
                       "forward_median": round(med_k3, 4), "forward_min": round(min_k3, 4)},
         "speedup_vs_all_full": None if ms_allfull is None else round(ms_allfull / ms_k3, 3),

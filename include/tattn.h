@@ -158,6 +158,20 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
 tattn_status tattn_forward(tattn_plan_t plan, const void* q, const void* k, const void* v, void* o,
                            void* stream);
 
+/*
+ * Reuse a plan for the next diffusion step ("APT": attention probabilities
+ * predicted across timesteps from their temporal similarity): the tier map,
+ * lists and work order stay those of the step the plan was routed on, and
+ * step 1 of tattn_plan (block means, scales, E4M3 codes, the transposed and
+ * low-tier V copies, and in PRICE mode the second moments) is recomputed
+ * from q, k, v, the next step's tensors, which must have the config's shape
+ * and strides.  The router is not run.  Afterwards the plan belongs to these
+ * k and v (tattn_forward checks the pointers).  Asynchronous on `stream`;
+ * TATTN_E_INVALID for a NULL or misaligned pointer, TATTN_E_STATE for a plan
+ * that has no tiers yet.
+ */
+tattn_status tattn_replan(tattn_plan_t plan, const void* q, const void* k, const void* v, void* stream);
+
 /* SYNC.  Replace the plan's tier map with a host map [B, H, Nq, Nk] of bytes in
  * {0, 1, 2}; diagonal tiles are forced FULL and the lists rebuilt.  Only for a
  * plan built in TATTN_MODE_EXTERNAL (TATTN_E_STATE otherwise); a byte outside

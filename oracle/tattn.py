@@ -494,6 +494,14 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
                 q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info)
 
 
+def oracle_replan(q, k, v, prev_plan, cfg_like):
+    """Plan reuse across diffusion steps (APT: attention probabilities
+    predicted across timesteps from their temporal similarity): the previous
+    step's tier map is taken as the prediction for this step, and only the
+    block means and fp8 codes are recomputed from this step's q, k, v."""
+    return oracle_plan(q, k, v, cfg_like, mode=3, external_tiers=prev_plan["tiers"])
+
+
 def oracle_forward(q, k, v, plan, bq, bk, rows=None):
     return attention_forward(q, k, v, plan["tiers"], bq, bk, plan["kbar"], plan["vbar"],
                              plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],

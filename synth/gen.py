@@ -97,3 +97,23 @@ def generate(cfg, seed: int = 0, f_cycles: float = F_CYCLES, a_gain: float = A_G
             bits[name] = bb
             arr[...] = bf16_bits_to_f32(bb)
     return {"q": q, "k": k, "v": v, "bits": bits, "temps": temps}
+
+
+def drift_step(g, cfg, step: int, sigma: float, seed: int = 0):
+    """The inputs of the next diffusion step: every element of Q, K and V moves
+    by independent N(0, sigma^2) noise (a random walk in time, so consecutive
+    steps stay similar), then rounds to bf16 again for bf16 workloads.  Drawn
+    from SeedSequence([seed, workload, 1000 + step]).  Returns a dict shaped
+    like generate()'s."""
+    sid = cfg.seed_cfg_id or cfg.cfg_id
+    rng = np.random.default_rng(np.random.SeedSequence([seed, sid, 1000 + step]))
+    out = {"temps": g["temps"]}
+    bits = None if g["bits"] is None else {}
+    for name in ("q", "k", "v"):
+        x = g[name] + np.float32(sigma) * rng.standard_normal(g[name].shape, dtype=np.float32)
+        if bits is not None:
+            bits[name] = to_bf16_bits(x)
+            x = bf16_bits_to_f32(bits[name])
+        out[name] = x.astype(np.float32)
+    out["bits"] = bits
+    return out

@@ -32,3 +32,18 @@ def test_tiny_is_fp32_and_temperatures():
     assert g["bits"] is None and g["q"].shape == (1, 2, 256, 64)
     g3 = generate(CONFIGS[3].with_(grid=(1, 2, 8)), heads=[0])
     assert np.all((g3["temps"] >= 0.5) & (g3["temps"] <= 2.0))
+
+
+def test_drift_step_is_a_seeded_small_move():
+    from synth import CONFIGS, drift_step, generate
+    cfg = CONFIGS[2].with_(heads=2)
+    g = generate(cfg)
+    a = drift_step(g, cfg, 1, 0.05)
+    b = drift_step(g, cfg, 1, 0.05)
+    c = drift_step(g, cfg, 2, 0.05)
+    for n in ("q", "k", "v"):
+        assert np.array_equal(a["bits"][n], b["bits"][n])
+        assert not np.array_equal(a["bits"][n], c["bits"][n])
+        d = a[n] - g[n]
+        assert abs(float(d.std()) - 0.05) < 0.005          # the walk's step size (plus bf16 rounding)
+        assert np.array_equal(to_bf16_bits(a[n]), a["bits"][n])

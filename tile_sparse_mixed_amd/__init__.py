@@ -14,7 +14,7 @@ import os
 
 import numpy as np
 
-__all__ = ["plan", "forward", "Plan", "TattnError", "load_library", "Config", "Stats",
+__all__ = ["plan", "replan", "forward", "Plan", "TattnError", "load_library", "Config", "Stats",
            "MODE_THRESHOLD", "MODE_ADAPTIVE", "MODE_ALL_FULL", "MODE_EXTERNAL", "MODE_PRICE",
            "SKIP", "LOW", "FULL"]
 
@@ -59,6 +59,7 @@ _SIGS = {
     "tattn_plan": (ctypes.c_int, [ctypes.POINTER(Config), _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
                                   ctypes.POINTER(_VP)]),
     "tattn_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP]),
+    "tattn_replan": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_set_tiers": (ctypes.c_int, [_VP, _VP, _VP]),
     "tattn_plan_get_tiers": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_get_lists": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
@@ -237,6 +238,19 @@ def plan(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, m
     cfg = make_config(B, H, N, d, block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
                       full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price)
     return Plan(cfg, q, k, v, workspace=workspace)
+
+
+def replan(p: Plan, q, k, v) -> Plan:
+    """Reuse ``p``'s tiers for the next diffusion step: recompute the block
+    means and fp8 copies from q, k, v (same shape and strides) without
+    re-routing.  Returns ``p``, now bound to these k and v."""
+    _check_tensors(q, k, v)
+    if tuple(q.shape) != p._shape(p.cfg.seq_len, p.cfg.head_dim) or \
+            tuple(q.stride()[:3]) != (p.cfg.stride_b, p.cfg.stride_h, p.cfg.stride_n):
+        raise ValueError("replan needs tensors of the plan's shape and strides")
+    _check(load_library().tattn_replan(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), _stream()))
+    p._k, p._v = k, v
+    return p
 
 
 def forward(p: Plan, q, k, v, out=None):

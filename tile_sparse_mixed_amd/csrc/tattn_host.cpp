@@ -257,6 +257,20 @@ tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const v
   return ok();
 }
 
+tattn_status tattn_replan(tattn_plan_t p, const void* q, const void* k, const void* v, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!q || !k || !v) return fail(TATTN_E_INVALID, "q, k and v must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
+  if (!p->has_tiers) return fail(TATTN_E_STATE, "plan has no tiers yet (nothing to reuse)");
+  PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+              p->ws, p->L, p->d, p->cfg.mode == TATTN_MODE_PRICE ? 1 : 0};
+  hipError_t e = launch_pool(pa, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+  p->k = k;
+  p->v = v;
+  return ok();
+}
+
 static tattn_status copy_out(void* dst, const unsigned char* src, size_t bytes, hipStream_t s) {
   hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
   if (e != hipSuccess) return hip_fail(e, "device-to-host copy");
