@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", default="wan_like",
+                    choices=["tiny", "small", "wan_like", "hunyuan_like", "fine_adaptive"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-allfull", action="store_true", help="skip the all-full comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -55,7 +56,7 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(config_id):
+def load_traffic(workload):
     """HBM traffic of one K3 launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source and this workload; else None."""
     try:
@@ -63,7 +64,7 @@ def load_traffic(config_id):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash() or t.get("config_id") != config_id:
+    if t.get("source_hash") != source_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -121,7 +122,7 @@ def main():
     import tile_sparse_mixed_amd as tsm
     from synth import CONFIGS, generate
 
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[args.workload]
     if cfg.mode not in (0, 1):
         print("bench.py: only threshold and entropy-adaptive workloads are benchmarked", file=sys.stderr)
         sys.exit(2)
@@ -240,7 +241,7 @@ def main():
     bf16_equiv = st["flops_bf16"] + st["flops_fp8"] * PEAK_BF16 / PEAK_FP8
     achieved = bf16_equiv / (ms_k3 * 1e-3) / 1e12
     tiles = st["n_full"] + st["n_low"] + st["n_skip"]
-    traffic = load_traffic(args.config)
+    traffic = load_traffic(args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -19,7 +19,7 @@ MODE_EXTERNAL = 3
 
 @dataclass(frozen=True)
 class WorkloadConfig:
-    cfg_id: int                 # 1..5; seeds the generator stream
+    stream: int                 # generator stream id (seeds the random draws)
     name: str
     batch: int
     heads: int
@@ -38,7 +38,7 @@ class WorkloadConfig:
     noise_sigma: float = 0.5
     temperature: bool = False   # per-head temperature T_h ~ U(0.5, 2) divides Q
     input_fp32: bool = False    # the tiny workload is specified in fp32
-    seed_cfg_id: int = 0        # generator stream to draw from (0: own cfg_id)
+    seed_stream: int = 0        # draw from another workload's stream (0: own stream)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -59,18 +59,18 @@ class WorkloadConfig:
 
 
 CONFIGS = {
-    1: WorkloadConfig(1, "tiny", 1, 2, (4, 8, 8), 64, 64, 64, 0.05, 0.005,
-                      noise_sigma=0.3, input_fp32=True),
-    2: WorkloadConfig(2, "small", 1, 12, (8, 16, 16), 64, 128, 64, 0.02, 0.002,
-                      noise_sigma=0.5),
-    3: WorkloadConfig(3, "wan_like", 1, 40, (21, 30, 52), 128, 128, 64, 0.01, 0.001,
-                      noise_sigma=0.5, temperature=True),
-    4: WorkloadConfig(4, "hunyuan_like", 1, 24, (33, 45, 80), 128, 128, 64, 0.01, 0.001,
-                      noise_sigma=0.5, temperature=True),
-    5: WorkloadConfig(5, "fine_adaptive", 1, 40, (21, 30, 52), 128, 64, 16, 0.01, 0.001,
-                      mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_cfg_id=3),
+    "tiny": WorkloadConfig(1, "tiny", 1, 2, (4, 8, 8), 64, 64, 64, 0.05, 0.005,
+                           noise_sigma=0.3, input_fp32=True),
+    "small": WorkloadConfig(2, "small", 1, 12, (8, 16, 16), 64, 128, 64, 0.02, 0.002,
+                            noise_sigma=0.5),
+    "wan_like": WorkloadConfig(3, "wan_like", 1, 40, (21, 30, 52), 128, 128, 64, 0.01, 0.001,
+                               noise_sigma=0.5, temperature=True),
+    "hunyuan_like": WorkloadConfig(4, "hunyuan_like", 1, 24, (33, 45, 80), 128, 128, 64, 0.01, 0.001,
+                                   noise_sigma=0.5, temperature=True),
+    "fine_adaptive": WorkloadConfig(5, "fine_adaptive", 1, 40, (21, 30, 52), 128, 64, 16, 0.01, 0.001,
+                                    mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
 }
 
 
-def get_config(cfg_id: int) -> WorkloadConfig:
-    return CONFIGS[cfg_id]
+def get_workload(name: str) -> WorkloadConfig:
+    return CONFIGS[name]

@@ -8,7 +8,7 @@ plus noise").  Nearby tokens therefore carry similar keys, which is the
 spatio-temporal correlation that makes tile-level routing worthwhile.
 
 Recipe (fixed draw order, one numpy Generator per workload):
-  rng = default_rng(SeedSequence([seed, cfg_id]))
+  rng = default_rng(SeedSequence([seed, stream]))
   Omega (8x3) ~ N(0, (2*pi*f)^2);  beta (8) ~ U[0, 2*pi)
   per head h: W_Q, W_K (8 x d) ~ N(0, a^2/8), W_V ~ N(0, 1/8) so that V is
               unit-scale; T_h ~ U(0.5, 2) if the
@@ -58,7 +58,7 @@ def generate(cfg, seed: int = 0, f_cycles: float = F_CYCLES, a_gain: float = A_G
     random stream is advanced identically, so head h's tensors do not depend on
     which other heads were requested.
     """
-    sid = cfg.seed_cfg_id or cfg.cfg_id
+    sid = cfg.seed_stream or cfg.stream
     rng = np.random.default_rng(np.random.SeedSequence([seed, sid]))
     d = cfg.head_dim
     sigma = cfg.noise_sigma if noise_sigma is None else noise_sigma
@@ -105,7 +105,7 @@ def drift_step(g, cfg, step: int, sigma: float, seed: int = 0):
     steps stay similar), then rounds to bf16 again for bf16 workloads.  Drawn
     from SeedSequence([seed, workload, 1000 + step]).  Returns a dict shaped
     like generate()'s."""
-    sid = cfg.seed_cfg_id or cfg.cfg_id
+    sid = cfg.seed_stream or cfg.stream
     rng = np.random.default_rng(np.random.SeedSequence([seed, sid, 1000 + step]))
     out = {"temps": g["temps"]}
     bits = None if g["bits"] is None else {}

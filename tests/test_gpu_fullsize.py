@@ -19,8 +19,8 @@ from gpu_cases import OracleCfg, band_mask
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    "wan_32760x40": (3, 4, [0, 21, 39]),          # workload id, generated heads, sampled heads
-    "hunyuan_118800x24": (4, 2, [0, 23]),
+    "wan_32760x40": ("wan_like", 4, [0, 21, 39]),          # workload, generated heads, sampled heads
+    "hunyuan_118800x24": ("hunyuan_like", 2, [0, 23]),
 }
 
 
@@ -41,8 +41,8 @@ def _device_tiled(bits, heads):
 @pytest.mark.parametrize("name", list(CASES))
 def test_full_size_sampled(name):
     import tile_sparse_mixed_amd as tsm
-    cfg_id, gen_heads, sample_heads = CASES[name]
-    cfg = CONFIGS[cfg_id]
+    wl, gen_heads, sample_heads = CASES[name]
+    cfg = CONFIGS[wl]
     _log(f"[full {name}] N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} (generating {gen_heads} heads)")
     g = generate(cfg.with_(heads=gen_heads))
     dev = _device_tiled(g["bits"], cfg.heads)
@@ -81,7 +81,7 @@ def test_full_size_fine_adaptive():
     tiles, k_h from the entropy of p on 256 sampled query blocks per head."""
     import tile_sparse_mixed_amd as tsm
     import torch
-    cfg = CONFIGS[5]
+    cfg = CONFIGS["fine_adaptive"]
     gen_heads, sample_heads = 3, [0, 20, 38]
     _log(f"[full fine_adaptive] N={cfg.seq_len} H={cfg.heads} tile={cfg.block_q}x{cfg.block_k}")
     g = generate(cfg.with_(heads=gen_heads))

@@ -68,7 +68,7 @@ def test_batch_and_token_major_layout(tiles):
     import tile_sparse_mixed_amd as tsm
     import torch
     bq, bk = tiles
-    cfg = CONFIGS[2].with_(batch=2, heads=3, grid=(4, 9, 13), block_q=bq, block_k=bk)   # N = 468
+    cfg = CONFIGS["small"].with_(batch=2, heads=3, grid=(4, 9, 13), block_q=bq, block_k=bk)   # N = 468
     g = generate(cfg)
     dev = _bnhd(g["bits"])
     assert dev["q"].stride() == (cfg.seq_len * cfg.heads * 64, 64, cfg.heads * 64, 1)
@@ -93,7 +93,7 @@ def test_short_sequences(n, tiles):
     """One (partial) query block; with 16-key blocks, a few key blocks."""
     import tile_sparse_mixed_amd as tsm
     bq, bk = tiles
-    cfg = CONFIGS[2].with_(heads=2, grid=(1, 1, n), block_q=bq, block_k=bk)
+    cfg = CONFIGS["small"].with_(heads=2, grid=(1, 1, n), block_q=bq, block_k=bk)
     g = generate(cfg)
     dev = _contig(g["bits"])
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=bq, block_k=bk, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
@@ -109,7 +109,7 @@ def test_short_sequences(n, tiles):
 
 def test_top_k_with_16_key_blocks():
     import tile_sparse_mixed_amd as tsm
-    cfg = CONFIGS[5].with_(grid=(2, 10, 50), heads=2, mode=0, top_k=9)   # N = 1000, Nk = 63
+    cfg = CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0, top_k=9)   # N = 1000, Nk = 63
     g = generate(cfg)
     dev = _contig(g["bits"])
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi,

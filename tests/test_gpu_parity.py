@@ -17,14 +17,14 @@ from gpu_cases import OracleCfg, band_mask, device_inputs, gpu_plan, oracle_head
 pytestmark = pytest.mark.gpu
 
 SMALL = {
-    "tiny": CONFIGS[1],
-    "small": CONFIGS[2],
-    "ragged128": CONFIGS[3].with_(grid=(2, 10, 50), heads=3),          # N=1000: Nq=8 (last 104), Nk=16 (last 40)
-    "ragged64x64": CONFIGS[2].with_(grid=(3, 7, 9), heads=2, block_q=64, head_dim=128),   # N=189
-    "d64_ragged": CONFIGS[2].with_(grid=(5, 9, 13), heads=2),         # N=585
+    "tiny": CONFIGS["tiny"],
+    "small": CONFIGS["small"],
+    "ragged128": CONFIGS["wan_like"].with_(grid=(2, 10, 50), heads=3),          # N=1000: Nq=8 (last 104), Nk=16 (last 40)
+    "ragged64x64": CONFIGS["small"].with_(grid=(3, 7, 9), heads=2, block_q=64, head_dim=128),   # N=189
+    "d64_ragged": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2),         # N=585
     # 64q x 16k tiles: FULL / LOW steps gather four key blocks
-    "fine64x16": CONFIGS[5].with_(grid=(2, 10, 50), heads=2, mode=0),  # N=1000: Nq=16 (last 40), Nk=63 (last 8)
-    "fine_d64": CONFIGS[2].with_(grid=(5, 9, 13), heads=2, block_q=64, block_k=16),   # N=585: Nk=37 (last 9)
+    "fine64x16": CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0),  # N=1000: Nq=16 (last 40), Nk=63 (last 8)
+    "fine_d64": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2, block_q=64, block_k=16),   # N=585: Nk=37 (last 9)
 }
 
 
@@ -77,7 +77,7 @@ def test_router_tiers_and_lists(case):
 
 
 def test_router_top_k():
-    cfg = CONFIGS[2].with_(heads=3, top_k=7)
+    cfg = CONFIGS["small"].with_(heads=3, top_k=7)
     g, dev = device_inputs(cfg)
     oc = OracleCfg(cfg)
     p = gpu_plan(dev, cfg)
@@ -157,7 +157,7 @@ def test_threshold_end_to_end_bf16_out(case):
 
 
 def test_constant_keys_skip_is_exact():
-    cfg = CONFIGS[3].with_(grid=(2, 10, 50), heads=2)
+    cfg = CONFIGS["wan_like"].with_(grid=(2, 10, 50), heads=2)
     import torch
     import tile_sparse_mixed_amd as tsm
     g, dev = device_inputs(cfg)
@@ -181,7 +181,7 @@ def test_constant_keys_skip_is_exact():
 
 
 def test_unit_values_give_unit_output():
-    cfg = CONFIGS[3].with_(grid=(2, 10, 50), heads=2)
+    cfg = CONFIGS["wan_like"].with_(grid=(2, 10, 50), heads=2)
     import torch
     import tile_sparse_mixed_amd as tsm
     g, dev = device_inputs(cfg)

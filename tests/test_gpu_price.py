@@ -16,12 +16,12 @@ from gpu_cases import OracleCfg
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # name: (config, overrides, projection gain or None)
-    "small_gain1": (2, dict(heads=3), 1.0),
-    "small": (2, dict(heads=2), None),
-    "d128_ragged": (3, dict(heads=2, grid=(3, 10, 23)), None),           # N = 690
-    "d128_ragged_gain1": (3, dict(heads=2, grid=(3, 10, 23), temperature=False), 1.0),
-    "fine64x16": (5, dict(heads=2, grid=(2, 10, 50), mode=4), 1.0),        # N = 1000, Nk = 63
+    # name: (workload, overrides, projection gain or None)
+    "small_gain1": ("small", dict(heads=3), 1.0),
+    "small": ("small", dict(heads=2), None),
+    "d128_ragged": ("wan_like", dict(heads=2, grid=(3, 10, 23)), None),           # N = 690
+    "d128_ragged_gain1": ("wan_like", dict(heads=2, grid=(3, 10, 23), temperature=False), 1.0),
+    "fine64x16": ("fine_adaptive", dict(heads=2, grid=(2, 10, 50), mode=4), 1.0),   # N = 1000, Nk = 63
 }
 
 

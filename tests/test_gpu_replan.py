@@ -14,9 +14,9 @@ from gpu_cases import OracleCfg
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    "small": CONFIGS[2].with_(heads=2),
-    "d128_ragged": CONFIGS[3].with_(heads=2, grid=(3, 10, 23)),
-    "fine64x16": CONFIGS[5].with_(heads=2, grid=(2, 10, 50)),
+    "small": CONFIGS["small"].with_(heads=2),
+    "d128_ragged": CONFIGS["wan_like"].with_(heads=2, grid=(3, 10, 23)),
+    "fine64x16": CONFIGS["fine_adaptive"].with_(heads=2, grid=(2, 10, 50)),
 }
 
 

@@ -18,7 +18,7 @@ def _cfg(c):
 
 
 def test_reuse_on_the_same_step_is_the_plan():
-    c = CONFIGS[2].with_(heads=1)
+    c = CONFIGS["small"].with_(heads=1)
     g = generate(c)
     q, k, v = g["q"][0, 0], g["k"][0, 0], g["v"][0, 0]
     p0 = T.oracle_plan(q, k, v, _cfg(c))
@@ -31,7 +31,7 @@ def test_reuse_on_the_same_step_is_the_plan():
 
 
 def test_reuse_on_the_next_step_keeps_tiers_and_repools():
-    c = CONFIGS[2].with_(heads=1)
+    c = CONFIGS["small"].with_(heads=1)
     g0 = generate(c)
     g1 = drift_step(g0, c, 1, 0.1)
     q0, k0, v0 = g0["q"][0, 0], g0["k"][0, 0], g0["v"][0, 0]

@@ -5,7 +5,7 @@ from synth import CONFIGS, generate, to_bf16_bits, bf16_bits_to_f32
 
 
 def test_deterministic_and_head_subset():
-    cfg = CONFIGS[2].with_(grid=(2, 8, 16), heads=4)
+    cfg = CONFIGS["small"].with_(grid=(2, 8, 16), heads=4)
     a = generate(cfg, seed=0)
     b = generate(cfg, seed=0)
     assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["v"], b["v"])
@@ -17,7 +17,7 @@ def test_deterministic_and_head_subset():
 
 
 def test_bf16_rounding_and_shapes():
-    cfg = CONFIGS[2].with_(grid=(2, 4, 8))
+    cfg = CONFIGS["small"].with_(grid=(2, 4, 8))
     g = generate(cfg)
     assert g["q"].shape == (1, 12, 64, 64)
     assert np.array_equal(bf16_bits_to_f32(g["bits"]["k"]), g["k"])
@@ -28,15 +28,15 @@ def test_bf16_rounding_and_shapes():
 
 
 def test_tiny_is_fp32_and_temperatures():
-    g = generate(CONFIGS[1])
+    g = generate(CONFIGS["tiny"])
     assert g["bits"] is None and g["q"].shape == (1, 2, 256, 64)
-    g3 = generate(CONFIGS[3].with_(grid=(1, 2, 8)), heads=[0])
+    g3 = generate(CONFIGS["wan_like"].with_(grid=(1, 2, 8)), heads=[0])
     assert np.all((g3["temps"] >= 0.5) & (g3["temps"] <= 2.0))
 
 
 def test_drift_step_is_a_seeded_small_move():
     from synth import CONFIGS, drift_step, generate
-    cfg = CONFIGS[2].with_(heads=2)
+    cfg = CONFIGS["small"].with_(heads=2)
     g = generate(cfg)
     a = drift_step(g, cfg, 1, 0.05)
     b = drift_step(g, cfg, 1, 0.05)
