@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (every head, bf16 output), checked on samples the oracle can
-compute: the whole tier map of a few heads, and a few query blocks of output
-(the first, an interior one, and the ragged last one).
+compute: the whole tier map of a few heads, and query blocks of output: the
+first, an interior one and the ragged last one, or (Hunyuan-like) 32 per head,
+the ragged last and the blocks with the most low-tier tiles among them.
 
 Generating every head of the 32760- and 118800-token workloads takes minutes
 on the host, so a reduced-head instance of each workload is generated and its
@@ -19,9 +20,27 @@ from gpu_cases import OracleCfg, band_mask
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    "wan_32760x40": ("wan_like", 4, [0, 21, 39]),          # workload, generated heads, sampled heads
-    "hunyuan_118800x24": ("hunyuan_like", 2, [0, 23]),
+    # workload, generated heads, sampled heads, sampled query blocks per head
+    "wan_32760x40": ("wan_like", 4, [0, 21, 39], 3),
+    "hunyuan_118800x24": ("hunyuan_like", 2, [0, 23], 32),
 }
+
+
+def _sample_rows(nq, n, tiers):
+    """n query blocks: the first, the ragged last, the rows with the most LOW
+    tiles, then evenly spaced ones."""
+    rows = [0, nq - 1]
+    for I in np.argsort(-(tiers == 1).sum(axis=1), kind="stable"):
+        if len(rows) >= min(n, nq) // 2:
+            break
+        if int(I) not in rows:
+            rows.append(int(I))
+    for I in np.linspace(0, nq - 1, n).astype(int):
+        if len(rows) >= min(n, nq):
+            break
+        if int(I) not in rows:
+            rows.append(int(I))
+    return sorted(rows)
 
 
 def _log(msg):
@@ -41,7 +60,7 @@ def _device_tiled(bits, heads):
 @pytest.mark.parametrize("name", list(CASES))
 def test_full_size_sampled(name):
     import tile_sparse_mixed_amd as tsm
-    wl, gen_heads, sample_heads = CASES[name]
+    wl, gen_heads, sample_heads, n_rows = CASES[name]
     cfg = CONFIGS[wl]
     _log(f"[full {name}] N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} (generating {gen_heads} heads)")
     g = generate(cfg.with_(heads=gen_heads))
@@ -55,8 +74,8 @@ def test_full_size_sampled(name):
     lists, counts = p.lists()
     oc = OracleCfg(cfg)
     nq = cfg.n_qblocks
-    rows = [0, nq // 2 + 1, nq - 1]
     for h in sample_heads:
+        rows = [0, nq // 2 + 1, nq - 1] if n_rows == 3 else _sample_rows(nq, n_rows, tiers[0, h])
         src = h % gen_heads
         q, k, v = g["q"][0, src], g["k"][0, src], g["v"][0, src]
         o = T.oracle_plan(q, k, v, oc)
