@@ -80,6 +80,7 @@ def test_full_size_sampled(name):
         q, k, v = g["q"][0, src], g["k"][0, src], g["v"][0, src]
         o = T.oracle_plan(q, k, v, oc)
         band = band_mask(o["p"], oc.tau_hi, oc.tau_lo)
+        assert band.sum() <= max(1, 1e-4 * band.size), (name, h, int(band.sum()))   # excused share < 0.01%
         assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), (name, h)
         li, co = T.build_lists(tiers[0, h])
         assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), (name, h)

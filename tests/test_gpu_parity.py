@@ -66,14 +66,19 @@ def test_router_tiers_and_lists(case):
     p = gpu_plan(dev, cfg)
     tiers, pgpu = p.tiers(with_p=True)
     lists, counts = p.lists()
+    excused = 0
     for b in range(cfg.batch):
         for h in range(cfg.heads):
             o = orc[b][h]
             band = band_mask(o["p"], oc.tau_hi, oc.tau_lo)
+            excused += int(band.sum())
             assert np.array_equal(tiers[b, h][~band], o["tiers"][~band]), (name, h)
             assert np.max(np.abs(pgpu[b, h] - o["p"]) / o["p"]) < 1e-6
             li, co = T.build_lists(tiers[b, h])
             assert np.array_equal(lists[b, h], li) and np.array_equal(counts[b, h], co), (name, h)
+    # the excused band stays a negligible share: under 0.01% of the tiles (at
+    # least one tile allowed on the small shapes)
+    assert excused <= max(1, 1e-4 * tiers.size), (name, excused, tiers.size)
 
 
 def test_router_top_k():
