@@ -24,7 +24,8 @@
  *   - "HierPAS" (abstract): a lightweight eager estimate of the attention
  *     pattern, sampling-based entropy for head-wise retention ratios,
  *     progressively reduced precision, a top-k engine.
- *   - "FG-Attn" (abstract): M x N tile granularity.
+ *   - "FG-Attn" (abstract): M x N tile granularity (key blocks down to 8 keys
+ *     here, gathered eight at a time into dense MFMA slabs).
  *
  * Conventions
  *   - Every pointer is a DEVICE pointer unless its comment says "host".
@@ -81,7 +82,7 @@ typedef enum { TATTN_BF16 = 0, TATTN_FP32 = 1 } tattn_dtype;
 
 typedef struct {
   int32_t batch, heads, seq_len, head_dim; /* head_dim in {64, 128}                          */
-  int32_t block_q, block_k;                /* block_q 64 or 128; block_k 64 or 16            */
+  int32_t block_q, block_k;                /* block_q 64 or 128; block_k 64, 16 or 8         */
   float tau_hi, tau_lo;                    /* 0 <= tau_lo <= tau_hi, finite                  */
   int32_t top_k;                           /* 0 = off, else 1..ceil(seq_len/block_k)         */
   int32_t mode;                            /* tattn_mode                                     */

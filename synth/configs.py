@@ -69,6 +69,10 @@ CONFIGS = {
                                    noise_sigma=0.5, temperature=True),
     "fine_adaptive": WorkloadConfig(5, "fine_adaptive", 1, 40, (21, 30, 52), 128, 64, 16, 0.01, 0.001,
                                     mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
+    # finer key granularity than the five described workloads: the same grid
+    # and rule with 8-key blocks (4095 key blocks per row)
+    "finer_adaptive": WorkloadConfig(6, "finer_adaptive", 1, 40, (21, 30, 52), 128, 64, 8, 0.01, 0.001,
+                                     mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
 }
 
 

@@ -96,14 +96,16 @@ def test_full_size_sampled(name):
             assert excess.max() <= 1e-2 and d.mean() <= 1.5e-3, (name, h, I, d.max(), d.mean())
 
 
-def test_full_size_fine_adaptive():
-    """The fine-grained head-adaptive workload: 32760 tokens x 40 heads, 64q x 16k
-    tiles, k_h from the entropy of p on 256 sampled query blocks per head."""
+@pytest.mark.parametrize("wl", ["fine_adaptive", "finer_adaptive"])
+def test_full_size_fine_adaptive(wl):
+    """The fine-grained head-adaptive workloads: 32760 tokens x 40 heads, 64q x
+    16k (and 64q x 8k) tiles, k_h from the entropy of p on 256 sampled query
+    blocks per head."""
     import tile_sparse_mixed_amd as tsm
     import torch
-    cfg = CONFIGS["fine_adaptive"]
+    cfg = CONFIGS[wl]
     gen_heads, sample_heads = 3, [0, 20, 38]
-    _log(f"[full fine_adaptive] N={cfg.seq_len} H={cfg.heads} tile={cfg.block_q}x{cfg.block_k}")
+    _log(f"[full {wl}] N={cfg.seq_len} H={cfg.heads} tile={cfg.block_q}x{cfg.block_k}")
     g = generate(cfg.with_(heads=gen_heads))
     dev = _device_tiled(g["bits"], cfg.heads)
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, mode="adaptive",

@@ -63,7 +63,7 @@ def _check_plan_and_output(cfg, g, p, out, what):
             assert err.max() <= 1e-2 and err.mean() <= 1e-3, (what, b, h, err.max(), err.mean())
 
 
-@pytest.mark.parametrize("tiles", [(128, 64), (64, 16)])
+@pytest.mark.parametrize("tiles", [(128, 64), (64, 16), (64, 8)])
 def test_batch_and_token_major_layout(tiles):
     import tile_sparse_mixed_amd as tsm
     import torch
@@ -88,7 +88,7 @@ def test_batch_and_token_major_layout(tiles):
 
 
 @pytest.mark.parametrize("n", [1, 5, 16, 64, 65, 127])
-@pytest.mark.parametrize("tiles", [(128, 64), (64, 16)])
+@pytest.mark.parametrize("tiles", [(128, 64), (64, 16), (64, 8)])
 def test_short_sequences(n, tiles):
     """One (partial) query block; with 16-key blocks, a few key blocks."""
     import tile_sparse_mixed_amd as tsm

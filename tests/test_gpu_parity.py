@@ -25,6 +25,10 @@ SMALL = {
     # 64q x 16k tiles: FULL / LOW steps gather four key blocks
     "fine64x16": CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0),  # N=1000: Nq=16 (last 40), Nk=63 (last 8)
     "fine_d64": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2, block_q=64, block_k=16),   # N=585: Nk=37 (last 9)
+    # 8-key blocks: FULL / LOW steps gather eight key blocks
+    "fine64x8": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=8),   # N=189: Nk=24 (last 5)
+    "fine128x8_d64": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2, block_k=8),   # N=585: Nq=5, Nk=74 (last 1)
+    "fine64x8_long": CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0, block_k=8),   # N=1000: Nk=125
 }
 
 
@@ -211,7 +215,7 @@ def _rank_ambiguous_rows(p, k):
     return np.abs(s[:, k - 1] - s[:, k]) <= 1e-12 * s[:, k - 1]
 
 
-@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged", "fine64x16", "fine_d64"])
+@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged", "fine64x16", "fine_d64", "fine64x8", "fine128x8_d64"])
 def test_adaptive_mode(name):
     """Entropy-adaptive mode: k_h and r_h per head, rank tiers (top ceil(full_frac
     k_h) FULL, the rest of the top k_h LOW), lists, and the output under them."""

@@ -13,7 +13,8 @@
 //   k8               E4M3 codes of K_J, row-major with k8_pos d order,
 //   vt               V_J as fp16, transposed ([d][key]) in the key order the
 //                    fused kernel's P.V uses (vt_pos for 64-key blocks, vt16_pos
-//                    for 16-key blocks, which the kernel gathers four at a time),
+//                    for 16-key blocks, which the kernel gathers four at a time,
+//                    natural order for 8-key blocks, gathered eight at a time),
 //   vlow             the low tier's V operand, fl16(fl32(decode(E4M3(v * inv)) * sv)),
 //                    in the same transposed layout.
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
@@ -141,7 +142,7 @@ __device__ inline ColMoments col_moments(double s1, double s2, int n) {
 
 template <int D, int BK, bool MOM>
 __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
-  static_assert(BK == 64 || BK == 16, "key blocks are 64 or 16 keys");
+  static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
   constexpr int QR = BK / 8;   // 16-byte chunks per stored row of BK keys
   using BL = BlockLoad<D, BK>;
   __shared__ double red[BL::RT * D];
@@ -318,8 +319,10 @@ hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
   const Dims& d = a.d;
   if (d.Bk == 64)
     hipLaunchKernelGGL((k1_kv<D, 64, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
-  else
+  else if (d.Bk == 16)
     hipLaunchKernelGGL((k1_kv<D, 16, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_kv<D, 8, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d.Bq == 128)

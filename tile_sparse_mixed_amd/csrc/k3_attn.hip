@@ -23,7 +23,10 @@
 // With 16-key blocks ("FG-Attn": M x N tiles with a small N) a FULL or LOW
 // step gathers up to four consecutive entries of the row's list into one
 // 64-key step: K and E4M3 K rows per DMA instruction, V^T columns per lane (a
-// 16-key block keeps its within-group key order at any column group).
+// 16-key block keeps its within-group key order at any column group).  With
+// 8-key blocks a step gathers eight: each block's K rows go to the score rows
+// whose P values form one 8-key chunk of the P.V operand (slot8 / kk8), so the
+// block's V^T row is one 16-byte load in natural key order.
 //
 // Data movement: every step's operands go global -> LDS with direct
 // buffer_load_dwordx4 ... lds (no staging registers) into one of two stage
@@ -111,16 +114,19 @@ __device__ inline int offK8(int row, int ch) {                                  
   return D == 128 ? row * 128 + ((ch ^ swz128(row)) << 4) : row * 64 + ((ch ^ swz64(row)) << 4);
 }
 
-// score scale of each 16-key group of a staged step (one value for 64-key blocks)
+// score scale of each 16-key group of a staged step (one value for 64-key
+// blocks); with 8-key blocks, of this lane's four P chunks (slots 2 cc + lane
+// half), held per lane so the eight slot scales need no scalar registers
 template <int G>
 struct StepScale {
-  float c[G];
+  static constexpr int N = G == 8 ? 4 : G;
+  float c[N];
 };
 
 template <int D, int NW, int BK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
-  static_assert(BK == 64 || BK == 16, "key blocks are 64 or 16 keys");
+  static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
   constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
   constexpr int R1 = 128 * D;
@@ -212,13 +218,6 @@ void k3_attn(AttnArgs a) {
   auto list_idx = [&](int t, int g) { return t < sF ? G * t + g : nF + G * (t - tLow) + g; };
   auto list_end = [&](int t) { return t < sF ? nF : nK; };
   auto list_at = [&](int t) { return (int)slist[list_idx(t, 0)]; };
-  // the G key blocks of a step; a group past the list end repeats the first
-  // block (finite operands; its scores are masked)
-  auto step_blocks = [&](int t, int* J) __attribute__((always_inline)) {
-    const int i0 = list_idx(t, 0), e = list_end(t);
-#pragma unroll
-    for (int g = 0; g < G; g++) J[g] = __builtin_amdgcn_readfirstlane((int)slist[i0 + g < e ? i0 + g : i0]);
-  };
 
   // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
   //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
@@ -261,19 +260,24 @@ void k3_attn(AttnArgs a) {
   const int vlc = (lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1);
   const int vgrp = vlc >> 1;
   const int vlane = (lane >> 3) * 32 + (vlc & 1) * 16;
-  // caller's K as one resource per head for 16-key gathers: rows past N read as zero
+  // caller's K as one resource per head for 16- and 8-key gathers: rows past N read as zero
   const __amdgpu_buffer_rsrc_t rKh = make_rsrc(kin, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
-  // V^T rows of the step's G blocks (per-block [D][BK] layout) from `base`
-  auto load_vt16g = [&](unsigned char* reg, int base, const int* J) __attribute__((always_inline)) {
+  // V^T rows of the step's G blocks (per-block [D][BK] layout) from `base`.
+  // 16-key blocks: logical chunk vlc holds 8 keys of column group vlc / 2, half
+  // vlc & 1 of that block's 32-byte row; 8-key blocks: chunk vlc is slot vlc's
+  // whole 16-byte row.
+  // jv (8-key blocks): lane g < 8 holds the step's block of slot g
+  auto load_vt16g = [&](unsigned char* reg, int base, int jv) __attribute__((always_inline)) {
     if constexpr (G == 1) {
-      (void)reg; (void)base; (void)J;
+      (void)reg; (void)base; (void)jv;
     } else {
-      const int Jl = vgrp == 0 ? J[0] : vgrp == 1 ? J[1] : vgrp == 2 ? J[2] : J[3];
-      const int vo = vlane + Jl * (D * 32);
+      constexpr int ROWB = BK * 2;                  // bytes per stored V^T row of a block
+      const int vo = G == 4 ? vlane + __shfl(jv, vgrp, 64) * (D * ROWB)
+                            : (lane >> 3) * ROWB + __shfl(jv, vlc, 64) * (D * ROWB);
 #pragma unroll
       for (int i = 0; i < NI16; i++) {
         const int k = wave + NW * i;
-        dma16(rS, reg + k * 1024, vo, base + k * 256);
+        dma16(rS, reg + k * 1024, vo, base + k * 8 * ROWB);
       }
     }
   };
@@ -292,32 +296,61 @@ void k3_attn(AttnArgs a) {
     const int kind = step_kind(t);
     if constexpr (G > 1) {
       if (((KINDS & (1 << kFull)) && kind == kFull) || ((KINDS & (1 << kLow)) && kind == kLow)) {
-        int J[G];
-        step_blocks(t, J);
+        // one block index per lane (lane g < G: the step's g-th block), read
+        // straight from the list; a runtime slot then selects by lane, never by
+        // indexing an array (which the compiler would place in scratch memory)
+        int jv;
+        {
+          const int i0 = list_idx(t, 0), e = list_end(t), g = lane & (G - 1);
+          jv = (int)slist[i0 + g < e ? i0 + g : i0];
+        }
         if (kind == kFull) {
 #pragma unroll
           for (int i = 0; i < NI16; i++) {
             const int k = wave + NW * i;
             const int row0 = k * RPI;                // first stage row of the instruction
-            const int g = row0 >> 4;
-            const int Jg = g == 0 ? J[0] : g == 1 ? J[1] : g == 2 ? J[2] : J[3];
-            dma16(rKh, st + k * 1024, lk[i % NSW] + (Jg * 16 + (row0 & 15)) * (int)dm.sn * 2, 0);
+            if constexpr (G == 4) {
+              const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
+              dma16(rKh, st + k * 1024, lk[i % NSW] + (Jg * 16 + (row0 & 15)) * (int)dm.sn * 2, 0);
+            } else if constexpr (D == 128) {
+              // score row m = row0 + rr16 takes key kk8(m) of slot slot8(m); an
+              // instruction's four rows share one slot
+              const int Js = __builtin_amdgcn_readlane(jv, slot8(row0));
+              dma16(rKh, st + k * 1024, lk[i % NSW] + (Js * 8 + kk8(row0)) * (int)dm.sn * 2, 0);
+            } else {
+              const int m = row0 + rr16;
+              dma16(rKh, st + k * 1024,
+                    lk[i % NSW] + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - rr16) * (int)dm.sn * 2, 0);
+            }
           }
-          load_vt16g(st + R1, (int)SL.vt, J);
+          load_vt16g(st + R1, (int)SL.vt, jv);
 #pragma unroll
-          for (int g = 0; g < G; g++) cst.c[g] = cF;
+          for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = cF;
         } else {
 #pragma unroll
           for (int i = 0; i < NI8; i++) {
             const int k = wave + NW * i;
             const int row0 = k * (1024 / D);         // E4M3 rows are D bytes
-            const int g = row0 >> 4;
-            const int Jg = g == 0 ? J[0] : g == 1 ? J[1] : g == 2 ? J[2] : J[3];
-            dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + (Jg * 16 + (row0 & 15)) * D);
+            if constexpr (G == 4) {
+              const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
+              dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + (Jg * 16 + (row0 & 15)) * D);
+            } else {
+              const int ri = D == 128 ? lane >> 3 : lane >> 2;   // row of the lane inside the instruction
+              const int m = row0 + ri;
+              dma16(rS, st + k * 1024, voffK8 + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - ri) * D, (int)SL.k8);
+            }
           }
-          load_vt16g(st + R1, (int)SL.vlow, J);
+          load_vt16g(st + R1, (int)SL.vlow, jv);
 #pragma unroll
-          for (int g = 0; g < G; g++) cst.c[g] = sq * skp[J[g]] * cF;
+          for (int g = 0; g < StepScale<G>::N; g++) {
+            if constexpr (G == 8) {
+              const float s0 = skp[__builtin_amdgcn_readlane(jv, 2 * g)];
+              const float s1 = skp[__builtin_amdgcn_readlane(jv, 2 * g + 1)];
+              cst.c[g] = sq * (lh ? s1 : s0) * cF;
+            } else {
+              cst.c[g] = sq * skp[__builtin_amdgcn_readlane(jv, g)] * cF;
+            }
+          }
         }
         return;
       }
@@ -358,7 +391,7 @@ void k3_attn(AttnArgs a) {
         load_vt16(st + R1, rS, (int)SL.vbarT + c * 128 * D);
       }
 #pragma unroll
-      for (int g = 0; g < G; g++) cst.c[g] = 1.0f;
+      for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = 1.0f;
     }
   };
 
@@ -443,6 +476,12 @@ void k3_attn(AttnArgs a) {
   };
   // ---- online softmax of x = s * c (base-2 units; tmax already scaled) into
   // the fp16 P operand, raising m when needed.
+  // score scale of this lane's P chunk cc: one per step (64-key blocks), per
+  // 16-key group (16-key blocks), per slot 2 cc + lane half (8-key blocks)
+  auto chunk_scale = [&](const StepScale<G>& cs, int cc) __attribute__((always_inline)) {
+    if constexpr (G == 1) return cs.c[0];
+    else return cs.c[cc];
+  };
   auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
     tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const bool need = tmax > m_run + kLazy;
@@ -462,7 +501,7 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 8; tt++) {
         const int e = 8 * cc + tt;
-        pb[cc][tt] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cs.c[G == 1 ? 0 : cc], nm)));
+        pb[cc][tt] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], chunk_scale(cs, cc), nm)));
       }
     // l accumulates the fp16 P values the P.V MFMA multiplies, two per
     // v_dot2_f32_f16 (fp32 accumulation)
@@ -511,21 +550,32 @@ void k3_attn(AttnArgs a) {
     } else {
       // Lists are ascending, so a partial group or the ragged last block only
       // occurs in the last step of the phase.  Register (b, r) is key
-      // 8((r >> 2) & 1) + 4lh + r % 4 of group 2b + r / 8.
+      // 8((r >> 2) & 1) + 4lh + r % 4 of 16-key block 2b + r / 8, or key
+      // 4((r >> 2) & 1) + r % 4 of 8-key block (slot) 4b + 2(r / 8) + lh.
       if (t == (LOW ? nSteps - 1 : sF - 1)) {
         const int i0 = list_idx(t, 0), e = list_end(t);
+        // valid keys of each block: 0 past the list end, fewer in block Nk - 1
         int lim[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
           const int Jg = (int)slist[i0 + g < e ? i0 + g : i0];
-          lim[g] = (i0 + g >= e ? 0 : Jg == dm.Nk - 1 ? dm.N - 16 * Jg : 16) - 4 * lh;
-          opaque(lim[g]);
+          lim[g] = i0 + g >= e ? 0 : Jg == dm.Nk - 1 ? dm.N - BK * Jg : BK;
+        }
+        // this lane's limit for P chunk q = 2b + (r >> 3), against the key index
+        // of register r inside its block
+        int ql[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          ql[q] = G == 4 ? lim[q] - 4 * lh : (lh ? lim[2 * q + 1] : lim[2 * q]);
+          opaque(ql[q]);
         }
 #pragma unroll
         for (int b = 0; b < 2; b++)
 #pragma unroll
-          for (int r = 0; r < 16; r++)
-            if (8 * ((r >> 2) & 1) + (r & 3) >= lim[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
+          for (int r = 0; r < 16; r++) {
+            const int kk = G == 4 ? 8 * ((r >> 2) & 1) + (r & 3) : (r & 3) + 4 * ((r >> 2) & 1);
+            if (kk >= ql[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
+          }
       }
       float tmax = -INFINITY;
 #pragma unroll
@@ -533,7 +583,7 @@ void k3_attn(AttnArgs a) {
         float m = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
-        tmax = __builtin_fmaxf(tmax, m * c.c[cc]);
+        tmax = __builtin_fmaxf(tmax, m * chunk_scale(c, cc));
       }
       softmax(s, c, tmax);
     }
@@ -554,7 +604,7 @@ void k3_attn(AttnArgs a) {
     // (only the chunk holding block Nk - 1 can match)
     const int lastpos = dm.Nk - 1 - 64 * schunk[ci] - 4 * lh;
     const float lglast = __log2f(static_cast<float>(dm.N - (dm.Nk - 1) * BK));
-    constexpr float lgfull = BK == 64 ? 6.0f : 4.0f;   // log2(BK)
+    constexpr float lgfull = BK == 64 ? 6.0f : BK == 16 ? 4.0f : 3.0f;   // log2(BK)
     float tmax = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; b++)
@@ -568,7 +618,7 @@ void k3_attn(AttnArgs a) {
       }
     StepScale<G> one;
 #pragma unroll
-    for (int g = 0; g < G; g++) one.c[g] = 1.0f;
+    for (int g = 0; g < StepScale<G>::N; g++) one.c[g] = 1.0f;
     softmax(s, one, tmax);
   };
 
@@ -695,8 +745,10 @@ template <int D, int NW>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   if (a.d.Bk == 64)
     hipLaunchKernelGGL((k3_attn<D, NW, 64>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
-  else
+  else if (a.d.Bk == 16)
     hipLaunchKernelGGL((k3_attn<D, NW, 16>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k3_attn<D, NW, 8>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -54,9 +54,19 @@ __host__ __device__ inline int vt_pos(int key) {
 // swap of key bits 2 and 3.  A 16-key block stored with this order can be
 // placed at any column group of a 64-key tile.
 __host__ __device__ inline int vt16_pos(int k) { return 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3); }
-// key whose value sits at element e of a stored row of BK keys (BK = 64 or 16)
+// 8-key blocks: a step of eight blocks (slots) places slot s's keys at the
+// score rows whose P values form one 8-key chunk of the P.V operand, chunk
+// (s >> 1) in lane half (s & 1):
+//   score row m holds key kk8(m) of slot slot8(m).
+// A chunk then lists its slot's keys in order, so a block's V^T row is stored
+// [d][8] in natural key order and one 16-byte load fetches it.
+__host__ __device__ inline int slot8(int m) { return 2 * (2 * (m >> 5) + ((m >> 4) & 1)) + ((m >> 2) & 1); }
+__host__ __device__ inline int kk8(int m) { return (m & 3) + 4 * ((m >> 3) & 1); }
+
+// key whose value sits at element e of a stored row of BK keys (BK = 64, 16 or 8)
 template <int BK>
 __host__ __device__ inline int vt_key(int e) {
+  if (BK == 8) return e;
   if (BK == 16) return (e & 3) | ((e >> 1) & 4) | ((e << 1) & 8);
   const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
   return 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);

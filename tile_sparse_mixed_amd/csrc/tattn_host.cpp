@@ -122,8 +122,8 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "head_dim, block_q and block_k must be >= 1");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(TATTN_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
-  if ((c->block_k != 64 && c->block_k != 16) || (c->block_q != 64 && c->block_q != 128))
-    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported (block_q 64 or 128, block_k 64 or 16)", c->block_q,
+  if ((c->block_k != 64 && c->block_k != 16 && c->block_k != 8) || (c->block_q != 64 && c->block_q != 128))
+    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported (block_q 64 or 128, block_k 64, 16 or 8)", c->block_q,
                 c->block_k);
   if (c->mode < 0 || c->mode > 4) return fail(TATTN_E_INVALID, "mode %d out of range", c->mode);
   if (c->mode == TATTN_MODE_PRICE && (!std::isfinite(c->price) || c->price < 0.0f))
@@ -153,9 +153,9 @@ static tattn_status validate(const tattn_config* c) {
   if (nk > kMaxNk) return fail(TATTN_E_UNSUPPORTED, "%lld key blocks exceed the limit of %d", (long long)nk, kMaxNk);
   if ((int64_t)c->batch * c->heads * nq > 0x7fffffffLL || (int64_t)c->batch * c->heads * nk > 0x7fffffffLL)
     return fail(TATTN_E_UNSUPPORTED, "problem too large for one launch");
-  // 16-key blocks address a head's K rows with 32-bit byte offsets
-  if (c->block_k == 16 && (int64_t)c->seq_len * c->stride_n * 2 > 0x7fffffffLL)
-    return fail(TATTN_E_UNSUPPORTED, "seq_len x stride_n too large for 16-key blocks");
+  // 16- and 8-key blocks address a head's K rows with 32-bit byte offsets
+  if (c->block_k != 64 && (int64_t)c->seq_len * c->stride_n * 2 > 0x7fffffffLL)
+    return fail(TATTN_E_UNSUPPORTED, "seq_len x stride_n too large for %d-key blocks", c->block_k);
   return ok();
 }
 
@@ -367,7 +367,8 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
         if (host_k8)
           for (int c = 0; c < d.D; c++) host_k8[(bh * d.N + n) * d.D + c] = k8[J * tile + r * d.D + k8_pos(c)];
         if (host_vlow)
-          for (int c = 0; c < d.D; c++) host_vlow[(bh * d.N + n) * d.D + c] = vl[J * tile + c * d.Bk + (d.Bk == 64 ? vt_pos(r) : vt16_pos(r))];
+          for (int c = 0; c < d.D; c++)
+            host_vlow[(bh * d.N + n) * d.D + c] = vl[J * tile + c * d.Bk + (d.Bk == 64 ? vt_pos(r) : d.Bk == 16 ? vt16_pos(r) : r)];
       }
   }
   return ok();
