@@ -48,6 +48,7 @@ def test_valid_configs(lib):
     assert status(lib, good(mode="adaptive")) == 0
     assert status(lib, good(seq_len=118800, heads=24)) == 0
     assert status(lib, good(top_k=10)) == 0
+    assert status(lib, good(block_q=64, block_k=8)) == 0                 # 4095 key blocks
     assert status(lib, good(mode="price", price=0.01)) == 0
     assert status(lib, good(mode="price", price=0.0)) == 0
 
@@ -56,6 +57,8 @@ def test_valid_configs(lib):
     (dict(batch=0), -1), (dict(heads=-1), -1), (dict(seq_len=0), -1),
     (dict(head_dim=96), -2), (dict(block_q=32), -2), (dict(block_k=32), -2),
     (dict(block_k=16, strides=(40 * 32760 * 128 * 4096, 32760 * 128 * 4096, 128 * 4096)), -2),
+    (dict(block_k=8, strides=(40 * 32760 * 128 * 4096, 32760 * 128 * 4096, 128 * 4096)), -2),
+    (dict(block_k=8, seq_len=32776), -2),                                # 4097 key blocks
     (dict(tau_hi=0.001, tau_lo=0.01), -1), (dict(tau_lo=-0.1), -1), (dict(tau_hi=float("inf")), -1),
     (dict(top_k=-1), -1), (dict(top_k=513), -1), (dict(mode=7), -1),
     (dict(mode="adaptive", keep_min=0.6, keep_max=0.5), -1), (dict(mode="adaptive", full_frac=0.0), -1),
