@@ -101,9 +101,11 @@ __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
 struct Red {
   double d[kWaves];
   int i[kWaves * 4];
-  int hist[256];   // radix-select digit histogram
-  int sel[2];      // selected digit, count of candidates above it
-  int chunk[kMaxNk / 64];   // per chunk of 64 key blocks: holds a skipped block
+  uint64_t u[kWaves];
+  // radix-select digit histogram, one per wave: a pair of waves shares a word,
+  // 16 bits each (a wave counts at most kMaxNk / kWaves values)
+  int hist[kWaves / 2][256];
+  int sel[3];      // selected digit, count of candidates above it, candidates holding it
 };
 
 __device__ double block_max_d(double v, Red& r) {
@@ -137,24 +139,60 @@ __device__ int block_sum_i(int v, Red& r) {
   return s;
 }
 
+// Largest (MAX) or smallest bit pattern among the pv[J] whose bits match
+// `prefix` under `mask`; at least one does.
+template <bool MAX>
+__device__ uint64_t block_extreme_bits(const double* pv, int n, uint64_t prefix, uint64_t mask, Red& r) {
+  uint64_t v = MAX ? 0ull : ~0ull;
+  for (int J = threadIdx.x; J < n; J += kThreads) {
+    const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
+    if ((b & mask) == prefix) v = MAX ? (b > v ? b : v) : (b < v ? b : v);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t x = __shfl_xor(v, o, 64);
+    v = MAX ? (x > v ? x : v) : (x < v ? x : v);
+  }
+  if ((threadIdx.x & 63) == 0) r.u[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t e = r.u[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; w++) e = MAX ? (r.u[w] > e ? r.u[w] : e) : (r.u[w] < e ? r.u[w] : e);
+  __syncthreads();
+  return e;
+}
+
 // Bits of the k-th largest value (1 <= k <= n) among the non-negative doubles
 // pv[0..n).  Non-negative doubles order like their bit patterns, so this is a
 // radix select from the top byte down: per byte, a histogram of that byte over
 // the values that match the bytes chosen so far, then the byte at which the
-// count from the top reaches the remaining rank.  (Measured against 11-bit
-// digits: 8-bit digits are faster; fewer bins to clear and scan per pass
-// outweigh the contention of the top byte.)
+// count from the top reaches the remaining rank.  Once that rank is the first
+// or the last of the values still matching, one max or min reduction ends the
+// select; on continuous data this happens after two or three bytes.
+// (Measured against 11-bit digits: 8-bit digits are faster; fewer bins to
+// clear and scan per pass outweigh the contention of the top byte.)
 __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
   uint64_t prefix = 0, mask = 0;
   int kk = k;   // rank of the wanted value among the values matching `prefix`
   const int lane = threadIdx.x & 63;
   for (int sh = 56; sh >= 0; sh -= 8) {
     constexpr int bins = 256;
-    for (int i = threadIdx.x; i < bins; i += kThreads) r.hist[i] = 0;
+    for (int i = threadIdx.x; i < bins * (kWaves / 2); i += kThreads) (&r.hist[0][0])[i] = 0;
     __syncthreads();
-    for (int J = threadIdx.x; J < n; J += kThreads) {
-      const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
-      if ((b & mask) == prefix) atomicAdd(&r.hist[(b >> sh) & (bins - 1)], 1);
+    {
+      int* hw = r.hist[threadIdx.x >> 7];
+      const int one = 1 << (((threadIdx.x >> 6) & 1) * 16);
+      for (int J = threadIdx.x; J < n; J += kThreads) {
+        const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
+        if ((b & mask) == prefix) atomicAdd(&hw[(b >> sh) & (bins - 1)], one);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < bins) {   // fold the per-wave counts into one histogram
+      int c = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves / 2; ww++) c += (r.hist[ww][threadIdx.x] & 0xffff) + (r.hist[ww][threadIdx.x] >> 16);
+      r.hist[0][threadIdx.x] = c;
     }
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -162,7 +200,7 @@ __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
       // inclusive scan of the lane totals from the top digit down
       const int w = bins >> 6;
       int tot = 0;
-      for (int j = 0; j < w; j++) tot += r.hist[bins - 1 - lane * w - j];
+      for (int j = 0; j < w; j++) tot += r.hist[0][bins - 1 - lane * w - j];
       int cum = tot;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -174,10 +212,11 @@ __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
       if (lane == L) {
         int above = cum - tot;
         for (int j = 0; j < w; j++) {
-          const int c = r.hist[bins - 1 - lane * w - j];
+          const int c = r.hist[0][bins - 1 - lane * w - j];
           if (above + c >= kk) {
             r.sel[0] = bins - 1 - lane * w - j;
             r.sel[1] = above;
+            r.sel[2] = c;
             break;
           }
           above += c;
@@ -188,29 +227,37 @@ __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
     prefix |= (uint64_t)r.sel[0] << sh;
     mask |= (uint64_t)(bins - 1) << sh;
     kk -= r.sel[1];
+    const int cand = r.sel[2];
     __syncthreads();
+    if (sh > 0 && kk == 1) return block_extreme_bits<true>(pv, n, prefix, mask, r);
+    if (sh > 0 && kk == cand) return block_extreme_bits<false>(pv, n, prefix, mask, r);
   }
   return prefix;
 }
 
 // rank(J) < k  <=>  p_J > x_k  or  (p_J == x_k and J is among the first `need`
-// tiles equal to x_k in ascending J), need = k - #{p > x_k}.  Marks such
-// tiles in `keep` (1) and the rest 0.
-__device__ void mark_top_k(const double* pv, int n, int k, unsigned char* keep, Red& r) {
-  if (k >= n) {
-    for (int J = threadIdx.x; J < n; J += kThreads) keep[J] = 1;
-    __syncthreads();
-    return;
-  }
-  if (k <= 0) {
-    for (int J = threadIdx.x; J < n; J += kThreads) keep[J] = 0;
+// tiles equal to x_k in ascending J), need = k - #{p > x_k}.  Calls
+// mark(J, rank(J) < k) once for every tile; a barrier follows.
+template <class Mark>
+__device__ void mark_top_k(const double* pv, int n, int k, Mark mark, Red& r) {
+  if (k >= n || k <= 0) {
+    for (int J = threadIdx.x; J < n; J += kThreads) mark(J, k > 0);
     __syncthreads();
     return;
   }
   const uint64_t xb = kth_largest_bits(pv, n, k, r);
-  int gt = 0;
-  for (int J = threadIdx.x; J < n; J += kThreads) gt += ((uint64_t)__double_as_longlong(pv[J]) > xb);
-  const int need = k - block_sum_i(gt, r);
+  int ge = 0;   // #{p > x} in the low 16 bits, #{p == x} above (n <= 4096)
+  for (int J = threadIdx.x; J < n; J += kThreads) {
+    const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
+    ge += (b > xb) + ((b == xb) << 16);
+  }
+  ge = block_sum_i(ge, r);
+  const int need = k - (ge & 0xffff);
+  if (need == (ge >> 16)) {   // every tile equal to x is kept: no ordering among them needed
+    for (int J = threadIdx.x; J < n; J += kThreads) mark(J, (uint64_t)__double_as_longlong(pv[J]) >= xb);
+    __syncthreads();
+    return;
+  }
   int base = 0;   // equal-to-x tiles already seen in earlier chunks
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int J0 = 0; J0 < n; J0 += kThreads) {
@@ -227,7 +274,7 @@ __device__ void mark_top_k(const double* pv, int n, int k, unsigned char* keep, 
       if (ww < w) woff += r.i[ww];
       tot += r.i[ww];
     }
-    if (J < n) keep[J] = (b > xb) || (eq && base + woff + pre < need);
+    if (J < n) mark(J, (b > xb) || (eq && base + woff + pre < need));
     base += tot;
     __syncthreads();
   }
@@ -246,50 +293,62 @@ __device__ inline void diag_range(const Dims& dm, int I, int& j0, int& j1) {
 // blocks holding a skipped block), G = 64 / Bk key blocks per step; it orders
 // the fused kernel's work.
 __device__ void compact_row(const unsigned char* tr, int n, int bk, int16_t* list, int* counts, Red& r) {
-  int c[3] = {0, 0, 0};
-  const int nch = (n + 63) / 64;
-  for (int i = threadIdx.x; i < nch; i += kThreads) r.chunk[i] = 0;
-  __syncthreads();
-  for (int J = threadIdx.x; J < n; J += kThreads) {
-    c[tr[J]]++;
-    if (tr[J] == TATTN_SKIP) r.chunk[J >> 6] = 1;
+  // each wave owns a run of whole 64-tile chunks: it counts its tiers, one
+  // barrier publishes the per-wave counts, then it writes its run in order
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nch = (n + 63) / 64, cpw = (nch + kWaves - 1) / kWaves;
+  const int c0 = w * cpw, c1 = min(nch, c0 + cpw);
+  const uint64_t below = (1ull << lane) - 1;
+  int cnt[3] = {0, 0, 0}, sch = 0;
+  for (int c = c0; c < c1; c++) {
+    const int J = c * 64 + lane;
+    const int tv = J < n ? tr[J] : -1;
+#pragma unroll
+    for (int T = 0; T < 3; T++) {
+      const uint64_t bal = __ballot(tv == T);
+      cnt[T] += __popcll(bal);
+      if (T == TATTN_SKIP) sch += bal != 0;
+    }
   }
-  const int nF = block_sum_i(c[2], r), nL = block_sum_i(c[1], r), nS = block_sum_i(c[0], r);
+  if (lane == 0) {
+#pragma unroll
+    for (int T = 0; T < 3; T++) r.i[w * 4 + T] = cnt[T];
+    r.i[w * 4 + 3] = sch;
+  }
+  __syncthreads();
+  int woff[3] = {0, 0, 0}, tot[3] = {0, 0, 0}, snc = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ww++) {
+#pragma unroll
+    for (int T = 0; T < 3; T++) {
+      if (ww < w) woff[T] += r.i[ww * 4 + T];
+      tot[T] += r.i[ww * 4 + T];
+    }
+    snc += r.i[ww * 4 + 3];
+  }
+  const int nF = tot[TATTN_FULL], nL = tot[TATTN_LOW], nS = tot[TATTN_SKIP];
   if (threadIdx.x == 0) {
-    int snc = 0;
-    for (int i = 0; i < nch; i++) snc += r.chunk[i];
     const int G = 64 / bk;
     counts[0] = nF;
     counts[1] = nL;
     counts[2] = nS;
     counts[3] = (nF + G - 1) / G + (nL + G - 1) / G + 2 * snc;
   }
-  int base[3] = {nF + nL, nF, 0};   // indexed by tier value: SKIP, LOW, FULL
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int J0 = 0; J0 < n; J0 += kThreads) {
-    const int J = J0 + threadIdx.x;
+  int base[3];   // indexed by tier value
+  base[TATTN_SKIP] = nF + nL + woff[TATTN_SKIP];
+  base[TATTN_LOW] = nF + woff[TATTN_LOW];
+  base[TATTN_FULL] = woff[TATTN_FULL];
+  for (int c = c0; c < c1; c++) {
+    const int J = c * 64 + lane;
     const int tv = J < n ? tr[J] : -1;
-    int pre = 0;
 #pragma unroll
     for (int T = 0; T < 3; T++) {
       const uint64_t bal = __ballot(tv == T);
-      if (tv == T) pre = __popcll(bal & ((1ull << lane) - 1));
-      if (lane == 0) r.i[w * 4 + T] = __popcll(bal);
+      if (tv == T) list[base[T] + __popcll(bal & below)] = static_cast<int16_t>(J);
+      base[T] += __popcll(bal);
     }
-    __syncthreads();
-    int woff[3] = {0, 0, 0}, tot[3] = {0, 0, 0};
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ww++)
-#pragma unroll
-      for (int T = 0; T < 3; T++) {
-        if (ww < w) woff[T] += r.i[ww * 4 + T];
-        tot[T] += r.i[ww * 4 + T];
-      }
-    if (tv >= 0) list[base[tv] + woff[tv] + pre] = static_cast<int16_t>(J);
-#pragma unroll
-    for (int T = 0; T < 3; T++) base[T] += tot[T];
-    __syncthreads();
   }
+  __syncthreads();   // r.i is free again
 }
 
 // ------------------------------------------------------------------ price router
@@ -385,19 +444,18 @@ __device__ void price_row(const RouterArgs& a, int bh, int64_t row, const double
 // their occupancy.
 enum { K2B_TIERS = 0, K2B_ENTROPY = 1, K2B_PRICE = 2 };
 
-inline size_t k2b_lds_bytes(int nk) { return ((size_t)nk * 10 + 15) / 16 * 16; }
+inline size_t k2b_lds_bytes(int nk) { return ((size_t)nk * 9 + 15) / 16 * 16; }
 
 // One workgroup per (b, h, I) (tiers) or per (b, h, sampled row s) (entropy).
 template <int WHAT>
 __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
-  // row buffers sized by the launch for this Nk: p (f64), tiers, keep marks
+  // row buffers sized by the launch for this Nk: p (f64), tiers
   extern __shared__ __attribute__((aligned(16))) unsigned char k2b_dyn[];
   __shared__ Red r;
   const Dims& dm = a.d;
   const int n = dm.Nk;
   double* pv = reinterpret_cast<double*>(k2b_dyn);
   unsigned char* tr = k2b_dyn + (size_t)n * 8;
-  unsigned char* keep = tr + n;
   int bh, I, s = 0;
   if (WHAT == K2B_ENTROPY) {
     const int S = min(a.samples, dm.Nq);
@@ -445,13 +503,14 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
     }
   } else if (a.mode == TATTN_MODE_THRESHOLD) {
     const double th = a.tau_hi, tl = a.tau_lo;
-    if (a.top_k > 0) mark_top_k(pv, n, a.top_k, keep, r);
     for (int J = threadIdx.x; J < n; J += kThreads) {
       const double p = pv[J];
-      unsigned char t = p >= th ? TATTN_FULL : (p >= tl ? TATTN_LOW : TATTN_SKIP);
-      if (a.top_k > 0 && !keep[J]) t = TATTN_SKIP;
-      tr[J] = t;
+      tr[J] = p >= th ? TATTN_FULL : (p >= tl ? TATTN_LOW : TATTN_SKIP);
       pout[J] = static_cast<float>(p);
+    }
+    if (a.top_k > 0) {
+      __syncthreads();
+      mark_top_k(pv, n, a.top_k, [&](int J, bool kept) { if (!kept) tr[J] = TATTN_SKIP; }, r);
     }
   } else {  // ADAPTIVE
     const int S2 = min(a.samples, dm.Nq);
@@ -469,14 +528,9 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
       reinterpret_cast<int*>(a.ws + a.L.kh)[bh] = kh;
       reinterpret_cast<double*>(a.ws + a.L.rh)[bh] = rr;
     }
-    mark_top_k(pv, n, kh, keep, r);
-    for (int J = threadIdx.x; J < n; J += kThreads) tr[J] = keep[J] ? TATTN_LOW : TATTN_SKIP;
-    __syncthreads();
-    mark_top_k(pv, n, nfull, keep, r);
-    for (int J = threadIdx.x; J < n; J += kThreads) {
-      if (keep[J]) tr[J] = TATTN_FULL;
-      pout[J] = static_cast<float>(pv[J]);
-    }
+    mark_top_k(pv, n, kh, [&](int J, bool kept) { tr[J] = kept ? TATTN_LOW : TATTN_SKIP; }, r);
+    mark_top_k(pv, n, nfull, [&](int J, bool kept) { if (kept) tr[J] = TATTN_FULL; }, r);
+    for (int J = threadIdx.x; J < n; J += kThreads) pout[J] = static_cast<float>(pv[J]);
   }
   __syncthreads();
   int j0, j1;
