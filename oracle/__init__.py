@@ -15,6 +15,8 @@ Each function names the passage of the pages it follows:
     attention pattern; sampling-based entropy gives head-wise retention
     ratios; progressively lower precision for less critical regions; top-k.
   * "FG-Attn" abstract (searcharxiv author page): M x N tile granularity.
+  * "Triage" abstract again for the optional fourth tier: skimming a tile in a
+    4-bit format (here OCP MXFP4, oracle/mxfp4.py).
 Formulas the pages leave open follow the readings listed with the design
 (block-mean router with +ln n_J; the low tier quantises Q, K, V to E4M3 with
 one scale per block and keeps the probabilities in the accumulation path).
@@ -23,9 +25,9 @@ Parity status: every function is pinned by tests/test_oracle_*.py except the
 entropy -> retention-ratio mapping of the head-adaptive mode, whose formula the
 pages do not fix ("parity unpinned"; only its [5%, 50%] clip is external).
 """
-from . import e4m3  # noqa: F401
+from . import e4m3, mxfp4  # noqa: F401
 from .tattn import (  # noqa: F401
-    SKIP, LOW, FULL, block_sizes, pool_means, router, tiers_threshold, tiers_adaptive,
+    SKIP, LOW, FULL, SKIM, skim_operands, block_sizes, pool_means, router, tiers_threshold, tiers_adaptive,
     head_retention, diagonal_mask, build_lists, quantise_blocks, low_values, attention_forward,
     oracle_plan, oracle_forward, naive_attention, effective_weights,
 )

@@ -41,9 +41,9 @@ import math
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, mxfp4
 
-SKIP, LOW, FULL = 0, 1, 2
+SKIP, LOW, FULL, SKIM = 0, 1, 2, 3
 
 LOG2E = 1.0 / math.log(2.0)
 
@@ -112,12 +112,17 @@ def row_ranks(p: np.ndarray) -> np.ndarray:
     return ranks
 
 
-def tiers_threshold(p: np.ndarray, tau_hi: float, tau_lo: float, top_k: int = 0) -> np.ndarray:
+def tiers_threshold(p: np.ndarray, tau_hi: float, tau_lo: float, top_k: int = 0,
+                    tau_skim: float = 0.0) -> np.ndarray:
     """Dual thresholds on the router probability (APT's dual thresholding at
     tile granularity): FULL if p >= tau_hi, LOW if tau_lo <= p < tau_hi, SKIP
-    below tau_lo.  With top_k > 0 only a row's top_k tiles (HierPAS: top-k) may
-    be kept; thresholds then act inside them.  Diagonal forcing is separate."""
+    below tau_lo.  With tau_skim > 0 a third threshold splits the band below
+    tau_lo: SKIM (the 4-bit tier, Triage's skimming) if tau_skim <= p < tau_lo.
+    With top_k > 0 only a row's top_k tiles (HierPAS: top-k) may be kept;
+    thresholds then act inside them.  Diagonal forcing is separate."""
     t = np.full(p.shape, SKIP, dtype=np.uint8)
+    if tau_skim > 0:
+        t[p >= tau_skim] = SKIM
     t[p >= tau_lo] = LOW
     t[p >= tau_hi] = FULL
     if top_k > 0:
@@ -272,15 +277,17 @@ def tiers_price(p: np.ndarray, eS: np.ndarray, eL: np.ndarray, price: float, bk:
 
 def build_lists(t: np.ndarray):
     """Per query block: kept/skipped key-block indices, [FULL asc | LOW asc |
-    SKIP asc], and the three counts (APT's mask management, as compacted lists)."""
+    SKIM asc | SKIP asc], and the counts of FULL, LOW and SKIP (the SKIM count
+    is the rest of the row) (APT's mask management, as compacted lists)."""
     nq, nk = t.shape
     lists = np.empty((nq, nk), dtype=np.int16)
     counts = np.empty((nq, 3), dtype=np.int32)
     for i in range(nq):
         f = np.nonzero(t[i] == FULL)[0]
         lo = np.nonzero(t[i] == LOW)[0]
+        k4 = np.nonzero(t[i] == SKIM)[0]
         s = np.nonzero(t[i] == SKIP)[0]
-        lists[i] = np.concatenate([f, lo, s]).astype(np.int16)
+        lists[i] = np.concatenate([f, lo, k4, s]).astype(np.int16)
         counts[i] = (f.size, lo.size, s.size)
     return lists, counts
 
@@ -309,6 +316,21 @@ def quantise_blocks(x: np.ndarray, b: int):
     return codes, scale, inv
 
 
+def skim_operands(q, k, v):
+    """Operands of skim tiles (Triage: skimming in a 4-bit format): Q, K and V
+    each quantised to MXFP4 per token row, one E8M0 scale per 32 consecutive
+    channels.  Scores use the dequantised q and k exactly; the value operand is
+    the dequantised v rounded to float16 (the precision the kernel multiplies
+    it in; exact unless it falls outside float16's normal range).  Returns a
+    dict of the dequantised operands (float64 [n, d]) and the codes and scale
+    bytes of k and v."""
+    _, _, qd = mxfp4.quantise(q)
+    kc, ks, kd = mxfp4.quantise(k)
+    vc, vs, vd = mxfp4.quantise(v)
+    return dict(q=qd, k=kd, v=vd.astype(np.float16).astype(np.float64), k_codes=kc, k_scales=ks,
+                v_codes=vc, v_scales=vs)
+
+
 def low_values(v8: np.ndarray, sv: np.ndarray, b: int) -> np.ndarray:
     """Value operand of low-precision tiles: the dequantised E4M3 value
     decode(code) * scale, formed in float32 and rounded to float16 (the
@@ -328,7 +350,7 @@ def _padded(x, nb, b):
 
 
 def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
-                      rows=None, return_partials=False):
+                      rows=None, return_partials=False, mx4=None):
     """One pass over all tiles of every query row, merging per-tile partials
     exactly (Triage: skip, low precision and full tiles in a single pass).
 
@@ -337,6 +359,8 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
           X^ = decode(X8) * scale (q^, k^ exact in float64), values
           v^_j = fl16(fl32(decode(V8_j) * scale_J)) (the fp16 value operand
           the low tier multiplies); partial (max s^, sum e^{s^-m}, sum e^{s^-m} v^_j).
+    SKIM: the same on the MXFP4 copies (``mx4``, from skim_operands): scores
+          <q4_i, k4_j>/sqrt(d), values v4_j (Triage: skimming in 4 bits).
     SKIP: sigma = <q_i, k_J>/sqrt(d) + ln n_J; partial (sigma, 1, v_J): one
           score weighted by n_J, valued by the block mean (Triage).
     Merge: M = max m; O_i = sum o e^{m-M} / sum l e^{m-M}.
@@ -356,6 +380,8 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     Kh = _padded(e4m3.decode(k8), nk, bk)                              # code values
     Vh = _padded(low_values(v8, sv, bk), nk, bk)
     Qc = e4m3.decode(q8)
+    if np.any(t == SKIM):
+        Kq, Vq = _padded(mx4["k"], nk, bk), _padded(mx4["v"], nk, bk)
     kb64, vb64 = kbar.astype(np.float64), vbar.astype(np.float64)
     lnk = np.log(ksz.astype(np.float64))
     out = np.zeros((n, d), dtype=np.float64)
@@ -384,6 +410,15 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
             ms.append(mt)
             ls.append(e.sum(axis=2))
             os_.append(np.matmul(e.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
+        K4 = np.nonzero(t[i] == SKIM)[0]
+        if K4.size:
+            s = (mx4["q"][r0:r1] @ Kq[K4].reshape(-1, d).T).reshape(r1 - r0, K4.size, bk) * isd
+            s = np.where(valid[K4][None], s, -np.inf)
+            m = s.max(axis=2)
+            e = np.exp(s - m[..., None])
+            ms.append(m)
+            ls.append(e.sum(axis=2))
+            os_.append(np.matmul(e.transpose(1, 0, 2), Vq[K4]).transpose(1, 0, 2))
         Sk = np.nonzero(t[i] == SKIP)[0]
         skip_sigma = None
         if Sk.size:
@@ -409,11 +444,12 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     return out
 
 
-def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
+def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv, mx4=None):
     """Dense [n, n] weight matrix W of the method on tiny inputs, together with
     the value matrix each weight multiplies: FULL W_ij = e^{s_ij-M}/L against
-    v_j; LOW W_ij = e^{s^_ij-M}/L against v^_j; SKIP W_ij = e^{sigma-M}/(n_J L)
-    against v_j.  Then O = rowsum(W * Vsel)."""
+    v_j; LOW W_ij = e^{s^_ij-M}/L against v^_j; SKIM W_ij = e^{s4_ij-M}/L
+    against v4_j; SKIP W_ij = e^{sigma-M}/(n_J L) against v_j.  Then
+    O = rowsum(W * Vsel)."""
     n, d = q.shape
     nq, nk = t.shape
     isd = 1.0 / math.sqrt(d)
@@ -425,6 +461,7 @@ def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
     qc = e4m3.decode(q8)
     W = np.zeros((n, n))
     sel_low = np.zeros((n, n), dtype=bool)
+    sel_skim = np.zeros((n, n), dtype=bool)
     for i in range(n):
         I = qblk[i]
         logits = np.full(n, -np.inf)
@@ -435,6 +472,9 @@ def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
             elif t[I, J] == SKIP:
                 sig = float(q[i] @ kbar[J].astype(np.float64)) * isd + math.log(ksz[J])
                 logits[j0:j1] = sig - math.log(ksz[J])
+            elif t[I, J] == SKIM:
+                logits[j0:j1] = (mx4["k"][j0:j1] @ mx4["q"][i]) * isd
+                sel_skim[i, j0:j1] = True
             else:
                 logits[j0:j1] = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
                 sel_low[i, j0:j1] = True
@@ -442,6 +482,8 @@ def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv):
         w = np.exp(logits - M)
         W[i] = w / w.sum()
     vsel = np.where(sel_low[:, :, None], vhat[None, :, :], v[None, :, :].astype(np.float64))
+    if mx4 is not None:
+        vsel = np.where(sel_skim[:, :, None], mx4["v"][None, :, :], vsel)
     return W, vsel
 
 
@@ -470,7 +512,8 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     r_h, k_h = None, None
     price_info = None
     if mode == 0:      # threshold
-        t = tiers_threshold(p, cfg_like.tau_hi, cfg_like.tau_lo, cfg_like.top_k)
+        t = tiers_threshold(p, cfg_like.tau_hi, cfg_like.tau_lo, cfg_like.top_k,
+                            getattr(cfg_like, "tau_skim", 0.0))
     elif mode == 1:    # adaptive
         r_h, k_h, _ = head_retention(p, cfg_like.entropy_samples, cfg_like.keep_min, cfg_like.keep_max)
         t = tiers_adaptive(p, k_h, cfg_like.full_frac)
@@ -490,8 +533,9 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     q8, sq, iq = quantise_blocks(q, bq)
     k8, sk, ik = quantise_blocks(k, bk)
     v8, sv, iv = quantise_blocks(v, bk)
+    mx4 = skim_operands(q, k, v) if d % mxfp4.BLOCK == 0 else None
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
-                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info)
+                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info, mx4=mx4)
 
 
 def oracle_replan(q, k, v, prev_plan, cfg_like):
@@ -505,4 +549,4 @@ def oracle_replan(q, k, v, prev_plan, cfg_like):
 def oracle_forward(q, k, v, plan, bq, bk, rows=None):
     return attention_forward(q, k, v, plan["tiers"], bq, bk, plan["kbar"], plan["vbar"],
                              plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],
-                             rows=rows)
+                             rows=rows, mx4=plan.get("mx4"))
