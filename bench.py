@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 MFMA
 PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense fp8 MFMA
+PEAK_FP4 = 10100.0   # TFLOP/s, MI355X dense fp4 MFMA
 PEAK_HBM = 8000.0    # GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k3_traffic.json")
 
@@ -34,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan_like",
-                    choices=["tiny", "small", "wan_like", "hunyuan_like", "fine_adaptive", "finer_adaptive"])
+                    choices=["tiny", "small", "wan_like", "hunyuan_like", "fine_adaptive", "finer_adaptive",
+                             "wan_skim"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-allfull", action="store_true", help="skip the all-full comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -82,6 +84,7 @@ def cpu_baseline(g, cfg, budget_s, price=None):
         top_k, mode = cfg.top_k, (4 if price is not None else cfg.mode)
         keep_min, keep_max, full_frac = 0.05, 0.5, 0.1
         entropy_samples = 256
+        tau_skim = float(np.float32(cfg.tau_skim))
     OC.price = float(np.float32(price)) if price is not None else 0.0
     q, k, v = g["q"][0, 0], g["k"][0, 0], g["v"][0, 0]
     t0 = time.perf_counter()
@@ -141,11 +144,11 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def mk(mode, ws=None):
+    def mk(mode, ws=None, skim=True):
         return tsm.plan(q, k, v, block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
                         top_k=cfg.top_k, mode=mode, keep_min=cfg.keep_min, keep_max=cfg.keep_max,
                         full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, workspace=ws,
-                        price=args.price or 0.0)
+                        price=args.price or 0.0, tau_skim=cfg.tau_skim if mode != "all_full" and skim else 0.0)
 
     out = torch.empty_like(q)
     plan = mk(run_mode)
@@ -158,7 +161,7 @@ def main():
     if run_mode == "threshold":
         pr = plan.tiers(with_p=True)[1]
         n_band = int(sum(np.count_nonzero(np.abs(pr - np.float32(t)) <= 1e-5 * np.float32(t))
-                         for t in (cfg.tau_hi, cfg.tau_lo)))
+                         for t in (cfg.tau_hi, cfg.tau_lo) + ((cfg.tau_skim,) if cfg.tau_skim > 0 else ())))
         del pr
     kh_summary = None
     if run_mode == "adaptive":   # k_h per head: min / median / max and a 10-bin histogram
@@ -212,6 +215,7 @@ def main():
 
     ms_allfull = None
     quality = None
+    skim_cmp = None
     if not args.no_allfull:
         pf = mk("all_full")
         dense_out = torch.empty_like(out)
@@ -227,6 +231,22 @@ def main():
                    "max_abs": round(float(diff.abs().max()), 5),
                    "rel_l2": round(float((num.sum() / b.flatten(2).pow(2).sum()).sqrt()), 6),
                    "cosine_min_row": round(float(torch.nn.functional.cosine_similarity(a, b, dim=-1).min()), 6)}
+        if cfg.tau_skim > 0 and run_mode == "threshold":
+            # the SKIM band run as LOW tiles and as SKIP tiles (same map otherwise):
+            # what the fourth tier costs and buys against its neighbours
+            t_map = plan.tiers()
+            skim_cmp = {"skim_share": round(float((t_map == tsm.SKIM).mean()), 4),
+                        "with_skim": {"forward_ms": round(ms_k3, 4), "rel_l2": quality["rel_l2"]}}
+            for name, tier in (("band_as_low", tsm.LOW), ("band_as_skip", tsm.SKIP)):
+                pe = mk("external", skim=False)   # no SKIM bytes: the kernel without the tier
+                pe.set_tiers(np.where(t_map == tsm.SKIM, tier, t_map).astype(np.uint8))
+                alt = torch.empty_like(out)
+                tsm.forward(pe, q, k, v, alt)
+                ms_alt = timed(lambda: tsm.forward(pe, q, k, v, alt), args.steps)[0]
+                af = alt.float()
+                rel = float(((af - b).flatten(2).pow(2).sum() / b.flatten(2).pow(2).sum()).sqrt())
+                skim_cmp[name] = {"forward_ms": round(ms_alt, 4), "rel_l2": round(rel, 6)}
+                del pe, alt, af
         del dense_out, a, b, diff, num
 
     if args.copy_calibration:
@@ -237,10 +257,10 @@ def main():
         torch.cuda.synchronize()
 
     dense = st["flops_dense"]
-    executed = st["flops_bf16"] + st["flops_fp8"]
-    bf16_equiv = st["flops_bf16"] + st["flops_fp8"] * PEAK_BF16 / PEAK_FP8
+    executed = st["flops_bf16"] + st["flops_fp8"] + st["flops_fp4"]
+    bf16_equiv = st["flops_bf16"] + st["flops_fp8"] * PEAK_BF16 / PEAK_FP8 + st["flops_fp4"] * PEAK_BF16 / PEAK_FP4
     achieved = bf16_equiv / (ms_k3 * 1e-3) / 1e12
-    tiles = st["n_full"] + st["n_low"] + st["n_skip"]
+    tiles = st["n_full"] + st["n_low"] + st["n_skip"] + st["n_skim"]
     traffic = load_traffic(args.workload)
 
     cpu = None
@@ -255,11 +275,13 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16+fp8 (fp32 accumulate)",
+        "dtype": "bf16+fp8" + ("+fp4" if st["n_skim"] else "") + " (fp32 accumulate)",
         "data": "synthetic" + (f" ({args.gen_heads} generated heads tiled to {cfg.heads})" if tiled else ""),
         "config": {"workload": f"{cfg.name}: {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]}={cfg.seq_len} tokens, "
                                f"{cfg.heads} heads, d={cfg.head_dim}, tiles {cfg.block_q}q x {cfg.block_k}k, "
-                               + (f"tau_hi={cfg.tau_hi}, tau_lo={cfg.tau_lo}" if run_mode == "threshold" else
+                               + (f"tau_hi={cfg.tau_hi}, tau_lo={cfg.tau_lo}"
+                                  + (f", tau_skim={cfg.tau_skim} (MXFP4 tier)" if cfg.tau_skim > 0 else "")
+                                  if run_mode == "threshold" else
                                   f"price router, price={args.price}" if run_mode == "price" else
                                   f"entropy-adaptive k_h (keep {cfg.keep_min}-{cfg.keep_max}, FULL share "
                                   f"{cfg.full_frac}, {cfg.entropy_samples} sampled query blocks)"),
@@ -276,14 +298,18 @@ def main():
         "all_full_tflops": None if ms_allfull is None else round(dense / (ms_allfull * 1e-3) / 1e12, 2),
         "tiers": {"full": round(st["n_full"] / tiles, 4), "low": round(st["n_low"] / tiles, 4),
                   "skip": round(st["n_skip"] / tiles, 4), "diagonal": st["n_diag"],
+                  **({"skim": round(st["n_skim"] / tiles, 4)} if st["n_skim"] else {}),
                   "near_threshold": n_band},
         "head_retention": kh_summary,
         "quality": quality,
+        "skim_tier": skim_cmp,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16, 4), "traffic": traffic,
                      "kernel": "k3_attn (fused three-tier forward)",
                      "work": f"bf16 {st['flops_bf16'] / 1e12:.3f} TFLOP + fp8 {st['flops_fp8'] / 1e12:.3f} TFLOP "
-                             f"(fp8 at half weight) per launch"},
+                             f"(fp8 at half weight)"
+                             + (f" + fp4 {st['flops_fp4'] / 1e12:.3f} TFLOP (fp4 at the bf16/fp4 peak ratio)"
+                                if st["n_skim"] else "") + " per launch"},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

@@ -7,14 +7,18 @@
  *   FULL  exact scores and values in bf16 (fp32 accumulation),
  *   LOW   fp8 E4M3 operands with one scale per block,
  *   SKIP  the tile is replaced by its block means: one score
- *         q_i . kbar_J / sqrt(d) + ln n_J valued by vbar_J.
+ *         q_i . kbar_J / sqrt(d) + ln n_J valued by vbar_J,
+ * and optionally a fourth, between LOW and SKIP:
+ *   SKIM  MXFP4 operands (E2M1 codes, one power-of-two E8M0 scale per 32
+ *         channels of a token row) on the block-scaled fp4 MFMA.
  * Tiers come from a block router, p_IJ = softmax_J(qbar_I . kbar_J / sqrt(d)
  * + ln n_J), with dual thresholds tau_hi / tau_lo and an optional per-row
  * top-k, or from an entropy-derived per-head top-k, or from a per-tile error
  * prediction weighed against one price; diagonal tiles are always FULL.
  * Sources of the method:
  *   - "Triage" (abstract): three approximation tiers per tile, skipping by
- *     block means, one fused kernel over all tiers in a single pass; a
+ *     block means, skimming in a 4-bit floating-point format (the SKIM tier
+ *     here), one fused kernel over all tiers in a single pass; a
  *     router that predicts each tile's error under each tier from block
  *     statistics and promotes a tile only when the error reduction pays for
  *     the extra compute at a single price.
@@ -62,11 +66,12 @@ typedef enum {
   TATTN_E_STATE = -5         /* a plan used against other tensors, or in the wrong mode */
 } tattn_status;
 
-/* Tier-map byte values. */
-typedef enum { TATTN_SKIP = 0, TATTN_LOW = 1, TATTN_FULL = 2 } tattn_tier;
+/* Tier-map byte values.  By accuracy: FULL > LOW > SKIM > SKIP. */
+typedef enum { TATTN_SKIP = 0, TATTN_LOW = 1, TATTN_FULL = 2, TATTN_SKIM = 3 } tattn_tier;
 
 typedef enum {
-  TATTN_MODE_THRESHOLD = 0,  /* FULL if p >= tau_hi, LOW if tau_lo <= p < tau_hi, else SKIP;
+  TATTN_MODE_THRESHOLD = 0,  /* FULL if p >= tau_hi, LOW if tau_lo <= p < tau_hi, else SKIP,
+                                except SKIM if tau_skim > 0 and tau_skim <= p < tau_lo;
                                 top_k > 0 first keeps only the row's top_k tiles        */
   TATTN_MODE_ADAPTIVE = 1,   /* per head k_h from the entropy of p on sampled rows; per row
                                 the top ceil(full_frac*k_h) tiles FULL, the rest of the top
@@ -92,6 +97,10 @@ typedef struct {
   int64_t stride_b, stride_h, stride_n;    /* element strides shared by Q, K, V and O        */
   float price;                             /* PRICE: error per FULL tile of work, >= 0,
                                               finite; ignored by the other modes             */
+  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite, <= tau_lo, and
+                                              block_k 64) enables it: THRESHOLD uses it as the
+                                              SKIM / SKIP threshold, EXTERNAL accepts SKIM bytes;
+                                              ignored by the other modes                     */
 } tattn_config;
 
 typedef struct tattn_plan_s* tattn_plan_t;  /* opaque host object; device state is in the workspace */
@@ -100,9 +109,11 @@ typedef struct {
   int64_t n_full, n_low, n_skip;  /* tiles per tier, over all (b, h, I, J)           */
   int64_t n_diag;                 /* diagonal tiles (always FULL)                    */
   double flops_bf16;              /* executed 16-bit MFMA flops: FULL and SKIP tiles,
-                                     and the P.V half of LOW tiles                  */
+                                     and the P.V half of LOW and SKIM tiles         */
   double flops_fp8;               /* executed fp8 MFMA flops: the score half of LOW  */
   double flops_dense;             /* 4 * N^2 * d * B * H: dense-equivalent work      */
+  int64_t n_skim;                 /* SKIM tiles                                      */
+  double flops_fp4;               /* executed fp4 MFMA flops: the score half of SKIM */
 } tattn_stats;
 
 /* Check a config without touching any device.  Host only; no HIP calls. */
@@ -151,8 +162,10 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
 /*
  * The fused three-tier pass ("Triage": one kernel, all tiers, single pass):
  * for every query block, an online softmax over its FULL tiles (bf16 MFMA),
- * its LOW tiles (scores from E4M3 Q and K on fp8 MFMA, values from E4M3 V) and
- * its SKIP tiles (block means with a ln n_J bias), then O = acc / l.
+ * its LOW tiles (scores from E4M3 Q and K on fp8 MFMA, values from E4M3 V),
+ * its SKIM tiles (scores from MXFP4 Q and K on the block-scaled fp4 MFMA,
+ * values from MXFP4 V) and its SKIP tiles (block means with a ln n_J bias),
+ * then O = acc / l.
  * o: output tensor with the config's strides, dtype cfg->out_dtype.
  * k and v must be the pointers the plan was built with (TATTN_E_STATE if not).
  */
@@ -174,9 +187,10 @@ tattn_status tattn_forward(tattn_plan_t plan, const void* q, const void* k, cons
 tattn_status tattn_replan(tattn_plan_t plan, const void* q, const void* k, const void* v, void* stream);
 
 /* SYNC.  Replace the plan's tier map with a host map [B, H, Nq, Nk] of bytes in
- * {0, 1, 2}; diagonal tiles are forced FULL and the lists rebuilt.  Only for a
- * plan built in TATTN_MODE_EXTERNAL (TATTN_E_STATE otherwise); a byte outside
- * {0,1,2} gives TATTN_E_INVALID and leaves the plan unchanged. */
+ * {0, 1, 2}, or {0, 1, 2, 3} when the config has tau_skim > 0; diagonal tiles
+ * are forced FULL and the lists rebuilt.  Only for a plan built in
+ * TATTN_MODE_EXTERNAL (TATTN_E_STATE otherwise); any other byte gives
+ * TATTN_E_INVALID and leaves the plan unchanged. */
 tattn_status tattn_plan_set_tiers(tattn_plan_t plan, const uint8_t* host_tiers, void* stream);
 
 /* SYNC.  Copy out the tier map [B, H, Nq, Nk] (bytes) and/or the router
@@ -185,8 +199,9 @@ tattn_status tattn_plan_set_tiers(tattn_plan_t plan, const uint8_t* host_tiers, 
 tattn_status tattn_plan_get_tiers(tattn_plan_t plan, uint8_t* host_tiers, float* host_p, void* stream);
 
 /* SYNC.  Copy out the compacted lists [B, H, Nq, Nk] (int16 key-block indices,
- * per row FULL ascending, then LOW ascending, then SKIP ascending) and/or the
- * counts [B, H, Nq, 3] (int32: n_full, n_low, n_skip).  Either may be NULL. */
+ * per row FULL ascending, then LOW ascending, then SKIM ascending, then SKIP
+ * ascending) and/or the counts [B, H, Nq, 3] (int32: n_full, n_low, n_skip;
+ * the row's SKIM count is Nk minus their sum).  Either may be NULL. */
 tattn_status tattn_plan_get_lists(tattn_plan_t plan, int16_t* host_lists, int32_t* host_counts,
                                   void* stream);
 
@@ -201,6 +216,17 @@ tattn_status tattn_plan_get_pool(tattn_plan_t plan, float* qbar, float* kbar, fl
  * patterns of fl16(fl32(decode(E4M3(v * inv)) * scale)) per element of V).
  * Either may be NULL. */
 tattn_status tattn_plan_get_codes(tattn_plan_t plan, uint8_t* host_k8, uint16_t* host_vlow, void* stream);
+
+/* SYNC.  SKIM tier (config tau_skim > 0; TATTN_E_STATE otherwise): copy out,
+ * in the canonical layout, the MXFP4 copies of K and V.  k4 [B, H, seq_len,
+ * head_dim/2] bytes: E2M1 codes, channel 2m in the low nibble of byte m and
+ * 2m+1 in the high nibble; k4s [B, H, seq_len, head_dim/32] bytes: the E8M0
+ * scale of each 32 channels, e + 127 for the scale 2^e, e = floor(log2(amax))
+ * - 2 clamped to [-127, 127] (-127 for an all-zero block); vskim [B, H,
+ * seq_len, head_dim]: fp16 bit patterns of the SKIM tier's value operand,
+ * fl16(code value * 2^e) of V's MXFP4 codes.  Any pointer may be NULL. */
+tattn_status tattn_plan_get_mx4(tattn_plan_t plan, uint8_t* host_k4, uint8_t* host_k4s, uint16_t* host_vskim,
+                                void* stream);
 
 /* SYNC.  PRICE mode: copy out the block second moments the router used
  * (float32): q2 [B,H,Nq,d] and m2q [B,H,Nq] (query mean square per dimension

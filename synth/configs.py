@@ -39,6 +39,7 @@ class WorkloadConfig:
     temperature: bool = False   # per-head temperature T_h ~ U(0.5, 2) divides Q
     input_fp32: bool = False    # the tiny workload is specified in fp32
     seed_stream: int = 0        # draw from another workload's stream (0: own stream)
+    tau_skim: float = 0.0       # > 0: the MXFP4 SKIM tier for tau_skim <= p < tau_lo
     extra: dict = field(default_factory=dict)
 
     @property
@@ -73,6 +74,10 @@ CONFIGS = {
     # and rule with 8-key blocks (4095 key blocks per row)
     "finer_adaptive": WorkloadConfig(6, "finer_adaptive", 1, 40, (21, 30, 52), 128, 64, 8, 0.01, 0.001,
                                      mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
+    # the Wan-like workload with the optional fourth tier: tiles whose router
+    # probability lies in [tau_skim, tau_lo) run in MXFP4 instead of being skipped
+    "wan_skim": WorkloadConfig(7, "wan_skim", 1, 40, (21, 30, 52), 128, 128, 64, 0.01, 0.001,
+                               noise_sigma=0.5, temperature=True, seed_stream=3, tau_skim=2e-4),
 }
 
 

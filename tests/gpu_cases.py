@@ -35,6 +35,7 @@ class OracleCfg:
         self.keep_min, self.keep_max = as_f32(cfg.keep_min), as_f32(cfg.keep_max)
         self.full_frac = as_f32(cfg.full_frac)
         self.entropy_samples = cfg.entropy_samples
+        self.tau_skim = as_f32(cfg.tau_skim)
 
 
 def oracle_head(g, b, h, ocfg, mode=None, external=None):
@@ -42,8 +43,11 @@ def oracle_head(g, b, h, ocfg, mode=None, external=None):
     return T.oracle_plan(q, k, v, ocfg, mode=mode, external_tiers=external)
 
 
-def band_mask(p, tau_hi, tau_lo, rel=1e-5):
-    return (np.abs(p - tau_hi) <= rel * tau_hi) | (np.abs(p - tau_lo) <= rel * tau_lo)
+def band_mask(p, tau_hi, tau_lo, rel=1e-5, tau_skim=0.0):
+    m = (np.abs(p - tau_hi) <= rel * tau_hi) | (np.abs(p - tau_lo) <= rel * tau_lo)
+    if tau_skim > 0:
+        m |= np.abs(p - tau_skim) <= rel * tau_skim
+    return m
 
 
 def gpu_plan(dev, cfg, mode=None, out_fp32=True, top_k=None):

@@ -51,6 +51,10 @@ def test_valid_configs(lib):
     assert status(lib, good(block_q=64, block_k=8)) == 0                 # 4095 key blocks
     assert status(lib, good(mode="price", price=0.01)) == 0
     assert status(lib, good(mode="price", price=0.0)) == 0
+    assert status(lib, good(tau_skim=1e-4)) == 0                         # SKIM tier, threshold mode
+    assert status(lib, good(tau_skim=0.001)) == 0                        # tau_skim == tau_lo
+    assert status(lib, good(mode="external", tau_skim=1e-4)) == 0
+    assert status(lib, good(mode="adaptive", block_q=64, block_k=16, tau_skim=1e-4)) == 0   # ignored there
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -66,6 +70,8 @@ def test_valid_configs(lib):
     (dict(seq_len=64 * 5000), -2),
     (dict(mode="price", price=-1.0), -1), (dict(mode="price", price=float("nan")), -1),
     (dict(mode=5), -1),
+    (dict(tau_skim=-1e-4), -1), (dict(tau_skim=0.002), -1), (dict(tau_skim=float("nan")), -1),
+    (dict(tau_skim=1e-4, block_q=64, block_k=16), -2), (dict(mode="external", tau_skim=1e-4, block_k=8), -2),
 ])
 def test_invalid_configs(lib, kw, code):
     st = status(lib, good(**kw))
@@ -106,6 +112,14 @@ def test_workspace_formula(lib):
     assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="price", price=0.01)), ctypes.byref(m)) == 0
     extra = BH * Nq * Nk * 8 + BH * (Nq + Nk) * D * 4 + BH * (Nq + 4 * Nk) * 4
     assert extra <= m.value - n.value <= extra * 1.05
+    # the SKIM tier adds the MXFP4 K codes and scales and the fp16 SKIM V operand
+    k = ctypes.c_size_t()
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(tau_skim=1e-4)), ctypes.byref(k)) == 0
+    extra = BH * Nk * 64 * (D // 2 + D // 32 + 2 * D)
+    assert extra <= k.value - n.value <= extra * 1.01
+    # ... and only where a SKIM tile can occur
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="all_full", tau_skim=1e-4)), ctypes.byref(k)) == 0
+    assert k.value == n.value
 
 
 def test_plan_rejects_bad_pointers_before_any_launch(lib):
@@ -121,7 +135,17 @@ def test_plan_rejects_bad_pointers_before_any_launch(lib):
     assert out.value is None
     assert lib.tattn_forward(None, 16, 32, 48, 64, None) == -1
     assert lib.tattn_plan_stats(None, None) == -1
+    assert lib.tattn_plan_get_mx4(None, None, None, None, None) == -1
     lib.tattn_plan_destroy(None)
+
+
+def test_config_layout_matches_header(lib):
+    """The binding's struct has the header's field order; tau_skim is last."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} tattn_config;", text, flags=re.S).group(1)
+    names = re.findall(r"([a-z_]+)\s*[,;]", body)
+    assert names == [f for f, _ in Config._fields_]
+    assert ctypes.sizeof(Config) == 96
 
 
 def test_status_strings(lib):

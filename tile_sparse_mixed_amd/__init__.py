@@ -16,10 +16,10 @@ import numpy as np
 
 __all__ = ["plan", "replan", "forward", "Plan", "TattnError", "load_library", "Config", "Stats",
            "MODE_THRESHOLD", "MODE_ADAPTIVE", "MODE_ALL_FULL", "MODE_EXTERNAL", "MODE_PRICE",
-           "SKIP", "LOW", "FULL"]
+           "SKIP", "LOW", "FULL", "SKIM"]
 
 MODE_THRESHOLD, MODE_ADAPTIVE, MODE_ALL_FULL, MODE_EXTERNAL, MODE_PRICE = 0, 1, 2, 3, 4
-SKIP, LOW, FULL = 0, 1, 2
+SKIP, LOW, FULL, SKIM = 0, 1, 2, 3
 _MODES = {"threshold": MODE_THRESHOLD, "adaptive": MODE_ADAPTIVE, "all_full": MODE_ALL_FULL,
           "external": MODE_EXTERNAL, "price": MODE_PRICE}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtattn.so")
@@ -40,13 +40,13 @@ class Config(ctypes.Structure):
                 ("full_frac", ctypes.c_float), ("entropy_samples", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
-                ("price", ctypes.c_float)]
+                ("price", ctypes.c_float), ("tau_skim", ctypes.c_float)]
 
 
 class Stats(ctypes.Structure):
     _fields_ = [("n_full", ctypes.c_int64), ("n_low", ctypes.c_int64), ("n_skip", ctypes.c_int64),
                 ("n_diag", ctypes.c_int64), ("flops_bf16", ctypes.c_double), ("flops_fp8", ctypes.c_double),
-                ("flops_dense", ctypes.c_double)]
+                ("flops_dense", ctypes.c_double), ("n_skim", ctypes.c_int64), ("flops_fp4", ctypes.c_double)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -65,6 +65,7 @@ _SIGS = {
     "tattn_plan_get_lists": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_get_pool": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_get_codes": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+    "tattn_plan_get_mx4": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_stats": (ctypes.c_int, [_VP, ctypes.POINTER(Stats)]),
     "tattn_plan_get_kh": (ctypes.c_int, [_VP, _VP, _VP]),
     "tattn_plan_get_moments": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
@@ -100,13 +101,13 @@ def _check(status):
 
 def make_config(batch, heads, seq_len, head_dim, block_q, block_k, tau_hi=0.0, tau_lo=0.0, top_k=0,
                 mode="threshold", keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256,
-                out_fp32=False, strides=None, price=0.0):
+                out_fp32=False, strides=None, price=0.0, tau_skim=0.0):
     if strides is None:
         strides = (heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
     return Config(batch, heads, seq_len, head_dim, block_q, block_k, float(tau_hi), float(tau_lo), int(top_k), m,
                   float(keep_min), float(keep_max), float(full_frac), int(entropy_samples), 0,
-                  1 if out_fp32 else 0, *[int(s) for s in strides], float(price))
+                  1 if out_fp32 else 0, *[int(s) for s in strides], float(price), float(tau_skim))
 
 
 def _stream():
@@ -189,6 +190,18 @@ class Plan:
         _check(load_library().tattn_plan_get_codes(self._handle, k8.ctypes.data, vlow.ctypes.data, _stream()))
         return k8, vlow.view(np.float16)
 
+    def mx4(self):
+        """SKIM tier: the MXFP4 copies of K (codes, two per byte, [B, H, N,
+        d/2] uint8; E8M0 scale bytes [B, H, N, d/32]) and the SKIM value
+        operand as float16 [B, H, N, d]."""
+        n, d = self.cfg.seq_len, self.cfg.head_dim
+        k4 = np.empty(self._shape(n, d // 2), np.uint8)
+        k4s = np.empty(self._shape(n, d // 32), np.uint8)
+        vs = np.empty(self._shape(n, d), np.uint16)
+        _check(load_library().tattn_plan_get_mx4(self._handle, k4.ctypes.data, k4s.ctypes.data, vs.ctypes.data,
+                                                 _stream()))
+        return dict(k4=k4, k4s=k4s, vskim=vs.view(np.float16))
+
     def stats(self) -> dict:
         st = Stats()
         _check(load_library().tattn_plan_stats(self._handle, ctypes.byref(st)))
@@ -229,14 +242,17 @@ def _check_tensors(q, k, v):
 
 def plan(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, mode="threshold",
          keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256, out_fp32=False,
-         workspace=None, price=0.0) -> Plan:
+         workspace=None, price=0.0, tau_skim=0.0) -> Plan:
     """Pool, quantise and route (K1, K2).  q, k, v: bf16 [B, H, N, d] on the GPU.
-    ``workspace`` (a uint8 GPU tensor, e.g. an earlier plan's) is reused when
-    large enough; the earlier plan must not be used afterwards."""
+    ``tau_skim`` > 0 adds the MXFP4 SKIM tier (threshold and external modes,
+    64-key blocks).  ``workspace`` (a uint8 GPU tensor, e.g. an earlier
+    plan's) is reused when large enough; the earlier plan must not be used
+    afterwards."""
     _check_tensors(q, k, v)
     B, H, N, d = q.shape
     cfg = make_config(B, H, N, d, block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
-                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price)
+                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price,
+                      tau_skim=tau_skim)
     return Plan(cfg, q, k, v, workspace=workspace)
 
 

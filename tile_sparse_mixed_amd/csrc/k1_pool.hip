@@ -18,6 +18,7 @@
 //   vlow             the low tier's V operand, fl16(fl32(decode(E4M3(v * inv)) * sv)),
 //                    in the same transposed layout.
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
+// With the SKIM tier a third kernel writes MXFP4 copies of K and V (k1_mx4).
 // For the price router both also write second moments from float64 sums of
 // squares ("Triage": the router works from block statistics): per dimension
 // the query mean square and the key variance, per block the key and value
@@ -314,6 +315,70 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   }
 }
 
+// MXFP4 copies of K_J and V_J for the SKIM tier (64-key blocks; "Triage":
+// skimming a tile in a 4-bit format).  Per key row and 32 channels one E8M0
+// scale and 32 E2M1 codes.  K: codes [64][D/2] (channel 2m in the low nibble
+// of byte m) and scale bytes [64][D/32], row-major; V: the dequantised values
+// fl16(code value * 2^e), transposed [D][64] in vt_pos order like the other
+// V operands.  Rows past N are zero (codes 0, scale byte 0).
+template <int D>
+__global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
+  constexpr int NB = D / 32;            // scale blocks per row
+  __shared__ uint16_t tileV[64 * D];    // dequantised V, fp16 [key][d]
+  const Dims& dm = a.d;
+  const int bh = blockIdx.x / dm.Nk, J = blockIdx.x % dm.Nk;
+  const int b = bh / dm.H, h = bh % dm.H;
+  const int rows = min(64, dm.N - J * 64);
+  const int64_t off = (int64_t)b * dm.sb + (int64_t)h * dm.sh + (int64_t)J * 64 * dm.sn;
+  unsigned char* slab = a.ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
+  unsigned char* k4 = slab + a.L.sl.k4 + (int64_t)J * 64 * (D / 2);
+  unsigned char* k4s = slab + a.L.sl.k4s + (int64_t)J * 64 * NB;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(slab + a.L.sl.vskim) + (int64_t)J * 64 * D;
+  for (int u = threadIdx.x; u < 2 * 64 * NB; u += kThreads) {
+    const bool isv = u >= 64 * NB;
+    const int w = isv ? u - 64 * NB : u;
+    const int r = w / NB, c = w % NB;
+    const uint16_t* src = (isv ? a.v : a.k) + off + (int64_t)r * dm.sn + 32 * c;
+    float x[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (r < rows) raw = reinterpret_cast<const uint4*>(src)[i];
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float f = __uint_as_float(e & 1 ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
+        x[8 * i + e] = f;
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
+      }
+    }
+    const int ex = mx4_exponent(amax);
+    if (!isv) {
+      uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
+      *reinterpret_cast<uint4*>(k4 + r * (D / 2) + 16 * c) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      k4s[r * NB + c] = static_cast<unsigned char>(ex + 127);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; e++)
+        tileV[r * D + 32 * c + e] = f32_to_f16(ldexpf(e2m1_value(e2m1_code(ldexpf(x[e], -ex))), ex));
+    }
+  }
+  __syncthreads();
+  // element e of stored row d holds key vt_key<64>(e), 8 elements per store
+  for (int u = threadIdx.x; u < D * 8; u += kThreads) {
+    const int d = u / 8, q = u % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; e2++)
+      w[e2] = uint32_t(tileV[vt_key<64>(q * 8 + 2 * e2) * D + d]) |
+              (uint32_t(tileV[vt_key<64>(q * 8 + 2 * e2 + 1) * D + d]) << 16);
+    *reinterpret_cast<uint4*>(vs + d * 64 + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <int D, bool MOM>
 hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
   const Dims& d = a.d;
@@ -329,6 +394,10 @@ hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k1_q<D, 128, MOM>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((k1_q<D, 64, MOM>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || !a.mx4) return e;
+  if (d.Bk != 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k1_mx4<D>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -5,9 +5,10 @@
 //      probability of the block as the importance metric; the ln n_J term
 //      weights a key block by its real size).
 // K2b  per query block I: p_IJ = softmax_J(S_IJ) (float64), then the tier map:
-//        THRESHOLD  FULL if p >= tau_hi, LOW if p >= tau_lo, else SKIP, after an
-//                   optional top-k by (p desc, J asc) ("APT": dual thresholds;
-//                   "HierPAS": top-k),
+//        THRESHOLD  FULL if p >= tau_hi, LOW if p >= tau_lo, SKIM if p >=
+//                   tau_skim > 0 ("Triage": the 4-bit skim tier), else SKIP;
+//                   then an optional top-k by (p desc, J asc) ("APT": dual
+//                   thresholds; "HierPAS": top-k),
 //        ADAPTIVE   k_h from the entropy of p on sampled rows (K2e), then the top
 //                   ceil(full_frac*k_h) tiles FULL, the rest of the top k_h LOW
 //                   ("HierPAS": sampling-based entropy, head-wise retention),
@@ -16,7 +17,7 @@
 //                   block second moments, K2a's spread product) plus price x
 //                   work ("Triage": error-predicting router, one price);
 //      diagonal tiles forced FULL; then a stable compaction into
-//      [FULL asc | LOW asc | SKIP asc] with wavefront ballots.
+//      [FULL asc | LOW asc | SKIM asc | SKIP asc] with wavefront ballots.
 // K2c  compaction only, for a tier map supplied by the caller.
 // K2d  the order in which the fused kernel takes its rows (longest last rows first).
 // Ranks and cuts use exact comparisons of the float64 p values.
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void k2a_scores(RouterArgs a) {
 // ------------------------------------------------------------------ block reductions
 struct Red {
   double d[kWaves];
-  int i[kWaves * 4];
+  int i[kWaves * 8];
   uint64_t u[kWaves];
   // radix-select digit histogram, one per wave: a pair of waves shares a word,
   // 16 bits each (a wave counts at most kMaxNk / kWaves values)
@@ -287,11 +288,12 @@ __device__ inline void diag_range(const Dims& dm, int I, int& j0, int& j1) {
   j1 = (r1 - 1) / dm.Bk;
 }
 
-// Stable compaction of the tier row `tr` (in LDS) into lists/counts.  counts
-// = (n_full, n_low, n_skip, steps): steps is the number of steps the fused
-// kernel takes for the row, ceil(nF/G) + ceil(nL/G) + 2 x (chunks of 64 key
-// blocks holding a skipped block), G = 64 / Bk key blocks per step; it orders
-// the fused kernel's work.
+// Stable compaction of the tier row `tr` (in LDS) into lists [FULL | LOW |
+// SKIM | SKIP] and counts = (n_full, n_low, n_skip, steps): steps is the
+// number of steps the fused kernel takes for the row, ceil(nF/G) + ceil(nL/G)
+// + ceil(nK/G) + 2 x (chunks of 64 key blocks holding a skipped block), G =
+// 64 / Bk key blocks per step, nK the SKIM count; it orders the fused
+// kernel's work.
 __device__ void compact_row(const unsigned char* tr, int n, int bk, int16_t* list, int* counts, Red& r) {
   // each wave owns a run of whole 64-tile chunks: it counts its tiers, one
   // barrier publishes the per-wave counts, then it writes its run in order
@@ -299,12 +301,12 @@ __device__ void compact_row(const unsigned char* tr, int n, int bk, int16_t* lis
   const int nch = (n + 63) / 64, cpw = (nch + kWaves - 1) / kWaves;
   const int c0 = w * cpw, c1 = min(nch, c0 + cpw);
   const uint64_t below = (1ull << lane) - 1;
-  int cnt[3] = {0, 0, 0}, sch = 0;
+  int cnt[4] = {0, 0, 0, 0}, sch = 0;   // indexed by tier value
   for (int c = c0; c < c1; c++) {
     const int J = c * 64 + lane;
     const int tv = J < n ? tr[J] : -1;
 #pragma unroll
-    for (int T = 0; T < 3; T++) {
+    for (int T = 0; T < 4; T++) {
       const uint64_t bal = __ballot(tv == T);
       cnt[T] += __popcll(bal);
       if (T == TATTN_SKIP) sch += bal != 0;
@@ -312,37 +314,38 @@ __device__ void compact_row(const unsigned char* tr, int n, int bk, int16_t* lis
   }
   if (lane == 0) {
 #pragma unroll
-    for (int T = 0; T < 3; T++) r.i[w * 4 + T] = cnt[T];
-    r.i[w * 4 + 3] = sch;
+    for (int T = 0; T < 4; T++) r.i[w * 8 + T] = cnt[T];
+    r.i[w * 8 + 4] = sch;
   }
   __syncthreads();
-  int woff[3] = {0, 0, 0}, tot[3] = {0, 0, 0}, snc = 0;
+  int woff[4] = {0, 0, 0, 0}, tot[4] = {0, 0, 0, 0}, snc = 0;
 #pragma unroll
   for (int ww = 0; ww < kWaves; ww++) {
 #pragma unroll
-    for (int T = 0; T < 3; T++) {
-      if (ww < w) woff[T] += r.i[ww * 4 + T];
-      tot[T] += r.i[ww * 4 + T];
+    for (int T = 0; T < 4; T++) {
+      if (ww < w) woff[T] += r.i[ww * 8 + T];
+      tot[T] += r.i[ww * 8 + T];
     }
-    snc += r.i[ww * 4 + 3];
+    snc += r.i[ww * 8 + 4];
   }
-  const int nF = tot[TATTN_FULL], nL = tot[TATTN_LOW], nS = tot[TATTN_SKIP];
+  const int nF = tot[TATTN_FULL], nL = tot[TATTN_LOW], nS = tot[TATTN_SKIP], nK = tot[TATTN_SKIM];
   if (threadIdx.x == 0) {
     const int G = 64 / bk;
     counts[0] = nF;
     counts[1] = nL;
     counts[2] = nS;
-    counts[3] = (nF + G - 1) / G + (nL + G - 1) / G + 2 * snc;
+    counts[3] = (nF + G - 1) / G + (nL + G - 1) / G + (nK + G - 1) / G + 2 * snc;
   }
-  int base[3];   // indexed by tier value
-  base[TATTN_SKIP] = nF + nL + woff[TATTN_SKIP];
-  base[TATTN_LOW] = nF + woff[TATTN_LOW];
+  int base[4];   // indexed by tier value
   base[TATTN_FULL] = woff[TATTN_FULL];
+  base[TATTN_LOW] = nF + woff[TATTN_LOW];
+  base[TATTN_SKIM] = nF + nL + woff[TATTN_SKIM];
+  base[TATTN_SKIP] = nF + nL + nK + woff[TATTN_SKIP];
   for (int c = c0; c < c1; c++) {
     const int J = c * 64 + lane;
     const int tv = J < n ? tr[J] : -1;
 #pragma unroll
-    for (int T = 0; T < 3; T++) {
+    for (int T = 0; T < 4; T++) {
       const uint64_t bal = __ballot(tv == T);
       if (tv == T) list[base[T] + __popcll(bal & below)] = static_cast<int16_t>(J);
       base[T] += __popcll(bal);
@@ -502,10 +505,10 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
       pout[J] = 0.0f;
     }
   } else if (a.mode == TATTN_MODE_THRESHOLD) {
-    const double th = a.tau_hi, tl = a.tau_lo;
+    const double th = a.tau_hi, tl = a.tau_lo, tk = a.tau_skim;
     for (int J = threadIdx.x; J < n; J += kThreads) {
       const double p = pv[J];
-      tr[J] = p >= th ? TATTN_FULL : (p >= tl ? TATTN_LOW : TATTN_SKIP);
+      tr[J] = p >= th ? TATTN_FULL : p >= tl ? TATTN_LOW : (tk > 0.0 && p >= tk) ? TATTN_SKIM : TATTN_SKIP;
       pout[J] = static_cast<float>(p);
     }
     if (a.top_k > 0) {

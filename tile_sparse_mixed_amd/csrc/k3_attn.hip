@@ -55,7 +55,7 @@ namespace {
 
 constexpr float kLazy = 8.0f;   // raise m only when a tile max exceeds it by this much (log2)
 
-enum StepKind { kFull = 0, kLow = 1, kSkipS = 2, kSkipPV = 3 };
+enum StepKind { kFull = 0, kLow = 1, kSkipS = 2, kSkipPV = 3, kSkim = 4 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -123,16 +123,19 @@ struct StepScale {
   float c[N];
 };
 
-template <int D, int NW, int BK>
+// SKIM: the instance also runs the SKIM tier (64-key blocks only); the other
+// instances carry none of its code.
+template <int D, int NW, int BK, bool SKIM>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
   static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
+  static_assert(!SKIM || BK == 64, "the SKIM tier runs on 64-key blocks");
   constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
   constexpr int R1 = 128 * D;
   __shared__ __attribute__((aligned(1024))) unsigned char stA[STAGE];   // stage of even steps
   __shared__ __attribute__((aligned(1024))) unsigned char stB[STAGE];   // stage of odd steps
-  __shared__ int16_t slist[kMaxNk];          // the row's FULL then LOW key blocks
+  __shared__ int16_t slist[kMaxNk];          // the row's FULL, LOW (and SKIM) key blocks
   __shared__ uint64_t smask[64];             // per visited chunk: bit j = block 64c + j skipped
   __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
   __shared__ int snc;
@@ -160,9 +163,10 @@ void k3_attn(AttnArgs a) {
   const int* counts = reinterpret_cast<const int*>(ws + a.L.counts) + row * 4;
   const int nF = counts[0], nL = counts[1];
   const int nK = nF + nL;
+  const int nSk = SKIM ? dm.Nk - nK - counts[2] : 0;   // SKIM tiles follow LOW in the list
   {
     const int16_t* list = reinterpret_cast<const int16_t*>(ws + a.L.lists) + row * dm.Nk;
-    for (int i = tid; i < nK; i += NW * 64) slist[i] = list[i];
+    for (int i = tid; i < nK + nSk; i += NW * 64) slist[i] = list[i];
   }
   if (wave == 0) {   // lane c: the skip mask of key-block chunk c, from the tier row
     const unsigned char* tiers = ws + a.L.tiers + row * dm.Nk;
@@ -182,7 +186,7 @@ void k3_attn(AttnArgs a) {
   }
   __syncthreads();
   const int sF = (nF + G - 1) / G, sL = (nL + G - 1) / G;   // FULL / LOW steps
-  const int nSteps = sF + 2 * snc + sL;
+  const int nSteps = sF + 2 * snc + sL + nSk;
 
   const uint16_t* kin = a.k + toff;
   const unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
@@ -207,15 +211,19 @@ void k3_attn(AttnArgs a) {
   const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
 
   // step order: FULL tiles, then the skip chunks (score / P.V pairs), then LOW
-  // tiles, so the bf16 Q registers are dead before the E4M3 copy is made.
-  const int nS2 = 2 * snc, tLow = sF + nS2;
+  // tiles, so the bf16 Q registers are dead before the E4M3 copy is made, then
+  // SKIM tiles.
+  const int nS2 = 2 * snc, tLow = sF + nS2, tSk = tLow + sL;
   auto step_kind = [&](int t) __attribute__((always_inline)) {
     if (t < sF) return (int)kFull;
     if (t < tLow) return ((t - sF) & 1) ? (int)kSkipPV : (int)kSkipS;
+    if (SKIM && t >= tSk) return (int)kSkim;
     return (int)kLow;
   };
-  // list entry of key block g of a FULL or LOW step, and the end of its list
-  auto list_idx = [&](int t, int g) { return t < sF ? G * t + g : nF + G * (t - tLow) + g; };
+  // list entry of key block g of a FULL, LOW or SKIM step, and the end of its list
+  auto list_idx = [&](int t, int g) {
+    return t < sF ? G * t + g : (SKIM && t >= tSk) ? nK + (t - tSk) + g : nF + G * (t - tLow) + g;
+  };
   auto list_end = [&](int t) { return t < sF ? nF : nK; };
   auto list_at = [&](int t) { return (int)slist[list_idx(t, 0)]; };
 
@@ -250,6 +258,12 @@ void k3_attn(AttnArgs a) {
   // (instruction k covers rows 16k..16k+15: swz64(r) = ((lane >> 3) & 3) ^ (lane >> 5)).
   int voffK8 = D == 128 ? voffV
                               : (lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 16);
+  // [64][D/2] MXFP4 K tiles (SKIM): an instruction covers 2048/D rows of D/32
+  // chunks; LDS slot c of row r holds chunk c ^ swz4(r), swz4(r) = (r >> 2) & 3
+  // for 64-byte rows and (r >> 3) & 1 for 32-byte rows, which inside an
+  // instruction is (lane >> 4) masked to the chunk count
+  constexpr int C4 = D / 32;   // 16-byte chunks per MXFP4 row = scale bytes per row
+  const int voffK4 = (lane / C4) * (D / 2) + (((lane & (C4 - 1)) ^ ((lane >> 4) & (C4 - 1))) * 16);
   // one resource over this head's slab; every workspace operand is a scalar
   // sub-offset of it
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(slab, (uint32_t)SL.bytes);
@@ -378,6 +392,20 @@ void k3_attn(AttnArgs a) {
       }
       load_vt16(st + R1, rS, (int)SL.vlow + J * 128 * D);
       cst.c[0] = sq * skp[J] * cF;
+    } else if (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
+      // MXFP4 K [64][D/2] into R0, its scale bytes [64][D/32] after it (one
+      // D/32-byte load per lane from wave 0, into a 4-byte LDS slot per
+      // lane), fp16 dequantised V^T into R1
+      const int J = list_at(t);
+      for (int k = wave; k < D / 32; k += NW) dma16(rS, st + k * 1024, voffK4, (int)SL.k4 + J * 32 * D + k * 1024);
+      if (wave == 0) {
+        if constexpr (D == 128)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 4, lane * 4, (int)SL.k4s + J * 2 * D, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 2, lane * 2, (int)SL.k4s + J * 2 * D, 0, 0);
+      }
+      load_vt16(st + R1, rS, (int)SL.vskim + J * 128 * D);
+      cst.c[0] = cF;
     } else {
       const int c = schunk[(t - sF) >> 1];
       if ((KINDS & (1 << kSkipS)) && kind == kSkipS) {
@@ -460,6 +488,34 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int b = 0; b < 2; b++)
         s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[2 * i + b], q8[i], s[b], 0, 0, 0, 0, 0, 0);
+  };
+  // S^T of a SKIM step on the block-scaled fp4 MFMA: lane (ln, lh) holds
+  // channels 64i + 32lh .. +31 of key rows ln and ln + 32 (from the stage) and
+  // of its query row (q4, made once per row): one E8M0 block each, whose
+  // scale bytes the MFMA applies (opsel picks the byte of the key row's word).
+  auto scores_fp4 = [&](const unsigned char* st, f32x16* s, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
+    const int sw = D == 128 ? (ln >> 2) & 3 : (ln >> 3) & 1;
+    i32x8 ka[D / 32];
+    int ks[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      const int r = ln + 32 * b;
+      // the scale DMA gives every lane a 4-byte LDS slot, also for the 2-byte rows of D = 64
+      const uint32_t word = D == 128 ? *reinterpret_cast<const uint32_t*>(st + 32 * D + 4 * r)
+                                     : static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(st + 32 * D + 4 * r));
+      ks[b] = static_cast<int>(word >> (8 * lh));   // byte 2i of ks = scale of block 2i + lh
+#pragma unroll
+      for (int i = 0; i < D / 64; i++) {
+        const uint4 v = *reinterpret_cast<const uint4*>(st + r * (D / 2) + (((2 * i + lh) ^ sw) << 4));
+        ka[2 * i + b] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[b], q4[0], s[b], 4, 4, 0, ks[b], 0, q4s[0]);
+      if constexpr (D == 128)
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[2 + b], q4[1], s[b], 4, 4, 2, ks[b], 0, q4s[1]);
+    }
   };
   // Key of register (b, r) of this lane: 32b + 8(r/4) + 4lh + r%4.  Masks keys
   // >= nvalid (the ragged last tile).
@@ -552,7 +608,7 @@ void k3_attn(AttnArgs a) {
       // occurs in the last step of the phase.  Register (b, r) is key
       // 8((r >> 2) & 1) + 4lh + r % 4 of 16-key block 2b + r / 8, or key
       // 4((r >> 2) & 1) + r % 4 of 8-key block (slot) 4b + 2(r / 8) + lh.
-      if (t == (LOW ? nSteps - 1 : sF - 1)) {
+      if (t == (LOW ? tSk - 1 : sF - 1)) {
         const int i0 = list_idx(t, 0), e = list_end(t);
         // valid keys of each block: 0 past the list end, fewer in block Nk - 1
         int lim[G];
@@ -587,6 +643,15 @@ void k3_attn(AttnArgs a) {
       }
       softmax(s, c, tmax);
     }
+    pv(st);
+  };
+  // a SKIM tile (64-key blocks) staged in `st`
+  auto skim_step = [&](int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    scores_fp4(st, s, q4, q4s);
+    const int J = list_at(t);
+    if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
+    softmax(s, c, row_max(s) * c.c[0]);
     pv(st);
   };
   // pooled keys of a chunk of 64 skipped-candidate blocks: scores only
@@ -645,12 +710,14 @@ void k3_attn(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     refresh();
   };
-  using KAll = std::integral_constant<int, 15>;
-  using KAfterFull = std::integral_constant<int, (1 << kFull) | (1 << kSkipS) | (1 << kLow)>;
+  constexpr int kSk = SKIM ? 1 << kSkim : 0;
+  using KAll = std::integral_constant<int, 15 | kSk>;
+  using KAfterFull = std::integral_constant<int, (1 << kFull) | (1 << kSkipS) | (1 << kLow) | kSk>;
   using KSkipS = std::integral_constant<int, 1 << kSkipS>;
   using KSkipPV = std::integral_constant<int, 1 << kSkipPV>;
-  using KAfterSkip = std::integral_constant<int, (1 << kSkipS) | (1 << kLow)>;
-  using KLow = std::integral_constant<int, 1 << kLow>;
+  using KAfterSkip = std::integral_constant<int, (1 << kSkipS) | (1 << kLow) | kSk>;
+  using KLow = std::integral_constant<int, (1 << kLow) | kSk>;
+  using KSkimOnly = std::integral_constant<int, kSk>;
   if (nSteps > 0) issue(KAll{}, 0, stA, cA);
   wait_vm0();
   __syncthreads();
@@ -686,8 +753,8 @@ void k3_attn(AttnArgs a) {
     if (t & 1) skip_pairs(P1{});
     else skip_pairs(P0{});
   }
-  if (t < nSteps) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
-                      // fp8 instruction i = bf16 chunks 4i..4i+3)
+  if (t < tSk) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
+                   // fp8 instruction i = bf16 chunks 4i..4i+3)
     i32x8 q8reg[D / 64];
     const float iq = reinterpret_cast<const float*>(ws + a.L.iq)[row];
 #pragma unroll
@@ -705,11 +772,47 @@ void k3_attn(AttnArgs a) {
         q8reg[i][2 * cc + 1] = hi;
       }
     }
-    run_phase(nSteps, [&](auto p, int tt) __attribute__((always_inline)) {
+    run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
       if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
       kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
       next();
     });
+  }
+  if constexpr (SKIM) {
+    if (t < nSteps) {   // SKIM tiles remain: the MXFP4 copy of this lane's Q row,
+                        // channels 64i + 32lh .. +31 for instruction i
+      i32x8 q4reg[D / 64];
+      int q4s[D / 64];
+      const uint16_t* qp = a.q + toff + (int64_t)qrow * dm.sn + 32 * lh;
+#pragma unroll
+      for (int i = 0; i < D / 64; i++) {
+        float x[32];
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          uint4 raw = make_uint4(0, 0, 0, 0);
+          if (qrow < dm.N) raw = *reinterpret_cast<const uint4*>(qp + 64 * i + 8 * j);
+          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float f = __uint_as_float(e & 1 ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
+            x[8 * j + e] = f;
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
+          }
+        }
+        const int ex = mx4_exponent(amax);
+        uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
+        q4reg[i] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+        q4s[i] = ex + 127;
+      }
+      run_phase(nSteps, [&](auto p, int tt) __attribute__((always_inline)) {
+        if (tt + 1 < nSteps) issue(KSkimOnly{}, tt + 1, stg(flip(p)), scl(flip(p)));
+        skim_step(tt, stg(p), scl(p), q4reg, q4s);
+        next();
+      });
+    }
   }
 
   // ---- epilogue: O = acc / l
@@ -743,12 +846,15 @@ void k3_attn(AttnArgs a) {
 
 template <int D, int NW>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  if (a.d.Bk == 64)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+  if (a.skim && a.d.Bk != 64) return hipErrorInvalidValue;
+  if (a.skim)
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, true>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+  else if (a.d.Bk == 64)
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, false>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
   else if (a.d.Bk == 16)
-    hipLaunchKernelGGL((k3_attn<D, NW, 16>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 16, false>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((k3_attn<D, NW, 8>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 8, false>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -102,6 +102,34 @@ __device__ inline uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint
 __device__ inline uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
 
 // ---------------------------------------------------------------------------
+// MXFP4 (OCP Microscaling): E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6; code = 2 * exponent field + mantissa bit, bit 3 the sign) with one E8M0
+// scale 2^e per 32 elements, e = floor(log2 amax) - 2 (2 = the exponent of
+// E2M1's largest normal), clamped to [-127, 127]; -127 for an all-zero block.
+__device__ inline int mx4_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int e = ilogbf(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// E2M1 code of y (the element already divided by its block scale, |y| < 8):
+// round to nearest, ties to even, on the grid spacing of y's binade (0.5 below
+// 2, 1 in [2, 4), 2 above), magnitudes past 6 clamped to 6.
+__device__ inline uint32_t e2m1_code(float y) {
+  const float a = __builtin_fabsf(y);
+  uint32_t c;
+  if (a < 2.0f) c = static_cast<uint32_t>(__builtin_rintf(a * 2.0f));            // codes 0..4
+  else if (a < 4.0f) c = static_cast<uint32_t>(__builtin_rintf(a)) + 2u;         // 2, 3, 4 -> 4, 5, 6
+  else c = __builtin_rintf(a * 0.5f) >= 3.0f ? 7u : 6u;                          // 6 (or 8) -> 7, 4 -> 6
+  return c | (y < 0.0f ? 8u : 0u);
+}
+// value of an E2M1 code
+__device__ inline float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float mag = m < 2u ? 0.5f * static_cast<float>(m) : ldexpf(1.0f + 0.5f * static_cast<float>(m & 1u), (int)(m >> 1) - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
 // Wave-level reductions (wave64).
 __device__ inline float wave_max(float v) {
 #pragma unroll

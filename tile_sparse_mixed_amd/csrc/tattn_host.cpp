@@ -54,7 +54,7 @@ Dims make_dims(const tattn_config& c) {
   return d;
 }
 
-Layout make_layout(const Dims& d, int entropy_samples, bool moments) {
+Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -85,6 +85,10 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments) {
     sl.kbhi = sub(Nk * D * 2);
     sl.kblo = sub(Nk * D * 2);
     sl.vbarT = sub((size_t)d.NkC * 64 * D * 2);
+    const size_t k4n = skim ? Nk * Bk : 0;
+    sl.k4 = sub(k4n * D / 2);
+    sl.k4s = sub(k4n * D / 32);
+    sl.vskim = sub(k4n * D * 2);
     sl.bytes = o;
   }
   L.slab = take(BH * L.sl.bytes);
@@ -113,6 +117,14 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The SKIM tier is on for a positive tau_skim in THRESHOLD and EXTERNAL modes.
+static bool skim_on(const tattn_config& c) {
+  return c.tau_skim > 0.0f && (c.mode == TATTN_MODE_THRESHOLD || c.mode == TATTN_MODE_EXTERNAL);
+}
+static Layout layout_of(const tattn_config& c) {
+  return make_layout(make_dims(c), c.entropy_samples, c.mode == TATTN_MODE_PRICE, skim_on(c));
+}
+
 static tattn_status validate(const tattn_config* c) {
   if (!c) return fail(TATTN_E_INVALID, "config is NULL");
   if (c->batch < 1 || c->heads < 1 || c->seq_len < 1)
@@ -130,6 +142,10 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "price must be finite and >= 0 (got %g)", c->price);
   if (!std::isfinite(c->tau_hi) || !std::isfinite(c->tau_lo) || c->tau_lo < 0.0f || c->tau_lo > c->tau_hi)
     return fail(TATTN_E_INVALID, "thresholds need 0 <= tau_lo <= tau_hi (got %g, %g)", c->tau_lo, c->tau_hi);
+  if (!std::isfinite(c->tau_skim) || c->tau_skim < 0.0f || c->tau_skim > c->tau_lo)
+    return fail(TATTN_E_INVALID, "tau_skim needs 0 <= tau_skim <= tau_lo (got %g, tau_lo %g)", c->tau_skim, c->tau_lo);
+  if (skim_on(*c) && c->block_k != 64)
+    return fail(TATTN_E_UNSUPPORTED, "the SKIM tier needs 64-key blocks (block_k %d)", c->block_k);
   const int64_t nq = (c->seq_len + (int64_t)c->block_q - 1) / c->block_q;
   const int64_t nk = (c->seq_len + (int64_t)c->block_k - 1) / c->block_k;
   if (c->top_k < 0 || c->top_k > nk) return fail(TATTN_E_INVALID, "top_k %d outside [0, %lld]", c->top_k, (long long)nk);
@@ -181,7 +197,7 @@ tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes) {
   tattn_status st = validate(cfg);
   if (st != TATTN_OK) return st;
   if (!bytes) return fail(TATTN_E_INVALID, "bytes is NULL");
-  *bytes = make_layout(make_dims(*cfg), cfg->entropy_samples, cfg->mode == TATTN_MODE_PRICE).total;
+  *bytes = layout_of(*cfg).total;
   return ok();
 }
 
@@ -199,6 +215,7 @@ static RouterArgs router_args(const tattn_plan_s* p) {
   r.full_frac = p->cfg.full_frac;
   r.samples = std::max(1, p->cfg.entropy_samples);
   r.price = p->cfg.price;
+  r.tau_skim = skim_on(p->cfg) ? p->cfg.tau_skim : 0.0f;
   return r;
 }
 
@@ -211,7 +228,7 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
   if (!q || !k || !v) return fail(TATTN_E_INVALID, "q, k and v must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
   const Dims d = make_dims(*cfg);
-  const Layout L = make_layout(d, cfg->entropy_samples, cfg->mode == TATTN_MODE_PRICE);
+  const Layout L = layout_of(*cfg);
   if (!workspace) return fail(TATTN_E_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -227,7 +244,7 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
   p->has_tiers = cfg->mode != TATTN_MODE_EXTERNAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-              p->ws, L, d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0};
+              p->ws, L, d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(*cfg) ? 1 : 0};
   hipError_t e = launch_pool(pa, s);
   if (e != hipSuccess) {
     delete p;
@@ -251,7 +268,7 @@ tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const v
   if (k != p->k || v != p->v) return fail(TATTN_E_STATE, "k and v differ from the tensors the plan was built with");
   if (!p->has_tiers) return fail(TATTN_E_STATE, "external-mode plan has no tiers yet (call tattn_plan_set_tiers)");
   AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), o,
-             p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d};
+             p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d, skim_on(p->cfg) ? 1 : 0};
   hipError_t e = launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return ok();
@@ -263,7 +280,7 @@ tattn_status tattn_replan(tattn_plan_t p, const void* q, const void* k, const vo
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
   if (!p->has_tiers) return fail(TATTN_E_STATE, "plan has no tiers yet (nothing to reuse)");
   PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-              p->ws, p->L, p->d, p->cfg.mode == TATTN_MODE_PRICE ? 1 : 0};
+              p->ws, p->L, p->d, p->cfg.mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(p->cfg) ? 1 : 0};
   hipError_t e = launch_pool(pa, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
   p->k = k;
@@ -287,8 +304,11 @@ tattn_status tattn_plan_set_tiers(tattn_plan_t p, const uint8_t* host_tiers, voi
   if (p->cfg.mode != TATTN_MODE_EXTERNAL) return fail(TATTN_E_STATE, "set_tiers needs a plan built in EXTERNAL mode");
   if (!host_tiers) return fail(TATTN_E_INVALID, "tiers is NULL");
   const size_t n = (size_t)p->d.BH * p->d.Nq * p->d.Nk;
+  const unsigned top = skim_on(p->cfg) ? TATTN_SKIM : TATTN_FULL;
   for (size_t i = 0; i < n; i++)
-    if (host_tiers[i] > 2) return fail(TATTN_E_INVALID, "tier byte %u at index %zu is not 0, 1 or 2", host_tiers[i], i);
+    if (host_tiers[i] > top)
+      return fail(TATTN_E_INVALID, "tier byte %u at index %zu is not a tier%s", host_tiers[i], i,
+                  host_tiers[i] == TATTN_SKIM ? " (SKIM needs tau_skim > 0)" : "");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(p->ws + p->L.tiers, host_tiers, n, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "host-to-device copy");
@@ -374,6 +394,33 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
   return ok();
 }
 
+tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_k4s, uint16_t* host_vskim,
+                                void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!skim_on(p->cfg)) return fail(TATTN_E_STATE, "MXFP4 copies exist only with the SKIM tier (tau_skim > 0)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Dims& d = p->d;
+  const int hb = d.D / 2, nsc = d.D / 32;
+  tattn_status st;
+  std::vector<uint8_t> slab(p->L.sl.bytes);
+  for (size_t bh = 0; bh < (size_t)d.BH; bh++) {
+    if ((st = copy_out(slab.data(), p->ws + p->L.slab + bh * p->L.sl.bytes, slab.size(), s)) != TATTN_OK) return st;
+    if ((st = sync(s)) != TATTN_OK) return st;
+    const uint8_t* k4 = slab.data() + p->L.sl.k4;
+    const uint8_t* k4s = slab.data() + p->L.sl.k4s;
+    const uint16_t* vs = reinterpret_cast<const uint16_t*>(slab.data() + p->L.sl.vskim);
+    for (int J = 0; J < d.Nk; J++)
+      for (int r = 0; r < 64 && J * 64 + r < d.N; r++) {
+        const size_t n = (size_t)J * 64 + r, at = bh * d.N + n;
+        if (host_k4) std::memcpy(host_k4 + at * hb, k4 + n * hb, hb);
+        if (host_k4s) std::memcpy(host_k4s + at * nsc, k4s + n * nsc, nsc);
+        if (host_vskim)
+          for (int c = 0; c < d.D; c++) host_vskim[at * d.D + c] = vs[(size_t)J * 64 * d.D + c * 64 + vt_pos(r)];
+      }
+  }
+  return ok();
+}
+
 tattn_status tattn_plan_get_moments(tattn_plan_t p, float* q2, float* m2q, float* kvar, float* m2k, float* vvar,
                                     float* m2v, float* vnorm, void* stream) {
   if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
@@ -419,6 +466,10 @@ tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {
         } else if (tr[J] == TATTN_LOW) {   // fp8 scores, 16-bit P.V
           st.n_low++;
           st.flops_fp8 += 2.0 * mI * nJ * D;
+          st.flops_bf16 += 2.0 * mI * nJ * D;
+        } else if (tr[J] == TATTN_SKIM) {  // fp4 scores, 16-bit P.V
+          st.n_skim++;
+          st.flops_fp4 += 2.0 * mI * nJ * D;
           st.flops_bf16 += 2.0 * mI * nJ * D;
         } else {
           st.n_skip++;

@@ -32,6 +32,10 @@ struct Slab {
   size_t kblo;    // bf16 [Nk][D]       K block means, lo part (kbar = hi + lo to ~2^-17)
   size_t vbarT;   // fp16 [NkC][D][64]  V block means transposed per chunk of 64 blocks,
                   //                    vt_pos order, zero past Nk
+  // SKIM tier only (zero-sized otherwise; 64-key blocks)
+  size_t k4;      // u8   [Nk][64][D/2]  MXFP4 K codes, channel 2m in the low nibble of byte m
+  size_t k4s;     // u8   [Nk][64][D/32] E8M0 scale of each 32 channels of a K row
+  size_t vskim;   // fp16 [Nk][D][64]   SKIM value operand fl16(decode(MXFP4 V)), vt_pos order
   size_t bytes;   // slab size (256-byte multiple)
 };
 
@@ -47,6 +51,7 @@ struct Layout {
   size_t tiers;                 // u8  [BH][Nq][Nk]
   size_t lists;                 // i16 [BH][Nq][Nk]
   size_t counts;                // i32 [BH][Nq][4]   n_full, n_low, n_skip, fused-kernel steps
+                                //                   (n_skim = Nk - n_full - n_low - n_skip)
   size_t order;                 // i32 [BH * Nq]     the fused kernel's row order
   size_t ent;                   // f64 [BH][Ssamp]   entropy of the sampled rows
   size_t kh;                    // i32 [BH]
@@ -61,7 +66,7 @@ struct Layout {
 };
 
 Dims make_dims(const tattn_config& c);
-Layout make_layout(const Dims& d, int entropy_samples, bool moments);
+Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim);
 
 // ---- launchers (all asynchronous on `s`; return the launch status)
 struct PoolArgs {
@@ -72,6 +77,7 @@ struct PoolArgs {
   Layout L;
   Dims d;
   int moments;   // also write the second-moment statistics (price router)
+  int mx4;       // also write the MXFP4 copies of K and V (SKIM tier)
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 
@@ -85,6 +91,7 @@ struct RouterArgs {
   float keep_min, keep_max, full_frac;
   int samples;
   float price;
+  float tau_skim;   // > 0: THRESHOLD tiles with tau_skim <= p < tau_lo are SKIM
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 // Rebuild lists and counts from the tier map already in the workspace
@@ -99,6 +106,7 @@ struct AttnArgs {
   unsigned char* ws;
   Layout L;
   Dims d;
+  int skim;   // the plan may hold SKIM tiles (64-key blocks)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
