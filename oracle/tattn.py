@@ -533,7 +533,8 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     q8, sq, iq = quantise_blocks(q, bq)
     k8, sk, ik = quantise_blocks(k, bk)
     v8, sv, iv = quantise_blocks(v, bk)
-    mx4 = skim_operands(q, k, v) if d % mxfp4.BLOCK == 0 else None
+    # the MXFP4 copies, where a SKIM tile needs them
+    mx4 = skim_operands(q, k, v) if np.any(t == SKIM) else None
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
                 q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info, mx4=mx4)
 
