@@ -2,7 +2,8 @@
 MXFP4 copies of K and V bit for bit against the oracle's codec, the four-tier
 threshold map and its lists against the oracle outside the threshold bands,
 the fused kernel's output under the GPU's tiers and under random external
-four-tier maps, and the full-size Wan-like shape on sampled query blocks."""
+four-tier maps, the full-size Wan-like shape and the largest key-block count
+on sampled query blocks, all-zero blocks, top-k, and plan reuse."""
 import numpy as np
 import pytest
 
@@ -10,7 +11,7 @@ from oracle import mxfp4
 from oracle import tattn as T
 from synth import CONFIGS
 
-from gpu_cases import OracleCfg, as_f32, band_mask, device_inputs
+from gpu_cases import OracleCfg, band_mask, device_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +140,100 @@ def test_full_size_wan_shape_sampled():
         oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
         ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k, rows=rows)
         _check_out(out[0, h], ref, f"full size h{h}", rows=rows, bq=cfg.block_q)
+
+
+def test_zero_blocks_in_skim_tiles():
+    """All-zero K, V and Q blocks and zeros inside the ragged last block, every
+    non-diagonal tile SKIM: scale byte 0 (2^-127) for the zero rows and an
+    exact zero contribution from their codes."""
+    import tile_sparse_mixed_amd as tsm
+    from synth.gen import bf16_bits_to_f32
+    cfg = CASES["d128_ragged"]
+    g, _ = device_inputs(cfg)
+    import torch
+    bits = {n: g["bits"][n].copy() for n in ("q", "k", "v")}
+    bits["k"][:, :, 3 * 64:4 * 64] = 0
+    bits["v"][:, :, 5 * 64:6 * 64] = 0
+    bits["q"][:, :, 128:256] = 0
+    bits["v"][:, :, -7:] = 0
+    for n in ("q", "k", "v"):
+        g[n] = bf16_bits_to_f32(bits[n])
+    dev = {n: torch.from_numpy(bits[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    p = _plan(tsm, dev, cfg, mode="external")
+    t = np.full((1, cfg.heads, cfg.n_qblocks, cfg.n_kblocks), T.SKIM, np.uint8)
+    p.set_tiers(t)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    m = p.mx4()
+    assert np.all(m["k4s"][0, :, 3 * 64:4 * 64] == 0) and np.all(m["k4"][0, :, 3 * 64:4 * 64] == 0)
+    oc = OracleCfg(cfg, mode=3)
+    for h in range(cfg.heads):
+        q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
+        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=t[0, h])
+        _check_out(out[0, h], T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k), f"zero blocks h{h}")
+
+
+def test_replan_keeps_skim_tiles_and_refreshes_mx4():
+    from synth import drift_step
+    import tile_sparse_mixed_amd as tsm
+    import torch
+    cfg = CASES["d128_ragged"]
+    g0, dev0 = device_inputs(cfg)
+    g1 = drift_step(g0, cfg, 1, 0.1)
+    dev1 = {n: torch.from_numpy(g1["bits"][n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    p = _plan(tsm, dev0, cfg)
+    t0 = p.tiers()
+    assert np.any(t0 == T.SKIM)
+    tsm.replan(p, dev1["q"], dev1["k"], dev1["v"])
+    out = tsm.forward(p, dev1["q"], dev1["k"], dev1["v"]).cpu().numpy()
+    assert np.array_equal(p.tiers(), t0)
+    m = p.mx4()
+    oc = OracleCfg(cfg)
+    for h in range(cfg.heads):
+        q1, k1, v1 = g1["q"][0, h], g1["k"][0, h], g1["v"][0, h]
+        kc, ks, _ = mxfp4.quantise(k1)
+        assert np.array_equal(m["k4"][0, h], mxfp4.pack_nibbles(kc)) and np.array_equal(m["k4s"][0, h], ks)
+        r = T.oracle_replan(q1, k1, v1, {"tiers": t0[0, h]}, oc)
+        _check_out(out[0, h], T.oracle_forward(q1, k1, v1, r, cfg.block_q, cfg.block_k), f"replan h{h}")
+
+
+def test_top_k_with_four_tiers():
+    import tile_sparse_mixed_amd as tsm
+    cfg = CASES["small"].with_(top_k=12)
+    g, dev = device_inputs(cfg)
+    p = _plan(tsm, dev, cfg)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    tiers = p.tiers()
+    oc = OracleCfg(cfg)
+    for h in range(cfg.heads):
+        q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
+        o = T.oracle_plan(q, k, v, oc)
+        band = band_mask(o["p"], oc.tau_hi, oc.tau_lo, tau_skim=oc.tau_skim)
+        srt = -np.sort(-o["p"], axis=1)
+        band |= (np.abs(srt[:, 11] - srt[:, 12]) <= 1e-12 * srt[:, 11])[:, None]
+        assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), h
+        diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
+        assert np.all(((tiers[0, h] != T.SKIP) & ~diag).sum(axis=1) <= 12)
+        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
+        _check_out(out[0, h], T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k), f"top-k h{h}")
+
+
+def test_largest_key_block_count_with_skim():
+    """4096 key blocks (N = 262144, d = 64, 128x64 tiles) with the SKIM tier:
+    tiers and lists outside the bands, output on three sampled query blocks."""
+    import tile_sparse_mixed_amd as tsm
+    cfg = CONFIGS["small"].with_(heads=1, grid=(64, 64, 64), tau_skim=1e-4)
+    assert cfg.n_kblocks == 4096
+    g, dev = device_inputs(cfg)
+    p = _plan(tsm, dev, cfg)
+    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
+    tiers = p.tiers()
+    _log(f"[skim max Nk] FULL/LOW/SKIM/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 3, 0)]}")
+    oc = OracleCfg(cfg)
+    q, k, v = g["q"][0, 0], g["k"][0, 0], g["v"][0, 0]
+    o = T.oracle_plan(q, k, v, oc)
+    band = band_mask(o["p"], oc.tau_hi, oc.tau_lo, tau_skim=oc.tau_skim)
+    assert np.array_equal(tiers[0, 0][~band], o["tiers"][~band])
+    rows = [0, cfg.n_qblocks // 3, cfg.n_qblocks - 1]
+    oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, 0])
+    ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k, rows=rows)
+    _check_out(out[0, 0], ref, "max Nk", rows=rows, bq=cfg.block_q)
