@@ -67,6 +67,25 @@ __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // stage).
 __device__ inline void wait_vm0_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
+// lgkmcnt(0) alone: this wave's LDS reads (and scalar loads) have returned.
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// vmcnt(n): at most this wave's n newest vector-memory instructions still in
+// flight (they complete in issue order).  n is wave-uniform; past 8 it waits
+// for all, which is only slower.
+__device__ inline void wait_vm_n(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
 // One wave: copy 64 lanes x 16 bytes into LDS[dst .. dst+1024); lane l's bytes
 // come from byte offset voff (per lane) + soff (uniform) of buffer `r`.  A
 // read past the buffer's num_records returns zeros.
@@ -133,9 +152,22 @@ void k3_attn(AttnArgs a) {
   constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
   constexpr int R1 = 128 * D;
-  __shared__ __attribute__((aligned(1024))) unsigned char stA[STAGE];   // stage of even steps
-  __shared__ __attribute__((aligned(1024))) unsigned char stB[STAGE];   // stage of odd steps
-  __shared__ int16_t slist[kMaxNk];          // the row's FULL, LOW (and SKIM) key blocks
+  // Two-wave workgroups (64-row query blocks) keep ONE stage and refill its
+  // halves in turn: the K half of step t+1 while step t runs its softmax and
+  // P.V, the V half while step t+1 scores.  That halves their LDS, so a CU
+  // holds four of them (two waves per SIMD) instead of two (one per SIMD).
+  // The halves are then two arrays (stA = R0, stB = R1), so that the
+  // compiler's wait insertion sees a DMA into one half never alias reads of
+  // the other.
+  constexpr bool SPLIT = NW == 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char stA[SPLIT ? R1 : STAGE];   // stage of even steps
+  __shared__ __attribute__((aligned(1024))) unsigned char stB[SPLIT ? R1 : STAGE];   // stage of odd steps
+  // the R1 region of a stage
+  auto r1 = [&](const unsigned char* st) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (SPLIT) return stB;
+    else return const_cast<unsigned char*>(st) + R1;
+  };
+  extern __shared__ int16_t slist[];         // the row's FULL, LOW (and SKIM) key blocks: Nk entries
   __shared__ uint64_t smask[64];             // per visited chunk: bit j = block 64c + j skipped
   __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
   __shared__ int snc;
@@ -305,8 +337,12 @@ void k3_attn(AttnArgs a) {
   };
   // KINDS: bit mask of the step kinds that can occur where this is called; the
   // other branches are not generated, so their address terms are not kept live.
-  auto issue = [&](auto kinds, int t, unsigned char* st, StepScale<G>& cst) __attribute__((always_inline)) {
+  // PART: 1 = the R0 half (K, E4M3 K, MXFP4 K and its scales, kbar hi) and
+  // the step's score scale; 2 = the R1 half (V^T, low-tier or SKIM V^T, kbar
+  // lo, vbar^T); 3 = both.  Per wave, every R1 half is NI16 instructions.
+  auto issue_part = [&](auto kinds, auto part, int t, unsigned char* st, StepScale<G>& cst) __attribute__((always_inline)) {
     constexpr int KINDS = decltype(kinds)::value;
+    constexpr bool PA = decltype(part)::value & 1, PB = decltype(part)::value & 2;
     const int kind = step_kind(t);
     if constexpr (G > 1) {
       if (((KINDS & (1 << kFull)) && kind == kFull) || ((KINDS & (1 << kLow)) && kind == kLow)) {
@@ -319,50 +355,58 @@ void k3_attn(AttnArgs a) {
           jv = (int)slist[i0 + g < e ? i0 + g : i0];
         }
         if (kind == kFull) {
+          if constexpr (PA) {
 #pragma unroll
-          for (int i = 0; i < NI16; i++) {
-            const int k = wave + NW * i;
-            const int row0 = k * RPI;                // first stage row of the instruction
-            if constexpr (G == 4) {
-              const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
-              dma16(rKh, st + k * 1024, lk[i % NSW] + (Jg * 16 + (row0 & 15)) * (int)dm.sn * 2, 0);
-            } else if constexpr (D == 128) {
-              // score row m = row0 + rr16 takes key kk8(m) of slot slot8(m); an
-              // instruction's four rows share one slot
-              const int Js = __builtin_amdgcn_readlane(jv, slot8(row0));
-              dma16(rKh, st + k * 1024, lk[i % NSW] + (Js * 8 + kk8(row0)) * (int)dm.sn * 2, 0);
-            } else {
-              const int m = row0 + rr16;
-              dma16(rKh, st + k * 1024,
-                    lk[i % NSW] + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - rr16) * (int)dm.sn * 2, 0);
+            for (int i = 0; i < NI16; i++) {
+              const int k = wave + NW * i;
+              const int row0 = k * RPI;                // first stage row of the instruction
+              if constexpr (G == 4) {
+                const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
+                dma16(rKh, st + k * 1024, lk[i % NSW] + (Jg * 16 + (row0 & 15)) * (int)dm.sn * 2, 0);
+              } else if constexpr (D == 128) {
+                // score row m = row0 + rr16 takes key kk8(m) of slot slot8(m); an
+                // instruction's four rows share one slot
+                const int Js = __builtin_amdgcn_readlane(jv, slot8(row0));
+                dma16(rKh, st + k * 1024, lk[i % NSW] + (Js * 8 + kk8(row0)) * (int)dm.sn * 2, 0);
+              } else {
+                const int m = row0 + rr16;
+                dma16(rKh, st + k * 1024,
+                      lk[i % NSW] + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - rr16) * (int)dm.sn * 2, 0);
+              }
             }
           }
-          load_vt16g(st + R1, (int)SL.vt, jv);
+          if constexpr (PB) load_vt16g(r1(st), (int)SL.vt, jv);
+          if constexpr (PA) {
 #pragma unroll
-          for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = cF;
+            for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = cF;
+          }
         } else {
+          if constexpr (PA) {
 #pragma unroll
-          for (int i = 0; i < NI8; i++) {
-            const int k = wave + NW * i;
-            const int row0 = k * (1024 / D);         // E4M3 rows are D bytes
-            if constexpr (G == 4) {
-              const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
-              dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + (Jg * 16 + (row0 & 15)) * D);
-            } else {
-              const int ri = D == 128 ? lane >> 3 : lane >> 2;   // row of the lane inside the instruction
-              const int m = row0 + ri;
-              dma16(rS, st + k * 1024, voffK8 + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - ri) * D, (int)SL.k8);
+            for (int i = 0; i < NI8; i++) {
+              const int k = wave + NW * i;
+              const int row0 = k * (1024 / D);         // E4M3 rows are D bytes
+              if constexpr (G == 4) {
+                const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
+                dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + (Jg * 16 + (row0 & 15)) * D);
+              } else {
+                const int ri = D == 128 ? lane >> 3 : lane >> 2;   // row of the lane inside the instruction
+                const int m = row0 + ri;
+                dma16(rS, st + k * 1024, voffK8 + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - ri) * D, (int)SL.k8);
+              }
             }
           }
-          load_vt16g(st + R1, (int)SL.vlow, jv);
+          if constexpr (PB) load_vt16g(r1(st), (int)SL.vlow, jv);
+          if constexpr (PA) {
 #pragma unroll
-          for (int g = 0; g < StepScale<G>::N; g++) {
-            if constexpr (G == 8) {
-              const float s0 = skp[__builtin_amdgcn_readlane(jv, 2 * g)];
-              const float s1 = skp[__builtin_amdgcn_readlane(jv, 2 * g + 1)];
-              cst.c[g] = sq * (lh ? s1 : s0) * cF;
-            } else {
-              cst.c[g] = sq * skp[__builtin_amdgcn_readlane(jv, g)] * cF;
+            for (int g = 0; g < StepScale<G>::N; g++) {
+              if constexpr (G == 8) {
+                const float s0 = skp[__builtin_amdgcn_readlane(jv, 2 * g)];
+                const float s1 = skp[__builtin_amdgcn_readlane(jv, 2 * g + 1)];
+                cst.c[g] = sq * (lh ? s1 : s0) * cF;
+              } else {
+                cst.c[g] = sq * skp[__builtin_amdgcn_readlane(jv, g)] * cF;
+              }
             }
           }
         }
@@ -371,56 +415,67 @@ void k3_attn(AttnArgs a) {
     }
     if (G == 1 && (KINDS & (1 << kFull)) && kind == kFull) {
       const int J = list_at(t);
-      // one resource per tile: rows past N read as zeros (and are masked)
-      const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
-      const __amdgpu_buffer_rsrc_t rK = make_rsrc(kin + (int64_t)J * 64 * dm.sn, rows * (uint32_t)dm.sn * 2);
+      if constexpr (PA) {
+        // one resource per tile: rows past N read as zeros (and are masked)
+        const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
+        const __amdgpu_buffer_rsrc_t rK = make_rsrc(kin + (int64_t)J * 64 * dm.sn, rows * (uint32_t)dm.sn * 2);
 #pragma unroll
-      for (int i = 0; i < NI16; i++) {
-        const int k = wave + NW * i;
-        // the row offset stays in the lane offset: the range check that zeroes
-        // rows past N covers the lane offset, not the scalar one
-        dma16(rK, st + k * 1024, lk[i % NSW] + k * RPI * (int)dm.sn * 2, 0);
+        for (int i = 0; i < NI16; i++) {
+          const int k = wave + NW * i;
+          // the row offset stays in the lane offset: the range check that zeroes
+          // rows past N covers the lane offset, not the scalar one
+          dma16(rK, st + k * 1024, lk[i % NSW] + k * RPI * (int)dm.sn * 2, 0);
+        }
       }
-      load_vt16(st + R1, rS, (int)SL.vt + J * 128 * D);
-      cst.c[0] = cF;
+      if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vt + J * 128 * D);
+      if constexpr (PA) cst.c[0] = cF;
     } else if (G == 1 && (KINDS & (1 << kLow)) && kind == kLow) {
       const int J = list_at(t);
+      if constexpr (PA) {
 #pragma unroll
-      for (int i = 0; i < NI8; i++) {
-        const int k = wave + NW * i;
-        dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+        for (int i = 0; i < NI8; i++) {
+          const int k = wave + NW * i;
+          dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+        }
       }
-      load_vt16(st + R1, rS, (int)SL.vlow + J * 128 * D);
-      cst.c[0] = sq * skp[J] * cF;
+      if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vlow + J * 128 * D);
+      if constexpr (PA) cst.c[0] = sq * skp[J] * cF;
     } else if (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
       // MXFP4 K [64][D/2] into R0, its scale bytes [64][D/32] after it (one
       // D/32-byte load per lane from wave 0, into a 4-byte LDS slot per
       // lane), fp16 dequantised V^T into R1
       const int J = list_at(t);
-      for (int k = wave; k < D / 32; k += NW) dma16(rS, st + k * 1024, voffK4, (int)SL.k4 + J * 32 * D + k * 1024);
-      if (wave == 0) {
-        if constexpr (D == 128)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 4, lane * 4, (int)SL.k4s + J * 2 * D, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 2, lane * 2, (int)SL.k4s + J * 2 * D, 0, 0);
+      if constexpr (PA) {
+        for (int k = wave; k < D / 32; k += NW) dma16(rS, st + k * 1024, voffK4, (int)SL.k4 + J * 32 * D + k * 1024);
+        if (wave == 0) {
+          if constexpr (D == 128)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 4, lane * 4, (int)SL.k4s + J * 2 * D, 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 2, lane * 2, (int)SL.k4s + J * 2 * D, 0, 0);
+        }
       }
-      load_vt16(st + R1, rS, (int)SL.vskim + J * 128 * D);
-      cst.c[0] = cF;
+      if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vskim + J * 128 * D);
+      if constexpr (PA) cst.c[0] = cF;
     } else {
       const int c = schunk[(t - sF) >> 1];
       if ((KINDS & (1 << kSkipS)) && kind == kSkipS) {
 #pragma unroll
         for (int i = 0; i < NI16; i++) {
           const int k = wave + NW * i;
-          dma16(rS, st + k * 1024, lkb[i % NSW], (int)SL.kbhi + c * 128 * D + k * 1024);
-          dma16(rS, st + R1 + k * 1024, lkb[i % NSW], (int)SL.kblo + c * 128 * D + k * 1024);
+          if constexpr (PA) dma16(rS, st + k * 1024, lkb[i % NSW], (int)SL.kbhi + c * 128 * D + k * 1024);
+          if constexpr (PB) dma16(rS, r1(st) + k * 1024, lkb[i % NSW], (int)SL.kblo + c * 128 * D + k * 1024);
         }
       } else if (KINDS & (1 << kSkipPV)) {
-        load_vt16(st + R1, rS, (int)SL.vbarT + c * 128 * D);
+        if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vbarT + c * 128 * D);
       }
+      if constexpr (PA) {
 #pragma unroll
-      for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = 1.0f;
+        for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = 1.0f;
+      }
     }
+  };
+  auto issue = [&](auto kinds, int t, unsigned char* st, StepScale<G>& cst) __attribute__((always_inline)) {
+    issue_part(kinds, std::integral_constant<int, 3>{}, t, st, cst);
   };
 
   // ---- per-lane LDS operand offsets, relative to a stage.  Rows 32b + ln have
@@ -434,7 +489,7 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < D / 16; c++) offk[c] = offK<D>(ln, 2 * c + lh);
 #pragma unroll
-  for (int c = 0; c < 4; c++) offv[c] = R1 + offV(ln, 2 * c + lh);
+  for (int c = 0; c < 4; c++) offv[c] = offV(ln, 2 * c + lh);   // within R1
 #pragma unroll
   for (int i = 0; i < D / 64; i++) {
     const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
@@ -585,7 +640,7 @@ void k3_attn(AttnArgs a) {
     for (int cc = 0; cc < 4; cc++)
 #pragma unroll
       for (int db = 0; db < D / 32; db++)
-        va[cc * (D / 32) + db] = *reinterpret_cast<const f16x8*>(st + offv[cc] + db * 32 * 128);
+        va[cc * (D / 32) + db] = *reinterpret_cast<const f16x8*>(r1(st) + offv[cc] + db * 32 * 128);
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
 #pragma unroll
@@ -593,12 +648,10 @@ void k3_attn(AttnArgs a) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cc * (D / 32) + db], pb[cc], acc[db], 0, 0, 0);
     pipeline_reads_mfma<D / 8, D / 16>();
   };
-  // a kept tile (FULL: bf16 scores, LOW: E4M3 scores) staged in `st`
-  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q8) __attribute__((always_inline)) {
+  // a kept tile (FULL: bf16 scores, LOW: E4M3 scores): masks and softmax of
+  // its scores s
+  auto kept_soft = [&](auto low_tag, int t, f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) {
     constexpr bool LOW = decltype(low_tag)::value;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    if constexpr (LOW) scores_fp8(st, s, q8);
-    else scores_bf16(st, s);
     if constexpr (G == 1) {
       const int J = list_at(t);
       if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
@@ -643,22 +696,34 @@ void k3_attn(AttnArgs a) {
       }
       softmax(s, c, tmax);
     }
+  };
+  // a kept tile staged in `st`: scores, softmax, P.V
+  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q8) __attribute__((always_inline)) {
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    if constexpr (decltype(low_tag)::value) scores_fp8(st, s, q8);
+    else scores_bf16(st, s);
+    kept_soft(low_tag, t, s, c);
     pv(st);
   };
-  // a SKIM tile (64-key blocks) staged in `st`
-  auto skim_step = [&](int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    scores_fp4(st, s, q4, q4s);
+  // a SKIM tile (64-key blocks): mask and softmax of its scores s
+  auto skim_soft = [&](int t, f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) {
     const int J = list_at(t);
     if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
     softmax(s, c, row_max(s) * c.c[0]);
+  };
+  auto skim_step = [&](int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    scores_fp4(st, s, q4, q4s);
+    skim_soft(t, s, c);
     pv(st);
   };
-  // pooled keys of a chunk of 64 skipped-candidate blocks: scores only
-  auto skip_scores = [&](int t, const unsigned char* st) __attribute__((always_inline)) {
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // pooled keys of a chunk of 64 skipped-candidate blocks: scores only (hi
+  // part from R0, lo part from R1), then the bias and the softmax
+  auto skip_S = [&](const unsigned char* st, f32x16* s) __attribute__((always_inline)) {
     scores_bf16(st, s);
-    scores_bf16(st + R1, s);   // low half of kbar
+    scores_bf16(r1(st), s);   // low half of kbar
+  };
+  auto skip_soft = [&](int t, f32x16* s) __attribute__((always_inline)) {
     // bias log2(n_J) for the row's skipped blocks, -inf for the others.  Key
     // 32b + 8(r/4) + 4lh + r%4 of the chunk is bit 32b + 8(r/4) + r%4 of the
     // chunk's mask shifted right by 4lh.
@@ -685,6 +750,11 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
     for (int g = 0; g < StepScale<G>::N; g++) one.c[g] = 1.0f;
     softmax(s, one, tmax);
+  };
+  auto skip_scores = [&](int t, const unsigned char* st) __attribute__((always_inline)) {
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    skip_S(st, s);
+    skip_soft(t, s);
   };
 
   // ---- the step loop, in phases (FULL, skip chunks as score / P.V pairs, then
@@ -718,44 +788,9 @@ void k3_attn(AttnArgs a) {
   using KAfterSkip = std::integral_constant<int, (1 << kSkipS) | (1 << kLow) | kSk>;
   using KLow = std::integral_constant<int, (1 << kLow) | kSk>;
   using KSkimOnly = std::integral_constant<int, kSk>;
-  if (nSteps > 0) issue(KAll{}, 0, stA, cA);
-  wait_vm0();
-  __syncthreads();
-  int t = 0;
-  // a phase of single steps [t, end): two copies of the body, one per parity
-  auto run_phase = [&](int end, auto body) __attribute__((always_inline)) {
-    while (t < end) {
-      if ((t & 1) == 0) {
-        body(P0{}, t);
-        if (++t == end) break;
-      }
-      body(P1{}, t);
-      ++t;
-    }
-  };
-  run_phase(sF, [&](auto p, int tt) __attribute__((always_inline)) {
-    if (tt + 1 < nSteps) issue(KAfterFull{}, tt + 1, stg(flip(p)), scl(flip(p)));
-    kept_step(std::false_type{}, tt, stg(p), scl(p), nullptr);
-    next();
-  });
-  // skip pairs keep the parity of their first step
-  auto skip_pairs = [&](auto p) __attribute__((always_inline)) {
-    for (; t < tLow; t += 2) {
-      issue(KSkipPV{}, t + 1, stg(flip(p)), scl(flip(p)));
-      skip_scores(t, stg(p));
-      next();
-      if (t + 2 < nSteps) issue(KAfterSkip{}, t + 2, stg(p), scl(p));
-      pv(stg(flip(p)));
-      next();
-    }
-  };
-  if (t < tLow) {
-    if (t & 1) skip_pairs(P1{});
-    else skip_pairs(P0{});
-  }
-  if (t < tSk) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
-                   // fp8 instruction i = bf16 chunks 4i..4i+3)
-    i32x8 q8reg[D / 64];
+  // the E4M3 copy of this lane's Q (32 bytes per fp8 instruction i = bf16
+  // chunks 4i..4i+3), from the bf16 registers
+  auto make_q8 = [&](i32x8* q8reg) __attribute__((always_inline)) {
     const float iq = reinterpret_cast<const float*>(ws + a.L.iq)[row];
 #pragma unroll
     for (int i = 0; i < D / 64; i++) {
@@ -772,46 +807,187 @@ void k3_attn(AttnArgs a) {
         q8reg[i][2 * cc + 1] = hi;
       }
     }
-    run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
-      if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
-      kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
+  };
+  // the MXFP4 copy of this lane's Q row (channels 64i + 32lh .. +31 for
+  // instruction i, one E8M0 scale each), from Q in memory
+  auto make_q4 = [&](i32x8* q4reg, int* q4s) __attribute__((always_inline)) {
+    const uint16_t* qp = a.q + toff + (int64_t)qrow * dm.sn + 32 * lh;
+#pragma unroll
+    for (int i = 0; i < D / 64; i++) {
+      float x[32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (qrow < dm.N) raw = *reinterpret_cast<const uint4*>(qp + 64 * i + 8 * j);
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float f = __uint_as_float(e & 1 ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
+          x[8 * j + e] = f;
+          amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
+        }
+      }
+      const int ex = mx4_exponent(amax);
+      uint32_t pk[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
+      q4reg[i] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+      q4s[i] = ex + 127;
+    }
+  };
+
+  if constexpr (!SPLIT) {
+    if (nSteps > 0) issue(KAll{}, 0, stA, cA);
+    wait_vm0();
+    __syncthreads();
+    int t = 0;
+    // a phase of single steps [t, end): two copies of the body, one per parity
+    auto run_phase = [&](int end, auto body) __attribute__((always_inline)) {
+      while (t < end) {
+        if ((t & 1) == 0) {
+          body(P0{}, t);
+          if (++t == end) break;
+        }
+        body(P1{}, t);
+        ++t;
+      }
+    };
+    run_phase(sF, [&](auto p, int tt) __attribute__((always_inline)) {
+      if (tt + 1 < nSteps) issue(KAfterFull{}, tt + 1, stg(flip(p)), scl(flip(p)));
+      kept_step(std::false_type{}, tt, stg(p), scl(p), nullptr);
       next();
     });
-  }
-  if constexpr (SKIM) {
-    if (t < nSteps) {   // SKIM tiles remain: the MXFP4 copy of this lane's Q row,
-                        // channels 64i + 32lh .. +31 for instruction i
-      i32x8 q4reg[D / 64];
-      int q4s[D / 64];
-      const uint16_t* qp = a.q + toff + (int64_t)qrow * dm.sn + 32 * lh;
-#pragma unroll
-      for (int i = 0; i < D / 64; i++) {
-        float x[32];
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          uint4 raw = make_uint4(0, 0, 0, 0);
-          if (qrow < dm.N) raw = *reinterpret_cast<const uint4*>(qp + 64 * i + 8 * j);
-          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const float f = __uint_as_float(e & 1 ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
-            x[8 * j + e] = f;
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
-          }
-        }
-        const int ex = mx4_exponent(amax);
-        uint32_t pk[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
-        q4reg[i] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
-        q4s[i] = ex + 127;
+    // skip pairs keep the parity of their first step
+    auto skip_pairs = [&](auto p) __attribute__((always_inline)) {
+      for (; t < tLow; t += 2) {
+        issue(KSkipPV{}, t + 1, stg(flip(p)), scl(flip(p)));
+        skip_scores(t, stg(p));
+        next();
+        if (t + 2 < nSteps) issue(KAfterSkip{}, t + 2, stg(p), scl(p));
+        pv(stg(flip(p)));
+        next();
       }
-      run_phase(nSteps, [&](auto p, int tt) __attribute__((always_inline)) {
-        if (tt + 1 < nSteps) issue(KSkimOnly{}, tt + 1, stg(flip(p)), scl(flip(p)));
-        skim_step(tt, stg(p), scl(p), q4reg, q4s);
+    };
+    if (t < tLow) {
+      if (t & 1) skip_pairs(P1{});
+      else skip_pairs(P0{});
+    }
+    if (t < tSk) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
+                     // fp8 instruction i = bf16 chunks 4i..4i+3)
+      i32x8 q8reg[D / 64];
+      make_q8(q8reg);
+      run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
+        if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
+        kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
         next();
       });
+    }
+    if constexpr (SKIM) {
+      if (t < nSteps) {   // SKIM tiles remain: the MXFP4 copy of this lane's Q row,
+                          // channels 64i + 32lh .. +31 for instruction i
+        i32x8 q4reg[D / 64];
+        int q4s[D / 64];
+        make_q4(q4reg, q4s);
+        run_phase(nSteps, [&](auto p, int tt) __attribute__((always_inline)) {
+          if (tt + 1 < nSteps) issue(KSkimOnly{}, tt + 1, stg(flip(p)), scl(flip(p)));
+          skim_step(tt, stg(p), scl(p), q4reg, q4s);
+          next();
+        });
+      }
+    }
+
+  } else {
+    // ---- single stage (two-wave workgroups).  Step t's R0 half is staged
+    // when it starts and its R1 half may still be in flight.  After the
+    // score reads the R0 half of step t+1 is issued, after the P.V reads the
+    // R1 half, so before P.V this wave's outstanding DMA is [R1 of t, R0 of
+    // t+1] and the wait leaves R0 of t+1's instructions in flight.
+    using PA = std::integral_constant<int, 1>;
+    using PB = std::integral_constant<int, 2>;
+    auto bar = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // this wave's R0-half instructions for step u (none past the last step)
+    auto a_count = [&](int u) -> int {
+      if (u >= nSteps) return 0;
+      const int k = step_kind(u);
+      if (k == kFull || k == kSkipS) return NI16;
+      if (k == kLow) return NI8;
+      if (k == kSkipPV) return 0;
+      return (D / 32 - wave + NW - 1) / NW + (wave == 0 ? 1 : 0);   // SKIM: K rows and the scale words
+    };
+    if (nSteps > 0) {
+      issue_part(KAll{}, PA{}, 0, stA, cA);
+      issue_part(KAll{}, PB{}, 0, stA, cA);
+    }
+    wait_vm0();
+    __syncthreads();
+    int t = 0;
+    // One step.  S_fn(s): its scores from the stage; soft_fn(s, c): masks and
+    // softmax.  HS: the step scores; HP: it runs P.V; U1: its scores also
+    // read R1 (a skip chunk's lo half).
+    auto split_step = [&](auto nk, auto hs, auto hp, auto u1, auto S_fn, auto soft_fn) __attribute__((always_inline)) {
+      constexpr bool HS = decltype(hs)::value, HP = decltype(hp)::value, U1 = decltype(u1)::value;
+      const bool more = t + 1 < nSteps;
+      const StepScale<G> cur = cA;   // issuing step t+1's R0 half rewrites cA
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      if constexpr (U1) {            // R1 of this step as well
+        wait_vm0();
+        bar();
+      }
+      if constexpr (HS) S_fn(s);
+      wait_lgkm0();                  // every wave's R0 (and R1) reads have returned
+      bar();
+      if (more) issue_part(nk, PA{}, t + 1, stA, cA);
+      if constexpr (HS) soft_fn(s, cur);
+      if constexpr (HP) {
+        wait_vm_n(a_count(t + 1));   // R1 of step t landed in every wave
+        bar();
+        pv(stA);
+      }
+      wait_vm0_lgkm0();              // R0 of step t+1 landed, this wave's R1 reads returned
+      bar();
+      refresh();
+      if (more) issue_part(nk, PB{}, t + 1, stA, cA);
+      ++t;
+    };
+    using T0 = std::false_type;
+    using T1 = std::true_type;
+    auto no_S = [&](f32x16*) {};
+    auto no_soft = [&](f32x16*, const StepScale<G>&) {};
+    while (t < sF)
+      split_step(KAfterFull{}, T1{}, T1{}, T0{},
+                 [&](f32x16* s) __attribute__((always_inline)) { scores_bf16(stA, s); },
+                 [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T0{}, t, s, c); });
+    while (t < tLow) {
+      if (((t - sF) & 1) == 0)
+        split_step(KSkipPV{}, T1{}, T0{}, T1{},
+                   [&](f32x16* s) __attribute__((always_inline)) { skip_S(stA, s); },
+                   [&](f32x16* s, const StepScale<G>&) __attribute__((always_inline)) { skip_soft(t, s); });
+      else
+        split_step(KAfterSkip{}, T0{}, T1{}, T0{}, no_S, no_soft);
+    }
+    if (t < tSk) {
+      i32x8 q8reg[D / 64];
+      make_q8(q8reg);
+      while (t < tSk)
+        split_step(KLow{}, T1{}, T1{}, T0{},
+                   [&](f32x16* s) __attribute__((always_inline)) { scores_fp8(stA, s, q8reg); },
+                   [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T1{}, t, s, c); });
+    }
+    if constexpr (SKIM) {
+      if (t < nSteps) {
+        i32x8 q4reg[D / 64];
+        int q4s[D / 64];
+        make_q4(q4reg, q4s);
+        while (t < nSteps)
+          split_step(KSkimOnly{}, T1{}, T1{}, T0{},
+                     [&](f32x16* s) __attribute__((always_inline)) { scores_fp4(stA, s, q4reg, q4s); },
+                     [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { skim_soft(t, s, c); });
+      }
     }
   }
 
@@ -847,14 +1023,17 @@ void k3_attn(AttnArgs a) {
 template <int D, int NW>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   if (a.skim && a.d.Bk != 64) return hipErrorInvalidValue;
+  if (a.d.Nk > kMaxNk) return hipErrorInvalidValue;
+  const size_t lds = ((size_t)a.d.Nk * 2 + 15) / 16 * 16;   // the row's list (dynamic LDS)
+  const dim3 grid(a.d.BH * a.d.Nq), block(NW * 64);
   if (a.skim)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64, true>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, true>), grid, block, lds, s, a);
   else if (a.d.Bk == 64)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64, false>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, false>), grid, block, lds, s, a);
   else if (a.d.Bk == 16)
-    hipLaunchKernelGGL((k3_attn<D, NW, 16, false>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 16, false>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((k3_attn<D, NW, 8, false>), dim3(a.d.BH * a.d.Nq), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 8, false>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
