@@ -167,7 +167,7 @@ void k3_attn(AttnArgs a) {
     if constexpr (SPLIT) return stB;
     else return const_cast<unsigned char*>(st) + R1;
   };
-  extern __shared__ int16_t slist[];         // the row's FULL, LOW (and SKIM) key blocks: Nk entries
+  extern __shared__ int16_t slist[];         // the row's FULL, LOW (and SKIM) key blocks (list_cap entries)
   __shared__ uint64_t smask[64];             // per visited chunk: bit j = block 64c + j skipped
   __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
   __shared__ int snc;
@@ -193,9 +193,12 @@ void k3_attn(AttnArgs a) {
 
   const unsigned char* ws = a.ws;
   const int* counts = reinterpret_cast<const int*>(ws + a.L.counts) + row * 4;
-  const int nF = counts[0], nL = counts[1];
+  // the list in LDS holds a.list_cap entries, the plan's bound on a row's kept
+  // tiles; a row past it (not possible for a valid plan) is cut, never read past
+  const int cap = a.list_cap;
+  const int nF = min(counts[0], cap), nL = min(counts[1], cap - nF);
   const int nK = nF + nL;
-  const int nSk = SKIM ? dm.Nk - nK - counts[2] : 0;   // SKIM tiles follow LOW in the list
+  const int nSk = SKIM ? min(dm.Nk - counts[0] - counts[1] - counts[2], cap - nK) : 0;   // SKIM follows LOW
   {
     const int16_t* list = reinterpret_cast<const int16_t*>(ws + a.L.lists) + row * dm.Nk;
     for (int i = tid; i < nK + nSk; i += NW * 64) slist[i] = list[i];
@@ -1023,8 +1026,8 @@ void k3_attn(AttnArgs a) {
 template <int D, int NW>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   if (a.skim && a.d.Bk != 64) return hipErrorInvalidValue;
-  if (a.d.Nk > kMaxNk) return hipErrorInvalidValue;
-  const size_t lds = ((size_t)a.d.Nk * 2 + 15) / 16 * 16;   // the row's list (dynamic LDS)
+  if (a.d.Nk > kMaxNk || a.list_cap < 1 || a.list_cap > a.d.Nk) return hipErrorInvalidValue;
+  const size_t lds = ((size_t)a.list_cap * 2 + 15) / 16 * 16;   // the row's list (dynamic LDS)
   const dim3 grid(a.d.BH * a.d.Nq), block(NW * 64);
   if (a.skim)
     hipLaunchKernelGGL((k3_attn<D, NW, 64, true>), grid, block, lds, s, a);

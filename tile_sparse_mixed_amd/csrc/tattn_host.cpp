@@ -125,6 +125,21 @@ static Layout layout_of(const tattn_config& c) {
   return make_layout(make_dims(c), c.entropy_samples, c.mode == TATTN_MODE_PRICE, skim_on(c));
 }
 
+// Most tiles a row can keep (FULL, LOW or SKIM) under the config's rule:
+// ADAPTIVE keeps the top k_h <= ceil(keep_max * Nk) (the same float64 product
+// the router rounds up) plus the diagonal blocks, THRESHOLD with top-k keeps
+// top_k plus the diagonal; otherwise every tile may be kept.  The fused kernel
+// sizes the row's list in LDS by it.
+static int list_cap(const tattn_config& c, const Dims& d) {
+  const int64_t ndiag = d.Bq / d.Bk + 1;
+  int64_t cap = d.Nk;
+  if (c.mode == TATTN_MODE_ADAPTIVE)
+    cap = std::min<int64_t>(cap, (int64_t)std::ceil((double)c.keep_max * (double)d.Nk) + ndiag);
+  else if (c.mode == TATTN_MODE_THRESHOLD && c.top_k > 0)
+    cap = std::min<int64_t>(cap, (int64_t)c.top_k + ndiag);
+  return (int)cap;
+}
+
 static tattn_status validate(const tattn_config* c) {
   if (!c) return fail(TATTN_E_INVALID, "config is NULL");
   if (c->batch < 1 || c->heads < 1 || c->seq_len < 1)
@@ -268,7 +283,8 @@ tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const v
   if (k != p->k || v != p->v) return fail(TATTN_E_STATE, "k and v differ from the tensors the plan was built with");
   if (!p->has_tiers) return fail(TATTN_E_STATE, "external-mode plan has no tiers yet (call tattn_plan_set_tiers)");
   AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), o,
-             p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d, skim_on(p->cfg) ? 1 : 0};
+             p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d, skim_on(p->cfg) ? 1 : 0,
+             list_cap(p->cfg, p->d)};
   hipError_t e = launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return ok();

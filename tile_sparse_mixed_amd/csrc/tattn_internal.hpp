@@ -106,7 +106,8 @@ struct AttnArgs {
   unsigned char* ws;
   Layout L;
   Dims d;
-  int skim;   // the plan may hold SKIM tiles (64-key blocks)
+  int skim;       // the plan may hold SKIM tiles (64-key blocks)
+  int list_cap;   // bound on a row's FULL + LOW + SKIM tiles under the plan's mode (<= Nk)
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
