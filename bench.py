@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,10 +52,14 @@ def parse():
 
 
 def source_hash():
+    """Hash of the fused kernel's code (comments and blank lines stripped, so
+    an edit of a comment does not void the recorded counters)."""
     h = hashlib.sha256()
     for f in ("k3_attn.hip", "tattn_device.hpp"):
-        with open(os.path.join(ROOT, "tile_sparse_mixed_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tile_sparse_mixed_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        code = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in code if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

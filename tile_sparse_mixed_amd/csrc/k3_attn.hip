@@ -17,7 +17,11 @@
 //             hi + lo pair (two MFMAs: ~2^-17 precision), each scored with a
 //             log2(n_J) bias if J is skipped in this row and -inf otherwise
 //             ("Triage": a skipped tile is one score weighted by n_J),
-//   SKIP_PV   the same chunk's block means vbar_J (fp16, transposed) for P.V.
+//   SKIP_PV   the same chunk's block means vbar_J (fp16, transposed) for P.V,
+//   SKIM      (instances with SKIM = true, 64-key blocks) a 4-bit tile: S^T on
+//             the same instruction with MXFP4 operands and their E8M0 block
+//             scales ("Triage": skimming in 4 bits); P.V against the fp16
+//             dequantised MXFP4 V.
 // Skipped blocks are visited as whole chunks of 64 (contiguous operands),
 // masked to the row's SKIP set; chunks with no skipped block are not visited.
 // With 16-key blocks ("FG-Attn": M x N tiles with a small N) a FULL or LOW
@@ -34,7 +38,10 @@
 // __shared__ arrays and every step knows its stage at compile time (the step
 // loops are unrolled by two): the compiler's wait insertion then sees that the
 // DMA into one stage cannot alias the operand reads of the other and does not
-// put a vmcnt(0) in front of them, which would serialise the copy and the math.  Scalar buffer resources carry
+// put a vmcnt(0) in front of them, which would serialise the copy and the
+// math.  Two-wave workgroups keep one stage instead, as two arrays for its
+// halves, and refill each half as soon as its reads are done (see SPLIT).
+// Scalar buffer resources carry
 // the bases, so a lane needs one 32-bit offset per load pattern, and a
 // per-tile resource over the caller's K returns zeros for rows past N.  The
 // XOR swizzle that keeps the MFMA operand reads bank-conflict free is applied
