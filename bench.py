@@ -268,6 +268,15 @@ def main():
     tiles = st["n_full"] + st["n_low"] + st["n_skip"] + st["n_skim"]
     traffic = load_traffic(args.workload)
 
+    # the plan (K1 + K2) as an HBM-bound pass: algorithmic bytes = read Q, K, V
+    # (bf16) + E4M3 K and V + float32 means and scales (K1), + the means read
+    # back, the int16 lists and the counts (K2), over the plan time
+    N, d, H, Nq, Nk = cfg.seq_len, cfg.head_dim, cfg.heads * cfg.batch, cfg.n_qblocks, cfg.n_kblocks
+    rb = (3 * N * d * H * 2 + 2 * N * d * H + (Nq + 2 * Nk) * d * H * 4 + 2 * Nk * H * 4
+          + (Nq + Nk) * d * H * 4 + Nq * Nk * H * 2 + 12 * Nq * H)
+    router = {"bytes_algorithmic": rb, "gb_s": round(rb / (ms_plan * 1e-3) / 1e9, 1),
+              "frac_hbm": round(rb / (ms_plan * 1e-3) / 1e9 / PEAK_HBM, 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -300,6 +309,10 @@ def main():
         "forward_dense_equiv_tflops": round(dense / (ms_k3 * 1e-3) / 1e12, 2),
         "forward_executed_tflops": round(executed / (ms_k3 * 1e-3) / 1e12, 2),
         "mfma_utilisation_kept_tiles": round(achieved / PEAK_BF16, 4),
+        "peak_fractions": {"forward_dense_equiv_of_bf16": round(dense / (ms_k3 * 1e-3) / 1e12 / PEAK_BF16, 4),
+                           "forward_executed_of_bf16": round(executed / (ms_k3 * 1e-3) / 1e12 / PEAK_BF16, 4),
+                           "forward_executed_of_fp8": round(executed / (ms_k3 * 1e-3) / 1e12 / PEAK_FP8, 4)},
+        "router": router,
         "all_full_tflops": None if ms_allfull is None else round(dense / (ms_allfull * 1e-3) / 1e12, 2),
         "tiers": {"full": round(st["n_full"] / tiles, 4), "low": round(st["n_low"] / tiles, 4),
                   "skip": round(st["n_skip"] / tiles, 4), "diagonal": st["n_diag"],
