@@ -252,21 +252,24 @@ void k3_attn(AttnArgs a) {
   const float sq = reinterpret_cast<const float*>(ws + a.L.sq)[row];
   const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
 
-  // step order: FULL tiles, then the skip chunks (score / P.V pairs), then LOW
+  // step order: the skip chunks (score / P.V pairs), then FULL tiles, then LOW
   // tiles, so the bf16 Q registers are dead before the E4M3 copy is made, then
-  // SKIM tiles.
-  const int nS2 = 2 * snc, tLow = sF + nS2, tSk = tLow + sL;
+  // SKIM tiles.  (Skip chunks first: their loop then starts at an even step
+  // and is generated once, not once per stage parity, and the kernel fits its
+  // registers without spilling; with FULL first it spilled 42 VGPRs whose
+  // scratch reloads share vmcnt with the DMA.)
+  const int nS2 = 2 * snc, tLow = nS2 + sF, tSk = tLow + sL;
   auto step_kind = [&](int t) __attribute__((always_inline)) {
-    if (t < sF) return (int)kFull;
-    if (t < tLow) return ((t - sF) & 1) ? (int)kSkipPV : (int)kSkipS;
+    if (t < nS2) return (t & 1) ? (int)kSkipPV : (int)kSkipS;
+    if (t < tLow) return (int)kFull;
     if (SKIM && t >= tSk) return (int)kSkim;
     return (int)kLow;
   };
   // list entry of key block g of a FULL, LOW or SKIM step, and the end of its list
   auto list_idx = [&](int t, int g) {
-    return t < sF ? G * t + g : (SKIM && t >= tSk) ? nK + (t - tSk) + g : nF + G * (t - tLow) + g;
+    return t < tLow ? G * (t - nS2) + g : (SKIM && t >= tSk) ? nK + (t - tSk) + g : nF + G * (t - tLow) + g;
   };
-  auto list_end = [&](int t) { return t < sF ? nF : nK; };
+  auto list_end = [&](int t) { return t < tLow ? nF : nK; };
   auto list_at = [&](int t) { return (int)slist[list_idx(t, 0)]; };
 
   // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
@@ -467,7 +470,7 @@ void k3_attn(AttnArgs a) {
       if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vskim + J * 128 * D);
       if constexpr (PA) cst.c[0] = cF;
     } else {
-      const int c = schunk[(t - sF) >> 1];
+      const int c = schunk[t >> 1];
       if ((KINDS & (1 << kSkipS)) && kind == kSkipS) {
 #pragma unroll
         for (int i = 0; i < NI16; i++) {
@@ -671,7 +674,7 @@ void k3_attn(AttnArgs a) {
       // occurs in the last step of the phase.  Register (b, r) is key
       // 8((r >> 2) & 1) + 4lh + r % 4 of 16-key block 2b + r / 8, or key
       // 4((r >> 2) & 1) + r % 4 of 8-key block (slot) 4b + 2(r / 8) + lh.
-      if (t == (LOW ? tSk - 1 : sF - 1)) {
+      if (t == (LOW ? tSk - 1 : tLow - 1)) {
         const int i0 = list_idx(t, 0), e = list_end(t);
         // valid keys of each block: 0 past the list end, fewer in block Nk - 1
         int lim[G];
@@ -737,7 +740,7 @@ void k3_attn(AttnArgs a) {
     // bias log2(n_J) for the row's skipped blocks, -inf for the others.  Key
     // 32b + 8(r/4) + 4lh + r%4 of the chunk is bit 32b + 8(r/4) + r%4 of the
     // chunk's mask shifted right by 4lh.
-    const int ci = (t - sF) >> 1;
+    const int ci = t >> 1;
     const uint64_t msk = smask[ci] >> (4 * lh);
     const uint32_t mw[2] = {static_cast<uint32_t>(msk), static_cast<uint32_t>(msk >> 32)};
     // position of the ragged last block inside this lane's view of the chunk
@@ -767,8 +770,8 @@ void k3_attn(AttnArgs a) {
     skip_soft(t, s);
   };
 
-  // ---- the step loop, in phases (FULL, skip chunks as score / P.V pairs, then
-  // LOW).  Step t computes from stage t & 1 while step t+1's DMA fills the
+  // ---- the step loop, in phases (skip chunks as score / P.V pairs, FULL,
+  // LOW, SKIM).  Step t computes from stage t & 1 while step t+1's DMA fills the
   // other stage; the explicit vmcnt(0) + barrier publishes it.  The parity is
   // a compile-time tag, so each stage is a distinct array at every access.
   using P0 = std::integral_constant<int, 0>;
@@ -792,10 +795,10 @@ void k3_attn(AttnArgs a) {
   };
   constexpr int kSk = SKIM ? 1 << kSkim : 0;
   using KAll = std::integral_constant<int, 15 | kSk>;
-  using KAfterFull = std::integral_constant<int, (1 << kFull) | (1 << kSkipS) | (1 << kLow) | kSk>;
+  using KAfterFull = std::integral_constant<int, (1 << kFull) | (1 << kLow) | kSk>;
   using KSkipS = std::integral_constant<int, 1 << kSkipS>;
   using KSkipPV = std::integral_constant<int, 1 << kSkipPV>;
-  using KAfterSkip = std::integral_constant<int, (1 << kSkipS) | (1 << kLow) | kSk>;
+  using KAfterSkip = std::integral_constant<int, (1 << kSkipS) | (1 << kFull) | (1 << kLow) | kSk>;
   using KLow = std::integral_constant<int, (1 << kLow) | kSk>;
   using KSkimOnly = std::integral_constant<int, kSk>;
   // the E4M3 copy of this lane's Q (32 bytes per fp8 instruction i = bf16
@@ -863,26 +866,20 @@ void k3_attn(AttnArgs a) {
         ++t;
       }
     };
-    run_phase(sF, [&](auto p, int tt) __attribute__((always_inline)) {
+    // skip pairs first, from step 0 (even parity)
+    for (; t < nS2; t += 2) {
+      issue(KSkipPV{}, t + 1, stB, cB);
+      skip_scores(t, stA);
+      next();
+      if (t + 2 < nSteps) issue(KAfterSkip{}, t + 2, stA, cA);
+      pv(stB);
+      next();
+    }
+    run_phase(tLow, [&](auto p, int tt) __attribute__((always_inline)) {
       if (tt + 1 < nSteps) issue(KAfterFull{}, tt + 1, stg(flip(p)), scl(flip(p)));
       kept_step(std::false_type{}, tt, stg(p), scl(p), nullptr);
       next();
     });
-    // skip pairs keep the parity of their first step
-    auto skip_pairs = [&](auto p) __attribute__((always_inline)) {
-      for (; t < tLow; t += 2) {
-        issue(KSkipPV{}, t + 1, stg(flip(p)), scl(flip(p)));
-        skip_scores(t, stg(p));
-        next();
-        if (t + 2 < nSteps) issue(KAfterSkip{}, t + 2, stg(p), scl(p));
-        pv(stg(flip(p)));
-        next();
-      }
-    };
-    if (t < tLow) {
-      if (t & 1) skip_pairs(P1{});
-      else skip_pairs(P0{});
-    }
     if (t < tSk) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
                      // fp8 instruction i = bf16 chunks 4i..4i+3)
       i32x8 q8reg[D / 64];
@@ -968,18 +965,18 @@ void k3_attn(AttnArgs a) {
     using T1 = std::true_type;
     auto no_S = [&](f32x16*) {};
     auto no_soft = [&](f32x16*, const StepScale<G>&) {};
-    while (t < sF)
-      split_step(KAfterFull{}, T1{}, T1{}, T0{},
-                 [&](f32x16* s) __attribute__((always_inline)) { scores_bf16(stA, s); },
-                 [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T0{}, t, s, c); });
-    while (t < tLow) {
-      if (((t - sF) & 1) == 0)
+    while (t < nS2) {
+      if ((t & 1) == 0)
         split_step(KSkipPV{}, T1{}, T0{}, T1{},
                    [&](f32x16* s) __attribute__((always_inline)) { skip_S(stA, s); },
                    [&](f32x16* s, const StepScale<G>&) __attribute__((always_inline)) { skip_soft(t, s); });
       else
         split_step(KAfterSkip{}, T0{}, T1{}, T0{}, no_S, no_soft);
     }
+    while (t < tLow)
+      split_step(KAfterFull{}, T1{}, T1{}, T0{},
+                 [&](f32x16* s) __attribute__((always_inline)) { scores_bf16(stA, s); },
+                 [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T0{}, t, s, c); });
     if (t < tSk) {
       i32x8 q8reg[D / 64];
       make_q8(q8reg);
