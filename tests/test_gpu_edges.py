@@ -121,3 +121,44 @@ def test_equal_thresholds_have_no_low_tier():
     out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
     assert not np.any(p.tiers() == 1)
     _check(cfg, g, p, out, what="tau_hi == tau_lo")
+
+
+@pytest.mark.parametrize("bk", [16, 8])
+def test_adaptive_rows_at_the_list_bound(bk):
+    """keep_min = keep_max = 0.5 makes every head's k_h = ceil(0.5 Nk): each
+    row keeps k_h tiles plus any diagonal block outside them, the most the
+    fused kernel's list (sized by that bound) has to hold."""
+    import tile_sparse_mixed_amd as tsm
+    cfg = CONFIGS["fine_adaptive"].with_(heads=2, grid=(2, 10, 50), block_k=bk, keep_min=0.5, keep_max=0.5)
+    g = generate(cfg)
+    d = _dev(g["bits"])
+    p = tsm.plan(d["q"], d["k"], d["v"], block_q=cfg.block_q, block_k=bk, mode="adaptive", keep_min=0.5,
+                 keep_max=0.5, full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, out_fp32=True)
+    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
+    kh = p.kh()[0]
+    assert np.all(kh == int(np.ceil(0.5 * cfg.n_kblocks)))
+    tiers = p.tiers()
+    kept = (tiers != 0).sum(axis=3)
+    _log(f"[list bound bk{bk}] k_h {kh.tolist()}, kept per row {int(kept.min())}..{int(kept.max())} of {cfg.n_kblocks}")
+    oc = OracleCfg(cfg)
+    oc.keep_min = oc.keep_max = 0.5
+    for h in range(cfg.heads):
+        q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
+        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
+        ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k)
+        err = np.abs(out[0, h].astype(np.float64) - ref)
+        assert err.max() <= 1e-2 and err.mean() <= 1e-3, (bk, h, err.max(), err.mean())
+
+
+def test_top_k_rows_at_the_list_bound():
+    """top_k with every tile above the thresholds: rows keep exactly top_k
+    tiles plus the diagonal blocks, the list bound for top-k plans."""
+    import tile_sparse_mixed_amd as tsm
+    cfg = CONFIGS["small"].with_(heads=2, tau_hi=0.0, tau_lo=0.0, top_k=5)
+    g = generate(cfg)
+    d = _dev(g["bits"])
+    p = _plan(tsm, cfg, d)
+    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
+    kept = (p.tiers() != 0).sum(axis=3)
+    assert kept.min() >= 5
+    _check(cfg, g, p, out, top_k=5, what="top_k at bound")
