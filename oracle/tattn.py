@@ -168,7 +168,9 @@ def tiers_adaptive(p: np.ndarray, k_h: int, full_frac: float) -> np.ndarray:
 # (parity unpinned as a predictor; its exact identities are pinned).
 
 E4M3_U = 2.0 ** -4          # largest relative rounding error of an E4M3 normal value
+MXFP4_U = 2.0 ** -2         # largest relative rounding error of an E2M1 normal value
 COST_FULL, COST_LOW = 1.0, 0.75   # bf16-equivalent MFMA work per tile: LOW = fp8 scores (half) + fp16 P.V
+COST_SKIM = 0.625           # SKIM = fp4 scores (a quarter) + fp16 P.V
 
 
 def cost_skip(bk: int) -> float:
@@ -204,7 +206,7 @@ def block_moments(x: np.ndarray, b: int):
     return dict(m2=m2, var=var, tot_m2=tot_m2, tot_var=tot_var, mnorm=mnorm)
 
 
-def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d):
+def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d, skim=False):
     """Predicted relative output error of every tile (I, J) under SKIP and LOW
     (FULL: 0), float64 [Nq, Nk] each.  Inputs are the float32 block statistics
     of block_moments (q2 = query m2 per dimension, m2q its total; kvar = key
@@ -230,8 +232,12 @@ def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d):
             noise of RMS u sqrt(m2v/3):
             eL = vnorm expm1(sl2/2)
                  + (sqrt(vvar expm1(sl2)) + u sqrt(m2v/3)) / sqrt(n_eff).
+      SKIM  (MXFP4 copies, with skim=True): the same form with E2M1's bound
+            u = 2^-2 in place of E4M3's 2^-4 (its rounding is relative to the
+            32-element block's scale, and the relative bound covers it).
     The norm of the block mean stands in for the distance between the tile's
-    output and the row's.  Returns (s2, g, eS, eL)."""
+    output and the row's.  Returns (s2, g, eS, eL), and eK after them with
+    skim=True."""
     q2 = q2.astype(np.float64)
     kvar = kvar.astype(np.float64)
     s2 = (q2 @ kvar.T) / d                                              # [Nq, Nk]
@@ -245,7 +251,11 @@ def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d):
     mv = m2v.astype(np.float64)[None, :]
     eS = vn * (-np.expm1(-g)) + np.sqrt(vv * np.maximum(0.0, 1.0 / neff - 1.0 / nj))
     eL = vn * np.expm1(0.5 * sl2) + (np.sqrt(vv * np.expm1(sl2)) + E4M3_U * np.sqrt(mv / 3.0)) / np.sqrt(neff)
-    return s2, g, eS, eL
+    if not skim:
+        return s2, g, eS, eL
+    sk2 = (2.0 * MXFP4_U ** 2 / 3.0) * np.outer(m2q.astype(np.float64), m2k.astype(np.float64)) / float(d * d)
+    eK = vn * np.expm1(0.5 * sk2) + (np.sqrt(vv * np.expm1(sk2)) + MXFP4_U * np.sqrt(mv / 3.0)) / np.sqrt(neff)
+    return s2, g, eS, eL, eK
 
 
 def corrected_shares(S: np.ndarray, g: np.ndarray) -> np.ndarray:
@@ -256,23 +266,28 @@ def corrected_shares(S: np.ndarray, g: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=1, keepdims=True)
 
 
-def tiers_price(p: np.ndarray, eS: np.ndarray, eL: np.ndarray, price: float, bk: int):
+def tiers_price(p: np.ndarray, eS: np.ndarray, eL: np.ndarray, price: float, bk: int, eK=None):
     """Each tile takes the tier t minimising p_IJ * e_t + price * cost_t, i.e.
     it moves to a more accurate tier only when the predicted error reduction
     (the relative error scaled by the tile's share p of the row) pays for the
     extra work at the given price (Triage: one price sets the trade-off).
-    Ties go to the cheaper tier.  Returns the tier map and the three
-    objectives."""
+    With eK the SKIM tier is a fourth choice (Triage: skip, skim in 4 bits,
+    refine).  Ties go to the cheaper tier (SKIP < SKIM < LOW < FULL in work).
+    Returns the tier map and the objectives (SKIP, LOW, FULL, then SKIM)."""
     lam = float(price)
     oS = p * eS + lam * cost_skip(bk)
     oL = p * eL + lam * COST_LOW
     oF = np.full(p.shape, lam * COST_FULL)
     t = np.full(p.shape, SKIP, dtype=np.uint8)
     best = oS.copy()
+    if eK is not None:
+        oK = p * eK + lam * COST_SKIM
+        t[oK < best] = SKIM
+        best = np.minimum(best, oK)
     t[oL < best] = LOW
     best = np.minimum(best, oL)
     t[oF < best] = FULL
-    return t, (oS, oL, oF)
+    return t, ((oS, oL, oF) if eK is None else (oS, oL, oF, oK))
 
 
 def build_lists(t: np.ndarray):
@@ -521,11 +536,14 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
         t = np.full(p.shape, FULL, dtype=np.uint8)
     elif mode == 4:    # price
         qm, km, vm = block_moments(q, bq), block_moments(k, bk), block_moments(v, bk)
-        s2, g, eS, eL = tile_error_model(qm["m2"], qm["tot_m2"], km["var"], km["tot_m2"], vm["tot_var"],
-                                         vm["tot_m2"], vm["mnorm"], block_sizes(n, bk), d)
+        skim = getattr(cfg_like, "tau_skim", 0.0) > 0
+        errs = tile_error_model(qm["m2"], qm["tot_m2"], km["var"], km["tot_m2"], vm["tot_var"],
+                                vm["tot_m2"], vm["mnorm"], block_sizes(n, bk), d, skim=skim)
+        s2, g, eS, eL = errs[:4]
+        eK = errs[4] if skim else None
         pt = corrected_shares(S, g)
-        t, objs = tiers_price(pt, eS, eL, cfg_like.price, bk)
-        price_info = dict(qm=qm, km=km, vm=vm, s2=s2, g=g, pt=pt, eS=eS, eL=eL, objs=objs)
+        t, objs = tiers_price(pt, eS, eL, cfg_like.price, bk, eK=eK)
+        price_info = dict(qm=qm, km=km, vm=vm, s2=s2, g=g, pt=pt, eS=eS, eL=eL, eK=eK, objs=objs)
     else:              # external
         t = np.array(external_tiers, dtype=np.uint8, copy=True)
     t[diagonal_mask(n, bq, bk)] = FULL

@@ -176,3 +176,74 @@ def test_price_plan_forces_the_diagonal_and_partitions_lists():
     diag = T.diagonal_mask(n, bq, bk)
     assert np.all(plan["tiers"][diag] == FULL) and np.all(plan["tiers"][~diag] == SKIP)
     assert np.all(plan["counts"].sum(axis=1) == plan["tiers"].shape[1])
+
+
+def test_skim_score_noise_bounds_real_mxfp4_rounding():
+    """The SKIM tier's score-noise variance (2u^2/3) m2q m2k / d^2 with
+    u = 2^-2: real MXFP4 rounding of Gaussian data (through the oracle's own
+    codec, one scale per 32 channels) must come out below it, and within a
+    factor of 3; so must the value error against u sqrt(m2v/3)."""
+    from oracle import mxfp4
+    for seed in range(3):
+        r = np.random.default_rng(50 + seed)
+        d, b = 64, 64
+        q = (r.standard_normal((b, d)) * (1 + seed)).astype(np.float32)
+        k = (r.standard_normal((b, d)) * 0.7 + 0.2).astype(np.float32)
+        qh, kh = mxfp4.quantise(q)[2], mxfp4.quantise(k)[2]
+        err = (qh @ kh.T - q.astype(np.float64) @ k.astype(np.float64).T) / math.sqrt(d)
+        qm, km = T.block_moments(q, b), T.block_moments(k, b)
+        sk2 = (2.0 * T.MXFP4_U ** 2 / 3.0) * float(qm["tot_m2"][0]) * float(km["tot_m2"][0]) / d ** 2
+        ratio = float((err ** 2).mean()) / sk2
+        assert 1.0 / 3.0 <= ratio <= 1.0, (seed, ratio)
+        verr = math.sqrt(float(((kh - k.astype(np.float64)) ** 2).sum(axis=1).mean()))
+        vmod = T.MXFP4_U * math.sqrt(float(km["tot_m2"][0]) / 3.0)
+        assert vmod / 3.0 <= verr <= vmod, (seed, verr, vmod)
+
+
+def _rank4(t):
+    """Work order of the four tiers: SKIP < SKIM < LOW < FULL."""
+    return np.array([0, 2, 3, 1], np.int64)[np.asarray(t, np.int64)]
+
+
+def test_price_rule_structure_four_tiers():
+    """With the SKIM tier: its predicted error lies above LOW's (a coarser
+    format) and below SKIP's where skipping is costly; every tile takes the
+    minimum of its four objectives; raising the price never moves a tile to a
+    more costly tier; price 0 gives FULL, a prohibitive price SKIP; ties go
+    to the cheaper tier."""
+    r = np.random.default_rng(7)
+    n, d, bq, bk = 512, 32, 64, 32
+    q, k = [r.standard_normal((n, d)).astype(np.float32) for _ in range(2)]
+    # values sharing a mean direction: skipping loses the mass deficit on a
+    # large mean, while MXFP4's value error stays near LOW's, so SKIM pays for
+    # some tiles (with zero-mean values LOW dominates it everywhere)
+    v = (r.standard_normal((n, d)) * 0.3 + 3.0 * r.standard_normal((1, d))).astype(np.float32)
+    c = cfg(bq, bk, 0.0)
+    c.tau_skim = 1e-4
+    base = T.oracle_plan(q, k, v, c)
+    info, p = base["price"], base["price"]["pt"]
+    assert info["eK"] is not None and np.all(info["eK"] >= info["eL"])
+    seen = set()
+    prev = None
+    for lam in [0.0] + np.logspace(-5, 1, 61).tolist() + [1e3]:
+        t, objs = T.tiers_price(p, info["eS"], info["eL"], lam, bk, eK=info["eK"])
+        oS, oL, oF, oK = objs
+        by_tier = np.stack([oS, oL, oF, oK])          # indexed by tier byte
+        assert np.all(np.take_along_axis(by_tier, np.asarray(t, np.int64)[None], 0)[0] == by_tier.min(axis=0))
+        if prev is not None:
+            assert np.all(_rank4(t) <= _rank4(prev))
+        prev = t
+        seen |= set(np.unique(t).tolist())
+        if lam == 0.0:
+            assert np.all(t[(p * info["eS"] > 0) & (p * info["eK"] > 0)] == FULL)
+        if lam == 1e3:
+            assert np.all(t == SKIP)
+    assert T.SKIM in seen, seen
+    z = np.zeros((1, 3))
+    t, _ = T.tiers_price(z, z, z, 0.0, bk, eK=z)
+    assert np.all(t == SKIP)
+    # a SKIM/LOW tie at equal objectives goes to SKIM (the cheaper)
+    # (p = 1, price 1: SKIM 0.25 + 0.625 = LOW 0.125 + 0.75 = 0.875 < FULL 1 < SKIP)
+    t, _ = T.tiers_price(np.ones((1, 1)), np.full((1, 1), 10.0), np.full((1, 1), 0.125),
+                         1.0, bk, eK=np.full((1, 1), 0.25))
+    assert t[0, 0] == T.SKIM
