@@ -97,9 +97,10 @@ typedef struct {
   int64_t stride_b, stride_h, stride_n;    /* element strides shared by Q, K, V and O        */
   float price;                             /* PRICE: error per FULL tile of work, >= 0,
                                               finite; ignored by the other modes             */
-  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite, <= tau_lo, and
-                                              block_k 64) enables it: THRESHOLD uses it as the
-                                              SKIM / SKIP threshold, EXTERNAL accepts SKIM bytes;
+  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite, and block_k 64)
+                                              enables it: THRESHOLD uses it as the SKIM / SKIP
+                                              threshold (then <= tau_lo), EXTERNAL accepts SKIM
+                                              bytes, PRICE weighs SKIM as a fourth choice;
                                               ignored by the other modes                     */
 } tattn_config;
 
@@ -146,9 +147,10 @@ tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes /* hos
  *   LOW   vnorm expm1(sl2/2) + (sqrt(vvar expm1(sl2)) + u sqrt(m2v/3)) / sqrt(n_eff),
  *         sl2 = (2u^2/3) m2q m2k / d^2, u = 2^-4,
  *   FULL  0;
+ *   SKIM  (with tau_skim > 0) the LOW form with u = 2^-2 (MXFP4);
  * shares p~ = softmax_J(S + g); and gives the tile the tier with the least
- * p~ * error + price * work (work FULL 1, LOW 0.75, SKIP 1.5 / block_k;
- * ties to the cheaper tier).  All in float64.
+ * p~ * error + price * work (work FULL 1, LOW 0.75, SKIM 0.625, SKIP
+ * 1.5 / block_k; ties to the cheaper tier).  All in float64.
  * q, k, v: the caller's tensors.  The plan keeps derived copies of K and V
  * (E4M3 codes, a transposed fp16 V, means) in `workspace`, so a later
  * tattn_forward must be given the same k and v pointers with unchanged

@@ -244,8 +244,8 @@ def plan(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, m
          keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256, out_fp32=False,
          workspace=None, price=0.0, tau_skim=0.0) -> Plan:
     """Pool, quantise and route (K1, K2).  q, k, v: bf16 [B, H, N, d] on the GPU.
-    ``tau_skim`` > 0 adds the MXFP4 SKIM tier (threshold and external modes,
-    64-key blocks).  ``workspace`` (a uint8 GPU tensor, e.g. an earlier
+    ``tau_skim`` > 0 adds the MXFP4 SKIM tier (threshold, external and price
+    modes, 64-key blocks).  ``workspace`` (a uint8 GPU tensor, e.g. an earlier
     plan's) is reused when large enough; the earlier plan must not be used
     afterwards."""
     _check_tensors(q, k, v)

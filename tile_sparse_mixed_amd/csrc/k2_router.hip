@@ -15,7 +15,8 @@
 //        ALL_FULL   every tile FULL,
 //        PRICE      per tile the tier with the least predicted error (from
 //                   block second moments, K2a's spread product) plus price x
-//                   work ("Triage": error-predicting router, one price);
+//                   work, SKIM among the choices with tau_skim > 0
+//                   ("Triage": error-predicting router, one price);
 //      diagonal tiles forced FULL; then a stable compaction into
 //      [FULL asc | LOW asc | SKIM asc | SKIP asc] with wavefront ballots.
 // K2c  compaction only, for a tier map supplied by the caller.
@@ -360,6 +361,7 @@ __device__ void compact_row(const unsigned char* tr, int n, int bk, int16_t* lis
 // work).  Evaluated with every operation rounded on its own (no fused
 // multiply-add), in float64.
 constexpr double kE4m3U = 0.0625;   // 2^-4: largest relative rounding error of an E4M3 normal value
+constexpr double kE2m1U = 0.25;     // 2^-2: the same for an E2M1 (MXFP4) normal value
 
 // log-mass gain of a tile over its pooled estimate: lognormal mean s2/2 up to
 // s2 = 2 ln n, beyond it the largest of n scores dominates
@@ -369,10 +371,11 @@ __device__ inline double spread_gain(double s2, double lnn) {
 }
 
 struct PriceTile {
-  double s2, n, vnorm, vvar, m2v, sl2;
+  double s2, n, vnorm, vvar, m2v, sl2, sk2;   // sk2: the score-noise variance of MXFP4 copies
 };
 // the tier with the least p~ * error + price * work; ties to the cheaper tier
-__device__ inline unsigned char price_tier(const PriceTile& x, double pt, double price, double cost_skip) {
+// (SKIP < SKIM < LOW < FULL in work); SKIM competes only with `skim`
+__device__ inline unsigned char price_tier(const PriceTile& x, double pt, double price, double cost_skip, bool skim) {
 #pragma clang fp contract(off)
   const double neff = fmax(1.0, x.n * exp(-x.s2));
   const double lnn = log(x.n);
@@ -385,6 +388,15 @@ __device__ inline unsigned char price_tier(const PriceTile& x, double pt, double
   const double oF = price * 1.0;
   unsigned char t = TATTN_SKIP;
   double best = oS;
+  if (skim) {
+    const double eK = x.vnorm * expm1(0.5 * x.sk2) +
+                      (sqrt(x.vvar * expm1(x.sk2)) + kE2m1U * sqrt(x.m2v / 3.0)) / sqrt(neff);
+    const double oK = pt * eK + price * 0.625;
+    if (oK < best) {
+      t = TATTN_SKIM;
+      best = oK;
+    }
+  }
   if (oL < best) {
     t = TATTN_LOW;
     best = oL;
@@ -427,6 +439,8 @@ __device__ void price_row(const RouterArgs& a, int bh, int64_t row, const double
   sum = block_sum_d(sum, r);
   const double price = a.price, cost_skip = 1.5 / static_cast<double>(dm.Bk);
   const double cu = 2.0 * kE4m3U * kE4m3U / 3.0, dd = static_cast<double>(dm.D) * static_cast<double>(dm.D);
+  const double cu4 = 2.0 * kE2m1U * kE2m1U / 3.0;
+  const bool skim = a.tau_skim > 0.0f;
   for (int J = threadIdx.x; J < n; J += kThreads) {
     PriceTile x;
     x.s2 = s2r[J];
@@ -437,8 +451,9 @@ __device__ void price_row(const RouterArgs& a, int bh, int64_t row, const double
     {
 #pragma clang fp contract(off)
       x.sl2 = cu * (m2q * static_cast<double>(m2k[J])) / dd;
+      x.sk2 = cu4 * (m2q * static_cast<double>(m2k[J])) / dd;
     }
-    tr[J] = price_tier(x, pv[J] / sum, price, cost_skip);
+    tr[J] = price_tier(x, pv[J] / sum, price, cost_skip, skim);
   }
 }
 

@@ -117,9 +117,11 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim) 
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// The SKIM tier is on for a positive tau_skim in THRESHOLD and EXTERNAL modes.
+// The SKIM tier is on for a positive tau_skim in THRESHOLD, EXTERNAL and
+// PRICE modes.
 static bool skim_on(const tattn_config& c) {
-  return c.tau_skim > 0.0f && (c.mode == TATTN_MODE_THRESHOLD || c.mode == TATTN_MODE_EXTERNAL);
+  return c.tau_skim > 0.0f &&
+         (c.mode == TATTN_MODE_THRESHOLD || c.mode == TATTN_MODE_EXTERNAL || c.mode == TATTN_MODE_PRICE);
 }
 static Layout layout_of(const tattn_config& c) {
   return make_layout(make_dims(c), c.entropy_samples, c.mode == TATTN_MODE_PRICE, skim_on(c));
@@ -157,7 +159,9 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "price must be finite and >= 0 (got %g)", c->price);
   if (!std::isfinite(c->tau_hi) || !std::isfinite(c->tau_lo) || c->tau_lo < 0.0f || c->tau_lo > c->tau_hi)
     return fail(TATTN_E_INVALID, "thresholds need 0 <= tau_lo <= tau_hi (got %g, %g)", c->tau_lo, c->tau_hi);
-  if (!std::isfinite(c->tau_skim) || c->tau_skim < 0.0f || c->tau_skim > c->tau_lo)
+  if (!std::isfinite(c->tau_skim) || c->tau_skim < 0.0f)
+    return fail(TATTN_E_INVALID, "tau_skim must be finite and >= 0 (got %g)", c->tau_skim);
+  if (c->mode == TATTN_MODE_THRESHOLD && c->tau_skim > c->tau_lo)
     return fail(TATTN_E_INVALID, "tau_skim needs 0 <= tau_skim <= tau_lo (got %g, tau_lo %g)", c->tau_skim, c->tau_lo);
   if (skim_on(*c) && c->block_k != 64)
     return fail(TATTN_E_UNSUPPORTED, "the SKIM tier needs 64-key blocks (block_k %d)", c->block_k);
