@@ -33,7 +33,8 @@ ragged and keep their real sizes.
                                                           fused pass)
 
 Precision: float64 throughout, except that every fp8 code is decided on a
-float32 value (the precision in which the kernel forms it).  Means are
+float32 value and the low tier's dequantised values are formed in float32 and
+rounded to float16 (the precisions in which the kernel forms them).  Means are
 accumulated in float64 and stored as float32.
 """
 import math
@@ -330,37 +331,6 @@ def quantise_blocks(x: np.ndarray, b: int):
     return codes, scale, inv
 
 
-def value_exponents(x: np.ndarray, b: int) -> np.ndarray:
-    """Power-of-two fp8 scale exponent of every block of b rows of V: the
-    smallest integer e with max|X_block| <= 448 * 2^e (the largest E4M3
-    magnitude), 0 for an all-zero block, clamped to the E8M0 range [-127, 127].
-    The block's codes then fill the E4M3 range as a per-block scale
-    amax / 448 would, to within one binade."""
-    n = x.shape[0]
-    sizes = block_sizes(n, b)
-    e = np.zeros(sizes.size, dtype=np.int64)
-    for j, sz in enumerate(sizes):
-        a = float(np.abs(x[j * b: j * b + sz].astype(np.float64)).max())
-        if a == 0.0:
-            continue
-        f, ex = math.frexp(a / 448.0)            # a / 448 = f * 2^ex, f in [0.5, 1)
-        e[j] = ex - 1 if f == 0.5 else ex         # smallest e with a / 448 <= 2^e
-    return np.clip(e, -127, 127)
-
-
-def quantise_values(v: np.ndarray, b: int):
-    """fp8 E4M3 codes of V with one power-of-two scale 2^e per block of b rows
-    (HierPAS: reduced precision for less critical regions; the scale is a
-    power of two so that the matrix core applies it exactly):
-    code = E(v * 2^-e), the scaling exact.  Returns (codes uint8 [n, d],
-    scale f32 = 2^e, e int64)."""
-    e = value_exponents(v, b)
-    n = v.shape[0]
-    blk = np.repeat(np.arange(e.size), b)[:n]
-    codes = e4m3.encode(np.ldexp(v.astype(np.float64), -e[blk][:, None]))
-    return codes, np.ldexp(np.ones(e.size), e).astype(np.float32), e
-
-
 def skim_operands(q, k, v):
     """Operands of skim tiles (Triage: skimming in a 4-bit format): Q, K and V
     each quantised to MXFP4 per token row, one E8M0 scale per 32 consecutive
@@ -378,40 +348,12 @@ def skim_operands(q, k, v):
 
 def low_values(v8: np.ndarray, sv: np.ndarray, b: int) -> np.ndarray:
     """Value operand of low-precision tiles: the dequantised E4M3 value
-    decode(code) * scale, exact (the scale is a power of two).  Returns
-    float64 [n, d]."""
+    decode(code) * scale, formed in float32 and rounded to float16 (the
+    precision in which the kernel forms it).  Returns float64 [n, d]."""
     n = v8.shape[0]
     blk = np.repeat(np.arange(-(-n // b)), b)[:n]
-    return e4m3.decode(v8) * sv.astype(np.float64)[blk][:, None]
-
-
-LOG2E = 1.0 / math.log(2.0)
-P_TOP = 8            # a low tile's largest probability code lies in (2^7, 2^8]
-FLIP_REL = 2.0 ** -14
-
-
-def low_probabilities(t2: np.ndarray):
-    """Probability codes of low tiles (HierPAS: reduced precision for less
-    critical regions; the probabilities of a low tile are quantised to E4M3
-    too, against the tile's own maximum, so a tile's codes do not depend on
-    the order in which tiles are processed).  t2: base-2 scores [..., keys]
-    (-inf for masked keys).  Reference r = ceil(max t2), an integer, so that
-    merging tiles only scales by powers of two; y = fl32(2^(t2 - r + P_TOP)),
-    code = E(y).  Returns (code values decode(E(y)) in [0, 2^P_TOP], r, y
-    in float64 before the float32 rounding)."""
-    r = np.ceil(t2.max(axis=-1))
-    y = np.exp2(t2 - r[..., None] + P_TOP)
-    c = e4m3.decode(e4m3.encode(y.astype(np.float32)))
-    return c, r, y
-
-
-def low_flip_steps(y: np.ndarray) -> np.ndarray:
-    """How far a code may move where fp32 rounding could decide it the other
-    way: for values within FLIP_REL (relative) of an E4M3 rounding midpoint,
-    the gap between the two candidate code values, else 0."""
-    up = e4m3.decode(e4m3.encode((y * (1 + FLIP_REL)).astype(np.float32)))
-    dn = e4m3.decode(e4m3.encode((y * (1 - FLIP_REL)).astype(np.float32)))
-    return up - dn
+    prod = e4m3.decode(v8).astype(np.float32) * sv.astype(np.float32)[blk][:, None]
+    return prod.astype(np.float32).astype(np.float16).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------- O6/O7
@@ -423,17 +365,15 @@ def _padded(x, nb, b):
 
 
 def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
-                      rows=None, return_partials=False, mx4=None, flip_bound=False):
+                      rows=None, return_partials=False, mx4=None):
     """One pass over all tiles of every query row, merging per-tile partials
     exactly (Triage: skip, low precision and full tiles in a single pass).
 
     FULL: s_j = <q_i,k_j>/sqrt(d); partial (max s, sum e^{s-m}, sum e^{s-m} v_j).
-    LOW:  on the E4M3 copies: s^_j = <q^_i,k^_j>/sqrt(d) with
+    LOW:  the same on the E4M3 copies: s^_j = <q^_i,k^_j>/sqrt(d) with
           X^ = decode(X8) * scale (q^, k^ exact in float64), values
-          v^_j = decode(V8_j) * 2^e_J; probabilities quantised per tile
-          (low_probabilities): t_j = s^_j log2(e), r = ceil(max t),
-          pi_j = decode(E(fl32(2^(t_j - r + 8)))); partial
-          ((r - 8) ln 2, sum pi_j, sum pi_j v^_j).
+          v^_j = fl16(fl32(decode(V8_j) * scale_J)) (the fp16 value operand
+          the low tier multiplies); partial (max s^, sum e^{s^-m}, sum e^{s^-m} v^_j).
     SKIM: the same on the MXFP4 copies (``mx4``, from skim_operands): scores
           <q4_i, k4_j>/sqrt(d), values v4_j (Triage: skimming in 4 bits).
     SKIP: sigma = <q_i, k_J>/sqrt(d) + ln n_J; partial (sigma, 1, v_J): one
@@ -442,13 +382,7 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
 
     q, k, v: [n, d] (values as float64); t: tier map [Nq, Nk].
     ``rows`` restricts the computation to those query blocks (others left 0).
-    Returns O float64 [n, d] (and the per-row partial lists if requested).
-    With ``flip_bound`` also a per-row bound [n] on how far O may move when
-    low-tier probability codes within FLIP_REL of a rounding midpoint are
-    decided the other way (first order: sum over such codes of the code gap
-    times the tile factor times (max|v^_j| + max|O_i|), over the denominator).
-    Which way such a code goes depends on the last bits of an exponential, so
-    any implementation may differ there."""
+    Returns O float64 [n, d] (and the per-row partial lists if requested)."""
     n, d = q.shape
     nq, nk = t.shape
     isd = 1.0 / math.sqrt(d)
@@ -466,8 +400,6 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     kb64, vb64 = kbar.astype(np.float64), vbar.astype(np.float64)
     lnk = np.log(ksz.astype(np.float64))
     out = np.zeros((n, d), dtype=np.float64)
-    bound = np.zeros(n, dtype=np.float64)
-    vmax = np.abs(Vh).max(axis=2)                                      # [Nk, Bk]
     partials = {}
     for i in (range(nq) if rows is None else rows):
         r0, r1 = i * bq, min(n, (i + 1) * bq)
@@ -483,18 +415,16 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
             ls.append(e.sum(axis=2))
             os_.append(np.matmul(e.transpose(1, 0, 2), Vp[F]).transpose(1, 0, 2))
         L = np.nonzero(t[i] == LOW)[0]
-        low_flip = None
         if L.size:
             raw = (Qc[r0:r1] @ Kh[L].reshape(-1, d).T).reshape(r1 - r0, L.size, bk)
             sc = float(sq[i]) * sk.astype(np.float64)[L] * isd            # [nL]
             sh = raw * sc[None, :, None]
             sh = np.where(valid[L][None], sh, -np.inf)
-            pc, rt, y = low_probabilities(sh * LOG2E)
-            ms.append((rt - P_TOP) * math.log(2.0))
-            ls.append(pc.sum(axis=2))
-            os_.append(np.matmul(pc.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
-            if flip_bound:
-                low_flip = (low_flip_steps(y), ms[-1], vmax[L])
+            mt = sh.max(axis=2)
+            e = np.exp(sh - mt[..., None])
+            ms.append(mt)
+            ls.append(e.sum(axis=2))
+            os_.append(np.matmul(e.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
         K4 = np.nonzero(t[i] == SKIM)[0]
         if K4.size:
             s = (mx4["q"][r0:r1] @ Kq[K4].reshape(-1, d).T).reshape(r1 - r0, K4.size, bk) * isd
@@ -522,26 +452,17 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
             den += w.sum(axis=1)
             num += w @ vb64[Sk]
         out[r0:r1] = num / den[:, None]
-        if low_flip is not None:
-            steps, mlow, vm = low_flip                                     # [m, nL, Bk], [m, nL], [nL, Bk]
-            w = np.exp(mlow - M[:, None])
-            omax = np.abs(out[r0:r1]).max(axis=1)
-            g = (steps * (vm[None] + omax[:, None, None])).sum(axis=2)
-            bound[r0:r1] = (w * g).sum(axis=1) / den
         if return_partials:
             partials[i] = (ms, ls, os_, skip_sigma, M, den)
-    res = (out,)
     if return_partials:
-        res += (partials,)
-    if flip_bound:
-        res += (bound,)
-    return res[0] if len(res) == 1 else res
+        return out, partials
+    return out
 
 
 def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv, mx4=None):
     """Dense [n, n] weight matrix W of the method on tiny inputs, together with
     the value matrix each weight multiplies: FULL W_ij = e^{s_ij-M}/L against
-    v_j; LOW W_ij = pi_ij 2^(r_IJ - 8) e^{-M}/L against v^_j; SKIM W_ij = e^{s4_ij-M}/L
+    v_j; LOW W_ij = e^{s^_ij-M}/L against v^_j; SKIM W_ij = e^{s4_ij-M}/L
     against v4_j; SKIP W_ij = e^{sigma-M}/(n_J L) against v_j.  Then
     O = rowsum(W * Vsel)."""
     n, d = q.shape
@@ -570,10 +491,7 @@ def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv, mx4=None
                 logits[j0:j1] = (mx4["k"][j0:j1] @ mx4["q"][i]) * isd
                 sel_skim[i, j0:j1] = True
             else:
-                sh = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
-                pc, rt, _ = low_probabilities(sh * LOG2E)
-                with np.errstate(divide="ignore"):
-                    logits[j0:j1] = np.log(pc) + (rt - P_TOP) * math.log(2.0)
+                logits[j0:j1] = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
                 sel_low[i, j0:j1] = True
         M = logits.max()
         w = np.exp(logits - M)
@@ -632,7 +550,7 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     lists, counts = build_lists(t)
     q8, sq, iq = quantise_blocks(q, bq)
     k8, sk, ik = quantise_blocks(k, bk)
-    v8, sv, ev = quantise_values(v, bk)
+    v8, sv, iv = quantise_blocks(v, bk)
     # the MXFP4 copies, where a SKIM tile needs them
     mx4 = skim_operands(q, k, v) if np.any(t == SKIM) else None
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
@@ -647,7 +565,7 @@ def oracle_replan(q, k, v, prev_plan, cfg_like):
     return oracle_plan(q, k, v, cfg_like, mode=3, external_tiers=prev_plan["tiers"])
 
 
-def oracle_forward(q, k, v, plan, bq, bk, rows=None, flip_bound=False):
+def oracle_forward(q, k, v, plan, bq, bk, rows=None):
     return attention_forward(q, k, v, plan["tiers"], bq, bk, plan["kbar"], plan["vbar"],
                              plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],
-                             rows=rows, mx4=plan.get("mx4"), flip_bound=flip_bound)
+                             rows=rows, mx4=plan.get("mx4"))
