@@ -28,7 +28,6 @@ pages do not fix ("parity unpinned"; only its [5%, 50%] clip is external).
 from . import e4m3, mxfp4  # noqa: F401
 from .tattn import (  # noqa: F401
     SKIP, LOW, FULL, SKIM, skim_operands, block_sizes, pool_means, router, tiers_threshold, tiers_adaptive,
-    head_retention, diagonal_mask, build_lists, quantise_blocks, quantise_values, value_exponents, low_values,
-    attention_forward,
+    head_retention, diagonal_mask, build_lists, quantise_blocks, low_values, attention_forward,
     oracle_plan, oracle_forward, naive_attention, effective_weights,
 )

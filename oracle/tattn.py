@@ -33,8 +33,8 @@ ragged and keep their real sizes.
                                                           fused pass)
 
 Precision: float64 throughout, except that every fp8 code is decided on a
-float32 value and the low tier's dequantised values are rounded to float16
-(the precisions in which the kernel forms them).  Means are
+float32 value and the low tier's dequantised values are formed in float32 and
+rounded to float16 (the precisions in which the kernel forms them).  Means are
 accumulated in float64 and stored as float32.
 """
 import math
@@ -331,37 +331,6 @@ def quantise_blocks(x: np.ndarray, b: int):
     return codes, scale, inv
 
 
-def value_exponents(x: np.ndarray, b: int) -> np.ndarray:
-    """Power-of-two fp8 scale exponent of every block of b rows of V: the
-    smallest integer e with max|X_block| <= 448 * 2^e (the largest E4M3
-    magnitude), 0 for an all-zero block, clamped to [-127, 127].  The codes
-    fill the E4M3 range to within one binade, as amax / 448 would, and the
-    kernel's fp8-to-fp16 conversion applies the scale exactly (it takes a
-    power of two)."""
-    n = x.shape[0]
-    sizes = block_sizes(n, b)
-    e = np.zeros(sizes.size, dtype=np.int64)
-    for j, sz in enumerate(sizes):
-        a = float(np.abs(x[j * b: j * b + sz].astype(np.float64)).max())
-        if a == 0.0:
-            continue
-        f, ex = math.frexp(a / 448.0)            # a / 448 = f * 2^ex, f in [0.5, 1)
-        e[j] = ex - 1 if f == 0.5 else ex         # smallest e with a / 448 <= 2^e
-    return np.clip(e, -127, 127)
-
-
-def quantise_values(v: np.ndarray, b: int):
-    """fp8 E4M3 codes of V with one power-of-two scale 2^e per block of b rows
-    (HierPAS: reduced precision for less critical regions): code =
-    E(v * 2^-e), the scaling exact.  Returns (codes uint8 [n, d], scale f32 =
-    2^e, e int64)."""
-    e = value_exponents(v, b)
-    n = v.shape[0]
-    blk = np.repeat(np.arange(e.size), b)[:n]
-    codes = e4m3.encode(np.ldexp(v.astype(np.float64), -e[blk][:, None]))
-    return codes, np.ldexp(np.ones(e.size), e).astype(np.float32), e
-
-
 def skim_operands(q, k, v):
     """Operands of skim tiles (Triage: skimming in a 4-bit format): Q, K and V
     each quantised to MXFP4 per token row, one E8M0 scale per 32 consecutive
@@ -379,13 +348,12 @@ def skim_operands(q, k, v):
 
 def low_values(v8: np.ndarray, sv: np.ndarray, b: int) -> np.ndarray:
     """Value operand of low-precision tiles: the dequantised E4M3 value
-    decode(code) * scale (exact: the scale is a power of two) rounded once to
-    float16, the precision the kernel multiplies it in (exact inside
-    float16's normal range).  Returns float64 [n, d]."""
+    decode(code) * scale, formed in float32 and rounded to float16 (the
+    precision in which the kernel forms it).  Returns float64 [n, d]."""
     n = v8.shape[0]
     blk = np.repeat(np.arange(-(-n // b)), b)[:n]
-    prod = e4m3.decode(v8) * sv.astype(np.float64)[blk][:, None]
-    return prod.astype(np.float16).astype(np.float64)
+    prod = e4m3.decode(v8).astype(np.float32) * sv.astype(np.float32)[blk][:, None]
+    return prod.astype(np.float32).astype(np.float16).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------- O6/O7
@@ -404,8 +372,8 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     FULL: s_j = <q_i,k_j>/sqrt(d); partial (max s, sum e^{s-m}, sum e^{s-m} v_j).
     LOW:  the same on the E4M3 copies: s^_j = <q^_i,k^_j>/sqrt(d) with
           X^ = decode(X8) * scale (q^, k^ exact in float64), values
-          v^_j = fl16(decode(V8_j) * 2^e_J) (the fp16 value operand the low
-          tier multiplies); partial (max s^, sum e^{s^-m}, sum e^{s^-m} v^_j).
+          v^_j = fl16(fl32(decode(V8_j) * scale_J)) (the fp16 value operand
+          the low tier multiplies); partial (max s^, sum e^{s^-m}, sum e^{s^-m} v^_j).
     SKIM: the same on the MXFP4 copies (``mx4``, from skim_operands): scores
           <q4_i, k4_j>/sqrt(d), values v4_j (Triage: skimming in 4 bits).
     SKIP: sigma = <q_i, k_J>/sqrt(d) + ln n_J; partial (sigma, 1, v_J): one
@@ -582,7 +550,7 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     lists, counts = build_lists(t)
     q8, sq, iq = quantise_blocks(q, bq)
     k8, sk, ik = quantise_blocks(k, bk)
-    v8, sv, ev = quantise_values(v, bk)
+    v8, sv, iv = quantise_blocks(v, bk)
     # the MXFP4 copies, where a SKIM tile needs them
     mx4 = skim_operands(q, k, v) if np.any(t == SKIM) else None
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,

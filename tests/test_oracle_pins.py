@@ -246,43 +246,18 @@ def test_lists_partition_and_order():
         assert np.all(t[i, f] == FULL) and np.all(t[i, lo] == LOW) and np.all(t[i, s] == SKIP)
 
 
-def test_value_exponents_closed_form():
-    """The power-of-two V scale 2^e is the smallest with amax <= 448 * 2^e:
-    amax in (448 * 2^(e-1), 448 * 2^e] gives e; an all-zero block gives 0;
-    the codes then dequantise to within half an E4M3 step and use the top
-    binade of the format."""
+def test_low_values_round_once_to_fp16():
+    """The low tier's value operand is decode(code) * scale rounded to fp16:
+    within half an fp16 ulp of the exact product, and exact when the scale is
+    a power of two (the code values have 4 significant bits)."""
     r = np.random.default_rng(8)
-    for e in list(range(-20, 21)) + [-126, 100]:
-        for amax in (448.0 * 2.0 ** e, np.nextafter(448.0 * 2.0 ** e, 0), 448.0 * 2.0 ** (e - 1) * 1.0000001,
-                     448.0 * 2.0 ** e * r.uniform(0.51, 0.99)):
-            x = np.zeros((64, 4), np.float64)
-            x[5, 2] = -amax
-            x[7] = r.uniform(-1, 1, 4) * amax
-            got = T.value_exponents(x, 64)[0]
-            assert got == e, (e, amax, got)
-    assert T.value_exponents(np.zeros((64, 4)), 64)[0] == 0
-    v = (r.standard_normal((3 * 64, 8)) * np.array([1e-3, 1.0, 300.0]).repeat(64)[:, None]).astype(np.float32)
-    codes, sv, ev = T.quantise_values(v, 64)
-    assert np.array_equal(sv.astype(np.float64), 2.0 ** ev)
-    exact = T.e4m3.decode(codes) * np.repeat(2.0 ** ev, 64)[:, None]
-    big = np.abs(v) >= np.repeat(2.0 ** (ev - 6), 64)[:, None]      # above E4M3's subnormal range
-    assert np.all(np.abs(v - exact)[big] <= 2.0 ** -4 * np.abs(v)[big] * (1 + 1e-12))
-    for j in range(3):
-        assert 224.0 < np.abs(v[64 * j:64 * (j + 1)]).max() / sv[j] <= 448.0
-
-
-def test_low_values_exact_in_fp16_range():
-    """The low tier's value operand is decode(code) * 2^e rounded once to
-    fp16: exact while the product is an fp16 normal (code values have 4
-    significant bits), half an fp16 ulp below it, and infinite beyond 65504."""
-    r = np.random.default_rng(8)
-    codes = r.integers(0, 256, size=(64 * 4, 8)).astype(np.uint8)
-    codes[(codes & 0x7F) == 0x7F] = 0x7E
-    sv = np.ldexp(np.ones(4), [-7, 0, -20, 10]).astype(np.float32)
+    codes = r.integers(0, 256, size=(64 * 3, 8)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    sv = (r.uniform(0.001, 0.05, size=3)).astype(np.float32)
     got = T.low_values(codes, sv, 64)
     exact = T.e4m3.decode(codes) * np.repeat(sv.astype(np.float64), 64)[:, None]
-    normal = (np.abs(exact) >= 2.0 ** -14) & (np.abs(exact) <= 65504)
-    assert np.array_equal(got[normal], exact[normal])
-    sub = np.abs(exact) < 2.0 ** -14
-    assert np.all(np.abs(got[sub] - exact[sub]) <= 2.0 ** -25)
-    assert np.all(np.isinf(got[np.abs(exact) >= 65520]))
+    tol = np.maximum(np.abs(exact) * 2.0 ** -11, 2.0 ** -25)
+    assert np.all(np.abs(got - exact) <= tol * 1.0000001)
+    p2 = np.array([2.0 ** -7, 2.0 ** -3, 1.0], np.float32)
+    assert np.array_equal(T.low_values(codes, p2, 64), T.e4m3.decode(codes) * np.repeat(p2.astype(np.float64), 64)[:, None])
