@@ -141,14 +141,15 @@ __device__ int block_sum_i(int v, Red& r) {
   return s;
 }
 
-// Largest (MAX) or smallest bit pattern among the pv[J] whose bits match
-// `prefix` under `mask`; at least one does.
+// Largest (MAX) or smallest bit pattern among the pv[J] at or above `floor`
+// whose bits match `prefix` under `mask`; at least one does.
 template <bool MAX>
-__device__ uint64_t block_extreme_bits(const double* pv, int n, uint64_t prefix, uint64_t mask, Red& r) {
+__device__ uint64_t block_extreme_bits(const double* pv, int n, uint64_t prefix, uint64_t mask, uint64_t floor,
+                                       Red& r) {
   uint64_t v = MAX ? 0ull : ~0ull;
   for (int J = threadIdx.x; J < n; J += kThreads) {
     const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
-    if ((b & mask) == prefix) v = MAX ? (b > v ? b : v) : (b < v ? b : v);
+    if (b >= floor && (b & mask) == prefix) v = MAX ? (b > v ? b : v) : (b < v ? b : v);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -173,7 +174,9 @@ __device__ uint64_t block_extreme_bits(const double* pv, int n, uint64_t prefix,
 // select; on continuous data this happens after two or three bytes.
 // (Measured against 11-bit digits: 8-bit digits are faster; fewer bins to
 // clear and scan per pass outweigh the contention of the top byte.)
-__device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
+// Values below the bit pattern `floor` are left out; the caller guarantees
+// that the k-th largest is at or above it (0: none left out).
+__device__ uint64_t kth_largest_bits(const double* pv, int n, int k, uint64_t floor, Red& r) {
   uint64_t prefix = 0, mask = 0;
   int kk = k;   // rank of the wanted value among the values matching `prefix`
   const int lane = threadIdx.x & 63;
@@ -186,7 +189,7 @@ __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
       const int one = 1 << (((threadIdx.x >> 6) & 1) * 16);
       for (int J = threadIdx.x; J < n; J += kThreads) {
         const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
-        if ((b & mask) == prefix) atomicAdd(&hw[(b >> sh) & (bins - 1)], one);
+        if (b >= floor && (b & mask) == prefix) atomicAdd(&hw[(b >> sh) & (bins - 1)], one);
       }
     }
     __syncthreads();
@@ -231,23 +234,25 @@ __device__ uint64_t kth_largest_bits(const double* pv, int n, int k, Red& r) {
     kk -= r.sel[1];
     const int cand = r.sel[2];
     __syncthreads();
-    if (sh > 0 && kk == 1) return block_extreme_bits<true>(pv, n, prefix, mask, r);
-    if (sh > 0 && kk == cand) return block_extreme_bits<false>(pv, n, prefix, mask, r);
+    if (sh > 0 && kk == 1) return block_extreme_bits<true>(pv, n, prefix, mask, floor, r);
+    if (sh > 0 && kk == cand) return block_extreme_bits<false>(pv, n, prefix, mask, floor, r);
   }
   return prefix;
 }
 
 // rank(J) < k  <=>  p_J > x_k  or  (p_J == x_k and J is among the first `need`
 // tiles equal to x_k in ascending J), need = k - #{p > x_k}.  Calls
-// mark(J, rank(J) < k) once for every tile; a barrier follows.
+// mark(J, rank(J) < k) once for every tile; a barrier follows.  `floor`: a
+// bit pattern known to be at or below x_k (the select then skips the values
+// under it); returns x_k's bits (0 when k <= 0 or k >= n).
 template <class Mark>
-__device__ void mark_top_k(const double* pv, int n, int k, Mark mark, Red& r) {
+__device__ uint64_t mark_top_k(const double* pv, int n, int k, Mark mark, Red& r, uint64_t floor = 0) {
   if (k >= n || k <= 0) {
     for (int J = threadIdx.x; J < n; J += kThreads) mark(J, k > 0);
     __syncthreads();
-    return;
+    return 0;
   }
-  const uint64_t xb = kth_largest_bits(pv, n, k, r);
+  const uint64_t xb = kth_largest_bits(pv, n, k, floor, r);
   int ge = 0;   // #{p > x} in the low 16 bits, #{p == x} above (n <= 4096)
   for (int J = threadIdx.x; J < n; J += kThreads) {
     const uint64_t b = (uint64_t)__double_as_longlong(pv[J]);
@@ -258,7 +263,7 @@ __device__ void mark_top_k(const double* pv, int n, int k, Mark mark, Red& r) {
   if (need == (ge >> 16)) {   // every tile equal to x is kept: no ordering among them needed
     for (int J = threadIdx.x; J < n; J += kThreads) mark(J, (uint64_t)__double_as_longlong(pv[J]) >= xb);
     __syncthreads();
-    return;
+    return xb;
   }
   int base = 0;   // equal-to-x tiles already seen in earlier chunks
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -280,6 +285,7 @@ __device__ void mark_top_k(const double* pv, int n, int k, Mark mark, Red& r) {
     base += tot;
     __syncthreads();
   }
+  return xb;
 }
 
 // Diagonal tiles of query block I: key blocks whose token range meets I's.
@@ -546,8 +552,10 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
       reinterpret_cast<int*>(a.ws + a.L.kh)[bh] = kh;
       reinterpret_cast<double*>(a.ws + a.L.rh)[bh] = rr;
     }
-    mark_top_k(pv, n, kh, [&](int J, bool kept) { tr[J] = kept ? TATTN_LOW : TATTN_SKIP; }, r);
-    mark_top_k(pv, n, nfull, [&](int J, bool kept) { if (kept) tr[J] = TATTN_FULL; }, r);
+    // the FULL cut (rank nfull <= kh) lies at or above the k_h-th largest, so
+    // its select only counts the values from there up
+    const uint64_t xk = mark_top_k(pv, n, kh, [&](int J, bool kept) { tr[J] = kept ? TATTN_LOW : TATTN_SKIP; }, r);
+    mark_top_k(pv, n, nfull, [&](int J, bool kept) { if (kept) tr[J] = TATTN_FULL; }, r, xk);
     for (int J = threadIdx.x; J < n; J += kThreads) pout[J] = static_cast<float>(pv[J]);
   }
   __syncthreads();
