@@ -55,6 +55,10 @@ def test_valid_configs(lib):
     assert status(lib, good(tau_skim=0.001)) == 0                        # tau_skim == tau_lo
     assert status(lib, good(mode="external", tau_skim=1e-4)) == 0
     assert status(lib, good(mode="adaptive", block_q=64, block_k=16, tau_skim=1e-4)) == 0   # ignored there
+    # the price router weighs SKIM by its error model: no ordering against tau_lo
+    assert status(lib, good(mode="price", price=0.01, tau_skim=0.5)) == 0
+    assert status(lib, good(mode="price", price=0.01, tau_skim=-1e-4)) == -1
+    assert status(lib, good(mode="price", price=0.01, tau_skim=1e-4, block_q=64, block_k=16)) == -2
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -120,6 +124,11 @@ def test_workspace_formula(lib):
     # ... and only where a SKIM tile can occur
     assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="all_full", tau_skim=1e-4)), ctypes.byref(k)) == 0
     assert k.value == n.value
+    # the price router with SKIM holds both the moments and the MXFP4 copies
+    pk, sk = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="price", price=0.01, tau_skim=1e-4)), ctypes.byref(pk)) == 0
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(tau_skim=1e-4)), ctypes.byref(sk)) == 0
+    assert pk.value - m.value == sk.value - n.value
 
 
 def test_plan_rejects_bad_pointers_before_any_launch(lib):
