@@ -76,6 +76,29 @@ def load_traffic(workload):
     return t.get("bytes_per_launch")
 
 
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_vendor():
+    """The BLAS library numpy was built against, as numpy reports it."""
+    import numpy as np
+    try:
+        info = np.show_config(mode="dicts")
+        blas = info.get("Build Dependencies", {}).get("blas", {})
+        return f"{blas.get('name', 'unknown')} {blas.get('version', '')}".strip()
+    except Exception:   # older numpy without mode="dicts"
+        return "unknown"
+
+
 def cpu_baseline(g, cfg, budget_s, price=None):
     """Time the oracle (plan + forward) on one head: its full router, then as
     many query blocks as fit in the budget.  Returns dense-equivalent TFLOP/s
@@ -112,7 +135,7 @@ def cpu_baseline(g, cfg, budget_s, price=None):
     dense = 4.0 * rows * N * d
     threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
     return {"value": dense / t_sample / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(), "blas": _blas_vendor(),
             "sample": f"head 0 of {cfg.heads}: full router ({t_plan:.2f}s, charged pro rata) + {blocks} of "
                       f"{cfg.n_qblocks} query blocks ({rows} rows) forward in {t_fwd:.2f}s; numpy float64, "
                       f"BLAS threads={threads}"}
