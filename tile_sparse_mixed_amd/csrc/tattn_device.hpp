@@ -36,14 +36,12 @@ constexpr float kLog2_448 = 8.807354922057604f;
 //   key(b, r, h) = 32b + 8(r/4) + 4h + r%4,
 // i.e. P value number p = 16b + r of that lane.  The P.V contraction uses the
 // lane's own P values as the B operand, so V must be stored with the same key
-// order:
-//   fp8  (K = 64 per instruction): byte 32h + p of a transposed V row.
-//   bf16 (K = 16 per instruction, chunk c = p/8): element (2c + h)*8 + p%8.
+// order: with K = 16 per instruction (chunk c = p/8), element (2c + h)*8 + p%8
+// of a transposed V row.
 __host__ __device__ inline int key_p(int key) {  // P index inside its lane half
   return 16 * (key >> 5) + 4 * ((key >> 3) & 3) + (key & 3);
 }
 __host__ __device__ inline int key_h(int key) { return (key >> 2) & 1; }
-__host__ __device__ inline int v8_pos(int key) { return 32 * key_h(key) + key_p(key); }
 __host__ __device__ inline int vt_pos(int key) {
   const int p = key_p(key);
   return (2 * (p >> 3) + key_h(key)) * 8 + (p & 7);
@@ -89,11 +87,6 @@ template <bool HI>
 __device__ inline int cvt_fp8x2(float a, float b, int old) {
   a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
   b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-}
-// Same, for values already known to lie in [0, 448 * (1 + 2^-20)].
-template <bool HI>
-__device__ inline int cvt_fp8x2_nosat(float a, float b, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
