@@ -19,15 +19,20 @@ Each function names the passage of the pages it follows:
     4-bit format (here OCP MXFP4, oracle/mxfp4.py).
 Formulas the pages leave open follow the readings listed with the design
 (block-mean router with +ln n_J; the low tier quantises Q, K, V to E4M3 with
-one scale per block and keeps the probabilities in the accumulation path).
+one scale per block and its probabilities to E4M3 against the tile-local row
+maximum times 448, and sums those quantised probabilities into the row
+normaliser).
 
 Parity status: every function is pinned by tests/test_oracle_*.py except the
 entropy -> retention-ratio mapping of the head-adaptive mode, whose formula the
-pages do not fix ("parity unpinned"; only its [5%, 50%] clip is external).
+pages do not fix ("parity unpinned"; only its [5%, 50%] clip is external), and
+the price router's error model as a predictor (its exact identities and its
+derivation are pinned, its accuracy as a predictor is not: "parity unpinned").
 """
 from . import e4m3, mxfp4  # noqa: F401
 from .tattn import (  # noqa: F401
     SKIP, LOW, FULL, SKIM, skim_operands, block_sizes, pool_means, router, tiers_threshold, tiers_adaptive,
-    head_retention, diagonal_mask, build_lists, quantise_blocks, low_values, attention_forward,
+    head_retention, diagonal_mask, build_lists, quantise_blocks, dequantise, quantised_probabilities, low_scores,
+    attention_forward,
     oracle_plan, oracle_forward, naive_attention, effective_weights,
 )

@@ -32,10 +32,19 @@ ragged and keep their real sizes.
                                                           block means, one
                                                           fused pass)
 
+A low-precision tile (LOW, and the 4-bit SKIM tier) runs its whole tile on
+8-bit operands: scores from the E4M3 (or MXFP4) copies of q and k, the tile's
+probabilities quantised to E4M3 against the tile-local row maximum
+(pi_j = decode(E(fl32(448 e^{s_j - m_t}))) / 448, so the maximum lands on 448
+exactly and a tile's codes do not depend on the order tiles are visited in),
+values from the E4M3 copy of V, v^ = fl32(decode(code) * scale); the tile's
+share of the row normaliser sums the same pi (HierPAS: progressively reduced
+precision; APT: dual-precision execution).
+
 Precision: float64 throughout, except that every fp8 code is decided on a
-float32 value and the low tier's dequantised values are formed in float32 and
-rounded to float16 (the precisions in which the kernel forms them).  Means are
-accumulated in float64 and stored as float32.
+float32 value (the value the kernel converts) and the dequantised E4M3 values
+are products rounded once to float32.  Means are accumulated in float64 and
+stored as float32.
 """
 import math
 
@@ -169,8 +178,10 @@ def tiers_adaptive(p: np.ndarray, k_h: int, full_frac: float) -> np.ndarray:
 
 E4M3_U = 2.0 ** -4          # largest relative rounding error of an E4M3 normal value
 MXFP4_U = 2.0 ** -2         # largest relative rounding error of an E2M1 normal value
-COST_FULL, COST_LOW = 1.0, 0.75   # bf16-equivalent MFMA work per tile: LOW = fp8 scores (half) + fp16 P.V
-COST_SKIM = 0.625           # SKIM = fp4 scores (a quarter) + fp16 P.V
+# bf16-equivalent MFMA work per tile, at the matrix rates (fp8 twice, fp4 four
+# times the bf16 rate): LOW = fp8 scores + fp8 P.V; SKIM = fp4 scores + fp8 P.V
+COST_FULL, COST_LOW = 1.0, 0.5
+COST_SKIM = 0.375
 
 
 def cost_skip(bk: int) -> float:
@@ -232,9 +243,10 @@ def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d, skim=False):
             noise of RMS u sqrt(m2v/3):
             eL = vnorm expm1(sl2/2)
                  + (sqrt(vvar expm1(sl2)) + u sqrt(m2v/3)) / sqrt(n_eff).
-      SKIM  (MXFP4 copies, with skim=True): the same form with E2M1's bound
-            u = 2^-2 in place of E4M3's 2^-4 (its rounding is relative to the
-            32-element block's scale, and the relative bound covers it).
+      SKIM  (MXFP4 scores, with skim=True): the same form with E2M1's bound
+            u = 2^-2 in place of E4M3's 2^-4 in the score noise sk2 (its
+            rounding is relative to the 32-element block's scale, and the
+            relative bound covers it); its values are E4M3 as in LOW.
     The norm of the block mean stands in for the distance between the tile's
     output and the row's.  Returns (s2, g, eS, eL), and eK after them with
     skim=True."""
@@ -254,7 +266,7 @@ def tile_error_model(q2, m2q, kvar, m2k, vvar, m2v, vnorm, n_k, d, skim=False):
     if not skim:
         return s2, g, eS, eL
     sk2 = (2.0 * MXFP4_U ** 2 / 3.0) * np.outer(m2q.astype(np.float64), m2k.astype(np.float64)) / float(d * d)
-    eK = vn * np.expm1(0.5 * sk2) + (np.sqrt(vv * np.expm1(sk2)) + MXFP4_U * np.sqrt(mv / 3.0)) / np.sqrt(neff)
+    eK = vn * np.expm1(0.5 * sk2) + (np.sqrt(vv * np.expm1(sk2)) + E4M3_U * np.sqrt(mv / 3.0)) / np.sqrt(neff)
     return s2, g, eS, eL, eK
 
 
@@ -331,29 +343,50 @@ def quantise_blocks(x: np.ndarray, b: int):
     return codes, scale, inv
 
 
-def skim_operands(q, k, v):
-    """Operands of skim tiles (Triage: skimming in a 4-bit format): Q, K and V
-    each quantised to MXFP4 per token row, one E8M0 scale per 32 consecutive
-    channels.  Scores use the dequantised q and k exactly; the value operand is
-    the dequantised v rounded to float16 (the precision the kernel multiplies
-    it in; exact unless it falls outside float16's normal range).  Returns a
-    dict of the dequantised operands (float64 [n, d]) and the codes and scale
-    bytes of k and v."""
+def skim_operands(q, k):
+    """Score operands of skim tiles (Triage: skimming a tile in a 4-bit
+    format): Q and K each quantised to MXFP4 per token row, one E8M0 scale per
+    32 consecutive channels; the scores use the dequantised values exactly.
+    (A skim tile's probabilities and values are those of the low tier: see
+    quantised_probabilities.)  Returns a dict of the dequantised operands
+    (float64 [n, d]) and the codes and scale bytes of k."""
     _, _, qd = mxfp4.quantise(q)
     kc, ks, kd = mxfp4.quantise(k)
-    vc, vs, vd = mxfp4.quantise(v)
-    return dict(q=qd, k=kd, v=vd.astype(np.float16).astype(np.float64), k_codes=kc, k_scales=ks,
-                v_codes=vc, v_scales=vs)
+    return dict(q=qd, k=kd, k_codes=kc, k_scales=ks)
 
 
-def low_values(v8: np.ndarray, sv: np.ndarray, b: int) -> np.ndarray:
-    """Value operand of low-precision tiles: the dequantised E4M3 value
-    decode(code) * scale, formed in float32 and rounded to float16 (the
-    precision in which the kernel forms it).  Returns float64 [n, d]."""
-    n = v8.shape[0]
+def dequantise(codes: np.ndarray, scale: np.ndarray, b: int) -> np.ndarray:
+    """X^ = fl32(decode(code) * scale) with the scale of each row's block of b
+    rows.  Returns float64 [n, d] (values representable in float32)."""
+    n = codes.shape[0]
     blk = np.repeat(np.arange(-(-n // b)), b)[:n]
-    prod = e4m3.decode(v8).astype(np.float32) * sv.astype(np.float32)[blk][:, None]
-    return prod.astype(np.float32).astype(np.float16).astype(np.float64)
+    return (e4m3.decode(codes).astype(np.float32) * scale.astype(np.float32)[blk][:, None]).astype(np.float64)
+
+
+P_MAX = 448.0   # E4M3's largest finite value: the tile maximum's probability code
+
+
+def quantised_probabilities(s: np.ndarray):
+    """Probabilities of a low-precision tile (HierPAS: reduced precision for
+    less critical tiles), quantised to E4M3 against the tile-local row maximum:
+      m_t  = max_j s_j over the tile's keys (per query row; s float64, -inf
+             marks a key past the end of the sequence),
+      x_j  = fl32(448 e^{s_j - m_t})            (the maximum lands on 448),
+      c_j  = E(x_j)                             (round to nearest even),
+      pi_j = decode(c_j) / 448.
+    s: [..., n] scores of one tile per leading index.  Returns (m_t, x, c, pi)
+    with x float64 (float32 values), c uint8 and pi float64."""
+    mt = s.max(axis=-1)
+    x = (P_MAX * np.exp(s - mt[..., None])).astype(np.float32).astype(np.float64)
+    c = e4m3.encode(x)
+    return mt, x, c, e4m3.decode(c) / P_MAX
+
+
+def low_scores(qc: np.ndarray, sq: float, kc: np.ndarray, sk: float, d: int) -> np.ndarray:
+    """Scores of a LOW tile from the E4M3 copies: s^_ij = <q^_i, k^_j>/sqrt(d)
+    with q^ = decode(q8) sq and k^ = decode(k8) sk taken exactly (float64).
+    qc: [m, d] and kc: [n, d] decoded code values."""
+    return (qc @ kc.T) * (float(sq) * float(sk) / math.sqrt(d))
 
 
 # ----------------------------------------------------------------------------- O6/O7
@@ -365,23 +398,27 @@ def _padded(x, nb, b):
 
 
 def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
-                      rows=None, return_partials=False, mx4=None):
+                      rows=None, return_partials=False, mx4=None, p_codes=None):
     """One pass over all tiles of every query row, merging per-tile partials
     exactly (Triage: skip, low precision and full tiles in a single pass).
 
     FULL: s_j = <q_i,k_j>/sqrt(d); partial (max s, sum e^{s-m}, sum e^{s-m} v_j).
-    LOW:  the same on the E4M3 copies: s^_j = <q^_i,k^_j>/sqrt(d) with
-          X^ = decode(X8) * scale (q^, k^ exact in float64), values
-          v^_j = fl16(fl32(decode(V8_j) * scale_J)) (the fp16 value operand
-          the low tier multiplies); partial (max s^, sum e^{s^-m}, sum e^{s^-m} v^_j).
-    SKIM: the same on the MXFP4 copies (``mx4``, from skim_operands): scores
-          <q4_i, k4_j>/sqrt(d), values v4_j (Triage: skimming in 4 bits).
+    LOW:  scores s^_j from the E4M3 copies (low_scores), probabilities
+          quantised against the tile max (quantised_probabilities), values
+          v^_j = fl32(decode(V8_j) * sv_J); partial (m_t, sum pi_j, sum pi_j v^_j).
+    SKIM: the same with scores from the MXFP4 copies (``mx4``, skim_operands):
+          <q4_i, k4_j>/sqrt(d) (Triage: skimming in 4 bits); probabilities and
+          values as in LOW.
     SKIP: sigma = <q_i, k_J>/sqrt(d) + ln n_J; partial (sigma, 1, v_J): one
           score weighted by n_J, valued by the block mean (Triage).
     Merge: M = max m; O_i = sum o e^{m-M} / sum l e^{m-M}.
 
     q, k, v: [n, d] (values as float64); t: tier map [Nq, Nk].
     ``rows`` restricts the computation to those query blocks (others left 0).
+    ``p_codes``: optional {(I, J): uint8 [m_I, n_J]} probability codes used in
+    place of the quantised ones for those LOW / SKIM tiles (a tile's codes are
+    not unique where x_j lies on a rounding midpoint to within the precision
+    of its scores; the caller decides which codes are admissible).
     Returns O float64 [n, d] (and the per-row partial lists if requested)."""
     n, d = q.shape
     nq, nk = t.shape
@@ -390,17 +427,29 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     valid = np.arange(bk)[None, :] < ksz[:, None]                      # [Nk, Bk]
     Kp = _padded(k.astype(np.float64), nk, bk)
     Vp = _padded(v.astype(np.float64), nk, bk)
-    kblk = np.repeat(np.arange(nk), bk)[:n]
-    qblk = np.repeat(np.arange(nq), bq)[:n]
     Kh = _padded(e4m3.decode(k8), nk, bk)                              # code values
-    Vh = _padded(low_values(v8, sv, bk), nk, bk)
+    Vh = _padded(dequantise(v8, sv, bk), nk, bk)
     Qc = e4m3.decode(q8)
     if np.any(t == SKIM):
-        Kq, Vq = _padded(mx4["k"], nk, bk), _padded(mx4["v"], nk, bk)
+        Kq = _padded(mx4["k"], nk, bk)
     kb64, vb64 = kbar.astype(np.float64), vbar.astype(np.float64)
     lnk = np.log(ksz.astype(np.float64))
     out = np.zeros((n, d), dtype=np.float64)
     partials = {}
+
+    def quantised_partial(i, Js, s):
+        """(m_t, sum pi, sum pi v^) of the quantised tiles Js of row i; s [m, nJ, bk]."""
+        mt, _, c, pi = quantised_probabilities(np.where(valid[Js][None], s, -np.inf))
+        if p_codes is not None:
+            for a, J in enumerate(Js):
+                if (i, int(J)) in p_codes:
+                    c[:, a, :] = 0
+                    cc = np.asarray(p_codes[(i, int(J))], np.uint8)
+                    c[:, a, :cc.shape[1]] = cc
+                    pi[:, a, :] = e4m3.decode(c[:, a, :]) / P_MAX
+        pi = np.where(valid[Js][None], pi, 0.0)
+        return mt, pi.sum(axis=2), np.matmul(pi.transpose(1, 0, 2), Vh[Js]).transpose(1, 0, 2)
+
     for i in (range(nq) if rows is None else rows):
         r0, r1 = i * bq, min(n, (i + 1) * bq)
         Q = q[r0:r1].astype(np.float64)
@@ -418,22 +467,17 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
         if L.size:
             raw = (Qc[r0:r1] @ Kh[L].reshape(-1, d).T).reshape(r1 - r0, L.size, bk)
             sc = float(sq[i]) * sk.astype(np.float64)[L] * isd            # [nL]
-            sh = raw * sc[None, :, None]
-            sh = np.where(valid[L][None], sh, -np.inf)
-            mt = sh.max(axis=2)
-            e = np.exp(sh - mt[..., None])
-            ms.append(mt)
-            ls.append(e.sum(axis=2))
-            os_.append(np.matmul(e.transpose(1, 0, 2), Vh[L]).transpose(1, 0, 2))
+            m, l, o = quantised_partial(i, L, raw * sc[None, :, None])
+            ms.append(m)
+            ls.append(l)
+            os_.append(o)
         K4 = np.nonzero(t[i] == SKIM)[0]
         if K4.size:
             s = (mx4["q"][r0:r1] @ Kq[K4].reshape(-1, d).T).reshape(r1 - r0, K4.size, bk) * isd
-            s = np.where(valid[K4][None], s, -np.inf)
-            m = s.max(axis=2)
-            e = np.exp(s - m[..., None])
+            m, l, o = quantised_partial(i, K4, s)
             ms.append(m)
-            ls.append(e.sum(axis=2))
-            os_.append(np.matmul(e.transpose(1, 0, 2), Vq[K4]).transpose(1, 0, 2))
+            ls.append(l)
+            os_.append(o)
         Sk = np.nonzero(t[i] == SKIP)[0]
         skip_sigma = None
         if Sk.size:
@@ -461,44 +505,55 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
 
 def effective_weights(q, k, v, t, bq, bk, kbar, q8, sq, k8, sk, v8, sv, mx4=None):
     """Dense [n, n] weight matrix W of the method on tiny inputs, together with
-    the value matrix each weight multiplies: FULL W_ij = e^{s_ij-M}/L against
-    v_j; LOW W_ij = e^{s^_ij-M}/L against v^_j; SKIM W_ij = e^{s4_ij-M}/L
-    against v4_j; SKIP W_ij = e^{sigma-M}/(n_J L) against v_j.  Then
-    O = rowsum(W * Vsel)."""
+    the value matrix each weight multiplies, built one query row and one tile
+    at a time with scalar bookkeeping:
+      FULL  w_j = e^{s_j - M} against v_j,
+      LOW   w_j = pi_j e^{m_t - M} against v^_j (scores from the E4M3 copies),
+      SKIM  the same with scores from the MXFP4 copies,
+      SKIP  w_j = e^{sigma - M} / n_J for every j in J, against v_j,
+    with M the largest of the row's FULL scores, LOW / SKIM tile maxima and
+    SKIP scores, and W = w / sum w.  Then O = rowsum(W * Vsel)."""
     n, d = q.shape
     nq, nk = t.shape
     isd = 1.0 / math.sqrt(d)
     ksz = block_sizes(n, bk)
-    kblk = np.repeat(np.arange(nk), bk)[:n]
     qblk = np.repeat(np.arange(nq), bq)[:n]
     khat = e4m3.decode(k8)
-    vhat = low_values(v8, sv, bk)
+    vhat = dequantise(v8, sv, bk)
     qc = e4m3.decode(q8)
     W = np.zeros((n, n))
-    sel_low = np.zeros((n, n), dtype=bool)
-    sel_skim = np.zeros((n, n), dtype=bool)
+    sel_q = np.zeros((n, n), dtype=bool)
     for i in range(n):
         I = qblk[i]
-        logits = np.full(n, -np.inf)
+        refs, terms = [], []          # per tile: (reference m, list of (j, factor))
         for J in range(nk):
             j0, j1 = J * bk, J * bk + ksz[J]
-            if t[I, J] == FULL:
-                logits[j0:j1] = (k[j0:j1] @ q[i]) * isd
-            elif t[I, J] == SKIP:
-                sig = float(q[i] @ kbar[J].astype(np.float64)) * isd + math.log(ksz[J])
-                logits[j0:j1] = sig - math.log(ksz[J])
-            elif t[I, J] == SKIM:
-                logits[j0:j1] = (mx4["k"][j0:j1] @ mx4["q"][i]) * isd
-                sel_skim[i, j0:j1] = True
+            tier = t[I, J]
+            if tier == FULL:
+                s = (k[j0:j1].astype(np.float64) @ q[i].astype(np.float64)) * isd
+                m = float(s.max())
+                refs.append(m)
+                terms.append([(j0 + a, math.exp(float(s[a]) - m)) for a in range(j1 - j0)])
+            elif tier == SKIP:
+                sig = float(q[i].astype(np.float64) @ kbar[J].astype(np.float64)) * isd + math.log(ksz[J])
+                refs.append(sig)
+                terms.append([(j0 + a, 1.0 / ksz[J]) for a in range(j1 - j0)])
             else:
-                logits[j0:j1] = (khat[j0:j1] @ qc[i]) * float(sq[I]) * float(sk[J]) * isd
-                sel_low[i, j0:j1] = True
-        M = logits.max()
-        w = np.exp(logits - M)
-        W[i] = w / w.sum()
-    vsel = np.where(sel_low[:, :, None], vhat[None, :, :], v[None, :, :].astype(np.float64))
-    if mx4 is not None:
-        vsel = np.where(sel_skim[:, :, None], mx4["v"][None, :, :], vsel)
+                if tier == SKIM:
+                    s = (mx4["k"][j0:j1] @ mx4["q"][i]) * isd
+                else:
+                    s = low_scores(qc[i:i + 1], sq[I], khat[j0:j1], sk[J], d)[0]
+                m, _, _, pi = quantised_probabilities(s)
+                refs.append(float(m))
+                terms.append([(j0 + a, float(pi[a])) for a in range(j1 - j0)])
+                sel_q[i, j0:j1] = True
+        M = max(refs)
+        for m, tl in zip(refs, terms):
+            f = math.exp(m - M)
+            for j, w in tl:
+                W[i, j] = w * f
+        W[i] /= W[i].sum()
+    vsel = np.where(sel_q[:, :, None], vhat[None, :, :], v[None, :, :].astype(np.float64))
     return W, vsel
 
 
@@ -552,7 +607,7 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     k8, sk, ik = quantise_blocks(k, bk)
     v8, sv, iv = quantise_blocks(v, bk)
     # the MXFP4 copies, where a SKIM tile needs them
-    mx4 = skim_operands(q, k, v) if np.any(t == SKIM) else None
+    mx4 = skim_operands(q, k) if np.any(t == SKIM) else None
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
                 q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info, mx4=mx4)
 
@@ -565,7 +620,7 @@ def oracle_replan(q, k, v, prev_plan, cfg_like):
     return oracle_plan(q, k, v, cfg_like, mode=3, external_tiers=prev_plan["tiers"])
 
 
-def oracle_forward(q, k, v, plan, bq, bk, rows=None):
+def oracle_forward(q, k, v, plan, bq, bk, rows=None, p_codes=None):
     return attention_forward(q, k, v, plan["tiers"], bq, bk, plan["kbar"], plan["vbar"],
                              plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],
-                             rows=rows, mx4=plan.get("mx4"))
+                             rows=rows, mx4=plan.get("mx4"), p_codes=p_codes)

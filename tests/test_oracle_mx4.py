@@ -129,17 +129,40 @@ def _plan_and_fwd(q, k, v, bq, bk, t):
     return plan, o
 
 
-def test_skim_on_representable_inputs_is_exact_attention():
+def test_skim_scores_on_representable_inputs_are_exact():
+    """On inputs MXFP4 keeps exactly, a SKIM tile's scores are the exact
+    scores: its partial equals the low tier's quantised-probability partial
+    (codes against the tile maximum, E4M3 values) computed here from the
+    unquantised q and k, tile by tile.  (The forward runs the map as given,
+    diagonal tiles included.)"""
     r = np.random.default_rng(7)
     n, d, bq, bk = 200, 64, 64, 16          # ragged last blocks
     q = _representable(r, n, d, -8, -4)
     k, v = _representable(r, n, d, -4, -1), _representable(r, n, d, -3, 0)
     nq, nk = -(-n // bq), -(-n // bk)
-    plan, o = _plan_and_fwd(q, k, v, bq, bk, np.full((nq, nk), SKIM, np.uint8))
-    for x, name in ((q, "q"), (k, "k"), (v, "v")):
+    t = np.full((nq, nk), SKIM, np.uint8)
+    plan, o = _plan_and_fwd(q, k, v, bq, bk, t)
+    for x, name in ((q, "q"), (k, "k")):
         assert np.array_equal(plan["mx4"][name], x.astype(np.float64))
-    ref = T.naive_attention(q, k, v)
-    assert np.max(np.abs(o - ref)) < 1e-12
+    vh = T.dequantise(plan["v8"], plan["sv"], bk)
+    isd = 1.0 / np.sqrt(d)
+    for i in range(0, n, 7):
+        I = i // bq
+        refs, nums, dens = [], [], []
+        for J in range(nk):
+            j0, j1 = J * bk, min(n, (J + 1) * bk)
+            s = (k[j0:j1].astype(np.float64) @ q[i].astype(np.float64)) * isd
+            if t[I, J] == FULL:
+                m = s.max()
+                e = np.exp(s - m)
+                refs.append(m); dens.append(e.sum()); nums.append(e @ v[j0:j1].astype(np.float64))
+            else:
+                m, _, _, pi = T.quantised_probabilities(s)
+                refs.append(m); dens.append(pi.sum()); nums.append(pi @ vh[j0:j1])
+        M = max(refs)
+        w = np.exp(np.array(refs) - M)
+        ref = (w[:, None] * np.array(nums)).sum(0) / (w * np.array(dens)).sum()
+        assert np.max(np.abs(o[i] - ref)) < 1e-12, i
 
 
 def test_skim_differs_from_full_on_general_inputs():

@@ -1,5 +1,7 @@
 """Pins of the attention oracle to closed forms, identities and hand-worked
-examples (P1, P2, P3, P5, P7, P8 and the fp8 error bound)."""
+examples (P1, P2, P3, P5, P7, P8, the fp8 error bound, and the low tier's
+quantised probabilities against a hand-worked tile and a scalar-loop
+recomputation)."""
 import math
 import os
 from types import SimpleNamespace
@@ -28,7 +30,7 @@ def fwd(q, k, v, plan, c, tiers=None, rows=None):
     t = plan["tiers"] if tiers is None else tiers
     return T.attention_forward(q, k, v, t, c.block_q, c.block_k, plan["kbar"], plan["vbar"],
                                plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],
-                               rows=rows)
+                               rows=rows, mx4=plan.get("mx4"))
 
 
 def _read(name):
@@ -246,18 +248,132 @@ def test_lists_partition_and_order():
         assert np.all(t[i, f] == FULL) and np.all(t[i, lo] == LOW) and np.all(t[i, s] == SKIP)
 
 
-def test_low_values_round_once_to_fp16():
-    """The low tier's value operand is decode(code) * scale rounded to fp16:
-    within half an fp16 ulp of the exact product, and exact when the scale is
-    a power of two (the code values have 4 significant bits)."""
+def test_dequantise_rounds_once_to_fp32():
+    """The low tier's value operand is decode(code) * scale rounded once to
+    float32: within half a float32 ulp of the exact product, and exact when
+    the scale is a power of two (the code values have 4 significant bits)."""
     r = np.random.default_rng(8)
     codes = r.integers(0, 256, size=(64 * 3, 8)).astype(np.uint8)
     codes[codes == 0x7F] = 0x7E
     codes[codes == 0xFF] = 0xFE
     sv = (r.uniform(0.001, 0.05, size=3)).astype(np.float32)
-    got = T.low_values(codes, sv, 64)
+    got = T.dequantise(codes, sv, 64)
     exact = T.e4m3.decode(codes) * np.repeat(sv.astype(np.float64), 64)[:, None]
-    tol = np.maximum(np.abs(exact) * 2.0 ** -11, 2.0 ** -25)
+    tol = np.abs(exact) * 2.0 ** -24
     assert np.all(np.abs(got - exact) <= tol * 1.0000001)
+    assert not np.array_equal(got, exact)             # the rounding happens
     p2 = np.array([2.0 ** -7, 2.0 ** -3, 1.0], np.float32)
-    assert np.array_equal(T.low_values(codes, p2, 64), T.e4m3.decode(codes) * np.repeat(p2.astype(np.float64), 64)[:, None])
+    assert np.array_equal(T.dequantise(codes, p2, 64), T.e4m3.decode(codes) * np.repeat(p2.astype(np.float64), 64)[:, None])
+
+
+def test_low_hand_example():
+    """A hand-worked LOW tile (tests/golden/low_hand_example.txt): the codes of
+    its probabilities and the merged output."""
+    g = _read("low_hand_example.txt")
+    q = np.array(g["q"], np.float32)
+    k = np.array(g["k"], np.float32)
+    v = np.array(g["v"], np.float32)
+    c = cfg(2, 2)
+    t = np.array([[FULL, LOW], [LOW, FULL]], np.uint8)
+    plan = T.oracle_plan(q, k, v, c, mode=3, external_tiers=t)
+    assert plan["sq"][0] == np.float32(2.0 ** -8) and plan["sk"][1] == np.float32(2.0 ** -8)
+    s = T.low_scores(T.e4m3.decode(plan["q8"][0:2]), plan["sq"][0], T.e4m3.decode(plan["k8"][2:4]),
+                     plan["sk"][1], 4)
+    _, _, codes, _ = T.quantised_probabilities(s)
+    assert codes[0].tolist() == [int(x) for x in g["codes01_row0"][0]]
+    o = fwd(q, k, v, plan, c)
+    assert abs(o[0, 0] - g["O0"][0][0]) < 1e-12
+
+
+def _scalar_e4m3():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("e4m3pins", os.path.join(os.path.dirname(__file__),
+                                                                           "test_oracle_e4m3.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod._bitwise_rne_e4m3
+
+
+@pytest.mark.parametrize("n,d,bq,bk", [(96, 16, 32, 16), (70, 8, 32, 32)])
+def test_low_partials_against_scalar_loops(n, d, bq, bk):
+    """Every LOW tile's partial (m_t, sum pi, sum pi v^) against explicit loops:
+    scores summed term by term from the decoded codes, the tile maximum, x =
+    float32(448 e^{s - m_t}) encoded by the bitwise E4M3 encoder of the codec
+    pins, values decode(code) * scale rounded to float32."""
+    import struct
+    enc = _scalar_e4m3()
+    q, k, v = rand_qkv(n, d, 31 + n, scale=1.4)
+    c = cfg(bq, bk)
+    nq, nk = -(-n // bq), -(-n // bk)
+    t = np.full((nq, nk), LOW, np.uint8)
+    plan = T.oracle_plan(q, k, v, c, mode=3, external_tiers=t)
+    t = plan["tiers"]
+    _, parts = T.attention_forward(q, k, v, t, bq, bk, plan["kbar"], plan["vbar"], plan["q8"], plan["sq"],
+                                   plan["k8"], plan["sk"], plan["v8"], plan["sv"], return_partials=True)
+    dec = T.e4m3.DECODE
+    f32 = lambda x: struct.unpack("<f", struct.pack("<f", x))[0]
+    for I in range(nq):
+        ms, ls, os_, _, _, _ = parts[I]
+        lows = [J for J in range(nk) if t[I, J] == LOW]
+        if not lows:
+            continue
+        m_low, l_low, o_low = ms[-1], ls[-1], os_[-1]             # LOW is the last kept group here
+        for a, J in enumerate(lows):
+            keys = range(J * bk, min(n, (J + 1) * bk))
+            for ii, i in enumerate(range(I * bq, min(n, (I + 1) * bq))):
+                s = []
+                for j in keys:
+                    acc = 0.0
+                    for x in range(d):
+                        acc += dec[plan["q8"][i, x]] * dec[plan["k8"][j, x]]
+                    s.append(acc * float(plan["sq"][I]) * float(plan["sk"][J]) / math.sqrt(d))
+                mt = max(s)
+                pis = [dec[enc(f32(448.0 * math.exp(sj - mt)))] / 448.0 for sj in s]
+                assert max(pis) == 1.0                               # the maximum lands on 448
+                vh = [[f32(dec[plan["v8"][j, x]] * float(plan["sv"][J])) for x in range(d)] for j in keys]
+                assert abs(m_low[ii, a] - mt) <= 1e-12 * max(1.0, abs(mt))
+                assert abs(l_low[ii, a] - sum(pis)) <= 1e-12
+                ov = [sum(p * vh[jj][x] for jj, p in enumerate(pis)) for x in range(d)]
+                assert np.max(np.abs(o_low[ii, a] - np.array(ov))) <= 1e-12
+
+
+def test_quantised_probabilities_structure():
+    """Codes of a quantised tile: the maximum is code 0x7E (448) in every row,
+    codes are monotone in the scores, keys past the sequence end get code 0,
+    and each x lies within half an E4M3 step of its code's value."""
+    r = np.random.default_rng(12)
+    s = r.standard_normal((40, 64)) * 3.0
+    s[:, 50:] = -np.inf
+    mt, x, c, pi = T.quantised_probabilities(s)
+    assert np.all(c.max(axis=1) == 0x7E) and np.all(pi.max(axis=1) == 1.0)
+    assert np.all(c[:, 50:] == 0) and np.all(pi[:, 50:] == 0)
+    for row in range(40):
+        o = np.argsort(s[row, :50])
+        assert np.all(np.diff(c[row, :50][o].astype(int)) >= 0)
+    val = T.e4m3.decode(c)
+    # half a step: 2^-4 relative for normals (>= 2^-6), 2^-10 absolute below
+    tol = np.maximum(np.abs(val) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(x - val) <= tol * 1.0000001)
+
+
+def test_p_codes_override():
+    """Given its own codes the forward is unchanged; a code moved to the
+    neighbouring E4M3 value changes only that tile's row."""
+    n, d, bq, bk = 128, 16, 32, 32
+    q, k, v = rand_qkv(n, d, 41, scale=1.3)
+    c = cfg(bq, bk)
+    t = np.full((4, 4), LOW, np.uint8)
+    plan = T.oracle_plan(q, k, v, c, mode=3, external_tiers=t)
+    t = plan["tiers"]
+    o = fwd(q, k, v, plan, c)
+    s = T.low_scores(T.e4m3.decode(plan["q8"][0:32]), plan["sq"][0], T.e4m3.decode(plan["k8"][64:96]),
+                     plan["sk"][2], d)
+    codes = T.quantised_probabilities(s)[2]
+    o_same = T.oracle_forward(q, k, v, plan, bq, bk, p_codes={(0, 2): codes})
+    assert np.array_equal(o, o_same)
+    alt = codes.copy()
+    j = int(np.argmax(codes[5] < 0x7E))
+    alt[5, j] += 1
+    o_alt = T.oracle_forward(q, k, v, plan, bq, bk, p_codes={(0, 2): alt})
+    diff = np.abs(o_alt - o).max(axis=1)
+    assert diff[5] > 0 and np.all(diff[np.arange(n) != 5] == 0)

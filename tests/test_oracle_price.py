@@ -243,7 +243,7 @@ def test_price_rule_structure_four_tiers():
     t, _ = T.tiers_price(z, z, z, 0.0, bk, eK=z)
     assert np.all(t == SKIP)
     # a SKIM/LOW tie at equal objectives goes to SKIM (the cheaper)
-    # (p = 1, price 1: SKIM 0.25 + 0.625 = LOW 0.125 + 0.75 = 0.875 < FULL 1 < SKIP)
+    # (p = 1, price 1: SKIM 0.25 + 0.375 = LOW 0.125 + 0.5 = 0.625 < FULL 1 < SKIP)
     t, _ = T.tiers_price(np.ones((1, 1)), np.full((1, 1), 10.0), np.full((1, 1), 0.125),
                          1.0, bk, eK=np.full((1, 1), 0.25))
     assert t[0, 0] == T.SKIM

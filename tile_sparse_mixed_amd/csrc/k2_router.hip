@@ -390,14 +390,14 @@ __device__ inline unsigned char price_tier(const PriceTile& x, double pt, double
   const double eL = x.vnorm * expm1(0.5 * x.sl2) +
                     (sqrt(x.vvar * expm1(x.sl2)) + kE4m3U * sqrt(x.m2v / 3.0)) / sqrt(neff);
   const double oS = pt * eS + price * cost_skip;
-  const double oL = pt * eL + price * 0.75;
+  const double oL = pt * eL + price * 0.5;
   const double oF = price * 1.0;
   unsigned char t = TATTN_SKIP;
   double best = oS;
   if (skim) {
     const double eK = x.vnorm * expm1(0.5 * x.sk2) +
-                      (sqrt(x.vvar * expm1(x.sk2)) + kE2m1U * sqrt(x.m2v / 3.0)) / sqrt(neff);
-    const double oK = pt * eK + price * 0.625;
+                      (sqrt(x.vvar * expm1(x.sk2)) + kE4m3U * sqrt(x.m2v / 3.0)) / sqrt(neff);
+    const double oK = pt * eK + price * 0.375;
     if (oK < best) {
       t = TATTN_SKIM;
       best = oK;
