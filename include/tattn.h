@@ -109,12 +109,15 @@ typedef struct tattn_plan_s* tattn_plan_t;  /* opaque host object; device state 
 typedef struct {
   int64_t n_full, n_low, n_skip;  /* tiles per tier, over all (b, h, I, J)           */
   int64_t n_diag;                 /* diagonal tiles (always FULL)                    */
-  double flops_bf16;              /* executed 16-bit MFMA flops: FULL and SKIP tiles,
-                                     and the P.V half of LOW and SKIM tiles         */
-  double flops_fp8;               /* executed fp8 MFMA flops: the score half of LOW  */
+  double flops_bf16;              /* 16-bit MFMA flops: FULL tiles (4 m n d), SKIP
+                                     tiles (4 m d: one pooled key each), and the
+                                     P.V half of LOW tiles with 16- or 8-key blocks */
+  double flops_fp8;               /* fp8 MFMA flops: LOW tiles (4 m n d with 64-key
+                                     blocks, else the score half), the P.V half of
+                                     SKIM tiles                                     */
   double flops_dense;             /* 4 * N^2 * d * B * H: dense-equivalent work      */
   int64_t n_skim;                 /* SKIM tiles                                      */
-  double flops_fp4;               /* executed fp4 MFMA flops: the score half of SKIM */
+  double flops_fp4;               /* fp4 MFMA flops: the score half of SKIM tiles    */
 } tattn_stats;
 
 /* Check a config without touching any device.  Host only; no HIP calls. */
@@ -127,9 +130,8 @@ tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes /* hos
 /*
  * Build a plan: block pooling, fp8 quantisation and routing.
  *  1. Block means qbar_I, kbar_J, vbar_J (float64 sums, stored as float32) and,
- *     per block, amax, scale = amax/448 and E4M3 codes of K and V (V kept as the
- *     fp16 dequantised values the low tier multiplies), plus the Q-block scales
- *     ("Triage": block means; "HierPAS": reduced precision).
+ *     per block, amax, scale = amax/448 and E4M3 codes of K and V, plus the
+ *     Q-block scales ("Triage": block means; "HierPAS": reduced precision).
  *  2. Router p_IJ = softmax_J(qbar_I . kbar_J / sqrt(d) + ln n_J) in float64
  *     ("APT": attention probability as importance), and
  *  3. the tier map by `cfg->mode` (dual thresholds, top-k, entropy-adaptive,
@@ -164,22 +166,66 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
 /*
  * The fused three-tier pass ("Triage": one kernel, all tiers, single pass):
  * for every query block, an online softmax over its FULL tiles (bf16 MFMA),
- * its LOW tiles (scores from E4M3 Q and K on fp8 MFMA, values from E4M3 V),
- * its SKIM tiles (scores from MXFP4 Q and K on the block-scaled fp4 MFMA,
- * values from MXFP4 V) and its SKIP tiles (block means with a ln n_J bias),
- * then O = acc / l.
- * o: output tensor with the config's strides, dtype cfg->out_dtype.
- * k and v must be the pointers the plan was built with (TATTN_E_STATE if not).
+ * its LOW tiles, its SKIM tiles and its SKIP tiles (block means with a ln n_J
+ * bias), then O = acc / l.  A LOW tile's scores come from E4M3 Q and K on the
+ * fp8 MFMA ("HierPAS": reduced precision for less critical tiles; "APT":
+ * dual-precision execution); its probabilities are quantised to E4M3 against
+ * the tile's row maximum (x_j = 448 e^{s_j - m_t}, so the maximum is 448), and
+ * P.V runs on the fp8 MFMA against the E4M3 V (64-key blocks; with 16- and
+ * 8-key blocks the quantised probabilities meet the dequantised V in fp16),
+ * the row normaliser summing the same quantised probabilities.  A SKIM tile
+ * ("Triage": skimming in 4 bits) takes its scores from MXFP4 Q and K on the
+ * block-scaled fp4 MFMA and is otherwise a LOW tile.
+ * q: the queries; the LOW tier's per-block Q scales are taken from q itself,
+ * so q may differ from the tensor the plan was routed with (the tiers stay
+ * the plan's).  o: output tensor with the config's strides, dtype
+ * cfg->out_dtype.  k and v must be the pointers the plan was built with
+ * (TATTN_E_STATE if not).
  */
 tattn_status tattn_forward(tattn_plan_t plan, const void* q, const void* k, const void* v, void* o,
                            void* stream);
 
 /*
+ * tattn_forward that also writes the probability codes of the LOW and SKIM
+ * steps of selected query blocks, for checking them against a reference
+ * (several codes are correct where 448 e^{s - m_t} lies on a rounding
+ * midpoint to within the precision of the scores).  Same arithmetic and
+ * output as tattn_forward.
+ *   dump_slot  device int32 [B*H*Nq]: slot of query block (b, h, I) at index
+ *              (b*H + h)*Nq + I, or -1 for a block not dumped
+ *   dump_steps device-side stride in steps per slot; a row's LOW steps come
+ *              first, then its SKIM steps, and steps >= dump_steps are not
+ *              written
+ *   dump       device uint8 [slots][dump_steps][block_q][64], 16-byte aligned:
+ *              byte (slot, step s, query row i of the block, 32 h + p) is the
+ *              code of score register (b = p / 16, r = p % 16) of lane half h,
+ *              i.e. of staged key 32 b + 8 (r / 4) + 4 h + r % 4 of the step.
+ *              A 64-key step is one key block; a 16-key step gathers the next
+ *              four list entries (staged key m: block m / 16, key m % 16); an
+ *              8-key step gathers eight (staged key m: block slot8(m), key
+ *              kk8(m) as defined with the kernels: slot 2(2(m/32) + (m/16)%2)
+ *              + (m/4)%2, key m%4 + 4((m/8)%2)).  Codes of keys past a block's
+ *              end are 0.  Unwritten bytes keep their contents.
+ * TATTN_E_INVALID for NULL pointers or dump_steps < 1; otherwise as
+ * tattn_forward.
+ */
+tattn_status tattn_forward_dump(tattn_plan_t plan, const void* q, const void* k, const void* v, void* o,
+                                const int32_t* dump_slot, int32_t dump_steps, uint8_t* dump, void* stream);
+
+/* Host only.  The most kept (FULL, LOW or SKIM) tiles a query block can hold
+ * under `cfg`'s tier rule, which sizes the fused kernel's per-row list: the
+ * top k_h bound ceil(keep_max * Nk) plus the diagonal blocks (ADAPTIVE), top_k
+ * plus the diagonal blocks (THRESHOLD with top-k), else Nk.  A forward that
+ * meets a row above it cuts the row and flags the plan; tattn_plan_stats then
+ * returns TATTN_E_STATE. */
+tattn_status tattn_list_bound(const tattn_config* cfg, int32_t* bound /* host out */);
+
+/*
  * Reuse a plan for the next diffusion step ("APT": attention probabilities
  * predicted across timesteps from their temporal similarity): the tier map,
  * lists and work order stay those of the step the plan was routed on, and
- * step 1 of tattn_plan (block means, scales, E4M3 codes, the transposed and
- * low-tier V copies, and in PRICE mode the second moments) is recomputed
+ * step 1 of tattn_plan (block means, scales, E4M3 codes, the transposed V
+ * copies, and in PRICE mode the second moments) is recomputed
  * from q, k, v, the next step's tensors, which must have the config's shape
  * and strides.  The router is not run.  Afterwards the plan belongs to these
  * k and v (tattn_forward checks the pointers).  Asynchronous on `stream`;
@@ -214,21 +260,18 @@ tattn_status tattn_plan_get_pool(tattn_plan_t plan, float* qbar, float* kbar, fl
                                  float* sk, float* sv, void* stream);
 
 /* SYNC.  Copy out, in the canonical layout [B, H, seq_len, head_dim], the
- * E4M3 codes of K (bytes) and the low tier's value operand (fp16 bit
- * patterns of fl16(fl32(decode(E4M3(v * inv)) * scale)) per element of V).
- * Either may be NULL. */
-tattn_status tattn_plan_get_codes(tattn_plan_t plan, uint8_t* host_k8, uint16_t* host_vlow, void* stream);
+ * E4M3 codes of K and of V (bytes, E(x * inv) with the block's inverse scale
+ * fl32(448 / amax)).  Either may be NULL. */
+tattn_status tattn_plan_get_codes(tattn_plan_t plan, uint8_t* host_k8, uint8_t* host_v8, void* stream);
 
 /* SYNC.  SKIM tier (config tau_skim > 0; TATTN_E_STATE otherwise): copy out,
- * in the canonical layout, the MXFP4 copies of K and V.  k4 [B, H, seq_len,
+ * in the canonical layout, the MXFP4 copy of K.  k4 [B, H, seq_len,
  * head_dim/2] bytes: E2M1 codes, channel 2m in the low nibble of byte m and
  * 2m+1 in the high nibble; k4s [B, H, seq_len, head_dim/32] bytes: the E8M0
  * scale of each 32 channels, e + 127 for the scale 2^e, e = floor(log2(amax))
- * - 2 clamped to [-127, 127] (-127 for an all-zero block); vskim [B, H,
- * seq_len, head_dim]: fp16 bit patterns of the SKIM tier's value operand,
- * fl16(code value * 2^e) of V's MXFP4 codes.  Any pointer may be NULL. */
-tattn_status tattn_plan_get_mx4(tattn_plan_t plan, uint8_t* host_k4, uint8_t* host_k4s, uint16_t* host_vskim,
-                                void* stream);
+ * - 2 clamped to [-127, 127] (-127 for an all-zero block).  Either pointer may
+ * be NULL. */
+tattn_status tattn_plan_get_mx4(tattn_plan_t plan, uint8_t* host_k4, uint8_t* host_k4s, void* stream);
 
 /* SYNC.  PRICE mode: copy out the block second moments the router used
  * (float32): q2 [B,H,Nq,d] and m2q [B,H,Nq] (query mean square per dimension
@@ -239,7 +282,10 @@ tattn_status tattn_plan_get_mx4(tattn_plan_t plan, uint8_t* host_k4, uint8_t* ho
 tattn_status tattn_plan_get_moments(tattn_plan_t plan, float* q2, float* m2q, float* kvar, float* m2k,
                                     float* vvar, float* m2v, float* vnorm, void* stream);
 
-/* SYNC.  Tier counts and executed / dense-equivalent flops of the plan. */
+/* SYNC.  Tier counts and executed / dense-equivalent flops of the plan.
+ * TATTN_E_STATE if a forward on this plan cut a row at its list bound (see
+ * tattn_list_bound); the flag is cleared by the next tattn_plan or
+ * tattn_replan. */
 tattn_status tattn_plan_stats(tattn_plan_t plan, tattn_stats* host_out);
 
 /* SYNC.  ADAPTIVE mode: per (b, h) k_h (int32 [B*H]) and r_h (float64 [B*H]);

@@ -104,10 +104,10 @@ def test_workspace_formula(lib):
     n = ctypes.c_size_t()
     assert lib.tattn_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == 0
     BH, Nq, Nk, D = 40, 256, 512, 128
-    # dominant regions: E4M3 K (1 B), fp16 V^T and fp16 low-tier V^T (2 + 2 B) per key
+    # dominant regions: E4M3 K and V (1 + 1 B) and the fp16 V^T (2 B) per key
     # element; float64 logits, float32 p, tiers and int16 lists per tile; float32
     # means and the bf16 hi/lo + fp16 pooled operands per block row
-    floor = (BH * Nk * 64 * D * 5 + BH * Nq * Nk * (8 + 4 + 1 + 2) + BH * (Nq + 2 * Nk) * D * 4
+    floor = (BH * Nk * 64 * D * 4 + BH * Nq * Nk * (8 + 4 + 1 + 2) + BH * (Nq + 2 * Nk) * D * 4
              + BH * Nk * D * 6)
     assert floor <= n.value <= floor * 1.05
     assert lib.tattn_workspace_bytes(ctypes.byref(good(head_dim=96)), ctypes.byref(n)) == -2
@@ -116,10 +116,10 @@ def test_workspace_formula(lib):
     assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="price", price=0.01)), ctypes.byref(m)) == 0
     extra = BH * Nq * Nk * 8 + BH * (Nq + Nk) * D * 4 + BH * (Nq + 4 * Nk) * 4
     assert extra <= m.value - n.value <= extra * 1.05
-    # the SKIM tier adds the MXFP4 K codes and scales and the fp16 SKIM V operand
+    # the SKIM tier adds the MXFP4 K codes and scales
     k = ctypes.c_size_t()
     assert lib.tattn_workspace_bytes(ctypes.byref(good(tau_skim=1e-4)), ctypes.byref(k)) == 0
-    extra = BH * Nk * 64 * (D // 2 + D // 32 + 2 * D)
+    extra = BH * Nk * 64 * (D // 2 + D // 32)
     assert extra <= k.value - n.value <= extra * 1.01
     # ... and only where a SKIM tile can occur
     assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="all_full", tau_skim=1e-4)), ctypes.byref(k)) == 0
@@ -161,3 +161,46 @@ def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.tattn_status_str(s)
     assert lib.tattn_status_str(-99) == b"unknown status"
+
+
+def test_forward_dump_rejects_bad_arguments(lib):
+    """Argument checks of the code-dump forward run before any device call."""
+    buf = (ctypes.c_uint8 * 64)()
+    slot = (ctypes.c_int32 * 4)()
+    assert lib.tattn_forward_dump(None, None, None, None, None, None, 1, ctypes.addressof(buf), None) == -1
+    assert lib.tattn_forward_dump(None, None, None, None, None, ctypes.addressof(slot), 0,
+                                  ctypes.addressof(buf), None) == -1
+    assert lib.tattn_forward_dump(None, None, None, None, None, ctypes.addressof(slot), 1,
+                                  ctypes.addressof(buf) + 1, None) == -1
+
+
+@pytest.mark.parametrize("mode,extra", [("adaptive", {}), ("adaptive", dict(keep_min=0.5, keep_max=0.5)),
+                                        ("threshold", dict(top_k=3)), ("threshold", dict(top_k=1)),
+                                        ("threshold", {}), ("price", dict(price=0.01))])
+@pytest.mark.parametrize("tiles", [(128, 64), (64, 64), (64, 16), (64, 8), (128, 16)])
+def test_list_bound_holds_every_row(mode, extra, tiles):
+    """The fused kernel's per-row list bound (host only) against the most kept
+    tiles any row of the oracle's plan holds, on small generated workloads."""
+    import numpy as np
+    from oracle import tattn as T
+    from synth import CONFIGS, generate
+    bq, bk = tiles
+    cfg = CONFIGS["small"].with_(heads=2, grid=(4, 9, 13), block_q=bq, block_k=bk,
+                                 mode={"threshold": 0, "adaptive": 1, "price": 4}[mode],
+                                 **{k: v for k, v in extra.items() if k != "price"})
+    c = make_config(1, cfg.heads, cfg.seq_len, cfg.head_dim, bq, bk, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
+                    top_k=cfg.top_k, mode=mode, keep_min=cfg.keep_min, keep_max=cfg.keep_max,
+                    full_frac=cfg.full_frac, price=extra.get("price", 0.0))
+    bound = tsm.list_bound(c)
+    assert 1 <= bound <= cfg.n_kblocks
+    g = generate(cfg)
+
+    class OC:
+        block_q, block_k, tau_hi, tau_lo = bq, bk, float(np.float32(cfg.tau_hi)), float(np.float32(cfg.tau_lo))
+        top_k, keep_min, keep_max, full_frac = cfg.top_k, float(np.float32(cfg.keep_min)), \
+            float(np.float32(cfg.keep_max)), float(np.float32(cfg.full_frac))
+        entropy_samples, price, tau_skim = cfg.entropy_samples, float(np.float32(extra.get("price", 0.0))), 0.0
+        mode = cfg.mode
+    for h in range(cfg.heads):
+        o = T.oracle_plan(g["q"][0, h], g["k"][0, h], g["v"][0, h], OC)
+        assert int((o["tiers"] != T.SKIP).sum(axis=1).max()) <= bound, (mode, tiles, h)

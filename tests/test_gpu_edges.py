@@ -10,7 +10,7 @@ from oracle import tattn as T
 from synth import CONFIGS, generate
 from synth.gen import to_bf16_bits, bf16_bits_to_f32
 
-from gpu_cases import OracleCfg, band_mask
+from gpu_cases import check_forward, OracleCfg, band_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,8 @@ def _plan(tsm, cfg, d, **kw):
     return tsm.plan(d["q"], d["k"], d["v"], **args)
 
 
-def _check(cfg, g, p, out, rows=None, top_k=None, what=""):
+def _check(cfg, g, p, d, rows=None, top_k=None, what=""):
+    import tile_sparse_mixed_amd as tsm
     oc = OracleCfg(cfg, top_k=top_k)
     tiers = p.tiers()
     for h in range(cfg.heads):
@@ -42,13 +43,8 @@ def _check(cfg, g, p, out, rows=None, top_k=None, what=""):
             srt = -np.sort(-o["p"], axis=1)
             band |= (np.abs(srt[:, oc.top_k - 1] - srt[:, oc.top_k]) <= 1e-12 * srt[:, oc.top_k - 1])[:, None]
         assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), (what, h)
-        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
-        ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k, rows=rows)
-        for I in (range(cfg.n_qblocks) if rows is None else rows):
-            r0, r1 = I * cfg.block_q, min(cfg.seq_len, (I + 1) * cfg.block_q)
-            err = np.abs(out[0, h, r0:r1].astype(np.float64) - ref[r0:r1])
-            assert err.max() <= 1e-2 and err.mean() <= 1e-3, (what, h, I, err.max(), err.mean())
-        _log(f"  {what} h{h}: ok (tiers F/L/S {[round(float((tiers[0, h] == x).mean()), 4) for x in (2, 1, 0)]})")
+        _log(f"  {what} h{h}: tiers F/L/S {[round(float((tiers[0, h] == x).mean()), 4) for x in (2, 1, 0)]}")
+    check_forward(tsm, p, d, g, cfg, OracleCfg(cfg, mode=3), rows=rows, what=what, log=_log)
 
 
 @pytest.mark.parametrize("bk", [64, 16])
@@ -65,9 +61,8 @@ def test_largest_key_block_count(bk):
     g = generate(cfg)
     d = _dev(g["bits"])
     p = _plan(tsm, cfg, d)
-    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
     nq = cfg.n_qblocks
-    _check(cfg, g, p, out, rows=[0, nq // 3, nq - 1], what=f"maxNk bk{bk}")
+    _check(cfg, g, p, d, rows=[0, nq // 3, nq - 1], what=f"maxNk bk{bk}")
 
 
 def _zeroed(cfg):
@@ -93,8 +88,7 @@ def test_all_zero_blocks():
     pool = p.pool()
     assert np.all(pool["sk"][0, :, 3] == 1.0) and np.all(pool["sv"][0, :, 5] == 1.0)
     assert np.all(pool["sq"][0, :, 1] == 1.0)
-    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
-    _check(cfg, g, p, out, what="zero blocks")
+    _check(cfg, g, p, d, what="zero blocks")
 
 
 @pytest.mark.parametrize("top_k", [1, 32])
@@ -105,8 +99,7 @@ def test_top_k_extremes(top_k):
     g = generate(cfg)
     d = _dev(g["bits"])
     p = _plan(tsm, cfg, d)
-    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
-    _check(cfg, g, p, out, top_k=top_k, what=f"top_k {top_k}")
+    _check(cfg, g, p, d, top_k=top_k, what=f"top_k {top_k}")
     if top_k == 1:
         diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
         assert np.all(((p.tiers()[0] != 0) & ~diag).sum(axis=2) <= 1)
@@ -118,9 +111,8 @@ def test_equal_thresholds_have_no_low_tier():
     g = generate(cfg)
     d = _dev(g["bits"])
     p = _plan(tsm, cfg, d)
-    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
     assert not np.any(p.tiers() == 1)
-    _check(cfg, g, p, out, what="tau_hi == tau_lo")
+    _check(cfg, g, p, d, what="tau_hi == tau_lo")
 
 
 @pytest.mark.parametrize("bk", [16, 8])
@@ -134,20 +126,12 @@ def test_adaptive_rows_at_the_list_bound(bk):
     d = _dev(g["bits"])
     p = tsm.plan(d["q"], d["k"], d["v"], block_q=cfg.block_q, block_k=bk, mode="adaptive", keep_min=0.5,
                  keep_max=0.5, full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, out_fp32=True)
-    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
     kh = p.kh()[0]
     assert np.all(kh == int(np.ceil(0.5 * cfg.n_kblocks)))
     tiers = p.tiers()
     kept = (tiers != 0).sum(axis=3)
     _log(f"[list bound bk{bk}] k_h {kh.tolist()}, kept per row {int(kept.min())}..{int(kept.max())} of {cfg.n_kblocks}")
-    oc = OracleCfg(cfg)
-    oc.keep_min = oc.keep_max = 0.5
-    for h in range(cfg.heads):
-        q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
-        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
-        ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k)
-        err = np.abs(out[0, h].astype(np.float64) - ref)
-        assert err.max() <= 1e-2 and err.mean() <= 1e-3, (bk, h, err.max(), err.mean())
+    check_forward(tsm, p, d, g, cfg, OracleCfg(cfg, mode=3), what=f"list bound bk{bk}", log=_log)
 
 
 def test_top_k_rows_at_the_list_bound():
@@ -158,7 +142,6 @@ def test_top_k_rows_at_the_list_bound():
     g = generate(cfg)
     d = _dev(g["bits"])
     p = _plan(tsm, cfg, d)
-    out = tsm.forward(p, d["q"], d["k"], d["v"]).cpu().numpy()
     kept = (p.tiers() != 0).sum(axis=3)
     assert kept.min() >= 5
-    _check(cfg, g, p, out, top_k=5, what="top_k at bound")
+    _check(cfg, g, p, d, top_k=5, what="top_k at bound")

@@ -8,7 +8,7 @@ import pytest
 from oracle import tattn as T
 from synth import CONFIGS, generate
 
-from gpu_cases import OracleCfg, band_mask
+from gpu_cases import check_forward, OracleCfg, band_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,8 @@ def _rank_ambiguous_rows(p, k):
     return np.abs(s[:, k - 1] - s[:, k]) <= 1e-12 * s[:, k - 1]
 
 
-def _check_plan_and_output(cfg, g, p, out, what):
+def _check_plan_and_output(cfg, g, p, dev, what):
+    import tile_sparse_mixed_amd as tsm
     oc = OracleCfg(cfg)
     tiers = p.tiers()
     lists, counts = p.lists()
@@ -56,11 +57,8 @@ def _check_plan_and_output(cfg, g, p, out, what):
             assert np.array_equal(tiers[b, h][~band], o["tiers"][~band]), (what, b, h)
             li, co = T.build_lists(tiers[b, h])
             assert np.array_equal(lists[b, h], li) and np.array_equal(counts[b, h], co), (what, b, h)
-            oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[b, h])
-            ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k)
-            err = np.abs(out[b, h].astype(np.float64) - ref)
-            _log(f"  {what} b{b} h{h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
-            assert err.max() <= 1e-2 and err.mean() <= 1e-3, (what, b, h, err.max(), err.mean())
+    out, _ = check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=what, log=_log)
+    return out
 
 
 @pytest.mark.parametrize("tiles", [(128, 64), (64, 16), (64, 8)])
@@ -77,7 +75,7 @@ def test_batch_and_token_major_layout(tiles):
     out_t = tsm.forward(p, dev["q"], dev["k"], dev["v"])
     assert out_t.stride() == dev["q"].stride()
     o32 = out_t.cpu().numpy()
-    _check_plan_and_output(cfg, g, p, o32, f"bnhd {bq}x{bk}")
+    assert np.array_equal(_check_plan_and_output(cfg, g, p, dev, f"bnhd {bq}x{bk}"), o32)
     # bf16 output in the same layout: the same tiers, each value rounded once
     p16 = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=bq, block_k=bk, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo)
     assert np.array_equal(p16.tiers(), p.tiers())
@@ -98,8 +96,7 @@ def test_short_sequences(n, tiles):
     dev = _contig(g["bits"])
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=bq, block_k=bk, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
                  out_fp32=True)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
-    _check_plan_and_output(cfg, g, p, out, f"N={n} {bq}x{bk}")
+    _check_plan_and_output(cfg, g, p, dev, f"N={n} {bq}x{bk}")
     pf = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=bq, block_k=bk, mode="all_full", out_fp32=True)
     outf = tsm.forward(pf, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     for h in range(cfg.heads):
@@ -114,7 +111,6 @@ def test_top_k_with_16_key_blocks():
     dev = _contig(g["bits"])
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi,
                  tau_lo=cfg.tau_lo, top_k=9, out_fp32=True)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
-    _check_plan_and_output(cfg, g, p, out, "top-9 64x16")
+    _check_plan_and_output(cfg, g, p, dev, "top-9 64x16")
     kept_nondiag = (p.tiers()[0] != 0) & ~T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)[None]
     assert kept_nondiag.sum(axis=2).max() <= 9

@@ -2,9 +2,11 @@
 
 Bars (see the method's tolerances): pooled means, scales and E4M3 codes
 bit-exact; the tier map bit-exact outside the 1e-5 relative band around each
-threshold; lists and counts exact; the output under the oracle's tier map
-within max-abs 1e-2 and mean-abs 1e-3 (unit-scale V), and within 5e-3 max-abs
-when every tile is FULL.
+threshold; lists and counts exact; the low tier's probability codes equal to
+the oracle's except, by one step, where the oracle's value lies on a rounding
+midpoint to within the precision of the kernel's scores; the output under the
+oracle's tier map (merged over those codes) within max-abs 1e-2 and mean-abs
+1e-3 (unit-scale V), and within 5e-3 max-abs when every tile is FULL.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import pytest
 from oracle import tattn as T
 from synth import CONFIGS
 
-from gpu_cases import OracleCfg, band_mask, device_inputs, gpu_plan, oracle_head
+from gpu_cases import OracleCfg, band_mask, check_forward, device_inputs, gpu_plan, oracle_head
 
 pytestmark = pytest.mark.gpu
 
@@ -51,18 +53,16 @@ def test_pool_bitexact(case):
     name, cfg, g, dev, oc, orc = case
     p = gpu_plan(dev, cfg)
     pool = p.pool()
-    k8, vlow = p.codes()
+    k8, v8 = p.codes()
     for b in range(cfg.batch):
         for h in range(cfg.heads):
             o = orc[b][h]
             for key in ("qbar", "kbar", "vbar", "sq", "sk", "sv"):
                 assert np.array_equal(pool[key][b, h], o[key]), (name, key, h)
             assert np.array_equal(k8[b, h], o["k8"]), (name, "k8", h)
-            want = T.low_values(o["v8"], o["sv"], cfg.block_k).astype(np.float16).view(np.uint16)
-            got = vlow[b, h].view(np.uint16)
-            bad = np.argwhere(got != want)
-            assert bad.size == 0, (name, "vlow", h, [(tuple(i), int(got[tuple(i)]), int(want[tuple(i)]))
-                                                     for i in bad[:6]])
+            bad = np.argwhere(v8[b, h] != o["v8"])
+            assert bad.size == 0, (name, "v8", h, [(tuple(i), int(v8[b, h][tuple(i)]), int(o["v8"][tuple(i)]))
+                                                   for i in bad[:6]])
 
 
 def test_router_tiers_and_lists(case):
@@ -124,11 +124,7 @@ def test_forward_under_oracle_tiers(case):
     t = np.stack([[orc[b][h]["tiers"] for h in range(cfg.heads)] for b in range(cfg.batch)])
     p.set_tiers(t)
     assert np.array_equal(p.tiers(), t)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
-    for h in range(cfg.heads):
-        o = orc[0][h]
-        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], o, cfg.block_q, cfg.block_k)
-        _compare(out[0, h], ref, 1e-2, 1e-3, f"{name} oracle-tiers h{h}")
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"{name} oracle tiers", log=_log)
 
 
 def test_forward_random_tiers(case):
@@ -141,28 +137,19 @@ def test_forward_random_tiers(case):
                    size=(cfg.batch, cfg.heads, cfg.n_qblocks, cfg.n_kblocks))
     p.set_tiers(t)
     tg = p.tiers()
+    diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
     for h in range(cfg.heads):
-        diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
         assert np.all(tg[0, h][diag] == 2) and np.array_equal(tg[0, h][~diag], t[0, h][~diag])
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
-    for h in range(cfg.heads):
-        o = oracle_head(g, 0, h, oc, mode=3, external=tg[0, h])
-        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], o, cfg.block_q, cfg.block_k)
-        _compare(out[0, h], ref, 1e-2, 1e-3, f"{name} random-tiers h{h}")
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"{name} random tiers", log=_log)
 
 
 def test_threshold_end_to_end_bf16_out(case):
+    """Routing and forward as the benchmark runs them (bf16 output): the output
+    against the oracle rounded to bf16."""
     name, cfg, g, dev, oc, orc = case
     import tile_sparse_mixed_amd as tsm
     p = gpu_plan(dev, cfg, out_fp32=False)
-    tg = p.tiers()
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).float().cpu().numpy()
-    for h in range(cfg.heads):
-        o = oracle_head(g, 0, h, oc, mode=3, external=tg[0, h])
-        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], o, cfg.block_q, cfg.block_k)
-        # bf16 output adds up to half a bf16 ulp (2^-9 relative) of rounding
-        err = np.abs(out[0, h] - ref) - np.abs(ref) * 2.0 ** -9
-        assert err.max() <= 1e-2 and np.abs(out[0, h] - ref).mean() <= 1.5e-3, (name, h)
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"{name} threshold bf16", log=_log)
 
 
 def test_constant_keys_skip_is_exact():
@@ -227,7 +214,6 @@ def test_adaptive_mode(name):
     kh, rh = p.kh()
     tiers = p.tiers()
     lists, counts = p.lists()
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     nk = cfg.n_kblocks
     for h in range(cfg.heads):
         o = oracle_head(g, 0, h, oc)
@@ -240,6 +226,4 @@ def test_adaptive_mode(name):
             assert np.array_equal(tiers[0, h][~amb], o["tiers"][~amb]), (name, h)
         li, co = T.build_lists(tiers[0, h])
         assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), (name, h)
-        oe = oracle_head(g, 0, h, oc, mode=3, external=tiers[0, h])
-        ref = T.oracle_forward(g["q"][0, h], g["k"][0, h], g["v"][0, h], oe, cfg.block_q, cfg.block_k)
-        _compare(out[0, h], ref, 1e-2, 1e-3, f"{name} adaptive h{h} (k_h {kh[h]})")
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"{name} adaptive (k_h {kh.tolist()})", log=_log)

@@ -1,5 +1,5 @@
 """GPU parity of the MXFP4 SKIM tier (tau_skim > 0): the pooling kernel's
-MXFP4 copies of K and V bit for bit against the oracle's codec, the four-tier
+MXFP4 copy of K bit for bit against the oracle's codec, the four-tier
 threshold map and its lists against the oracle outside the threshold bands,
 the fused kernel's output under the GPU's tiers and under random external
 four-tier maps, the full-size Wan-like shape and the largest key-block count
@@ -11,7 +11,7 @@ from oracle import mxfp4
 from oracle import tattn as T
 from synth import CONFIGS
 
-from gpu_cases import OracleCfg, band_mask, device_inputs
+from gpu_cases import check_forward, OracleCfg, band_mask, device_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -32,15 +32,6 @@ def _plan(tsm, dev, cfg, mode="threshold", out_fp32=True):
                     tau_lo=cfg.tau_lo, top_k=cfg.top_k, mode=mode, out_fp32=out_fp32, tau_skim=cfg.tau_skim)
 
 
-def _check_out(out, ref, what, rows=None, bq=None):
-    if rows is not None:
-        sel = np.concatenate([np.arange(I * bq, min(out.shape[0], (I + 1) * bq)) for I in rows])
-        out, ref = out[sel], ref[sel]
-    err = np.abs(out.astype(np.float64) - ref)
-    _log(f"  {what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
-    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (what, err.max(), err.mean())
-
-
 @pytest.mark.parametrize("name", list(CASES))
 def test_mx4_copies_bit_exact(name):
     import tile_sparse_mixed_amd as tsm
@@ -50,11 +41,9 @@ def test_mx4_copies_bit_exact(name):
     m = p.mx4()
     for h in range(cfg.heads):
         kc, ks, _ = mxfp4.quantise(g["k"][0, h])
-        _, _, vd = mxfp4.quantise(g["v"][0, h])
         assert np.array_equal(m["k4"][0, h], mxfp4.pack_nibbles(kc)), (name, h)
         assert np.array_equal(m["k4s"][0, h], ks), (name, h)
-        assert np.array_equal(m["vskim"][0, h].view(np.uint16), vd.astype(np.float16).view(np.uint16)), (name, h)
-    _log(f"[mx4 {name}] codes, scales and values bit-exact")
+    _log(f"[mx4 {name}] codes and scales bit-exact")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -63,7 +52,6 @@ def test_four_tier_threshold_parity(name):
     cfg = CASES[name]
     g, dev = device_inputs(cfg)
     p = _plan(tsm, dev, cfg)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     tiers = p.tiers()
     lists, counts = p.lists()
     st = p.stats()
@@ -77,8 +65,7 @@ def test_four_tier_threshold_parity(name):
         assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), (name, h)
         li, co = T.build_lists(tiers[0, h])
         assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), (name, h)
-        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
-        _check_out(out[0, h], T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k), f"h{h}")
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"skim {name}", log=_log)
 
 
 @pytest.mark.parametrize("name,seed", [("small", 1), ("d128_ragged", 2), ("d128_q64", 3)])
@@ -95,13 +82,12 @@ def test_external_four_tier_maps(name, seed):
                     ("all_skim", np.full((1, cfg.heads, nq, nk), T.SKIM))):
         p = _plan(tsm, dev, cfg, mode="external")
         p.set_tiers(t.astype(np.uint8))
-        out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
         tg = p.tiers()
         for h in range(cfg.heads):
             q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
             oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=t[0, h])
             assert np.array_equal(tg[0, h], oe["tiers"])
-            _check_out(out[0, h], T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k), f"{name} {what} h{h}")
+        check_forward(tsm, p, dev, g, cfg, oc, what=f"{name} {what}", log=_log)
 
 
 def test_skim_bytes_need_the_tier():
@@ -124,7 +110,6 @@ def test_full_size_wan_shape_sampled():
     cfg = CONFIGS["wan_skim"]
     g, dev = device_inputs(cfg, heads=[0, 7])
     p = _plan(tsm, dev, cfg)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     tiers = p.tiers()
     lists, counts = p.lists()
     _log(f"[skim full size] FULL/LOW/SKIM/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 3, 0)]}")
@@ -137,9 +122,8 @@ def test_full_size_wan_shape_sampled():
         assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), h
         li, co = T.build_lists(tiers[0, h])
         assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), h
-        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
-        ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k, rows=rows)
-        _check_out(out[0, h], ref, f"full size h{h}", rows=rows, bq=cfg.block_q)
+    check_forward(tsm, p, dev, g, cfg.with_(heads=2), OracleCfg(cfg, mode=3), rows=rows, what="skim full size",
+                  log=_log)
 
 
 def test_zero_blocks_in_skim_tiles():
@@ -162,14 +146,9 @@ def test_zero_blocks_in_skim_tiles():
     p = _plan(tsm, dev, cfg, mode="external")
     t = np.full((1, cfg.heads, cfg.n_qblocks, cfg.n_kblocks), T.SKIM, np.uint8)
     p.set_tiers(t)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     m = p.mx4()
     assert np.all(m["k4s"][0, :, 3 * 64:4 * 64] == 0) and np.all(m["k4"][0, :, 3 * 64:4 * 64] == 0)
-    oc = OracleCfg(cfg, mode=3)
-    for h in range(cfg.heads):
-        q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
-        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=t[0, h])
-        _check_out(out[0, h], T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k), f"zero blocks h{h}")
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what="zero blocks", log=_log)
 
 
 def test_replan_keeps_skim_tiles_and_refreshes_mx4():
@@ -184,16 +163,12 @@ def test_replan_keeps_skim_tiles_and_refreshes_mx4():
     t0 = p.tiers()
     assert np.any(t0 == T.SKIM)
     tsm.replan(p, dev1["q"], dev1["k"], dev1["v"])
-    out = tsm.forward(p, dev1["q"], dev1["k"], dev1["v"]).cpu().numpy()
     assert np.array_equal(p.tiers(), t0)
     m = p.mx4()
-    oc = OracleCfg(cfg)
     for h in range(cfg.heads):
-        q1, k1, v1 = g1["q"][0, h], g1["k"][0, h], g1["v"][0, h]
-        kc, ks, _ = mxfp4.quantise(k1)
+        kc, ks, _ = mxfp4.quantise(g1["k"][0, h])
         assert np.array_equal(m["k4"][0, h], mxfp4.pack_nibbles(kc)) and np.array_equal(m["k4s"][0, h], ks)
-        r = T.oracle_replan(q1, k1, v1, {"tiers": t0[0, h]}, oc)
-        _check_out(out[0, h], T.oracle_forward(q1, k1, v1, r, cfg.block_q, cfg.block_k), f"replan h{h}")
+    check_forward(tsm, p, dev1, g1, cfg, OracleCfg(cfg, mode=3), what="skim replan", log=_log)
 
 
 def test_top_k_with_four_tiers():
@@ -201,7 +176,6 @@ def test_top_k_with_four_tiers():
     cfg = CASES["small"].with_(top_k=12)
     g, dev = device_inputs(cfg)
     p = _plan(tsm, dev, cfg)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     tiers = p.tiers()
     oc = OracleCfg(cfg)
     for h in range(cfg.heads):
@@ -213,8 +187,7 @@ def test_top_k_with_four_tiers():
         assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), h
         diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
         assert np.all(((tiers[0, h] != T.SKIP) & ~diag).sum(axis=1) <= 12)
-        oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, h])
-        _check_out(out[0, h], T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k), f"top-k h{h}")
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what="skim top-k", log=_log)
 
 
 def test_largest_key_block_count_with_skim():
@@ -225,7 +198,6 @@ def test_largest_key_block_count_with_skim():
     assert cfg.n_kblocks == 4096
     g, dev = device_inputs(cfg)
     p = _plan(tsm, dev, cfg)
-    out = tsm.forward(p, dev["q"], dev["k"], dev["v"]).cpu().numpy()
     tiers = p.tiers()
     _log(f"[skim max Nk] FULL/LOW/SKIM/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 3, 0)]}")
     oc = OracleCfg(cfg)
@@ -234,6 +206,4 @@ def test_largest_key_block_count_with_skim():
     band = band_mask(o["p"], oc.tau_hi, oc.tau_lo, tau_skim=oc.tau_skim)
     assert np.array_equal(tiers[0, 0][~band], o["tiers"][~band])
     rows = [0, cfg.n_qblocks // 3, cfg.n_qblocks - 1]
-    oe = T.oracle_plan(q, k, v, oc, mode=3, external_tiers=tiers[0, 0])
-    ref = T.oracle_forward(q, k, v, oe, cfg.block_q, cfg.block_k, rows=rows)
-    _check_out(out[0, 0], ref, "max Nk", rows=rows, bq=cfg.block_q)
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), rows=rows, what="skim max Nk", log=_log)

@@ -14,7 +14,8 @@ import os
 
 import numpy as np
 
-__all__ = ["plan", "replan", "forward", "Plan", "TattnError", "load_library", "Config", "Stats",
+__all__ = ["plan", "replan", "forward", "forward_dump", "list_bound", "Plan", "TattnError", "load_library",
+           "Config", "Stats",
            "MODE_THRESHOLD", "MODE_ADAPTIVE", "MODE_ALL_FULL", "MODE_EXTERNAL", "MODE_PRICE",
            "SKIP", "LOW", "FULL", "SKIM"]
 
@@ -59,13 +60,15 @@ _SIGS = {
     "tattn_plan": (ctypes.c_int, [ctypes.POINTER(Config), _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
                                   ctypes.POINTER(_VP)]),
     "tattn_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP]),
+    "tattn_forward_dump": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]),
+    "tattn_list_bound": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_int32)]),
     "tattn_replan": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_set_tiers": (ctypes.c_int, [_VP, _VP, _VP]),
     "tattn_plan_get_tiers": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_get_lists": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_get_pool": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_get_codes": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
-    "tattn_plan_get_mx4": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
+    "tattn_plan_get_mx4": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_stats": (ctypes.c_int, [_VP, ctypes.POINTER(Stats)]),
     "tattn_plan_get_kh": (ctypes.c_int, [_VP, _VP, _VP]),
     "tattn_plan_get_moments": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
@@ -183,24 +186,20 @@ class Plan:
         return out
 
     def codes(self):
-        """(E4M3 codes of K as uint8, the low tier's fp16 V operand as float16),
-        both [B, H, N, d]."""
+        """E4M3 codes of K and of V as uint8, both [B, H, N, d]."""
         k8 = np.empty(self._shape(self.cfg.seq_len, self.cfg.head_dim), np.uint8)
-        vlow = np.empty(k8.shape, np.uint16)
-        _check(load_library().tattn_plan_get_codes(self._handle, k8.ctypes.data, vlow.ctypes.data, _stream()))
-        return k8, vlow.view(np.float16)
+        v8 = np.empty(k8.shape, np.uint8)
+        _check(load_library().tattn_plan_get_codes(self._handle, k8.ctypes.data, v8.ctypes.data, _stream()))
+        return k8, v8
 
     def mx4(self):
-        """SKIM tier: the MXFP4 copies of K (codes, two per byte, [B, H, N,
-        d/2] uint8; E8M0 scale bytes [B, H, N, d/32]) and the SKIM value
-        operand as float16 [B, H, N, d]."""
+        """SKIM tier: the MXFP4 copy of K (codes, two per byte, [B, H, N,
+        d/2] uint8; E8M0 scale bytes [B, H, N, d/32])."""
         n, d = self.cfg.seq_len, self.cfg.head_dim
         k4 = np.empty(self._shape(n, d // 2), np.uint8)
         k4s = np.empty(self._shape(n, d // 32), np.uint8)
-        vs = np.empty(self._shape(n, d), np.uint16)
-        _check(load_library().tattn_plan_get_mx4(self._handle, k4.ctypes.data, k4s.ctypes.data, vs.ctypes.data,
-                                                 _stream()))
-        return dict(k4=k4, k4s=k4s, vskim=vs.view(np.float16))
+        _check(load_library().tattn_plan_get_mx4(self._handle, k4.ctypes.data, k4s.ctypes.data, _stream()))
+        return dict(k4=k4, k4s=k4s)
 
     def stats(self) -> dict:
         st = Stats()
@@ -269,16 +268,47 @@ def replan(p: Plan, q, k, v) -> Plan:
     return p
 
 
+def list_bound(cfg: Config) -> int:
+    """The most kept tiles a query block can hold under cfg's tier rule
+    (host only: no device needed)."""
+    b = ctypes.c_int32(0)
+    _check(load_library().tattn_list_bound(ctypes.byref(cfg), ctypes.byref(b)))
+    return int(b.value)
+
+
+def _out_like(p, q, out):
+    import torch
+    dt = torch.float32 if p.cfg.out_dtype == 1 else torch.bfloat16
+    if out is None:
+        return torch.empty_strided(q.shape, q.stride(), dtype=dt, device=q.device)
+    if out.dtype != dt or out.stride() != q.stride() or out.shape != q.shape:
+        raise ValueError("out must match q's shape and strides and the plan's output dtype")
+    return out
+
+
+def forward_dump(p: Plan, q, k, v, rows, steps, out=None):
+    """The fused pass, also returning the probability codes of the LOW and
+    SKIM steps of the query blocks ``rows`` (a list of (b, h, I)): a uint8
+    array [len(rows), steps, block_q, 64] (byte layout as tattn_forward_dump
+    documents; steps past a row's count are zero)."""
+    import torch
+    _check_tensors(q, k, v)
+    out = _out_like(p, q, out)
+    slot = torch.full((p.cfg.batch * p.cfg.heads * p.n_q,), -1, dtype=torch.int32)
+    for i, (b, h, I) in enumerate(rows):
+        slot[(b * p.cfg.heads + h) * p.n_q + I] = i
+    slot = slot.to(q.device)
+    dump = torch.zeros((max(1, len(rows)), int(steps), p.cfg.block_q, 64), dtype=torch.uint8, device=q.device)
+    _check(load_library().tattn_forward_dump(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                             slot.data_ptr(), int(steps), dump.data_ptr(), _stream()))
+    return out, dump.cpu().numpy()[:len(rows)]
+
+
 def forward(p: Plan, q, k, v, out=None):
     """The fused three-tier pass (K3).  Returns O [B, H, N, d] (bf16, or fp32
     if the plan was made with out_fp32=True)."""
-    import torch
     _check_tensors(q, k, v)
-    dt = torch.float32 if p.cfg.out_dtype == 1 else torch.bfloat16
-    if out is None:
-        out = torch.empty_strided(q.shape, q.stride(), dtype=dt, device=q.device)
-    elif out.dtype != dt or out.stride() != q.stride() or out.shape != q.shape:
-        raise ValueError("out must match q's shape and strides and the plan's output dtype")
+    out = _out_like(p, q, out)
     _check(load_library().tattn_forward(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                         _stream()))
     return out

@@ -12,13 +12,18 @@
 //   sk_J, sv_J       amax/448 (1 for an all-zero block),
 //   k8               E4M3 codes of K_J, row-major with k8_pos d order,
 //   vt               V_J as fp16, transposed ([d][key]) in the key order the
-//                    fused kernel's P.V uses (vt_pos for 64-key blocks, vt16_pos
-//                    for 16-key blocks, which the kernel gathers four at a time,
-//                    natural order for 8-key blocks, gathered eight at a time),
-//   vlow             the low tier's V operand, fl16(fl32(decode(E4M3(v * inv)) * sv)),
-//                    in the same transposed layout.
+//                    fused kernel's FULL P.V uses (vt_pos for 64-key blocks,
+//                    vt16_pos for 16-key blocks, which the kernel gathers four at
+//                    a time, natural order for 8-key blocks, gathered eight at a
+//                    time),
+//   v8t              E4M3 codes of V_J, transposed ([d][key]): the A operand of the
+//                    low tier's fp8 P.V for 64-key blocks (pv8_key order), key
+//                    order otherwise,
+//   vlow             16- and 8-key blocks: the low tier's fp16 V operand,
+//                    fl16(fl32(decode(E4M3(v * inv)) * sv)), in vt's layout (their
+//                    gathered steps mix blocks of different scales in one P.V).
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
-// With the SKIM tier a third kernel writes MXFP4 copies of K and V (k1_mx4).
+// With the SKIM tier a third kernel writes the MXFP4 copy of K (k1_mx4).
 // For the price router both also write second moments from float64 sums of
 // squares ("Triage": the router works from block statistics): per dimension
 // the query mean square and the key variance, per block the key and value
@@ -166,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   float* sk = reinterpret_cast<float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk + J;
   float* sv = reinterpret_cast<float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk + J;
   unsigned char* k8 = slab + a.L.sl.k8 + (int64_t)J * BK * D;
+  unsigned char* v8t = slab + a.L.sl.v8t + (int64_t)J * BK * D;
   uint16_t* vlow = reinterpret_cast<uint16_t*>(slab + a.L.sl.vlow) + (int64_t)J * BK * D;
   uint16_t* vt = reinterpret_cast<uint16_t*>(slab + a.L.sl.vt) + (int64_t)J * BK * D;
 
@@ -257,29 +263,53 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
     }
     *reinterpret_cast<uint4*>(vt + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  // vlow: same layout as vt; element = fl16(fl32(decode(code)) * sv) of the E4M3 code
-  // of v * inv (the hardware converter decodes exactly).
-  const float svf = scale448(amax);
-  for (int u = t; u < D * QR; u += kThreads) {
-    const int d = u / QR, q = u % QR;
-    uint32_t w[4];
+  // v8t: D rows of BK codes of v * inv; element e of row d holds key
+  // pv8_key(e) (64-key blocks) or key e; ES elements per store
+  constexpr int ES = BK < 16 ? BK : 16, SR = BK / ES;
+  for (int u = t; u < D * SR; u += kThreads) {
+    const int d = u / SR, q = u % SR;
+    uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int e2 = 0; e2 < 4; e2++) {
-      float f[2];
+    for (int e4 = 0; e4 < ES / 4; e4++) {
+      float f[4];
 #pragma unroll
-      for (int z = 0; z < 2; z++) {
-        const int key = vt_key<BK>(q * 8 + e2 * 2 + z);
-        f[z] = bf16_to_f32(tileT[key * D + d]) * inv;
+      for (int z = 0; z < 4; z++) {
+        const int e = q * ES + e4 * 4 + z;
+        f[z] = bf16_to_f32(tileT[(BK == 64 ? pv8_key(e) : e) * D + d]) * inv;
       }
-      const int code2 = cvt_fp8x2<false>(f[0], f[1], 0);
-      const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8(code2, false);
-      // Round the product to fp32 first, then to fp16: the opaque step keeps
-      // the compiler from fusing both roundings into one mixed-precision FMA.
-      float p0 = dec.x * svf, p1 = dec.y * svf;
-      opaque(p0, p1);
-      w[e2] = uint32_t(f32_to_f16(p0)) | (uint32_t(f32_to_f16(p1)) << 16);
+      const int wd = cvt_fp8x2<false>(f[0], f[1], 0);
+      w[e4] = static_cast<uint32_t>(cvt_fp8x2<true>(f[2], f[3], wd));
     }
-    *reinterpret_cast<uint4*>(vlow + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    if constexpr (ES == 16)
+      *reinterpret_cast<uint4*>(v8t + d * BK + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    else
+      *reinterpret_cast<uint2*>(v8t + d * BK + q * 8) = make_uint2(w[0], w[1]);
+  }
+  if constexpr (BK < 64) {
+    // vlow: same layout as vt; element = fl16(fl32(decode(code)) * sv) of the E4M3
+    // code of v * inv (the hardware converter decodes exactly).
+    const float svf = scale448(amax);
+    for (int u = t; u < D * QR; u += kThreads) {
+      const int d = u / QR, q = u % QR;
+      uint32_t w[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; e2++) {
+        float f[2];
+#pragma unroll
+        for (int z = 0; z < 2; z++) {
+          const int key = vt_key<BK>(q * 8 + e2 * 2 + z);
+          f[z] = bf16_to_f32(tileT[key * D + d]) * inv;
+        }
+        const int code2 = cvt_fp8x2<false>(f[0], f[1], 0);
+        const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8(code2, false);
+        // Round the product to fp32 first, then to fp16: the opaque step keeps
+        // the compiler from fusing both roundings into one mixed-precision FMA.
+        float p0 = dec.x * svf, p1 = dec.y * svf;
+        opaque(p0, p1);
+        w[e2] = uint32_t(f32_to_f16(p0)) | (uint32_t(f32_to_f16(p1)) << 16);
+      }
+      *reinterpret_cast<uint4*>(vlow + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -299,6 +329,7 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   BL bl;
   double colsum, colsq = 0.0;
   float amax;
+  if (blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<int*>(ws + a.L.flag)[0] = 0;   // a fresh plan's error flags
   load_block<D, BQ, MOM>(a.q + off, dm.sn, rows, bl, red, colsum, amax, &colsq);
   if (threadIdx.x < D) qbar[threadIdx.x] = static_cast<float>(colsum / static_cast<double>(rows));
   if (MOM) {   // query mean square per dimension and its total
@@ -315,16 +346,14 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   }
 }
 
-// MXFP4 copies of K_J and V_J for the SKIM tier (64-key blocks; "Triage":
-// skimming a tile in a 4-bit format).  Per key row and 32 channels one E8M0
-// scale and 32 E2M1 codes.  K: codes [64][D/2] (channel 2m in the low nibble
-// of byte m) and scale bytes [64][D/32], row-major; V: the dequantised values
-// fl16(code value * 2^e), transposed [D][64] in vt_pos order like the other
-// V operands.  Rows past N are zero (codes 0, scale byte 0).
+// MXFP4 copy of K_J for the SKIM tier (64-key blocks; "Triage": skimming a
+// tile's scores in a 4-bit format).  Per key row and 32 channels one E8M0
+// scale and 32 E2M1 codes: codes [64][D/2] (channel 2m in the low nibble of
+// byte m) and scale bytes [64][D/32], row-major.  Rows past N are zero (codes
+// 0, scale byte 0).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
   constexpr int NB = D / 32;            // scale blocks per row
-  __shared__ uint16_t tileV[64 * D];    // dequantised V, fp16 [key][d]
   const Dims& dm = a.d;
   const int bh = blockIdx.x / dm.Nk, J = blockIdx.x % dm.Nk;
   const int b = bh / dm.H, h = bh % dm.H;
@@ -333,12 +362,9 @@ __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
   unsigned char* slab = a.ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
   unsigned char* k4 = slab + a.L.sl.k4 + (int64_t)J * 64 * (D / 2);
   unsigned char* k4s = slab + a.L.sl.k4s + (int64_t)J * 64 * NB;
-  uint16_t* vs = reinterpret_cast<uint16_t*>(slab + a.L.sl.vskim) + (int64_t)J * 64 * D;
-  for (int u = threadIdx.x; u < 2 * 64 * NB; u += kThreads) {
-    const bool isv = u >= 64 * NB;
-    const int w = isv ? u - 64 * NB : u;
+  for (int w = threadIdx.x; w < 64 * NB; w += kThreads) {
     const int r = w / NB, c = w % NB;
-    const uint16_t* src = (isv ? a.v : a.k) + off + (int64_t)r * dm.sn + 32 * c;
+    const uint16_t* src = a.k + off + (int64_t)r * dm.sn + 32 * c;
     float x[32];
     float amax = 0.0f;
 #pragma unroll
@@ -354,28 +380,11 @@ __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
       }
     }
     const int ex = mx4_exponent(amax);
-    if (!isv) {
-      uint32_t pk[4] = {0, 0, 0, 0};
+    uint32_t pk[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
-      *reinterpret_cast<uint4*>(k4 + r * (D / 2) + 16 * c) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      k4s[r * NB + c] = static_cast<unsigned char>(ex + 127);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; e++)
-        tileV[r * D + 32 * c + e] = f32_to_f16(ldexpf(e2m1_value(e2m1_code(ldexpf(x[e], -ex))), ex));
-    }
-  }
-  __syncthreads();
-  // element e of stored row d holds key vt_key<64>(e), 8 elements per store
-  for (int u = threadIdx.x; u < D * 8; u += kThreads) {
-    const int d = u / 8, q = u % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; e2++)
-      w[e2] = uint32_t(tileV[vt_key<64>(q * 8 + 2 * e2) * D + d]) |
-              (uint32_t(tileV[vt_key<64>(q * 8 + 2 * e2 + 1) * D + d]) << 16);
-    *reinterpret_cast<uint4*>(vs + d * 64 + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
+    *reinterpret_cast<uint4*>(k4 + r * (D / 2) + 16 * c) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    k4s[r * NB + c] = static_cast<unsigned char>(ex + 127);
   }
 }
 

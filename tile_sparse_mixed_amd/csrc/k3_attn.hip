@@ -11,8 +11,15 @@
 //             v_mfma_f32_32x32x16_bf16, O^T += V^T P^T on the fp16 variant
 //             (P in [0, 2^8] keeps 3 more mantissa bits than bf16 would),
 //   LOW       a low-precision tile: S^T on v_mfma_f32_32x32x64_f8f6f4 from the
-//             E4M3 copies of Q and K scaled by sq*sk; P.V against the fp16
-//             dequantised E4M3 V,
+//             E4M3 copies of Q and K scaled by sq*sk; the probabilities
+//             quantised to E4M3 against the tile's row maximum (448 at the
+//             maximum); O^T += V8^T P8^T on the same fp8 instruction against the
+//             E4M3 V, merged with the weight 2^(tile max - m) * sv / 448, and
+//             the row sum of the codes from one more fp8 MFMA against ones
+//             (16- and 8-key blocks: the quantised probabilities times their
+//             block's weight in fp16, P.V on the fp16 MFMA against the fp16
+//             dequantised V, since one fp8 P.V there would mix blocks of
+//             different scales),
 //   SKIP_S    64 pooled keys kbar_J of one chunk of 64 key blocks, as a bf16
 //             hi + lo pair (two MFMAs: ~2^-17 precision), each scored with a
 //             log2(n_J) bias if J is skipped in this row and -inf otherwise
@@ -20,8 +27,8 @@
 //   SKIP_PV   the same chunk's block means vbar_J (fp16, transposed) for P.V,
 //   SKIM      (instances with SKIM = true, 64-key blocks) a 4-bit tile: S^T on
 //             the same instruction with MXFP4 operands and their E8M0 block
-//             scales ("Triage": skimming in 4 bits); P.V against the fp16
-//             dequantised MXFP4 V.
+//             scales ("Triage": skimming in 4 bits); probabilities and P.V as
+//             in LOW.
 // Skipped blocks are visited as whole chunks of 64 (contiguous operands),
 // masked to the row's SKIP set; chunks with no skipped block are not visited.
 // With 16-key blocks ("FG-Attn": M x N tiles with a small N) a FULL or LOW
@@ -52,6 +59,12 @@
 // Running state per lane: m (base-2 reference), l (sum of the weights
 // relative to 2^m) and the O^T accumulator.  m is raised only when a tile's
 // max exceeds it by more than 8, so most steps skip the rescale.
+//
+// The LOW-tier Q scales are taken here from the Q block the kernel is given
+// (its amax over the workgroup), so a forward with other queries than the
+// plan's keeps the low tier exact to its definition.  Instances with DUMP =
+// true also write every LOW and SKIM step's probability codes of the rows the
+// caller selected (tattn_forward_dump).
 #include <type_traits>
 
 #include "tattn_device.hpp"
@@ -147,11 +160,12 @@ template <int G>
 struct StepScale {
   static constexpr int N = G == 8 ? 4 : G;
   float c[N];
+  float v;   // E4M3 value scale of a 64-key LOW or SKIM step's block
 };
 
 // SKIM: the instance also runs the SKIM tier (64-key blocks only); the other
-// instances carry none of its code.
-template <int D, int NW, int BK, bool SKIM>
+// instances carry none of its code.  DUMP: the probability-code dump.
+template <int D, int NW, int BK, bool SKIM, bool DUMP>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
   static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
@@ -178,6 +192,7 @@ void k3_attn(AttnArgs a) {
   __shared__ uint64_t smask[64];             // per visited chunk: bit j = block 64c + j skipped
   __shared__ unsigned char schunk[64];       // chunks holding at least one skipped block
   __shared__ int snc;
+  __shared__ float samax[NW];                // per wave: max |q| of its rows
 
   const Dims& dm = a.d;
   // ---- work mapping: workgroup x takes row (b, h, I) = order[x], which is the
@@ -198,6 +213,25 @@ void k3_attn(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, lh = lane >> 5;
 
+  // ---- Q rows of this wave as bf16 B operands: lane (ln, lh) holds
+  // q[row][16c + 8lh .. +8] for chunk c; rows past N are zero.
+  const int qrow = I * (32 * NW) + wave * 32 + ln;
+  bf16x8 qreg[D / 16];
+  {
+    uint32_t mx = 0;   // largest |q| of the lane's values, as bf16 bits (monotone in the magnitude)
+#pragma unroll
+    for (int c = 0; c < D / 16; c++) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qrow < dm.N) v = *reinterpret_cast<const uint4*>(a.q + toff + (int64_t)qrow * dm.sn + 16 * c + 8 * lh);
+      qreg[c] = __builtin_bit_cast(bf16x8, v);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) mx = max(mx, max(w4[j] & 0x7fffu, (w4[j] >> 16) & 0x7fffu));
+    }
+    const float am = wave_max(__uint_as_float(mx << 16));
+    if (lane == 0) samax[wave] = am;
+  }
+
   const unsigned char* ws = a.ws;
   const int* counts = reinterpret_cast<const int*>(ws + a.L.counts) + row * 4;
   // the list in LDS holds a.list_cap entries, the plan's bound on a row's kept
@@ -206,6 +240,8 @@ void k3_attn(AttnArgs a) {
   const int nF = min(counts[0], cap), nL = min(counts[1], cap - nF);
   const int nK = nF + nL;
   const int nSk = SKIM ? min(dm.Nk - counts[0] - counts[1] - counts[2], cap - nK) : 0;   // SKIM follows LOW
+  if (tid == 0 && counts[0] + counts[1] + (SKIM ? dm.Nk - counts[0] - counts[1] - counts[2] : 0) > cap)
+    atomicOr(reinterpret_cast<int*>(a.ws + a.L.flag), 1);   // reported by tattn_plan_stats
   {
     const int16_t* list = reinterpret_cast<const int16_t*>(ws + a.L.lists) + row * dm.Nk;
     for (int i = tid; i < nK + nSk; i += NW * 64) slist[i] = list[i];
@@ -238,19 +274,19 @@ void k3_attn(AttnArgs a) {
   // the DMA already in flight (a vector load would share vmcnt with it).
   typedef __attribute__((address_space(4))) const float cfloat;
   cfloat* skp = (cfloat*)(reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk);
+  cfloat* svp = (cfloat*)(reinterpret_cast<const float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk);
 
-  // ---- Q rows of this wave as bf16 B operands: lane (ln, lh) holds
-  // q[row][16c + 8lh .. +8] for chunk c.
-  const int qrow = I * (32 * NW) + wave * 32 + ln;
-  bf16x8 qreg[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; c++) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (qrow < dm.N) v = *reinterpret_cast<const uint4*>(a.q + toff + (int64_t)qrow * dm.sn + 16 * c + 8 * lh);
-    qreg[c] = __builtin_bit_cast(bf16x8, v);
-  }
-  const float sq = reinterpret_cast<const float*>(ws + a.L.sq)[row];
   const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
+  // the Q block's E4M3 scale and its inverse, from the block's amax (as the
+  // pooling kernel forms them: a float64 quotient rounded once)
+  float sq, iq;
+  {
+    float am = samax[0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) am = __builtin_fmaxf(am, samax[w]);
+    sq = am == 0.0f ? 1.0f : static_cast<float>(static_cast<double>(am) / 448.0);
+    iq = am == 0.0f ? 1.0f : static_cast<float>(448.0 / static_cast<double>(am));
+  }
 
   // step order: the skip chunks (score / P.V pairs), then FULL tiles, then LOW
   // tiles, so the bf16 Q registers are dead before the E4M3 copy is made, then
@@ -274,7 +310,9 @@ void k3_attn(AttnArgs a) {
 
   // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
   //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
-  //   LOW     R0 = K8 [64][D] E4M3,      R1 = V low^T [D][64] fp16
+  //   LOW     R0 = K8 [64][D] E4M3,      R1 = V8^T [D][64] E4M3 (64-key blocks)
+  //                                         or V low^T [D][64] fp16 (16, 8)
+  //   SKIM    R0 = K4 [64][D/2] + scales, R1 = V8^T [D][64] E4M3
   //   SKIP_S  R0 = kbar hi [64][D] bf16, R1 = kbar lo [64][D] bf16
   //   SKIP_PV                            R1 = vbar^T [D][64] fp16
   // Wave w issues the 1 KB instructions k = w, w + NW, ...  A 16-bit row of D
@@ -309,6 +347,10 @@ void k3_attn(AttnArgs a) {
   // instruction is (lane >> 4) masked to the chunk count
   constexpr int C4 = D / 32;   // 16-byte chunks per MXFP4 row = scale bytes per row
   const int voffK4 = (lane / C4) * (D / 2) + (((lane & (C4 - 1)) ^ ((lane >> 4) & (C4 - 1))) * 16);
+  // [D][64] E4M3 V^T tiles (64-key blocks): 64-byte rows, an instruction covers
+  // rows 16k..16k+15; LDS slot c of row r holds chunk c ^ swzv8(r), swzv8(r) =
+  // (r >> 2) & 3, which inside an instruction is (lane >> 4) & 3
+  const int voffV8 = (lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   // one resource over this head's slab; every workspace operand is a scalar
   // sub-offset of it
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(slab, (uint32_t)SL.bytes);
@@ -348,11 +390,18 @@ void k3_attn(AttnArgs a) {
       dma16(r, reg + k * 1024, voffV, base + k * 1024);
     }
   };
+  auto load_v8 = [&](unsigned char* reg, int J) __attribute__((always_inline)) {   // [D][64] E4M3 V^T of block J
+#pragma unroll
+    for (int i = 0; i < NI8; i++) {
+      const int k = wave + NW * i;
+      dma16(rS, reg + k * 1024, voffV8, (int)SL.v8t + J * 64 * D + k * 1024);
+    }
+  };
   // KINDS: bit mask of the step kinds that can occur where this is called; the
   // other branches are not generated, so their address terms are not kept live.
   // PART: 1 = the R0 half (K, E4M3 K, MXFP4 K and its scales, kbar hi) and
-  // the step's score scale; 2 = the R1 half (V^T, low-tier or SKIM V^T, kbar
-  // lo, vbar^T); 3 = both.  Per wave, every R1 half is NI16 instructions.
+  // the step's scales; 2 = the R1 half (V^T, E4M3 V^T or the fp16 low-tier V^T,
+  // kbar lo, vbar^T); 3 = both.
   auto issue_part = [&](auto kinds, auto part, int t, unsigned char* st, StepScale<G>& cst) __attribute__((always_inline)) {
     constexpr int KINDS = decltype(kinds)::value;
     constexpr bool PA = decltype(part)::value & 1, PB = decltype(part)::value & 2;
@@ -451,8 +500,11 @@ void k3_attn(AttnArgs a) {
           dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
         }
       }
-      if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vlow + J * 128 * D);
-      if constexpr (PA) cst.c[0] = sq * skp[J] * cF;
+      if constexpr (PB) load_v8(r1(st), J);
+      if constexpr (PA) {
+        cst.c[0] = sq * skp[J] * cF;
+        cst.v = svp[J];
+      }
     } else if (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
       // MXFP4 K [64][D/2] into R0, its scale bytes [64][D/32] after it (one
       // D/32-byte load per lane from wave 0, into a 4-byte LDS slot per
@@ -467,8 +519,11 @@ void k3_attn(AttnArgs a) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 2, lane * 2, (int)SL.k4s + J * 2 * D, 0, 0);
         }
       }
-      if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vskim + J * 128 * D);
-      if constexpr (PA) cst.c[0] = cF;
+      if constexpr (PB) load_v8(r1(st), J);
+      if constexpr (PA) {
+        cst.c[0] = cF;
+        cst.v = svp[J];
+      }
     } else {
       const int c = schunk[t >> 1];
       if ((KINDS & (1 << kSkipS)) && kind == kSkipS) {
@@ -498,11 +553,14 @@ void k3_attn(AttnArgs a) {
   // lets it fold the stage base into the ds_read immediate instead.
   constexpr int KROW = D == 128 ? 256 : 128;   // bytes per bf16 K row
   constexpr int K8ROW = D;                     // bytes per E4M3 K row
-  int offk[D / 16], offv[4], offk8[D / 32];
+  int offk[D / 16], offv[4], offk8[D / 32], offv8[2];
 #pragma unroll
   for (int c = 0; c < D / 16; c++) offk[c] = offK<D>(ln, 2 * c + lh);
 #pragma unroll
   for (int c = 0; c < 4; c++) offv[c] = offV(ln, 2 * c + lh);   // within R1
+  // E4M3 V^T rows (64 bytes): chunks 2lh, 2lh + 1 of row ln at slots chunk ^ swzv8(ln)
+#pragma unroll
+  for (int c = 0; c < 2; c++) offv8[c] = ln * 64 + (((2 * lh + c) ^ ((ln >> 2) & 3)) << 4);
 #pragma unroll
   for (int i = 0; i < D / 64; i++) {
     const int ch0 = (D == 128 ? 4 * i : 0) + 2 * lh;
@@ -513,6 +571,7 @@ void k3_attn(AttnArgs a) {
     opaque_arr(offk);
     opaque_arr(offv);
     opaque_arr(offk8);
+    opaque_arr(offv8);
     opaque_arr(lk);
     opaque_arr(lkb);
     opaque(voffV, voffK8);
@@ -524,6 +583,22 @@ void k3_attn(AttnArgs a) {
   for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   f16x8 pb[4];
+  i32x8 p8;        // probability codes of a quantised step (LOW, SKIM)
+  float wpv = 0;   // its P.V weight (64-key blocks)
+  const int dsl = DUMP ? a.dslot[row] : -1;
+  // sum of the fp16 P values the P.V MFMA multiplies, two per
+  // v_dot2_f32_f16 (fp32 accumulation), so numerator and denominator see the
+  // same rounding
+  auto half_sum = [](const f16x8* p) __attribute__((always_inline)) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    float ps = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) ps = __builtin_amdgcn_fdot2(h2{p[cc][2 * j], p[cc][2 * j + 1]}, one2, ps, false);
+    return ps;
+  };
 
   // ---- score blocks S^T = K Q^T of the 64 keys of a step (two 32x32 blocks)
   // All operands of a phase are read from LDS before its MFMAs are issued, so
@@ -606,8 +681,9 @@ void k3_attn(AttnArgs a) {
     if constexpr (G == 1) return cs.c[0];
     else return cs.c[cc];
   };
-  auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
-    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  // raise the running reference m to a step's maximum tmax (base 2, already
+  // reduced over the lane pair) when it exceeds m by more than kLazy
+  auto raise_max = [&](float tmax) __attribute__((always_inline)) {
     const bool need = tmax > m_run + kLazy;
     if (__ballot(need)) {
       const float mn = need ? tmax : m_run;
@@ -619,6 +695,9 @@ void k3_attn(AttnArgs a) {
         for (int r = 0; r < 16; r++) acc[db][r] *= al;
       m_run = mn;
     }
+  };
+  auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
+    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)));
     const float nm = -m_run;
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
@@ -627,16 +706,7 @@ void k3_attn(AttnArgs a) {
         const int e = 8 * cc + tt;
         pb[cc][tt] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], chunk_scale(cs, cc), nm)));
       }
-    // l accumulates the fp16 P values the P.V MFMA multiplies, two per
-    // v_dot2_f32_f16 (fp32 accumulation)
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    float psum = 0.0f;
-#pragma unroll
-    for (int cc = 0; cc < 4; cc++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) psum = __builtin_amdgcn_fdot2(h2{pb[cc][2 * j], pb[cc][2 * j + 1]}, one2, psum, false);
-    l_run += psum;
+    l_run += half_sum(pb);
   };
   auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
     float m = -INFINITY;
@@ -661,6 +731,105 @@ void k3_attn(AttnArgs a) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cc * (D / 32) + db], pb[cc], acc[db], 0, 0, 0);
     pipeline_reads_mfma<D / 8, D / 16>();
   };
+
+  // ---- quantised probabilities (LOW and SKIM tiles).  Scores x = s * c in
+  // base 2; per row the tile maximum tm; codes E(448 * 2^(x - tm)), so the
+  // maximum lands on 448; the tile's weight relative to the running reference
+  // is 2^(tm - m) / 448 per code unit.  The codes stay in p8 in register
+  // order (byte p = 16b + r of lane half h: score register (b, r)), which is
+  // the B operand of the fp8 P.V.
+  auto dump_codes = [&](int ds) __attribute__((always_inline)) {
+    if constexpr (DUMP) {
+      if (dsl >= 0 && ds < a.dsteps) {
+        unsigned char* o = a.dump + ((static_cast<int64_t>(dsl) * a.dsteps + ds) * (32 * NW) + 32 * wave + ln) * 64 + 32 * lh;
+        reinterpret_cast<uint4*>(o)[0] = make_uint4(p8[0], p8[1], p8[2], p8[3]);
+        reinterpret_cast<uint4*>(o)[1] = make_uint4(p8[4], p8[5], p8[6], p8[7]);
+      }
+    } else {
+      (void)ds;
+    }
+  };
+  // codes of four scores x = s * c - tm + log2(448) into one dword
+  auto codes4 = [&](float s0, float s1, float s2, float s3, float c, float nm) __attribute__((always_inline)) {
+    const int w = cvt_fp8x2<false>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, nm)),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, nm)), 0);
+    return cvt_fp8x2<true>(__builtin_amdgcn_exp2f(__builtin_fmaf(s2, c, nm)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(s3, c, nm)), w);
+  };
+  // 64-key tile: one maximum per row (over both lane halves); the row sum of
+  // the codes from the fp8 MFMA against ones (every result register holds the
+  // column sum, so each lane half adds half of it); the P.V weight in wpv
+  auto quant_soft64 = [&](f32x16* s, float c, float sv, int ds) __attribute__((always_inline)) {
+    float tm = row_max(s);
+    tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32, 64)) * c;
+    raise_max(tm);
+    const float nm = kLog2_448 - tm;
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+      const int b = w >> 2, r0 = 4 * (w & 3);
+      p8[w] = codes4(s[b][r0], s[b][r0 + 1], s[b][r0 + 2], s[b][r0 + 3], c, nm);
+    }
+    dump_codes(ds);
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p8, f32x16{}, 0, 0, 0, 0, 0, 0);
+    const float g = __builtin_amdgcn_exp2f(tm - m_run);
+    l_run = __builtin_fmaf(rs[0], g * (0.5f / 448.0f), l_run);
+    wpv = g * (sv * (1.0f / 448.0f));
+  };
+  // 16- and 8-key blocks: one maximum per block (chunk cc of the lane: 16-key
+  // block cc over both lane halves, or 8-key slot 2cc + lane half), and the
+  // fp16 P.V operand decode(code) * 2^(tm_block - m) / 448
+  auto quant_soft_g = [&](f32x16* s, const StepScale<G>& cs, int ds) __attribute__((always_inline)) {
+    float tb[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
+      tb[cc] = m * chunk_scale(cs, cc);
+      if constexpr (G == 4) tb[cc] = __builtin_fmaxf(tb[cc], __shfl_xor(tb[cc], 32, 64));
+    }
+    float tmax = __builtin_fmaxf(__builtin_fmaxf(tb[0], tb[1]), __builtin_fmaxf(tb[2], tb[3]));
+    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)));
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {
+      const bool live = tb[cc] > -INFINITY;   // a slot past the list's end has no keys
+      const float nm = live ? kLog2_448 - tb[cc] : 0.0f;
+      const float gw = live ? __builtin_amdgcn_exp2f(tb[cc] - m_run) * (1.0f / 448.0f) : 0.0f;
+      const float c = chunk_scale(cs, cc);
+      const int b = cc >> 1, r0 = 8 * (cc & 1);
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int w = codes4(s[b][r0 + 4 * j], s[b][r0 + 4 * j + 1], s[b][r0 + 4 * j + 2], s[b][r0 + 4 * j + 3], c, nm);
+        p8[2 * cc + j] = w;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        pb[cc][4 * j] = static_cast<_Float16>(lo.x * gw);
+        pb[cc][4 * j + 1] = static_cast<_Float16>(lo.y * gw);
+        pb[cc][4 * j + 2] = static_cast<_Float16>(hi.x * gw);
+        pb[cc][4 * j + 3] = static_cast<_Float16>(hi.y * gw);
+      }
+    }
+    dump_codes(ds);
+    l_run += half_sum(pb);
+  };
+  // ---- O^T += wpv * V8^T P8^T on the fp8 MFMA (64-key LOW and SKIM tiles):
+  // row d = 32db + ln of the staged E4M3 V^T, bytes 32lh .. 32lh + 31
+  auto pv8 = [&](const unsigned char* st) __attribute__((always_inline)) {
+    i32x8 va[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; db++) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(r1(st) + offv8[0] + db * 32 * 64);
+      const uint4 hi = *reinterpret_cast<const uint4*>(r1(st) + offv8[1] + db * 32 * 64);
+      va[db] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; db++) {
+      const f32x16 x = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], p8, f32x16{}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[db][r] = __builtin_fmaf(x[r], wpv, acc[db][r]);
+    }
+  };
   // a kept tile (FULL: bf16 scores, LOW: E4M3 scores): masks and softmax of
   // its scores s
   auto kept_soft = [&](auto low_tag, int t, f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) {
@@ -668,7 +837,8 @@ void k3_attn(AttnArgs a) {
     if constexpr (G == 1) {
       const int J = list_at(t);
       if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
-      softmax(s, c, row_max(s) * c.c[0]);
+      if constexpr (LOW) quant_soft64(s, c.c[0], c.v, t - tLow);
+      else softmax(s, c, row_max(s) * c.c[0]);
     } else {
       // Lists are ascending, so a partial group or the ragged last block only
       // occurs in the last step of the phase.  Register (b, r) is key
@@ -699,36 +869,42 @@ void k3_attn(AttnArgs a) {
             if (kk >= ql[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
           }
       }
-      float tmax = -INFINITY;
+      if constexpr (LOW) {
+        quant_soft_g(s, c, t - tLow);
+      } else {
+        float tmax = -INFINITY;
 #pragma unroll
-      for (int cc = 0; cc < 4; cc++) {
-        float m = -INFINITY;
+        for (int cc = 0; cc < 4; cc++) {
+          float m = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
-        tmax = __builtin_fmaxf(tmax, m * chunk_scale(c, cc));
+          for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
+          tmax = __builtin_fmaxf(tmax, m * chunk_scale(c, cc));
+        }
+        softmax(s, c, tmax);
       }
-      softmax(s, c, tmax);
     }
   };
   // a kept tile staged in `st`: scores, softmax, P.V
   auto kept_step = [&](auto low_tag, int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q8) __attribute__((always_inline)) {
+    constexpr bool LOW = decltype(low_tag)::value;
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    if constexpr (decltype(low_tag)::value) scores_fp8(st, s, q8);
+    if constexpr (LOW) scores_fp8(st, s, q8);
     else scores_bf16(st, s);
     kept_soft(low_tag, t, s, c);
-    pv(st);
+    if constexpr (LOW && G == 1) pv8(st);
+    else pv(st);
   };
-  // a SKIM tile (64-key blocks): mask and softmax of its scores s
+  // a SKIM tile (64-key blocks): mask and quantised probabilities of its scores s
   auto skim_soft = [&](int t, f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) {
     const int J = list_at(t);
     if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
-    softmax(s, c, row_max(s) * c.c[0]);
+    quant_soft64(s, c.c[0], c.v, t - tLow);
   };
   auto skim_step = [&](int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
     scores_fp4(st, s, q4, q4s);
     skim_soft(t, s, c);
-    pv(st);
+    pv8(st);
   };
   // pooled keys of a chunk of 64 skipped-candidate blocks: scores only (hi
   // part from R0, lo part from R1), then the bias and the softmax
@@ -804,7 +980,6 @@ void k3_attn(AttnArgs a) {
   // the E4M3 copy of this lane's Q (32 bytes per fp8 instruction i = bf16
   // chunks 4i..4i+3), from the bf16 registers
   auto make_q8 = [&](i32x8* q8reg) __attribute__((always_inline)) {
-    const float iq = reinterpret_cast<const float*>(ws + a.L.iq)[row];
 #pragma unroll
     for (int i = 0; i < D / 64; i++) {
 #pragma unroll
@@ -935,9 +1110,10 @@ void k3_attn(AttnArgs a) {
     int t = 0;
     // One step.  S_fn(s): its scores from the stage; soft_fn(s, c): masks and
     // softmax.  HS: the step scores; HP: it runs P.V; U1: its scores also
-    // read R1 (a skip chunk's lo half).
-    auto split_step = [&](auto nk, auto hs, auto hp, auto u1, auto S_fn, auto soft_fn) __attribute__((always_inline)) {
+    // read R1 (a skip chunk's lo half); PV8: its P.V is the fp8 one.
+    auto split_step = [&](auto nk, auto hs, auto hp, auto u1, auto q8pv, auto S_fn, auto soft_fn) __attribute__((always_inline)) {
       constexpr bool HS = decltype(hs)::value, HP = decltype(hp)::value, U1 = decltype(u1)::value;
+      constexpr bool PV8 = decltype(q8pv)::value;   // P.V on the fp8 MFMA (quantised 64-key steps)
       const bool more = t + 1 < nSteps;
       const StepScale<G> cur = cA;   // issuing step t+1's R0 half rewrites cA
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -953,7 +1129,8 @@ void k3_attn(AttnArgs a) {
       if constexpr (HP) {
         wait_vm_n(a_count(t + 1));   // R1 of step t landed in every wave
         bar();
-        pv(stA);
+        if constexpr (PV8) pv8(stA);
+        else pv(stA);
       }
       wait_vm0_lgkm0();              // R0 of step t+1 landed, this wave's R1 reads returned
       bar();
@@ -967,21 +1144,21 @@ void k3_attn(AttnArgs a) {
     auto no_soft = [&](f32x16*, const StepScale<G>&) {};
     while (t < nS2) {
       if ((t & 1) == 0)
-        split_step(KSkipPV{}, T1{}, T0{}, T1{},
+        split_step(KSkipPV{}, T1{}, T0{}, T1{}, T0{},
                    [&](f32x16* s) __attribute__((always_inline)) { skip_S(stA, s); },
                    [&](f32x16* s, const StepScale<G>&) __attribute__((always_inline)) { skip_soft(t, s); });
       else
-        split_step(KAfterSkip{}, T0{}, T1{}, T0{}, no_S, no_soft);
+        split_step(KAfterSkip{}, T0{}, T1{}, T0{}, T0{}, no_S, no_soft);
     }
     while (t < tLow)
-      split_step(KAfterFull{}, T1{}, T1{}, T0{},
+      split_step(KAfterFull{}, T1{}, T1{}, T0{}, T0{},
                  [&](f32x16* s) __attribute__((always_inline)) { scores_bf16(stA, s); },
                  [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T0{}, t, s, c); });
     if (t < tSk) {
       i32x8 q8reg[D / 64];
       make_q8(q8reg);
       while (t < tSk)
-        split_step(KLow{}, T1{}, T1{}, T0{},
+        split_step(KLow{}, T1{}, T1{}, T0{}, std::integral_constant<bool, G == 1>{},
                    [&](f32x16* s) __attribute__((always_inline)) { scores_fp8(stA, s, q8reg); },
                    [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T1{}, t, s, c); });
     }
@@ -991,7 +1168,7 @@ void k3_attn(AttnArgs a) {
         int q4s[D / 64];
         make_q4(q4reg, q4s);
         while (t < nSteps)
-          split_step(KSkimOnly{}, T1{}, T1{}, T0{},
+          split_step(KSkimOnly{}, T1{}, T1{}, T0{}, T1{},
                      [&](f32x16* s) __attribute__((always_inline)) { scores_fp4(stA, s, q4reg, q4s); },
                      [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { skim_soft(t, s, c); });
       }
@@ -1027,31 +1204,37 @@ void k3_attn(AttnArgs a) {
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool DUMP>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   if (a.skim && a.d.Bk != 64) return hipErrorInvalidValue;
   if (a.d.Nk > kMaxNk || a.list_cap < 1 || a.list_cap > a.d.Nk) return hipErrorInvalidValue;
+  if (DUMP && (!a.dslot || !a.dump || a.dsteps < 1)) return hipErrorInvalidValue;
   const size_t lds = ((size_t)a.list_cap * 2 + 15) / 16 * 16;   // the row's list (dynamic LDS)
   const dim3 grid(a.d.BH * a.d.Nq), block(NW * 64);
   if (a.skim)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64, true>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, true, DUMP>), grid, block, lds, s, a);
   else if (a.d.Bk == 64)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP>), grid, block, lds, s, a);
   else if (a.d.Bk == 16)
-    hipLaunchKernelGGL((k3_attn<D, NW, 16, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 16, false, DUMP>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((k3_attn<D, NW, 8, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 8, false, DUMP>), grid, block, lds, s, a);
   return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_dn(const AttnArgs& a, hipStream_t s) {
+  return a.dump ? launch_one<D, NW, true>(a, s) : launch_one<D, NW, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int D = a.d.D, BQ = a.d.Bq;
-  if (D == 128 && BQ == 128) return launch_one<128, 4>(a, s);
-  if (D == 128 && BQ == 64) return launch_one<128, 2>(a, s);
-  if (D == 64 && BQ == 128) return launch_one<64, 4>(a, s);
-  if (D == 64 && BQ == 64) return launch_one<64, 2>(a, s);
+  if (D == 128 && BQ == 128) return launch_dn<128, 4>(a, s);
+  if (D == 128 && BQ == 64) return launch_dn<128, 2>(a, s);
+  if (D == 64 && BQ == 128) return launch_dn<64, 4>(a, s);
+  if (D == 64 && BQ == 64) return launch_dn<64, 2>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -70,6 +70,17 @@ __host__ __device__ inline int vt_key(int e) {
   return 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
 }
 
+// Key order of a stored E4M3 V^T row of a 64-key tile (the A operand of the
+// fp8 P.V MFMA).  The fp8 MFMA takes 32 bytes per lane in the same k
+// positions for A and B; the B operand of a lane (query column, half h) is
+// its own 32 probability codes in register order p = 16b + r, i.e. of keys
+// 32b + 8(r/4) + 4h + r%4.  Byte 32h + p of V^T row d therefore holds
+// V[key][d] of that key.
+__host__ __device__ inline int pv8_key(int e) {
+  const int h = e >> 5, p = e & 31, r = p & 15;
+  return 32 * (p >> 4) + 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
 // d permutation of a stored fp8 K row: byte position 64i + 32g + p holds
 // d = 64i + 16(p/8) + 8g + p%8, so that a lane (group g) reads its 32 bytes
 // for instruction i contiguously, in the order its bf16 Q registers give.
@@ -114,12 +125,6 @@ __device__ inline uint32_t e2m1_code(float y) {
   else if (a < 4.0f) c = static_cast<uint32_t>(__builtin_rintf(a)) + 2u;         // 2, 3, 4 -> 4, 5, 6
   else c = __builtin_rintf(a * 0.5f) >= 3.0f ? 7u : 6u;                          // 6 (or 8) -> 7, 4 -> 6
   return c | (y < 0.0f ? 8u : 0u);
-}
-// value of an E2M1 code
-__device__ inline float e2m1_value(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const float mag = m < 2u ? 0.5f * static_cast<float>(m) : ldexpf(1.0f + 0.5f * static_cast<float>(m & 1u), (int)(m >> 1) - 1);
-  return (c & 8u) ? -mag : mag;
 }
 
 // ---------------------------------------------------------------------------

@@ -80,7 +80,8 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim) 
       return at;
     };
     sl.vt = sub(Nk * Bk * D * 2);
-    sl.vlow = sub(Nk * Bk * D * 2);
+    sl.v8t = sub(Nk * Bk * D);
+    sl.vlow = sub(Bk < 64 ? Nk * Bk * D * 2 : 0);
     sl.k8 = sub(Nk * Bk * D);
     sl.kbhi = sub(Nk * D * 2);
     sl.kblo = sub(Nk * D * 2);
@@ -88,7 +89,6 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim) 
     const size_t k4n = skim ? Nk * Bk : 0;
     sl.k4 = sub(k4n * D / 2);
     sl.k4s = sub(k4n * D / 32);
-    sl.vskim = sub(k4n * D * 2);
     sl.bytes = o;
   }
   L.slab = take(BH * L.sl.bytes);
@@ -280,7 +280,8 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
   return ok();
 }
 
-tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const void* v, void* o, void* stream) {
+static tattn_status forward_impl(tattn_plan_t p, const void* q, const void* k, const void* v, void* o,
+                                 const int32_t* dslot, int32_t dsteps, uint8_t* dump, void* stream) {
   if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
   if (!q || !o) return fail(TATTN_E_INVALID, "q and o must be non-NULL");
   if (!aligned16(q) || !aligned16(o)) return fail(TATTN_E_INVALID, "q and o must be 16-byte aligned");
@@ -288,9 +289,29 @@ tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const v
   if (!p->has_tiers) return fail(TATTN_E_STATE, "external-mode plan has no tiers yet (call tattn_plan_set_tiers)");
   AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), o,
              p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d, skim_on(p->cfg) ? 1 : 0,
-             list_cap(p->cfg, p->d)};
+             list_cap(p->cfg, p->d), dslot, dump, dsteps};
   hipError_t e = launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return ok();
+}
+
+tattn_status tattn_forward(tattn_plan_t p, const void* q, const void* k, const void* v, void* o, void* stream) {
+  return forward_impl(p, q, k, v, o, nullptr, 0, nullptr, stream);
+}
+
+tattn_status tattn_forward_dump(tattn_plan_t p, const void* q, const void* k, const void* v, void* o,
+                                const int32_t* dump_slot, int32_t dump_steps, uint8_t* dump, void* stream) {
+  if (!dump_slot || !dump) return fail(TATTN_E_INVALID, "dump_slot and dump must be non-NULL");
+  if (dump_steps < 1) return fail(TATTN_E_INVALID, "dump_steps must be >= 1 (got %d)", dump_steps);
+  if (!aligned16(dump)) return fail(TATTN_E_INVALID, "dump must be 16-byte aligned");
+  return forward_impl(p, q, k, v, o, dump_slot, dump_steps, dump, stream);
+}
+
+tattn_status tattn_list_bound(const tattn_config* cfg, int32_t* bound) {
+  tattn_status st = validate(cfg);
+  if (st != TATTN_OK) return st;
+  if (!bound) return fail(TATTN_E_INVALID, "bound is NULL");
+  *bound = list_cap(*cfg, make_dims(*cfg));
   return ok();
 }
 
@@ -389,7 +410,7 @@ tattn_status tattn_plan_get_pool(tattn_plan_t p, float* qbar, float* kbar, float
   return sync(s);
 }
 
-tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* host_vlow, void* stream) {
+tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint8_t* host_v8, void* stream) {
   if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Dims& d = p->d;
@@ -400,22 +421,23 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint16_t* ho
     if ((st = copy_out(slab.data(), p->ws + p->L.slab + bh * p->L.sl.bytes, slab.size(), s)) != TATTN_OK) return st;
     if ((st = sync(s)) != TATTN_OK) return st;
     const uint8_t* k8 = slab.data() + p->L.sl.k8;
-    const uint16_t* vl = reinterpret_cast<const uint16_t*>(slab.data() + p->L.sl.vlow);
+    const uint8_t* v8 = slab.data() + p->L.sl.v8t;
+    // stored position of key r inside a V^T row of a block
+    std::vector<int> vpos(d.Bk);
+    for (int e = 0; e < d.Bk; e++) vpos[d.Bk == 64 ? pv8_key(e) : e] = e;
     for (int J = 0; J < d.Nk; J++)
       for (int r = 0; r < d.Bk && J * d.Bk + r < d.N; r++) {
         const size_t n = (size_t)J * d.Bk + r;
         if (host_k8)
           for (int c = 0; c < d.D; c++) host_k8[(bh * d.N + n) * d.D + c] = k8[J * tile + r * d.D + k8_pos(c)];
-        if (host_vlow)
-          for (int c = 0; c < d.D; c++)
-            host_vlow[(bh * d.N + n) * d.D + c] = vl[J * tile + c * d.Bk + (d.Bk == 64 ? vt_pos(r) : d.Bk == 16 ? vt16_pos(r) : r)];
+        if (host_v8)
+          for (int c = 0; c < d.D; c++) host_v8[(bh * d.N + n) * d.D + c] = v8[J * tile + c * d.Bk + vpos[r]];
       }
   }
   return ok();
 }
 
-tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_k4s, uint16_t* host_vskim,
-                                void* stream) {
+tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_k4s, void* stream) {
   if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
   if (!skim_on(p->cfg)) return fail(TATTN_E_STATE, "MXFP4 copies exist only with the SKIM tier (tau_skim > 0)");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -428,14 +450,11 @@ tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_
     if ((st = sync(s)) != TATTN_OK) return st;
     const uint8_t* k4 = slab.data() + p->L.sl.k4;
     const uint8_t* k4s = slab.data() + p->L.sl.k4s;
-    const uint16_t* vs = reinterpret_cast<const uint16_t*>(slab.data() + p->L.sl.vskim);
     for (int J = 0; J < d.Nk; J++)
       for (int r = 0; r < 64 && J * 64 + r < d.N; r++) {
         const size_t n = (size_t)J * 64 + r, at = bh * d.N + n;
         if (host_k4) std::memcpy(host_k4 + at * hb, k4 + n * hb, hb);
         if (host_k4s) std::memcpy(host_k4s + at * nsc, k4s + n * nsc, nsc);
-        if (host_vskim)
-          for (int c = 0; c < d.D; c++) host_vskim[at * d.D + c] = vs[(size_t)J * 64 * d.D + c * 64 + vt_pos(r)];
       }
   }
   return ok();
@@ -469,6 +488,12 @@ tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {
   if (e != hipSuccess) return hip_fail(e, "device synchronize");
   e = hipMemcpy(t.data(), p->ws + p->L.tiers, t.size(), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "device-to-host copy");
+  int32_t flag = 0;
+  e = hipMemcpy(&flag, p->ws + p->L.flag, sizeof(flag), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "device-to-host copy");
+  if (flag & 1)
+    return fail(TATTN_E_STATE, "a forward met a row with more kept tiles than its list bound (%d): the row was cut",
+                list_cap(p->cfg, d));
   tattn_stats st{};
   const double D = d.D;
   for (int bh = 0; bh < d.BH; bh++)
@@ -483,14 +508,15 @@ tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {
         if (tr[J] == TATTN_FULL) {
           st.n_full++;
           st.flops_bf16 += 4.0 * mI * nJ * D;
-        } else if (tr[J] == TATTN_LOW) {   // fp8 scores, 16-bit P.V
+        } else if (tr[J] == TATTN_LOW) {   // fp8 scores; fp8 P.V (64-key blocks) or fp16 P.V
           st.n_low++;
           st.flops_fp8 += 2.0 * mI * nJ * D;
-          st.flops_bf16 += 2.0 * mI * nJ * D;
-        } else if (tr[J] == TATTN_SKIM) {  // fp4 scores, 16-bit P.V
+          if (d.Bk == 64) st.flops_fp8 += 2.0 * mI * nJ * D;
+          else st.flops_bf16 += 2.0 * mI * nJ * D;
+        } else if (tr[J] == TATTN_SKIM) {  // fp4 scores, fp8 P.V
           st.n_skim++;
           st.flops_fp4 += 2.0 * mI * nJ * D;
-          st.flops_bf16 += 2.0 * mI * nJ * D;
+          st.flops_fp8 += 2.0 * mI * nJ * D;
         } else {
           st.n_skip++;
           st.flops_bf16 += 4.0 * mI * D;

@@ -25,9 +25,12 @@ struct Dims {
 // caller's K: one contiguous block per (b, h), so a single buffer resource
 // with scalar sub-offsets covers it.  Offsets are bytes from the slab start.
 struct Slab {
-  size_t vt;      // fp16 [Nk][D][64]   V^T, keys permuted within a tile (vt_pos)
-  size_t vlow;    // fp16 [Nk][D][64]   low-tier values fl16(decode(E4M3) * sv), same layout
-  size_t k8;      // u8   [Nk][64][D]   E4M3 K, d permuted within a row (k8_pos)
+  size_t vt;      // fp16 [Nk][D][Bk]   V^T, keys permuted within a tile (vt_pos)
+  size_t v8t;     // u8   [Nk][D][Bk]   E4M3 V^T: 64-key blocks in the fp8 P.V operand's
+                  //                    key order (pv8_key), smaller blocks in key order
+  size_t vlow;    // fp16 [Nk][D][Bk]   16- and 8-key blocks only: the low tier's fp16 V
+                  //                    operand fl16(fl32(decode(E4M3) * sv)), vt's layout
+  size_t k8;      // u8   [Nk][Bk][D]   E4M3 K, d permuted within a row (k8_pos)
   size_t kbhi;    // bf16 [Nk][D]       K block means, hi part
   size_t kblo;    // bf16 [Nk][D]       K block means, lo part (kbar = hi + lo to ~2^-17)
   size_t vbarT;   // fp16 [NkC][D][64]  V block means transposed per chunk of 64 blocks,
@@ -35,7 +38,6 @@ struct Slab {
   // SKIM tier only (zero-sized otherwise; 64-key blocks)
   size_t k4;      // u8   [Nk][64][D/2]  MXFP4 K codes, channel 2m in the low nibble of byte m
   size_t k4s;     // u8   [Nk][64][D/32] E8M0 scale of each 32 channels of a K row
-  size_t vskim;   // fp16 [Nk][D][64]   SKIM value operand fl16(decode(MXFP4 V)), vt_pos order
   size_t bytes;   // slab size (256-byte multiple)
 };
 
@@ -61,7 +63,9 @@ struct Layout {
   size_t kvar, m2k;             // [BH][Nk][D], [BH][Nk]   key variance per dim, mean-square total
   size_t vvar, m2v, vnorm;      // [BH][Nk] each           value variance total, mean-square total, mean norm
   size_t s2;                    // f64 [BH][Nq][Nk]        within-tile score spread
-  size_t flag;                  // i32 [4]   device-side error flags
+  size_t flag;                  // i32 [4]   device-side error flags (cleared by the pooling
+                                //           kernel; [0] bit 0: a row held more kept tiles
+                                //           than the fused kernel's list bound)
   size_t total;
 };
 
@@ -108,6 +112,12 @@ struct AttnArgs {
   Dims d;
   int skim;       // the plan may hold SKIM tiles (64-key blocks)
   int list_cap;   // bound on a row's FULL + LOW + SKIM tiles under the plan's mode (<= Nk)
+  // probability-code dump (tattn_forward_dump; null otherwise): row r with
+  // dslot[r] >= 0 writes the codes of its LOW and SKIM steps s < dsteps to
+  // dump[((dslot[r] * dsteps + s) * Bq + row in block) * 64 + 32 * half + p]
+  const int* dslot;
+  unsigned char* dump;
+  int dsteps;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
