@@ -7,10 +7,13 @@ heads, d = 128, 128x64 tiles, tau_hi = 0.01, tau_lo = 0.001, bf16 inputs
 already resident in HBM.
 
 Prints ONE JSON line.  `value` is dense-equivalent TFLOP/s of the step
-(4 N^2 d H / t_step).  The roofline entry covers the fused kernel (K3): its
-executed MFMA work, with fp8 flops counted at half weight (the fp8 peak is
-twice the bf16 one), over its average launch time measured with HIP events on
-the stream it runs on, against the 2.5 PFLOP/s dense bf16 peak.
+(4 N^2 d H / t_step).  The roofline entry covers the fused kernel (K3): the
+MFMA utilisation on kept tiles, U = (F_bf16 / P_bf16 + F_fp8 / P_fp8 + F_fp4 /
+P_fp4) / t, with F the algorithmic flops of the tier map (FULL tiles 4 m n d in
+bf16, LOW tiles 4 m n d in fp8, SKIM tiles 2 m n d in fp4 plus 2 m n d in fp8,
+SKIP tiles 4 m d in bf16) and t the kernel's average launch time measured with
+HIP events on the stream it runs on; reported as bf16-equivalent TFLOP/s
+against the 2.5 PFLOP/s dense bf16 peak, so frac = U.
 """
 import argparse
 import hashlib
@@ -27,7 +30,7 @@ PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 MFMA
 PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense fp8 MFMA
 PEAK_FP4 = 10100.0   # TFLOP/s, MI355X dense fp4 MFMA
 PEAK_HBM = 8000.0    # GB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k3_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k3_counters.json")
 
 
 def parse():
@@ -63,17 +66,18 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """HBM traffic of one K3 launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source and this workload; else None."""
+def load_counters(workload):
+    """Counter figures of one K3 launch from committed rocprofv3 runs (HBM bytes
+    from FETCH_SIZE / WRITE_SIZE, copy-calibrated; the MFMA-busy fraction), if
+    they were taken on the current kernel source and this workload; else {}."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(COUNTERS_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("source_hash") != source_hash() or t.get("workload") != workload:
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    return t
 
 
 def _cpu_model():
@@ -99,46 +103,73 @@ def _blas_vendor():
         return "unknown"
 
 
-def cpu_baseline(g, cfg, budget_s, price=None):
-    """Time the oracle (plan + forward) on one head: its full router, then as
-    many query blocks as fit in the budget.  Returns dense-equivalent TFLOP/s
-    of the sample, scaled like the GPU figure (4 * rows * N * d per row block)."""
+def _oracle_worker(args):
+    """One pool worker: the oracle's plan of one head (timed), then forward
+    query blocks in a fixed random order until the budget is spent (timed)."""
+    q, k, v, ocfg, n_qblocks, block_q, block_k, budget_s, seed = args
+    from threadpoolctl import threadpool_limits
     import numpy as np
     from oracle import tattn as T
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        plan = T.oracle_plan(q, k, v, ocfg)
+        t_plan = time.perf_counter() - t0
+        rows = blocks = 0
+        t1 = time.perf_counter()
+        for I in np.random.default_rng(seed).permutation(n_qblocks):
+            T.oracle_forward(q, k, v, plan, block_q, block_k, rows=[int(I)])
+            rows += min(block_q, q.shape[0] - int(I) * block_q)
+            blocks += 1
+            if time.perf_counter() - t1 > budget_s:
+                break
+        t_fwd = time.perf_counter() - t1
+    return t_plan, t_fwd, rows, blocks
 
-    class OC:
-        block_q, block_k = cfg.block_q, cfg.block_k
-        tau_hi, tau_lo = float(np.float32(cfg.tau_hi)), float(np.float32(cfg.tau_lo))
-        top_k, mode = cfg.top_k, (4 if price is not None else cfg.mode)
-        keep_min, keep_max, full_frac = 0.05, 0.5, 0.1
-        entropy_samples = 256
-        tau_skim = float(np.float32(cfg.tau_skim))
-    OC.price = float(np.float32(price)) if price is not None else 0.0
-    q, k, v = g["q"][0, 0], g["k"][0, 0], g["v"][0, 0]
+
+class _OracleCfg:
+    """The oracle's view of a workload's tier rule (plain attributes, picklable)."""
+
+    def __init__(self, cfg, price):
+        import numpy as np
+        f32 = lambda x: float(np.float32(x))
+        self.block_q, self.block_k = cfg.block_q, cfg.block_k
+        self.tau_hi, self.tau_lo, self.tau_skim = f32(cfg.tau_hi), f32(cfg.tau_lo), f32(cfg.tau_skim)
+        self.top_k, self.mode = cfg.top_k, (4 if price is not None else cfg.mode)
+        self.keep_min, self.keep_max, self.full_frac = f32(cfg.keep_min), f32(cfg.keep_max), f32(cfg.full_frac)
+        self.entropy_samples = cfg.entropy_samples
+        self.price = f32(price) if price is not None else 0.0
+
+
+def cpu_baseline(g, cfg, budget_s, price=None):
+    """The oracle on the host's cores: a process pool over heads, one BLAS
+    thread per worker, each worker owning one head: its full plan (pool,
+    router, tiers) timed, then query blocks of its forward until the budget is
+    spent.  Returns the pool's aggregate dense-equivalent TFLOP/s (each
+    worker's rows at 4 rows N d, its plan charged pro rata to the query blocks
+    it ran), with plan and forward times reported separately."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), g["q"].shape[1]))
+    oc = _OracleCfg(cfg, price)
+    jobs = [(g["q"][0, h], g["k"][0, h], g["v"][0, h], oc, cfg.n_qblocks, cfg.block_q, cfg.block_k, budget_s, h)
+            for h in range(workers)]
     t0 = time.perf_counter()
-    plan = T.oracle_plan(q, k, v, OC)
-    t_plan = time.perf_counter() - t0
-    N, d = q.shape
-    rows = 0
-    blocks = 0
-    order = np.random.default_rng(0).permutation(cfg.n_qblocks)
-    t1 = time.perf_counter()
-    for I in order:
-        T.oracle_forward(q, k, v, plan, cfg.block_q, cfg.block_k, rows=[int(I)])
-        rows += min(cfg.block_q, N - int(I) * cfg.block_q)
-        blocks += 1
-        if time.perf_counter() - t1 > budget_s:
-            break
-    t_fwd = time.perf_counter() - t1
-    # plan cost attributed per query block, as the GPU step includes it
-    t_sample = t_fwd + t_plan * blocks / cfg.n_qblocks
-    dense = 4.0 * rows * N * d
-    threads = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
-    return {"value": dense / t_sample / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(threads),
-            "kind": "oracle", "cpu_model": _cpu_model(), "blas": _blas_vendor(),
-            "sample": f"head 0 of {cfg.heads}: full router ({t_plan:.2f}s, charged pro rata) + {blocks} of "
-                      f"{cfg.n_qblocks} query blocks ({rows} rows) forward in {t_fwd:.2f}s; numpy float64, "
-                      f"BLAS threads={threads}"}
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_worker, jobs))
+    wall = time.perf_counter() - t0
+    N, d = g["q"].shape[2], g["q"].shape[3]
+    rate = 0.0
+    for t_plan, t_fwd, rows, blocks in res:
+        rate += 4.0 * rows * N * d / (t_fwd + t_plan * blocks / cfg.n_qblocks)
+    t_plan = sum(r[0] for r in res) / len(res)
+    t_blk = sum(r[1] for r in res) / sum(r[3] for r in res)
+    return {"value": round(rate / 1e12, 5), "unit": "TFLOP/s (dense-equivalent)", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas": _blas_vendor(),
+            "plan_s_per_head": round(t_plan, 3), "forward_s_per_query_block": round(t_blk, 4),
+            "step_s_estimate": round((t_plan + t_blk * cfg.n_qblocks) * cfg.heads / workers, 1),
+            "sample": f"{workers} worker processes (one BLAS thread each), one head each of {cfg.heads}: the full "
+                      f"plan ({t_plan:.2f} s per head) then {sum(r[3] for r in res)} query blocks of forward in "
+                      f"total ({t_blk:.3f} s each); numpy float64 oracle, pool wall {wall:.1f} s"}
 
 
 def main():
@@ -289,7 +320,7 @@ def main():
     bf16_equiv = st["flops_bf16"] + st["flops_fp8"] * PEAK_BF16 / PEAK_FP8 + st["flops_fp4"] * PEAK_BF16 / PEAK_FP4
     achieved = bf16_equiv / (ms_k3 * 1e-3) / 1e12
     tiles = st["n_full"] + st["n_low"] + st["n_skip"] + st["n_skim"]
-    traffic = load_traffic(args.workload)
+    counters = load_counters(args.workload)
 
     # the plan (K1 + K2) as an HBM-bound pass: algorithmic bytes = read Q, K, V
     # (bf16) + E4M3 K and V + float32 means and scales (K1), + the means read
@@ -345,12 +376,13 @@ def main():
         "quality": quality,
         "skim_tier": skim_cmp,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16, 4), "traffic": traffic,
+                     "frac": round(achieved / PEAK_BF16, 4), "traffic": counters.get("bytes_per_launch"),
                      "kernel": "k3_attn (fused three-tier forward)",
                      "work": f"bf16 {st['flops_bf16'] / 1e12:.3f} TFLOP + fp8 {st['flops_fp8'] / 1e12:.3f} TFLOP "
-                             f"(fp8 at half weight)"
+                             f"(fp8 at the bf16/fp8 peak ratio, 1/2)"
                              + (f" + fp4 {st['flops_fp4'] / 1e12:.3f} TFLOP (fp4 at the bf16/fp4 peak ratio)"
-                                if st["n_skim"] else "") + " per launch"},
+                                if st["n_skim"] else "") + " per launch: U = frac",
+                     "mfma_busy": counters.get("mfma_busy")},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

@@ -583,8 +583,15 @@ void k3_attn(AttnArgs a) {
   for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   f16x8 pb[4];
-  i32x8 p8;        // probability codes of a quantised step (LOW, SKIM)
-  float wpv = 0;   // its P.V weight (64-key blocks)
+  i32x8 p8;          // probability codes of a quantised step (LOW, SKIM)
+  // From the first quantised 64-key step on, the accumulator holds O^T / accF
+  // (relative to 2^m): a step's weight w = 2^(tile max - m) sv / 448 is split
+  // into w = wm 2^wk, wm in [1, 2); the MFMA's per-column E8M0 scale applies
+  // 2^wk to the codes, the accumulator is multiplied by accF / wm and the
+  // MFMA accumulates into it directly, and accF becomes wm.
+  float accF = 1.0f;
+  float wr = 1.0f;   // accF / wm of the current quantised step
+  int wk = 127;      // its E8M0 scale byte, wk + 127
   const int dsl = DUMP ? a.dslot[row] : -1;
   // sum of the fp16 P values the P.V MFMA multiplies, two per
   // v_dot2_f32_f16 (fp32 accumulation), so numerator and denominator see the
@@ -683,21 +690,25 @@ void k3_attn(AttnArgs a) {
   };
   // raise the running reference m to a step's maximum tmax (base 2, already
   // reduced over the lane pair) when it exceeds m by more than kLazy
-  auto raise_max = [&](float tmax) __attribute__((always_inline)) {
+  auto raise_max = [&](float tmax, auto lazy) __attribute__((always_inline)) {
     const bool need = tmax > m_run + kLazy;
     if (__ballot(need)) {
       const float mn = need ? tmax : m_run;
       const float al = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
       l_run *= al;
+      if constexpr (decltype(lazy)::value) {
+        accF *= al;   // the quantised phases carry the factor instead
+      } else {
 #pragma unroll
-      for (int db = 0; db < D / 32; db++)
+        for (int db = 0; db < D / 32; db++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc[db][r] *= al;
+          for (int r = 0; r < 16; r++) acc[db][r] *= al;
+      }
       m_run = mn;
     }
   };
   auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
-    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)));
+    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)), std::false_type{});
     const float nm = -m_run;
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
@@ -749,20 +760,23 @@ void k3_attn(AttnArgs a) {
       (void)ds;
     }
   };
-  // codes of four scores x = s * c - tm + log2(448) into one dword
+  // codes of four scores, x = 2^(s * c - tm + log2(448)), into one dword.
+  // x is at most 448 up to rounding (far below 464, where the converter
+  // would stop rounding to 448), so it needs no clamp.
   auto codes4 = [&](float s0, float s1, float s2, float s3, float c, float nm) __attribute__((always_inline)) {
-    const int w = cvt_fp8x2<false>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, nm)),
-                                   __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, nm)), 0);
-    return cvt_fp8x2<true>(__builtin_amdgcn_exp2f(__builtin_fmaf(s2, c, nm)),
-                           __builtin_amdgcn_exp2f(__builtin_fmaf(s3, c, nm)), w);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, nm)),
+                                                  __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, nm)), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(__builtin_fmaf(s2, c, nm)),
+                                           __builtin_amdgcn_exp2f(__builtin_fmaf(s3, c, nm)), w, true);
   };
   // 64-key tile: one maximum per row (over both lane halves); the row sum of
   // the codes from the fp8 MFMA against ones (every result register holds the
-  // column sum, so each lane half adds half of it); the P.V weight in wpv
+  // column sum, so each lane half adds half of it); the P.V weight split into
+  // the accumulator factor and the E8M0 column scale (wr, wk)
   auto quant_soft64 = [&](f32x16* s, float c, float sv, int ds) __attribute__((always_inline)) {
     float tm = row_max(s);
     tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32, 64)) * c;
-    raise_max(tm);
+    raise_max(tm, std::true_type{});
     const float nm = kLog2_448 - tm;
 #pragma unroll
     for (int w = 0; w < 8; w++) {
@@ -775,7 +789,16 @@ void k3_attn(AttnArgs a) {
     const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p8, f32x16{}, 0, 0, 0, 0, 0, 0);
     const float g = __builtin_amdgcn_exp2f(tm - m_run);
     l_run = __builtin_fmaf(rs[0], g * (0.5f / 448.0f), l_run);
-    wpv = g * (sv * (1.0f / 448.0f));
+    const float w = g * (sv * (1.0f / 448.0f));
+    // w = wm 2^e, wm in [1, 2).  A weight below 2^-127 (a tile negligible
+    // against the running reference) leaves accF and adds its codes at the
+    // smallest scale, 2^-127.
+    const int e = __builtin_amdgcn_frexp_expf(w) - 1;
+    const float wm = __builtin_amdgcn_frexp_mantf(w) * 2.0f;
+    const bool tiny = e < -127 || !(w > 0.0f);
+    wr = tiny ? 1.0f : accF * __builtin_amdgcn_rcpf(wm);
+    accF = tiny ? accF : wm;
+    wk = tiny ? 0 : e + 127;
   };
   // 16- and 8-key blocks: one maximum per block (chunk cc of the lane: 16-key
   // block cc over both lane halves, or 8-key slot 2cc + lane half), and the
@@ -791,7 +814,7 @@ void k3_attn(AttnArgs a) {
       if constexpr (G == 4) tb[cc] = __builtin_fmaxf(tb[cc], __shfl_xor(tb[cc], 32, 64));
     }
     float tmax = __builtin_fmaxf(__builtin_fmaxf(tb[0], tb[1]), __builtin_fmaxf(tb[2], tb[3]));
-    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)));
+    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)), std::false_type{});
 #pragma unroll
     for (int cc = 0; cc < 4; cc++) {
       const bool live = tb[cc] > -INFINITY;   // a slot past the list's end has no keys
@@ -813,8 +836,9 @@ void k3_attn(AttnArgs a) {
     dump_codes(ds);
     l_run += half_sum(pb);
   };
-  // ---- O^T += wpv * V8^T P8^T on the fp8 MFMA (64-key LOW and SKIM tiles):
-  // row d = 32db + ln of the staged E4M3 V^T, bytes 32lh .. 32lh + 31
+  // ---- acc = acc * wr + V8^T (P8^T 2^(wk - 127)) on the fp8 MFMA (64-key LOW
+  // and SKIM tiles): row d = 32db + ln of the staged E4M3 V^T, bytes 32lh ..
+  // 32lh + 31; the column (query) scale is the B operand's E8M0 scale
   auto pv8 = [&](const unsigned char* st) __attribute__((always_inline)) {
     i32x8 va[D / 32];
 #pragma unroll
@@ -825,9 +849,9 @@ void k3_attn(AttnArgs a) {
     }
 #pragma unroll
     for (int db = 0; db < D / 32; db++) {
-      const f32x16 x = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], p8, f32x16{}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[db][r] = __builtin_fmaf(x[r], wpv, acc[db][r]);
+      for (int r = 0; r < 16; r++) acc[db][r] *= wr;
+      acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], p8, acc[db], 0, 0, 0, 127, 0, wk);
     }
   };
   // a kept tile (FULL: bf16 scores, LOW: E4M3 scores): masks and softmax of
@@ -963,6 +987,7 @@ void k3_attn(AttnArgs a) {
   };
   auto flip = [](auto p) { return std::integral_constant<int, 1 - decltype(p)::value>{}; };
   auto next = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);   // the step's work stays ahead of its closing wait
     wait_vm0_lgkm0();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
@@ -1177,7 +1202,7 @@ void k3_attn(AttnArgs a) {
 
   // ---- epilogue: O = acc / l
   const float L = l_run + __shfl_xor(l_run, 32, 64);
-  const float scale = 1.0f / L;
+  const float scale = accF / L;
   if (qrow < dm.N) {
     if (a.out_fp32) {
       float* o = reinterpret_cast<float*>(a.o) + toff + (int64_t)qrow * dm.sn;
