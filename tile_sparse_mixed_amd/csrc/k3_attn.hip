@@ -70,6 +70,11 @@
 #include "tattn_device.hpp"
 #include "tattn_internal.hpp"
 
+// Every fused multiply-add below is written out; no other product is fused
+// with a sum, so every instance of the kernel (with or without the code dump)
+// rounds the same operations the same way.
+#pragma clang fp contract(off)
+
 namespace tattn {
 namespace {
 
