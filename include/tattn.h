@@ -212,6 +212,23 @@ tattn_status tattn_forward(tattn_plan_t plan, const void* q, const void* k, cons
 tattn_status tattn_forward_dump(tattn_plan_t plan, const void* q, const void* k, const void* v, void* o,
                                 const int32_t* dump_slot, int32_t dump_steps, uint8_t* dump, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): tattn_plan followed
+ * by tattn_forward in one call, with the workspace in a static device array
+ * of the library (64 MiB on each GPU the library runs on, held until the
+ * process ends) instead of the caller's.  Calls no allocating routine.
+ * cfg: any routed mode (EXTERNAL gives TATTN_E_STATE); q, k, v, o as for
+ * tattn_plan / tattn_forward.  TATTN_E_WORKSPACE, before anything is
+ * launched, when tattn_workspace_bytes(cfg) exceeds 64 MiB.  Every call on a
+ * GPU uses that GPU's one array: calls that overlap on one GPU (two streams,
+ * two threads) race and give undefined results; calls in one stream are
+ * ordered.  The array keeps the last call's contents; every region a call
+ * reads it has written first.  Asynchronous on `stream`.
+ */
+tattn_status tattn_attention_static(const tattn_config* cfg, const void* q, const void* k, const void* v, void* o,
+                                    void* stream);
+
 /* Host only.  The most kept (FULL, LOW or SKIM) tiles a query block can hold
  * under `cfg`'s tier rule, which sizes the fused kernel's per-row list: the
  * top k_h bound ceil(keep_max * Nk) plus the diagonal blocks (ADAPTIVE), top_k

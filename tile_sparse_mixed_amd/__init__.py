@@ -14,7 +14,7 @@ import os
 
 import numpy as np
 
-__all__ = ["plan", "replan", "forward", "forward_dump", "list_bound", "Plan", "TattnError", "load_library",
+__all__ = ["plan", "replan", "forward", "forward_dump", "list_bound", "attention_static", "Plan", "TattnError", "load_library",
            "Config", "Stats",
            "MODE_THRESHOLD", "MODE_ADAPTIVE", "MODE_ALL_FULL", "MODE_EXTERNAL", "MODE_PRICE",
            "SKIP", "LOW", "FULL", "SKIM"]
@@ -62,6 +62,7 @@ _SIGS = {
     "tattn_forward": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP]),
     "tattn_forward_dump": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]),
     "tattn_list_bound": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_int32)]),
+    "tattn_attention_static": (ctypes.c_int, [ctypes.POINTER(Config), _VP, _VP, _VP, _VP, _VP]),
     "tattn_replan": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_set_tiers": (ctypes.c_int, [_VP, _VP, _VP]),
     "tattn_plan_get_tiers": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
@@ -302,6 +303,27 @@ def forward_dump(p: Plan, q, k, v, rows, steps, out=None):
     _check(load_library().tattn_forward_dump(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                              slot.data_ptr(), int(steps), dump.data_ptr(), _stream()))
     return out, dump.cpu().numpy()[:len(rows)]
+
+
+def attention_static(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, mode="threshold",
+                     keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256, out_fp32=False, price=0.0,
+                     tau_skim=0.0, out=None):
+    """Plan and forward in one call with the library's static workspace (no
+    device allocation inside the call; ``out`` may be preallocated).
+    Problems whose workspace exceeds 64 MiB raise."""
+    import torch
+    _check_tensors(q, k, v)
+    B, H, N, d = q.shape
+    cfg = make_config(B, H, N, d, block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
+                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price, tau_skim=tau_skim)
+    dt = torch.float32 if out_fp32 else torch.bfloat16
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=dt, device=q.device)
+    elif out.dtype != dt or out.stride() != q.stride() or out.shape != q.shape:
+        raise ValueError("out must match q's shape and strides and the output dtype")
+    _check(load_library().tattn_attention_static(ctypes.byref(cfg), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 out.data_ptr(), _stream()))
+    return out
 
 
 def forward(p: Plan, q, k, v, out=None):

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -194,6 +195,36 @@ static tattn_status validate(const tattn_config* c) {
   return ok();
 }
 
+// ---- static scratch of tattn_attention_static: a file-scope device array
+// (one per GPU, held until the process ends) whose device address is taken
+// once per device with hipGetSymbolAddress; host code uses only that address.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device, with that device current).
+static tattn_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TATTN_E_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign)
+      return fail(TATTN_E_HIP, "static scratch address %p is not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TATTN_OK;
+}
+
 }  // namespace tattn
 
 using namespace tattn;
@@ -238,6 +269,29 @@ static RouterArgs router_args(const tattn_plan_s* p) {
   return r;
 }
 
+// Fill *p and launch the plan's kernels (pooling, then routing unless
+// EXTERNAL) into `workspace`; the caller has validated cfg and the workspace.
+static tattn_status plan_into(tattn_plan_s* p, const tattn_config* cfg, const void* q, const void* k, const void* v,
+                              void* workspace, void* stream) {
+  p->cfg = *cfg;
+  p->d = make_dims(*cfg);
+  p->L = layout_of(*cfg);
+  p->ws = static_cast<unsigned char*>(workspace);
+  p->k = k;
+  p->v = v;
+  p->has_tiers = cfg->mode != TATTN_MODE_EXTERNAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+              p->ws, p->L, p->d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(*cfg) ? 1 : 0};
+  hipError_t e = launch_pool(pa, s);
+  if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+  if (cfg->mode != TATTN_MODE_EXTERNAL) {
+    e = launch_router(router_args(p), s);
+    if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+  }
+  return ok();
+}
+
 tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, const void* v, void* workspace,
                         size_t workspace_bytes, void* stream, tattn_plan_t* out) {
   tattn_status st = validate(cfg);
@@ -246,7 +300,6 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
   *out = nullptr;
   if (!q || !k || !v) return fail(TATTN_E_INVALID, "q, k and v must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
-  const Dims d = make_dims(*cfg);
   const Layout L = layout_of(*cfg);
   if (!workspace) return fail(TATTN_E_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TATTN_E_WORKSPACE, "workspace must be 256-byte aligned");
@@ -254,27 +307,10 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
     return fail(TATTN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
   tattn_plan_s* p = new (std::nothrow) tattn_plan_s;
   if (!p) return fail(TATTN_E_INVALID, "out of host memory");
-  p->cfg = *cfg;
-  p->d = d;
-  p->L = L;
-  p->ws = static_cast<unsigned char*>(workspace);
-  p->k = k;
-  p->v = v;
-  p->has_tiers = cfg->mode != TATTN_MODE_EXTERNAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-              p->ws, L, d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(*cfg) ? 1 : 0};
-  hipError_t e = launch_pool(pa, s);
-  if (e != hipSuccess) {
+  st = plan_into(p, cfg, q, k, v, workspace, stream);
+  if (st != TATTN_OK) {
     delete p;
-    return hip_fail(e, "pool kernel launch");
-  }
-  if (cfg->mode != TATTN_MODE_EXTERNAL) {
-    e = launch_router(router_args(p), s);
-    if (e != hipSuccess) {
-      delete p;
-      return hip_fail(e, "router kernel launch");
-    }
+    return st;
   }
   *out = p;
   return ok();
@@ -305,6 +341,28 @@ tattn_status tattn_forward_dump(tattn_plan_t p, const void* q, const void* k, co
   if (dump_steps < 1) return fail(TATTN_E_INVALID, "dump_steps must be >= 1 (got %d)", dump_steps);
   if (!aligned16(dump)) return fail(TATTN_E_INVALID, "dump must be 16-byte aligned");
   return forward_impl(p, q, k, v, o, dump_slot, dump_steps, dump, stream);
+}
+
+tattn_status tattn_attention_static(const tattn_config* cfg, const void* q, const void* k, const void* v, void* o,
+                                    void* stream) {
+  tattn_status st = validate(cfg);
+  if (st != TATTN_OK) return st;
+  if (cfg->mode == TATTN_MODE_EXTERNAL)
+    return fail(TATTN_E_STATE, "tattn_attention_static routes its own tiers (EXTERNAL mode has none to run)");
+  if (!q || !k || !v || !o) return fail(TATTN_E_INVALID, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(TATTN_E_INVALID, "q, k, v and o must be 16-byte aligned");
+  const size_t need = layout_of(*cfg).total;
+  if (need > kStaticScratchBytes)
+    return fail(TATTN_E_WORKSPACE, "the problem needs %zu bytes of workspace; the static scratch holds %zu",
+                need, (size_t)kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != TATTN_OK) return st;
+  tattn_plan_s p;   // host state on the stack: nothing is allocated
+  st = plan_into(&p, cfg, q, k, v, ws, stream);
+  if (st != TATTN_OK) return st;
+  return forward_impl(&p, q, k, v, o, nullptr, 0, nullptr, stream);
 }
 
 tattn_status tattn_list_bound(const tattn_config* cfg, int32_t* bound) {
