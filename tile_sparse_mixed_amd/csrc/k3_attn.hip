@@ -118,6 +118,13 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
+// max(x of lane l, x of lane l ^ 32): v_permlane32_swap exchanges the two
+// halves of the wave between two registers without an LDS round trip
+__device__ inline float max_lane_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
@@ -135,6 +142,28 @@ __device__ inline void pipeline_reads_mfma() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// Schedule of one software-pipelined low-tier step (one basic block): the
+// next step's K reads, its D/32 score MFMAs spread through this step's
+// softmax VALU, the row-sum MFMA, the V reads, then each P.V MFMA behind the
+// 16 multiplies of the accumulator block it consumes.
+template <int D>
+__device__ inline void schedule_low_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);     // DS reads: next step's K codes
+#pragma unroll
+  for (int i = 0; i < D / 32; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);       // VALU: this step's softmax
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA: next step's scores
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA: row sum of the codes
+  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);     // DS reads: this step's V codes
+#pragma unroll
+  for (int i = 0; i < D / 32; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);       // VALU: accumulator block i times wr
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA: P.V into block i
+  }
 }
 
 // LDS swizzles.  An MFMA operand read has the lanes of a half-wave read 16
@@ -176,8 +205,7 @@ void k3_attn(AttnArgs a) {
   static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
   static_assert(!SKIM || BK == 64, "the SKIM tier runs on 64-key blocks");
   constexpr int G = 64 / BK;          // key blocks per 64-key step
-  constexpr int STAGE = 256 * D;      // bytes: region R0 = [0, 128D), R1 = [128D, 256D)
-  constexpr int R1 = 128 * D;
+  constexpr int R1 = 128 * D;         // bytes of each half of a stage (R0: K-side operands, R1: V-side)
   // Two-wave workgroups (64-row query blocks) keep ONE stage and refill its
   // halves in turn: the K half of step t+1 while step t runs its softmax and
   // P.V, the V half while step t+1 scores.  That halves their LDS, so a CU
@@ -186,12 +214,18 @@ void k3_attn(AttnArgs a) {
   // compiler's wait insertion sees a DMA into one half never alias reads of
   // the other.
   constexpr bool SPLIT = NW == 2;
-  __shared__ __attribute__((aligned(1024))) unsigned char stA[SPLIT ? R1 : STAGE];   // stage of even steps
-  __shared__ __attribute__((aligned(1024))) unsigned char stB[SPLIT ? R1 : STAGE];   // stage of odd steps
+  // Four-wave workgroups keep two stages, each as two arrays (R0 and R1):
+  // the software-pipelined low phase refills the R0 half of one stage while
+  // the R1 half of the same stage is read, and separate arrays let the wait
+  // insertion see that these never alias.
+  __shared__ __attribute__((aligned(1024))) unsigned char stA[R1];   // R0 of even steps (two-wave: the one stage's R0)
+  __shared__ __attribute__((aligned(1024))) unsigned char stB[R1];   // R0 of odd steps (two-wave: the one stage's R1)
+  __shared__ __attribute__((aligned(1024))) unsigned char svA[SPLIT ? 16 : R1];   // R1 of even steps
+  __shared__ __attribute__((aligned(1024))) unsigned char svB[SPLIT ? 16 : R1];   // R1 of odd steps
   // the R1 region of a stage
   auto r1 = [&](const unsigned char* st) __attribute__((always_inline)) -> unsigned char* {
     if constexpr (SPLIT) return stB;
-    else return const_cast<unsigned char*>(st) + R1;
+    else return st == stA ? svA : svB;
   };
   extern __shared__ int16_t slist[];         // the row's FULL, LOW (and SKIM) key blocks (list_cap entries)
   __shared__ uint64_t smask[64];             // per visited chunk: bit j = block 64c + j skipped
@@ -588,7 +622,7 @@ void k3_attn(AttnArgs a) {
   for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   f16x8 pb[4];
-  i32x8 p8;          // probability codes of a quantised step (LOW, SKIM)
+  i32x8 p8 = {};     // probability codes of a quantised step (LOW, SKIM)
   // From the first quantised 64-key step on, the accumulator holds O^T / accF
   // (relative to 2^m): a step's weight w = 2^(tile max - m) sv / 448 is split
   // into w = wm 2^wk, wm in [1, 2); the MFMA's per-column E8M0 scale applies
@@ -713,7 +747,7 @@ void k3_attn(AttnArgs a) {
     }
   };
   auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
-    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)), std::false_type{});
+    raise_max(max_lane_halves(tmax), std::false_type{});
     const float nm = -m_run;
 #pragma unroll
     for (int cc = 0; cc < 4; cc++)
@@ -768,9 +802,11 @@ void k3_attn(AttnArgs a) {
   // codes of four scores, x = 2^(s * c - tm + log2(448)), into one dword.
   // x is at most 448 up to rounding (far below 464, where the converter
   // would stop rounding to 448), so it needs no clamp.
-  auto codes4 = [&](float s0, float s1, float s2, float s3, float c, float nm) __attribute__((always_inline)) {
+  // `old` is the dword's previous value: both halves are overwritten, and
+  // passing the register it already occupies needs no copy.
+  auto codes4 = [&](float s0, float s1, float s2, float s3, float c, float nm, int old) __attribute__((always_inline)) {
     const int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, nm)),
-                                                  __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, nm)), 0, false);
+                                                  __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, nm)), old, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(__builtin_fmaf(s2, c, nm)),
                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s3, c, nm)), w, true);
   };
@@ -780,18 +816,18 @@ void k3_attn(AttnArgs a) {
   // the accumulator factor and the E8M0 column scale (wr, wk)
   auto quant_soft64 = [&](f32x16* s, float c, float sv, int ds) __attribute__((always_inline)) {
     float tm = row_max(s);
-    tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32, 64)) * c;
+    tm = max_lane_halves(tm) * c;
     raise_max(tm, std::true_type{});
     const float nm = kLog2_448 - tm;
 #pragma unroll
     for (int w = 0; w < 8; w++) {
       const int b = w >> 2, r0 = 4 * (w & 3);
-      p8[w] = codes4(s[b][r0], s[b][r0 + 1], s[b][r0 + 2], s[b][r0 + 3], c, nm);
+      p8[w] = codes4(s[b][r0], s[b][r0 + 1], s[b][r0 + 2], s[b][r0 + 3], c, nm, p8[w]);
     }
     dump_codes(ds);
-    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p8, f32x16{}, 0, 0, 0, 0, 0, 0);
+    // the ones as an FP4 (E2M1 1.0 = 0x2) operand: four registers instead of eight
+    const i32x8 ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p8, f32x16{}, 4, 0, 0, 0, 0, 0);
     const float g = __builtin_amdgcn_exp2f(tm - m_run);
     l_run = __builtin_fmaf(rs[0], g * (0.5f / 448.0f), l_run);
     const float w = g * (sv * (1.0f / 448.0f));
@@ -816,10 +852,10 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
       tb[cc] = m * chunk_scale(cs, cc);
-      if constexpr (G == 4) tb[cc] = __builtin_fmaxf(tb[cc], __shfl_xor(tb[cc], 32, 64));
+      if constexpr (G == 4) tb[cc] = max_lane_halves(tb[cc]);
     }
     float tmax = __builtin_fmaxf(__builtin_fmaxf(tb[0], tb[1]), __builtin_fmaxf(tb[2], tb[3]));
-    raise_max(__builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64)), std::false_type{});
+    raise_max(max_lane_halves(tmax), std::false_type{});
 #pragma unroll
     for (int cc = 0; cc < 4; cc++) {
       const bool live = tb[cc] > -INFINITY;   // a slot past the list's end has no keys
@@ -829,7 +865,8 @@ void k3_attn(AttnArgs a) {
       const int b = cc >> 1, r0 = 8 * (cc & 1);
 #pragma unroll
       for (int j = 0; j < 2; j++) {
-        const int w = codes4(s[b][r0 + 4 * j], s[b][r0 + 4 * j + 1], s[b][r0 + 4 * j + 2], s[b][r0 + 4 * j + 3], c, nm);
+        const int w = codes4(s[b][r0 + 4 * j], s[b][r0 + 4 * j + 1], s[b][r0 + 4 * j + 2], s[b][r0 + 4 * j + 3], c, nm,
+                             p8[2 * cc + j]);
         p8[2 * cc + j] = w;
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
         pb[cc][4 * j] = static_cast<_Float16>(lo.x * gw);
@@ -1089,11 +1126,100 @@ void k3_attn(AttnArgs a) {
                      // fp8 instruction i = bf16 chunks 4i..4i+3)
       i32x8 q8reg[D / 64];
       make_q8(q8reg);
-      run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
-        if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
-        kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
-        next();
-      });
+      if constexpr (G == 1) {
+        // Software pipeline: step t+1's score MFMAs are issued ahead of step
+        // t's softmax, so the matrix core works while the VALU quantises the
+        // probabilities.  Entering iteration t: the scores of step t are in
+        // registers (sE for even t, sO for odd t), step t's V is in R1 of its
+        // stage, step t+1's R0 half (its K codes) has landed in the other
+        // stage.  Iteration t refills R0 of step t's stage with step t+2's K
+        // half and R1 of the other stage with step t+1's V half, then scores
+        // step t+1 and finishes step t.
+        //
+        // List window: lane l holds the key block, score scale and value
+        // scale of step tLow + wb + l (the LOW entries, then the SKIM ones),
+        // read once per 32 steps; a step takes its entries with readlane, so
+        // it waits on neither an LDS read of the list nor a scalar-memory
+        // load of the scales.
+        int wb = 0, jw, jn = 0;
+        float cw, vw, cn = 0.0f, vn = 0.0f;
+        auto window = [&](int base, int& jx, float& cx, float& vx) __attribute__((always_inline)) {
+          const int i = nF + base + lane;
+          const int J = i < nK + nSk ? (int)slist[i] : 0;
+          jx = J;
+          cx = sq * skp[J] * cF;
+          vx = svp[J];
+        };
+        auto rl = [](int x, int l) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, l); };
+        auto rlf = [](float x, int l) __attribute__((always_inline)) {
+          return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+        };
+        auto low_k = [&](int J, unsigned char* st) __attribute__((always_inline)) {   // E4M3 K of block J into R0
+#pragma unroll
+          for (int i = 0; i < NI8; i++) {
+            const int k = wave + NW * i;
+            dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+          }
+        };
+        using PartK = std::integral_constant<int, 1>;
+        window(0, jw, cw, vw);
+        f32x16 sE[2], sO[2];
+        auto sreg = [&](auto p) __attribute__((always_inline)) -> f32x16* {
+          if constexpr (decltype(p)::value) return sO;
+          else return sE;
+        };
+        // prologue: step t is staged whole; stage the K half of step t+1
+        auto prologue = [&](auto p) __attribute__((always_inline)) {
+          if (t + 1 < tSk) low_k(rl(jw, 1), stg(flip(p)));
+          else if (t + 1 < nSteps) issue_part(KLow{}, PartK{}, t + 1, stg(flip(p)), scl(flip(p)));   // a SKIM step
+          f32x16* sc = sreg(p);
+          sc[0] = f32x16{};
+          sc[1] = f32x16{};
+          scores_fp8(stg(p), sc, q8reg);
+          next();
+        };
+        if (t & 1) prologue(P1{});
+        else prologue(P0{});
+        run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
+          // The window slides by 32 steps: at o = 61 the next one is loaded
+          // (landed by the step's closing wait), at o = 62 it is taken.  Both
+          // branches stay ahead of the step's compute, which is then one basic
+          // block up to its closing barrier.
+          const int k = tt - tLow;
+          if (k - wb == 62) {
+            jw = jn;
+            cw = cn;
+            vw = vn;
+            wb += 32;
+          }
+          const int o = k - wb;   // o <= 61: steps k .. k+2 are in the window
+          if (o == 61) window(wb + 32, jn, cn, vn);
+          const int J = rl(jw, o);
+          const float c = rlf(cw, o), sv = rlf(vw, o);
+          if (tt + 2 < tSk) low_k(rl(jw, o + 2), stg(p));
+          else if (tt + 2 < nSteps) issue_part(KLow{}, PartK{}, tt + 2, stg(p), scl(p));   // a SKIM step
+          if (tt + 1 < nSteps) load_v8(r1(stg(flip(p))), rl(jw, o + 1));   // LOW and SKIM: E4M3 V^T
+          f32x16* sc = sreg(p);
+          if (J == dm.Nk - 1) mask_tail(sc, dm.N - 64 * J);   // the ragged last block (a branch)
+          // (the last iteration scores a stale, in-bounds R0 and drops the
+          // result: unconditional, the score MFMAs share a block with the
+          // softmax and the scheduler can interleave them)
+          f32x16* sn = sreg(flip(p));
+          sn[0] = f32x16{};
+          sn[1] = f32x16{};
+          scores_fp8(stg(flip(p)), sn, q8reg);
+          quant_soft64(sc, c, sv, k);
+          pv8(stg(p));
+          schedule_low_step<D>();
+          next();
+        });
+      } else {
+        run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
+          if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
+          kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
+          next();
+        });
+      }
     }
     if constexpr (SKIM) {
       if (t < nSteps) {   // SKIM tiles remain: the MXFP4 copy of this lane's Q row,
