@@ -397,9 +397,6 @@ void k3_attn(AttnArgs a) {
   // holds logical chunk lc = (lane & 7) ^ swz128(d), i.e. 8 keys of column
   // group lc / 2; the lane fetches them from that group's block, stored
   // [D][16] (32 bytes per row d), half lc & 1 of the row.
-  const int vlc = (lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1);
-  const int vgrp = vlc >> 1;
-  const int vlane = (lane >> 3) * 32 + (vlc & 1) * 16;
   // caller's K as one resource per head for 16- and 8-key gathers: rows past N read as zero
   const __amdgpu_buffer_rsrc_t rKh = make_rsrc(kin, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
   // V^T rows of the step's G blocks (per-block [D][BK] layout) from `base`.
@@ -412,8 +409,13 @@ void k3_attn(AttnArgs a) {
       (void)reg; (void)base; (void)jv;
     } else {
       constexpr int ROWB = BK * 2;                  // bytes per stored V^T row of a block
-      const int vo = G == 4 ? vlane + __shfl(jv, vgrp, 64) * (D * ROWB)
-                            : (lane >> 3) * ROWB + __shfl(jv, vlc, 64) * (D * ROWB);
+      // from an opaque lane index at every step: hoisted, these terms stayed
+      // live across the kernel and spilled in the two-wave instances
+      int lr = lane;
+      opaque(lr);
+      const int vlc = (lr & 7) ^ ((lr >> 3) & 7) ^ (wave & 1);
+      const int vo = G == 4 ? (lr >> 3) * 32 + (vlc & 1) * 16 + __shfl(jv, vlc >> 1, 64) * (D * ROWB)
+                            : (lr >> 3) * ROWB + __shfl(jv, vlc, 64) * (D * ROWB);
 #pragma unroll
       for (int i = 0; i < NI16; i++) {
         const int k = wave + NW * i;
@@ -470,9 +472,12 @@ void k3_attn(AttnArgs a) {
                 const int Js = __builtin_amdgcn_readlane(jv, slot8(row0));
                 dma16(rKh, st + k * 1024, lk[i % NSW] + (Js * 8 + kk8(row0)) * (int)dm.sn * 2, 0);
               } else {
-                const int m = row0 + rr16;
+                int lr = lane;   // opaque, as for the E4M3 rows below
+                opaque(lr);
+                const int r16 = lr / CH;
+                const int m = row0 + r16;
                 dma16(rKh, st + k * 1024,
-                      lk[i % NSW] + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - rr16) * (int)dm.sn * 2, 0);
+                      lk[i % NSW] + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - r16) * (int)dm.sn * 2, 0);
               }
             }
           }
@@ -491,7 +496,12 @@ void k3_attn(AttnArgs a) {
                 const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
                 dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + (Jg * 16 + (row0 & 15)) * D);
               } else {
-                const int ri = D == 128 ? lane >> 3 : lane >> 2;   // row of the lane inside the instruction
+                // the lane's terms are recomputed at every step from an opaque
+                // lane index: hoisted out of the loop, the per-instruction
+                // addresses stayed live across the kernel and spilled
+                int lr = lane;
+                opaque(lr);
+                const int ri = D == 128 ? lr >> 3 : lr >> 2;   // row of the lane inside the instruction
                 const int m = row0 + ri;
                 dma16(rS, st + k * 1024, voffK8 + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - ri) * D, (int)SL.k8);
               }
@@ -791,7 +801,9 @@ void k3_attn(AttnArgs a) {
   auto dump_codes = [&](int ds) __attribute__((always_inline)) {
     if constexpr (DUMP) {
       if (dsl >= 0 && ds < a.dsteps) {
-        unsigned char* o = a.dump + ((static_cast<int64_t>(dsl) * a.dsteps + ds) * (32 * NW) + 32 * wave + ln) * 64 + 32 * lh;
+        int lr = lane;   // opaque: the lane's term is not kept live across the kernel
+        opaque(lr);
+        unsigned char* o = a.dump + ((static_cast<int64_t>(dsl) * a.dsteps + ds) * (32 * NW) + 32 * wave + (lr & 31)) * 64 + 32 * (lr >> 5);
         reinterpret_cast<uint4*>(o)[0] = make_uint4(p8[0], p8[1], p8[2], p8[3]);
         reinterpret_cast<uint4*>(o)[1] = make_uint4(p8[4], p8[5], p8[6], p8[7]);
       }
@@ -1331,12 +1343,17 @@ void k3_attn(AttnArgs a) {
     }
   }
 
-  // ---- epilogue: O = acc / l
+  // ---- epilogue: O = acc / l.  The row's address is formed again here from
+  // an opaque lane index: shared with the Q loads, it stayed live across the
+  // kernel and spilled in the two-wave instances.
   const float L = l_run + __shfl_xor(l_run, 32, 64);
   const float scale = accF / L;
-  if (qrow < dm.N) {
+  int lo = ln;
+  opaque(lo);
+  const int orow = I * (32 * NW) + wave * 32 + lo;
+  if (orow < dm.N) {
     if (a.out_fp32) {
-      float* o = reinterpret_cast<float*>(a.o) + toff + (int64_t)qrow * dm.sn;
+      float* o = reinterpret_cast<float*>(a.o) + toff + (int64_t)orow * dm.sn;
 #pragma unroll
       for (int db = 0; db < D / 32; db++)
 #pragma unroll
@@ -1346,7 +1363,7 @@ void k3_attn(AttnArgs a) {
                                                            acc[db][4 * j + 2] * scale, acc[db][4 * j + 3] * scale);
         }
     } else {
-      uint16_t* o = reinterpret_cast<uint16_t*>(a.o) + toff + (int64_t)qrow * dm.sn;
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.o) + toff + (int64_t)orow * dm.sn;
 #pragma unroll
       for (int db = 0; db < D / 32; db++)
 #pragma unroll
