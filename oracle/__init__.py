@@ -31,7 +31,7 @@ derivation are pinned, its accuracy as a predictor is not: "parity unpinned").
 """
 from . import e4m3, mxfp4  # noqa: F401
 from .tattn import (  # noqa: F401
-    SKIP, LOW, FULL, SKIM, skim_operands, block_sizes, pool_means, router, tiers_threshold, tiers_adaptive,
+    SKIP, LOW, FULL, SKIM, skim_operands, refine_operands, refine_scores, block_sizes, pool_means, router, tiers_threshold, tiers_adaptive,
     head_retention, diagonal_mask, build_lists, quantise_blocks, dequantise, quantised_probabilities, low_scores,
     attention_forward,
     oracle_plan, oracle_forward, naive_attention, effective_weights,

@@ -39,7 +39,9 @@ probabilities quantised to E4M3 against the tile-local row maximum
 exactly and a tile's codes do not depend on the order tiles are visited in),
 values from the E4M3 copy of V, v^ = fl32(decode(code) * scale); the tile's
 share of the row normaliser sums the same pi (HierPAS: progressively reduced
-precision; APT: dual-precision execution).
+precision; APT: dual-precision execution).  In the refine variant of the low
+tier the scores come from MXFP4 copies with an MXFP4 residual correction
+(Triage: refining a tile with 4-bit residual correction; refine_operands).
 
 Precision: float64 throughout, except that every fp8 code is decided on a
 float32 value (the value the kernel converts) and the dequantised E4M3 values
@@ -355,6 +357,31 @@ def skim_operands(q, k):
     return dict(q=qd, k=kd, k_codes=kc, k_scales=ks)
 
 
+def refine_operands(q, k):
+    """Score operands of the residual-corrected refine variant of the low tier
+    (Triage: a tile refined with 4-bit residual correction).  Each of Q and K
+    is quantised to MXFP4 per token row (one E8M0 scale per 32 channels), and
+    the rounding residual x - x4 is quantised to MXFP4 again with its own
+    scales: x ~ x4 + x4r.  A tile's scores keep the three products of order
+    up to one in the residuals, <q4, k4> + <q4, k4r> + <q4r, k4> (over
+    sqrt(d)); the product of the two residuals is of second order and dropped
+    (reading R20).  Returns the dequantised operands (float64 [n, d]) and the
+    codes and scale bytes of k and of its residual."""
+    _, _, qd = mxfp4.quantise(q)
+    _, _, qrd = mxfp4.quantise(np.asarray(q, np.float64) - qd)
+    kc, ks, kd = mxfp4.quantise(k)
+    krc, krs, krd = mxfp4.quantise(np.asarray(k, np.float64) - kd)
+    return dict(q=qd, qr=qrd, k=kd, kr=krd, k_codes=kc, k_scales=ks, kr_codes=krc, kr_scales=krs)
+
+
+def refine_scores(qa, ka):
+    """Unscaled refine scores of query rows against key rows: with qa = (q4,
+    q4r) and ka = (k4, k4r), <q4, k4> + <q4, k4r> + <q4r, k4>."""
+    q4, q4r = qa
+    k4, k4r = ka
+    return q4 @ k4.T + q4 @ k4r.T + q4r @ k4.T
+
+
 def dequantise(codes: np.ndarray, scale: np.ndarray, b: int) -> np.ndarray:
     """X^ = fl32(decode(code) * scale) with the scale of each row's block of b
     rows.  Returns float64 [n, d] (values representable in float32)."""
@@ -398,7 +425,7 @@ def _padded(x, nb, b):
 
 
 def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
-                      rows=None, return_partials=False, mx4=None, p_codes=None):
+                      rows=None, return_partials=False, mx4=None, p_codes=None, refine=None):
     """One pass over all tiles of every query row, merging per-tile partials
     exactly (Triage: skip, low precision and full tiles in a single pass).
 
@@ -406,6 +433,8 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     LOW:  scores s^_j from the E4M3 copies (low_scores), probabilities
           quantised against the tile max (quantised_probabilities), values
           v^_j = fl32(decode(V8_j) * sv_J); partial (m_t, sum pi_j, sum pi_j v^_j).
+          With ``refine`` (refine_operands) a LOW tile's scores are instead
+          <q4,k4> + <q4,k4r> + <q4r,k4> over sqrt(d) (refine_scores).
     SKIM: the same with scores from the MXFP4 copies (``mx4``, skim_operands):
           <q4_i, k4_j>/sqrt(d) (Triage: skimming in 4 bits); probabilities and
           values as in LOW.
@@ -432,6 +461,8 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
     Qc = e4m3.decode(q8)
     if np.any(t == SKIM):
         Kq = _padded(mx4["k"], nk, bk)
+    if refine is not None:
+        Kr4, Kr4r = _padded(refine["k"], nk, bk), _padded(refine["kr"], nk, bk)
     kb64, vb64 = kbar.astype(np.float64), vbar.astype(np.float64)
     lnk = np.log(ksz.astype(np.float64))
     out = np.zeros((n, d), dtype=np.float64)
@@ -464,7 +495,14 @@ def attention_forward(q, k, v, t, bq, bk, kbar, vbar, q8, sq, k8, sk, v8, sv,
             ls.append(e.sum(axis=2))
             os_.append(np.matmul(e.transpose(1, 0, 2), Vp[F]).transpose(1, 0, 2))
         L = np.nonzero(t[i] == LOW)[0]
-        if L.size:
+        if L.size and refine is not None:
+            s = refine_scores((refine["q"][r0:r1], refine["qr"][r0:r1]),
+                              (Kr4[L].reshape(-1, d), Kr4r[L].reshape(-1, d)))
+            m, l, o = quantised_partial(i, L, s.reshape(r1 - r0, L.size, bk) * isd)
+            ms.append(m)
+            ls.append(l)
+            os_.append(o)
+        elif L.size:
             raw = (Qc[r0:r1] @ Kh[L].reshape(-1, d).T).reshape(r1 - r0, L.size, bk)
             sc = float(sq[i]) * sk.astype(np.float64)[L] * isd            # [nL]
             m, l, o = quantised_partial(i, L, raw * sc[None, :, None])
@@ -606,10 +644,13 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
     q8, sq, iq = quantise_blocks(q, bq)
     k8, sk, ik = quantise_blocks(k, bk)
     v8, sv, iv = quantise_blocks(v, bk)
-    # the MXFP4 copies, where a SKIM tile needs them
+    # the MXFP4 copies, where a SKIM tile needs them; the residual-corrected
+    # ones where the low tier runs refined
     mx4 = skim_operands(q, k) if np.any(t == SKIM) else None
+    refine = refine_operands(q, k) if getattr(cfg_like, "low_refine", 0) else None
     return dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, p=p, tiers=t, lists=lists, counts=counts,
-                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info, mx4=mx4)
+                q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, r_h=r_h, k_h=k_h, price=price_info, mx4=mx4,
+                refine=refine)
 
 
 def oracle_replan(q, k, v, prev_plan, cfg_like):
@@ -623,4 +664,4 @@ def oracle_replan(q, k, v, prev_plan, cfg_like):
 def oracle_forward(q, k, v, plan, bq, bk, rows=None, p_codes=None):
     return attention_forward(q, k, v, plan["tiers"], bq, bk, plan["kbar"], plan["vbar"],
                              plan["q8"], plan["sq"], plan["k8"], plan["sk"], plan["v8"], plan["sv"],
-                             rows=rows, mx4=plan.get("mx4"), p_codes=p_codes)
+                             rows=rows, mx4=plan.get("mx4"), p_codes=p_codes, refine=plan.get("refine"))
