@@ -49,6 +49,8 @@ def parse():
                          "and launch; for the large workloads, whose full host-side generation takes minutes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for counter scaling)")
+    ap.add_argument("--low-refine", action="store_true",
+                    help="score LOW tiles on MXFP4 with residual correction instead of E4M3 (and compare)")
     ap.add_argument("--price", type=float, default=None,
                     help="route with the price router at this price instead of the workload's own tier rule")
     return ap.parse_args()
@@ -203,11 +205,13 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def mk(mode, ws=None, skim=True):
+    def mk(mode, ws=None, skim=True, refine=None):
+        refine = args.low_refine if refine is None else refine
         return tsm.plan(q, k, v, block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
                         top_k=cfg.top_k, mode=mode, keep_min=cfg.keep_min, keep_max=cfg.keep_max,
                         full_frac=cfg.full_frac, entropy_samples=cfg.entropy_samples, workspace=ws,
-                        price=args.price or 0.0, tau_skim=cfg.tau_skim if mode != "all_full" and skim else 0.0)
+                        price=args.price or 0.0, tau_skim=cfg.tau_skim if mode != "all_full" and skim else 0.0,
+                        low_refine=refine and mode != "all_full")
 
     out = torch.empty_like(q)
     plan = mk(run_mode)
@@ -275,6 +279,7 @@ def main():
     ms_allfull = None
     quality = None
     skim_cmp = None
+    refine_cmp = None
     if not args.no_allfull:
         pf = mk("all_full")
         dense_out = torch.empty_like(out)
@@ -306,6 +311,31 @@ def main():
                 rel = float(((af - b).flatten(2).pow(2).sum() / b.flatten(2).pow(2).sum()).sqrt())
                 skim_cmp[name] = {"forward_ms": round(ms_alt, 4), "rel_l2": round(rel, 6)}
                 del pe, alt, af
+        if args.low_refine:
+            # the same tier map with LOW tiles scored on the E4M3 copies: what
+            # the residual-corrected MXFP4 scores cost and buy against them
+            refine_cmp = {"low_share": round(float((plan.tiers() == tsm.LOW).mean()), 4),
+                          "refined_mxfp4": {"forward_ms": round(ms_k3, 4), "rel_l2": quality["rel_l2"]}}
+            pe = mk(run_mode, refine=False)
+            alt = torch.empty_like(out)
+            tsm.forward(pe, q, k, v, alt)
+            ms_alt = timed(lambda: tsm.forward(pe, q, k, v, alt), args.steps)[0]
+            af = alt.float()
+            rel = float(((af - b).flatten(2).pow(2).sum() / b.flatten(2).pow(2).sum()).sqrt())
+            refine_cmp["e4m3"] = {"forward_ms": round(ms_alt, 4), "rel_l2": round(rel, 6)}
+            # each low tier's own error: against the same map with its LOW
+            # tiles run as FULL tiles (bf16 scores, exact probabilities)
+            pf = mk("external", refine=False)
+            t_map = plan.tiers()
+            pf.set_tiers(np.where(t_map == tsm.LOW, tsm.FULL, t_map).astype(np.uint8))
+            ref = torch.empty_like(out)
+            tsm.forward(pf, q, k, v, ref)
+            rf = ref.float()
+            den = rf.flatten(2).pow(2).sum()
+            for key, o_ in (("refined_mxfp4", a), ("e4m3", af)):
+                refine_cmp[key]["rel_l2_vs_low_as_full"] = round(float(((o_ - rf).flatten(2).pow(2).sum() / den).sqrt()), 6)
+            refine_cmp["rel_l2_refined_vs_e4m3"] = round(float(((a - af).flatten(2).pow(2).sum() / den).sqrt()), 6)
+            del pe, alt, af, pf, ref, rf
         del dense_out, a, b, diff, num
 
     if args.copy_calibration:
@@ -320,7 +350,7 @@ def main():
     bf16_equiv = st["flops_bf16"] + st["flops_fp8"] * PEAK_BF16 / PEAK_FP8 + st["flops_fp4"] * PEAK_BF16 / PEAK_FP4
     achieved = bf16_equiv / (ms_k3 * 1e-3) / 1e12
     tiles = st["n_full"] + st["n_low"] + st["n_skip"] + st["n_skim"]
-    counters = load_counters(args.workload)
+    counters = {} if args.low_refine else load_counters(args.workload)   # counters are of the E4M3 kernel
 
     # the plan (K1 + K2) as an HBM-bound pass: algorithmic bytes = read Q, K, V
     # (bf16) + E4M3 K and V + float32 means and scales (K1), + the means read
@@ -343,7 +373,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16+fp8" + ("+fp4" if st["n_skim"] else "") + " (fp32 accumulate)",
+        "dtype": "bf16+fp8" + ("+fp4" if st["flops_fp4"] else "") + " (fp32 accumulate)",
         "data": "synthetic" + (f" ({args.gen_heads} generated heads tiled to {cfg.heads})" if tiled else ""),
         "config": {"workload": f"{cfg.name}: {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]}={cfg.seq_len} tokens, "
                                f"{cfg.heads} heads, d={cfg.head_dim}, tiles {cfg.block_q}q x {cfg.block_k}k, "
@@ -375,13 +405,14 @@ def main():
         "head_retention": kh_summary,
         "quality": quality,
         "skim_tier": skim_cmp,
+        "low_refine": refine_cmp,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16, 4), "traffic": counters.get("bytes_per_launch"),
                      "kernel": "k3_attn (fused three-tier forward)",
                      "work": f"bf16 {st['flops_bf16'] / 1e12:.3f} TFLOP + fp8 {st['flops_fp8'] / 1e12:.3f} TFLOP "
                              f"(fp8 at the bf16/fp8 peak ratio, 1/2)"
                              + (f" + fp4 {st['flops_fp4'] / 1e12:.3f} TFLOP (fp4 at the bf16/fp4 peak ratio)"
-                                if st["n_skim"] else "") + " per launch: U = frac",
+                                if st["flops_fp4"] else "") + " per launch: U = frac",
                      "mfma_busy": counters.get("mfma_busy")},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

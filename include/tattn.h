@@ -102,6 +102,12 @@ typedef struct {
                                               threshold (then <= tau_lo), EXTERNAL accepts SKIM
                                               bytes, PRICE weighs SKIM as a fourth choice;
                                               ignored by the other modes                     */
+  int32_t low_refine;                      /* 0: LOW tiles score on E4M3 copies of Q and K.
+                                              1 (block_k 64, no SKIM tier): they score on
+                                              MXFP4 copies with an MXFP4 residual correction
+                                              ("Triage": refining a tile with 4-bit residual
+                                              correction): <q4,k4> + <q4,k4r> + <q4r,k4>;
+                                              probabilities and values as before          */
 } tattn_config;
 
 typedef struct tattn_plan_s* tattn_plan_t;  /* opaque host object; device state is in the workspace */
@@ -117,7 +123,8 @@ typedef struct {
                                      SKIM tiles                                     */
   double flops_dense;             /* 4 * N^2 * d * B * H: dense-equivalent work      */
   int64_t n_skim;                 /* SKIM tiles                                      */
-  double flops_fp4;               /* fp4 MFMA flops: the score half of SKIM tiles    */
+  double flops_fp4;               /* fp4 MFMA flops: the score half of SKIM tiles,
+                                     and of refined LOW tiles (three fp4 passes)    */
 } tattn_stats;
 
 /* Check a config without touching any device.  Host only; no HIP calls. */
@@ -289,6 +296,13 @@ tattn_status tattn_plan_get_codes(tattn_plan_t plan, uint8_t* host_k8, uint8_t* 
  * - 2 clamped to [-127, 127] (-127 for an all-zero block).  Either pointer may
  * be NULL. */
 tattn_status tattn_plan_get_mx4(tattn_plan_t plan, uint8_t* host_k4, uint8_t* host_k4s, void* stream);
+
+/* SYNC.  Refined low tier (config low_refine = 1; TATTN_E_STATE otherwise):
+ * copy out, in tattn_plan_get_mx4's layouts, the MXFP4 copy of K's rounding
+ * residual k - dequant(k4): codes k4r and E8M0 scale bytes k4rs, with the
+ * same per-32-channel rule applied to the residual.  tattn_plan_get_mx4 gives
+ * the first-level copy under this config too.  Either pointer may be NULL. */
+tattn_status tattn_plan_get_mx4_residual(tattn_plan_t plan, uint8_t* host_k4r, uint8_t* host_k4rs, void* stream);
 
 /* SYNC.  PRICE mode: copy out the block second moments the router used
  * (float32): q2 [B,H,Nq,d] and m2q [B,H,Nq] (query mean square per dimension

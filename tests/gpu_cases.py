@@ -36,6 +36,7 @@ class OracleCfg:
         self.full_frac = as_f32(cfg.full_frac)
         self.entropy_samples = cfg.entropy_samples
         self.tau_skim = as_f32(cfg.tau_skim)
+        self.low_refine = 0      # set to 1 for the refined low tier
 
 
 def oracle_head(g, b, h, ocfg, mode=None, external=None):
@@ -165,14 +166,22 @@ def tile_reference(oe, I, J, bq, bk, n, kind):
     d = oe["q8"].shape[1]
     r0, r1 = I * bq, min(n, (I + 1) * bq)
     j0, j1 = J * bk, min(n, (J + 1) * bk)
-    if kind == T.LOW:
-        qa, ka = dec[oe["q8"][r0:r1]], dec[oe["k8"][j0:j1]]
-        scale = float(oe["sq"][I]) * float(oe["sk"][J]) / np.sqrt(d)
-    else:
-        qa, ka = oe["mx4"]["q"][r0:r1], oe["mx4"]["k"][j0:j1]
+    if kind == T.LOW and oe.get("refine") is not None:
+        # refined low tier: three products (T.refine_scores), each on the fp4 MFMA
+        R = oe["refine"]
+        q4, q4r, k4, k4r = R["q"][r0:r1], R["qr"][r0:r1], R["k"][j0:j1], R["kr"][j0:j1]
         scale = 1.0 / np.sqrt(d)
-    s = (qa @ ka.T) * scale
-    absum = (np.abs(qa) @ np.abs(ka).T) * scale                      # natural-log units
+        s = T.refine_scores((q4, q4r), (k4, k4r)) * scale
+        absum = T.refine_scores((np.abs(q4), np.abs(q4r)), (np.abs(k4), np.abs(k4r))) * scale
+    else:
+        if kind == T.LOW:
+            qa, ka = dec[oe["q8"][r0:r1]], dec[oe["k8"][j0:j1]]
+            scale = float(oe["sq"][I]) * float(oe["sk"][J]) / np.sqrt(d)
+        else:
+            qa, ka = oe["mx4"]["q"][r0:r1], oe["mx4"]["k"][j0:j1]
+            scale = 1.0 / np.sqrt(d)
+        s = (qa @ ka.T) * scale
+        absum = (np.abs(qa) @ np.abs(ka).T) * scale                  # natural-log units
     mt, x, codes, _ = T.quantised_probabilities(s)
     l2e = 1.0 / np.log(2.0)
     # base-2 exponent error: MFMA sums of s_j and of the maximum, the float32

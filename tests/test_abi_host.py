@@ -59,6 +59,14 @@ def test_valid_configs(lib):
     assert status(lib, good(mode="price", price=0.01, tau_skim=0.5)) == 0
     assert status(lib, good(mode="price", price=0.01, tau_skim=-1e-4)) == -1
     assert status(lib, good(mode="price", price=0.01, tau_skim=1e-4, block_q=64, block_k=16)) == -2
+    # the refined low tier: 64-key blocks, not with the SKIM tier, any mode
+    for m in ("threshold", "adaptive", "price", "external", "all_full"):
+        assert status(lib, good(mode=m, price=0.01, low_refine=True)) == 0, m
+    assert status(lib, good(low_refine=True, block_q=64, block_k=16)) == -2
+    assert status(lib, good(low_refine=True, tau_skim=1e-4)) == -2
+    c = good()
+    c.low_refine = 2
+    assert status(lib, c) == -1
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -124,6 +132,11 @@ def test_workspace_formula(lib):
     # ... and only where a SKIM tile can occur
     assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="all_full", tau_skim=1e-4)), ctypes.byref(k)) == 0
     assert k.value == n.value
+    # the refined low tier adds the MXFP4 K codes and scales and those of its residual
+    r = ctypes.c_size_t()
+    assert lib.tattn_workspace_bytes(ctypes.byref(good(low_refine=True)), ctypes.byref(r)) == 0
+    extra = 2 * BH * Nk * 64 * (D // 2 + D // 32)
+    assert extra <= r.value - n.value <= extra * 1.01
     # the price router with SKIM holds both the moments and the MXFP4 copies
     pk, sk = ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.tattn_workspace_bytes(ctypes.byref(good(mode="price", price=0.01, tau_skim=1e-4)), ctypes.byref(pk)) == 0
@@ -149,12 +162,12 @@ def test_plan_rejects_bad_pointers_before_any_launch(lib):
 
 
 def test_config_layout_matches_header(lib):
-    """The binding's struct has the header's field order; tau_skim is last."""
+    """The binding's struct has the header's field order; low_refine is last."""
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     body = re.search(r"typedef struct \{(.*?)\} tattn_config;", text, flags=re.S).group(1)
     names = re.findall(r"([a-z_]+)\s*[,;]", body)
     assert names == [f for f, _ in Config._fields_]
-    assert ctypes.sizeof(Config) == 96
+    assert ctypes.sizeof(Config) == 104
 
 
 def test_status_strings(lib):

@@ -41,7 +41,7 @@ class Config(ctypes.Structure):
                 ("full_frac", ctypes.c_float), ("entropy_samples", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
-                ("price", ctypes.c_float), ("tau_skim", ctypes.c_float)]
+                ("price", ctypes.c_float), ("tau_skim", ctypes.c_float), ("low_refine", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -70,6 +70,7 @@ _SIGS = {
     "tattn_plan_get_pool": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "tattn_plan_get_codes": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_get_mx4": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+    "tattn_plan_get_mx4_residual": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "tattn_plan_stats": (ctypes.c_int, [_VP, ctypes.POINTER(Stats)]),
     "tattn_plan_get_kh": (ctypes.c_int, [_VP, _VP, _VP]),
     "tattn_plan_get_moments": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
@@ -105,13 +106,14 @@ def _check(status):
 
 def make_config(batch, heads, seq_len, head_dim, block_q, block_k, tau_hi=0.0, tau_lo=0.0, top_k=0,
                 mode="threshold", keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256,
-                out_fp32=False, strides=None, price=0.0, tau_skim=0.0):
+                out_fp32=False, strides=None, price=0.0, tau_skim=0.0, low_refine=False):
     if strides is None:
         strides = (heads * seq_len * head_dim, seq_len * head_dim, head_dim)
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
     return Config(batch, heads, seq_len, head_dim, block_q, block_k, float(tau_hi), float(tau_lo), int(top_k), m,
                   float(keep_min), float(keep_max), float(full_frac), int(entropy_samples), 0,
-                  1 if out_fp32 else 0, *[int(s) for s in strides], float(price), float(tau_skim))
+                  1 if out_fp32 else 0, *[int(s) for s in strides], float(price), float(tau_skim),
+                  1 if low_refine else 0)
 
 
 def _stream():
@@ -202,6 +204,16 @@ class Plan:
         _check(load_library().tattn_plan_get_mx4(self._handle, k4.ctypes.data, k4s.ctypes.data, _stream()))
         return dict(k4=k4, k4s=k4s)
 
+    def mx4_residual(self):
+        """Refined low tier: the MXFP4 copy of K's rounding residual (layouts
+        as mx4())."""
+        n, d = self.cfg.seq_len, self.cfg.head_dim
+        k4r = np.empty(self._shape(n, d // 2), np.uint8)
+        k4rs = np.empty(self._shape(n, d // 32), np.uint8)
+        _check(load_library().tattn_plan_get_mx4_residual(self._handle, k4r.ctypes.data, k4rs.ctypes.data,
+                                                          _stream()))
+        return dict(k4r=k4r, k4rs=k4rs)
+
     def stats(self) -> dict:
         st = Stats()
         _check(load_library().tattn_plan_stats(self._handle, ctypes.byref(st)))
@@ -242,17 +254,18 @@ def _check_tensors(q, k, v):
 
 def plan(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, mode="threshold",
          keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256, out_fp32=False,
-         workspace=None, price=0.0, tau_skim=0.0) -> Plan:
+         workspace=None, price=0.0, tau_skim=0.0, low_refine=False) -> Plan:
     """Pool, quantise and route (K1, K2).  q, k, v: bf16 [B, H, N, d] on the GPU.
     ``tau_skim`` > 0 adds the MXFP4 SKIM tier (threshold, external and price
-    modes, 64-key blocks).  ``workspace`` (a uint8 GPU tensor, e.g. an earlier
+    modes, 64-key blocks).  ``low_refine`` scores LOW tiles on MXFP4 copies
+    with residual correction instead of E4M3 (64-key blocks, no SKIM tier).  ``workspace`` (a uint8 GPU tensor, e.g. an earlier
     plan's) is reused when large enough; the earlier plan must not be used
     afterwards."""
     _check_tensors(q, k, v)
     B, H, N, d = q.shape
     cfg = make_config(B, H, N, d, block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
                       full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price,
-                      tau_skim=tau_skim)
+                      tau_skim=tau_skim, low_refine=low_refine)
     return Plan(cfg, q, k, v, workspace=workspace)
 
 
@@ -307,7 +320,7 @@ def forward_dump(p: Plan, q, k, v, rows, steps, out=None):
 
 def attention_static(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, mode="threshold",
                      keep_min=0.05, keep_max=0.5, full_frac=0.1, entropy_samples=256, out_fp32=False, price=0.0,
-                     tau_skim=0.0, out=None):
+                     tau_skim=0.0, out=None, low_refine=False):
     """Plan and forward in one call with the library's static workspace (no
     device allocation inside the call; ``out`` may be preallocated).
     Problems whose workspace exceeds 64 MiB raise."""
@@ -315,7 +328,8 @@ def attention_static(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001
     _check_tensors(q, k, v)
     B, H, N, d = q.shape
     cfg = make_config(B, H, N, d, block_q, block_k, tau_hi, tau_lo, top_k, mode, keep_min, keep_max,
-                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price, tau_skim=tau_skim)
+                      full_frac, entropy_samples, out_fp32, strides=q.stride()[:3], price=price, tau_skim=tau_skim,
+                      low_refine=low_refine)
     dt = torch.float32 if out_fp32 else torch.bfloat16
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=dt, device=q.device)

@@ -23,7 +23,8 @@
 //                    fl16(fl32(decode(E4M3(v * inv)) * sv)), in vt's layout (their
 //                    gathered steps mix blocks of different scales in one P.V).
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
-// With the SKIM tier a third kernel writes the MXFP4 copy of K (k1_mx4).
+// With the SKIM tier or the refined low tier a third kernel writes the MXFP4
+// copy of K (k1_mx4), for the latter also that of its rounding residual.
 // For the price router both also write second moments from float64 sums of
 // squares ("Triage": the router works from block statistics): per dimension
 // the query mean square and the key variance, per block the key and value
@@ -346,12 +347,16 @@ __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   }
 }
 
-// MXFP4 copy of K_J for the SKIM tier (64-key blocks; "Triage": skimming a
-// tile's scores in a 4-bit format).  Per key row and 32 channels one E8M0
-// scale and 32 E2M1 codes: codes [64][D/2] (channel 2m in the low nibble of
-// byte m) and scale bytes [64][D/32], row-major.  Rows past N are zero (codes
-// 0, scale byte 0).
-template <int D>
+// MXFP4 copy of K_J for the SKIM tier and the refined low tier (64-key
+// blocks; "Triage": skimming a tile's scores in a 4-bit format).  Per key row
+// and 32 channels one E8M0 scale and 32 E2M1 codes: codes [64][D/2] (channel
+// 2m in the low nibble of byte m) and scale bytes [64][D/32], row-major.
+// RESID (refined low tier, "Triage": refining with 4-bit residual
+// correction): also the MXFP4 copy of the rounding residual x - code * 2^e,
+// which is exact in float32 (bf16 x against a 2-bit-significand grid point
+// within 2^(e+1) of it), with its own scales, in the k4r / k4rs regions.  Rows
+// past N are zero (codes 0, scale byte 0).
+template <int D, bool RESID>
 __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
   constexpr int NB = D / 32;            // scale blocks per row
   const Dims& dm = a.d;
@@ -381,10 +386,28 @@ __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
     }
     const int ex = mx4_exponent(amax);
     uint32_t pk[4] = {0, 0, 0, 0};
+    float ramax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
+    for (int e = 0; e < 32; e++) {
+      const uint32_t code = e2m1_code(ldexpf(x[e], -ex));
+      pk[e >> 3] |= code << (4 * (e & 7));
+      if constexpr (RESID) {
+        x[e] -= ldexpf(e2m1_value(code), ex);   // the residual, in place
+        ramax = __builtin_fmaxf(ramax, __builtin_fabsf(x[e]));
+      }
+    }
     *reinterpret_cast<uint4*>(k4 + r * (D / 2) + 16 * c) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     k4s[r * NB + c] = static_cast<unsigned char>(ex + 127);
+    if constexpr (RESID) {
+      const int er = mx4_exponent(ramax);
+      uint32_t rk[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 32; e++) rk[e >> 3] |= e2m1_code(ldexpf(x[e], -er)) << (4 * (e & 7));
+      unsigned char* k4r = slab + a.L.sl.k4r + (int64_t)J * 64 * (D / 2);
+      unsigned char* k4rs = slab + a.L.sl.k4rs + (int64_t)J * 64 * NB;
+      *reinterpret_cast<uint4*>(k4r + r * (D / 2) + 16 * c) = make_uint4(rk[0], rk[1], rk[2], rk[3]);
+      k4rs[r * NB + c] = static_cast<unsigned char>(er + 127);
+    }
   }
 }
 
@@ -406,7 +429,10 @@ hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess || !a.mx4) return e;
   if (d.Bk != 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k1_mx4<D>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  if (a.resid)
+    hipLaunchKernelGGL((k1_mx4<D, true>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_mx4<D, false>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

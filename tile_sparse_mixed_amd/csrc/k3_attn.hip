@@ -166,6 +166,31 @@ __device__ inline void schedule_low_step() {
   }
 }
 
+// Schedule of a pipelined refined low-tier step: per score block of the next
+// step its K4, residual and scale-word reads, then its 3 D/64 fp4 MFMAs
+// spread through this step's quantisation; the row-sum MFMA; then the P.V as
+// in schedule_low_step.
+template <int D>
+__device__ inline void schedule_refine_step() {
+#pragma unroll
+  for (int b = 0; b < 2; b++) {
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 32 + 2, 0);   // DS reads: one score block's K operands
+#pragma unroll
+    for (int i = 0; i < 3 * D / 64; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);          // VALU: this step's quantisation
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA: next step's scores
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA: row sum of the codes
+  __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);     // DS reads: this step's V codes
+#pragma unroll
+  for (int i = 0; i < D / 32; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);       // VALU: accumulator block i times wr
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA: P.V into block i
+  }
+}
+
 // LDS swizzles.  An MFMA operand read has the lanes of a half-wave read 16
 // bytes at the same logical chunk of 32 consecutive rows.  gfx950 serves a
 // ds_read_b128 16 lanes at a time across 64 four-byte banks (256 bytes), so
@@ -199,10 +224,17 @@ struct StepScale {
 
 // SKIM: the instance also runs the SKIM tier (64-key blocks only); the other
 // instances carry none of its code.  DUMP: the probability-code dump.
-template <int D, int NW, int BK, bool SKIM, bool DUMP>
+// REFINE: LOW tiles score on MXFP4 copies of Q and K with an MXFP4 residual
+// correction, <q4,k4> + <q4,k4r> + <q4r,k4> on the block-scaled fp4 MFMA
+// ("Triage": refining a tile with 4-bit residual correction); their
+// probabilities and P.V are the E4M3 ones.  R0 of such a step holds K4 rows
+// [64][D/2] at 0, their scale words at 32 D, the residual rows at 64 D and
+// their scale words at 96 D.
+template <int D, int NW, int BK, bool SKIM, bool DUMP, bool REFINE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
   static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
+  static_assert(!REFINE || (BK == 64 && !SKIM), "the refined low tier runs on 64-key blocks without SKIM");
   static_assert(!SKIM || BK == 64, "the SKIM tier runs on 64-key blocks");
   constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int R1 = 128 * D;         // bytes of each half of a stage (R0: K-side operands, R1: V-side)
@@ -438,6 +470,22 @@ void k3_attn(AttnArgs a) {
       dma16(rS, reg + k * 1024, voffV8, (int)SL.v8t + J * 64 * D + k * 1024);
     }
   };
+  // MXFP4 K rows of block J and of its residual, with their scale words, into
+  // the R0 region `st` of a refined LOW step
+  auto refine_k = [&](int J, unsigned char* st) __attribute__((always_inline)) {
+    for (int k = wave; k < D / 32; k += NW) {
+      dma16(rS, st + k * 1024, voffK4, (int)SL.k4 + J * 32 * D + k * 1024);
+      dma16(rS, st + 64 * D + k * 1024, voffK4, (int)SL.k4r + J * 32 * D + k * 1024);
+    }
+    if (wave == 0 || wave == NW - 1) {
+      unsigned char* dst = st + (wave == 0 ? 32 * D : 96 * D);
+      const int src = (wave == 0 ? (int)SL.k4s : (int)SL.k4rs) + J * 2 * D;
+      if constexpr (D == 128)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)dst, 4, lane * 4, src, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)dst, 2, lane * 2, src, 0, 0);
+    }
+  };
   // KINDS: bit mask of the step kinds that can occur where this is called; the
   // other branches are not generated, so their address terms are not kept live.
   // PART: 1 = the R0 half (K, E4M3 K, MXFP4 K and its scales, kbar hi) and
@@ -543,15 +591,19 @@ void k3_attn(AttnArgs a) {
     } else if (G == 1 && (KINDS & (1 << kLow)) && kind == kLow) {
       const int J = list_at(t);
       if constexpr (PA) {
+        if constexpr (REFINE) {
+          refine_k(J, st);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NI8; i++) {
-          const int k = wave + NW * i;
-          dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+          for (int i = 0; i < NI8; i++) {
+            const int k = wave + NW * i;
+            dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+          }
         }
       }
       if constexpr (PB) load_v8(r1(st), J);
       if constexpr (PA) {
-        cst.c[0] = sq * skp[J] * cF;
+        cst.c[0] = REFINE ? cF : sq * skp[J] * cF;   // refined: the fp4 scales are inside the MFMA
         cst.v = svp[J];
       }
     } else if (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
@@ -687,6 +739,46 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int b = 0; b < 2; b++)
         s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[2 * i + b], q8[i], s[b], 0, 0, 0, 0, 0, 0);
+  };
+  // S^T of a refined LOW step: scores_fp4's operand layout, three passes per
+  // instruction: K4 x Q4, the K residual x Q4, K4 x the Q residual.
+  auto scores_refine = [&](const unsigned char* st, f32x16* s, const i32x8* q4, const int* q4s, const i32x8* q4r,
+                           const int* q4rs) __attribute__((always_inline)) {
+    const int sw = D == 128 ? (ln >> 2) & 3 : (ln >> 3) & 1;
+    // one score block (32 keys) at a time, its operands read just before its
+    // MFMAs: all of them at once would need 32 more registers than the
+    // pipelined step has
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      const int r = ln + 32 * b;
+      uint32_t word, wordr;
+      if constexpr (D == 128) {
+        word = *reinterpret_cast<const uint32_t*>(st + 32 * D + 4 * r);
+        wordr = *reinterpret_cast<const uint32_t*>(st + 96 * D + 4 * r);
+      } else {
+        word = *reinterpret_cast<const uint16_t*>(st + 32 * D + 4 * r);
+        wordr = *reinterpret_cast<const uint16_t*>(st + 96 * D + 4 * r);
+      }
+      const int ks = static_cast<int>(word >> (8 * lh)), krs = static_cast<int>(wordr >> (8 * lh));
+      i32x8 ka[D / 64], kr[D / 64];
+#pragma unroll
+      for (int i = 0; i < D / 64; i++) {
+        const int off = r * (D / 2) + (((2 * i + lh) ^ sw) << 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(st + off);
+        const uint4 w = *reinterpret_cast<const uint4*>(st + 64 * D + off);
+        ka[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        kr[i] = i32x8{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      }
+      // opsel picks byte 2i of the key row's word: the scale of the lane's block
+      s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[0], q4[0], s[b], 4, 4, 0, ks, 0, q4s[0]);
+      s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[0], q4[0], s[b], 4, 4, 0, krs, 0, q4s[0]);
+      s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[0], q4r[0], s[b], 4, 4, 0, ks, 0, q4rs[0]);
+      if constexpr (D == 128) {
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[1], q4[1], s[b], 4, 4, 2, ks, 0, q4s[1]);
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[1], q4[1], s[b], 4, 4, 2, krs, 0, q4s[1]);
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[1], q4r[1], s[b], 4, 4, 2, ks, 0, q4rs[1]);
+      }
+    }
   };
   // S^T of a SKIM step on the block-scaled fp4 MFMA: lane (ln, lh) holds
   // channels 64i + 32lh .. +31 of key rows ln and ln + 32 (from the stage) and
@@ -1077,32 +1169,61 @@ void k3_attn(AttnArgs a) {
   };
   // the MXFP4 copy of this lane's Q row (channels 64i + 32lh .. +31 for
   // instruction i, one E8M0 scale each), from Q in memory
-  auto make_q4 = [&](i32x8* q4reg, int* q4s) __attribute__((always_inline)) {
-    const uint16_t* qp = a.q + toff + (int64_t)qrow * dm.sn + 32 * lh;
-#pragma unroll
-    for (int i = 0; i < D / 64; i++) {
-      float x[32];
-      float amax = 0.0f;
+  auto make_q4 = [&](i32x8* q4reg, int* q4s, i32x8* q4rreg = nullptr, int* q4rs = nullptr) __attribute__((always_inline)) {
+    // buffer loads through a resource over the head's rows: a row past N
+    // reads as zeros without a branch
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + toff, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
+    const int qoff = (qrow * (int)dm.sn + 32 * lh) * 2;
+    auto load32 = [&](int i, float* x) __attribute__((always_inline)) {   // channels 64i + 32lh .. +31
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (qrow < dm.N) raw = *reinterpret_cast<const uint4*>(qp + 64 * i + 8 * j);
+        const uint4 raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qoff + (64 * i + 8 * j) * 2, 0, 0));
         const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float f = __uint_as_float(e & 1 ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
-          x[8 * j + e] = f;
-          amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
-        }
+        for (int e = 0; e < 8; e++) x[8 * j + e] = __uint_as_float(e & 1 ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16));
       }
-      const int ex = mx4_exponent(amax);
+    };
+    auto encode32 = [&](const float* x, int& ex) __attribute__((always_inline)) {   // MXFP4 codes of 32 values
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; e++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[e]));
+      ex = mx4_exponent(amax);
       uint32_t pk[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 32; e++) pk[e >> 3] |= e2m1_code(ldexpf(x[e], -ex)) << (4 * (e & 7));
-      q4reg[i] = i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+      return i32x8{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+    };
+#pragma unroll
+    for (int i = 0; i < D / 64; i++) {
+      float x[32];
+      load32(i, x);
+      int ex;
+      q4reg[i] = encode32(x, ex);
       q4s[i] = ex + 127;
     }
+    if constexpr (REFINE) {
+      // the residual x - code 2^e (exact in float32), one 32-channel chunk at
+      // a time from a second read of Q: computed in the first pass it kept
+      // twice the values live and the register allocator spilled
+#pragma unroll
+      for (int i = 0; i < D / 64; i++) {
+        __builtin_amdgcn_sched_barrier(0);
+        float x[32];
+        load32(i, x);
+        const int ex = q4s[i] - 127;
+#pragma unroll
+        for (int e = 0; e < 32; e++)
+          x[e] -= ldexpf(e2m1_value((static_cast<uint32_t>(q4reg[i][e >> 3]) >> (4 * (e & 7))) & 15u), ex);
+        int er;
+        q4rreg[i] = encode32(x, er);
+        q4rs[i] = er + 127;
+      }
+    } else {
+      (void)q4rreg;
+      (void)q4rs;
+    }
   };
+
 
   if constexpr (!SPLIT) {
     if (nSteps > 0) issue(KAll{}, 0, stA, cA);
@@ -1135,9 +1256,18 @@ void k3_attn(AttnArgs a) {
       next();
     });
     if (t < tSk) {   // LOW tiles remain: make the E4M3 copy of Q (32 bytes per
-                     // fp8 instruction i = bf16 chunks 4i..4i+3)
+                     // fp8 instruction i = bf16 chunks 4i..4i+3), or for the
+                     // refined tier the MXFP4 copy of Q and of its residual
       i32x8 q8reg[D / 64];
-      make_q8(q8reg);
+      i32x8 q4reg[REFINE ? D / 64 : 1], q4rreg[REFINE ? D / 64 : 1];
+      int q4s[REFINE ? D / 64 : 1], q4rs[REFINE ? D / 64 : 1];
+      if constexpr (REFINE) make_q4(q4reg, q4s, q4rreg, q4rs);
+      else make_q8(q8reg);
+      // a LOW step's scores from the K operands staged in `st`
+      auto low_scores = [&](const unsigned char* st, f32x16* sc) __attribute__((always_inline)) {
+        if constexpr (REFINE) scores_refine(st, sc, q4reg, q4s, q4rreg, q4rs);
+        else scores_fp8(st, sc, q8reg);
+      };
       if constexpr (G == 1) {
         // Software pipeline: step t+1's score MFMAs are issued ahead of step
         // t's softmax, so the matrix core works while the VALU quantises the
@@ -1159,18 +1289,22 @@ void k3_attn(AttnArgs a) {
           const int i = nF + base + lane;
           const int J = i < nK + nSk ? (int)slist[i] : 0;
           jx = J;
-          cx = sq * skp[J] * cF;
+          cx = REFINE ? cF : sq * skp[J] * cF;   // refined: the fp4 scales are inside the MFMA
           vx = svp[J];
         };
         auto rl = [](int x, int l) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(x, l); };
         auto rlf = [](float x, int l) __attribute__((always_inline)) {
           return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
         };
-        auto low_k = [&](int J, unsigned char* st) __attribute__((always_inline)) {   // E4M3 K of block J into R0
+        auto low_k = [&](int J, unsigned char* st) __attribute__((always_inline)) {   // the K operands of block J into R0
+          if constexpr (REFINE) {
+            refine_k(J, st);
+          } else {
 #pragma unroll
-          for (int i = 0; i < NI8; i++) {
-            const int k = wave + NW * i;
-            dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+            for (int i = 0; i < NI8; i++) {
+              const int k = wave + NW * i;
+              dma16(rS, st + k * 1024, voffK8, (int)SL.k8 + J * 64 * D + k * 1024);
+            }
           }
         };
         using PartK = std::integral_constant<int, 1>;
@@ -1187,7 +1321,7 @@ void k3_attn(AttnArgs a) {
           f32x16* sc = sreg(p);
           sc[0] = f32x16{};
           sc[1] = f32x16{};
-          scores_fp8(stg(p), sc, q8reg);
+          low_scores(stg(p), sc);
           next();
         };
         if (t & 1) prologue(P1{});
@@ -1219,10 +1353,11 @@ void k3_attn(AttnArgs a) {
           f32x16* sn = sreg(flip(p));
           sn[0] = f32x16{};
           sn[1] = f32x16{};
-          scores_fp8(stg(flip(p)), sn, q8reg);
+          low_scores(stg(flip(p)), sn);
           quant_soft64(sc, c, sv, k);
           pv8(stg(p));
-          schedule_low_step<D>();
+          if constexpr (REFINE) schedule_refine_step<D>();
+          else schedule_low_step<D>();
           next();
         });
       } else {
@@ -1265,7 +1400,8 @@ void k3_attn(AttnArgs a) {
       if (u >= nSteps) return 0;
       const int k = step_kind(u);
       if (k == kFull || k == kSkipS) return NI16;
-      if (k == kLow) return NI8;
+      if (k == kLow)   // refined: K rows and residual rows, one scale-word load each from the first and last wave
+        return REFINE ? 2 * ((D / 32 - wave + NW - 1) / NW) + (wave == 0 ? 1 : 0) + (wave == NW - 1 ? 1 : 0) : NI8;
       if (k == kSkipPV) return 0;
       return (D / 32 - wave + NW - 1) / NW + (wave == 0 ? 1 : 0);   // SKIM: K rows and the scale words
     };
@@ -1324,10 +1460,16 @@ void k3_attn(AttnArgs a) {
                  [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T0{}, t, s, c); });
     if (t < tSk) {
       i32x8 q8reg[D / 64];
-      make_q8(q8reg);
+      i32x8 q4reg[REFINE ? D / 64 : 1], q4rreg[REFINE ? D / 64 : 1];
+      int q4s[REFINE ? D / 64 : 1], q4rs[REFINE ? D / 64 : 1];
+      if constexpr (REFINE) make_q4(q4reg, q4s, q4rreg, q4rs);
+      else make_q8(q8reg);
       while (t < tSk)
         split_step(KLow{}, T1{}, T1{}, T0{}, std::integral_constant<bool, G == 1>{},
-                   [&](f32x16* s) __attribute__((always_inline)) { scores_fp8(stA, s, q8reg); },
+                   [&](f32x16* s) __attribute__((always_inline)) {
+                     if constexpr (REFINE) scores_refine(stA, s, q4reg, q4s, q4rreg, q4rs);
+                     else scores_fp8(stA, s, q8reg);
+                   },
                    [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T1{}, t, s, c); });
     }
     if constexpr (SKIM) {
@@ -1379,19 +1521,22 @@ void k3_attn(AttnArgs a) {
 
 template <int D, int NW, bool DUMP>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  if (a.skim && a.d.Bk != 64) return hipErrorInvalidValue;
+  if ((a.skim || a.refine) && a.d.Bk != 64) return hipErrorInvalidValue;
+  if (a.skim && a.refine) return hipErrorInvalidValue;
   if (a.d.Nk > kMaxNk || a.list_cap < 1 || a.list_cap > a.d.Nk) return hipErrorInvalidValue;
   if (DUMP && (!a.dslot || !a.dump || a.dsteps < 1)) return hipErrorInvalidValue;
   const size_t lds = ((size_t)a.list_cap * 2 + 15) / 16 * 16;   // the row's list (dynamic LDS)
   const dim3 grid(a.d.BH * a.d.Nq), block(NW * 64);
   if (a.skim)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64, true, DUMP>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, true, DUMP, false>), grid, block, lds, s, a);
+  else if (a.refine)
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP, true>), grid, block, lds, s, a);
   else if (a.d.Bk == 64)
-    hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP, false>), grid, block, lds, s, a);
   else if (a.d.Bk == 16)
-    hipLaunchKernelGGL((k3_attn<D, NW, 16, false, DUMP>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 16, false, DUMP, false>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((k3_attn<D, NW, 8, false, DUMP>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((k3_attn<D, NW, 8, false, DUMP, false>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 

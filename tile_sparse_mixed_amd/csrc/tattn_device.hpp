@@ -117,14 +117,27 @@ __device__ inline int mx4_exponent(float amax) {
 }
 // E2M1 code of y (the element already divided by its block scale, |y| < 8):
 // round to nearest, ties to even, on the grid spacing of y's binade (0.5 below
-// 2, 1 in [2, 4), 2 above), magnitudes past 6 clamped to 6.
+// 2, 1 in [2, 4), 2 above), magnitudes past 6 clamped to 6.  Every candidate
+// is computed and one is selected, so the code has no branches (a branchy form
+// compiled to divergent regions that spilled registers where it is unrolled).
 __device__ inline uint32_t e2m1_code(float y) {
   const float a = __builtin_fabsf(y);
-  uint32_t c;
-  if (a < 2.0f) c = static_cast<uint32_t>(__builtin_rintf(a * 2.0f));            // codes 0..4
-  else if (a < 4.0f) c = static_cast<uint32_t>(__builtin_rintf(a)) + 2u;         // 2, 3, 4 -> 4, 5, 6
-  else c = __builtin_rintf(a * 0.5f) >= 3.0f ? 7u : 6u;                          // 6 (or 8) -> 7, 4 -> 6
-  return c | (y < 0.0f ? 8u : 0u);
+  const float c_lo = __builtin_rintf(a * 2.0f);                        // [0, 2): codes 0..4
+  const float c_mid = __builtin_rintf(a) + 2.0f;                       // [2, 4): 2, 3, 4 -> 4, 5, 6
+  const float c_hi = __builtin_rintf(a * 0.5f) >= 3.0f ? 7.0f : 6.0f;  // 6 (or 8) -> 7, 4 -> 6
+  const float c = a < 2.0f ? c_lo : (a < 4.0f ? c_mid : c_hi);
+  return static_cast<uint32_t>(c) | (y < 0.0f ? 8u : 0u);
+}
+
+// Value of an E2M1 code (bit 3 the sign): 0, 0.5, 1, 1.5, 2, 3, 4, 6
+// (branch-free, as e2m1_code).
+__device__ inline float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float sub = 0.5f * static_cast<float>(m);                                     // m = 0, 1
+  const float nrm = __builtin_amdgcn_ldexpf(1.0f + 0.5f * static_cast<float>(m & 1u),
+                                            static_cast<int>(m >> 1) - 1);            // m >= 2
+  const float mag = m < 2u ? sub : nrm;
+  return (c & 8u) ? -mag : mag;
 }
 
 // ---------------------------------------------------------------------------

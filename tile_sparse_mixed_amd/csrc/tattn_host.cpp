@@ -55,7 +55,7 @@ Dims make_dims(const tattn_config& c) {
   return d;
 }
 
-Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim) {
+Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim, bool refine) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -87,9 +87,11 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim) 
     sl.kbhi = sub(Nk * D * 2);
     sl.kblo = sub(Nk * D * 2);
     sl.vbarT = sub((size_t)d.NkC * 64 * D * 2);
-    const size_t k4n = skim ? Nk * Bk : 0;
+    const size_t k4n = skim || refine ? Nk * Bk : 0, k4rn = refine ? Nk * Bk : 0;
     sl.k4 = sub(k4n * D / 2);
     sl.k4s = sub(k4n * D / 32);
+    sl.k4r = sub(k4rn * D / 2);
+    sl.k4rs = sub(k4rn * D / 32);
     sl.bytes = o;
   }
   L.slab = take(BH * L.sl.bytes);
@@ -124,8 +126,10 @@ static bool skim_on(const tattn_config& c) {
   return c.tau_skim > 0.0f &&
          (c.mode == TATTN_MODE_THRESHOLD || c.mode == TATTN_MODE_EXTERNAL || c.mode == TATTN_MODE_PRICE);
 }
+// The refined low tier: LOW tiles score on MXFP4 copies with residual correction.
+static bool refine_on(const tattn_config& c) { return c.low_refine == 1; }
 static Layout layout_of(const tattn_config& c) {
-  return make_layout(make_dims(c), c.entropy_samples, c.mode == TATTN_MODE_PRICE, skim_on(c));
+  return make_layout(make_dims(c), c.entropy_samples, c.mode == TATTN_MODE_PRICE, skim_on(c), refine_on(c));
 }
 
 // Most tiles a row can keep (FULL, LOW or SKIM) under the config's rule:
@@ -166,6 +170,11 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "tau_skim needs 0 <= tau_skim <= tau_lo (got %g, tau_lo %g)", c->tau_skim, c->tau_lo);
   if (skim_on(*c) && c->block_k != 64)
     return fail(TATTN_E_UNSUPPORTED, "the SKIM tier needs 64-key blocks (block_k %d)", c->block_k);
+  if (c->low_refine != 0 && c->low_refine != 1) return fail(TATTN_E_INVALID, "low_refine must be 0 or 1 (got %d)", c->low_refine);
+  if (refine_on(*c) && c->block_k != 64)
+    return fail(TATTN_E_UNSUPPORTED, "the refined low tier needs 64-key blocks (block_k %d)", c->block_k);
+  if (refine_on(*c) && skim_on(*c))
+    return fail(TATTN_E_UNSUPPORTED, "the refined low tier and the SKIM tier are not combined");
   const int64_t nq = (c->seq_len + (int64_t)c->block_q - 1) / c->block_q;
   const int64_t nk = (c->seq_len + (int64_t)c->block_k - 1) / c->block_k;
   if (c->top_k < 0 || c->top_k > nk) return fail(TATTN_E_INVALID, "top_k %d outside [0, %lld]", c->top_k, (long long)nk);
@@ -282,7 +291,8 @@ static tattn_status plan_into(tattn_plan_s* p, const tattn_config* cfg, const vo
   p->has_tiers = cfg->mode != TATTN_MODE_EXTERNAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-              p->ws, p->L, p->d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(*cfg) ? 1 : 0};
+              p->ws, p->L, p->d, cfg->mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(*cfg) || refine_on(*cfg) ? 1 : 0,
+              refine_on(*cfg) ? 1 : 0};
   hipError_t e = launch_pool(pa, s);
   if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
   if (cfg->mode != TATTN_MODE_EXTERNAL) {
@@ -325,7 +335,7 @@ static tattn_status forward_impl(tattn_plan_t p, const void* q, const void* k, c
   if (!p->has_tiers) return fail(TATTN_E_STATE, "external-mode plan has no tiers yet (call tattn_plan_set_tiers)");
   AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), o,
              p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d, skim_on(p->cfg) ? 1 : 0,
-             list_cap(p->cfg, p->d), dslot, dump, dsteps};
+             refine_on(p->cfg) ? 1 : 0, list_cap(p->cfg, p->d), dslot, dump, dsteps};
   hipError_t e = launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return ok();
@@ -379,7 +389,8 @@ tattn_status tattn_replan(tattn_plan_t p, const void* q, const void* k, const vo
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(TATTN_E_INVALID, "q, k, v must be 16-byte aligned");
   if (!p->has_tiers) return fail(TATTN_E_STATE, "plan has no tiers yet (nothing to reuse)");
   PoolArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-              p->ws, p->L, p->d, p->cfg.mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(p->cfg) ? 1 : 0};
+              p->ws, p->L, p->d, p->cfg.mode == TATTN_MODE_PRICE ? 1 : 0, skim_on(p->cfg) || refine_on(p->cfg) ? 1 : 0,
+              refine_on(p->cfg) ? 1 : 0};
   hipError_t e = launch_pool(pa, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
   p->k = k;
@@ -495,9 +506,9 @@ tattn_status tattn_plan_get_codes(tattn_plan_t p, uint8_t* host_k8, uint8_t* hos
   return ok();
 }
 
-tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_k4s, void* stream) {
-  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
-  if (!skim_on(p->cfg)) return fail(TATTN_E_STATE, "MXFP4 copies exist only with the SKIM tier (tau_skim > 0)");
+// Copy out one MXFP4 region pair of every head's slab in the canonical layout.
+static tattn_status get_mx4_pair(tattn_plan_t p, size_t codes_off, size_t scales_off, uint8_t* host_codes,
+                                 uint8_t* host_scales, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Dims& d = p->d;
   const int hb = d.D / 2, nsc = d.D / 32;
@@ -506,16 +517,29 @@ tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_
   for (size_t bh = 0; bh < (size_t)d.BH; bh++) {
     if ((st = copy_out(slab.data(), p->ws + p->L.slab + bh * p->L.sl.bytes, slab.size(), s)) != TATTN_OK) return st;
     if ((st = sync(s)) != TATTN_OK) return st;
-    const uint8_t* k4 = slab.data() + p->L.sl.k4;
-    const uint8_t* k4s = slab.data() + p->L.sl.k4s;
+    const uint8_t* k4 = slab.data() + codes_off;
+    const uint8_t* k4s = slab.data() + scales_off;
     for (int J = 0; J < d.Nk; J++)
       for (int r = 0; r < 64 && J * 64 + r < d.N; r++) {
         const size_t n = (size_t)J * 64 + r, at = bh * d.N + n;
-        if (host_k4) std::memcpy(host_k4 + at * hb, k4 + n * hb, hb);
-        if (host_k4s) std::memcpy(host_k4s + at * nsc, k4s + n * nsc, nsc);
+        if (host_codes) std::memcpy(host_codes + at * hb, k4 + n * hb, hb);
+        if (host_scales) std::memcpy(host_scales + at * nsc, k4s + n * nsc, nsc);
       }
   }
   return ok();
+}
+
+tattn_status tattn_plan_get_mx4(tattn_plan_t p, uint8_t* host_k4, uint8_t* host_k4s, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!skim_on(p->cfg) && !refine_on(p->cfg))
+    return fail(TATTN_E_STATE, "MXFP4 copies exist only with the SKIM tier (tau_skim > 0) or low_refine = 1");
+  return get_mx4_pair(p, p->L.sl.k4, p->L.sl.k4s, host_k4, host_k4s, stream);
+}
+
+tattn_status tattn_plan_get_mx4_residual(tattn_plan_t p, uint8_t* host_k4r, uint8_t* host_k4rs, void* stream) {
+  if (!p) return fail(TATTN_E_INVALID, "plan is NULL");
+  if (!refine_on(p->cfg)) return fail(TATTN_E_STATE, "the MXFP4 residual exists only with low_refine = 1");
+  return get_mx4_pair(p, p->L.sl.k4r, p->L.sl.k4rs, host_k4r, host_k4rs, stream);
 }
 
 tattn_status tattn_plan_get_moments(tattn_plan_t p, float* q2, float* m2q, float* kvar, float* m2k, float* vvar,
@@ -566,9 +590,10 @@ tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {
         if (tr[J] == TATTN_FULL) {
           st.n_full++;
           st.flops_bf16 += 4.0 * mI * nJ * D;
-        } else if (tr[J] == TATTN_LOW) {   // fp8 scores; fp8 P.V (64-key blocks) or fp16 P.V
-          st.n_low++;
-          st.flops_fp8 += 2.0 * mI * nJ * D;
+        } else if (tr[J] == TATTN_LOW) {   // fp8 scores (refined: three fp4 passes); fp8 P.V (64-key
+          st.n_low++;                      // blocks) or fp16 P.V
+          if (refine_on(p->cfg)) st.flops_fp4 += 6.0 * mI * nJ * D;
+          else st.flops_fp8 += 2.0 * mI * nJ * D;
           if (d.Bk == 64) st.flops_fp8 += 2.0 * mI * nJ * D;
           else st.flops_bf16 += 2.0 * mI * nJ * D;
         } else if (tr[J] == TATTN_SKIM) {  // fp4 scores, fp8 P.V
