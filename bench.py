@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan_like",
                     choices=["tiny", "small", "wan_like", "hunyuan_like", "fine_adaptive", "finer_adaptive",
-                             "wan_skim"])
+                             "wan_skim", "fine_skim", "fg4_adaptive", "fg1_adaptive"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-allfull", action="store_true", help="skip the all-full comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")

@@ -87,7 +87,7 @@ typedef enum { TATTN_BF16 = 0, TATTN_FP32 = 1 } tattn_dtype;
 
 typedef struct {
   int32_t batch, heads, seq_len, head_dim; /* head_dim in {64, 128}                          */
-  int32_t block_q, block_k;                /* block_q 64 or 128; block_k 64, 16 or 8         */
+  int32_t block_q, block_k;                /* block_q 64 or 128; block_k 64, 16, 8, 4, 2, 1  */
   float tau_hi, tau_lo;                    /* 0 <= tau_lo <= tau_hi, finite                  */
   int32_t top_k;                           /* 0 = off, else 1..ceil(seq_len/block_k)         */
   int32_t mode;                            /* tattn_mode                                     */
@@ -97,8 +97,8 @@ typedef struct {
   int64_t stride_b, stride_h, stride_n;    /* element strides shared by Q, K, V and O        */
   float price;                             /* PRICE: error per FULL tile of work, >= 0,
                                               finite; ignored by the other modes             */
-  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite, and block_k 64)
-                                              enables it: THRESHOLD uses it as the SKIM / SKIP
+  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite, and block_k
+                                              64, 16 or 8) enables it: THRESHOLD uses it as the SKIM / SKIP
                                               threshold (then <= tau_lo), EXTERNAL accepts SKIM
                                               bytes, PRICE weighs SKIM as a fourth choice;
                                               ignored by the other modes                     */
@@ -117,10 +117,11 @@ typedef struct {
   int64_t n_diag;                 /* diagonal tiles (always FULL)                    */
   double flops_bf16;              /* 16-bit MFMA flops: FULL tiles (4 m n d), SKIP
                                      tiles (4 m d: one pooled key each), and the
-                                     P.V half of LOW tiles with 16- or 8-key blocks */
+                                     P.V half of LOW and SKIM tiles with blocks
+                                     below 64 keys                                  */
   double flops_fp8;               /* fp8 MFMA flops: LOW tiles (4 m n d with 64-key
                                      blocks, else the score half), the P.V half of
-                                     SKIM tiles                                     */
+                                     SKIM tiles with 64-key blocks                  */
   double flops_dense;             /* 4 * N^2 * d * B * H: dense-equivalent work      */
   int64_t n_skim;                 /* SKIM tiles                                      */
   double flops_fp4;               /* fp4 MFMA flops: the score half of SKIM tiles,
@@ -161,8 +162,9 @@ tattn_status tattn_workspace_bytes(const tattn_config* cfg, size_t* bytes /* hos
  * p~ * error + price * work (work FULL 1, LOW 0.75, SKIM 0.625, SKIP
  * 1.5 / block_k; ties to the cheaper tier).  All in float64.
  * q, k, v: the caller's tensors.  The plan keeps derived copies of K and V
- * (E4M3 codes, a transposed fp16 V, means) in `workspace`, so a later
- * tattn_forward must be given the same k and v pointers with unchanged
+ * (E4M3 and MXFP4 codes, the low tier's dequantised V for blocks below 64
+ * keys, means) in `workspace`, and FULL tiles read k and v themselves, so a
+ * later tattn_forward must be given the same k and v pointers with unchanged
  * contents.  *out receives a new host handle (free with tattn_plan_destroy);
  * it stays valid while the workspace lives.  In TATTN_MODE_EXTERNAL the
  * router is not run and the plan has no tiers until tattn_plan_set_tiers.
@@ -178,8 +180,8 @@ tattn_status tattn_plan(const tattn_config* cfg, const void* q, const void* k, c
  * fp8 MFMA ("HierPAS": reduced precision for less critical tiles; "APT":
  * dual-precision execution); its probabilities are quantised to E4M3 against
  * the tile's row maximum (x_j = 448 e^{s_j - m_t}, so the maximum is 448), and
- * P.V runs on the fp8 MFMA against the E4M3 V (64-key blocks; with 16- and
- * 8-key blocks the quantised probabilities meet the dequantised V in fp16),
+ * P.V runs on the fp8 MFMA against the E4M3 V (64-key blocks; with smaller
+ * blocks the quantised probabilities meet the dequantised V in fp16),
  * the row normaliser summing the same quantised probabilities.  A SKIM tile
  * ("Triage": skimming in 4 bits) takes its scores from MXFP4 Q and K on the
  * block-scaled fp4 MFMA and is otherwise a LOW tile.
@@ -208,11 +210,12 @@ tattn_status tattn_forward(tattn_plan_t plan, const void* q, const void* k, cons
  *              code of score register (b = p / 16, r = p % 16) of lane half h,
  *              i.e. of staged key 32 b + 8 (r / 4) + 4 h + r % 4 of the step.
  *              A 64-key step is one key block; a 16-key step gathers the next
- *              four list entries (staged key m: block m / 16, key m % 16); an
- *              8-key step gathers eight (staged key m: block slot8(m), key
- *              kk8(m) as defined with the kernels: slot 2(2(m/32) + (m/16)%2)
- *              + (m/4)%2, key m%4 + 4((m/8)%2)).  Codes of keys past a block's
- *              end are 0.  Unwritten bytes keep their contents.
+ *              four list entries (staged key m: block m / 16, key m % 16); a
+ *              step of BK <= 8 keys per block gathers 64 / BK (staged key m:
+ *              block p / BK, key p % BK of the step's blocks, p = m with bits
+ *              2 and 3 swapped).  Codes of keys past a block's end are 0; with
+ *              one-key blocks every live key's code is 448 (0x7E).  Unwritten
+ *              bytes keep their contents.
  * TATTN_E_INVALID for NULL pointers or dump_steps < 1; otherwise as
  * tattn_forward.
  */

@@ -74,6 +74,18 @@ CONFIGS = {
     # and rule with 8-key blocks (4095 key blocks per row)
     "finer_adaptive": WorkloadConfig(6, "finer_adaptive", 1, 40, (21, 30, 52), 128, 64, 8, 0.01, 0.001,
                                      mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
+    # the fine workload's grid and 64x16 tiles under threshold tiers with the
+    # fourth tier: SKIM steps gather four 16-key blocks
+    "fine_skim": WorkloadConfig(10, "fine_skim", 1, 40, (21, 30, 52), 128, 64, 16, 0.01, 0.001,
+                                noise_sigma=0.5, temperature=True, seed_stream=3, tau_skim=1e-4),
+    # key blocks below 8 keys ("FG-Attn": M x N tiles down to N = 1) on the
+    # first frames of the Wan-like grid, sized to the 4096 key blocks a row
+    # may hold: 4-key blocks over 10 frames (3900 blocks), one-key blocks over
+    # 2 frames (3120 blocks)
+    "fg4_adaptive": WorkloadConfig(8, "fg4_adaptive", 1, 40, (10, 30, 52), 128, 64, 4, 0.01, 0.001,
+                                   mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
+    "fg1_adaptive": WorkloadConfig(9, "fg1_adaptive", 1, 40, (2, 30, 52), 128, 64, 1, 0.01, 0.001,
+                                   mode=MODE_ADAPTIVE, noise_sigma=0.5, temperature=True, seed_stream=3),
     # the Wan-like workload with the optional fourth tier: tiles whose router
     # probability lies in [tau_skim, tau_lo) run in MXFP4 instead of being skipped
     "wan_skim": WorkloadConfig(7, "wan_skim", 1, 40, (21, 30, 52), 128, 128, 64, 0.01, 0.001,

@@ -82,12 +82,12 @@ def _e4m3_table():
     return _DEC
 
 
-def _slot8(m):
-    return 2 * (2 * (m >> 5) + ((m >> 4) & 1)) + ((m >> 2) & 1)
-
-
-def _kk8(m):
-    return (m & 3) + 4 * ((m >> 3) & 1)
+def _prow(m):
+    """Place of staged key m's P value in the P.V operand order (bits 2 and 3
+    of m swapped): with blocks of bk <= 8 keys, staged key m is key
+    _prow(m) % bk of the step's block _prow(m) // bk (include/tattn.h,
+    tattn_forward_dump)."""
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1)
 
 
 # staged key of dump byte (half h, p): 32 (p / 16) + 8 ((p % 16) / 4) + 4 h + p % 4
@@ -96,11 +96,21 @@ _STAGED = 32 * ((_POS & 31) >> 4) + 8 * ((_POS & 15) >> 2) + 4 * (_POS >> 5) + (
 
 
 def quant_steps(counts_row, nk, bk, skim):
-    """(LOW steps, SKIM steps) of one query block."""
+    """(LOW steps, SKIM steps) of one query block: a step holds one 64-key
+    block or gathers 64 / bk smaller blocks of its tier."""
     nf, nl, ns = (int(x) for x in counts_row)
     g = 64 // bk
     nsk = nk - nf - nl - ns if skim else 0
-    return -(-nl // g), nsk
+    return -(-nl // g), -(-nsk // g)
+
+
+def _staged(m, g, bk):
+    """(slot, key) of staged key m of a step that gathers g blocks of bk keys."""
+    if g == 1:
+        return 0, m
+    if g == 4:
+        return m >> 4, m & 15
+    return _prow(m) // bk, _prow(m) % bk
 
 
 def kernel_tile_codes(dump_row, lists_row, counts_row, n, bq, bk, I, skim):
@@ -110,35 +120,22 @@ def kernel_tile_codes(dump_row, lists_row, counts_row, n, bq, bk, I, skim):
     g = 64 // bk
     m_i = min(bq, n - I * bq)
     sl, ssk = quant_steps(counts_row, nk, bk, skim)
+    nsk = nk - nf - nl - ns if skim else 0
     out = {}
-    low = lists_row[nf:nf + nl]
-    for s in range(sl):
-        blocks = low[g * s: g * s + g]
-        codes = dump_row[s, :m_i, :]                                   # [m_I, 64] by dump byte
-        for e in range(64):
-            m = _STAGED[e]
-            if g == 1:
-                gi, key = 0, m
-            elif g == 4:
-                gi, key = m >> 4, m & 15
-            else:
-                gi, key = _slot8(m), _kk8(m)
-            if gi >= len(blocks):
-                continue
-            J = int(blocks[gi])
-            nj = min(bk, n - J * bk)
-            if key >= nj:
-                continue
-            out.setdefault(J, np.zeros((m_i, nj), np.uint8))[:, key] = codes[:, e]
-    sk_blocks = lists_row[nf + nl: nf + nl + ssk]
-    for s in range(ssk):
-        J = int(sk_blocks[s])
-        nj = min(64, n - J * 64)
-        t = np.zeros((m_i, nj), np.uint8)
-        for e in range(64):
-            if _STAGED[e] < nj:
-                t[:, _STAGED[e]] = dump_row[sl + s, :m_i, e]
-        out[J] = t
+    # LOW steps first, then SKIM steps (tattn_forward_dump)
+    for first, tiles, nsteps in ((0, lists_row[nf:nf + nl], sl), (sl, lists_row[nf + nl:nf + nl + nsk], ssk)):
+        for s in range(nsteps):
+            blocks = tiles[g * s: g * s + g]
+            codes = dump_row[first + s, :m_i, :]                           # [m_I, 64] by dump byte
+            for e in range(64):
+                gi, key = _staged(_STAGED[e], g, bk)
+                if gi >= len(blocks):
+                    continue
+                J = int(blocks[gi])
+                nj = min(bk, n - J * bk)
+                if key >= nj:
+                    continue
+                out.setdefault(J, np.zeros((m_i, nj), np.uint8))[:, key] = codes[:, e]
     return out
 
 

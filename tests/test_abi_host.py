@@ -49,6 +49,9 @@ def test_valid_configs(lib):
     assert status(lib, good(seq_len=118800, heads=24)) == 0
     assert status(lib, good(top_k=10)) == 0
     assert status(lib, good(block_q=64, block_k=8)) == 0                 # 4095 key blocks
+    assert status(lib, good(block_q=64, block_k=4, seq_len=16380)) == 0   # 4095 key blocks
+    assert status(lib, good(block_q=128, block_k=2, seq_len=8192)) == 0   # 4096 key blocks
+    assert status(lib, good(block_q=64, block_k=1, seq_len=4096)) == 0    # one key per block
     assert status(lib, good(mode="price", price=0.01)) == 0
     assert status(lib, good(mode="price", price=0.0)) == 0
     assert status(lib, good(tau_skim=1e-4)) == 0                         # SKIM tier, threshold mode
@@ -58,7 +61,11 @@ def test_valid_configs(lib):
     # the price router weighs SKIM by its error model: no ordering against tau_lo
     assert status(lib, good(mode="price", price=0.01, tau_skim=0.5)) == 0
     assert status(lib, good(mode="price", price=0.01, tau_skim=-1e-4)) == -1
-    assert status(lib, good(mode="price", price=0.01, tau_skim=1e-4, block_q=64, block_k=16)) == -2
+    assert status(lib, good(mode="price", price=0.01, tau_skim=1e-4, block_q=64, block_k=16)) == 0
+    # the SKIM tier on 16- and 8-key blocks (gathered steps), not below
+    assert status(lib, good(tau_skim=1e-4, block_q=64, block_k=16)) == 0
+    assert status(lib, good(mode="external", tau_skim=1e-4, block_k=8)) == 0
+    assert status(lib, good(tau_skim=1e-4, block_q=64, block_k=4, seq_len=16380)) == -2
     # the refined low tier: 64-key blocks, not with the SKIM tier, any mode
     for m in ("threshold", "adaptive", "price", "external", "all_full"):
         assert status(lib, good(mode=m, price=0.01, low_refine=True)) == 0, m
@@ -75,6 +82,7 @@ def test_valid_configs(lib):
     (dict(block_k=16, strides=(40 * 32760 * 128 * 4096, 32760 * 128 * 4096, 128 * 4096)), -2),
     (dict(block_k=8, strides=(40 * 32760 * 128 * 4096, 32760 * 128 * 4096, 128 * 4096)), -2),
     (dict(block_k=8, seq_len=32776), -2),                                # 4097 key blocks
+    (dict(block_k=1, seq_len=4097), -2), (dict(block_k=3, seq_len=4096), -2),
     (dict(tau_hi=0.001, tau_lo=0.01), -1), (dict(tau_lo=-0.1), -1), (dict(tau_hi=float("inf")), -1),
     (dict(top_k=-1), -1), (dict(top_k=513), -1), (dict(mode=7), -1),
     (dict(mode="adaptive", keep_min=0.6, keep_max=0.5), -1), (dict(mode="adaptive", full_frac=0.0), -1),
@@ -83,7 +91,8 @@ def test_valid_configs(lib):
     (dict(mode="price", price=-1.0), -1), (dict(mode="price", price=float("nan")), -1),
     (dict(mode=5), -1),
     (dict(tau_skim=-1e-4), -1), (dict(tau_skim=0.002), -1), (dict(tau_skim=float("nan")), -1),
-    (dict(tau_skim=1e-4, block_q=64, block_k=16), -2), (dict(mode="external", tau_skim=1e-4, block_k=8), -2),
+    (dict(tau_skim=1e-4, block_q=64, block_k=2, seq_len=8192), -2),
+    (dict(mode="external", tau_skim=1e-4, block_k=1, seq_len=4096), -2),
 ])
 def test_invalid_configs(lib, kw, code):
     st = status(lib, good(**kw))
@@ -112,10 +121,11 @@ def test_workspace_formula(lib):
     n = ctypes.c_size_t()
     assert lib.tattn_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == 0
     BH, Nq, Nk, D = 40, 256, 512, 128
-    # dominant regions: E4M3 K and V (1 + 1 B) and the fp16 V^T (2 B) per key
-    # element; float64 logits, float32 p, tiers and int16 lists per tile; float32
-    # means and the bf16 hi/lo + fp16 pooled operands per block row
-    floor = (BH * Nk * 64 * D * 4 + BH * Nq * Nk * (8 + 4 + 1 + 2) + BH * (Nq + 2 * Nk) * D * 4
+    # dominant regions: E4M3 K and V (1 + 1 B) per key element (FULL tiles read
+    # the caller's V, so there is no 16-bit V copy); float64 logits, float32 p,
+    # tiers and int16 lists per tile; float32 means and the bf16 hi/lo + fp16
+    # pooled operands per block row
+    floor = (BH * Nk * 64 * D * 2 + BH * Nq * Nk * (8 + 4 + 1 + 2) + BH * (Nq + 2 * Nk) * D * 4
              + BH * Nk * D * 6)
     assert floor <= n.value <= floor * 1.05
     assert lib.tattn_workspace_bytes(ctypes.byref(good(head_dim=96)), ctypes.byref(n)) == -2

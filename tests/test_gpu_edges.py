@@ -47,15 +47,18 @@ def _check(cfg, g, p, d, rows=None, top_k=None, what=""):
     check_forward(tsm, p, d, g, cfg, OracleCfg(cfg, mode=3), rows=rows, what=what, log=_log)
 
 
-@pytest.mark.parametrize("bk", [64, 16])
+@pytest.mark.parametrize("bk", [64, 16, 1])
 def test_largest_key_block_count(bk):
     """4096 key blocks: N = 262144 tokens at 64-key blocks (d = 64, 128-row
-    query blocks), N = 65536 at 16-key blocks (d = 128, 64-row query blocks)."""
+    query blocks), N = 65536 at 16-key blocks (d = 128, 64-row query blocks),
+    N = 4096 at one-key blocks (d = 128, 64-row query blocks)."""
     import tile_sparse_mixed_amd as tsm
     if bk == 64:
         cfg = CONFIGS["small"].with_(heads=1, grid=(64, 64, 64))
-    else:
+    elif bk == 16:
         cfg = CONFIGS["fine_adaptive"].with_(heads=1, grid=(16, 64, 64), mode=0)
+    else:
+        cfg = CONFIGS["fine_adaptive"].with_(heads=1, grid=(4, 32, 32), mode=0, block_k=1)
     assert cfg.n_kblocks == 4096
     _log(f"[max Nk] N={cfg.seq_len} d={cfg.head_dim} tiles {cfg.block_q}x{cfg.block_k}")
     g = generate(cfg)
@@ -115,7 +118,7 @@ def test_equal_thresholds_have_no_low_tier():
     _check(cfg, g, p, d, what="tau_hi == tau_lo")
 
 
-@pytest.mark.parametrize("bk", [16, 8])
+@pytest.mark.parametrize("bk", [16, 8, 4, 1])
 def test_adaptive_rows_at_the_list_bound(bk):
     """keep_min = keep_max = 0.5 makes every head's k_h = ceil(0.5 Nk): each
     row keeps k_h tiles plus any diagonal block outside them, the most the

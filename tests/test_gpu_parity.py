@@ -31,6 +31,13 @@ SMALL = {
     "fine64x8": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=8),   # N=189: Nk=24 (last 5)
     "fine128x8_d64": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2, block_k=8),   # N=585: Nq=5, Nk=74 (last 1)
     "fine64x8_long": CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0, block_k=8),   # N=1000: Nk=125
+    # blocks below 8 keys: steps gather 16, 32 or 64 blocks
+    "fine64x4": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=4),   # N=189: Nk=48 (last 1)
+    "fine128x4_d64": CONFIGS["small"].with_(grid=(3, 7, 9), heads=2, block_k=4),   # N=189: Nk=48 (last 1)
+    "fine128x2_d64": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2, block_k=2),   # N=585: Nk=293 (last 1)
+    "fine64x2": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=2),   # N=189: Nk=95 (last 1)
+    "fine64x1": CONFIGS["fine_adaptive"].with_(grid=(2, 5, 13), heads=2, mode=0, block_k=1),   # N=130: Nk=130
+    "fine128x1_d64": CONFIGS["small"].with_(grid=(3, 7, 9), heads=2, block_k=1),   # N=189: Nk=189
 }
 
 
@@ -202,7 +209,8 @@ def _rank_ambiguous_rows(p, k):
     return np.abs(s[:, k - 1] - s[:, k]) <= 1e-12 * s[:, k - 1]
 
 
-@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged", "fine64x16", "fine_d64", "fine64x8", "fine128x8_d64"])
+@pytest.mark.parametrize("name", ["small", "ragged128", "d64_ragged", "fine64x16", "fine_d64", "fine64x8", "fine128x8_d64",
+                                  "fine64x4", "fine128x2_d64", "fine64x1"])
 def test_adaptive_mode(name):
     """Entropy-adaptive mode: k_h and r_h per head, rank tiers (top ceil(full_frac
     k_h) FULL, the rest of the top k_h LOW), lists, and the output under them."""

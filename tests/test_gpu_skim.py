@@ -20,6 +20,11 @@ CASES = {
     "small_q64": CONFIGS["small"].with_(heads=2, block_q=64, tau_skim=3e-4),                   # two waves
     "d128_ragged": CONFIGS["wan_like"].with_(heads=2, grid=(3, 10, 23), tau_skim=1e-4),        # N 690
     "d128_q64": CONFIGS["wan_like"].with_(heads=2, grid=(2, 10, 50), block_q=64, tau_skim=1e-4),
+    # gathered steps: four 16-key or eight 8-key SKIM blocks per step
+    "fine64x16": CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0, tau_skim=1e-4),   # N 1000, Nk 63
+    "fine64x8": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=8, tau_skim=1e-4),
+    "fine64x8_d64": CONFIGS["small"].with_(heads=2, grid=(5, 9, 13), block_q=64, block_k=8, tau_skim=3e-4),
+    "fine128x16_d64": CONFIGS["small"].with_(heads=2, grid=(5, 9, 13), block_k=16, tau_skim=3e-4),
 }
 
 
@@ -68,7 +73,8 @@ def test_four_tier_threshold_parity(name):
     check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"skim {name}", log=_log)
 
 
-@pytest.mark.parametrize("name,seed", [("small", 1), ("d128_ragged", 2), ("d128_q64", 3)])
+@pytest.mark.parametrize("name,seed", [("small", 1), ("d128_ragged", 2), ("d128_q64", 3), ("fine64x16", 4),
+                                       ("fine64x8_d64", 5), ("fine128x16_d64", 6)])
 def test_external_four_tier_maps(name, seed):
     """Random maps over all four tiers, and a map that is SKIM everywhere but
     the diagonal."""

@@ -46,7 +46,11 @@ def test_static_workspace_matches_plan_and_forward():
 def test_static_workspace_limit_and_mode():
     import tile_sparse_mixed_amd as tsm
     lib = tsm.load_library()
-    big = tsm.make_config(1, 4, 32760, 128, 128, 64, tau_hi=0.01, tau_lo=0.001)      # ~76 MiB of workspace
+    big = tsm.make_config(1, 8, 32760, 128, 128, 64, tau_hi=0.01, tau_lo=0.001)      # ~87 MiB of workspace
+    need = ctypes.c_size_t()
+    assert lib.tattn_workspace_bytes(ctypes.byref(big), ctypes.byref(need)) == 0
+    # the fake pointers below are only safe while the call must refuse the size
+    assert need.value > (64 << 20), need.value
     fake = ctypes.c_void_p(1 << 20)                                                  # aligned, never dereferenced
     assert lib.tattn_attention_static(ctypes.byref(big), fake, fake, fake, fake, None) == -3
     assert b"static scratch" in lib.tattn_last_error()

@@ -11,17 +11,15 @@
 //                    the last block also zeroes the chunk's columns past Nk,
 //   sk_J, sv_J       amax/448 (1 for an all-zero block),
 //   k8               E4M3 codes of K_J, row-major with k8_pos d order,
-//   vt               V_J as fp16, transposed ([d][key]) in the key order the
-//                    fused kernel's FULL P.V uses (vt_pos for 64-key blocks,
-//                    vt16_pos for 16-key blocks, which the kernel gathers four at
-//                    a time, natural order for 8-key blocks, gathered eight at a
-//                    time),
 //   v8t              E4M3 codes of V_J, transposed ([d][key]): the A operand of the
 //                    low tier's fp8 P.V for 64-key blocks (pv8_key order), key
 //                    order otherwise,
 //   vlow             16- and 8-key blocks: the low tier's fp16 V operand,
-//                    fl16(fl32(decode(E4M3(v * inv)) * sv)), in vt's layout (their
-//                    gathered steps mix blocks of different scales in one P.V).
+//                    fl16(fl32(decode(E4M3(v * inv)) * sv)), as rows [key][d]
+//                    (the fused kernel gathers four or eight blocks per step, so
+//                    one P.V mixes blocks of different scales and the fp8 P.V
+//                    with one column scale per 32 keys does not apply).
+// The FULL tiles' V operand is the caller's V itself (read by rows).
 // Per (b, h, query block I) one workgroup writes qbar_I, sq_I and iq_I = 448/amax.
 // With the SKIM tier or the refined low tier a third kernel writes the MXFP4
 // copy of K (k1_mx4), for the latter also that of its rounding residual.
@@ -149,8 +147,8 @@ __device__ inline ColMoments col_moments(double s1, double s2, int n) {
 
 template <int D, int BK, bool MOM>
 __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
-  static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
-  constexpr int QR = BK / 8;   // 16-byte chunks per stored row of BK keys
+  static_assert(BK == 64 || BK == 16 || BK == 8 || BK == 4 || BK == 2 || BK == 1,
+                "key blocks are 64, 16, 8, 4, 2 or 1 keys");
   using BL = BlockLoad<D, BK>;
   __shared__ double red[BL::RT * D];
   __shared__ float fred[kThreads / 64];
@@ -174,7 +172,6 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   unsigned char* k8 = slab + a.L.sl.k8 + (int64_t)J * BK * D;
   unsigned char* v8t = slab + a.L.sl.v8t + (int64_t)J * BK * D;
   uint16_t* vlow = reinterpret_cast<uint16_t*>(slab + a.L.sl.vlow) + (int64_t)J * BK * D;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(slab + a.L.sl.vt) + (int64_t)J * BK * D;
 
   const int t = threadIdx.x;
   const int c = t % BL::CH, r0 = t / BL::CH;
@@ -246,62 +243,49 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   amax = block_max(amax, fred);   // contains the barrier that publishes tileT
   const float inv = inv448(amax);
   if (t == 0) *sv = scale448(amax);
-  // vt (fp16): D rows of BK keys = QR chunks of 8 elements; element e of row d
-  // holds key vt_key<BK>(e).
-  for (int u = t; u < D * QR; u += kThreads) {
-    const int d = u / QR, q = u % QR;
-    uint32_t w[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; e2++) {
-      uint32_t lohi[2];
-#pragma unroll
-      for (int z = 0; z < 2; z++) {
-        const int key = vt_key<BK>(q * 8 + e2 * 2 + z);
-        // bf16 -> fp16 is exact for |v| in [2^-14, 65504]; smaller values round
-        lohi[z] = f32_to_f16(bf16_to_f32(tileT[key * D + d]));
-      }
-      w[e2] = lohi[0] | (lohi[1] << 16);
-    }
-    *reinterpret_cast<uint4*>(vt + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
   // v8t: D rows of BK codes of v * inv; element e of row d holds key
-  // pv8_key(e) (64-key blocks) or key e; ES elements per store
+  // pv8_key(e) (64-key blocks) or key e; ES elements per store (one byte per
+  // store below 8 keys)
   constexpr int ES = BK < 16 ? BK : 16, SR = BK / ES;
-  for (int u = t; u < D * SR; u += kThreads) {
-    const int d = u / SR, q = u % SR;
-    uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int e4 = 0; e4 < ES / 4; e4++) {
-      float f[4];
-#pragma unroll
-      for (int z = 0; z < 4; z++) {
-        const int e = q * ES + e4 * 4 + z;
-        f[z] = bf16_to_f32(tileT[(BK == 64 ? pv8_key(e) : e) * D + d]) * inv;
-      }
-      const int wd = cvt_fp8x2<false>(f[0], f[1], 0);
-      w[e4] = static_cast<uint32_t>(cvt_fp8x2<true>(f[2], f[3], wd));
+  if constexpr (BK < 8) {
+    for (int u = t; u < D * BK; u += kThreads) {
+      const int d = u / BK, e = u % BK;
+      v8t[d * BK + e] = static_cast<unsigned char>(cvt_fp8x2<false>(bf16_to_f32(tileT[e * D + d]) * inv, 0.0f, 0) & 0xff);
     }
-    if constexpr (ES == 16)
-      *reinterpret_cast<uint4*>(v8t + d * BK + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    else
-      *reinterpret_cast<uint2*>(v8t + d * BK + q * 8) = make_uint2(w[0], w[1]);
+  } else {
+    for (int u = t; u < D * SR; u += kThreads) {
+      const int d = u / SR, q = u % SR;
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e4 = 0; e4 < ES / 4; e4++) {
+        float f[4];
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          const int e = q * ES + e4 * 4 + z;
+          f[z] = bf16_to_f32(tileT[(BK == 64 ? pv8_key(e) : e) * D + d]) * inv;
+        }
+        const int wd = cvt_fp8x2<false>(f[0], f[1], 0);
+        w[e4] = static_cast<uint32_t>(cvt_fp8x2<true>(f[2], f[3], wd));
+      }
+      if constexpr (ES == 16)
+        *reinterpret_cast<uint4*>(v8t + d * BK + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      else
+        *reinterpret_cast<uint2*>(v8t + d * BK + q * 8) = make_uint2(w[0], w[1]);
+    }
   }
   if constexpr (BK < 64) {
-    // vlow: same layout as vt; element = fl16(fl32(decode(code)) * sv) of the E4M3
-    // code of v * inv (the hardware converter decodes exactly).
+    // vlow: rows [key][D] (the fused kernel gathers them like K rows);
+    // element = fl16(fl32(decode(code)) * sv) of the E4M3 code of v * inv (the
+    // hardware converter decodes exactly).
     const float svf = scale448(amax);
-    for (int u = t; u < D * QR; u += kThreads) {
-      const int d = u / QR, q = u % QR;
+    for (int u = t; u < BK * (D / 8); u += kThreads) {
+      const int key = u / (D / 8), c8 = u % (D / 8);
       uint32_t w[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; e2++) {
-        float f[2];
-#pragma unroll
-        for (int z = 0; z < 2; z++) {
-          const int key = vt_key<BK>(q * 8 + e2 * 2 + z);
-          f[z] = bf16_to_f32(tileT[key * D + d]) * inv;
-        }
-        const int code2 = cvt_fp8x2<false>(f[0], f[1], 0);
+        const float f0 = bf16_to_f32(tileT[key * D + c8 * 8 + 2 * e2]) * inv;
+        const float f1 = bf16_to_f32(tileT[key * D + c8 * 8 + 2 * e2 + 1]) * inv;
+        const int code2 = cvt_fp8x2<false>(f0, f1, 0);
         const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8(code2, false);
         // Round the product to fp32 first, then to fp16: the opaque step keeps
         // the compiler from fusing both roundings into one mixed-precision FMA.
@@ -309,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
         opaque(p0, p1);
         w[e2] = uint32_t(f32_to_f16(p0)) | (uint32_t(f32_to_f16(p1)) << 16);
       }
-      *reinterpret_cast<uint4*>(vlow + d * BK + q * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(vlow + key * D + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -360,7 +344,8 @@ template <int D, bool RESID>
 __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
   constexpr int NB = D / 32;            // scale blocks per row
   const Dims& dm = a.d;
-  const int bh = blockIdx.x / dm.Nk, J = blockIdx.x % dm.Nk;
+  const int NG = (dm.N + 63) / 64;       // 64-row groups of the sequence
+  const int bh = blockIdx.x / NG, J = blockIdx.x % NG;
   const int b = bh / dm.H, h = bh % dm.H;
   const int rows = min(64, dm.N - J * 64);
   const int64_t off = (int64_t)b * dm.sb + (int64_t)h * dm.sh + (int64_t)J * 64 * dm.sn;
@@ -418,8 +403,14 @@ hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k1_kv<D, 64, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   else if (d.Bk == 16)
     hipLaunchKernelGGL((k1_kv<D, 16, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
-  else
+  else if (d.Bk == 8)
     hipLaunchKernelGGL((k1_kv<D, 8, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  else if (d.Bk == 4)
+    hipLaunchKernelGGL((k1_kv<D, 4, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  else if (d.Bk == 2)
+    hipLaunchKernelGGL((k1_kv<D, 2, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_kv<D, 1, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d.Bq == 128)
@@ -428,11 +419,10 @@ hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k1_q<D, 64, MOM>), dim3(d.BH * d.Nq), dim3(kThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || !a.mx4) return e;
-  if (d.Bk != 64) return hipErrorInvalidValue;
   if (a.resid)
-    hipLaunchKernelGGL((k1_mx4<D, true>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_mx4<D, true>), dim3(d.BH * ((d.N + 63) / 64)), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k1_mx4<D, false>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k1_mx4<D, false>), dim3(d.BH * ((d.N + 63) / 64)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -6,10 +6,10 @@
 // rows 32w..32w+31 and computes S^T = K Q^T, so each lane holds one query
 // column and its softmax statistics stay inside the lane pair (l, l^32).
 // The workgroup walks a sequence of 64-key steps:
-//   FULL      a kept tile: K (bf16, the caller's tensor) and V^T (fp16
-//             copy, exact for bf16 values in fp16's normal range); S^T on
-//             v_mfma_f32_32x32x16_bf16, O^T += V^T P^T on the fp16 variant
-//             (P in [0, 2^8] keeps 3 more mantissa bits than bf16 would),
+//   FULL      a kept tile: K and V rows of the caller's bf16 tensors; S^T on
+//             v_mfma_f32_32x32x16_bf16, O^T += V^T P^T on the same
+//             instruction with P in bf16 and the V^T operand read from the V
+//             rows by the transposing LDS read (no V copy in the plan),
 //   LOW       a low-precision tile: S^T on v_mfma_f32_32x32x64_f8f6f4 from the
 //             E4M3 copies of Q and K scaled by sq*sk; the probabilities
 //             quantised to E4M3 against the tile's row maximum (448 at the
@@ -31,13 +31,13 @@
 //             in LOW.
 // Skipped blocks are visited as whole chunks of 64 (contiguous operands),
 // masked to the row's SKIP set; chunks with no skipped block are not visited.
-// With 16-key blocks ("FG-Attn": M x N tiles with a small N) a FULL or LOW
-// step gathers up to four consecutive entries of the row's list into one
-// 64-key step: K and E4M3 K rows per DMA instruction, V^T columns per lane (a
-// 16-key block keeps its within-group key order at any column group).  With
-// 8-key blocks a step gathers eight: each block's K rows go to the score rows
-// whose P values form one 8-key chunk of the P.V operand (slot8 / kk8), so the
-// block's V^T row is one 16-byte load in natural key order.
+// With 16-key blocks ("FG-Attn": M x N tiles with a small N, down to N = 1)
+// a FULL or LOW step gathers up to four consecutive entries of the row's list
+// into one 64-key step; with blocks of BK <= 8 keys it gathers 64 / BK (slots,
+// down to one key each).  The K, V, E4M3 K and low-tier V rows of a block go
+// to score rows chosen so that its keys are consecutive P values of one lane
+// half (slotg / kkg); the V^T operand is read from the V rows by the
+// transposing LDS read, so any placement of keys on score rows works.
 //
 // Data movement: every step's operands go global -> LDS with direct
 // buffer_load_dwordx4 ... lds (no staging registers) into one of two stage
@@ -144,6 +144,20 @@ __device__ inline void pipeline_reads_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
+// The same for operands of two LDS reads each (the transposing V reads):
+// `ahead` operands' reads first, then each MFMA followed by the next
+// operand's two reads.
+template <int N, int AHEAD>
+__device__ inline void pipeline_reads2_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // DS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Schedule of one software-pipelined low-tier step (one basic block): the
 // next step's K reads, its D/32 score MFMAs spread through this step's
 // softmax VALU, the row-sum MFMA, the V reads, then each P.V MFMA behind the
@@ -207,18 +221,27 @@ __device__ inline int offK(int row, int ch) {                                   
   return D == 128 ? row * 256 + ((ch ^ swz256(row)) << 4) : row * 128 + ((ch ^ swz128(row)) << 4);
 }
 __device__ inline int offV(int d, int ch) { return d * 128 + ((ch ^ swz128(d)) << 4); }   // [D][64] 16-bit
+// V rows [64][D] 16-bit (FULL tiles): chunk c of row r sits at slot c ^ swzv(r).
+// Their P.V operand is read with the transposing LDS read, whose half-wave
+// takes four consecutive rows 4u..4u+3 at four chunks each; XORing chunk bit
+// 2 (and bit 3 at 256-byte rows) with the row's place in its group of four
+// puts those 16 chunks on 16 distinct slots modulo 256 bytes.
+template <int D>
+__device__ inline int swzv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 template <int D>
 __device__ inline int offK8(int row, int ch) {                                  // [64][D] bytes
   return D == 128 ? row * 128 + ((ch ^ swz128(row)) << 4) : row * 64 + ((ch ^ swz64(row)) << 4);
 }
 
-// score scale of each 16-key group of a staged step (one value for 64-key
-// blocks); with 8-key blocks, of this lane's four P chunks (slots 2 cc + lane
-// half), held per lane so the eight slot scales need no scalar registers
+// score scale of a staged step: one value for 64-key blocks, one per 16-key
+// group for 16-key blocks; with blocks of <= 8 keys the factor common to the
+// step (sq * log2(e) / sqrt(d) on LOW steps) and, per lane g < G, the E4M3 K
+// scale of slot g (read per lane by the step's P values)
 template <int G>
 struct StepScale {
-  static constexpr int N = G == 8 ? 4 : G;
+  static constexpr int N = G == 4 ? 4 : 1;
   float c[N];
+  float kv;  // blocks of <= 8 keys, LOW steps: lane g < G holds slot g's sk
   float v;   // E4M3 value scale of a 64-key LOW or SKIM step's block
 };
 
@@ -233,9 +256,10 @@ struct StepScale {
 template <int D, int NW, int BK, bool SKIM, bool DUMP, bool REFINE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
-  static_assert(BK == 64 || BK == 16 || BK == 8, "key blocks are 64, 16 or 8 keys");
+  static_assert(BK == 64 || BK == 16 || BK == 8 || BK == 4 || BK == 2 || BK == 1,
+                "key blocks are 64, 16, 8, 4, 2 or 1 keys");
   static_assert(!REFINE || (BK == 64 && !SKIM), "the refined low tier runs on 64-key blocks without SKIM");
-  static_assert(!SKIM || BK == 64, "the SKIM tier runs on 64-key blocks");
+  static_assert(!SKIM || BK >= 8, "the SKIM tier runs on 64-, 16- and 8-key blocks");
   constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int R1 = 128 * D;         // bytes of each half of a stage (R0: K-side operands, R1: V-side)
   // Two-wave workgroups (64-row query blocks) keep ONE stage and refill its
@@ -335,9 +359,11 @@ void k3_attn(AttnArgs a) {
   }
   __syncthreads();
   const int sF = (nF + G - 1) / G, sL = (nL + G - 1) / G;   // FULL / LOW steps
-  const int nSteps = sF + 2 * snc + sL + nSk;
+  const int sSk = (nSk + G - 1) / G;                         // SKIM steps
+  const int nSteps = sF + 2 * snc + sL + sSk;
 
   const uint16_t* kin = a.k + toff;
+  const uint16_t* vin = a.v + toff;
   const unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
   const Slab SL = a.L.sl;
   // sk is read through the constant address space: a uniform load there is a
@@ -346,6 +372,7 @@ void k3_attn(AttnArgs a) {
   typedef __attribute__((address_space(4))) const float cfloat;
   cfloat* skp = (cfloat*)(reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk);
   cfloat* svp = (cfloat*)(reinterpret_cast<const float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk);
+  const float* skg = reinterpret_cast<const float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk;   // per-lane loads
 
   const float cF = kLog2e / __builtin_sqrtf(static_cast<float>(D));
   // the Q block's E4M3 scale and its inverse, from the block's amax (as the
@@ -374,15 +401,15 @@ void k3_attn(AttnArgs a) {
   };
   // list entry of key block g of a FULL, LOW or SKIM step, and the end of its list
   auto list_idx = [&](int t, int g) {
-    return t < tLow ? G * (t - nS2) + g : (SKIM && t >= tSk) ? nK + (t - tSk) + g : nF + G * (t - tLow) + g;
+    return t < tLow ? G * (t - nS2) + g : (SKIM && t >= tSk) ? nK + G * (t - tSk) + g : nF + G * (t - tLow) + g;
   };
-  auto list_end = [&](int t) { return t < tLow ? nF : nK; };
+  auto list_end = [&](int t) { return t < tLow ? nF : (SKIM && t >= tSk) ? nK + nSk : nK; };
   auto list_at = [&](int t) { return (int)slist[list_idx(t, 0)]; };
 
   // ---- DMA of step t's operands into stage `st`.  Region layouts (bytes):
-  //   FULL    R0 = K [64][D] bf16,       R1 = V^T [D][64] fp16
+  //   FULL    R0 = K [64][D] bf16,       R1 = V [64][D] bf16 (the caller's rows)
   //   LOW     R0 = K8 [64][D] E4M3,      R1 = V8^T [D][64] E4M3 (64-key blocks)
-  //                                         or V low^T [D][64] fp16 (16, 8)
+  //                                         or V low [64][D] fp16 rows (16, 8)
   //   SKIM    R0 = K4 [64][D/2] + scales, R1 = V8^T [D][64] E4M3
   //   SKIP_S  R0 = kbar hi [64][D] bf16, R1 = kbar lo [64][D] bf16
   //   SKIP_PV                            R1 = vbar^T [D][64] fp16
@@ -405,6 +432,15 @@ void k3_attn(AttnArgs a) {
     lk[j] = rr16 * (int)dm.sn * 2 + sw;
     lkb[j] = rr16 * 2 * D + sw;
   }
+  // Caller's V rows: instruction k covers rows k RPI + rr16 and RPI is a
+  // multiple of 4, so swzv(row) = swzv(rr16) for every instruction.  Formed
+  // at each use from an opaque lane index (not held across the loop).
+  // rowb: bytes between source rows.
+  auto lv_of = [&](int rowb) __attribute__((always_inline)) {
+    int lr = lane_here();
+    const int r = lr / CH, c = lr % CH;
+    return r * rowb + ((c ^ swzv<D>(r)) << 4);
+  };
   // [D][64] 16-bit tiles: instruction k covers rows 8k..8k+7, so swz128(r) =
   // ((lane >> 3) & 7) ^ (k & 1), and k & 1 == wave & 1 because NW is even.
   int voffV = (lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) * 16);
@@ -429,33 +465,36 @@ void k3_attn(AttnArgs a) {
   // holds logical chunk lc = (lane & 7) ^ swz128(d), i.e. 8 keys of column
   // group lc / 2; the lane fetches them from that group's block, stored
   // [D][16] (32 bytes per row d), half lc & 1 of the row.
-  // caller's K as one resource per head for 16- and 8-key gathers: rows past N read as zero
+  // caller's K and V as one resource per head each for 16- and 8-key gathers:
+  // rows past N read as zero
   const __amdgpu_buffer_rsrc_t rKh = make_rsrc(kin, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
-  // V^T rows of the step's G blocks (per-block [D][BK] layout) from `base`.
-  // 16-key blocks: logical chunk vlc holds 8 keys of column group vlc / 2, half
-  // vlc & 1 of that block's 32-byte row; 8-key blocks: chunk vlc is slot vlc's
-  // whole 16-byte row.
-  // jv (8-key blocks): lane g < 8 holds the step's block of slot g
-  auto load_vt16g = [&](unsigned char* reg, int base, int jv) __attribute__((always_inline)) {
-    if constexpr (G == 1) {
-      (void)reg; (void)base; (void)jv;
-    } else {
-      constexpr int ROWB = BK * 2;                  // bytes per stored V^T row of a block
-      // from an opaque lane index at every step: hoisted, these terms stayed
-      // live across the kernel and spilled in the two-wave instances
-      int lr = lane;
-      opaque(lr);
-      const int vlc = (lr & 7) ^ ((lr >> 3) & 7) ^ (wave & 1);
-      const int vo = G == 4 ? (lr >> 3) * 32 + (vlc & 1) * 16 + __shfl(jv, vlc >> 1, 64) * (D * ROWB)
-                            : (lr >> 3) * ROWB + __shfl(jv, vlc, 64) * (D * ROWB);
+  const __amdgpu_buffer_rsrc_t rVh = make_rsrc(vin, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
+  // 16-bit rows [64][D] of the step's G blocks from the per-head resource r
+  // (the caller's K or V, rows past N reading as zero, or the low tier's V
+  // rows), rowb bytes apart, lane offsets off(i) of instruction i.  Score row
+  // m holds key m & 15 of block m >> 4 (16-key blocks) or key kkg(m) of slot
+  // slotg(m) (blocks of <= 8 keys).
+  // jv: lane g < G holds the step's block of slot g
+  auto gather16 = [&](__amdgpu_buffer_rsrc_t r, unsigned char* reg, int jv, int rowb, auto off) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NI16; i++) {
-        const int k = wave + NW * i;
-        dma16(rS, reg + k * 1024, vo, base + k * 8 * ROWB);
+    for (int i = 0; i < NI16; i++) {
+      const int k = wave + NW * i;
+      const int row0 = k * RPI;                // first stage row of the instruction
+      if constexpr (G == 4) {
+        const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
+        dma16(r, reg + k * 1024, off(i) + (Jg * 16 + (row0 & 15)) * rowb, 0);
+      } else if constexpr (D == 128 && BK >= 4) {
+        // an instruction's four rows are four consecutive keys of one slot
+        const int Js = __builtin_amdgcn_readlane(jv, slotg<BK>(row0));
+        dma16(r, reg + k * 1024, off(i) + (Js * BK + kkg<BK>(row0)) * rowb, 0);
+      } else {
+        int lr = lane_here();   // opaque, as for the E4M3 rows below
+        const int r16 = lr / CH;
+        const int m = row0 + r16;
+        dma16(r, reg + k * 1024, off(i) + (__shfl(jv, slotg<BK>(m), 64) * BK + kkg<BK>(m) - r16) * rowb, 0);
       }
     }
   };
-
   auto load_vt16 = [&](unsigned char* reg, __amdgpu_buffer_rsrc_t r, int base) {   // [D][64] 16-bit
 #pragma unroll
     for (int i = 0; i < NI16; i++) {
@@ -496,7 +535,8 @@ void k3_attn(AttnArgs a) {
     constexpr bool PA = decltype(part)::value & 1, PB = decltype(part)::value & 2;
     const int kind = step_kind(t);
     if constexpr (G > 1) {
-      if (((KINDS & (1 << kFull)) && kind == kFull) || ((KINDS & (1 << kLow)) && kind == kLow)) {
+      if (((KINDS & (1 << kFull)) && kind == kFull) || ((KINDS & (1 << kLow)) && kind == kLow) ||
+          (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim)) {
         // one block index per lane (lane g < G: the step's g-th block), read
         // straight from the list; a runtime slot then selects by lane, never by
         // indexing an array (which the compiler would place in scratch memory)
@@ -505,36 +545,55 @@ void k3_attn(AttnArgs a) {
           const int i0 = list_idx(t, 0), e = list_end(t), g = lane & (G - 1);
           jv = (int)slist[i0 + g < e ? i0 + g : i0];
         }
-        if (kind == kFull) {
-          if constexpr (PA) {
-#pragma unroll
-            for (int i = 0; i < NI16; i++) {
-              const int k = wave + NW * i;
-              const int row0 = k * RPI;                // first stage row of the instruction
-              if constexpr (G == 4) {
-                const int Jg = __builtin_amdgcn_readlane(jv, row0 >> 4);
-                dma16(rKh, st + k * 1024, lk[i % NSW] + (Jg * 16 + (row0 & 15)) * (int)dm.sn * 2, 0);
-              } else if constexpr (D == 128) {
-                // score row m = row0 + rr16 takes key kk8(m) of slot slot8(m); an
-                // instruction's four rows share one slot
-                const int Js = __builtin_amdgcn_readlane(jv, slot8(row0));
-                dma16(rKh, st + k * 1024, lk[i % NSW] + (Js * 8 + kk8(row0)) * (int)dm.sn * 2, 0);
-              } else {
-                int lr = lane;   // opaque, as for the E4M3 rows below
-                opaque(lr);
-                const int r16 = lr / CH;
-                const int m = row0 + r16;
-                dma16(rKh, st + k * 1024,
-                      lk[i % NSW] + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - r16) * (int)dm.sn * 2, 0);
-              }
-            }
+        if ((KINDS & (1 << kFull)) && kind == kFull) {
+          if constexpr (PA) gather16(rKh, st, jv, (int)dm.sn * 2, [&](int i) { return lk[i % NSW]; });
+          if constexpr (PB) {
+            const int lv = lv_of((int)dm.sn * 2);
+            gather16(rVh, r1(st), jv, (int)dm.sn * 2, [&](int) { return lv; });
           }
-          if constexpr (PB) load_vt16g(r1(st), (int)SL.vt, jv);
           if constexpr (PA) {
 #pragma unroll
             for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = cF;
           }
-        } else {
+        } else if (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
+          // MXFP4 K rows (D/2 bytes) per lane from their slots, then one
+          // scale word per row (wave 0; a 4-byte LDS slot per lane)
+          if constexpr (PA) {
+            int lr = lane_here();   // opaque, as for the E4M3 rows below
+            constexpr int C4R = D / 32;                  // 16-byte chunks per MXFP4 row
+            const int ri = lr / C4R;                     // row of the lane inside an instruction
+            // D/32 instructions over NW waves (at d = 64 with four waves, two
+            // of them issue none)
+#pragma unroll
+            for (int i = 0; i < (D / 32 + NW - 1) / NW; i++) {
+              const int k = wave + NW * i;
+              if constexpr ((D / 32) % NW != 0) {
+                if (k >= D / 32) break;
+              }
+              const int m = k * (2048 / D) + ri;
+              const int key = G == 4 ? __shfl(jv, m >> 4, 64) * 16 + (m & 15)
+                                     : __shfl(jv, slotg<BK>(m), 64) * BK + kkg<BK>(m);
+              dma16(rS, st + k * 1024, (((lr & (C4R - 1)) ^ ((lr >> 4) & (C4R - 1))) << 4) + key * (D / 2), (int)SL.k4);
+            }
+            if (wave == 0) {
+              const int key = G == 4 ? __shfl(jv, lr >> 4, 64) * 16 + (lr & 15)
+                                     : __shfl(jv, slotg<BK>(lr), 64) * BK + kkg<BK>(lr);
+              if constexpr (D == 128)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 4, key * 4, (int)SL.k4s, 0, 0);
+              else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(st + 32 * D), 2, key * 2, (int)SL.k4s, 0, 0);
+            }
+          }
+          if constexpr (PB) {   // the low tier's fp16 V rows, as for LOW steps
+            const int lv = lv_of(2 * D) + (int)SL.vlow;
+            gather16(rS, r1(st), jv, 2 * D, [&](int) { return lv; });
+          }
+          if constexpr (PA) {   // the fp4 scores carry their scales: the step's factor only
+#pragma unroll
+            for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = cF;
+            if constexpr (G >= 8) cst.kv = 1.0f;
+          }
+        } else if (KINDS & (1 << kLow)) {
           if constexpr (PA) {
 #pragma unroll
             for (int i = 0; i < NI8; i++) {
@@ -547,25 +606,26 @@ void k3_attn(AttnArgs a) {
                 // the lane's terms are recomputed at every step from an opaque
                 // lane index: hoisted out of the loop, the per-instruction
                 // addresses stayed live across the kernel and spilled
-                int lr = lane;
-                opaque(lr);
+                int lr = lane_here();
                 const int ri = D == 128 ? lr >> 3 : lr >> 2;   // row of the lane inside the instruction
                 const int m = row0 + ri;
-                dma16(rS, st + k * 1024, voffK8 + (__shfl(jv, slot8(m), 64) * 8 + kk8(m) - ri) * D, (int)SL.k8);
+                dma16(rS, st + k * 1024, voffK8 + (__shfl(jv, slotg<BK>(m), 64) * BK + kkg<BK>(m) - ri) * D,
+                      (int)SL.k8);
               }
             }
           }
-          if constexpr (PB) load_vt16g(r1(st), (int)SL.vlow, jv);
+          if constexpr (PB) {   // the low tier's fp16 V rows (slab rows of 2D bytes)
+            const int lv = lv_of(2 * D) + (int)SL.vlow;
+            gather16(rS, r1(st), jv, 2 * D, [&](int) { return lv; });
+          }
           if constexpr (PA) {
+            if constexpr (G == 4) {
 #pragma unroll
-            for (int g = 0; g < StepScale<G>::N; g++) {
-              if constexpr (G == 8) {
-                const float s0 = skp[__builtin_amdgcn_readlane(jv, 2 * g)];
-                const float s1 = skp[__builtin_amdgcn_readlane(jv, 2 * g + 1)];
-                cst.c[g] = sq * (lh ? s1 : s0) * cF;
-              } else {
-                cst.c[g] = sq * skp[__builtin_amdgcn_readlane(jv, g)] * cF;
-              }
+              for (int g = 0; g < 4; g++) cst.c[g] = sq * skp[__builtin_amdgcn_readlane(jv, g)] * cF;
+            } else {
+              // one vector load (it lands with the step's DMA)
+              cst.c[0] = sq * cF;
+              cst.kv = skg[jv];
             }
           }
         }
@@ -586,7 +646,16 @@ void k3_attn(AttnArgs a) {
           dma16(rK, st + k * 1024, lk[i % NSW] + k * RPI * (int)dm.sn * 2, 0);
         }
       }
-      if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vt + J * 128 * D);
+      if constexpr (PB) {
+        const uint32_t rows = (uint32_t)min(64, dm.N - J * 64);
+        const __amdgpu_buffer_rsrc_t rV = make_rsrc(vin + (int64_t)J * 64 * dm.sn, rows * (uint32_t)dm.sn * 2);
+        const int lv = lv_of((int)dm.sn * 2);
+#pragma unroll
+        for (int i = 0; i < NI16; i++) {
+          const int k = wave + NW * i;
+          dma16(rV, r1(st) + k * 1024, lv + k * RPI * (int)dm.sn * 2, 0);
+        }
+      }
       if constexpr (PA) cst.c[0] = cF;
     } else if (G == 1 && (KINDS & (1 << kLow)) && kind == kLow) {
       const int J = list_at(t);
@@ -606,10 +675,10 @@ void k3_attn(AttnArgs a) {
         cst.c[0] = REFINE ? cF : sq * skp[J] * cF;   // refined: the fp4 scales are inside the MFMA
         cst.v = svp[J];
       }
-    } else if (SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
+    } else if (G == 1 && SKIM && (KINDS & (1 << kSkim)) && kind == kSkim) {
       // MXFP4 K [64][D/2] into R0, its scale bytes [64][D/32] after it (one
       // D/32-byte load per lane from wave 0, into a 4-byte LDS slot per
-      // lane), fp16 dequantised V^T into R1
+      // lane), the E4M3 V^T into R1
       const int J = list_at(t);
       if constexpr (PA) {
         for (int k = wave; k < D / 32; k += NW) dma16(rS, st + k * 1024, voffK4, (int)SL.k4 + J * 32 * D + k * 1024);
@@ -683,7 +752,7 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; db++) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
-  f16x8 pb[4];
+  f16x8 pb[4];       // the P operand: fp16, or the bits of bf16 P (FULL tiles)
   i32x8 p8 = {};     // probability codes of a quantised step (LOW, SKIM)
   // From the first quantised 64-key step on, the accumulator holds O^T / accF
   // (relative to 2^m): a step's weight w = 2^(tile max - m) sv / 448 is split
@@ -705,6 +774,20 @@ void k3_attn(AttnArgs a) {
     for (int cc = 0; cc < 4; cc++)
 #pragma unroll
       for (int j = 0; j < 4; j++) ps = __builtin_amdgcn_fdot2(h2{p[cc][2 * j], p[cc][2 * j + 1]}, one2, ps, false);
+    return ps;
+  };
+
+  // the same for bf16 P values (v_dot2_f32_bf16)
+  auto bf16_sum = [](const f16x8* p) __attribute__((always_inline)) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float ps = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {
+      const bf16x8 q = __builtin_bit_cast(bf16x8, p[cc]);
+#pragma unroll
+      for (int j = 0; j < 4; j++) ps = __builtin_amdgcn_fdot2_f32_bf16(b2{q[2 * j], q[2 * j + 1]}, one2, ps, false);
+    }
     return ps;
   };
 
@@ -744,7 +827,8 @@ void k3_attn(AttnArgs a) {
   // instruction: K4 x Q4, the K residual x Q4, K4 x the Q residual.
   auto scores_refine = [&](const unsigned char* st, f32x16* s, const i32x8* q4, const int* q4s, const i32x8* q4r,
                            const int* q4rs) __attribute__((always_inline)) {
-    const int sw = D == 128 ? (ln >> 2) & 3 : (ln >> 3) & 1;
+    const int lsw = lane_here();   // the row swizzle from the hardware lane index (not held across the kernel)
+    const int sw = D == 128 ? (lsw >> 2) & 3 : (lsw >> 3) & 1;
     // one score block (32 keys) at a time, its operands read just before its
     // MFMAs: all of them at once would need 32 more registers than the
     // pipelined step has
@@ -785,7 +869,26 @@ void k3_attn(AttnArgs a) {
   // of its query row (q4, made once per row): one E8M0 block each, whose
   // scale bytes the MFMA applies (opsel picks the byte of the key row's word).
   auto scores_fp4 = [&](const unsigned char* st, f32x16* s, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
-    const int sw = D == 128 ? (ln >> 2) & 3 : (ln >> 3) & 1;
+    const int lsw = lane_here();   // the row swizzle from the hardware lane index (not held across the kernel)
+    const int sw = D == 128 ? (lsw >> 2) & 3 : (lsw >> 3) & 1;
+    if constexpr (SPLIT && G > 1 && D == 128) {
+      // one score block at a time (the two-wave instances with gathered
+      // steps have no room for both blocks' operands)
+#pragma unroll
+      for (int b = 0; b < 2; b++) {
+        const int r = (lsw & 31) + 32 * b;
+        const int ks = static_cast<int>(*reinterpret_cast<const uint32_t*>(st + 32 * D + 4 * r) >> (8 * lh));
+        i32x8 kb[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+          const uint4 v = *reinterpret_cast<const uint4*>(st + r * (D / 2) + (((2 * i + lh) ^ sw) << 4));
+          kb[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        }
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kb[0], q4[0], s[b], 4, 4, 0, ks, 0, q4s[0]);
+        s[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kb[1], q4[1], s[b], 4, 4, 2, ks, 0, q4s[1]);
+      }
+      return;
+    }
     i32x8 ka[D / 32];
     int ks[2];
 #pragma unroll
@@ -823,11 +926,12 @@ void k3_attn(AttnArgs a) {
   };
   // ---- online softmax of x = s * c (base-2 units; tmax already scaled) into
   // the fp16 P operand, raising m when needed.
-  // score scale of this lane's P chunk cc: one per step (64-key blocks), per
-  // 16-key group (16-key blocks), per slot 2 cc + lane half (8-key blocks)
+  // score scale of this lane's P chunk cc: per 16-key group with 16-key
+  // blocks, else the step's (with blocks of <= 8 keys the common factor, which
+  // FULL steps use as is)
   auto chunk_scale = [&](const StepScale<G>& cs, int cc) __attribute__((always_inline)) {
-    if constexpr (G == 1) return cs.c[0];
-    else return cs.c[cc];
+    if constexpr (G == 4) return cs.c[cc];
+    else return cs.c[0];
   };
   // raise the running reference m to a step's maximum tmax (base 2, already
   // reduced over the lane pair) when it exceeds m by more than kLazy
@@ -848,7 +952,9 @@ void k3_attn(AttnArgs a) {
       m_run = mn;
     }
   };
-  auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax) __attribute__((always_inline)) {
+  // BF: the P operand in bf16 (FULL tiles), else fp16 (skip chunks)
+  auto softmax = [&](f32x16* s, const StepScale<G>& cs, float tmax, auto bf) __attribute__((always_inline)) {
+    constexpr bool BF = decltype(bf)::value;
     raise_max(max_lane_halves(tmax), std::false_type{});
     const float nm = -m_run;
 #pragma unroll
@@ -856,9 +962,11 @@ void k3_attn(AttnArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 8; tt++) {
         const int e = 8 * cc + tt;
-        pb[cc][tt] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], chunk_scale(cs, cc), nm)));
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], chunk_scale(cs, cc), nm));
+        if constexpr (BF) pb[cc][tt] = __builtin_bit_cast(_Float16, static_cast<__bf16>(x));
+        else pb[cc][tt] = static_cast<_Float16>(x);
       }
-    l_run += half_sum(pb);
+    l_run += BF ? bf16_sum(pb) : half_sum(pb);
   };
   auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
     float m = -INFINITY;
@@ -868,7 +976,8 @@ void k3_attn(AttnArgs a) {
       for (int r = 0; r < 16; r++) m = __builtin_fmaxf(m, s[b][r]);
     return m;
   };
-  // ---- O^T += V^T P^T from region R1 (fp16 V, low-tier V, or block means)
+  // ---- O^T += V^T P^T of a skip chunk from region R1: the pooled V^T [D][64]
+  // fp16, keys in the P.V operand's order (vt_pos)
   auto pv = [&](const unsigned char* st) __attribute__((always_inline)) {
     f16x8 va[D / 8];
 #pragma unroll
@@ -884,6 +993,56 @@ void k3_attn(AttnArgs a) {
     pipeline_reads_mfma<D / 8, D / 16>();
   };
 
+  // ---- O^T += V^T P^T from V rows in R1, read transposed, two 4-row reads per
+  // operand (score rows 16cc + 4lh + 0..3, then + 8): a FULL step's caller V
+  // against bf16 P on the bf16 MFMA (BF), or the low tier's fp16 V rows of a
+  // gathered step against fp16 P on the fp16 MFMA.
+  //
+  // Transposing reads (ds_read_b64_tr_b16): in each 16-lane group the lanes
+  // name sixteen 8-byte pieces, lane 4u + a the piece at row u, columns
+  // 4a..4a+3 of a 4-row x 16-column block, and lane 4a + c then receives
+  // column 4a + c of the four rows (an in-bounds probe on gfx950 confirmed this
+  // lane mapping).  The A operand of P chunk cc is V^T at d = 32db + ln over
+  // the score rows 16cc + 4lh + 0..3 and 16cc + 8 + 4lh + 0..3 (the keys of the
+  // lane's P values, in their order), so group g = lane >> 4 reads columns
+  // 32db + 16(g & 1) .. +15 of rows 16cc + 4lh (+ 8) + u.  The lane offsets
+  // are formed here from an opaque lane index, so they are not held in
+  // registers across the step loop.
+  auto pv_rows = [&](const unsigned char* st, auto bf) __attribute__((always_inline)) {
+    constexpr bool BF = decltype(bf)::value;
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const unsigned char* r = r1(st);
+    int lr = lane_here();
+    int offtr[D / 32];
+    {
+      const int u = (lr >> 2) & 3, aa = lr & 3, gg = (lr >> 4) & 1, row = 4 * (lr >> 5) + u;
+#pragma unroll
+      for (int db = 0; db < D / 32; db++)
+        offtr[db] = row * (2 * D) + (((4 * db + 2 * gg + (aa >> 1)) ^ swzv<D>(row)) << 4) + 8 * (aa & 1);
+    }
+    bf16x8 va[D / 8];
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int db = 0; db < D / 32; db++) {
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(r + offtr[db] + 16 * cc * (2 * D)));
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(r + offtr[db] + (16 * cc + 8) * (2 * D)));
+        va[cc * (D / 32) + db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++)
+#pragma unroll
+      for (int db = 0; db < D / 32; db++)
+        if constexpr (BF)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc * (D / 32) + db], __builtin_bit_cast(bf16x8, pb[cc]),
+                                                            acc[db], 0, 0, 0);
+        else
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[cc * (D / 32) + db]), pb[cc],
+                                                           acc[db], 0, 0, 0);
+    pipeline_reads2_mfma<D / 8, D / 16>();
+  };
+
   // ---- quantised probabilities (LOW and SKIM tiles).  Scores x = s * c in
   // base 2; per row the tile maximum tm; codes E(448 * 2^(x - tm)), so the
   // maximum lands on 448; the tile's weight relative to the running reference
@@ -893,8 +1052,7 @@ void k3_attn(AttnArgs a) {
   auto dump_codes = [&](int ds) __attribute__((always_inline)) {
     if constexpr (DUMP) {
       if (dsl >= 0 && ds < a.dsteps) {
-        int lr = lane;   // opaque: the lane's term is not kept live across the kernel
-        opaque(lr);
+        int lr = lane_here();   // opaque: the lane's term is not kept live across the kernel
         unsigned char* o = a.dump + ((static_cast<int64_t>(dsl) * a.dsteps + ds) * (32 * NW) + 32 * wave + (lr & 31)) * 64 + 32 * (lr >> 5);
         reinterpret_cast<uint4*>(o)[0] = make_uint4(p8[0], p8[1], p8[2], p8[3]);
         reinterpret_cast<uint4*>(o)[1] = make_uint4(p8[4], p8[5], p8[6], p8[7]);
@@ -945,9 +1103,8 @@ void k3_attn(AttnArgs a) {
     accF = tiny ? accF : wm;
     wk = tiny ? 0 : e + 127;
   };
-  // 16- and 8-key blocks: one maximum per block (chunk cc of the lane: 16-key
-  // block cc over both lane halves, or 8-key slot 2cc + lane half), and the
-  // fp16 P.V operand decode(code) * 2^(tm_block - m) / 448
+  // 16-key blocks: one maximum per block (chunk cc of the lane over both lane
+  // halves), and the fp16 P.V operand decode(code) * 2^(tm_block - m) / 448
   auto quant_soft_g = [&](f32x16* s, const StepScale<G>& cs, int ds) __attribute__((always_inline)) {
     float tb[4];
 #pragma unroll
@@ -955,8 +1112,7 @@ void k3_attn(AttnArgs a) {
       float m = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
-      tb[cc] = m * chunk_scale(cs, cc);
-      if constexpr (G == 4) tb[cc] = max_lane_halves(tb[cc]);
+      tb[cc] = max_lane_halves(m * chunk_scale(cs, cc));
     }
     float tmax = __builtin_fmaxf(__builtin_fmaxf(tb[0], tb[1]), __builtin_fmaxf(tb[2], tb[3]));
     raise_max(max_lane_halves(tmax), std::false_type{});
@@ -969,14 +1125,81 @@ void k3_attn(AttnArgs a) {
       const int b = cc >> 1, r0 = 8 * (cc & 1);
 #pragma unroll
       for (int j = 0; j < 2; j++) {
-        const int w = codes4(s[b][r0 + 4 * j], s[b][r0 + 4 * j + 1], s[b][r0 + 4 * j + 2], s[b][r0 + 4 * j + 3], c, nm,
-                             p8[2 * cc + j]);
+        // (0, not the register's old codes, as the kept half: p8 is then not
+        // live between steps)
+        const int w = codes4(s[b][r0 + 4 * j], s[b][r0 + 4 * j + 1], s[b][r0 + 4 * j + 2], s[b][r0 + 4 * j + 3], c, nm, 0);
         p8[2 * cc + j] = w;
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
         pb[cc][4 * j] = static_cast<_Float16>(lo.x * gw);
         pb[cc][4 * j + 1] = static_cast<_Float16>(lo.y * gw);
         pb[cc][4 * j + 2] = static_cast<_Float16>(hi.x * gw);
         pb[cc][4 * j + 3] = static_cast<_Float16>(hi.y * gw);
+      }
+    }
+    dump_codes(ds);
+    l_run += half_sum(pb);
+  };
+  // Blocks of BK <= 8 keys: the lane's slot u holds its P values (flat
+  // register index 16b + r) u BK .. u BK + BK - 1, and is slot
+  // slotg(row of its first P value) of the step.  Scores are scaled in place
+  // by their slot's scale, then per slot the maximum tb, codes
+  // E(448 * 2^(x - tb)) and the fp16 P.V operand decode(code) * 2^(tb - m) / 448.
+  // One-key blocks: the code is 448 for every live key, so P is 2^(x - m).
+  auto quant_soft_s = [&](f32x16* s, const StepScale<G>& cs, int ds) __attribute__((always_inline)) {
+    constexpr int NS = BK <= 8 ? 32 / BK : 1;   // (instances with larger blocks never call it)
+    float tb[NS];
+#pragma unroll
+    for (int u = 0; u < NS; u++) {
+      const int f0 = u * BK, b = f0 >> 4, r0 = f0 & 15;
+      const int slot = slotg<BK>(32 * b + 8 * (r0 >> 2) + (r0 & 3)) + (8 / BK) * lh;
+      const float c = cs.c[0] * __shfl(cs.kv, slot, 64);
+      float m = -INFINITY;
+#pragma unroll
+      for (int z = 0; z < BK; z++) {
+        s[b][r0 + z] *= c;
+        m = __builtin_fmaxf(m, s[b][r0 + z]);
+      }
+      tb[u] = m;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NS; u++) tmax = __builtin_fmaxf(tmax, tb[u]);
+    raise_max(max_lane_halves(tmax), std::false_type{});
+    if constexpr (BK == 1) {
+#pragma unroll
+      for (int w = 0; w < 8; w++) {
+        int code = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int f = 4 * w + j;
+          const float x = s[f >> 4][f & 15];
+          const bool live = x > -INFINITY;
+          pb[f >> 3][f & 7] = static_cast<_Float16>(live ? __builtin_amdgcn_exp2f(x - m_run) : 0.0f);
+          code |= (live ? 0x7E : 0) << (8 * j);   // E4M3 448
+        }
+        p8[w] = code;
+      }
+    } else {
+      float nm[NS], gw[NS];
+#pragma unroll
+      for (int u = 0; u < NS; u++) {
+        const bool live = tb[u] > -INFINITY;   // a slot past the list's end has no keys
+        nm[u] = live ? kLog2_448 - tb[u] : 0.0f;
+        gw[u] = live ? __builtin_amdgcn_exp2f(tb[u] - m_run) * (1.0f / 448.0f) : 0.0f;
+      }
+#pragma unroll
+      for (int w = 0; w < 8; w++) {
+        const int f = 4 * w, b = f >> 4, r = f & 15;
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) x[j] = __builtin_amdgcn_exp2f(s[b][r + j] + nm[(f + j) / BK]);
+        const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);   // p8 not live between steps
+        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo2, true);
+        p8[w] = code;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(code, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(code, true);
+        const float dv[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int j = 0; j < 4; j++) pb[(f + j) >> 3][(f + j) & 7] = static_cast<_Float16>(dv[j] * gw[(f + j) / BK]);
       }
     }
     dump_codes(ds);
@@ -1008,39 +1231,48 @@ void k3_attn(AttnArgs a) {
       const int J = list_at(t);
       if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
       if constexpr (LOW) quant_soft64(s, c.c[0], c.v, t - tLow);
-      else softmax(s, c, row_max(s) * c.c[0]);
+      else softmax(s, c, row_max(s) * c.c[0], std::true_type{});
     } else {
       // Lists are ascending, so a partial group or the ragged last block only
-      // occurs in the last step of the phase.  Register (b, r) is key
-      // 8((r >> 2) & 1) + 4lh + r % 4 of 16-key block 2b + r / 8, or key
-      // 4((r >> 2) & 1) + r % 4 of 8-key block (slot) 4b + 2(r / 8) + lh.
-      if (t == (LOW ? tSk - 1 : tLow - 1)) {
+      // occurs in the last step of the phase.
+      if (t == (!LOW ? tLow - 1 : (SKIM && t >= tSk) ? nSteps - 1 : tSk - 1)) {
         const int i0 = list_idx(t, 0), e = list_end(t);
-        // valid keys of each block: 0 past the list end, fewer in block Nk - 1
-        int lim[G];
+        if constexpr (G == 4) {
+          // Register (b, r) is key 8((r >> 2) & 1) + 4lh + r % 4 of 16-key
+          // block 2b + r / 8.  Valid keys of each block: 0 past the list end,
+          // fewer in block Nk - 1.
+          int ql[4];
 #pragma unroll
-        for (int g = 0; g < G; g++) {
-          const int Jg = (int)slist[i0 + g < e ? i0 + g : i0];
-          lim[g] = i0 + g >= e ? 0 : Jg == dm.Nk - 1 ? dm.N - BK * Jg : BK;
-        }
-        // this lane's limit for P chunk q = 2b + (r >> 3), against the key index
-        // of register r inside its block
-        int ql[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          ql[q] = G == 4 ? lim[q] - 4 * lh : (lh ? lim[2 * q + 1] : lim[2 * q]);
-          opaque(ql[q]);
-        }
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int kk = G == 4 ? 8 * ((r >> 2) & 1) + (r & 3) : (r & 3) + 4 * ((r >> 2) & 1);
-            if (kk >= ql[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
+          for (int q = 0; q < 4; q++) {
+            const int Jg = (int)slist[i0 + q < e ? i0 + q : i0];
+            ql[q] = (i0 + q >= e ? 0 : Jg == dm.Nk - 1 ? dm.N - BK * Jg : BK) - 4 * lh;
+            opaque(ql[q]);
           }
+#pragma unroll
+          for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+              if (8 * ((r >> 2) & 1) + (r & 3) >= ql[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
+        } else {
+          // the lane's slot u: P values u BK + z hold keys z = 0 .. BK-1
+#pragma unroll
+          for (int u = 0; u < 32 / BK; u++) {
+            const int f0 = u * BK, b = f0 >> 4, r0 = f0 & 15;
+            const int slot = slotg<BK>(32 * b + 8 * (r0 >> 2) + (r0 & 3)) + (8 / BK) * lh;
+            const bool in = i0 + slot < e;
+            const int Js = in ? (int)slist[i0 + slot] : 0;
+            int lim = !in ? 0 : Js == dm.Nk - 1 ? dm.N - BK * Js : BK;
+            opaque(lim);
+#pragma unroll
+            for (int z = 0; z < BK; z++)
+              if (z >= lim) s[b][r0 + z] = -INFINITY;
+          }
+        }
       }
-      if constexpr (LOW) {
+      if constexpr (LOW && G == 4) {
         quant_soft_g(s, c, t - tLow);
+      } else if constexpr (LOW) {
+        quant_soft_s(s, c, t - tLow);
       } else {
         float tmax = -INFINITY;
 #pragma unroll
@@ -1050,7 +1282,7 @@ void k3_attn(AttnArgs a) {
           for (int r = 0; r < 8; r++) m = __builtin_fmaxf(m, s[cc >> 1][8 * (cc & 1) + r]);
           tmax = __builtin_fmaxf(tmax, m * chunk_scale(c, cc));
         }
-        softmax(s, c, tmax);
+        softmax(s, c, tmax, std::true_type{});
       }
     }
   };
@@ -1062,19 +1294,25 @@ void k3_attn(AttnArgs a) {
     else scores_bf16(st, s);
     kept_soft(low_tag, t, s, c);
     if constexpr (LOW && G == 1) pv8(st);
-    else pv(st);
+    else pv_rows(st, std::integral_constant<bool, !LOW>{});
   };
-  // a SKIM tile (64-key blocks): mask and quantised probabilities of its scores s
+  // a SKIM step: mask and quantised probabilities of its scores s (with
+  // gathered blocks as a LOW step's, the scale factor being the step's)
   auto skim_soft = [&](int t, f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) {
-    const int J = list_at(t);
-    if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
-    quant_soft64(s, c.c[0], c.v, t - tLow);
+    if constexpr (G == 1) {
+      const int J = list_at(t);
+      if (J == dm.Nk - 1) mask_tail(s, dm.N - 64 * J);
+      quant_soft64(s, c.c[0], c.v, t - tLow);
+    } else {
+      kept_soft(std::true_type{}, t, s, c);
+    }
   };
   auto skim_step = [&](int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q4, const int* q4s) __attribute__((always_inline)) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
     scores_fp4(st, s, q4, q4s);
     skim_soft(t, s, c);
-    pv8(st);
+    if constexpr (G == 1) pv8(st);
+    else pv_rows(st, std::false_type{});
   };
   // pooled keys of a chunk of 64 skipped-candidate blocks: scores only (hi
   // part from R0, lo part from R1), then the bias and the softmax
@@ -1093,7 +1331,7 @@ void k3_attn(AttnArgs a) {
     // (only the chunk holding block Nk - 1 can match)
     const int lastpos = dm.Nk - 1 - 64 * schunk[ci] - 4 * lh;
     const float lglast = __log2f(static_cast<float>(dm.N - (dm.Nk - 1) * BK));
-    constexpr float lgfull = BK == 64 ? 6.0f : BK == 16 ? 4.0f : 3.0f;   // log2(BK)
+    constexpr float lgfull = BK == 64 ? 6.0f : BK == 16 ? 4.0f : BK == 8 ? 3.0f : BK == 4 ? 2.0f : BK == 2 ? 1.0f : 0.0f;   // log2(BK)
     float tmax = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; b++)
@@ -1108,7 +1346,7 @@ void k3_attn(AttnArgs a) {
     StepScale<G> one;
 #pragma unroll
     for (int g = 0; g < StepScale<G>::N; g++) one.c[g] = 1.0f;
-    softmax(s, one, tmax);
+    softmax(s, one, tmax, std::false_type{});
   };
   auto skip_scores = [&](int t, const unsigned char* st) __attribute__((always_inline)) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -1173,7 +1411,10 @@ void k3_attn(AttnArgs a) {
     // buffer loads through a resource over the head's rows: a row past N
     // reads as zeros without a branch
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.q + toff, (uint32_t)dm.N * (uint32_t)dm.sn * 2);
-    const int qoff = (qrow * (int)dm.sn + 32 * lh) * 2;
+    // the row from an opaque lane index: the Q loads' row term is not held
+    // live from the kernel's start to here
+    int lr = lane_here();
+    const int qoff = ((I * (32 * NW) + wave * 32 + (lr & 31)) * (int)dm.sn + 32 * (lr >> 5)) * 2;
     auto load32 = [&](int i, float* x) __attribute__((always_inline)) {   // channels 64i + 32lh .. +31
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -1400,8 +1641,12 @@ void k3_attn(AttnArgs a) {
       if (u >= nSteps) return 0;
       const int k = step_kind(u);
       if (k == kFull || k == kSkipS) return NI16;
-      if (k == kLow)   // refined: K rows and residual rows, one scale-word load each from the first and last wave
-        return REFINE ? 2 * ((D / 32 - wave + NW - 1) / NW) + (wave == 0 ? 1 : 0) + (wave == NW - 1 ? 1 : 0) : NI8;
+      // LOW: refined, K rows and residual rows, one scale-word load each from
+      // the first and last wave; with blocks of <= 8 keys the E4M3 K rows and
+      // the per-lane load of the slots' scales
+      if (k == kLow)
+        return REFINE ? 2 * ((D / 32 - wave + NW - 1) / NW) + (wave == 0 ? 1 : 0) + (wave == NW - 1 ? 1 : 0)
+                      : NI8 + (G >= 8 ? 1 : 0);
       if (k == kSkipPV) return 0;
       return (D / 32 - wave + NW - 1) / NW + (wave == 0 ? 1 : 0);   // SKIM: K rows and the scale words
     };
@@ -1414,10 +1659,13 @@ void k3_attn(AttnArgs a) {
     int t = 0;
     // One step.  S_fn(s): its scores from the stage; soft_fn(s, c): masks and
     // softmax.  HS: the step scores; HP: it runs P.V; U1: its scores also
-    // read R1 (a skip chunk's lo half); PV8: its P.V is the fp8 one.
+    // read R1 (a skip chunk's lo half); Q8PV: which P.V it runs.
     auto split_step = [&](auto nk, auto hs, auto hp, auto u1, auto q8pv, auto S_fn, auto soft_fn) __attribute__((always_inline)) {
       constexpr bool HS = decltype(hs)::value, HP = decltype(hp)::value, U1 = decltype(u1)::value;
-      constexpr bool PV8 = decltype(q8pv)::value;   // P.V on the fp8 MFMA (quantised 64-key steps)
+      // P.V: 1 on the fp8 MFMA (quantised 64-key steps), 2 the FULL one on the
+      // caller's V rows, 3 the fp16 one on the low tier's V rows (gathered
+      // steps), 0 the fp16 one on the pooled V^T (skip chunks)
+      constexpr int PVK = static_cast<int>(decltype(q8pv)::value);
       const bool more = t + 1 < nSteps;
       const StepScale<G> cur = cA;   // issuing step t+1's R0 half rewrites cA
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -1433,7 +1681,9 @@ void k3_attn(AttnArgs a) {
       if constexpr (HP) {
         wait_vm_n(a_count(t + 1));   // R1 of step t landed in every wave
         bar();
-        if constexpr (PV8) pv8(stA);
+        if constexpr (PVK == 1) pv8(stA);
+        else if constexpr (PVK == 2) pv_rows(stA, std::true_type{});
+        else if constexpr (PVK == 3) pv_rows(stA, std::false_type{});
         else pv(stA);
       }
       wait_vm0_lgkm0();              // R0 of step t+1 landed, this wave's R1 reads returned
@@ -1455,7 +1705,7 @@ void k3_attn(AttnArgs a) {
         split_step(KAfterSkip{}, T0{}, T1{}, T0{}, T0{}, no_S, no_soft);
     }
     while (t < tLow)
-      split_step(KAfterFull{}, T1{}, T1{}, T0{}, T0{},
+      split_step(KAfterFull{}, T1{}, T1{}, T0{}, std::integral_constant<int, 2>{},
                  [&](f32x16* s) __attribute__((always_inline)) { scores_bf16(stA, s); },
                  [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { kept_soft(T0{}, t, s, c); });
     if (t < tSk) {
@@ -1465,7 +1715,7 @@ void k3_attn(AttnArgs a) {
       if constexpr (REFINE) make_q4(q4reg, q4s, q4rreg, q4rs);
       else make_q8(q8reg);
       while (t < tSk)
-        split_step(KLow{}, T1{}, T1{}, T0{}, std::integral_constant<bool, G == 1>{},
+        split_step(KLow{}, T1{}, T1{}, T0{}, std::integral_constant<int, G == 1 ? 1 : 3>{},
                    [&](f32x16* s) __attribute__((always_inline)) {
                      if constexpr (REFINE) scores_refine(stA, s, q4reg, q4s, q4rreg, q4rs);
                      else scores_fp8(stA, s, q8reg);
@@ -1478,7 +1728,7 @@ void k3_attn(AttnArgs a) {
         int q4s[D / 64];
         make_q4(q4reg, q4s);
         while (t < nSteps)
-          split_step(KSkimOnly{}, T1{}, T1{}, T0{}, T1{},
+          split_step(KSkimOnly{}, T1{}, T1{}, T0{}, std::integral_constant<int, G == 1 ? 1 : 3>{},
                      [&](f32x16* s) __attribute__((always_inline)) { scores_fp4(stA, s, q4reg, q4s); },
                      [&](f32x16* s, const StepScale<G>& c) __attribute__((always_inline)) { skim_soft(t, s, c); });
       }
@@ -1488,10 +1738,12 @@ void k3_attn(AttnArgs a) {
   // ---- epilogue: O = acc / l.  The row's address is formed again here from
   // an opaque lane index: shared with the Q loads, it stayed live across the
   // kernel and spilled in the two-wave instances.
-  const float L = l_run + __shfl_xor(l_run, 32, 64);
+  // the row's normaliser: this lane's l plus the other lane half's.  The swap
+  // returns (lanes 0-31: own, other) and (lanes 32-63: other, own).
+  const auto lsw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float L = __uint_as_float(lsw2[0]) + __uint_as_float(lsw2[1]);
   const float scale = accF / L;
-  int lo = ln;
-  opaque(lo);
+  const int lo = lane_here() & 31;
   const int orow = I * (32 * NW) + wave * 32 + lo;
   if (orow < dm.N) {
     if (a.out_fp32) {
@@ -1521,22 +1773,34 @@ void k3_attn(AttnArgs a) {
 
 template <int D, int NW, bool DUMP>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  if ((a.skim || a.refine) && a.d.Bk != 64) return hipErrorInvalidValue;
+  if ((a.skim && a.d.Bk < 8) || (a.refine && a.d.Bk != 64)) return hipErrorInvalidValue;
   if (a.skim && a.refine) return hipErrorInvalidValue;
   if (a.d.Nk > kMaxNk || a.list_cap < 1 || a.list_cap > a.d.Nk) return hipErrorInvalidValue;
   if (DUMP && (!a.dslot || !a.dump || a.dsteps < 1)) return hipErrorInvalidValue;
   const size_t lds = ((size_t)a.list_cap * 2 + 15) / 16 * 16;   // the row's list (dynamic LDS)
   const dim3 grid(a.d.BH * a.d.Nq), block(NW * 64);
-  if (a.skim)
+  if (a.skim && a.d.Bk == 64)
     hipLaunchKernelGGL((k3_attn<D, NW, 64, true, DUMP, false>), grid, block, lds, s, a);
+  else if (a.skim && a.d.Bk == 16)
+    hipLaunchKernelGGL((k3_attn<D, NW, 16, true, DUMP, false>), grid, block, lds, s, a);
+  else if (a.skim)
+    hipLaunchKernelGGL((k3_attn<D, NW, 8, true, DUMP, false>), grid, block, lds, s, a);
   else if (a.refine)
     hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP, true>), grid, block, lds, s, a);
   else if (a.d.Bk == 64)
     hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP, false>), grid, block, lds, s, a);
   else if (a.d.Bk == 16)
     hipLaunchKernelGGL((k3_attn<D, NW, 16, false, DUMP, false>), grid, block, lds, s, a);
-  else
+  else if (a.d.Bk == 8)
     hipLaunchKernelGGL((k3_attn<D, NW, 8, false, DUMP, false>), grid, block, lds, s, a);
+  else if (a.d.Bk == 4)
+    hipLaunchKernelGGL((k3_attn<D, NW, 4, false, DUMP, false>), grid, block, lds, s, a);
+  else if (a.d.Bk == 2)
+    hipLaunchKernelGGL((k3_attn<D, NW, 2, false, DUMP, false>), grid, block, lds, s, a);
+  else if (a.d.Bk == 1)
+    hipLaunchKernelGGL((k3_attn<D, NW, 1, false, DUMP, false>), grid, block, lds, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -47,28 +47,19 @@ __host__ __device__ inline int vt_pos(int key) {
   return (2 * (p >> 3) + key_h(key)) * 8 + (p & 7);
 }
 
-// Within one group of 16 keys (16g..16g+15, one P chunk of the P.V MFMA) the
-// permutation does not depend on g: vt_pos(16g + k) = 16g + vt16_pos(k), a
-// swap of key bits 2 and 3.  A 16-key block stored with this order can be
-// placed at any column group of a 64-key tile.
-__host__ __device__ inline int vt16_pos(int k) { return 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3); }
-// 8-key blocks: a step of eight blocks (slots) places slot s's keys at the
-// score rows whose P values form one 8-key chunk of the P.V operand, chunk
-// (s >> 1) in lane half (s & 1):
-//   score row m holds key kk8(m) of slot slot8(m).
-// A chunk then lists its slot's keys in order, so a block's V^T row is stored
-// [d][8] in natural key order and one 16-byte load fetches it.
-__host__ __device__ inline int slot8(int m) { return 2 * (2 * (m >> 5) + ((m >> 4) & 1)) + ((m >> 2) & 1); }
-__host__ __device__ inline int kk8(int m) { return (m & 3) + 4 * ((m >> 3) & 1); }
-
-// key whose value sits at element e of a stored row of BK keys (BK = 64, 16 or 8)
+// Key blocks of BK <= 8 keys: a step gathers G = 64 / BK blocks (slots), and
+//   score row m holds key prow(m) % BK of slot prow(m) / BK,
+// where prow(m), m with bits 2 and 3 swapped, is the place of row m's P value
+// in the P.V operand order (chunk c = prow / 16, lane half (prow / 8) & 1,
+// element prow % 8).  A slot's keys are then BK consecutive P values of one
+// lane half, so its maximum needs no exchange between lanes, and with
+// BK >= 4 the rows of a slot come in runs of four consecutive score rows,
+// which suits the row gathers of K and V.
+__host__ __device__ inline int prow(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 template <int BK>
-__host__ __device__ inline int vt_key(int e) {
-  if (BK == 8) return e;
-  if (BK == 16) return (e & 3) | ((e >> 1) & 4) | ((e << 1) & 8);
-  const int cc = e >> 3, hh = cc & 1, p = 8 * (cc >> 1) + (e & 7);
-  return 32 * (p >> 4) + 8 * ((p & 15) >> 2) + 4 * hh + (p & 3);
-}
+__host__ __device__ inline int slotg(int m) { return prow(m) / BK; }
+template <int BK>
+__host__ __device__ inline int kkg(int m) { return prow(m) % BK; }
 
 // Key order of a stored E4M3 V^T row of a 64-key tile (the A operand of the
 // fp8 P.V MFMA).  The fp8 MFMA takes 32 bytes per lane in the same k
@@ -161,6 +152,15 @@ __device__ inline int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// This lane's index in the wave, read from the hardware where it is used
+// (v_mbcnt): address terms formed from it need no register held across a
+// kernel, and the volatile asm keeps the compiler from merging the reads.
+__device__ inline int lane_here() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // Register values made opaque to the optimiser: nothing is hoisted, folded or

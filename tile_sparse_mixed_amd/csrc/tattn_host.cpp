@@ -80,14 +80,15 @@ Layout make_layout(const Dims& d, int entropy_samples, bool moments, bool skim, 
       o += (bytes + kAlign - 1) / kAlign * kAlign;
       return at;
     };
-    sl.vt = sub(Nk * Bk * D * 2);
     sl.v8t = sub(Nk * Bk * D);
     sl.vlow = sub(Bk < 64 ? Nk * Bk * D * 2 : 0);
     sl.k8 = sub(Nk * Bk * D);
     sl.kbhi = sub(Nk * D * 2);
     sl.kblo = sub(Nk * D * 2);
     sl.vbarT = sub((size_t)d.NkC * 64 * D * 2);
-    const size_t k4n = skim || refine ? Nk * Bk : 0, k4rn = refine ? Nk * Bk : 0;
+    // MXFP4 rows are made per 64-row group of the sequence
+    const size_t rows64 = (size_t)(d.N + 63) / 64 * 64;
+    const size_t k4n = skim || refine ? rows64 : 0, k4rn = refine ? rows64 : 0;
     sl.k4 = sub(k4n * D / 2);
     sl.k4s = sub(k4n * D / 32);
     sl.k4r = sub(k4rn * D / 2);
@@ -156,9 +157,10 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "head_dim, block_q and block_k must be >= 1");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(TATTN_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
-  if ((c->block_k != 64 && c->block_k != 16 && c->block_k != 8) || (c->block_q != 64 && c->block_q != 128))
-    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported (block_q 64 or 128, block_k 64, 16 or 8)", c->block_q,
-                c->block_k);
+  const int bk = c->block_k;
+  if ((bk != 64 && bk != 16 && bk != 8 && bk != 4 && bk != 2 && bk != 1) || (c->block_q != 64 && c->block_q != 128))
+    return fail(TATTN_E_UNSUPPORTED, "tile %dx%d not supported (block_q 64 or 128, block_k 64, 16, 8, 4, 2 or 1)",
+                c->block_q, c->block_k);
   if (c->mode < 0 || c->mode > 4) return fail(TATTN_E_INVALID, "mode %d out of range", c->mode);
   if (c->mode == TATTN_MODE_PRICE && (!std::isfinite(c->price) || c->price < 0.0f))
     return fail(TATTN_E_INVALID, "price must be finite and >= 0 (got %g)", c->price);
@@ -168,8 +170,8 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "tau_skim must be finite and >= 0 (got %g)", c->tau_skim);
   if (c->mode == TATTN_MODE_THRESHOLD && c->tau_skim > c->tau_lo)
     return fail(TATTN_E_INVALID, "tau_skim needs 0 <= tau_skim <= tau_lo (got %g, tau_lo %g)", c->tau_skim, c->tau_lo);
-  if (skim_on(*c) && c->block_k != 64)
-    return fail(TATTN_E_UNSUPPORTED, "the SKIM tier needs 64-key blocks (block_k %d)", c->block_k);
+  if (skim_on(*c) && c->block_k < 8)
+    return fail(TATTN_E_UNSUPPORTED, "the SKIM tier needs key blocks of 64, 16 or 8 keys (block_k %d)", c->block_k);
   if (c->low_refine != 0 && c->low_refine != 1) return fail(TATTN_E_INVALID, "low_refine must be 0 or 1 (got %d)", c->low_refine);
   if (refine_on(*c) && c->block_k != 64)
     return fail(TATTN_E_UNSUPPORTED, "the refined low tier needs 64-key blocks (block_k %d)", c->block_k);
@@ -198,7 +200,7 @@ static tattn_status validate(const tattn_config* c) {
   if (nk > kMaxNk) return fail(TATTN_E_UNSUPPORTED, "%lld key blocks exceed the limit of %d", (long long)nk, kMaxNk);
   if ((int64_t)c->batch * c->heads * nq > 0x7fffffffLL || (int64_t)c->batch * c->heads * nk > 0x7fffffffLL)
     return fail(TATTN_E_UNSUPPORTED, "problem too large for one launch");
-  // 16- and 8-key blocks address a head's K rows with 32-bit byte offsets
+  // blocks below 64 keys address a head's K and V rows with 32-bit byte offsets
   if (c->block_k != 64 && (int64_t)c->seq_len * c->stride_n * 2 > 0x7fffffffLL)
     return fail(TATTN_E_UNSUPPORTED, "seq_len x stride_n too large for %d-key blocks", c->block_k);
   return ok();
@@ -333,7 +335,7 @@ static tattn_status forward_impl(tattn_plan_t p, const void* q, const void* k, c
   if (!aligned16(q) || !aligned16(o)) return fail(TATTN_E_INVALID, "q and o must be 16-byte aligned");
   if (k != p->k || v != p->v) return fail(TATTN_E_STATE, "k and v differ from the tensors the plan was built with");
   if (!p->has_tiers) return fail(TATTN_E_STATE, "external-mode plan has no tiers yet (call tattn_plan_set_tiers)");
-  AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), o,
+  AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), o,
              p->cfg.out_dtype == TATTN_FP32 ? 1 : 0, p->ws, p->L, p->d, skim_on(p->cfg) ? 1 : 0,
              refine_on(p->cfg) ? 1 : 0, list_cap(p->cfg, p->d), dslot, dump, dsteps};
   hipError_t e = launch_attn(a, static_cast<hipStream_t>(stream));
@@ -519,12 +521,11 @@ static tattn_status get_mx4_pair(tattn_plan_t p, size_t codes_off, size_t scales
     if ((st = sync(s)) != TATTN_OK) return st;
     const uint8_t* k4 = slab.data() + codes_off;
     const uint8_t* k4s = slab.data() + scales_off;
-    for (int J = 0; J < d.Nk; J++)
-      for (int r = 0; r < 64 && J * 64 + r < d.N; r++) {
-        const size_t n = (size_t)J * 64 + r, at = bh * d.N + n;
-        if (host_codes) std::memcpy(host_codes + at * hb, k4 + n * hb, hb);
-        if (host_scales) std::memcpy(host_scales + at * nsc, k4s + n * nsc, nsc);
-      }
+    for (size_t n = 0; n < (size_t)d.N; n++) {   // rows are stored in sequence order
+      const size_t at = bh * d.N + n;
+      if (host_codes) std::memcpy(host_codes + at * hb, k4 + n * hb, hb);
+      if (host_scales) std::memcpy(host_scales + at * nsc, k4s + n * nsc, nsc);
+    }
   }
   return ok();
 }
@@ -596,10 +597,11 @@ tattn_status tattn_plan_stats(tattn_plan_t p, tattn_stats* out) {
           else st.flops_fp8 += 2.0 * mI * nJ * D;
           if (d.Bk == 64) st.flops_fp8 += 2.0 * mI * nJ * D;
           else st.flops_bf16 += 2.0 * mI * nJ * D;
-        } else if (tr[J] == TATTN_SKIM) {  // fp4 scores, fp8 P.V
+        } else if (tr[J] == TATTN_SKIM) {  // fp4 scores; fp8 P.V (64-key blocks) or fp16 P.V
           st.n_skim++;
           st.flops_fp4 += 2.0 * mI * nJ * D;
-          st.flops_fp8 += 2.0 * mI * nJ * D;
+          if (d.Bk == 64) st.flops_fp8 += 2.0 * mI * nJ * D;
+          else st.flops_bf16 += 2.0 * mI * nJ * D;
         } else {
           st.n_skip++;
           st.flops_bf16 += 4.0 * mI * D;

@@ -25,11 +25,10 @@ struct Dims {
 // caller's K: one contiguous block per (b, h), so a single buffer resource
 // with scalar sub-offsets covers it.  Offsets are bytes from the slab start.
 struct Slab {
-  size_t vt;      // fp16 [Nk][D][Bk]   V^T, keys permuted within a tile (vt_pos)
   size_t v8t;     // u8   [Nk][D][Bk]   E4M3 V^T: 64-key blocks in the fp8 P.V operand's
                   //                    key order (pv8_key), smaller blocks in key order
-  size_t vlow;    // fp16 [Nk][D][Bk]   16- and 8-key blocks only: the low tier's fp16 V
-                  //                    operand fl16(fl32(decode(E4M3) * sv)), vt's layout
+  size_t vlow;    // fp16 [Nk][Bk][D]   16- and 8-key blocks only: the low tier's fp16 V
+                  //                    operand fl16(fl32(decode(E4M3) * sv)) as rows
   size_t k8;      // u8   [Nk][Bk][D]   E4M3 K, d permuted within a row (k8_pos)
   size_t kbhi;    // bf16 [Nk][D]       K block means, hi part
   size_t kblo;    // bf16 [Nk][D]       K block means, lo part (kbar = hi + lo to ~2^-17)
@@ -109,6 +108,7 @@ hipError_t launch_compact(const RouterArgs& a, hipStream_t s);
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
+  const uint16_t* v;   // FULL tiles read the caller's V rows
   void* o;
   int out_fp32;
   unsigned char* ws;
