@@ -60,7 +60,7 @@ def source_hash():
     """Hash of the fused kernel's code (comments and blank lines stripped, so
     an edit of a comment does not void the recorded counters)."""
     h = hashlib.sha256()
-    for f in ("k3_attn.hip", "tattn_device.hpp"):
+    for f in ("k3_attn.hpp", "k3_attn.hip", "k3_bk64.hip", "tattn_device.hpp"):
         with open(os.path.join(ROOT, "tile_sparse_mixed_amd", "csrc", f)) as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
         code = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]

@@ -97,11 +97,13 @@ typedef struct {
   int64_t stride_b, stride_h, stride_n;    /* element strides shared by Q, K, V and O        */
   float price;                             /* PRICE: error per FULL tile of work, >= 0,
                                               finite; ignored by the other modes             */
-  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite, and block_k
-                                              64, 16 or 8) enables it: THRESHOLD uses it as the SKIM / SKIP
-                                              threshold (then <= tau_lo), EXTERNAL accepts SKIM
-                                              bytes, PRICE weighs SKIM as a fourth choice;
-                                              ignored by the other modes                     */
+  float tau_skim;                          /* 0 = no SKIM tier.  > 0 (finite) enables it:
+                                              THRESHOLD uses it as the SKIM / SKIP
+                                              threshold (then <= tau_lo), ADAPTIVE makes a
+                                              tile outside the kept ones SKIM where p >=
+                                              tau_skim, EXTERNAL accepts SKIM bytes, PRICE
+                                              weighs SKIM as a fourth choice; ignored by
+                                              ALL_FULL                                       */
   int32_t low_refine;                      /* 0: LOW tiles score on E4M3 copies of Q and K.
                                               1 (block_k 64, no SKIM tier): they score on
                                               MXFP4 copies with an MXFP4 residual correction

@@ -159,15 +159,19 @@ def head_retention(p: np.ndarray, samples: int, keep_min: float, keep_max: float
     return r, k, H
 
 
-def tiers_adaptive(p: np.ndarray, k_h: int, full_frac: float) -> np.ndarray:
+def tiers_adaptive(p: np.ndarray, k_h: int, full_frac: float, tau_skim: float = 0.0) -> np.ndarray:
     """Head-adaptive tiers: per row, the k_h highest-p tiles are kept; the top
     ceil(full_frac * k_h) of them run in bf16 (FULL), the rest of the kept ones
-    in fp8 (LOW), the remainder is skipped."""
+    in fp8 (LOW), the remainder is skipped.  With tau_skim > 0 (Triage's 4-bit
+    skim tier, reading R18) a tile outside the kept ones is SKIM when
+    p >= tau_skim (float32 tau widened to float64)."""
     ranks = row_ranks(p)
     nfull = int(math.ceil(full_frac * k_h))
     t = np.full(p.shape, SKIP, dtype=np.uint8)
     t[ranks < k_h] = LOW
     t[ranks < nfull] = FULL
+    if tau_skim > 0:
+        t[(t == SKIP) & (p >= float(np.float32(tau_skim)))] = SKIM
     return t
 
 
@@ -624,7 +628,7 @@ def oracle_plan(q, k, v, cfg_like, mode=None, external_tiers=None):
                             getattr(cfg_like, "tau_skim", 0.0))
     elif mode == 1:    # adaptive
         r_h, k_h, _ = head_retention(p, cfg_like.entropy_samples, cfg_like.keep_min, cfg_like.keep_max)
-        t = tiers_adaptive(p, k_h, cfg_like.full_frac)
+        t = tiers_adaptive(p, k_h, cfg_like.full_frac, getattr(cfg_like, "tau_skim", 0.0))
     elif mode == 2:    # all full
         t = np.full(p.shape, FULL, dtype=np.uint8)
     elif mode == 4:    # price

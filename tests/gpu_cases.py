@@ -219,7 +219,7 @@ def forward_checked(tsm, p, dev, g, cfg, oc, rows=None, heads=None, out=None, lo
     tiers = p.tiers()
     lists, counts = p.lists()
     nq, nk = cfg.n_qblocks, cfg.n_kblocks
-    skim = p.cfg.tau_skim > 0 and int(p.cfg.mode) in (0, 3, 4)
+    skim = p.cfg.tau_skim > 0 and int(p.cfg.mode) != 2     # every routed mode has the SKIM tier then
     heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)] if heads is None else heads
     sel = []
     for (b, h) in heads:

@@ -57,15 +57,16 @@ def test_valid_configs(lib):
     assert status(lib, good(tau_skim=1e-4)) == 0                         # SKIM tier, threshold mode
     assert status(lib, good(tau_skim=0.001)) == 0                        # tau_skim == tau_lo
     assert status(lib, good(mode="external", tau_skim=1e-4)) == 0
-    assert status(lib, good(mode="adaptive", block_q=64, block_k=16, tau_skim=1e-4)) == 0   # ignored there
+    assert status(lib, good(mode="adaptive", block_q=64, block_k=16, tau_skim=1e-4)) == 0   # SKIM below the kept tiles
     # the price router weighs SKIM by its error model: no ordering against tau_lo
     assert status(lib, good(mode="price", price=0.01, tau_skim=0.5)) == 0
     assert status(lib, good(mode="price", price=0.01, tau_skim=-1e-4)) == -1
     assert status(lib, good(mode="price", price=0.01, tau_skim=1e-4, block_q=64, block_k=16)) == 0
-    # the SKIM tier on 16- and 8-key blocks (gathered steps), not below
+    # the SKIM tier on gathered steps, down to one-key blocks
     assert status(lib, good(tau_skim=1e-4, block_q=64, block_k=16)) == 0
     assert status(lib, good(mode="external", tau_skim=1e-4, block_k=8)) == 0
-    assert status(lib, good(tau_skim=1e-4, block_q=64, block_k=4, seq_len=16380)) == -2
+    assert status(lib, good(tau_skim=1e-4, block_q=64, block_k=4, seq_len=16380)) == 0
+    assert status(lib, good(mode="external", tau_skim=1e-4, block_k=1, seq_len=4096)) == 0
     # the refined low tier: 64-key blocks, not with the SKIM tier, any mode
     for m in ("threshold", "adaptive", "price", "external", "all_full"):
         assert status(lib, good(mode=m, price=0.01, low_refine=True)) == 0, m
@@ -91,8 +92,7 @@ def test_valid_configs(lib):
     (dict(mode="price", price=-1.0), -1), (dict(mode="price", price=float("nan")), -1),
     (dict(mode=5), -1),
     (dict(tau_skim=-1e-4), -1), (dict(tau_skim=0.002), -1), (dict(tau_skim=float("nan")), -1),
-    (dict(tau_skim=1e-4, block_q=64, block_k=2, seq_len=8192), -2),
-    (dict(mode="external", tau_skim=1e-4, block_k=1, seq_len=4096), -2),
+    (dict(tau_skim=1e-4, block_q=64, block_k=2, seq_len=8194), -2),     # 4097 key blocks
 ])
 def test_invalid_configs(lib, kw, code):
     st = status(lib, good(**kw))
@@ -198,7 +198,9 @@ def test_forward_dump_rejects_bad_arguments(lib):
 
 
 @pytest.mark.parametrize("mode,extra", [("adaptive", {}), ("adaptive", dict(keep_min=0.5, keep_max=0.5)),
+                                        ("adaptive", dict(tau_skim=3e-4)),
                                         ("threshold", dict(top_k=3)), ("threshold", dict(top_k=1)),
+                                        ("threshold", dict(top_k=3, tau_skim=3e-4)),
                                         ("threshold", {}), ("price", dict(price=0.01))])
 @pytest.mark.parametrize("tiles", [(128, 64), (64, 64), (64, 16), (64, 8), (128, 16)])
 def test_list_bound_holds_every_row(mode, extra, tiles):
@@ -213,7 +215,7 @@ def test_list_bound_holds_every_row(mode, extra, tiles):
                                  **{k: v for k, v in extra.items() if k != "price"})
     c = make_config(1, cfg.heads, cfg.seq_len, cfg.head_dim, bq, bk, tau_hi=cfg.tau_hi, tau_lo=cfg.tau_lo,
                     top_k=cfg.top_k, mode=mode, keep_min=cfg.keep_min, keep_max=cfg.keep_max,
-                    full_frac=cfg.full_frac, price=extra.get("price", 0.0))
+                    full_frac=cfg.full_frac, price=extra.get("price", 0.0), tau_skim=extra.get("tau_skim", 0.0))
     bound = tsm.list_bound(c)
     assert 1 <= bound <= cfg.n_kblocks
     g = generate(cfg)
@@ -222,7 +224,8 @@ def test_list_bound_holds_every_row(mode, extra, tiles):
         block_q, block_k, tau_hi, tau_lo = bq, bk, float(np.float32(cfg.tau_hi)), float(np.float32(cfg.tau_lo))
         top_k, keep_min, keep_max, full_frac = cfg.top_k, float(np.float32(cfg.keep_min)), \
             float(np.float32(cfg.keep_max)), float(np.float32(cfg.full_frac))
-        entropy_samples, price, tau_skim = cfg.entropy_samples, float(np.float32(extra.get("price", 0.0))), 0.0
+        entropy_samples, price = cfg.entropy_samples, float(np.float32(extra.get("price", 0.0)))
+        tau_skim = float(np.float32(extra.get("tau_skim", 0.0)))
         mode = cfg.mode
     for h in range(cfg.heads):
         o = T.oracle_plan(g["q"][0, h], g["k"][0, h], g["v"][0, h], OC)

@@ -25,6 +25,10 @@ CASES = {
     "fine64x8": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=8, tau_skim=1e-4),
     "fine64x8_d64": CONFIGS["small"].with_(heads=2, grid=(5, 9, 13), block_q=64, block_k=8, tau_skim=3e-4),
     "fine128x16_d64": CONFIGS["small"].with_(heads=2, grid=(5, 9, 13), block_k=16, tau_skim=3e-4),
+    # blocks below 8 keys: 16, 32 or 64 SKIM blocks per step
+    "fine64x4": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=4, tau_skim=1e-4),
+    "fine128x2_d64": CONFIGS["small"].with_(heads=2, grid=(3, 7, 9), block_k=2, tau_skim=3e-4),
+    "fine64x1": CONFIGS["fine_adaptive"].with_(grid=(2, 5, 13), heads=2, mode=0, block_k=1, tau_skim=1e-4),
 }
 
 
@@ -74,7 +78,8 @@ def test_four_tier_threshold_parity(name):
 
 
 @pytest.mark.parametrize("name,seed", [("small", 1), ("d128_ragged", 2), ("d128_q64", 3), ("fine64x16", 4),
-                                       ("fine64x8_d64", 5), ("fine128x16_d64", 6)])
+                                       ("fine64x8_d64", 5), ("fine128x16_d64", 6), ("fine64x4", 7),
+                                       ("fine128x2_d64", 8), ("fine64x1", 9)])
 def test_external_four_tier_maps(name, seed):
     """Random maps over all four tiers, and a map that is SKIM everywhere but
     the diagonal."""
@@ -213,3 +218,44 @@ def test_largest_key_block_count_with_skim():
     assert np.array_equal(tiers[0, 0][~band], o["tiers"][~band])
     rows = [0, cfg.n_qblocks // 3, cfg.n_qblocks - 1]
     check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), rows=rows, what="skim max Nk", log=_log)
+
+
+def _rank_ambiguous_rows(p, k):
+    """Rows whose k-th and (k+1)-th largest p are equal to rounding (either
+    side may keep either tile)."""
+    if k <= 0 or k >= p.shape[1]:
+        return np.zeros(p.shape[0], bool)
+    s = -np.sort(-p, axis=1)
+    return np.abs(s[:, k - 1] - s[:, k]) <= 1e-12 * s[:, k - 1]
+
+
+@pytest.mark.parametrize("name", ["small", "fine64x16", "fine64x4", "fine64x1"])
+def test_adaptive_mode_with_skim(name):
+    """Head-adaptive tiers with the fourth tier: the top k_h tiles as without
+    it, the rest SKIM where p >= tau_skim and SKIP below; lists and the output
+    under the GPU's map."""
+    import tile_sparse_mixed_amd as tsm
+    cfg = CASES[name].with_(mode=1)
+    g, dev = device_inputs(cfg)
+    p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, mode="adaptive",
+                 keep_min=cfg.keep_min, keep_max=cfg.keep_max, full_frac=cfg.full_frac,
+                 entropy_samples=cfg.entropy_samples, tau_skim=cfg.tau_skim, out_fp32=True)
+    kh, _ = p.kh()
+    tiers = p.tiers()
+    lists, counts = p.lists()
+    assert p.stats()["n_skim"] == int((tiers == T.SKIM).sum()) > 0
+    _log(f"[adaptive skim {name}] k_h {kh.tolist()} FULL/LOW/SKIM/SKIP "
+         f"{[round(float((tiers == x).mean()), 3) for x in (2, 1, 3, 0)]}")
+    oc = OracleCfg(cfg)
+    for h in range(cfg.heads):
+        o = T.oracle_plan(g["q"][0, h], g["k"][0, h], g["v"][0, h], oc)
+        if kh[h] != o["k_h"]:
+            continue        # k_h on an integer boundary of r_h * Nk (checked in the three-tier tests)
+        nfull = int(np.ceil(oc.full_frac * o["k_h"]))
+        amb = _rank_ambiguous_rows(o["p"], o["k_h"]) | _rank_ambiguous_rows(o["p"], nfull)
+        band = np.abs(o["p"] - oc.tau_skim) <= 1e-5 * oc.tau_skim
+        ok = ~amb[:, None] & ~band
+        assert np.array_equal(tiers[0, h][ok], o["tiers"][ok]), (name, h)
+        li, co = T.build_lists(tiers[0, h])
+        assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), (name, h)
+    check_forward(tsm, p, dev, g, cfg, OracleCfg(cfg, mode=3), what=f"adaptive skim {name}", log=_log)

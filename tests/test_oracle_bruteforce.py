@@ -103,6 +103,26 @@ def test_bruteforce_adaptive_rank_tiers(nk, k_h, frac):
             assert t[I, J] == want
 
 
+@pytest.mark.parametrize("nk,k_h,frac,tau", [(8, 3, 0.1, 0.08), (9, 2, 0.5, 0.02), (6, 6, 0.34, 0.1)])
+def test_bruteforce_adaptive_rank_tiers_with_skim(nk, k_h, frac, tau):
+    """With the fourth tier, the tiles outside the top k_h split at tau_skim:
+    SKIM at or above it, SKIP below; the kept tiles are as without it."""
+    from oracle import SKIM
+    r = np.random.default_rng(nk * 100 + k_h)
+    p = r.dirichlet(np.ones(nk), size=5)
+    t = T.tiers_adaptive(p, k_h, frac, tau_skim=tau)
+    t0 = T.tiers_adaptive(p, k_h, frac)
+    nfull = math.ceil(frac * k_h)
+    tau32 = float(np.float32(tau))
+    for I in range(5):
+        for J in range(nk):
+            rank = sum(1 for J2 in range(nk) if p[I, J2] > p[I, J] or (p[I, J2] == p[I, J] and J2 < J))
+            want = FULL if rank < nfull else (LOW if rank < k_h else (SKIM if p[I, J] >= tau32 else SKIP))
+            assert t[I, J] == want
+    assert np.array_equal(t[t0 != SKIP], t0[t0 != SKIP])
+    assert np.array_equal(T.tiers_adaptive(p, k_h, frac, tau_skim=0.0), t0)
+
+
 def test_head_retention_clip_and_ceiling():
     nk = 100
     uniform = np.full((8, nk), 1.0 / nk)            # entropy ln(nk): perplexity nk -> clipped to 0.5

@@ -14,7 +14,7 @@
 //   v8t              E4M3 codes of V_J, transposed ([d][key]): the A operand of the
 //                    low tier's fp8 P.V for 64-key blocks (pv8_key order), key
 //                    order otherwise,
-//   vlow             16- and 8-key blocks: the low tier's fp16 V operand,
+//   vlow             blocks below 64 keys: the low tier's fp16 V operand,
 //                    fl16(fl32(decode(E4M3(v * inv)) * sv)), as rows [key][d]
 //                    (the fused kernel gathers four or eight blocks per step, so
 //                    one P.V mixes blocks of different scales and the fp8 P.V

@@ -556,6 +556,12 @@ __global__ __launch_bounds__(kThreads) void k2b_rows(RouterArgs a) {
     // its select only counts the values from there up
     const uint64_t xk = mark_top_k(pv, n, kh, [&](int J, bool kept) { tr[J] = kept ? TATTN_LOW : TATTN_SKIP; }, r);
     mark_top_k(pv, n, nfull, [&](int J, bool kept) { if (kept) tr[J] = TATTN_FULL; }, r, xk);
+    if (a.tau_skim > 0.0f) {   // the fourth tier: a tile outside the top k_h with p >= tau_skim
+      __syncthreads();
+      const double tk = a.tau_skim;
+      for (int J = threadIdx.x; J < n; J += kThreads)
+        if (tr[J] == TATTN_SKIP && pv[J] >= tk) tr[J] = TATTN_SKIM;
+    }
     for (int J = threadIdx.x; J < n; J += kThreads) pout[J] = static_cast<float>(pv[J]);
   }
   __syncthreads();

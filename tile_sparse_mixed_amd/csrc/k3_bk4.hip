@@ -1,0 +1,7 @@
+// The fused pass's instances with 4-key blocks (one translation unit per
+// key-block size, so that the instances compile in parallel).
+#include "k3_attn.hpp"
+
+namespace tattn {
+hipError_t launch_attn_bk4(const AttnArgs& a, hipStream_t s) { return launch_bk<4>(a, s); }
+}  // namespace tattn

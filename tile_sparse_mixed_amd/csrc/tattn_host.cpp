@@ -124,8 +124,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // The SKIM tier is on for a positive tau_skim in THRESHOLD, EXTERNAL and
 // PRICE modes.
 static bool skim_on(const tattn_config& c) {
-  return c.tau_skim > 0.0f &&
-         (c.mode == TATTN_MODE_THRESHOLD || c.mode == TATTN_MODE_EXTERNAL || c.mode == TATTN_MODE_PRICE);
+  return c.tau_skim > 0.0f && c.mode != TATTN_MODE_ALL_FULL;
 }
 // The refined low tier: LOW tiles score on MXFP4 copies with residual correction.
 static bool refine_on(const tattn_config& c) { return c.low_refine == 1; }
@@ -141,7 +140,7 @@ static Layout layout_of(const tattn_config& c) {
 static int list_cap(const tattn_config& c, const Dims& d) {
   const int64_t ndiag = d.Bq / d.Bk + 1;
   int64_t cap = d.Nk;
-  if (c.mode == TATTN_MODE_ADAPTIVE)
+  if (c.mode == TATTN_MODE_ADAPTIVE && !skim_on(c))   // (SKIM tiles lie outside the kept ones)
     cap = std::min<int64_t>(cap, (int64_t)std::ceil((double)c.keep_max * (double)d.Nk) + ndiag);
   else if (c.mode == TATTN_MODE_THRESHOLD && c.top_k > 0)
     cap = std::min<int64_t>(cap, (int64_t)c.top_k + ndiag);
@@ -170,8 +169,6 @@ static tattn_status validate(const tattn_config* c) {
     return fail(TATTN_E_INVALID, "tau_skim must be finite and >= 0 (got %g)", c->tau_skim);
   if (c->mode == TATTN_MODE_THRESHOLD && c->tau_skim > c->tau_lo)
     return fail(TATTN_E_INVALID, "tau_skim needs 0 <= tau_skim <= tau_lo (got %g, tau_lo %g)", c->tau_skim, c->tau_lo);
-  if (skim_on(*c) && c->block_k < 8)
-    return fail(TATTN_E_UNSUPPORTED, "the SKIM tier needs key blocks of 64, 16 or 8 keys (block_k %d)", c->block_k);
   if (c->low_refine != 0 && c->low_refine != 1) return fail(TATTN_E_INVALID, "low_refine must be 0 or 1 (got %d)", c->low_refine);
   if (refine_on(*c) && c->block_k != 64)
     return fail(TATTN_E_UNSUPPORTED, "the refined low tier needs 64-key blocks (block_k %d)", c->block_k);

@@ -27,7 +27,7 @@ struct Dims {
 struct Slab {
   size_t v8t;     // u8   [Nk][D][Bk]   E4M3 V^T: 64-key blocks in the fp8 P.V operand's
                   //                    key order (pv8_key), smaller blocks in key order
-  size_t vlow;    // fp16 [Nk][Bk][D]   16- and 8-key blocks only: the low tier's fp16 V
+  size_t vlow;    // fp16 [Nk][Bk][D]   blocks below 64 keys only: the low tier's fp16 V
                   //                    operand fl16(fl32(decode(E4M3) * sv)) as rows
   size_t k8;      // u8   [Nk][Bk][D]   E4M3 K, d permuted within a row (k8_pos)
   size_t kbhi;    // bf16 [Nk][D]       K block means, hi part
@@ -125,5 +125,12 @@ struct AttnArgs {
   int dsteps;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// the fused pass of one key-block size (k3_bk*.hip)
+hipError_t launch_attn_bk64(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bk16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bk8(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bk4(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bk2(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bk1(const AttnArgs& a, hipStream_t s);
 
 }  // namespace tattn
