@@ -1,7 +1,8 @@
 // K1: block pooling and per-block E4M3 quantisation, one streaming pass over
 // Q, K and V (HBM-bound).
 //
-// Per (b, h, key block J) one workgroup reads K_J and V_J once and writes
+// Per (b, h, key block J) one workgroup (with blocks below 64 keys: per group
+// of 64 keys, k1_kv_g) reads K_J and V_J once and writes
 //   kbar_J, vbar_J   float32 block means (float64 sums / n_J; "Triage": a skipped
 //                    tile is replaced by its block means),
 //   kbar16, kbarlo   the K means as a bf16 pair hi + lo (hi = bf16(kbar), lo =
@@ -298,6 +299,141 @@ __global__ __launch_bounds__(kThreads) void k1_kv(PoolArgs a) {
   }
 }
 
+// Blocks below 64 keys: one workgroup per (b, h, group of 64 keys), i.e.
+// 64 / BK blocks, with the same outputs as k1_kv.  The group's K (then V)
+// rows are staged in LDS as bf16 and every per-block reduction (float64
+// column sums, amax) reads them there, so each workgroup streams 64 rows; one
+// workgroup per block moved BK rows each and ran at a few percent of HBM
+// bandwidth.  (The price router's second moments stay on k1_kv.)
+template <int D, int BK>
+__global__ __launch_bounds__(kThreads) void k1_kv_g(PoolArgs a) {
+  static_assert(BK == 16 || BK == 8 || BK == 4 || BK == 2 || BK == 1, "gathered pooling is for blocks below 64 keys");
+  constexpr int GB = 64 / BK;          // key blocks of the group
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RT = kThreads / CH;    // rows per pass
+  __shared__ uint16_t tile[64 * D];    // the group's rows (bf16, exact)
+  __shared__ float ramax[64];          // per row: max |x|
+  __shared__ float binv[GB], bsc[GB];  // per block: inverse scale and scale
+
+  const Dims& dm = a.d;
+  const int NG = (dm.N + 63) / 64;
+  const int bh = blockIdx.x / NG, grp = blockIdx.x % NG;
+  const int b = bh / dm.H, h = bh % dm.H;
+  const int J0 = grp * GB;                         // the group's first block
+  const int nrows = min(64, dm.N - grp * 64);      // real rows of the group
+  const int nblk = min(GB, dm.Nk - J0);            // real blocks of the group
+  const int64_t off = (int64_t)b * dm.sb + (int64_t)h * dm.sh + (int64_t)grp * 64 * dm.sn;
+  unsigned char* ws = a.ws;
+  float* kbar = reinterpret_cast<float*>(ws + a.L.kbar) + ((int64_t)bh * dm.Nk + J0) * D;
+  float* vbar = reinterpret_cast<float*>(ws + a.L.vbar) + ((int64_t)bh * dm.Nk + J0) * D;
+  unsigned char* slab = ws + a.L.slab + (int64_t)bh * a.L.sl.bytes;
+  uint16_t* kbar16 = reinterpret_cast<uint16_t*>(slab + a.L.sl.kbhi) + (int64_t)J0 * D;
+  uint16_t* kbarlo = reinterpret_cast<uint16_t*>(slab + a.L.sl.kblo) + (int64_t)J0 * D;
+  uint16_t* vbarT = reinterpret_cast<uint16_t*>(slab + a.L.sl.vbarT) + (int64_t)(J0 / 64) * 64 * D;
+  float* sk = reinterpret_cast<float*>(ws + a.L.sk) + (int64_t)bh * dm.Nk + J0;
+  float* sv = reinterpret_cast<float*>(ws + a.L.sv) + (int64_t)bh * dm.Nk + J0;
+  unsigned char* k8 = slab + a.L.sl.k8 + (int64_t)J0 * BK * D;
+  unsigned char* v8t = slab + a.L.sl.v8t + (int64_t)J0 * BK * D;
+  uint16_t* vlow = reinterpret_cast<uint16_t*>(slab + a.L.sl.vlow) + (int64_t)J0 * BK * D;
+  const int t = threadIdx.x, c = t % CH, r0 = t / CH;
+
+  // stage 64 rows of `src` (zeros past N) and each row's |x| maximum: the CH
+  // lanes of a row are consecutive lanes of one wave
+  auto stage = [&](const uint16_t* src) {
+    for (int r = r0; r < 64; r += RT) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (r < nrows) raw = *reinterpret_cast<const uint4*>(src + (int64_t)r * dm.sn + c * 8);
+      *reinterpret_cast<uint4*>(tile + r * D + c * 8) = raw;
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t mx = 0;   // |x| as bf16 bits (monotone in the magnitude)
+#pragma unroll
+      for (int j = 0; j < 4; j++) mx = max(mx, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+#pragma unroll
+      for (int o = CH / 2; o > 0; o >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o, 64)));
+      if (c == 0) ramax[r] = __uint_as_float(mx << 16);
+    }
+    __syncthreads();
+    if (t < GB) {   // per block: amax -> scale, inverse scale (1 for an all-zero block)
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < BK; e++) am = __builtin_fmaxf(am, ramax[t * BK + e]);
+      bsc[t] = scale448(am);
+      binv[t] = inv448(am);
+    }
+  };
+  // per block and column: the float64 sum of the block's real rows, as a mean
+  auto block_mean = [&](int g, int d) {
+    const int rows = min(BK, dm.N - (J0 + g) * BK);
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < BK; e++) s += static_cast<double>(bf16_to_f32(tile[(g * BK + e) * D + d]));
+    return static_cast<float>(s / static_cast<double>(rows));
+  };
+
+  // ---- K: means (and the bf16 hi / lo pair), scales, codes
+  stage(a.k + off);
+  for (int u = t; u < nblk * D; u += kThreads) {
+    const int g = u / D, d = u % D;
+    const float m = block_mean(g, d);
+    kbar[g * D + d] = m;
+    const uint16_t hi = f32_to_bf16(m);
+    kbar16[g * D + d] = hi;
+    kbarlo[g * D + d] = f32_to_bf16(m - bf16_to_f32(hi));   // the difference is exact in fp32
+  }
+  __syncthreads();   // block scales published
+  if (t < nblk) sk[t] = bsc[t];
+  for (int r = r0; r < nblk * BK; r += RT) {
+    const float inv = binv[r / BK];
+    const uint4 raw = *reinterpret_cast<const uint4*>(tile + r * D + c * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) f[e] = __uint_as_float(e & 1 ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+    int w0 = 0, w1 = 0;
+    w0 = cvt_fp8x2<false>(f[0] * inv, f[1] * inv, w0);
+    w0 = cvt_fp8x2<true>(f[2] * inv, f[3] * inv, w0);
+    w1 = cvt_fp8x2<false>(f[4] * inv, f[5] * inv, w1);
+    w1 = cvt_fp8x2<true>(f[6] * inv, f[7] * inv, w1);
+    *reinterpret_cast<uint2*>(k8 + r * D + k8_pos(c * 8)) = make_uint2(w0, w1);
+  }
+  __syncthreads();   // every read of the K rows done before V overwrites them
+
+  // ---- V: means (and their fp16 transposed chunk), scales, transposed
+  // codes, the low tier's fp16 rows
+  stage(a.v + off);
+  for (int u = t; u < nblk * D; u += kThreads) {
+    const int g = u / D, d = u % D, J = J0 + g;
+    const float m = block_mean(g, d);
+    vbar[g * D + d] = m;
+    vbarT[d * 64 + vt_pos(J & 63)] = f32_to_f16(m);
+    if (J == dm.Nk - 1)   // finite zeros in the chunk's unused columns (they meet P = 0)
+      for (int j = (J & 63) + 1; j < 64; j++) vbarT[d * 64 + vt_pos(j)] = 0;
+  }
+  __syncthreads();
+  if (t < nblk) sv[t] = bsc[t];
+  for (int u = t; u < nblk * D * BK; u += kThreads) {   // v8t: block g's row d holds its BK keys in order
+    const int g = u / (D * BK), d = (u / BK) % D, e = u % BK;
+    v8t[u] = static_cast<unsigned char>(
+        cvt_fp8x2<false>(bf16_to_f32(tile[(g * BK + e) * D + d]) * binv[g], 0.0f, 0) & 0xff);
+  }
+  for (int r = r0; r < nblk * BK; r += RT) {   // vlow rows: fl16(fl32(decode(code)) * sv)
+    const float inv = binv[r / BK], svf = bsc[r / BK];
+    const uint4 raw = *reinterpret_cast<const uint4*>(tile + r * D + c * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; e2++) {
+      const float f0 = __uint_as_float(w[e2] << 16) * inv, f1 = __uint_as_float(w[e2] & 0xffff0000u) * inv;
+      const int code2 = cvt_fp8x2<false>(f0, f1, 0);
+      const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8(code2, false);
+      float p0 = dec.x * svf, p1 = dec.y * svf;
+      opaque(p0, p1);   // round the product to fp32 first, then to fp16 (no fused mixed-precision op)
+      o[e2] = uint32_t(f32_to_f16(p0)) | (uint32_t(f32_to_f16(p1)) << 16);
+    }
+    *reinterpret_cast<uint4*>(vlow + r * D + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <int D, int BQ, bool MOM>
 __global__ __launch_bounds__(kThreads) void k1_q(PoolArgs a) {
   using BL = BlockLoad<D, BQ>;
@@ -399,7 +535,18 @@ __global__ __launch_bounds__(kThreads) void k1_mx4(PoolArgs a) {
 template <int D, bool MOM>
 hipError_t launch_pool_d(const PoolArgs& a, hipStream_t s) {
   const Dims& d = a.d;
-  if (d.Bk == 64)
+  const dim3 groups(d.BH * ((d.N + 63) / 64));   // 64-key groups (blocks below 64 keys)
+  if (!MOM && d.Bk == 16)
+    hipLaunchKernelGGL((k1_kv_g<D, 16>), groups, dim3(kThreads), 0, s, a);
+  else if (!MOM && d.Bk == 8)
+    hipLaunchKernelGGL((k1_kv_g<D, 8>), groups, dim3(kThreads), 0, s, a);
+  else if (!MOM && d.Bk == 4)
+    hipLaunchKernelGGL((k1_kv_g<D, 4>), groups, dim3(kThreads), 0, s, a);
+  else if (!MOM && d.Bk == 2)
+    hipLaunchKernelGGL((k1_kv_g<D, 2>), groups, dim3(kThreads), 0, s, a);
+  else if (!MOM && d.Bk == 1)
+    hipLaunchKernelGGL((k1_kv_g<D, 1>), groups, dim3(kThreads), 0, s, a);
+  else if (d.Bk == 64)
     hipLaunchKernelGGL((k1_kv<D, 64, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
   else if (d.Bk == 16)
     hipLaunchKernelGGL((k1_kv<D, 16, MOM>), dim3(d.BH * d.Nk), dim3(kThreads), 0, s, a);
