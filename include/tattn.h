@@ -105,7 +105,7 @@ typedef struct {
                                               weighs SKIM as a fourth choice; ignored by
                                               ALL_FULL                                       */
   int32_t low_refine;                      /* 0: LOW tiles score on E4M3 copies of Q and K.
-                                              1 (block_k 64, no SKIM tier): they score on
+                                              1 (no SKIM tier): they score on
                                               MXFP4 copies with an MXFP4 residual correction
                                               ("Triage": refining a tile with 4-bit residual
                                               correction): <q4,k4> + <q4,k4r> + <q4r,k4>;

@@ -67,10 +67,11 @@ def test_valid_configs(lib):
     assert status(lib, good(mode="external", tau_skim=1e-4, block_k=8)) == 0
     assert status(lib, good(tau_skim=1e-4, block_q=64, block_k=4, seq_len=16380)) == 0
     assert status(lib, good(mode="external", tau_skim=1e-4, block_k=1, seq_len=4096)) == 0
-    # the refined low tier: 64-key blocks, not with the SKIM tier, any mode
+    # the refined low tier: any block size, not with the SKIM tier, any mode
     for m in ("threshold", "adaptive", "price", "external", "all_full"):
         assert status(lib, good(mode=m, price=0.01, low_refine=True)) == 0, m
-    assert status(lib, good(low_refine=True, block_q=64, block_k=16)) == -2
+    assert status(lib, good(low_refine=True, block_q=64, block_k=16)) == 0
+    assert status(lib, good(low_refine=True, block_q=64, block_k=1, seq_len=4096)) == 0
     assert status(lib, good(low_refine=True, tau_skim=1e-4)) == -2
     c = good()
     c.low_refine = 2

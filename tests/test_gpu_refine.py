@@ -3,7 +3,7 @@ tile with 4-bit residual correction): the pooling kernel's MXFP4 copy of K
 and of its residual bit for bit against the oracle's codec, and the fused
 kernel's output against the oracle under the GPU's tier map, with the
 probability codes admitted as for the E4M3 low tier, for 128- and 64-row
-query blocks at d = 128 and 64, ragged lengths, the threshold and adaptive
+query blocks at d = 128 and 64, key blocks of 64 down to one key, ragged lengths, the threshold and adaptive
 routers, fp32 and bf16 outputs; plus the code-dumping forward equal to the
 plain one bit for bit."""
 import numpy as np
@@ -22,6 +22,11 @@ CASES = {
     "small_q64": CONFIGS["small"].with_(heads=2, block_q=64),                    # two waves
     "d128_ragged": CONFIGS["wan_like"].with_(heads=2, grid=(3, 10, 23)),         # N 690
     "d128_q64": CONFIGS["wan_like"].with_(heads=2, grid=(2, 10, 50), block_q=64),
+    # gathered steps: refined 16-, 8-, 4- and one-key blocks
+    "fine64x16": CONFIGS["fine_adaptive"].with_(grid=(2, 10, 50), heads=2, mode=0),
+    "fine128x8_d64": CONFIGS["small"].with_(grid=(5, 9, 13), heads=2, block_k=8),
+    "fine64x4": CONFIGS["fine_adaptive"].with_(grid=(3, 7, 9), heads=2, mode=0, block_k=4),
+    "fine64x1": CONFIGS["fine_adaptive"].with_(grid=(2, 5, 13), heads=2, mode=0, block_k=1),
 }
 
 

@@ -35,7 +35,7 @@ def test_fused_kernel_instances_use_no_scratch(tmp_path):
         scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
         assert len(names) == len(scratch), (len(names), len(scratch))
         k3 += [(n, s) for n, s in zip(names, scratch) if "k3_attn" in n]
-    # D x NW x DUMP x (six key-block sizes with and without SKIM, and the refined tier)
-    assert len(k3) == 2 * 2 * 2 * (6 * 2 + 1), len(k3)
+    # D x NW x DUMP x six key-block sizes x (three tiers, with SKIM, refined low tier)
+    assert len(k3) == 2 * 2 * 2 * 6 * 3, len(k3)
     spills = [(n, s) for n, s in k3 if s != 0]
     assert not spills, spills

@@ -258,7 +258,7 @@ def plan(q, k, v, block_q=128, block_k=64, tau_hi=0.01, tau_lo=0.001, top_k=0, m
     """Pool, quantise and route (K1, K2).  q, k, v: bf16 [B, H, N, d] on the GPU.
     ``tau_skim`` > 0 adds the MXFP4 SKIM tier (every mode but all-full, every
     key-block size).  ``low_refine`` scores LOW tiles on MXFP4 copies with
-    residual correction instead of E4M3 (64-key blocks, no SKIM tier).
+    residual correction instead of E4M3 (no SKIM tier).
     ``workspace`` (a uint8 GPU tensor, e.g. an earlier
     plan's) is reused when large enough; the earlier plan must not be used
     afterwards."""

@@ -247,20 +247,20 @@ struct StepScale {
   float v;   // E4M3 value scale of a 64-key LOW or SKIM step's block
 };
 
-// SKIM: the instance also runs the SKIM tier (64-key blocks only); the other
-// instances carry none of its code.  DUMP: the probability-code dump.
+// SKIM: the instance also runs the SKIM tier; the other instances carry none
+// of its code.  DUMP: the probability-code dump.
 // REFINE: LOW tiles score on MXFP4 copies of Q and K with an MXFP4 residual
 // correction, <q4,k4> + <q4,k4r> + <q4r,k4> on the block-scaled fp4 MFMA
 // ("Triage": refining a tile with 4-bit residual correction); their
-// probabilities and P.V are the E4M3 ones.  R0 of such a step holds K4 rows
+// probabilities and P.V are the low tier's.  R0 of such a step holds K4 rows
 // [64][D/2] at 0, their scale words at 32 D, the residual rows at 64 D and
-// their scale words at 96 D.
+// their scale words at 96 D (gathered per slot with blocks below 64 keys).
 template <int D, int NW, int BK, bool SKIM, bool DUMP, bool REFINE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2)))
 void k3_attn(AttnArgs a) {
   static_assert(BK == 64 || BK == 16 || BK == 8 || BK == 4 || BK == 2 || BK == 1,
                 "key blocks are 64, 16, 8, 4, 2 or 1 keys");
-  static_assert(!REFINE || (BK == 64 && !SKIM), "the refined low tier runs on 64-key blocks without SKIM");
+  static_assert(!REFINE || !SKIM, "the refined low tier runs without the SKIM tier");
   constexpr int G = 64 / BK;          // key blocks per 64-key step
   constexpr int R1 = 128 * D;         // bytes of each half of a stage (R0: K-side operands, R1: V-side)
   // Two-wave workgroups (64-row query blocks) keep ONE stage and refill its
@@ -586,6 +586,47 @@ void k3_attn(AttnArgs a) {
             }
           }
           if constexpr (PB) {   // the low tier's fp16 V rows, as for LOW steps
+            const int lv = lv_of(2 * D) + (int)SL.vlow;
+            gather16(rS, r1(st), jv, 2 * D, [&](int) { return lv; });
+          }
+          if constexpr (PA) {   // the fp4 scores carry their scales: the step's factor only
+#pragma unroll
+            for (int g = 0; g < StepScale<G>::N; g++) cst.c[g] = cF;
+            if constexpr (G >= 8) cst.kv = 1.0f;
+          }
+        } else if (REFINE && (KINDS & (1 << kLow))) {
+          // refined LOW steps: the MXFP4 K rows and their scale words, then the
+          // residual's rows and scale words (R0 at 0, 32 D, 64 D, 96 D), per
+          // lane from their slots
+          if constexpr (PA) {
+            const int lr = lane_here();
+            constexpr int C4R = D / 32;                  // 16-byte chunks per MXFP4 row
+            const int ri = lr / C4R;                     // row of the lane inside an instruction
+            const int sw = (((lr & (C4R - 1)) ^ ((lr >> 4) & (C4R - 1))) << 4);
+#pragma unroll
+            for (int i = 0; i < (D / 32 + NW - 1) / NW; i++) {
+              const int k = wave + NW * i;
+              if constexpr ((D / 32) % NW != 0) {
+                if (k >= D / 32) break;
+              }
+              const int m = k * (2048 / D) + ri;
+              const int key = G == 4 ? __shfl(jv, m >> 4, 64) * 16 + (m & 15)
+                                     : __shfl(jv, slotg<BK>(m), 64) * BK + kkg<BK>(m);
+              dma16(rS, st + k * 1024, sw + key * (D / 2), (int)SL.k4);
+              dma16(rS, st + 64 * D + k * 1024, sw + key * (D / 2), (int)SL.k4r);
+            }
+            if (wave == 0 || wave == NW - 1) {
+              const int key = G == 4 ? __shfl(jv, lr >> 4, 64) * 16 + (lr & 15)
+                                     : __shfl(jv, slotg<BK>(lr), 64) * BK + kkg<BK>(lr);
+              unsigned char* dst = st + (wave == 0 ? 32 * D : 96 * D);
+              const int src = wave == 0 ? (int)SL.k4s : (int)SL.k4rs;
+              if constexpr (D == 128)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)dst, 4, key * 4, src, 0, 0);
+              else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)dst, 2, key * 2, src, 0, 0);
+            }
+          }
+          if constexpr (PB) {   // the low tier's fp16 V rows
             const int lv = lv_of(2 * D) + (int)SL.vlow;
             gather16(rS, r1(st), jv, 2 * D, [&](int) { return lv; });
           }
@@ -1255,11 +1296,13 @@ void k3_attn(AttnArgs a) {
             for (int r = 0; r < 16; r++)
               if (8 * ((r >> 2) & 1) + (r & 3) >= ql[2 * b + (r >> 3)]) s[b][r] = -INFINITY;
         } else {
-          // the lane's slot u: P values u BK + z hold keys z = 0 .. BK-1
+          // the lane's slot u: P values u BK + z hold keys z = 0 .. BK-1 (the
+          // lane half from the hardware lane index: not held across the loop)
+          const int lhs = lane_here() >> 5;
 #pragma unroll
           for (int u = 0; u < 32 / BK; u++) {
             const int f0 = u * BK, b = f0 >> 4, r0 = f0 & 15;
-            const int slot = slotg<BK>(32 * b + 8 * (r0 >> 2) + (r0 & 3)) + (8 / BK) * lh;
+            const int slot = slotg<BK>(32 * b + 8 * (r0 >> 2) + (r0 & 3)) + (8 / BK) * lhs;
             const bool in = i0 + slot < e;
             const int Js = in ? (int)slist[i0 + slot] : 0;
             int lim = !in ? 0 : Js == dm.Nk - 1 ? dm.N - BK * Js : BK;
@@ -1288,10 +1331,11 @@ void k3_attn(AttnArgs a) {
     }
   };
   // a kept tile staged in `st`: scores, softmax, P.V
-  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, const StepScale<G>& c, const i32x8* q8) __attribute__((always_inline)) {
+  // low_scores(st, s): a LOW step's scores (E4M3 or refined); unused for FULL
+  auto kept_step = [&](auto low_tag, int t, const unsigned char* st, const StepScale<G>& c, auto low_scores) __attribute__((always_inline)) {
     constexpr bool LOW = decltype(low_tag)::value;
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    if constexpr (LOW) scores_fp8(st, s, q8);
+    if constexpr (LOW) low_scores(st, s);
     else scores_bf16(st, s);
     kept_soft(low_tag, t, s, c);
     if constexpr (LOW && G == 1) pv8(st);
@@ -1605,7 +1649,7 @@ void k3_attn(AttnArgs a) {
       } else {
         run_phase(tSk, [&](auto p, int tt) __attribute__((always_inline)) {
           if (tt + 1 < nSteps) issue(KLow{}, tt + 1, stg(flip(p)), scl(flip(p)));
-          kept_step(std::true_type{}, tt, stg(p), scl(p), q8reg);
+          kept_step(std::true_type{}, tt, stg(p), scl(p), low_scores);
           next();
         });
       }
@@ -1777,7 +1821,6 @@ void k3_attn(AttnArgs a) {
 // translation unit (k3_bk*.hip) so that the instances compile in parallel.
 template <int BK, int D, int NW, bool DUMP>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  if (a.refine && BK != 64) return hipErrorInvalidValue;
   if (a.skim && a.refine) return hipErrorInvalidValue;
   if (a.d.Nk > kMaxNk || a.list_cap < 1 || a.list_cap > a.d.Nk) return hipErrorInvalidValue;
   if (DUMP && (!a.dslot || !a.dump || a.dsteps < 1)) return hipErrorInvalidValue;
@@ -1785,14 +1828,10 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.d.BH * a.d.Nq), block(NW * 64);
   if (a.skim)
     hipLaunchKernelGGL((k3_attn<D, NW, BK, true, DUMP, false>), grid, block, lds, s, a);
-  else if constexpr (BK == 64) {
-    if (a.refine)
-      hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((k3_attn<D, NW, 64, false, DUMP, false>), grid, block, lds, s, a);
-  } else {
+  else if (a.refine)
+    hipLaunchKernelGGL((k3_attn<D, NW, BK, false, DUMP, true>), grid, block, lds, s, a);
+  else
     hipLaunchKernelGGL((k3_attn<D, NW, BK, false, DUMP, false>), grid, block, lds, s, a);
-  }
   return hipGetLastError();
 }
 

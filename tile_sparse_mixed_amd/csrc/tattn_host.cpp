@@ -170,8 +170,6 @@ static tattn_status validate(const tattn_config* c) {
   if (c->mode == TATTN_MODE_THRESHOLD && c->tau_skim > c->tau_lo)
     return fail(TATTN_E_INVALID, "tau_skim needs 0 <= tau_skim <= tau_lo (got %g, tau_lo %g)", c->tau_skim, c->tau_lo);
   if (c->low_refine != 0 && c->low_refine != 1) return fail(TATTN_E_INVALID, "low_refine must be 0 or 1 (got %d)", c->low_refine);
-  if (refine_on(*c) && c->block_k != 64)
-    return fail(TATTN_E_UNSUPPORTED, "the refined low tier needs 64-key blocks (block_k %d)", c->block_k);
   if (refine_on(*c) && skim_on(*c))
     return fail(TATTN_E_UNSUPPORTED, "the refined low tier and the SKIM tier are not combined");
   const int64_t nq = (c->seq_len + (int64_t)c->block_q - 1) / c->block_q;

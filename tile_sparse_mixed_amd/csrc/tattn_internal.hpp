@@ -34,7 +34,7 @@ struct Slab {
   size_t kblo;    // bf16 [Nk][D]       K block means, lo part (kbar = hi + lo to ~2^-17)
   size_t vbarT;   // fp16 [NkC][D][64]  V block means transposed per chunk of 64 blocks,
                   //                    vt_pos order, zero past Nk
-  // SKIM tier or refined low tier only (zero-sized otherwise; 64-key blocks)
+  // SKIM tier or refined low tier only (zero-sized otherwise)
   size_t k4;      // u8   [Nk][64][D/2]  MXFP4 K codes, channel 2m in the low nibble of byte m
   size_t k4s;     // u8   [Nk][64][D/32] E8M0 scale of each 32 channels of a K row
   // refined low tier only: the MXFP4 copy of the residual k - dequant(k4)
@@ -115,7 +115,7 @@ struct AttnArgs {
   Layout L;
   Dims d;
   int skim;       // the plan may hold SKIM tiles (64-key blocks)
-  int refine;     // LOW tiles score on MXFP4 with residual correction (64-key blocks)
+  int refine;     // LOW tiles score on MXFP4 with residual correction
   int list_cap;   // bound on a row's FULL + LOW + SKIM tiles under the plan's mode (<= Nk)
   // probability-code dump (tattn_forward_dump; null otherwise): row r with
   // dslot[r] >= 0 writes the codes of its LOW and SKIM steps s < dsteps to
