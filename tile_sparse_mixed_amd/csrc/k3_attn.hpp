@@ -743,7 +743,8 @@ void k3_attn(AttnArgs a) {
         for (int i = 0; i < NI16; i++) {
           const int k = wave + NW * i;
           if constexpr (PA) dma16(rS, st + k * 1024, lkb[i % NSW], (int)SL.kbhi + c * 128 * D + k * 1024);
-          if constexpr (PB) dma16(rS, r1(st) + k * 1024, lkb[i % NSW], (int)SL.kblo + c * 128 * D + k * 1024);
+          if constexpr (PB && BK > 1)   // (one-key blocks: the lo half is zero)
+            dma16(rS, r1(st) + k * 1024, lkb[i % NSW], (int)SL.kblo + c * 128 * D + k * 1024);
         }
       } else if (KINDS & (1 << kSkipPV)) {
         if constexpr (PB) load_vt16(r1(st), rS, (int)SL.vbarT + c * 128 * D);
@@ -1363,7 +1364,9 @@ void k3_attn(AttnArgs a) {
   // part from R0, lo part from R1), then the bias and the softmax
   auto skip_S = [&](const unsigned char* st, f32x16* s) __attribute__((always_inline)) {
     scores_bf16(st, s);
-    scores_bf16(r1(st), s);   // low half of kbar
+    // low half of kbar; with one-key blocks the mean is the key itself, a bf16
+    // value, so the low half is zero and its pass is left out
+    if constexpr (BK > 1) scores_bf16(r1(st), s);
   };
   auto skip_soft = [&](int t, f32x16* s) __attribute__((always_inline)) {
     // bias log2(n_J) for the row's skipped blocks, -inf for the others.  Key
@@ -1743,7 +1746,7 @@ void k3_attn(AttnArgs a) {
     auto no_soft = [&](f32x16*, const StepScale<G>&) {};
     while (t < nS2) {
       if ((t & 1) == 0)
-        split_step(KSkipPV{}, T1{}, T0{}, T1{}, T0{},
+        split_step(KSkipPV{}, T1{}, T0{}, std::integral_constant<bool, (BK > 1)>{}, T0{},
                    [&](f32x16* s) __attribute__((always_inline)) { skip_S(stA, s); },
                    [&](f32x16* s, const StepScale<G>&) __attribute__((always_inline)) { skip_soft(t, s); });
       else
