@@ -120,11 +120,12 @@ def test_full_size_sampled(name):
         assert np.array_equal(plain.float().cpu().numpy(), out), name
 
 
-@pytest.mark.parametrize("wl", ["fine_adaptive", "finer_adaptive"])
+@pytest.mark.parametrize("wl", ["fine_adaptive", "finer_adaptive", "fg4_adaptive", "fg1_adaptive"])
 def test_full_size_fine_adaptive(wl):
     """The fine-grained head-adaptive workloads: 32760 tokens x 40 heads, 64q x
-    16k (and 64q x 8k) tiles, k_h from the entropy of p on 256 sampled query
-    blocks per head."""
+    16k (and 64q x 8k) tiles, and 15600 (3120) tokens x 40 heads at 64q x 4k
+    (64q x 1k) tiles, k_h from the entropy of p on 256 sampled query blocks per
+    head."""
     import tile_sparse_mixed_amd as tsm
     import torch
     cfg = CONFIGS[wl]

@@ -113,17 +113,18 @@ def test_skim_bytes_need_the_tier():
         p.mx4()
 
 
-def test_full_size_wan_shape_sampled():
-    """32760 tokens x d 128 at 128x64 tiles with the SKIM tier (two of the
-    workload's heads): tiers and lists exact outside the bands, output on three
-    query blocks including the ragged last one."""
+@pytest.mark.parametrize("wl", ["wan_skim", "fine_skim"])
+def test_full_size_wan_shape_sampled(wl):
+    """32760 tokens x d 128 at 128x64 (and 64x16) tiles with the SKIM tier (two
+    of the workload's heads): tiers and lists exact outside the bands, output
+    on three query blocks including the ragged last one."""
     import tile_sparse_mixed_amd as tsm
-    cfg = CONFIGS["wan_skim"]
+    cfg = CONFIGS[wl]
     g, dev = device_inputs(cfg, heads=[0, 7])
     p = _plan(tsm, dev, cfg)
     tiers = p.tiers()
     lists, counts = p.lists()
-    _log(f"[skim full size] FULL/LOW/SKIM/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 3, 0)]}")
+    _log(f"[skim full size {wl}] FULL/LOW/SKIM/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 3, 0)]}")
     oc = OracleCfg(cfg)
     rows = [0, cfg.n_qblocks // 2, cfg.n_qblocks - 1]
     for h in range(2):
