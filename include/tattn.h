@@ -28,8 +28,9 @@
  *   - "HierPAS" (abstract): a lightweight eager estimate of the attention
  *     pattern, sampling-based entropy for head-wise retention ratios,
  *     progressively reduced precision, a top-k engine.
- *   - "FG-Attn" (abstract): M x N tile granularity (key blocks down to 8 keys
- *     here, gathered eight at a time into dense MFMA slabs).
+ *   - "FG-Attn" (abstract): M x N tile granularity (key blocks of 64, 16, 8,
+ *     4, 2 or 1 keys here; blocks below 64 keys are gathered 64 / block_k at
+ *     a time into dense 64-key MFMA slabs).
  *
  * Conventions
  *   - Every pointer is a DEVICE pointer unless its comment says "host".
@@ -75,7 +76,8 @@ typedef enum {
                                 top_k > 0 first keeps only the row's top_k tiles        */
   TATTN_MODE_ADAPTIVE = 1,   /* per head k_h from the entropy of p on sampled rows; per row
                                 the top ceil(full_frac*k_h) tiles FULL, the rest of the top
-                                k_h LOW, the remainder SKIP                              */
+                                k_h LOW, the remainder SKIP (SKIM where tau_skim > 0 and
+                                p >= tau_skim)                                           */
   TATTN_MODE_ALL_FULL = 2,   /* every tile FULL: dense attention through the same kernel */
   TATTN_MODE_EXTERNAL = 3,   /* tiers supplied with tattn_plan_set_tiers                 */
   TATTN_MODE_PRICE = 4       /* each tile takes the tier minimising predicted error plus
