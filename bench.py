@@ -177,8 +177,8 @@ def cpu_baseline(g, cfg, budget_s, price=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(heads shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(heads would shard across GPUs with no exchange; that path is not implemented)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
