@@ -44,8 +44,9 @@ tier the scores come from MXFP4 copies with an MXFP4 residual correction
 (Triage: refining a tile with 4-bit residual correction; refine_operands).
 
 Precision: float64 throughout, except that every fp8 code is decided on a
-float32 value (the value the kernel converts) and the dequantised E4M3 values
-are products rounded once to float32.  Means are accumulated in float64 and
+float32 value (a code is an integer decided by a floating-point value, and
+that decision is taken in float32 wherever it is made) and the dequantised
+E4M3 values are products rounded once to float32.  Means are accumulated in float64 and
 stored as float32.
 """
 import math
