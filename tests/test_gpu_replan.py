@@ -78,3 +78,31 @@ def test_replan_on_the_same_inputs_is_bit_identical_and_rebinds_k_v():
     assert torch.equal(a, b)
     with pytest.raises(tsm.TattnError):
         tsm.forward(p, d0["q"], d0["k"], d0["v"])     # the plan now belongs to the new K and V
+
+
+@pytest.mark.parametrize("name", ["small", "d128_ragged"])
+def test_forward_with_new_q_takes_its_own_q_scales(name):
+    """A forward given queries other than the ones the plan was routed with
+    (same K and V, no replan): the tiers stay the plan's, and the LOW tier's
+    per-block E4M3 Q scales come from the new queries.  The new queries are
+    the next step's, times 4 (exact in bf16), so every block's amax differs
+    from the routed one: with the routed scales the E4M3 copy of Q would
+    saturate.  Compared with the oracle under the plan's tiers on the new
+    queries."""
+    import tile_sparse_mixed_amd as tsm
+    from synth.gen import bf16_bits_to_f32, to_bf16_bits
+    cfg = CASES[name]
+    g0 = generate(cfg)
+    q_new = 4.0 * drift_step(g0, cfg, 1, 0.1)["q"]
+    g = dict(g0)
+    g["bits"] = dict(g0["bits"])
+    g["bits"]["q"] = to_bf16_bits(q_new)
+    g["q"] = bf16_bits_to_f32(g["bits"]["q"]).astype(np.float32)
+    assert np.array_equal(g["q"], q_new)
+    d0 = _dev(g0)
+    d = dict(d0, q=_dev(g)["q"])      # the plan's own K and V tensors
+    p = _plan(tsm, cfg, d0, "threshold")
+    t0 = p.tiers()
+    assert (t0 == 1).any(), "the case must have LOW tiles"
+    check_forward(tsm, p, d, g, cfg, OracleCfg(cfg, mode=3), what=f"new q {name}", log=_log)
+    assert np.array_equal(p.tiers(), t0)
