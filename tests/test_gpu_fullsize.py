@@ -161,3 +161,40 @@ def test_full_size_fine_adaptive(wl):
                            rows=lambda b, h, t: sample_rows(nq, 16, t), heads=[(0, h) for h in sample_heads],
                            what=f"{wl} bf16 output (k_h {[int(kh[h]) for h in sample_heads]})", log=_log)
     assert np.array_equal(plain.float().cpu().numpy(), out), wl
+
+
+def test_full_size_all_full_equals_dense():
+    """Every tile FULL at the Wan-like size (32760 tokens x 40 heads, 128x64
+    tiles), the launch the benchmark's all-full comparison times: sampled
+    query blocks of four distinct heads against textbook softmax(QK^T/sqrt d)V
+    in float64 over all 32760 keys, max-abs <= 5e-3; with bfloat16 output
+    half a bfloat16 ulp of the reference more."""
+    import tile_sparse_mixed_amd as tsm
+    cfg = CONFIGS["wan_like"]
+    gen_heads, sample_heads = 4, [0, 13, 26, 39]
+    g = generate(cfg.with_(heads=gen_heads))
+    dev = _device_tiled(g["bits"], cfg.heads)
+    nq = cfg.n_qblocks
+    rows = sorted({0, nq - 1, *np.linspace(0, nq - 1, 8).astype(int).tolist()})
+    refs = {}
+    for h in sample_heads:
+        src = h % gen_heads
+        q, k, v = g["q"][0, src], g["k"][0, src], g["v"][0, src]
+        for I in rows:
+            r0, r1 = I * cfg.block_q, min(cfg.seq_len, (I + 1) * cfg.block_q)
+            refs[(h, I)] = T.naive_attention(q[r0:r1], k, v)
+    for out_fp32 in (True, False):
+        p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, mode="all_full",
+                     out_fp32=out_fp32)
+        assert (p.tiers() == 2).all()
+        o = tsm.forward(p, dev["q"], dev["k"], dev["v"]).float().cpu().numpy()
+        worst = 0.0
+        for (h, I), ref in refs.items():
+            r0, r1 = I * cfg.block_q, min(cfg.seq_len, (I + 1) * cfg.block_q)
+            err = np.abs(o[0, h, r0:r1].astype(np.float64) - ref)
+            if not out_fp32:
+                err = err - np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 9)
+            worst = max(worst, float(err.max()))
+            assert err.max() <= 5e-3, (h, I, out_fp32, float(err.max()))
+        _log(f"[all-full 32760x40] {'fp32' if out_fp32 else 'bf16'} output: {len(refs)} query blocks, "
+             f"worst max-abs {worst:.3e}{' beyond half a bf16 ulp' if not out_fp32 else ''}")
