@@ -198,3 +198,38 @@ def test_full_size_all_full_equals_dense():
             assert err.max() <= 5e-3, (h, I, out_fp32, float(err.max()))
         _log(f"[all-full 32760x40] {'fp32' if out_fp32 else 'bf16'} output: {len(refs)} query blocks, "
              f"worst max-abs {worst:.3e}{' beyond half a bf16 ulp' if not out_fp32 else ''}")
+
+
+def test_full_size_refined_low_tier():
+    """The refined low tier (low_refine = 1: LOW scores from MXFP4 Q and K plus
+    the MXFP4 residual of each) in the Wan-like launch: 32760 tokens x 40
+    heads, 128x64 tiles, bf16 output.  Four distinct generated heads tiled to
+    40.  Tiers exact outside the bands, and 32 query blocks per sampled head
+    (the most-LOW and most-FULL rows among them) against the oracle's refined
+    tier with the kernel's probability codes admitted; the plain forward equal
+    to the code-dumping one bit for bit."""
+    import tile_sparse_mixed_amd as tsm
+    import torch
+    cfg = CONFIGS["wan_like"]
+    gen_heads, sample_heads = 4, [0, 13, 26, 39]
+    g = generate(cfg.with_(heads=gen_heads))
+    dev = _device_tiled(g["bits"], cfg.heads)
+    gt = _Tiled(g, gen_heads)
+    p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi,
+                 tau_lo=cfg.tau_lo, top_k=cfg.top_k, mode="threshold", out_fp32=False, low_refine=True)
+    plain = tsm.forward(p, dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    tiers = p.tiers()
+    oc = OracleCfg(cfg)
+    for h in sample_heads:
+        src = h % gen_heads
+        o = T.oracle_plan(g["q"][0, src], g["k"][0, src], g["v"][0, src], oc)
+        band = band_mask(o["p"], oc.tau_hi, oc.tau_lo)
+        assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), h
+    orf = OracleCfg(cfg, mode=3)
+    orf.low_refine = 1
+    nq = cfg.n_qblocks
+    out, _ = check_forward(tsm, p, dev, gt, cfg, orf, rows=lambda b, h, t: sample_rows(nq, 32, t),
+                           heads=[(0, h) for h in sample_heads], what="refined low tier, Wan-like bf16 output",
+                           log=_log)
+    assert np.array_equal(plain.float().cpu().numpy(), out)
