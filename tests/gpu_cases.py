@@ -282,3 +282,55 @@ def check_forward(tsm, p, dev, g, cfg, oc, rows=None, heads=None, what="", log=p
     log(f"  {what}: worst block max-abs {worst_max:.3e} mean-abs {worst_mean:.3e}"
         f"{' (bf16 output: max-abs beyond half a bf16 ulp; mean-abs against the oracle rounded to bf16)' if bf16 else ''}")
     return o, refs
+
+
+# ---- full-size launches from a few generated heads tiled to the full head count
+def sample_rows(nq, n, tiers):
+    """n query blocks: the first and the ragged last, the rows with the most
+    LOW tiles and with the most FULL tiles (a quarter of n each), then evenly
+    spaced ones."""
+    rows = [0, nq - 1]
+    for tier in (1, 2):
+        added = 0
+        for I in np.argsort(-(tiers == tier).sum(axis=1), kind="stable"):
+            if added >= n // 4 or len(rows) >= n:
+                break
+            if int(I) not in rows:
+                rows.append(int(I))
+                added += 1
+    for I in np.linspace(0, nq - 1, n).astype(int):
+        if len(rows) >= min(n, nq):
+            break
+        if int(I) not in rows:
+            rows.append(int(I))
+    return sorted(rows)
+
+
+def device_tiled(bits, heads):
+    import torch
+    out = {}
+    for n in ("q", "k", "v"):
+        t = torch.from_numpy(bits[n].view(np.int16)).view(torch.bfloat16).cuda()
+        idx = torch.arange(heads, device="cuda") % t.shape[1]
+        out[n] = t.index_select(1, idx).contiguous()
+    return out
+
+
+class TiledHeads:
+    """The generated heads seen at the tiled head indices."""
+
+    def __init__(self, g, gen_heads):
+        self.g, self.n = g, gen_heads
+
+    def __getitem__(self, name):
+        x = self.g[name]
+        return HeadView(x, self.n)
+
+
+class HeadView:
+    def __init__(self, x, n):
+        self.x, self.n = x, n
+
+    def __getitem__(self, idx):
+        b, h = idx
+        return self.x[b, h % self.n]

@@ -19,7 +19,7 @@ import pytest
 from oracle import tattn as T
 from synth import CONFIGS, generate
 
-from gpu_cases import OracleCfg, band_mask, check_forward
+from gpu_cases import OracleCfg, band_mask, check_forward, device_tiled, sample_rows, TiledHeads
 
 pytestmark = pytest.mark.gpu
 
@@ -30,59 +30,8 @@ CASES = {
 }
 
 
-def sample_rows(nq, n, tiers):
-    """n query blocks: the first and the ragged last, the rows with the most
-    LOW tiles and with the most FULL tiles (a quarter of n each), then evenly
-    spaced ones."""
-    rows = [0, nq - 1]
-    for tier in (1, 2):
-        added = 0
-        for I in np.argsort(-(tiers == tier).sum(axis=1), kind="stable"):
-            if added >= n // 4 or len(rows) >= n:
-                break
-            if int(I) not in rows:
-                rows.append(int(I))
-                added += 1
-    for I in np.linspace(0, nq - 1, n).astype(int):
-        if len(rows) >= min(n, nq):
-            break
-        if int(I) not in rows:
-            rows.append(int(I))
-    return sorted(rows)
-
-
 def _log(msg):
     print(msg, flush=True)
-
-
-def _device_tiled(bits, heads):
-    import torch
-    out = {}
-    for n in ("q", "k", "v"):
-        t = torch.from_numpy(bits[n].view(np.int16)).view(torch.bfloat16).cuda()
-        idx = torch.arange(heads, device="cuda") % t.shape[1]
-        out[n] = t.index_select(1, idx).contiguous()
-    return out
-
-
-class _Tiled:
-    """The generated heads seen at the tiled head indices."""
-
-    def __init__(self, g, gen_heads):
-        self.g, self.n = g, gen_heads
-
-    def __getitem__(self, name):
-        x = self.g[name]
-        return _Heads(x, self.n)
-
-
-class _Heads:
-    def __init__(self, x, n):
-        self.x, self.n = x, n
-
-    def __getitem__(self, idx):
-        b, h = idx
-        return self.x[b, h % self.n]
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -93,8 +42,8 @@ def test_full_size_sampled(name):
     cfg = CONFIGS[wl]
     _log(f"[full {name}] N={cfg.seq_len} H={cfg.heads} d={cfg.head_dim} (generating {gen_heads} heads)")
     g = generate(cfg.with_(heads=gen_heads))
-    dev = _device_tiled(g["bits"], cfg.heads)
-    gt = _Tiled(g, gen_heads)
+    dev = device_tiled(g["bits"], cfg.heads)
+    gt = TiledHeads(g, gen_heads)
     oc = OracleCfg(cfg)
     for out_fp32 in (False, True):
         p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k,
@@ -132,7 +81,7 @@ def test_full_size_fine_adaptive(wl):
     gen_heads, sample_heads = 3, [0, 20, 38]
     _log(f"[full {wl}] N={cfg.seq_len} H={cfg.heads} tile={cfg.block_q}x{cfg.block_k}")
     g = generate(cfg.with_(heads=gen_heads))
-    dev = _device_tiled(g["bits"], cfg.heads)
+    dev = device_tiled(g["bits"], cfg.heads)
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, mode="adaptive",
                  keep_min=cfg.keep_min, keep_max=cfg.keep_max, full_frac=cfg.full_frac,
                  entropy_samples=cfg.entropy_samples)
@@ -157,7 +106,7 @@ def test_full_size_fine_adaptive(wl):
                 if 0 < kk < nk:
                     amb |= np.abs(srt[:, kk - 1] - srt[:, kk]) <= 1e-12 * srt[:, kk - 1]
             assert np.array_equal(tiers[0, h][~amb], o["tiers"][~amb]), h
-    out, _ = check_forward(tsm, p, dev, _Tiled(g, gen_heads), cfg, oc,
+    out, _ = check_forward(tsm, p, dev, TiledHeads(g, gen_heads), cfg, oc,
                            rows=lambda b, h, t: sample_rows(nq, 16, t), heads=[(0, h) for h in sample_heads],
                            what=f"{wl} bf16 output (k_h {[int(kh[h]) for h in sample_heads]})", log=_log)
     assert np.array_equal(plain.float().cpu().numpy(), out), wl
@@ -173,7 +122,7 @@ def test_full_size_all_full_equals_dense():
     cfg = CONFIGS["wan_like"]
     gen_heads, sample_heads = 4, [0, 13, 26, 39]
     g = generate(cfg.with_(heads=gen_heads))
-    dev = _device_tiled(g["bits"], cfg.heads)
+    dev = device_tiled(g["bits"], cfg.heads)
     nq = cfg.n_qblocks
     rows = sorted({0, nq - 1, *np.linspace(0, nq - 1, 8).astype(int).tolist()})
     refs = {}
@@ -213,8 +162,8 @@ def test_full_size_refined_low_tier():
     cfg = CONFIGS["wan_like"]
     gen_heads, sample_heads = 4, [0, 13, 26, 39]
     g = generate(cfg.with_(heads=gen_heads))
-    dev = _device_tiled(g["bits"], cfg.heads)
-    gt = _Tiled(g, gen_heads)
+    dev = device_tiled(g["bits"], cfg.heads)
+    gt = TiledHeads(g, gen_heads)
     p = tsm.plan(dev["q"], dev["k"], dev["v"], block_q=cfg.block_q, block_k=cfg.block_k, tau_hi=cfg.tau_hi,
                  tau_lo=cfg.tau_lo, top_k=cfg.top_k, mode="threshold", out_fp32=False, low_refine=True)
     plain = tsm.forward(p, dev["q"], dev["k"], dev["v"])

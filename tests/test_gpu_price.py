@@ -14,7 +14,7 @@ from synth.gen import to_bf16_bits, bf16_bits_to_f32
 
 from types import SimpleNamespace
 
-from gpu_cases import check_forward, OracleCfg
+from gpu_cases import check_forward, OracleCfg, device_tiled, sample_rows, TiledHeads
 
 pytestmark = pytest.mark.gpu
 
@@ -207,3 +207,35 @@ def test_price_skim_off_matches_three_tier():
         o = T.oracle_plan(g["q"][0, h], g["k"][0, h], g["v"][0, h], oc)
         tie = _near_tie(o["price"]["objs"])
         assert not ((t[0, h] != o["tiers"]) & (~tie | diag)).any()
+
+
+def test_price_router_full_size_sampled():
+    """The price router in the Wan-like launch (32760 tokens x 40 heads,
+    128x64 tiles, price 0.01, bf16 output): four distinct generated heads
+    tiled to 40.  Tiers exact outside near-ties and lists exact on the sampled
+    heads, and 32 query blocks per sampled head (the most-LOW and most-FULL
+    rows among them) against the oracle under the GPU's tiers."""
+    import torch
+    import tile_sparse_mixed_amd as tsm
+    cfg = CONFIGS["wan_like"]
+    gen_heads, sample_heads, price = 4, [0, 13, 26, 39], 0.01
+    g = generate(cfg.with_(heads=gen_heads))
+    dev = device_tiled(g["bits"], cfg.heads)
+    p = _plan(dev, cfg, price, out_fp32=False)
+    torch.cuda.synchronize()
+    tiers = p.tiers()
+    lists, counts = p.lists()
+    _log(f"[price full size {price}] FULL/LOW/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 0)]}")
+    diag = T.diagonal_mask(cfg.seq_len, cfg.block_q, cfg.block_k)
+    for h in sample_heads:
+        o = _oracle(g, h % gen_heads, cfg, price)
+        tie = _near_tie(o["price"]["objs"])
+        assert tie.mean() < 1e-3, (h, tie.mean())
+        mism = (tiers[0, h] != o["tiers"]) & (~tie | diag)
+        assert not mism.any(), (h, np.argwhere(mism)[:5])
+        li, co = T.build_lists(tiers[0, h])
+        assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), h
+    nq = cfg.n_qblocks
+    check_forward(tsm, p, dev, TiledHeads(g, gen_heads), cfg, OracleCfg(cfg, mode=3),
+                  rows=lambda b, h, t: sample_rows(nq, 32, t), heads=[(0, h) for h in sample_heads],
+                  what=f"price {price} full size, bf16 output", log=_log)
