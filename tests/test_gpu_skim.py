@@ -9,9 +9,9 @@ import pytest
 
 from oracle import mxfp4
 from oracle import tattn as T
-from synth import CONFIGS
+from synth import CONFIGS, generate
 
-from gpu_cases import check_forward, OracleCfg, band_mask, device_inputs
+from gpu_cases import check_forward, OracleCfg, band_mask, device_inputs, device_tiled, sample_rows, TiledHeads
 
 pytestmark = pytest.mark.gpu
 
@@ -115,27 +115,37 @@ def test_skim_bytes_need_the_tier():
 
 @pytest.mark.parametrize("wl", ["wan_skim", "fine_skim"])
 def test_full_size_wan_shape_sampled(wl):
-    """32760 tokens x d 128 at 128x64 (and 64x16) tiles with the SKIM tier (two
-    of the workload's heads): tiers and lists exact outside the bands, output
-    on three query blocks including the ragged last one."""
+    """The SKIM tier in the full launch: 32760 tokens x 40 heads x d 128 at
+    128x64 (and 64x16) tiles, four distinct generated heads tiled to 40.
+    Tiers and lists exact outside the bands on the sampled heads, and 32
+    query blocks per sampled head (the first, the ragged last, the most-LOW
+    and most-FULL rows, evenly spaced ones) against the oracle under the GPU's
+    tiers; the plain forward equal to the code-dumping one bit for bit."""
+    import torch
     import tile_sparse_mixed_amd as tsm
     cfg = CONFIGS[wl]
-    g, dev = device_inputs(cfg, heads=[0, 7])
-    p = _plan(tsm, dev, cfg)
+    gen_heads, sample_heads = 4, [0, 13, 26, 39]
+    g = generate(cfg.with_(heads=gen_heads))
+    dev = device_tiled(g["bits"], cfg.heads)
+    p = _plan(tsm, dev, cfg, out_fp32=False)
+    plain = tsm.forward(p, dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
     tiers = p.tiers()
     lists, counts = p.lists()
     _log(f"[skim full size {wl}] FULL/LOW/SKIM/SKIP {[round(float((tiers == x).mean()), 4) for x in (2, 1, 3, 0)]}")
     oc = OracleCfg(cfg)
-    rows = [0, cfg.n_qblocks // 2, cfg.n_qblocks - 1]
-    for h in range(2):
-        q, k, v = g["q"][0, h], g["k"][0, h], g["v"][0, h]
-        o = T.oracle_plan(q, k, v, oc)
+    for h in sample_heads:
+        src = h % gen_heads
+        o = T.oracle_plan(g["q"][0, src], g["k"][0, src], g["v"][0, src], oc)
         band = band_mask(o["p"], oc.tau_hi, oc.tau_lo, tau_skim=oc.tau_skim)
         assert np.array_equal(tiers[0, h][~band], o["tiers"][~band]), h
         li, co = T.build_lists(tiers[0, h])
         assert np.array_equal(lists[0, h], li) and np.array_equal(counts[0, h], co), h
-    check_forward(tsm, p, dev, g, cfg.with_(heads=2), OracleCfg(cfg, mode=3), rows=rows, what="skim full size",
-                  log=_log)
+    nq = cfg.n_qblocks
+    out, _ = check_forward(tsm, p, dev, TiledHeads(g, gen_heads), cfg, OracleCfg(cfg, mode=3),
+                           rows=lambda b, h, t: sample_rows(nq, 32, t), heads=[(0, h) for h in sample_heads],
+                           what=f"skim full size {wl}", log=_log)
+    assert np.array_equal(plain.float().cpu().numpy(), out), wl
 
 
 def test_zero_blocks_in_skim_tiles():
