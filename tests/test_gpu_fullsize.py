@@ -69,16 +69,17 @@ def test_full_size_sampled(name):
         assert np.array_equal(plain.float().cpu().numpy(), out), name
 
 
-@pytest.mark.parametrize("wl", ["fine_adaptive", "finer_adaptive", "fg4_adaptive", "fg1_adaptive"])
+@pytest.mark.parametrize("wl", ["wan_adaptive", "fine_adaptive", "finer_adaptive", "fg4_adaptive", "fg1_adaptive"])
 def test_full_size_fine_adaptive(wl):
     """The fine-grained head-adaptive workloads: 32760 tokens x 40 heads, 64q x
     16k (and 64q x 8k) tiles, and 15600 (3120) tokens x 40 heads at 64q x 4k
     (64q x 1k) tiles, k_h from the entropy of p on 256 sampled query blocks per
-    head."""
+    head; and the Wan-like launch (128q x 64k tiles) under the same adaptive
+    rule."""
     import tile_sparse_mixed_amd as tsm
     import torch
-    cfg = CONFIGS[wl]
-    gen_heads, sample_heads = 3, [0, 20, 38]
+    cfg = CONFIGS["wan_like"].with_(mode=1) if wl == "wan_adaptive" else CONFIGS[wl]
+    gen_heads, sample_heads = 3, [0, 19, 38]   # generated heads 0, 1 and 2
     _log(f"[full {wl}] N={cfg.seq_len} H={cfg.heads} tile={cfg.block_q}x{cfg.block_k}")
     g = generate(cfg.with_(heads=gen_heads))
     dev = device_tiled(g["bits"], cfg.heads)
