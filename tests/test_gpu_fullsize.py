@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # workload, generated heads, sampled heads (distinct sources), query blocks per head
     "wan_32760x40": ("wan_like", 8, [0, 9, 18, 27, 36, 5, 14, 23], 32),
-    "hunyuan_118800x24": ("hunyuan_like", 2, [0, 23], 32),
+    "hunyuan_118800x24": ("hunyuan_like", 4, [0, 5, 10, 23], 32),
 }
 
 
